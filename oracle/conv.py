@@ -1,0 +1,190 @@
+"""Forward, backward and double backward of the CGTP convolution (oracle).
+
+TEST INFRASTRUCTURE ONLY.  Plain float64 PyTorch CPU code written from:
+
+* Sobek section 2.4, Eq. 7: r_ij = r_j - r_i (here pos[send] - pos[recv] + shift);
+* Sobek section 2.4, Eqs. 11-12 and LunaTP Algorithm 1: the conventional
+  schedule, m_i = sum_j sum_pi sum_a W_ij,pi,a T_pi,a(x_j, Y_ij) with
+  W = phi A materialised per path;
+* Sobek section 4.2, Eqs. 32-35: the streamed schedule, receiver state
+  S_i,pi,q,u,mo = sum_j phi_ij,q C_pi,u,mo(x_j, Y_ij), then m = S A;
+* Sobek section 3.2, Eqs. 18-22: the backward (h, A-bar, phi-bar, x-bar,
+  Y-bar), followed by the chain rule through Y(r) for the edge-vector and
+  position gradients;
+* Sobek section 3.3, Eqs. 23-31: the double backward, assembled as the
+  vector-Jacobian product of the backward map.
+
+The per-path angular contraction is LunaTP Eq. 1 with the real coupling
+tensors of ``cg``; no path normalisation factor beyond them (alpha_pi = 1).
+Loops run over paths (and, where memory demands, over edge or radial slices);
+everything inside a path is an einsum over edges and channels.
+"""
+
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+from . import cg as _cg
+from . import sh as _sh
+from .irreps import Problem
+
+_F64 = torch.float64
+
+
+def _t(a) -> torch.Tensor:
+    if isinstance(a, torch.Tensor):
+        return a.to(_F64)
+    return torch.as_tensor(np.asarray(a), dtype=_F64)
+
+
+def _idx(a) -> torch.Tensor:
+    return torch.as_tensor(np.asarray(a), dtype=torch.long)
+
+
+def edge_vectors(pos, shift, recv, send) -> torch.Tensor:
+    """Sobek Eq. 7: r_ij = r_j - r_i for edge i <- j, plus the periodic image shift."""
+    pos, shift = _t(pos), _t(shift)
+    recv, send = _idx(recv), _idx(send)
+    return pos[send] - pos[recv] + shift
+
+
+def _block(feat: torch.Tensor, b) -> torch.Tensor:
+    """View of block b of an ir_mul feature matrix as (rows, 2l+1, mul)."""
+    return feat[:, b.offset:b.offset + b.size].reshape(feat.shape[0], b.dim, b.mul)
+
+
+def _coupling(p) -> torch.Tensor:
+    return torch.as_tensor(_cg.real_cg(p.l1, p.l2, p.l3), dtype=_F64)
+
+
+def spherical_harmonics(problem: Problem, edge_vec) -> torch.Tensor:
+    return _sh.sh(problem.lmax_sh, _t(edge_vec))
+
+
+def _angular(problem: Problem, p, x: torch.Tensor, Y: torch.Tensor, send: torch.Tensor) -> torch.Tensor:
+    """T_pi(x_j, Y_ij)[e, m3, u] = sum_{m1, m2} c[m1, m2, m3] x_j[m1, u] Y[m2] (LunaTP Eq. 1)."""
+    bi, bs = problem.irreps_in[p.i_in], problem.irreps_sh[p.i_sh]
+    xj = _block(x, bi)[send]                      # (E, d1, C)
+    Yb = Y[:, bs.offset:bs.offset + bs.dim]       # (E, d2)
+    return torch.einsum("abc,eau,eb->ecu", _coupling(p), xj, Yb)
+
+
+def forward_conventional(problem: Problem, x, edge_vec, recv, send, phi, A,
+                         edge_chunk: int = 1 << 14) -> torch.Tensor:
+    """Sobek Eqs. 11-12: materialise W = phi A per path, form each edge message, sum into receivers."""
+    x, phi, A = _t(x), _t(phi), _t(A)
+    recv, send = _idx(recv), _idx(send)
+    N, E = x.shape[0], recv.shape[0]
+    Y = spherical_harmonics(problem, edge_vec)
+    out = torch.zeros(N, problem.c_out, dtype=_F64)
+    for p in problem.paths:
+        bo = problem.irreps_out[p.i_out]
+        Ap = A[:, p.weight_offset:p.weight_offset + p.n_weights]
+        acc = torch.zeros(N, bo.dim, bo.mul, dtype=_F64)
+        for s in range(0, E, edge_chunk):
+            sl = slice(s, min(E, s + edge_chunk))
+            T = _angular(problem, p, x, Y[sl], send[sl])            # (e, d3, C_in)
+            W = phi[sl] @ Ap                                        # materialised edge weights
+            if problem.mode == "uvu":
+                msg = W[:, None, :] * T
+            else:
+                W = W.reshape(-1, T.shape[2], bo.mul)               # (e, u, w)
+                msg = torch.einsum("euw,ecu->ecw", W, T)
+            acc.index_add_(0, recv[sl], msg)
+        out[:, bo.offset:bo.offset + bo.size] += acc.reshape(N, -1)
+    return out
+
+
+def receiver_state(problem: Problem, p, x, Y, recv, send, phi, N: int) -> torch.Tensor:
+    """Sobek Eq. 33: S[i, q, m3, u] = sum_{j in N(i)} phi_ij,q C_pi,u,m3(x_j, Y_ij)."""
+    Cang = _angular(problem, p, x, Y, send)                          # Eq. 32, (E, d3, C_in)
+    K = phi.shape[1]
+    S = torch.zeros(N, K, Cang.shape[1], Cang.shape[2], dtype=_F64)
+    for q in range(K):
+        S[:, q].index_add_(0, recv, phi[:, q, None, None] * Cang)
+    return S
+
+
+def forward_streamed(problem: Problem, x, edge_vec, recv, send, phi, A) -> torch.Tensor:
+    """Sobek Eqs. 33-35: receiver state S per path, then the channel product m = S A."""
+    x, phi, A = _t(x), _t(phi), _t(A)
+    recv, send = _idx(recv), _idx(send)
+    N, K = x.shape[0], phi.shape[1]
+    Y = spherical_harmonics(problem, edge_vec)
+    out = torch.zeros(N, problem.c_out, dtype=_F64)
+    for p in problem.paths:
+        bi, bo = problem.irreps_in[p.i_in], problem.irreps_out[p.i_out]
+        S = receiver_state(problem, p, x, Y, recv, send, phi, N)    # (N, K, d3, C_in)
+        Ap = A[:, p.weight_offset:p.weight_offset + p.n_weights]
+        if problem.mode == "uvu":
+            m = torch.einsum("iqcu,qu->icu", S, Ap)
+        else:
+            m = torch.einsum("iqcu,quw->icw", S, Ap.reshape(K, bi.mul, bo.mul))
+        out[:, bo.offset:bo.offset + bo.size] += m.reshape(N, -1)
+    return out
+
+
+def _sh_vjp(problem: Problem, edge_vec, Ybar: torch.Tensor) -> torch.Tensor:
+    """Chain rule through Y(r / |r|): returns J_Y(r)^T Ybar per edge."""
+    r = _t(edge_vec).clone().requires_grad_(True)
+    Y = _sh.sh(problem.lmax_sh, r)
+    (g,) = torch.autograd.grad(Y, r, grad_outputs=Ybar)
+    return g.detach()
+
+
+def backward(problem: Problem, x, edge_vec, recv, send, phi, A, grad_out,
+             n_nodes: Optional[int] = None, edge_chunk: int = 1 << 14) -> Dict[str, torch.Tensor]:
+    """Sobek Eqs. 18-22 plus the chain rule through Y(r) and r = pos[send] - pos[recv] + shift.
+
+    h_ij,pi,a = <mbar_i, T_pi,a(x_j, Y_ij)>;  Abar = sum phi h;  phibar = sum_pi,a A h;
+    xbar_j = sum_{i: j in N(i)} sum_pi,a w D_x T* mbar_i;  Ybar_ij = sum_pi,a w D_Y T* mbar_i;
+    ebar = J_Y^T Ybar;  posbar = sum_{out-edges} ebar - sum_{in-edges} ebar.
+    """
+    x, phi, A, gout = _t(x), _t(phi), _t(A), _t(grad_out)
+    recv, send = _idx(recv), _idx(send)
+    N = x.shape[0] if n_nodes is None else n_nodes
+    E, K = recv.shape[0], phi.shape[1]
+    Y = spherical_harmonics(problem, edge_vec)
+    gx = torch.zeros_like(x)
+    gphi = torch.zeros(E, K, dtype=_F64)
+    gA = torch.zeros_like(A)
+    gY = torch.zeros(E, problem.sh_dim, dtype=_F64)
+    for p in problem.paths:
+        bi, bs, bo = problem.irreps_in[p.i_in], problem.irreps_sh[p.i_sh], problem.irreps_out[p.i_out]
+        c = _coupling(p)
+        Ap = A[:, p.weight_offset:p.weight_offset + p.n_weights]
+        gAp = torch.zeros_like(Ap)
+        gxb = torch.zeros(x.shape[0], bi.dim, bi.mul, dtype=_F64)
+        for s in range(0, E, edge_chunk):
+            sl = slice(s, min(E, s + edge_chunk))
+            rs, ss = recv[sl], send[sl]
+            Yb = Y[sl, bs.offset:bs.offset + bs.dim]
+            xj = _block(x, bi)[ss]                       # (e, d1, C_in)
+            mb = _block(gout, bo)[rs]                    # (e, d3, C_out)
+            T = torch.einsum("abc,eau,eb->ecu", c, xj, Yb)
+            W = phi[sl] @ Ap
+            if problem.mode == "uvu":
+                h = (mb * T).sum(1)                                              # Eq. 18
+                Bx = torch.einsum("abc,eb,ecu->eau", c, Yb, mb)                  # D_x T* mbar
+                gxb.index_add_(0, ss, W[:, None, :] * Bx)                        # Eq. 21
+                gY[sl, bs.offset:bs.offset + bs.dim] += torch.einsum(
+                    "abc,eau,ecu,eu->eb", c, xj, mb, W)                          # Eq. 22
+            else:
+                W = W.reshape(-1, bi.mul, bo.mul)
+                h = torch.einsum("ecw,ecu->euw", mb, T).reshape(-1, p.n_weights)  # Eq. 18
+                Bx = torch.einsum("abc,eb,ecw->eaw", c, Yb, mb)
+                gxb.index_add_(0, ss, torch.einsum("euw,eaw->eau", W, Bx))       # Eq. 21
+                gY[sl, bs.offset:bs.offset + bs.dim] += torch.einsum(
+                    "abc,eau,ecw,euw->eb", c, xj, mb, W)                         # Eq. 22
+            gAp += phi[sl].T @ h                                                 # Eq. 19
+            gphi[sl] += h @ Ap.T                                                 # Eq. 20
+        gA[:, p.weight_offset:p.weight_offset + p.n_weights] = gAp
+        gx[:, bi.offset:bi.offset + bi.size] += gxb.reshape(x.shape[0], -1)
+    ge = _sh_vjp(problem, edge_vec, gY)
+    gpos = torch.zeros(N, 3, dtype=_F64)
+    gpos.index_add_(0, send, ge)
+    gpos.index_add_(0, recv, -ge)
+    return dict(x=gx, edge_vec=ge, pos=gpos, phi=gphi, A=gA, Y=gY)

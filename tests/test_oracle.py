@@ -1,0 +1,364 @@
+"""Pins of the CPU oracle against facts the pages and the mathematics fix (no GPU).
+
+Each test ties one oracle function to something other than itself: textbook
+coefficients, closed forms, SciPy's spherical harmonics, tables printed on the
+pages, symmetry (rotation and inversion equivariance), exact identities between
+the two schedules, brute force on tiny graphs and finite differences.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import cg, conv, csr, sh
+from oracle.irreps import make_problem, parse
+from tests.oracle_helpers import (golden_lines, make_case, random_rotation,
+                                  rotate_features, wigner_from_sh)
+
+LMAX = 6
+
+
+def _triples(lmax=LMAX):
+    for l1 in range(lmax + 1):
+        for l2 in range(lmax + 1):
+            for l3 in range(abs(l1 - l2), min(l1 + l2, lmax) + 1):
+                yield l1, l2, l3
+
+
+# --------------------------------------------------------------------------- CG
+
+def test_complex_cg_textbook_values():
+    n = 0
+    for line in golden_lines("clebsch_gordan_textbook.txt"):
+        l1, m1, l2, m2, L, M, expr = line.split(maxsplit=6)
+        ref = eval(expr, {"__builtins__": {}})
+        got = cg.complex_cg(int(l1), int(m1), int(l2), int(m2), int(L), int(M))
+        assert abs(got - ref) < 1e-15, line
+        n += 1
+    assert n == 15
+
+
+def test_complex_cg_zero_axial_closed_form():
+    # <l1 0 l2 0 | L 0> has a closed form in factorials (zero when l1 + l2 + L is odd).
+    for l1, l2, L in _triples():
+        s = l1 + l2 + L
+        got = cg.complex_cg(l1, 0, l2, 0, L, 0)
+        if s % 2:
+            assert got == 0.0
+            continue
+        g = s // 2
+        f = math.factorial
+        ref = ((-1) ** (g - L) * math.sqrt(2 * L + 1) * f(g) / (f(g - l1) * f(g - l2) * f(g - L))
+               * math.sqrt(f(2 * g - 2 * l1) * f(2 * g - 2 * l2) * f(2 * g - 2 * L) / f(2 * g + 1)))
+        assert abs(got - ref) < 1e-14
+
+
+def test_real_cg_orthonormal_columns():
+    for l1, l2, l3 in _triples():
+        c = cg.real_cg(l1, l2, l3).reshape(-1, 2 * l3 + 1)
+        np.testing.assert_allclose(c.T @ c, np.eye(2 * l3 + 1), atol=1e-14)
+
+
+def test_real_cg_scalar_identities():
+    for l in range(LMAX + 1):
+        np.testing.assert_allclose(cg.real_cg(0, l, l)[0], np.eye(2 * l + 1), atol=1e-15)
+        np.testing.assert_allclose(cg.real_cg(l, 0, l)[:, 0, :], np.eye(2 * l + 1), atol=1e-15)
+
+
+def test_real_cg_vector_products():
+    # (1,1->0) is the dot product / sqrt3; (1,1->1) the cross product / sqrt2 in (y, z, x) order.
+    np.testing.assert_allclose(cg.real_cg(1, 1, 0)[:, :, 0], np.eye(3) / math.sqrt(3), atol=1e-15)
+    eps = np.zeros((3, 3, 3))
+    for (a, b, c), s in {(0, 1, 2): 1, (1, 2, 0): 1, (2, 0, 1): 1,
+                         (0, 2, 1): -1, (2, 1, 0): -1, (1, 0, 2): -1}.items():
+        eps[a, b, c] = s
+    np.testing.assert_allclose(cg.real_cg(1, 1, 1), eps / math.sqrt(2), atol=1e-15)
+    g = np.random.default_rng(1)
+    u, v = g.normal(size=3), g.normal(size=3)
+    yzx = [1, 2, 0]
+    cross = np.einsum("abc,a,b->c", cg.real_cg(1, 1, 1), u[yzx], v[yzx]) * math.sqrt(2)
+    np.testing.assert_allclose(cross, np.cross(u, v)[yzx], atol=1e-14)
+
+
+def test_real_cg_rank2_symmetric_traceless():
+    c = cg.real_cg(1, 1, 2)
+    for m in range(5):
+        np.testing.assert_allclose(c[:, :, m], c[:, :, m].T, atol=1e-15)
+        assert abs(np.trace(c[:, :, m])) < 1e-15
+
+
+def test_real_cg_sign_rule():
+    for l1, l2, l3 in _triples():
+        flat = cg.real_cg(l1, l2, l3).reshape(-1)
+        assert flat[np.nonzero(flat)[0][0]] > 0
+
+
+def test_gaunt_identity_ties_cg_to_sh():
+    # sum c Y_l1(n) Y_l2(n) = kappa Y_l3(n), |kappa| = sqrt((2l1+1)(2l2+1)/(2l3+1)) |<l1 0 l2 0|l3 0>|.
+    n = sh.unit(torch.as_tensor(np.random.default_rng(2).normal(size=(40, 3))))
+    for l1, l2, l3 in _triples():
+        c = cg.real_cg(l1, l2, l3)
+        lhs = np.einsum("abc,na,nb->nc", c, sh.sh_l(l1, n).numpy(), sh.sh_l(l2, n).numpy())
+        k = math.sqrt((2 * l1 + 1) * (2 * l2 + 1) / (2 * l3 + 1)) * abs(cg.complex_cg(l1, 0, l2, 0, l3, 0))
+        y3 = sh.sh_l(l3, n).numpy()
+        if k == 0.0:
+            assert np.abs(lhs).max() < 1e-12
+            continue
+        kappa = (lhs * y3).sum() / (y3 * y3).sum()
+        assert abs(abs(kappa) - k) < 1e-12, (l1, l2, l3)
+        assert np.abs(lhs - kappa * y3).max() < 1e-12
+
+
+# --------------------------------------------------------------------------- SH
+
+def test_sh_closed_forms():
+    r = torch.as_tensor(np.random.default_rng(3).normal(size=(30, 3)))
+    n = (r / r.norm(dim=1, keepdim=True)).numpy()
+    x, y, z = n.T
+    Y = sh.sh(2, r).numpy()
+    np.testing.assert_allclose(Y[:, 0], 1.0, atol=1e-15)
+    np.testing.assert_allclose(Y[:, 1:4], math.sqrt(3) * np.stack([y, z, x], 1), atol=1e-14)
+    s15 = math.sqrt(15)
+    y2 = np.stack([s15 * x * y, s15 * y * z, math.sqrt(5) / 2 * (3 * z * z - 1), s15 * x * z,
+                   s15 / 2 * (x * x - y * y)], 1)
+    np.testing.assert_allclose(Y[:, 4:9], y2, atol=1e-13)
+
+
+def test_sh_component_norm():
+    r = torch.as_tensor(np.random.default_rng(4).normal(size=(30, 3)))
+    Y = sh.sh(LMAX, r).numpy()
+    for l in range(LMAX + 1):
+        np.testing.assert_allclose((Y[:, l * l:(l + 1) ** 2] ** 2).sum(1), 2 * l + 1, rtol=1e-13)
+
+
+def test_sh_matches_scipy_through_basis_change():
+    from scipy.special import sph_harm_y
+    r = np.random.default_rng(5).normal(size=(30, 3))
+    n = r / np.linalg.norm(r, axis=1, keepdims=True)
+    theta, phi = np.arccos(n[:, 2]), np.arctan2(n[:, 1], n[:, 0])
+    Y = sh.sh(LMAX, torch.as_tensor(r)).numpy()
+    for l in range(LMAX + 1):
+        Yc = np.stack([sph_harm_y(l, m, theta, phi) for m in range(-l, l + 1)], -1)
+        Yr = math.sqrt(4 * math.pi) * Yc @ cg.complex_to_real(l).T
+        assert np.abs(Yr.imag).max() < 1e-13
+        np.testing.assert_allclose(Yr.real, Y[:, l * l:(l + 1) ** 2], atol=1e-12)
+
+
+def test_sh_rotation_matrices_are_orthogonal():
+    R = random_rotation(6)
+    for l in range(LMAX + 1):
+        D = wigner_from_sh(l, R)
+        np.testing.assert_allclose(D @ D.T, np.eye(2 * l + 1), atol=1e-10)
+    P = np.eye(3)[[1, 2, 0]]
+    np.testing.assert_allclose(wigner_from_sh(1, R), P @ R @ P.T, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- paths
+
+def _alt(muls):
+    return "+".join(f"{m}x{l}{'e' if l % 2 == 0 else 'o'}" for l, m in enumerate(muls))
+
+
+def _sh_str(lmax):
+    return _alt([1] * (lmax + 1))
+
+
+def test_path_counts_sobek_table1():
+    n = 0
+    for line in golden_lines("sobek_table1_nw.txt"):
+        prof, nw, gib = line.split()
+        ir = _alt([int(v) for v in prof.split("/")])
+        P = make_problem(ir, _sh_str(2), ir, "uvw")
+        assert P.n_weights == int(nw)
+        # Sobek section 2.5: M_W = b |E| N_w bytes for the materialised edge weights.
+        assert round(4 * 1.0e6 * P.n_weights / 2 ** 30, 1) == float(gib)
+        n += 1
+    assert n == 4
+
+
+def test_path_counts_sobek_table3():
+    n = 0
+    for line in golden_lines("sobek_table3_nw.txt"):
+        prof, nw = line.split()
+        muls = [int(v) for v in prof.split("/")]
+        ir = _alt(muls)
+        P = make_problem(ir, _sh_str(len(muls) - 1), ir, "uvw")
+        assert P.n_weights == int(nw), prof
+        n += 1
+    assert n == 16
+
+
+def test_path_selection_lunatp_table1():
+    # Count per output (l, parity) the input multiplicity of every admissible path (triangle rule and
+    # sigma_out = sigma_in sigma_sh of Sobek Eq. 5); the table lists outputs of the edge irreps' kinds.
+    n = 0
+    for line in golden_lines("lunatp_table1_irreps.txt"):
+        case, nodes, edges, outs = [t.strip() for t in line.split("|")]
+        bi, bs = parse(nodes), parse(edges)
+        lmax = max(b.l for b in bs)
+        targets = {(b.l, b.parity) for b in bs}   # the table's outputs keep the edge (l, parity) set
+        counts = {}
+        for a in bi:
+            for s in bs:
+                for l3 in range(abs(a.l - s.l), min(a.l + s.l, lmax) + 1):
+                    key = (l3, a.parity * s.parity)
+                    if key not in targets:
+                        continue
+                    counts[key] = counts.get(key, 0) + a.mul
+        got = "+".join(f"{counts[k]}x{k[0]}{'e' if k[1] > 0 else 'o'}"
+                       for k in sorted(counts, key=lambda t: (t[0], -t[1])))
+        assert got == outs, case
+        n += 1
+    assert n == 10
+
+
+def test_path_selection_matches_problem_for_lunatp_c2():
+    # The channelwise problem of the 1,024-atom workload (LunaTP C2 irreps) has 17 paths:
+    # 3 into 0e, 5 into 1o, 5 into 2e, 4 into 3o (384/640/640/512 channels in LunaTP's table).
+    P = make_problem(_alt([128] * 3), _sh_str(3), _alt([128] * 4), "uvu")
+    per_out = [sum(1 for p in P.paths if p.i_out == k) for k in range(4)]
+    assert per_out == [3, 5, 5, 4]
+    assert P.n_weights == 17 * 128
+
+
+# --------------------------------------------------------------------------- CSR
+
+def test_csr_matches_lexsort_and_inverts():
+    w = make_case(1).raw
+    perm, row_ptr, col = csr.receiver_csr(w.n_nodes, w.recv, w.send, w.image)
+    keys = (np.arange(len(w.recv)), w.image[:, 2], w.image[:, 1], w.image[:, 0], w.send, w.recv)
+    ref = np.lexsort(keys)
+    assert np.array_equal(perm, ref)
+    assert np.array_equal(np.diff(row_ptr), np.bincount(w.recv, minlength=w.n_nodes))
+    assert np.array_equal(col, w.send[ref])
+    sp, se = csr.source_csr(w.n_nodes, col)
+    sent = np.zeros(len(col), dtype=bool)
+    for j in range(w.n_nodes):
+        edges = se[sp[j]:sp[j + 1]]
+        assert np.all(np.diff(edges) > 0)
+        assert np.all(col[edges] == j)
+        sent[edges] = True
+    assert sent.all()
+
+
+# --------------------------------------------------------------------------- conv
+
+def _run(case, fn, **kw):
+    return fn(case.problem, case.x, case.edge_vec, case.recv, case.send, case.phi, case.A, **kw)
+
+
+def test_schedules_agree_fp64_config1():
+    c = make_case(1)
+    a = _run(c, conv.forward_conventional)
+    b = _run(c, conv.forward_streamed)
+    assert (a - b).abs().max().item() <= 1e-13 * a.abs().max().item()
+
+
+def test_schedules_agree_fp64_uvw_small():
+    c = make_case(1, irreps_override=dict(irreps_in="4x0e+3x1o+2x2e", irreps_out="3x0e+2x1o+4x2e", mode="uvw"))
+    a = _run(c, conv.forward_conventional)
+    b = _run(c, conv.forward_streamed)
+    assert (a - b).abs().max().item() <= 1e-13 * a.abs().max().item()
+
+
+@pytest.mark.parametrize("improper", [False, True])
+@pytest.mark.parametrize("mode", ["uvu", "uvw"])
+def test_equivariance_rotation_and_inversion(mode, improper):
+    ov = dict(irreps_in="3x0e+3x1o+3x2e+3x3o", irreps_out="3x0e+3x1o+3x2e+3x3o+3x1e", mode=mode,
+              irreps_sh=_sh_str(3))
+    c = make_case(1, irreps_override=ov)
+    R = random_rotation(11)
+    Rg = -R if improper else R
+    m = _run(c, conv.forward_conventional).numpy()
+    ev = (c.edge_vec.numpy() @ Rg.T)
+    xr = rotate_features(c.problem.irreps_in, c.x, R, improper)
+    mr = conv.forward_conventional(c.problem, xr, ev, c.recv, c.send, c.phi, c.A).numpy()
+    want = rotate_features(c.problem.irreps_out, m, R, improper)
+    np.testing.assert_allclose(mr, want, atol=1e-9 * np.abs(m).max())
+
+
+def test_linearity_and_relabelling():
+    c = make_case(1)
+    m = _run(c, conv.forward_conventional)
+    m2 = conv.forward_conventional(c.problem, 2.0 * c.x, c.edge_vec, c.recv, c.send, c.phi, -0.5 * c.A)
+    np.testing.assert_allclose(m2.numpy(), -m.numpy(), atol=1e-12)
+    m3 = conv.forward_conventional(c.problem, c.x, c.edge_vec, c.recv, c.send, 3.0 * c.phi, c.A)
+    np.testing.assert_allclose(m3.numpy(), 3.0 * m.numpy(), atol=1e-12)
+    g = np.random.default_rng(12).permutation(c.n_nodes)   # new label of node i is g[i]
+    inv = np.argsort(g)
+    mp = conv.forward_conventional(c.problem, c.x[inv], c.edge_vec, g[c.recv], g[c.send], c.phi, c.A)
+    np.testing.assert_allclose(mp.numpy(), m.numpy()[inv], atol=1e-12)
+
+
+def test_brute_force_scalar_graph():
+    # Scalars only: Y_0 = 1 and c(0,0,0) = 1, so m_i = sum_j (phi_ij A) * x_j.
+    P = make_problem("2x0e", "1x0e", "2x0e", "uvu")
+    pos = np.array([[0.0, 0.0, 0.0], [1.0, 0.2, 0.0], [0.1, 1.3, 0.4]])
+    recv = np.array([0, 0, 1, 2]); send = np.array([1, 2, 0, 1])
+    phi = np.array([[1.0, 2.0], [0.5, -1.0], [3.0, 0.0], [-2.0, 1.5]])
+    A = np.array([[0.3, -0.7], [1.1, 0.4]])
+    x = np.array([[1.0, 2.0], [-1.0, 0.5], [0.25, -3.0]])
+    ev = conv.edge_vectors(pos, np.zeros((4, 3)), recv, send)
+    m = conv.forward_conventional(P, x, ev, recv, send, phi, A).numpy()
+    want = np.zeros((3, 2))
+    for e in range(4):
+        for u in range(2):
+            want[recv[e], u] += (phi[e] @ A[:, u]) * x[send[e], u]
+    np.testing.assert_allclose(m, want, atol=1e-15)
+
+
+def test_backward_matches_finite_differences():
+    ov = dict(irreps_in="2x0e+2x1o+2x2e", irreps_out="2x0e+2x1o+2x2e", irreps_sh=_sh_str(2))
+    for mode in ("uvu", "uvw"):
+        ov["mode"] = mode
+        c = make_case(1, irreps_override=ov, n_nodes=12)
+        g = c.grad_out
+        b = conv.backward(c.problem, c.x, c.edge_vec, c.recv, c.send, c.phi, c.A, g)
+
+        def L(x=c.x, pos=c.pos, phi=c.phi, A=c.A):
+            ev = conv.edge_vectors(pos, c.shift, c.recv, c.send)
+            return float((conv.forward_conventional(c.problem, x, ev, c.recv, c.send, phi, A) * torch.as_tensor(g)).sum())
+
+        rng = np.random.default_rng(13)
+        h = 1e-6
+        for name, arr in (("x", c.x), ("pos", c.pos), ("phi", c.phi), ("A", c.A)):
+            for _ in range(4):
+                idx = tuple(int(rng.integers(s)) for s in arr.shape)
+                ap, am = arr.copy(), arr.copy()
+                ap[idx] += h
+                am[idx] -= h
+                fd = (L(**{name: ap}) - L(**{name: am})) / (2 * h)
+                got = float(b[name][idx])
+                assert abs(fd - got) <= 1e-6 * max(1.0, abs(got)), (mode, name, idx, fd, got)
+
+
+def test_backward_matches_autograd_config1():
+    c = make_case(1)
+    pos = torch.tensor(c.pos, requires_grad=True)
+    x = torch.tensor(c.x, requires_grad=True)
+    phi = torch.tensor(c.phi, requires_grad=True)
+    A = torch.tensor(c.A, requires_grad=True)
+    ev = conv.edge_vectors(pos, c.shift, c.recv, c.send)
+    m = conv.forward_conventional(c.problem, x, ev, c.recv, c.send, phi, A)
+    (m * torch.as_tensor(c.grad_out)).sum().backward()
+    b = conv.backward(c.problem, c.x, c.edge_vec, c.recv, c.send, c.phi, c.A, c.grad_out)
+    for k, ref in (("x", x.grad), ("pos", pos.grad), ("phi", phi.grad), ("A", A.grad)):
+        np.testing.assert_allclose(b[k].numpy(), ref.numpy(), atol=1e-12 * ref.abs().max().item())
+
+
+def test_sh_gradient_complex_step():
+    # J_Y^T v from autograd against complex-step derivatives of the analytic polynomial form.
+    r = np.random.default_rng(14).normal(size=(5, 3))
+    v = np.random.default_rng(15).normal(size=(5, (LMAX + 1) ** 2))
+    P = make_problem("1x0e", _sh_str(LMAX), "1x0e", "uvu")
+    got = conv._sh_vjp(P, r, torch.as_tensor(v)).numpy()
+    h = 1e-30
+    for d in range(3):
+        rc = r.astype(np.complex128)
+        rc[:, d] += 1j * h
+        dY = sh.sh(LMAX, torch.as_tensor(rc)).numpy().imag / h
+        np.testing.assert_allclose((dY * v).sum(1), got[:, d], rtol=1e-12, atol=1e-12)
