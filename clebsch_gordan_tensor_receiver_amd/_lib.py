@@ -1,0 +1,263 @@
+"""ctypes binding of ``libcgtp.so`` (argument marshalling only).
+
+Every computation runs in the library's HIP kernels; torch tensors are used only to own
+device memory and to name the current HIP stream.  If the library is missing or fails to
+load, every entry point raises: there is no CPU fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libcgtp.so")
+
+CHANNELWISE, FULLY_CONNECTED = 0, 1
+F32, F64 = 0, 1
+STREAMED, CONVENTIONAL = 0, 1
+OP_FORWARD, OP_BACKWARD, OP_DOUBLE_BACKWARD = 0, 1, 2
+
+EXPORTED = [
+    "cgtp_plan_create", "cgtp_plan_destroy", "cgtp_plan_info", "cgtp_plan_path", "cgtp_plan_cg_table",
+    "cgtp_plan_compile", "cgtp_plan_set_scratch_budget", "cgtp_graph_build", "cgtp_graph_export",
+    "cgtp_graph_dims", "cgtp_graph_upload", "cgtp_graph_destroy", "cgtp_workspace_size",
+    "cgtp_conv_forward", "cgtp_conv_backward", "cgtp_check_edges", "cgtp_error_string", "cgtp_last_error",
+]
+
+
+class CgtpError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"cgtp status {status}: {message}")
+        self.status = status
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in (
+        "n_paths", "n_weights", "c_in", "c_out", "sh_dim", "lmax_sh", "num_radial", "mode", "dtype",
+        "n_in_blocks", "n_out_blocks", "cg_nnz", "g_nnz")]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run clebsch_gordan_tensor_receiver_amd.build.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, Z, V = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+    ip = ctypes.POINTER(ctypes.c_int32)
+    sig = {
+        "cgtp_plan_create": [ctypes.c_char_p, ctypes.c_char_p, ctypes.c_char_p, I, I, I, ctypes.POINTER(P)],
+        "cgtp_plan_destroy": [P],
+        "cgtp_plan_info": [P, ctypes.POINTER(PlanInfo)],
+        "cgtp_plan_path": [P, I, ip],
+        "cgtp_plan_cg_table": [P, I, ip, ctypes.POINTER(ctypes.c_double), I, ctypes.POINTER(ctypes.c_int)],
+        "cgtp_plan_compile": [P, I],
+        "cgtp_plan_set_scratch_budget": [P, Z],
+        "cgtp_graph_build": [I, I, ip, ip, ip, ip, ctypes.POINTER(P)],
+        "cgtp_graph_export": [P, ip, ip, ip, ip],
+        "cgtp_graph_dims": [P, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)],
+        "cgtp_graph_upload": [P],
+        "cgtp_graph_destroy": [P],
+        "cgtp_workspace_size": [P, P, I, ctypes.POINTER(Z)],
+        "cgtp_conv_forward": [P, P, I, V, V, V, V, V, V, V, Z, V],
+        "cgtp_conv_backward": [P, P, V, V, V, V, V, V, V, V, V, V, V, V, Z, V],
+        "cgtp_check_edges": [P, P, V, V, V, Z, V, ctypes.POINTER(ctypes.c_int)],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    lib.cgtp_error_string.argtypes = [ctypes.c_int]
+    lib.cgtp_error_string.restype = ctypes.c_char_p
+    lib.cgtp_last_error.argtypes = []
+    lib.cgtp_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def check(status: int) -> None:
+    if status != 0:
+        lib = load()
+        raise CgtpError(status, f"{lib.cgtp_error_string(status).decode()}: {lib.cgtp_last_error().decode()}")
+
+
+def _i32(a: Optional[np.ndarray]):
+    if a is None:
+        return None, None
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _ptr(t) -> Optional[int]:
+    """Device address of a torch tensor (None stays NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+class Plan:
+    def __init__(self, irreps_in: str, irreps_sh: str, irreps_out: str, mode: str = "uvu",
+                 dtype: str = "float32", num_radial: int = 8):
+        lib = load()
+        h = ctypes.c_void_p()
+        m = {"uvu": CHANNELWISE, "uvw": FULLY_CONNECTED}[mode]
+        d = {"float32": F32, "float64": F64}[dtype]
+        check(lib.cgtp_plan_create(irreps_in.encode(), irreps_sh.encode(), irreps_out.encode(), m, d,
+                                   int(num_radial), ctypes.byref(h)))
+        self.handle = h
+        self.dtype = dtype
+        self.mode = mode
+        info = PlanInfo()
+        check(lib.cgtp_plan_info(h, ctypes.byref(info)))
+        self.info = {n: getattr(info, n) for n, _ in PlanInfo._fields_}
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and _lib is not None:
+            _lib.cgtp_plan_destroy(h)
+            self.handle = None
+
+    def path(self, k: int):
+        desc = np.zeros(9, dtype=np.int32)
+        check(load().cgtp_plan_path(self.handle, k, desc.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
+        return dict(zip(("i_in", "i_sh", "i_out", "l1", "l2", "l3", "weight_offset", "n_weights", "cg_nnz"),
+                        desc.tolist()))
+
+    def cg_table(self, k: int):
+        lib = load()
+        n = ctypes.c_int()
+        check(lib.cgtp_plan_cg_table(self.handle, k, None, None, 0, ctypes.byref(n)))
+        idx = np.zeros((n.value, 3), dtype=np.int32)
+        val = np.zeros(n.value, dtype=np.float64)
+        check(lib.cgtp_plan_cg_table(self.handle, k, idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                     val.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), n.value, ctypes.byref(n)))
+        return idx, val
+
+    def compile(self, ops=(OP_FORWARD,)) -> None:
+        mask = 0
+        for o in ops:
+            mask |= 1 << o
+        check(load().cgtp_plan_compile(self.handle, mask))
+
+    def set_scratch_budget(self, nbytes: int) -> None:
+        check(load().cgtp_plan_set_scratch_budget(self.handle, int(nbytes)))
+
+
+class Graph:
+    def __init__(self, n_nodes: int, recv, send, image=None):
+        lib = load()
+        recv, rp = _i32(recv)
+        send, sp = _i32(send)
+        image, ip = _i32(None if image is None else np.asarray(image).reshape(-1))
+        self.n_nodes = int(n_nodes)
+        self.n_edges = int(len(recv))
+        self.perm = np.zeros(self.n_edges, dtype=np.int32)
+        h = ctypes.c_void_p()
+        check(lib.cgtp_graph_build(self.n_nodes, self.n_edges, rp, sp, ip,
+                                   self.perm.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), ctypes.byref(h)))
+        self.handle = h
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and _lib is not None:
+            _lib.cgtp_graph_destroy(h)
+            self.handle = None
+
+    def export(self):
+        n, e = self.n_nodes, self.n_edges
+        rp = np.zeros(n + 1, np.int32)
+        col = np.zeros(max(e, 1), np.int32)
+        sp = np.zeros(n + 1, np.int32)
+        se = np.zeros(max(e, 1), np.int32)
+        P = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))  # noqa: E731
+        check(load().cgtp_graph_export(self.handle, P(rp), P(col), P(sp), P(se)))
+        return rp, col[:e], sp, se[:e]
+
+    def upload(self) -> None:
+        check(load().cgtp_graph_upload(self.handle))
+
+
+def workspace_size(plan: Plan, graph: Graph, op: int) -> int:
+    n = ctypes.c_size_t()
+    check(load().cgtp_workspace_size(plan.handle, graph.handle, op, ctypes.byref(n)))
+    return int(n.value)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return int(stream)
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def conv_forward(plan: Plan, graph: Graph, schedule: int, x, pos, shift, phi, A, out, workspace, stream=None):
+    check(load().cgtp_conv_forward(plan.handle, graph.handle, schedule, _ptr(x), _ptr(pos), _ptr(shift), _ptr(phi),
+                                   _ptr(A), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)))
+
+
+def conv_backward(plan: Plan, graph: Graph, x, pos, shift, phi, A, grad_out, grad_x=None, grad_pos=None,
+                  grad_edge_vec=None, grad_phi=None, grad_A=None, workspace=None, stream=None):
+    check(load().cgtp_conv_backward(plan.handle, graph.handle, _ptr(x), _ptr(pos), _ptr(shift), _ptr(phi), _ptr(A),
+                                    _ptr(grad_out), _ptr(grad_x), _ptr(grad_pos), _ptr(grad_edge_vec),
+                                    _ptr(grad_phi), _ptr(grad_A), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+class Convolution:
+    """A plan, a graph and a workspace bound together, called with torch device tensors.
+
+    Per-edge inputs (shift, phi) must already be in the graph's receiver-sorted order
+    (``graph.perm`` maps sorted positions to the caller's edge indices).
+    """
+
+    def __init__(self, plan: Plan, graph: Graph):
+        import torch
+        self.plan, self.graph = plan, graph
+        self.torch_dtype = torch.float64 if plan.dtype == "float64" else torch.float32
+        self._ws = {}
+
+    def workspace(self, op: int):
+        import torch
+        n = workspace_size(self.plan, self.graph, op)
+        ws = self._ws.get(op)
+        if ws is None or ws.numel() < n:
+            ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+            self._ws[op] = ws
+        return ws
+
+    def forward(self, x, pos, shift, phi, A, schedule: int = CONVENTIONAL, out=None):
+        import torch
+        if out is None:
+            out = torch.empty((self.graph.n_nodes, self.plan.info["c_out"]), dtype=self.torch_dtype, device="cuda")
+        conv_forward(self.plan, self.graph, schedule, x, pos, shift, phi, A, out, self.workspace(OP_FORWARD))
+        return out
+
+    def backward(self, x, pos, shift, phi, A, grad_out, want=("x", "pos", "edge_vec", "phi", "A")):
+        import torch
+        n, e = self.graph.n_nodes, self.graph.n_edges
+        info = self.plan.info
+        dt = dict(dtype=self.torch_dtype, device="cuda")
+        outs = dict(
+            x=torch.empty((n, info["c_in"]), **dt) if "x" in want else None,
+            pos=torch.empty((n, 3), **dt) if "pos" in want else None,
+            edge_vec=torch.empty((max(e, 1), 3), **dt) if "edge_vec" in want else None,
+            phi=torch.empty((max(e, 1), info["num_radial"]), **dt) if "phi" in want else None,
+            A=torch.empty((info["num_radial"], info["n_weights"]), **dt) if "A" in want else None,
+        )
+        conv_backward(self.plan, self.graph, x, pos, shift, phi, A, grad_out, grad_x=outs["x"], grad_pos=outs["pos"],
+                      grad_edge_vec=outs["edge_vec"], grad_phi=outs["phi"], grad_A=outs["A"],
+                      workspace=self.workspace(OP_BACKWARD))
+        return {k: v for k, v in outs.items() if v is not None}

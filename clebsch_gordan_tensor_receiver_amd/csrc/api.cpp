@@ -1,0 +1,284 @@
+// The extern "C" surface declared in include/cgtp.h.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "cgtp.h"
+#include "graph.hpp"
+#include "kernels.hpp"
+#include "plan.hpp"
+
+struct cgtp_plan_s {
+  cgtp::Plan p;
+};
+struct cgtp_graph_s {
+  cgtp::Graph g;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+cgtp_status_t fail(cgtp_status_t st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+cgtp_status_t ok() {
+  g_last_error.clear();
+  return CGTP_OK;
+}
+
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+// Edges of G rows that fit in the scratch budget (at least the largest in-degree).
+long long g_chunk_edges(const cgtp::Plan& p, const cgtp::Graph& g) {
+  long long row = (long long)p.g_stride * (long long)p.elem();
+  long long cap = std::max<long long>(1, (long long)(p.scratch_budget / size_t(row)));
+  return std::max<long long>(cap, g.max_in_degree);
+}
+
+long long max_chunk_edges(const cgtp::Graph& g, const std::vector<std::pair<int, int>>& ch) {
+  long long m = 0;
+  for (auto& c : ch) m = std::max<long long>(m, g.row_ptr[c.second] - g.row_ptr[c.first]);
+  return m;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* cgtp_error_string(cgtp_status_t s) {
+  switch (s) {
+    case CGTP_OK: return "ok";
+    case CGTP_ERR_INVALID_ARG: return "invalid argument";
+    case CGTP_ERR_UNSUPPORTED: return "unsupported";
+    case CGTP_ERR_WORKSPACE: return "workspace too small";
+    case CGTP_ERR_DEGENERATE_EDGE: return "zero-length edge";
+    case CGTP_ERR_HIP: return "HIP runtime error";
+    case CGTP_ERR_COMPILE: return "kernel compilation failed";
+  }
+  return "unknown status";
+}
+
+const char* cgtp_last_error(void) { return g_last_error.c_str(); }
+
+cgtp_status_t cgtp_plan_create(const char* irreps_in, const char* irreps_sh, const char* irreps_out, cgtp_mode_t mode,
+                               cgtp_dtype_t dtype, int num_radial, cgtp_plan_t* out) {
+  if (!out) return fail(CGTP_ERR_INVALID_ARG, "out is null");
+  *out = nullptr;
+  cgtp_plan_s* h = new (std::nothrow) cgtp_plan_s();
+  if (!h) return fail(CGTP_ERR_INVALID_ARG, "out of host memory");
+  std::string err;
+  cgtp_status_t st = cgtp::build_plan(irreps_in, irreps_sh, irreps_out, mode, dtype, num_radial, &h->p, &err);
+  if (st != CGTP_OK) {
+    delete h;
+    return fail(st, err);
+  }
+  *out = h;
+  return ok();
+}
+
+cgtp_status_t cgtp_plan_destroy(cgtp_plan_t plan) {
+  delete plan;
+  return ok();
+}
+
+cgtp_status_t cgtp_plan_info(cgtp_plan_t plan, cgtp_plan_info_t* out) {
+  if (!plan || !out) return fail(CGTP_ERR_INVALID_ARG, "null argument");
+  const cgtp::Plan& p = plan->p;
+  out->n_paths = int(p.paths.size());
+  out->n_weights = p.n_w;
+  out->c_in = p.c_in;
+  out->c_out = p.c_out;
+  out->sh_dim = p.sh_dim;
+  out->lmax_sh = p.lmax;
+  out->num_radial = p.K;
+  out->mode = int(p.mode);
+  out->dtype = int(p.dtype);
+  out->n_in_blocks = int(p.in.size());
+  out->n_out_blocks = int(p.out.size());
+  out->cg_nnz = p.cg_nnz;
+  out->g_nnz = p.g_width;
+  return ok();
+}
+
+cgtp_status_t cgtp_plan_path(cgtp_plan_t plan, int path, int32_t* desc) {
+  if (!plan || !desc) return fail(CGTP_ERR_INVALID_ARG, "null argument");
+  if (path < 0 || path >= int(plan->p.paths.size())) return fail(CGTP_ERR_INVALID_ARG, "path out of range");
+  const cgtp::Path& P = plan->p.paths[path];
+  int32_t v[9] = {P.i_in, P.i_sh, P.i_out, P.l1, P.l2, P.l3, P.w_off, P.n_w, int32_t(P.terms.size())};
+  std::memcpy(desc, v, sizeof v);
+  return ok();
+}
+
+cgtp_status_t cgtp_plan_cg_table(cgtp_plan_t plan, int path, int32_t* m123, double* val, int capacity, int* nnz) {
+  if (!plan || !nnz) return fail(CGTP_ERR_INVALID_ARG, "null argument");
+  if (path < 0 || path >= int(plan->p.paths.size())) return fail(CGTP_ERR_INVALID_ARG, "path out of range");
+  const cgtp::Path& P = plan->p.paths[path];
+  *nnz = int(P.terms.size());
+  for (int k = 0; k < std::min(capacity, *nnz); ++k) {
+    if (m123) {
+      m123[3 * k] = P.terms[k].m1;
+      m123[3 * k + 1] = P.terms[k].m2;
+      m123[3 * k + 2] = P.terms[k].m3;
+    }
+    if (val) val[k] = P.terms[k].c;
+  }
+  return ok();
+}
+
+cgtp_status_t cgtp_plan_set_scratch_budget(cgtp_plan_t plan, size_t bytes) {
+  if (!plan || bytes < 4096) return fail(CGTP_ERR_INVALID_ARG, "budget must be at least 4096 bytes");
+  plan->p.scratch_budget = bytes;
+  return ok();
+}
+
+cgtp_status_t cgtp_plan_compile(cgtp_plan_t plan, int ops) {
+  if (!plan) return fail(CGTP_ERR_INVALID_ARG, "null plan");
+  std::string err;
+  std::vector<std::string> fams;
+  if (plan->p.mode == CGTP_CHANNELWISE) {
+    if (ops & (1 << CGTP_OP_FORWARD)) {
+      fams.push_back("fwd");
+      fams.push_back("fwds");
+    }
+  }
+  for (auto& f : fams) {
+    cgtp_status_t st = cgtp::compile_family(plan->p, f, &err);
+    if (st != CGTP_OK) return fail(st, err);
+  }
+  return ok();
+}
+
+cgtp_status_t cgtp_graph_build(int n_nodes, int n_edges, const int32_t* recv, const int32_t* send,
+                               const int32_t* image, int32_t* perm_out, cgtp_graph_t* out) {
+  if (!out) return fail(CGTP_ERR_INVALID_ARG, "out is null");
+  *out = nullptr;
+  cgtp_graph_s* h = new (std::nothrow) cgtp_graph_s();
+  if (!h) return fail(CGTP_ERR_INVALID_ARG, "out of host memory");
+  std::string err;
+  cgtp_status_t st = cgtp::build_graph(n_nodes, n_edges, recv, send, image, &h->g, &err);
+  if (st != CGTP_OK) {
+    delete h;
+    return fail(st, err);
+  }
+  if (perm_out && n_edges > 0) std::memcpy(perm_out, h->g.perm.data(), sizeof(int32_t) * size_t(n_edges));
+  *out = h;
+  return ok();
+}
+
+cgtp_status_t cgtp_graph_export(cgtp_graph_t g, int32_t* row_ptr, int32_t* col, int32_t* src_ptr, int32_t* src_edge) {
+  if (!g) return fail(CGTP_ERR_INVALID_ARG, "null graph");
+  const cgtp::Graph& G = g->g;
+  if (row_ptr) std::memcpy(row_ptr, G.row_ptr.data(), sizeof(int32_t) * G.row_ptr.size());
+  if (src_ptr) std::memcpy(src_ptr, G.src_ptr.data(), sizeof(int32_t) * G.src_ptr.size());
+  if (col && G.e) std::memcpy(col, G.col.data(), sizeof(int32_t) * G.col.size());
+  if (src_edge && G.e) std::memcpy(src_edge, G.src_edge.data(), sizeof(int32_t) * G.src_edge.size());
+  return ok();
+}
+
+cgtp_status_t cgtp_graph_dims(cgtp_graph_t g, int* n_nodes, int* n_edges) {
+  if (!g) return fail(CGTP_ERR_INVALID_ARG, "null graph");
+  if (n_nodes) *n_nodes = g->g.n;
+  if (n_edges) *n_edges = g->g.e;
+  return ok();
+}
+
+cgtp_status_t cgtp_graph_upload(cgtp_graph_t g) {
+  if (!g) return fail(CGTP_ERR_INVALID_ARG, "null graph");
+  cgtp::DeviceGraph d;
+  std::string err;
+  cgtp_status_t st = cgtp::device_graph(g->g, &d, &err);
+  return st == CGTP_OK ? ok() : fail(st, err);
+}
+
+cgtp_status_t cgtp_graph_destroy(cgtp_graph_t g) {
+  if (!g) return ok();
+  for (auto& kv : g->g.dev) {
+    int cur = 0;
+    hipGetDevice(&cur);
+    hipSetDevice(kv.first);
+    hipFree(kv.second.base);
+    hipSetDevice(cur);
+  }
+  delete g;
+  return ok();
+}
+
+cgtp_status_t cgtp_workspace_size(cgtp_plan_t plan, cgtp_graph_t g, cgtp_op_t op, size_t* bytes) {
+  if (!plan || !g || !bytes) return fail(CGTP_ERR_INVALID_ARG, "null argument");
+  const cgtp::Plan& p = plan->p;
+  const cgtp::Graph& G = g->g;
+  auto ch = G.chunks(g_chunk_edges(p, G));
+  size_t e_max = size_t(max_chunk_edges(G, ch));
+  size_t need = align256(e_max * size_t(p.g_stride) * p.elem());
+  (void)op;
+  *bytes = std::max<size_t>(need, 256);
+  return ok();
+}
+
+cgtp_status_t cgtp_conv_forward(cgtp_plan_t plan, cgtp_graph_t g, cgtp_schedule_t schedule, const void* x,
+                                const void* pos, const void* shift, const void* phi, const void* A, void* out,
+                                void* workspace, size_t ws_bytes, void* stream) {
+  if (!plan || !g) return fail(CGTP_ERR_INVALID_ARG, "null plan or graph");
+  if (!x || !pos || !phi || !A || !out) return fail(CGTP_ERR_INVALID_ARG, "null tensor argument");
+  if (schedule != CGTP_STREAMED && schedule != CGTP_CONVENTIONAL) return fail(CGTP_ERR_INVALID_ARG, "bad schedule");
+  cgtp::Plan& p = plan->p;
+  cgtp::Graph& G = g->g;
+  if (p.mode != CGTP_CHANNELWISE) return fail(CGTP_ERR_UNSUPPORTED, "fully connected forward not built yet");
+  size_t need = 0;
+  cgtp_workspace_size(plan, g, CGTP_OP_FORWARD, &need);
+  if (ws_bytes < need || (!workspace && need > 0)) return fail(CGTP_ERR_WORKSPACE, "workspace too small");
+  std::string err;
+  cgtp::DeviceGraph d;
+  cgtp_status_t st = cgtp::device_graph(G, &d, &err);
+  if (st != CGTP_OK) return fail(st, err);
+  const char* fam = schedule == CGTP_STREAMED ? "fwds" : "fwd";
+  hipFunction_t kprep, kfwd;
+  if ((st = cgtp::get_kernel(p, fam, "cgtp_prep", &kprep, &err)) != CGTP_OK) return fail(st, err);
+  if ((st = cgtp::get_kernel(p, fam, schedule == CGTP_STREAMED ? "cgtp_fwd_streamed" : "cgtp_fwd", &kfwd, &err)) !=
+      CGTP_OK)
+    return fail(st, err);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto tasks = cgtp::forward_tasks(p);
+  int ntask = int(tasks.size());
+  void* G_ws = workspace;
+  for (auto& c : G.chunks(g_chunk_edges(p, G))) {
+    int i0 = c.first, nrec = c.second - c.first;
+    int e0 = G.row_ptr[c.first], e1 = G.row_ptr[c.second];
+    if (e1 > e0) {
+      void* a[] = {(void*)&pos, (void*)&shift, (void*)&d.recv, (void*)&d.col, &e0, &e1, &G_ws};
+      if ((st = cgtp::launch(kprep, unsigned((e1 - e0 + 255) / 256), 256, 0, s, a, &err)) != CGTP_OK)
+        return fail(st, err);
+    }
+    int per = (nrec + 7) / 8;
+    void* b[] = {(void*)&x, (void*)&phi, (void*)&A, &G_ws, (void*)&d.row_ptr, (void*)&d.col, &out, &i0, &nrec, &per, &e0};
+    if ((st = cgtp::launch(kfwd, unsigned(8 * ntask * per), 64, 0, s, b, &err)) != CGTP_OK) return fail(st, err);
+  }
+  return ok();
+}
+
+}  // extern "C"
+
+extern "C" {
+
+cgtp_status_t cgtp_conv_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x, const void* pos, const void* shift,
+                                 const void* phi, const void* A, const void* grad_out, void* grad_x, void* grad_pos,
+                                 void* grad_edge_vec, void* grad_phi, void* grad_A, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+  (void)plan; (void)g; (void)x; (void)pos; (void)shift; (void)phi; (void)A; (void)grad_out; (void)grad_x;
+  (void)grad_pos; (void)grad_edge_vec; (void)grad_phi; (void)grad_A; (void)workspace; (void)ws_bytes; (void)stream;
+  return fail(CGTP_ERR_UNSUPPORTED, "backward not built yet");
+}
+
+cgtp_status_t cgtp_check_edges(cgtp_plan_t plan, cgtp_graph_t g, const void* pos, const void* shift, void* workspace,
+                               size_t ws_bytes, void* stream, int* first_bad) {
+  (void)plan; (void)g; (void)pos; (void)shift; (void)workspace; (void)ws_bytes; (void)stream; (void)first_bad;
+  return fail(CGTP_ERR_UNSUPPORTED, "edge check not built yet");
+}
+
+}  // extern "C"

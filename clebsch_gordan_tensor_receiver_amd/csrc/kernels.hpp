@@ -1,0 +1,52 @@
+// Generated gfx950 kernels: source generation (codegen.cpp) and run-time compilation,
+// caching and launching (runtime.cpp).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <map>
+#include <memory>
+#include <string>
+#include <vector>
+
+#include "cgtp.h"
+
+namespace cgtp {
+
+struct Plan;
+
+// One generated translation unit ("family"): forward, streamed forward, backward, ...
+struct Module {
+  std::vector<char> code;                       // gfx950 code object
+  std::map<int, hipModule_t> loaded;            // per device
+  std::map<std::pair<int, std::string>, hipFunction_t> fns;
+};
+
+struct KernelSet {
+  std::map<std::string, Module> families;
+  ~KernelSet();
+};
+
+std::unique_ptr<KernelSet> make_kernel_set();
+
+// Kernel source of one family for a plan (deterministic text).
+std::string generate_source(const Plan& p, const std::string& family, std::string* err);
+
+// Work decomposition shared by the generator and the launcher.
+struct Task {
+  int group;   // output block (forward, receiver backward) or input block (source backward)
+  int cb;      // 64-channel block
+};
+std::vector<Task> forward_tasks(const Plan& p);
+std::vector<Task> source_tasks(const Plan& p);
+
+// Compile (once) and fetch a kernel of a family on the current device.
+cgtp_status_t get_kernel(Plan& p, const std::string& family, const std::string& name, hipFunction_t* f,
+                         std::string* err);
+cgtp_status_t compile_family(Plan& p, const std::string& family, std::string* err);
+
+// Launch helper: args is an array of pointers to the kernel arguments.
+cgtp_status_t launch(hipFunction_t f, unsigned grid, unsigned block, unsigned shmem, hipStream_t s,
+                     void** args, std::string* err);
+
+}  // namespace cgtp

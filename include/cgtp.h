@@ -1,0 +1,177 @@
+/*
+ * cgtp.h - C ABI of the MI355X (gfx950) Clebsch-Gordan tensor-product convolution.
+ *
+ * The operator (Sobek: Streaming Equivariant Tensor Product Convolutions, section 2.4,
+ * Eqs. 7 and 11-12; LunaTP: Enabling Efficient and Scalable Tensor Product for
+ * Equivariant MLIPs, section 2.1 Eq. 1 and section 2.2 Algorithm 1):
+ *
+ *   for every edge i <- j with vector r_ij = pos[j] - pos[i] + shift_ij,
+ *   m_i = sum_j sum_paths sum_a W_ij,pi,a T_pi,a(x_j, Y(r_ij / |r_ij|)),
+ *   W_ij,pi,a = sum_q phi_ij,q A_q,pi,a,
+ *
+ * where T_pi couples input block l1 of x_j with spherical-harmonic degree l2 into output
+ * degree l3 through real Clebsch-Gordan coefficients.  Two schedules give the same result
+ * up to rounding order (Sobek section 3.1, Eqs. 15-16): the conventional one forms the
+ * per-edge weights w (in registers, never as an edge-sized tensor), the streamed one
+ * accumulates the receiver state S_i = sum_j phi_ij (x) CG(x_j, Y_ij) and applies m = S A
+ * (Sobek section 4.2, Eqs. 32-35).
+ *
+ * Conventions fixed by this library (the pages leave them open):
+ *  - Irreps strings are "MULxLp" tokens joined by '+', p in {e, o}, e.g. "128x0e+128x1o".
+ *    The spherical-harmonic irreps must be "1x0e+1x1o+...+1xLp" with parity (-1)^l.
+ *  - Features use the ir_mul layout (Sobek section 4.5): block b of multiplicity C and
+ *    degree l occupies C*(2l+1) consecutive values, component m (0..2l) major, channel minor.
+ *    A node row holds its blocks back to back: x is N x C_in, out is N x C_out, row-major.
+ *  - Real spherical harmonics of the unit edge direction, component normalised
+ *    (sum_m Y_lm^2 = 2l+1), real combination of the Condon-Shortley complex harmonics,
+ *    m = -l..l, so Y_1 = sqrt(3) (y, z, x).
+ *  - Real Clebsch-Gordan tensors: unitary, first non-zero entry of each (l1,l2,l3) tensor in
+ *    row-major (m1,m2,m3) order positive; no further path normalisation.
+ *  - Paths are enumerated over (input block, SH block, output block) in lexicographic order;
+ *    a path needs |l1-l2| <= l3 <= l1+l2 and parity_in * parity_sh == parity_out
+ *    (Sobek section 2.2, Eq. 5); channelwise mode also needs mul_in == mul_out.  Paths into
+ *    the same output block are summed.
+ *  - A is K x N_w row-major.  Columns are path-major; within a path, channel u (channelwise,
+ *    n_pi = C) or the pair (u, w) with u major (fully connected, n_pi = C_in C_out)
+ *    (Sobek section 2.4, Eqs. 8-9 and 12).
+ *  - Edges: the graph handle sorts the caller's edge list into receiver-major CSR order
+ *    (LunaTP section 4.1).  Every per-edge array passed to a convolution call (shift, phi,
+ *    grad_edge_vec, ...) is in that receiver-sorted order.
+ *
+ * Memory and calls: handles are opaque and owned by the library; every tensor argument is a
+ * caller-owned device pointer in the plan's dtype (float or double) unless stated.  Calls
+ * run asynchronously on the caller's HIP stream (`stream` is a hipStream_t, NULL = default
+ * stream).  Outputs are overwritten, not accumulated.  The caller supplies a device
+ * workspace of at least cgtp_workspace_size() bytes; the convolution calls never allocate
+ * device memory except for the one-off upload of a graph to a device (see
+ * cgtp_graph_upload).  Errors are returned as status codes; nothing is thrown across the
+ * ABI.  cgtp_last_error() gives a readable message for the calling thread.
+ */
+#ifndef CGTP_H
+#define CGTP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct cgtp_plan_s* cgtp_plan_t;
+typedef struct cgtp_graph_s* cgtp_graph_t;
+
+typedef enum { CGTP_CHANNELWISE = 0, CGTP_FULLY_CONNECTED = 1 } cgtp_mode_t;
+typedef enum { CGTP_F32 = 0, CGTP_F64 = 1 } cgtp_dtype_t;
+typedef enum { CGTP_STREAMED = 0, CGTP_CONVENTIONAL = 1 } cgtp_schedule_t;
+typedef enum { CGTP_OP_FORWARD = 0, CGTP_OP_BACKWARD = 1, CGTP_OP_DOUBLE_BACKWARD = 2 } cgtp_op_t;
+
+typedef enum {
+  CGTP_OK = 0,
+  CGTP_ERR_INVALID_ARG = 1,    /* malformed irreps, bad sizes, null required pointer, bad CSR */
+  CGTP_ERR_UNSUPPORTED = 2,    /* valid request this build does not implement (see message)  */
+  CGTP_ERR_WORKSPACE = 3,      /* workspace smaller than cgtp_workspace_size()                */
+  CGTP_ERR_DEGENERATE_EDGE = 4,/* an edge of zero length was found by cgtp_check_edges        */
+  CGTP_ERR_HIP = 5,            /* a HIP runtime call failed (message names it)                */
+  CGTP_ERR_COMPILE = 6         /* run-time kernel compilation failed (message holds the log)  */
+} cgtp_status_t;
+
+typedef struct {
+  int n_paths;       /* P, number of CG paths                                   */
+  int n_weights;     /* N_w, columns of A                                       */
+  int c_in;          /* C_in, values per node of x                              */
+  int c_out;         /* C_out, values per node of out                           */
+  int sh_dim;        /* (L+1)^2, spherical-harmonic components                  */
+  int lmax_sh;       /* L                                                       */
+  int num_radial;    /* K, rows of A and columns of phi                         */
+  int mode;          /* cgtp_mode_t                                             */
+  int dtype;         /* cgtp_dtype_t                                            */
+  int n_in_blocks, n_out_blocks;
+  int cg_nnz;        /* non-zero real CG coefficients summed over paths         */
+  int g_nnz;         /* structural (m1, m3) pairs summed over paths: per-edge folded
+                        coefficients G_pi[m1,m3] = sum_m2 c[m1,m2,m3] Y[m2]       */
+} cgtp_plan_info_t;
+
+/* ---------------------------------------------------------------- plans (host only) */
+
+/* Build a plan: parse irreps, enumerate paths, compute the real CG tables.
+ * Host only, no device needed.  Kernels are generated and compiled for gfx950 the first time
+ * an operation needs them (or by cgtp_plan_compile).  Returns INVALID_ARG for malformed or
+ * inconsistent irreps or num_radial < 1, UNSUPPORTED for degrees above 6 or no paths. */
+cgtp_status_t cgtp_plan_create(const char* irreps_in, const char* irreps_sh, const char* irreps_out,
+                               cgtp_mode_t mode, cgtp_dtype_t dtype, int num_radial, cgtp_plan_t* out);
+cgtp_status_t cgtp_plan_destroy(cgtp_plan_t plan);
+cgtp_status_t cgtp_plan_info(cgtp_plan_t plan, cgtp_plan_info_t* out);
+
+/* Path descriptor: desc[0..8] = i_in, i_sh, i_out, l1, l2, l3, weight_offset, n_weights, cg_nnz. */
+cgtp_status_t cgtp_plan_path(cgtp_plan_t plan, int path, int32_t* desc);
+
+/* Sparse CG table of one path: up to `capacity` entries (m1, m2, m3) -> m123[3k..3k+2],
+ * value -> val[k], indices 0..2l, row-major order; *nnz receives the full count. */
+cgtp_status_t cgtp_plan_cg_table(cgtp_plan_t plan, int path, int32_t* m123, double* val,
+                                 int capacity, int* nnz);
+
+/* Generate and compile every kernel of `ops` (bit mask of 1 << cgtp_op_t) now.  Host only. */
+cgtp_status_t cgtp_plan_compile(cgtp_plan_t plan, int ops);
+
+/* Scratch budget in bytes for the per-edge folded coefficients and partial sums
+ * (default 256 MiB, the size of the MI355X Infinity Cache).  Larger graphs are processed in
+ * receiver chunks that fit it (Sobek Appendix B.2 bounds its scratch the same way). */
+cgtp_status_t cgtp_plan_set_scratch_budget(cgtp_plan_t plan, size_t bytes);
+
+/* ---------------------------------------------------------------- graphs */
+
+/* Sort an edge list into receiver CSR order and build the source CSR (host only, exact).
+ * Edge k is (recv[k] <- send[k]); image (E x 3 int32, may be NULL) holds the periodic image
+ * index, used only to break ties.  Order: (recv, send, image_x, image_y, image_z, k) ascending.
+ * perm_out (E int32, may be NULL) receives, for each sorted position, the caller's edge index.
+ * INVALID_ARG for n_nodes < 1, n_edges < 0 or an index outside [0, n_nodes). */
+cgtp_status_t cgtp_graph_build(int n_nodes, int n_edges, const int32_t* recv, const int32_t* send,
+                               const int32_t* image, int32_t* perm_out, cgtp_graph_t* out);
+
+/* Copy the CSR arrays to host memory: row_ptr[N+1], col[E] (sender of each sorted edge),
+ * src_ptr[N+1], src_edge[E] (sorted edge positions grouped by sender, ascending). Any may be NULL. */
+cgtp_status_t cgtp_graph_export(cgtp_graph_t g, int32_t* row_ptr, int32_t* col, int32_t* src_ptr,
+                                int32_t* src_edge);
+cgtp_status_t cgtp_graph_dims(cgtp_graph_t g, int* n_nodes, int* n_edges);
+
+/* Upload the CSR to the current device (once per device; later calls return at once).
+ * The convolution calls do it themselves on first use; call it before a timed region. */
+cgtp_status_t cgtp_graph_upload(cgtp_graph_t g);
+cgtp_status_t cgtp_graph_destroy(cgtp_graph_t g);
+
+/* ---------------------------------------------------------------- convolution (device) */
+
+/* Workspace bytes needed by `op` for this plan and graph (bounded by the scratch budget plus
+ * O(N + parameter) terms; never O(E x N_w)). */
+cgtp_status_t cgtp_workspace_size(cgtp_plan_t plan, cgtp_graph_t g, cgtp_op_t op, size_t* bytes);
+
+/* Forward.  x: N x C_in; pos: N x 3; shift: E x 3 receiver-sorted image shifts added to
+ * pos[send] - pos[recv] (NULL = no shift); phi: E x K receiver-sorted; A: K x N_w;
+ * out: N x C_out (overwritten). */
+cgtp_status_t cgtp_conv_forward(cgtp_plan_t plan, cgtp_graph_t g, cgtp_schedule_t schedule,
+                                const void* x, const void* pos, const void* shift, const void* phi,
+                                const void* A, void* out, void* workspace, size_t ws_bytes, void* stream);
+
+/* Backward of the forward map for the output cotangent grad_out (N x C_out) (Sobek section
+ * 3.2, Eqs. 18-22).  Outputs, each overwritten and each optional (NULL = not requested):
+ * grad_x (N x C_in), grad_pos (N x 3), grad_edge_vec (E x 3, gradient with respect to the
+ * edge vectors r_ij), grad_phi (E x K), grad_A (K x N_w).  grad_pos = sum over out-edges of
+ * grad_edge_vec minus sum over in-edges.  Reductions run in a fixed order: two identical
+ * calls give bitwise identical results. */
+cgtp_status_t cgtp_conv_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x, const void* pos,
+                                 const void* shift, const void* phi, const void* A, const void* grad_out,
+                                 void* grad_x, void* grad_pos, void* grad_edge_vec, void* grad_phi,
+                                 void* grad_A, void* workspace, size_t ws_bytes, void* stream);
+
+/* Check on the device that no edge has zero length.  Synchronises `stream`.  Returns
+ * DEGENERATE_EDGE (and the first offending sorted edge in *first_bad, else -1). */
+cgtp_status_t cgtp_check_edges(cgtp_plan_t plan, cgtp_graph_t g, const void* pos, const void* shift,
+                               void* workspace, size_t ws_bytes, void* stream, int* first_bad);
+
+const char* cgtp_error_string(cgtp_status_t status);
+const char* cgtp_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CGTP_H */
