@@ -47,6 +47,52 @@ long long max_chunk_edges(const cgtp::Graph& g, const std::vector<std::pair<int,
   return m;
 }
 
+constexpr int kMaxSlots = 256;  // A-bar partial slots per chunk (waves of one task)
+
+// Workspace plan of a backward call.
+struct BwdLayout {
+  long long cap = 0;            // edges per receiver chunk
+  std::vector<std::pair<int, int>> chunks;
+  int ntask_r = 0, ntask_s = 0, V = 0, row = 0;
+  int nslot = 0;                // A-bar partial slots (max over chunks)
+  size_t g_off = 0, ep_off = 0, ap_off = 0, gev_off = 0, total = 0;
+};
+
+void chunk_geometry(int nrec, int* per, int* rpw, int* nch) {
+  *per = (nrec + 7) / 8;
+  *rpw = std::max(1, (nrec + kMaxSlots - 1) / kMaxSlots);
+  *nch = (*per + *rpw - 1) / *rpw;
+}
+
+BwdLayout bwd_layout(const cgtp::Plan& p, const cgtp::Graph& g) {
+  BwdLayout L;
+  L.ntask_r = int(cgtp::recv_backward_tasks(p).size());
+  L.ntask_s = int(cgtp::source_tasks(p).size());
+  L.V = cgtp::edge_partial_width(p);
+  L.row = L.ntask_r * L.V;
+  long long row_bytes = (long long)(p.g_stride + L.row) * (long long)p.elem();
+  L.cap = std::max<long long>(std::max<long long>(1, (long long)(p.scratch_budget / size_t(row_bytes))),
+                              g.max_in_degree);
+  L.chunks = g.chunks(L.cap);
+  long long emax = max_chunk_edges(g, L.chunks);
+  for (auto& c : L.chunks) {
+    int per, rpw, nch;
+    chunk_geometry(c.second - c.first, &per, &rpw, &nch);
+    L.nslot = std::max(L.nslot, 8 * nch);
+  }
+  size_t off = 0;
+  L.g_off = off;
+  off += align256(size_t(emax) * size_t(p.g_stride) * p.elem());
+  L.ep_off = off;
+  off += align256(size_t(emax) * size_t(L.row) * p.elem());
+  L.ap_off = off;
+  off += align256(size_t(L.nslot) * size_t(p.K) * size_t(p.n_w) * p.elem());
+  L.gev_off = off;
+  off += align256(size_t(std::max(g.e, 1)) * 3 * p.elem());
+  L.total = off;
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -146,6 +192,7 @@ cgtp_status_t cgtp_plan_compile(cgtp_plan_t plan, int ops) {
       fams.push_back("fwd");
       fams.push_back("fwds");
     }
+    if (ops & (1 << CGTP_OP_BACKWARD)) fams.push_back("bwd");
   }
   for (auto& f : fams) {
     cgtp_status_t st = cgtp::compile_family(plan->p, f, &err);
@@ -198,13 +245,17 @@ cgtp_status_t cgtp_graph_upload(cgtp_graph_t g) {
 
 cgtp_status_t cgtp_graph_destroy(cgtp_graph_t g) {
   if (!g) return ok();
+  int cur = 0;
+  hipGetDevice(&cur);
   for (auto& kv : g->g.dev) {
-    int cur = 0;
-    hipGetDevice(&cur);
     hipSetDevice(kv.first);
     hipFree(kv.second.base);
-    hipSetDevice(cur);
   }
+  for (auto& kv : g->g.views) {
+    hipSetDevice(kv.first.first);
+    hipFree(kv.second.base);
+  }
+  hipSetDevice(cur);
   delete g;
   return ok();
 }
@@ -213,10 +264,15 @@ cgtp_status_t cgtp_workspace_size(cgtp_plan_t plan, cgtp_graph_t g, cgtp_op_t op
   if (!plan || !g || !bytes) return fail(CGTP_ERR_INVALID_ARG, "null argument");
   const cgtp::Plan& p = plan->p;
   const cgtp::Graph& G = g->g;
-  auto ch = G.chunks(g_chunk_edges(p, G));
-  size_t e_max = size_t(max_chunk_edges(G, ch));
-  size_t need = align256(e_max * size_t(p.g_stride) * p.elem());
-  (void)op;
+  size_t need = 0;
+  if (op == CGTP_OP_FORWARD) {
+    auto ch = G.chunks(g_chunk_edges(p, G));
+    need = align256(size_t(max_chunk_edges(G, ch)) * size_t(p.g_stride) * p.elem());
+  } else if (op == CGTP_OP_BACKWARD) {
+    need = bwd_layout(p, G).total;
+  } else {
+    return fail(CGTP_ERR_UNSUPPORTED, "double backward is not built yet");
+  }
   *bytes = std::max<size_t>(need, 256);
   return ok();
 }
@@ -264,15 +320,91 @@ cgtp_status_t cgtp_conv_forward(cgtp_plan_t plan, cgtp_graph_t g, cgtp_schedule_
 
 }  // extern "C"
 
+
 extern "C" {
 
 cgtp_status_t cgtp_conv_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x, const void* pos, const void* shift,
                                  const void* phi, const void* A, const void* grad_out, void* grad_x, void* grad_pos,
                                  void* grad_edge_vec, void* grad_phi, void* grad_A, void* workspace, size_t ws_bytes,
                                  void* stream) {
-  (void)plan; (void)g; (void)x; (void)pos; (void)shift; (void)phi; (void)A; (void)grad_out; (void)grad_x;
-  (void)grad_pos; (void)grad_edge_vec; (void)grad_phi; (void)grad_A; (void)workspace; (void)ws_bytes; (void)stream;
-  return fail(CGTP_ERR_UNSUPPORTED, "backward not built yet");
+  if (!plan || !g) return fail(CGTP_ERR_INVALID_ARG, "null plan or graph");
+  if (!x || !pos || !phi || !A || !grad_out) return fail(CGTP_ERR_INVALID_ARG, "null input tensor");
+  cgtp::Plan& p = plan->p;
+  cgtp::Graph& G = g->g;
+  if (p.mode != CGTP_CHANNELWISE) return fail(CGTP_ERR_UNSUPPORTED, "fully connected backward not built yet");
+  if (!grad_x && !grad_pos && !grad_edge_vec && !grad_phi && !grad_A) return ok();
+  BwdLayout L = bwd_layout(p, G);
+  if (!workspace || ws_bytes < L.total) return fail(CGTP_ERR_WORKSPACE, "workspace too small");
+  std::string err;
+  cgtp::DeviceGraph d;
+  cgtp_status_t st = cgtp::device_graph(G, &d, &err);
+  if (st != CGTP_OK) return fail(st, err);
+  const cgtp::SourceViews* views = nullptr;
+  if (grad_x && (st = cgtp::source_views(G, L.cap, &views, &err)) != CGTP_OK) return fail(st, err);
+  hipFunction_t kzero, kprep, krecv, ksrc, kfinal, kpos, kred;
+  const char* fam = "bwd";
+  if ((st = cgtp::get_kernel(p, fam, "cgtp_fill_zero", &kzero, &err)) != CGTP_OK ||
+      (st = cgtp::get_kernel(p, fam, "cgtp_prep", &kprep, &err)) != CGTP_OK ||
+      (st = cgtp::get_kernel(p, fam, "cgtp_bwd_recv", &krecv, &err)) != CGTP_OK ||
+      (st = cgtp::get_kernel(p, fam, "cgtp_bwd_src", &ksrc, &err)) != CGTP_OK ||
+      (st = cgtp::get_kernel(p, fam, "cgtp_edge_final", &kfinal, &err)) != CGTP_OK ||
+      (st = cgtp::get_kernel(p, fam, "cgtp_pos_grad", &kpos, &err)) != CGTP_OK ||
+      (st = cgtp::get_kernel(p, fam, "cgtp_a_reduce", &kred, &err)) != CGTP_OK)
+    return fail(st, err);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  void* Gb = ws + L.g_off;
+  void* ep = ws + L.ep_off;
+  void* ap = ws + L.ap_off;
+  void* gev = grad_edge_vec ? grad_edge_vec : static_cast<void*>(ws + L.gev_off);
+  const bool need_edge = grad_edge_vec || grad_pos || grad_phi;
+  void* gev_arg = (grad_edge_vec || grad_pos) ? gev : nullptr;
+  if (grad_A) {
+    long long n = (long long)L.nslot * p.K * p.n_w;
+    void* a[] = {&ap, &n};
+    if ((st = cgtp::launch(kzero, unsigned((n + 255) / 256), 256, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
+  }
+  const int nt_r = L.ntask_r, nt_s = L.ntask_s;
+  for (size_t c = 0; c < L.chunks.size(); ++c) {
+    int i0 = L.chunks[c].first, nrec = L.chunks[c].second - L.chunks[c].first;
+    int e0 = G.row_ptr[L.chunks[c].first], e1 = G.row_ptr[L.chunks[c].second];
+    if (e1 > e0) {
+      void* a[] = {(void*)&pos, (void*)&shift, (void*)&d.recv, (void*)&d.col, &e0, &e1, &Gb};
+      if ((st = cgtp::launch(kprep, unsigned((e1 - e0 + 255) / 256), 256, 0, s, a, &err)) != CGTP_OK)
+        return fail(st, err);
+    }
+    if (need_edge || grad_A) {
+      int per, rpw, nch;
+      chunk_geometry(nrec, &per, &rpw, &nch);
+      void* a[] = {(void*)&x, (void*)&phi, (void*)&A, &Gb, (void*)&d.row_ptr, (void*)&d.col, (void*)&grad_out,
+                   &ep, &ap, &i0, &nrec, &per, &nch, &rpw, &e0};
+      if ((st = cgtp::launch(krecv, unsigned(8 * nt_r * nch), 64, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
+    }
+    if (grad_x) {
+      int n = G.n, per = (G.n + 7) / 8, acc = c > 0 ? 1 : 0;
+      void* sp = static_cast<int32_t*>(views->base) + views->ptr_off[c];
+      void* se = static_cast<int32_t*>(views->base) + views->edge_off[c];
+      void* a[] = {(void*)&phi, (void*)&A, &Gb, (void*)&grad_out, (void*)&d.recv, &sp, &se, &grad_x, &n, &per, &e0,
+                   &acc};
+      if ((st = cgtp::launch(ksrc, unsigned(8 * nt_s * per), 64, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
+    }
+    if (need_edge && e1 > e0) {
+      void* a[] = {(void*)&pos, (void*)&shift, (void*)&d.recv, (void*)&d.col, &ep, &e0, &e1, &grad_phi, &gev_arg};
+      if ((st = cgtp::launch(kfinal, unsigned((e1 - e0 + 255) / 256), 256, 0, s, a, &err)) != CGTP_OK)
+        return fail(st, err);
+    }
+  }
+  if (grad_pos) {
+    int n = G.n;
+    void* a[] = {&gev, (void*)&d.row_ptr, (void*)&d.src_ptr, (void*)&d.src_edge, &n, &grad_pos};
+    if ((st = cgtp::launch(kpos, unsigned((n + 255) / 256), 256, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
+  }
+  if (grad_A) {
+    int n = p.K * p.n_w, ns = L.nslot;
+    void* a[] = {&ap, &ns, &n, &grad_A};
+    if ((st = cgtp::launch(kred, unsigned((n + 255) / 256), 256, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
+  }
+  return ok();
 }
 
 cgtp_status_t cgtp_check_edges(cgtp_plan_t plan, cgtp_graph_t g, const void* pos, const void* shift, void* workspace,

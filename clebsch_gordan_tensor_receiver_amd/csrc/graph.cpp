@@ -129,4 +129,53 @@ cgtp_status_t device_graph(Graph& g, DeviceGraph* out, std::string* err) {
   return CGTP_OK;
 }
 
+cgtp_status_t source_views(Graph& g, long long cap, const SourceViews** out, std::string* err) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    *err = "hipGetDevice failed";
+    return CGTP_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g.mu);
+  auto key = std::make_pair(dev, cap);
+  auto it = g.views.find(key);
+  if (it != g.views.end()) {
+    *out = &it->second;
+    return CGTP_OK;
+  }
+  SourceViews v;
+  v.chunks = g.chunks(cap);
+  std::vector<int32_t> host;
+  for (auto& c : v.chunks) {
+    const int e0 = g.row_ptr[c.first], e1 = g.row_ptr[c.second];
+    v.ptr_off.push_back(host.size());
+    size_t ptr_at = host.size();
+    host.resize(host.size() + size_t(g.n) + 1, 0);
+    std::vector<int32_t> edges;
+    for (int j = 0; j < g.n; ++j) {
+      for (int k = g.src_ptr[j]; k < g.src_ptr[j + 1]; ++k) {
+        int e = g.src_edge[k];
+        if (e >= e0 && e < e1) edges.push_back(e);
+      }
+      host[ptr_at + size_t(j) + 1] = int32_t(edges.size());
+    }
+    v.edge_off.push_back(host.size());
+    host.insert(host.end(), edges.begin(), edges.end());
+    host.push_back(0);  // keeps every chunk's edge array non-empty
+  }
+  hipError_t e = hipMalloc(&v.base, host.size() * sizeof(int32_t));
+  if (e != hipSuccess) {
+    *err = std::string("hipMalloc(source views): ") + hipGetErrorString(e);
+    return CGTP_ERR_HIP;
+  }
+  e = hipMemcpy(v.base, host.data(), host.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    hipFree(v.base);
+    *err = std::string("hipMemcpy(source views): ") + hipGetErrorString(e);
+    return CGTP_ERR_HIP;
+  }
+  auto res = g.views.emplace(key, std::move(v));
+  *out = &res.first->second;
+  return CGTP_OK;
+}
+
 }  // namespace cgtp

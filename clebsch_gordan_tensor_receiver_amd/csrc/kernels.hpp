@@ -32,13 +32,19 @@ std::unique_ptr<KernelSet> make_kernel_set();
 // Kernel source of one family for a plan (deterministic text).
 std::string generate_source(const Plan& p, const std::string& family, std::string* err);
 
-// Work decomposition shared by the generator and the launcher.
+// Work decomposition shared by the generator and the launcher.  A task is one wave's share of
+// a receiver (or sender): a block of the output (or input) features and 64 channels of it.
 struct Task {
-  int group;   // output block (forward, receiver backward) or input block (source backward)
-  int cb;      // 64-channel block
+  int group;              // output block (forward, receiver backward) or input block (source backward)
+  int cb;                 // 64-channel block
+  std::vector<int> paths; // paths handled (receiver backward: one register-budgeted subset)
 };
 std::vector<Task> forward_tasks(const Plan& p);
+std::vector<Task> recv_backward_tasks(const Plan& p);
 std::vector<Task> source_tasks(const Plan& p);
+// Values per edge and task written by the receiver backward (phi-bar partials then
+// Y-bar partials), padded to a multiple of 4.
+int edge_partial_width(const Plan& p);
 
 // Compile (once) and fetch a kernel of a family on the current device.
 cgtp_status_t get_kernel(Plan& p, const std::string& family, const std::string& name, hipFunction_t* f,
