@@ -26,6 +26,7 @@ EXPORTED = [
     "cgtp_plan_compile", "cgtp_plan_set_scratch_budget", "cgtp_graph_build", "cgtp_graph_export",
     "cgtp_graph_dims", "cgtp_graph_upload", "cgtp_graph_destroy", "cgtp_workspace_size",
     "cgtp_conv_forward", "cgtp_conv_backward", "cgtp_check_edges", "cgtp_error_string", "cgtp_last_error",
+    "cgtp_profile_begin", "cgtp_profile_end", "cgtp_profile_count", "cgtp_profile_get",
 ]
 
 
@@ -70,6 +71,11 @@ def load() -> ctypes.CDLL:
         "cgtp_conv_forward": [P, P, I, V, V, V, V, V, V, V, Z, V],
         "cgtp_conv_backward": [P, P, V, V, V, V, V, V, V, V, V, V, V, V, Z, V],
         "cgtp_check_edges": [P, P, V, V, V, Z, V, ctypes.POINTER(ctypes.c_int)],
+        "cgtp_profile_begin": [],
+        "cgtp_profile_end": [],
+        "cgtp_profile_count": [],
+        "cgtp_profile_get": [I, ctypes.c_char_p, I, ctypes.POINTER(ctypes.c_longlong),
+                             ctypes.POINTER(ctypes.c_double)],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -187,6 +193,24 @@ class Graph:
 
     def upload(self) -> None:
         check(load().cgtp_graph_upload(self.handle))
+
+
+def profile_begin() -> None:
+    check(load().cgtp_profile_begin())
+
+
+def profile_end():
+    """Stop launch timing; returns {kernel name: (launches, total ms)}."""
+    lib = load()
+    check(lib.cgtp_profile_end())
+    out = {}
+    for k in range(lib.cgtp_profile_count()):
+        buf = ctypes.create_string_buffer(128)
+        n = ctypes.c_longlong()
+        ms = ctypes.c_double()
+        check(lib.cgtp_profile_get(k, buf, 128, ctypes.byref(n), ctypes.byref(ms)))
+        out[buf.value.decode()] = (int(n.value), float(ms.value))
+    return out
 
 
 def workspace_size(plan: Plan, graph: Graph, op: int) -> int:

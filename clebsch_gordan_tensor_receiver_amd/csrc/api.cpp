@@ -2,6 +2,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <cstdio>
 #include <cstring>
 #include <new>
 #include <string>
@@ -411,6 +412,34 @@ cgtp_status_t cgtp_check_edges(cgtp_plan_t plan, cgtp_graph_t g, const void* pos
                                size_t ws_bytes, void* stream, int* first_bad) {
   (void)plan; (void)g; (void)pos; (void)shift; (void)workspace; (void)ws_bytes; (void)stream; (void)first_bad;
   return fail(CGTP_ERR_UNSUPPORTED, "edge check not built yet");
+}
+
+}  // extern "C"
+
+extern "C" {
+
+cgtp_status_t cgtp_profile_begin(void) {
+  cgtp::profile_begin();
+  return ok();
+}
+
+cgtp_status_t cgtp_profile_end(void) {
+  std::string err;
+  cgtp_status_t st = cgtp::profile_end(&err);
+  return st == CGTP_OK ? ok() : fail(st, err);
+}
+
+int cgtp_profile_count(void) { return int(cgtp::profile_entries().size()); }
+
+cgtp_status_t cgtp_profile_get(int index, char* name, int capacity, long long* launches, double* total_ms) {
+  auto v = cgtp::profile_entries();
+  if (index < 0 || index >= int(v.size())) return fail(CGTP_ERR_INVALID_ARG, "profile index out of range");
+  if (name && capacity > 0) {
+    std::snprintf(name, size_t(capacity), "%s", v[index].name.c_str());
+  }
+  if (launches) *launches = v[index].launches;
+  if (total_ms) *total_ms = v[index].ms;
+  return ok();
 }
 
 }  // extern "C"

@@ -51,6 +51,16 @@ cgtp_status_t get_kernel(Plan& p, const std::string& family, const std::string& 
                          std::string* err);
 cgtp_status_t compile_family(Plan& p, const std::string& family, std::string* err);
 
+// Launch timing (see cgtp_profile_begin in cgtp.h).
+struct ProfileEntry {
+  std::string name;
+  long long launches;
+  double ms;
+};
+void profile_begin();
+cgtp_status_t profile_end(std::string* err);
+std::vector<ProfileEntry> profile_entries();
+
 // Launch helper: args is an array of pointers to the kernel arguments.
 cgtp_status_t launch(hipFunction_t f, unsigned grid, unsigned block, unsigned shmem, hipStream_t s,
                      void** args, std::string* err);

@@ -9,6 +9,8 @@
 #include <cstdio>
 #include <cstdlib>
 #include <fstream>
+#include <map>
+#include <mutex>
 #include <sstream>
 
 #include "kernels.hpp"
@@ -112,6 +114,66 @@ cgtp_status_t compile_family(Plan& p, const std::string& family, std::string* er
   return CGTP_OK;
 }
 
+// ------------------------------------------------------------------ launch timing
+// While profiling is on, every launch is bracketed by two HIP events recorded on the launch
+// stream; profile_end() waits for them and accumulates the elapsed time per kernel name.
+namespace {
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::map<hipFunction_t, std::string> g_names;
+struct Pending {
+  std::string name;
+  hipEvent_t a, b;
+};
+std::vector<Pending> g_pending;
+std::vector<hipEvent_t> g_event_pool;
+std::map<std::string, std::pair<long long, double>> g_totals;  // name -> (launches, ms)
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+}  // namespace
+
+void profile_begin() {
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  g_prof_on = true;
+  g_totals.clear();
+}
+
+cgtp_status_t profile_end(std::string* err) {
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  g_prof_on = false;
+  cgtp_status_t st = CGTP_OK;
+  for (auto& p : g_pending) {
+    float ms = 0;
+    if (hipEventSynchronize(p.b) != hipSuccess || hipEventElapsedTime(&ms, p.a, p.b) != hipSuccess) {
+      *err = "hipEventElapsedTime failed";
+      st = CGTP_ERR_HIP;
+    }
+    auto& t = g_totals[p.name];
+    t.first += 1;
+    t.second += ms;
+    g_event_pool.push_back(p.a);
+    g_event_pool.push_back(p.b);
+  }
+  g_pending.clear();
+  return st;
+}
+
+std::vector<ProfileEntry> profile_entries() {
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  std::vector<ProfileEntry> out;
+  for (auto& kv : g_totals) out.push_back({kv.first, kv.second.first, kv.second.second});
+  return out;
+}
+
 cgtp_status_t get_kernel(Plan& p, const std::string& family, const std::string& name, hipFunction_t* f,
                          std::string* err) {
   cgtp_status_t st = compile_family(p, family, err);
@@ -146,6 +208,10 @@ cgtp_status_t get_kernel(Plan& p, const std::string& family, const std::string& 
     return CGTP_ERR_HIP;
   }
   m.fns[key] = fn;
+  {
+    std::lock_guard<std::mutex> plock(g_prof_mu);
+    g_names[fn] = name;
+  }
   *f = fn;
   return CGTP_OK;
 }
@@ -153,7 +219,24 @@ cgtp_status_t get_kernel(Plan& p, const std::string& family, const std::string& 
 cgtp_status_t launch(hipFunction_t f, unsigned grid, unsigned block, unsigned shmem, hipStream_t s, void** args,
                      std::string* err) {
   if (grid == 0) return CGTP_OK;
+  hipEvent_t ea = nullptr, eb = nullptr;
+  std::string pname;
+  {
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    if (g_prof_on) {
+      ea = take_event();
+      eb = take_event();
+      auto it = g_names.find(f);
+      pname = it == g_names.end() ? "?" : it->second;
+    }
+  }
+  if (ea) hipEventRecord(ea, s);
   hipError_t e = hipModuleLaunchKernel(f, grid, 1, 1, block, 1, 1, shmem, s, args, nullptr);
+  if (eb) {
+    hipEventRecord(eb, s);
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    g_pending.push_back({pname, ea, eb});
+  }
   if (e != hipSuccess) {
     *err = std::string("hipModuleLaunchKernel: ") + hipGetErrorString(e);
     return CGTP_ERR_HIP;

@@ -168,6 +168,19 @@ cgtp_status_t cgtp_conv_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x
 cgtp_status_t cgtp_check_edges(cgtp_plan_t plan, cgtp_graph_t g, const void* pos, const void* shift,
                                void* workspace, size_t ws_bytes, void* stream, int* first_bad);
 
+/* ---------------------------------------------------------------- launch timing */
+
+/* Start timing kernel launches: from now on every kernel the library launches (any plan, any
+ * thread) is bracketed by two HIP events recorded on its launch stream.  Costs a few
+ * microseconds per launch; leave it off in production timing. */
+cgtp_status_t cgtp_profile_begin(void);
+/* Stop timing, wait for the recorded events and total the elapsed time per kernel name. */
+cgtp_status_t cgtp_profile_end(void);
+/* Number of kernel names timed by the last begin/end pair, and the totals of entry `index`:
+ * the kernel name (NUL-terminated, truncated to `capacity`), launch count and summed ms. */
+int cgtp_profile_count(void);
+cgtp_status_t cgtp_profile_get(int index, char* name, int capacity, long long* launches, double* total_ms);
+
 const char* cgtp_error_string(cgtp_status_t status);
 const char* cgtp_last_error(void);
 
