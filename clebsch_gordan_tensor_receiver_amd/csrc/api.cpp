@@ -48,7 +48,10 @@ long long max_chunk_edges(const cgtp::Graph& g, const std::vector<std::pair<int,
   return m;
 }
 
-constexpr int kMaxSlots = 256;  // A-bar partial slots per chunk (waves of one task)
+// Launch geometry shared with the generated kernels (codegen.cpp).
+constexpr int kFwdSplit = 2;    // waves per receiver in the forward
+constexpr int kSrcSplit = 2;    // waves per sender in the source backward
+constexpr int kRecvGroup = 4;   // receivers (one wave each) per workgroup in the receiver backward
 
 // Workspace plan of a backward call.
 struct BwdLayout {
@@ -56,13 +59,14 @@ struct BwdLayout {
   std::vector<std::pair<int, int>> chunks;
   int ntask_r = 0, ntask_s = 0, V = 0, row = 0;
   int nslot = 0;                // A-bar partial slots (max over chunks)
+  long long emax = 0;           // edges of the largest chunk (stride of the edge partials)
   size_t g_off = 0, ep_off = 0, ap_off = 0, gev_off = 0, total = 0;
 };
 
-void chunk_geometry(int nrec, int* per, int* rpw, int* nch) {
+// Receivers per XCD and receiver groups per XCD of a chunk; the groups are the A-bar slots.
+void chunk_geometry(int nrec, int* per, int* nch) {
   *per = (nrec + 7) / 8;
-  *rpw = std::max(1, (nrec + kMaxSlots - 1) / kMaxSlots);
-  *nch = (*per + *rpw - 1) / *rpw;
+  *nch = (*per + kRecvGroup - 1) / kRecvGroup;
 }
 
 BwdLayout bwd_layout(const cgtp::Plan& p, const cgtp::Graph& g) {
@@ -75,10 +79,11 @@ BwdLayout bwd_layout(const cgtp::Plan& p, const cgtp::Graph& g) {
   L.cap = std::max<long long>(std::max<long long>(1, (long long)(p.scratch_budget / size_t(row_bytes))),
                               g.max_in_degree);
   L.chunks = g.chunks(L.cap);
-  long long emax = max_chunk_edges(g, L.chunks);
+  long long emax = std::max<long long>(1, max_chunk_edges(g, L.chunks));
+  L.emax = emax;
   for (auto& c : L.chunks) {
-    int per, rpw, nch;
-    chunk_geometry(c.second - c.first, &per, &rpw, &nch);
+    int per, nch;
+    chunk_geometry(c.second - c.first, &per, &nch);
     L.nslot = std::max(L.nslot, 8 * nch);
   }
   size_t off = 0;
@@ -309,12 +314,13 @@ cgtp_status_t cgtp_conv_forward(cgtp_plan_t plan, cgtp_graph_t g, cgtp_schedule_
     int e0 = G.row_ptr[c.first], e1 = G.row_ptr[c.second];
     if (e1 > e0) {
       void* a[] = {(void*)&pos, (void*)&shift, (void*)&d.recv, (void*)&d.col, &e0, &e1, &G_ws};
-      if ((st = cgtp::launch(kprep, unsigned((e1 - e0 + 255) / 256), 256, 0, s, a, &err)) != CGTP_OK)
+      if ((st = cgtp::launch(kprep, unsigned((e1 - e0 + 63) / 64), 64, 0, s, a, &err)) != CGTP_OK)
         return fail(st, err);
     }
     int per = (nrec + 7) / 8;
     void* b[] = {(void*)&x, (void*)&phi, (void*)&A, &G_ws, (void*)&d.row_ptr, (void*)&d.col, &out, &i0, &nrec, &per, &e0};
-    if ((st = cgtp::launch(kfwd, unsigned(8 * ntask * per), 64, 0, s, b, &err)) != CGTP_OK) return fail(st, err);
+    if ((st = cgtp::launch(kfwd, unsigned(8 * ntask * per), 64 * kFwdSplit, 0, s, b, &err)) != CGTP_OK)
+      return fail(st, err);
   }
   return ok();
 }
@@ -366,20 +372,22 @@ cgtp_status_t cgtp_conv_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x
     if ((st = cgtp::launch(kzero, unsigned((n + 255) / 256), 256, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
   }
   const int nt_r = L.ntask_r, nt_s = L.ntask_s;
+  int eps = int(L.emax);
   for (size_t c = 0; c < L.chunks.size(); ++c) {
     int i0 = L.chunks[c].first, nrec = L.chunks[c].second - L.chunks[c].first;
     int e0 = G.row_ptr[L.chunks[c].first], e1 = G.row_ptr[L.chunks[c].second];
     if (e1 > e0) {
       void* a[] = {(void*)&pos, (void*)&shift, (void*)&d.recv, (void*)&d.col, &e0, &e1, &Gb};
-      if ((st = cgtp::launch(kprep, unsigned((e1 - e0 + 255) / 256), 256, 0, s, a, &err)) != CGTP_OK)
+      if ((st = cgtp::launch(kprep, unsigned((e1 - e0 + 63) / 64), 64, 0, s, a, &err)) != CGTP_OK)
         return fail(st, err);
     }
     if (need_edge || grad_A) {
-      int per, rpw, nch;
-      chunk_geometry(nrec, &per, &rpw, &nch);
+      int per, nch;
+      chunk_geometry(nrec, &per, &nch);
       void* a[] = {(void*)&x, (void*)&phi, (void*)&A, &Gb, (void*)&d.row_ptr, (void*)&d.col, (void*)&grad_out,
-                   &ep, &ap, &i0, &nrec, &per, &nch, &rpw, &e0};
-      if ((st = cgtp::launch(krecv, unsigned(8 * nt_r * nch), 64, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
+                   &ep, &ap, &i0, &nrec, &per, &nch, &e0, &eps};
+      if ((st = cgtp::launch(krecv, unsigned(8 * nt_r * nch), 64 * kRecvGroup, 0, s, a, &err)) != CGTP_OK)
+        return fail(st, err);
     }
     if (grad_x) {
       int n = G.n, per = (G.n + 7) / 8, acc = c > 0 ? 1 : 0;
@@ -387,10 +395,12 @@ cgtp_status_t cgtp_conv_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x
       void* se = static_cast<int32_t*>(views->base) + views->edge_off[c];
       void* a[] = {(void*)&phi, (void*)&A, &Gb, (void*)&grad_out, (void*)&d.recv, &sp, &se, &grad_x, &n, &per, &e0,
                    &acc};
-      if ((st = cgtp::launch(ksrc, unsigned(8 * nt_s * per), 64, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
+      if ((st = cgtp::launch(ksrc, unsigned(8 * nt_s * per), 64 * kSrcSplit, 0, s, a, &err)) != CGTP_OK)
+        return fail(st, err);
     }
     if (need_edge && e1 > e0) {
-      void* a[] = {(void*)&pos, (void*)&shift, (void*)&d.recv, (void*)&d.col, &ep, &e0, &e1, &grad_phi, &gev_arg};
+      void* a[] = {(void*)&pos, (void*)&shift, (void*)&d.recv, (void*)&d.col, &ep, &e0, &e1, &eps, &grad_phi,
+                   &gev_arg};
       if ((st = cgtp::launch(kfinal, unsigned((e1 - e0 + 255) / 256), 256, 0, s, a, &err)) != CGTP_OK)
         return fail(st, err);
     }
@@ -398,12 +408,12 @@ cgtp_status_t cgtp_conv_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x
   if (grad_pos) {
     int n = G.n;
     void* a[] = {&gev, (void*)&d.row_ptr, (void*)&d.src_ptr, (void*)&d.src_edge, &n, &grad_pos};
-    if ((st = cgtp::launch(kpos, unsigned((n + 255) / 256), 256, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
+    if ((st = cgtp::launch(kpos, unsigned(n), 64, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
   }
   if (grad_A) {
     int n = p.K * p.n_w, ns = L.nslot;
     void* a[] = {&ap, &ns, &n, &grad_A};
-    if ((st = cgtp::launch(kred, unsigned((n + 255) / 256), 256, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
+    if ((st = cgtp::launch(kred, unsigned((n + 63) / 64), 256, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
   }
   return ok();
 }

@@ -29,6 +29,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <functional>
 #include <numeric>
 #include <set>
 #include <sstream>
@@ -117,34 +118,25 @@ void prelude(Out& o, const Plan& p, bool dual, bool reduce) {
     o.line("DEV D3 operator*(real c, D3 b) { return D3(c * b.v, c * b.x, c * b.y, c * b.z); }");
   }
   if (reduce) {
-    // Cross-lane helpers.  swap32(a, b): a <- [a lanes 0-31, b lanes 0-31], b <- [a 32-63, b 32-63];
-    // swap16 does the same between odd rows of a and even rows of b; rowsum leaves in every lane the
-    // sum of its 16-lane row.
-    // The lane swaps go through inline assembly with both registers tied: this compiler's
-    // __builtin_amdgcn_permlane{16,32}_swap return the new first operand for both results.
-    o.line("DEV void swp32(unsigned& a, unsigned& b) { asm volatile(\"s_nop 1\\n\\tv_permlane32_swap_b32 %0, %1"
-           "\\n\\ts_nop 1\" : \"+v\"(a), \"+v\"(b)); }");
-    o.line("DEV void swp16(unsigned& a, unsigned& b) { asm volatile(\"s_nop 1\\n\\tv_permlane16_swap_b32 %0, %1"
-           "\\n\\ts_nop 1\" : \"+v\"(a), \"+v\"(b)); }");
+    // Cross-lane helpers: rowsum leaves in every lane the sum of its 16-lane row (DPP), __shfl_rd
+    // reads one lane.  Lane swaps are emitted inline by emit_swaps.
     if (!f64) {
-      for (const char* w : {"32", "16"})
-        o.line(F("DEV void swap%s(real& a, real& b) { unsigned x = __builtin_bit_cast(unsigned, a),"
-                 " y = __builtin_bit_cast(unsigned, b); swp%s(x, y); a = __builtin_bit_cast(real, x);"
-                 " b = __builtin_bit_cast(real, y); }", w, w));
       o.line("template <int C> DEV real dpp(real v) { return __builtin_bit_cast(real, "
              "__builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), C, 0xF, 0xF, false)); }");
     } else {
-      for (const char* w : {"32", "16"})
-        o.line(F("DEV void swap%s(real& a, real& b) { unsigned long long x = __builtin_bit_cast(unsigned long long, a),"
-                 " y = __builtin_bit_cast(unsigned long long, b); unsigned xl = (unsigned)x, xh = (unsigned)(x >> 32),"
-                 " yl = (unsigned)y, yh = (unsigned)(y >> 32); swp%s(xl, yl); swp%s(xh, yh);"
-                 " a = __builtin_bit_cast(real, (unsigned long long)xl | ((unsigned long long)xh << 32));"
-                 " b = __builtin_bit_cast(real, (unsigned long long)yl | ((unsigned long long)yh << 32)); }", w, w, w));
       o.line("template <int C> DEV real dpp(real v) { unsigned long long x = __builtin_bit_cast(unsigned long long, v);");
       o.line("  unsigned lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned)x, C, 0xF, 0xF, false);");
       o.line("  unsigned hi = __builtin_amdgcn_update_dpp(0, (int)(unsigned)(x >> 32), C, 0xF, 0xF, false);");
       o.line("  return __builtin_bit_cast(real, (unsigned long long)lo | ((unsigned long long)hi << 32)); }");
     }
+    if (!f64)
+      o.line("DEV real __shfl_rd(real v, int l) { return __builtin_bit_cast(real, "
+             "__builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l)); }");
+    else
+      o.line("DEV real __shfl_rd(real v, int l) { unsigned long long x = __builtin_bit_cast(unsigned long long, v);"
+             " unsigned lo = __builtin_amdgcn_readlane((int)(unsigned)x, l), hi = __builtin_amdgcn_readlane("
+             "(int)(unsigned)(x >> 32), l); return __builtin_bit_cast(real, (unsigned long long)lo |"
+             " ((unsigned long long)hi << 32)); }");
     o.line("DEV real rowsum(real v) { v += dpp<0xB1>(v); v += dpp<0x4E>(v); v += dpp<0x141>(v);"
            " v += dpp<0x140>(v); return v; }");
   }
@@ -190,19 +182,23 @@ void emit_edge_vector(Out& o) {
   o.close();
 }
 
-// prep: lane = edge; writes the G row of every edge of [e0, e1) at G + (e - e0) * stride.
+// prep: lane = edge, one wave per 64 edges; writes the G row of every edge of [e0, e1) at
+// G + (e - e0) * stride.  Rows are produced 64 values at a time into an LDS tile and copied out
+// with 16-byte stores in which 16 lanes cover 256 contiguous bytes of one row.
 void emit_prep(Out& o, const Plan& p) {
-  o.line("extern \"C\" __global__ void __launch_bounds__(256)");
+  const int per = p.dtype == CGTP_F64 ? 2 : 4;  // values per 16-byte unit
+  const int block_vals = 16 * per;             // values per tile column block
+  o.line("extern \"C\" __global__ void __launch_bounds__(64)");
   o.open("cgtp_prep(const real* __restrict__ pos, const real* __restrict__ shift, const int* __restrict__ recv,"
          " const int* __restrict__ send, int e0, int e1, real* __restrict__ G)");
-  o.line("const int e = e0 + (int)(blockIdx.x * 256 + threadIdx.x);");
-  o.line("if (e >= e1) return;");
+  o.line("__shared__ V4 tile[64 * 17];");
+  o.line("const int lane = (int)threadIdx.x;");
+  o.line("const int eb = e0 + (int)blockIdx.x * 64;");
+  o.line("const int e = min(eb + lane, e1 - 1);");
   emit_edge_vector(o);
   o.line("const real inv = R(1) / sqrt(rx * rx + ry * ry + rz * rz);");
   o.line(F("real Y[%d];", p.sh_dim));
   o.line("sh_eval<real>(rx * inv, ry * inv, rz * inv, Y);");
-  o.line(F("V4* __restrict__ dst = (V4*)(G + (i64)(e - e0) * %d);", p.g_stride));
-  const int per = p.dtype == CGTP_F64 ? 2 : 4;
   std::vector<std::string> vals;
   for (const Path& P : p.paths) {
     int s = P.l2 * P.l2;
@@ -216,10 +212,23 @@ void emit_prep(Out& o, const Plan& p) {
     }
   }
   while (int(vals.size()) < p.g_stride) vals.push_back("R(0)");
-  for (int k = 0; k < p.g_stride; k += per) {
-    std::string v;
-    for (int t = 0; t < per; ++t) v += (t ? ", " : "") + vals[k + t];
-    o.line(F("dst[%d] = V4{", k / per) + v + "};");
+  const int nblocks = (p.g_stride + block_vals - 1) / block_vals;
+  for (int b = 0; b < nblocks; ++b) {
+    const int v0 = b * block_vals, nv = std::min(block_vals, p.g_stride - v0) / per;
+    o.open("");
+    for (int k = 0; k < nv; ++k) {
+      std::string v;
+      for (int t = 0; t < per; ++t) v += (t ? ", " : "") + vals[v0 + k * per + t];
+      o.line(F("tile[lane * 17 + %d] = V4{", k) + v + "};");
+    }
+    o.line("__syncthreads();");
+    o.open("for (int it = 0; it < 16; ++it)");
+    o.line("const int row = it * 4 + (lane >> 4), c = lane & 15;");
+    o.line(F("if (eb + row < e1 && c < %d) ((V4*)(G + (i64)(eb + row - e0) * %d + %d))[c] = tile[row * 17 + c];", nv,
+             p.g_stride, v0));
+    o.close();
+    o.line("__syncthreads();");
+    o.close();
   }
   o.close();
 }
@@ -244,14 +253,6 @@ std::vector<int> out_blocks_of(const Plan& p, const std::vector<int>& paths) {
   std::set<int> s;
   for (int pi : paths) s.insert(p.paths[pi].i_out);
   return std::vector<int>(s.begin(), s.end());
-}
-
-// x_j components of the input blocks used by `paths`, named x<block>_<m>.
-void emit_x_loads(Out& o, const Plan& p, const std::vector<int>& paths) {
-  for (int b : in_blocks_of(p, paths)) {
-    const Block& B = p.in[b];
-    for (int m = 0; m < B.dim(); ++m) o.line(F("const real x%d_%d = xj[%d];", b, m, B.offset + m * B.mul));
-  }
 }
 
 void emit_a_loads(Out& o, const Plan& p, const std::vector<int>& paths) {
@@ -295,34 +296,85 @@ const char* kFwdArgs =
     " const real* __restrict__ G, const int* __restrict__ row_ptr, const int* __restrict__ col,"
     " real* __restrict__ out";
 
-// Channelwise conventional forward of task (output block k, channel block cb) for one receiver.
-// Paths are processed in register-budgeted subsets, each re-walking the receiver's edges.
+constexpr int kFwdSplit = 2;   // waves sharing one receiver's edge list in the forward
+constexpr int kSrcSplit = 2;   // waves sharing one sender's edge list in the source backward
+constexpr int kRecvGroup = 4;  // receivers (one wave each) per workgroup in the receiver backward
+
+// Loop over the in-edges e0 + start, e0 + start + stride, ... of a receiver (`e0`, `e1` in
+// scope).  Rows x_j of the input blocks `blocks` are loaded one edge ahead (software
+// pipelining), so their latency overlaps the arithmetic of the current edge.  The body sees
+// e, j, g (G row), f<q> (phi) and x<b>_<m>.
+void emit_recv_edge_loop(Out& o, const Plan& p, const std::vector<int>& blocks, const std::string& start,
+                         const std::string& stride, const std::function<void()>& body) {
+  o.open("");
+  o.line("int e = e0 + " + start + ";");
+  o.open("if (e < e1)");
+  o.line("int jn = col[e];");
+  for (int b : blocks) {
+    const Block& B = p.in[b];
+    for (int m = 0; m < B.dim(); ++m)
+      o.line(F("real xn%d_%d = x[(i64)jn * %d + %d + uc];", b, m, p.c_in, B.offset + m * B.mul));
+  }
+  o.open("for (; e < e1; e += " + stride + ")");
+  o.line("const int j = jn;");
+  for (int b : blocks)
+    for (int m = 0; m < p.in[b].dim(); ++m) o.line(F("const real x%d_%d = xn%d_%d;", b, m, b, m));
+  o.line("{ const int en = e + " + stride + "; jn = col[en < e1 ? en : e]; }");
+  for (int b : blocks) {
+    const Block& B = p.in[b];
+    for (int m = 0; m < B.dim(); ++m)
+      o.line(F("xn%d_%d = x[(i64)jn * %d + %d + uc];", b, m, p.c_in, B.offset + m * B.mul));
+  }
+  o.line(F("const real* __restrict__ ph = phi + (i64)e * %d;", p.K));
+  o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", p.g_stride));
+  for (int q = 0; q < p.K; ++q) o.line(F("const real f%d = ph[%d];", q, q));
+  o.line("(void)j;");
+  body();
+  o.close();
+  o.close();
+  o.close();
+}
+
+// Combine per-wave partial sums acc<m> (m < n) of the waves of a workgroup through LDS in a fixed
+// order; afterwards wave 0 holds the total.  `sm` must hold (nw - 1) * n * 64 values.
+void emit_wave_combine(Out& o, const std::string& prefix, int n, int nw) {
+  o.open("if (w != 0)");
+  for (int m = 0; m < n; ++m) o.line(F("sm[((w - 1) * %d + %d) * 64 + lane] = %s%d;", n, m, prefix.c_str(), m));
+  o.close();
+  o.line("__syncthreads();");
+  o.open("if (w == 0)");
+  for (int k = 1; k < nw; ++k)
+    for (int m = 0; m < n; ++m)
+      o.line(F("%s%d += sm[(%d * %d + %d) * 64 + lane];", prefix.c_str(), m, k - 1, n, m));
+  o.close();
+}
+
+// Channelwise conventional forward of task (output block k, channel block cb) for one receiver;
+// the receiver's edges are dealt round-robin to the kFwdSplit waves of the workgroup and their
+// partial sums combined in LDS.  Paths are processed in register-budgeted subsets, each
+// re-walking the edges.
 void emit_fwd_task(Out& o, const Plan& p, int ti, const Task& T) {
   const Block& OB = p.out[T.group];
-  const int d3 = OB.dim(), MUL = OB.mul, K = p.K;
-  o.open(F("DEV void fwd_t%d(%s, int node, int e_base)", ti, kFwdArgs));
-  o.line(F("const int u = %d + (int)threadIdx.x;", T.cb * 64));
+  const int d3 = OB.dim(), MUL = OB.mul;
+  o.open(F("DEV void fwd_t%d(%s, real* sm, int node, int e_base)", ti, kFwdArgs));
+  o.line("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
+  o.line(F("const int u = %d + lane;", T.cb * 64));
   o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
   for (int m = 0; m < d3; ++m) o.line(F("real acc%d = R(0);", m));
   o.line("const int e0 = row_ptr[node], e1 = row_ptr[node + 1];");
   for (const auto& S : subsets(p, T.paths)) {
     o.open("");
     emit_a_loads(o, p, S);
-    o.open("for (int e = e0; e < e1; ++e)");
-    o.line("const int j = col[e];");
-    o.line(F("const real* __restrict__ ph = phi + (i64)e * %d;", K));
-    o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", p.g_stride));
-    o.line(F("const real* __restrict__ xj = x + (i64)j * %d + uc;", p.c_in));
-    for (int q = 0; q < K; ++q) o.line(F("const real f%d = ph[%d];", q, q));
-    emit_x_loads(o, p, S);
-    for (int pi : S) {
-      emit_w(o, p, pi);
-      emit_path_accumulate(o, p, pi);
-    }
-    o.close();
+    emit_recv_edge_loop(o, p, in_blocks_of(p, S), "w", std::to_string(kFwdSplit), [&] {
+      for (int pi : S) {
+        emit_w(o, p, pi);
+        emit_path_accumulate(o, p, pi);
+      }
+    });
     o.close();
   }
-  o.open(F("if (u < %d)", MUL));
+  emit_wave_combine(o, "acc", d3, kFwdSplit);
+  o.open(F("if (w == 0 && u < %d)", MUL));
   o.line(F("real* __restrict__ dst = out + (i64)node * %d + %d + u;", p.c_out, OB.offset));
   for (int m = 0; m < d3; ++m) o.line(F("dst[%d] = acc%d;", m * MUL, m));
   o.close();
@@ -334,8 +386,9 @@ void emit_fwd_task(Out& o, const Plan& p, int ti, const Task& T) {
 void emit_fwd_streamed_task(Out& o, const Plan& p, int ti, const Task& T) {
   const Block& OB = p.out[T.group];
   const int d3 = OB.dim(), MUL = OB.mul, K = p.K;
-  o.open(F("DEV void fwds_t%d(%s, int node, int e_base)", ti, kFwdArgs));
-  o.line(F("const int u = %d + (int)threadIdx.x;", T.cb * 64));
+  o.open(F("DEV void fwds_t%d(%s, real* sm, int node, int e_base)", ti, kFwdArgs));
+  o.line("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
+  o.line(F("const int u = %d + lane;", T.cb * 64));
   o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
   for (int m = 0; m < d3; ++m) o.line(F("real acc%d = R(0);", m));
   o.line("const int e0 = row_ptr[node], e1 = row_ptr[node + 1];");
@@ -344,48 +397,55 @@ void emit_fwd_streamed_task(Out& o, const Plan& p, int ti, const Task& T) {
     o.open("");
     for (int q = 0; q < K; ++q)
       for (int m = 0; m < d3; ++m) o.line(F("real S%d_%d = R(0);", q, m));
-    o.open("for (int e = e0; e < e1; ++e)");
-    o.line("const int j = col[e];");
-    o.line(F("const real* __restrict__ ph = phi + (i64)e * %d;", K));
-    o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", p.g_stride));
-    o.line(F("const real* __restrict__ xj = x + (i64)j * %d + uc;", p.c_in));
-    emit_x_loads(o, p, {pi});
-    std::vector<bool> started(d3, false);
-    for (size_t t = 0; t < P.gpairs.size(); ++t) {
-      int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3;
-      if (!started[m3])
-        o.line(F("real c%d = g[%d] * x%d_%d;", m3, P.g_off + int(t), P.i_in, m1));
-      else
-        o.line(F("c%d = fma(g[%d], x%d_%d, c%d);", m3, P.g_off + int(t), P.i_in, m1, m3));
-      started[m3] = true;
-    }
-    for (int q = 0; q < K; ++q) {
-      o.line(F("const real f%d = ph[%d];", q, q));
-      for (int m = 0; m < d3; ++m)
-        if (started[m]) o.line(F("S%d_%d = fma(f%d, c%d, S%d_%d);", q, m, q, m, q, m));
-    }
-    o.close();
+    emit_recv_edge_loop(o, p, {P.i_in}, "w", std::to_string(kFwdSplit), [&] {
+      std::vector<bool> started(d3, false);
+      for (size_t t = 0; t < P.gpairs.size(); ++t) {
+        int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3;
+        if (!started[m3])
+          o.line(F("real c%d = g[%d] * x%d_%d;", m3, P.g_off + int(t), P.i_in, m1));
+        else
+          o.line(F("c%d = fma(g[%d], x%d_%d, c%d);", m3, P.g_off + int(t), P.i_in, m1, m3));
+        started[m3] = true;
+      }
+      for (int q = 0; q < K; ++q)
+        for (int m = 0; m < d3; ++m)
+          if (started[m]) o.line(F("S%d_%d = fma(f%d, c%d, S%d_%d);", q, m, q, m, q, m));
+    });
     for (int q = 0; q < K; ++q) {
       o.line(F("const real a%d = A[%d + uc];", q, q * p.n_w + P.w_off));
       for (int m = 0; m < d3; ++m) o.line(F("acc%d = fma(S%d_%d, a%d, acc%d);", m, q, m, q, m));
     }
     o.close();
   }
-  o.open(F("if (u < %d)", MUL));
+  emit_wave_combine(o, "acc", d3, kFwdSplit);
+  o.open(F("if (w == 0 && u < %d)", MUL));
   o.line(F("real* __restrict__ dst = out + (i64)node * %d + %d + u;", p.c_out, OB.offset));
   for (int m = 0; m < d3; ++m) o.line(F("dst[%d] = acc%d;", m * MUL, m));
   o.close();
   o.close();
 }
 
-// One receiver per block.  Blocks are spread over the 8 XCDs round-robin by the hardware; this
-// mapping gives each XCD a contiguous receiver range (spatial neighbours, whose senders' rows
-// then stay in that XCD's L2) and runs the tasks in decreasing cost order inside it (LunaTP
-// section 4.2, task ordering).
-void emit_node_dispatch(Out& o, const std::string& kname, const std::string& args, const std::string& call,
-                        int ntask) {
-  o.line("extern \"C\" __global__ void __launch_bounds__(64)");
+int max_out_dim(const Plan& p) {
+  int d = 1;
+  for (auto& b : p.out) d = std::max(d, b.dim());
+  return d;
+}
+
+int max_in_dim(const Plan& p) {
+  int d = 1;
+  for (auto& b : p.in) d = std::max(d, b.dim());
+  return d;
+}
+
+// One receiver per workgroup of kFwdSplit waves.  Workgroups are spread over the 8 XCDs
+// round-robin by the hardware; this mapping gives each XCD a contiguous receiver range (spatial
+// neighbours, whose senders' rows then stay in that XCD's L2) and runs the tasks in decreasing
+// cost order inside it (LunaTP section 4.2, task ordering).
+void emit_node_dispatch(Out& o, const Plan& p, const std::string& kname, const std::string& args,
+                        const std::string& call, int ntask) {
+  o.line(F("extern \"C\" __global__ void __launch_bounds__(%d)", 64 * kFwdSplit));
   o.open(kname + "(" + args + ", int i0, int nrec, int per, int e_base)");
+  o.line(F("__shared__ real sm[%d];", (kFwdSplit - 1) * max_out_dim(p) * 64));
   o.line("const int b = (int)blockIdx.x;");
   o.line("const int xcd = b & 7, s = b >> 3;");
   o.line("const int t = s / per, il = s - t * per;");
@@ -393,8 +453,8 @@ void emit_node_dispatch(Out& o, const std::string& kname, const std::string& arg
   o.line("if (i >= nrec) return;");
   o.line("const int node = i0 + i;");
   o.open("switch (t)");
-  for (int k = 0; k < ntask; ++k) o.line(F("case %d: %s%d(%s, node, e_base); break;", k, call.c_str(), k,
-                                          "x, phi, A, G, row_ptr, col, out"));
+  for (int k = 0; k < ntask; ++k)
+    o.line(F("case %d: %s%d(x, phi, A, G, row_ptr, col, out, sm, node, e_base); break;", k, call.c_str(), k));
   o.line("default: break;");
   o.close();
   o.close();
@@ -402,107 +462,160 @@ void emit_node_dispatch(Out& o, const std::string& kname, const std::string& arg
 
 // ------------------------------------------------------------------------------ backward
 
+// Lane swaps of register pairs (a_k, b_k), emitted as inline-assembly blocks: one pair of
+// hazard wait states per block instead of per swap.  `width` is 32 or 16.  Registers are
+// float or double (a double is swapped as its two 32-bit halves).
+void emit_swaps(Out& o, const std::vector<std::pair<std::string, std::string>>& pairs, int width, bool f64) {
+  const int kMaxPerBlock = 14;  // 28 asm operands
+  std::vector<std::pair<std::string, std::string>> regs;
+  if (f64) {
+    o.open("");
+    for (auto& pr : pairs) {
+      for (const std::string* v : {&pr.first, &pr.second}) {
+        o.line(F("unsigned long long b_%s = __builtin_bit_cast(unsigned long long, %s);", v->c_str(), v->c_str()));
+        o.line(F("unsigned l_%s = (unsigned)b_%s, h_%s = (unsigned)(b_%s >> 32);", v->c_str(), v->c_str(), v->c_str(),
+                 v->c_str()));
+      }
+      regs.push_back({"l_" + pr.first, "l_" + pr.second});
+      regs.push_back({"h_" + pr.first, "h_" + pr.second});
+    }
+  } else {
+    regs = pairs;
+  }
+  for (size_t at = 0; at < regs.size(); at += kMaxPerBlock) {
+    size_t n = std::min(regs.size() - at, size_t(kMaxPerBlock));
+    std::string text = "s_nop 1\\n\\t";
+    std::string ops;
+    for (size_t k = 0; k < n; ++k) {
+      text += F("v_permlane%d_swap_b32 %%%d, %%%d\\n\\t", width, int(2 * k), int(2 * k + 1));
+      ops += F("%s\"+v\"(%s), \"+v\"(%s)", k ? ", " : "", regs[at + k].first.c_str(), regs[at + k].second.c_str());
+    }
+    text += "s_nop 1";
+    o.line("asm volatile(\"" + text + "\" : " + ops + ");");
+  }
+  if (f64) {
+    for (auto& pr : pairs)
+      for (const std::string* v : {&pr.first, &pr.second})
+        o.line(F("%s = __builtin_bit_cast(real, (unsigned long long)l_%s | ((unsigned long long)h_%s << 32));",
+                 v->c_str(), v->c_str(), v->c_str()));
+    o.close();
+  }
+}
+
 const char* kRecvArgs =
     "const real* __restrict__ x, const real* __restrict__ phi, const real* __restrict__ A,"
     " const real* __restrict__ G, const int* __restrict__ row_ptr, const int* __restrict__ col,"
     " const real* __restrict__ gout, real* __restrict__ ep, real* __restrict__ ap";
 
-// Receiver-major backward of task (output block k, path subset, channel block) over the
-// receivers [n0, n1).  Per edge: h_pi = <mbar, T_pi> (Eq. 18), phi-bar partials sum_pi A h (Eq. 20)
-// and Y-bar partials sum_pi w sum c x mbar (Eq. 22), reduced over the 64 channels of the wave
-// and stored in slot `ti` of the edge's partial row.  A-bar = sum_e phi h (Eq. 19) accumulates in
-// registers over all edges of the range and is added to the wave's partial slot at the end.
+// Receiver-major backward of task (output block k, path subset, channel block) for one receiver
+// per wave (node < 0: no receiver).  Per edge: h_pi = <mbar, T_pi> (Eq. 18), phi-bar partials
+// sum_pi A h (Eq. 20) and Y-bar partials sum_pi w sum c x mbar (Eq. 22), reduced over the 64
+// channels of the wave and stored in slot `ti` of the edge's partial column.  A-bar = sum_e phi h
+// (Eq. 19) accumulates in registers, is combined over the kRecvGroup waves of the workgroup in
+// LDS and added to the workgroup's partial slot.
 void emit_bwd_recv_task(Out& o, const Plan& p, int ti, const Task& T, int V) {
   const Block& OB = p.out[T.group];
   const int d3 = OB.dim(), MUL = OB.mul, K = p.K;
-  const int ROW = int(recv_backward_tasks(p).size()) * V;
-  o.open(F("DEV void bwr_t%d(%s, int n0, int n1, int e_base, int slot)", ti, kRecvArgs));
-  o.line("const int lane = (int)threadIdx.x;");
+  o.open(F("DEV void bwr_t%d(%s, real* sm, int node, int e_base, int eps, int slot)", ti, kRecvArgs));
+  o.line("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
   o.line(F("const int u = %d + lane;", T.cb * 64));
   o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
   emit_a_loads(o, p, T.paths);
+  std::vector<std::string> aa;
   for (int pi : T.paths)
-    for (int q = 0; q < K; ++q) o.line(F("real aa%d_%d = R(0);", pi, q));
-  o.open("for (int node = n0; node < n1; ++node)");
+    for (int q = 0; q < K; ++q) {
+      o.line(F("real aa%d = R(0);", int(aa.size())));
+      aa.push_back(F("aa%d", int(aa.size())));
+    }
+  o.open("if (node >= 0)");
   o.line(F("const real* __restrict__ gr = gout + (i64)node * %d + %d + uc;", p.c_out, OB.offset));
   for (int m = 0; m < d3; ++m) o.line(F("const real mb%d = u < %d ? gr[%d] : R(0);", m, MUL, m * MUL));
   o.line("const int e0 = row_ptr[node], e1 = row_ptr[node + 1];");
-  o.open("for (int e = e0; e < e1; ++e)");
-  o.line("const int j = col[e];");
-  o.line(F("const real* __restrict__ ph = phi + (i64)e * %d;", K));
-  o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", p.g_stride));
-  o.line(F("const real* __restrict__ xj = x + (i64)j * %d + uc;", p.c_in));
-  for (int q = 0; q < K; ++q) o.line(F("const real f%d = ph[%d];", q, q));
-  emit_x_loads(o, p, T.paths);
-  for (int v = 0; v < V; ++v) o.line(F("real v%d = R(0);", v));
-  for (int pi : T.paths) {
-    const Path& P = p.paths[pi];
-    const int s = K + P.l2 * P.l2;  // Y-bar slot of this path's SH block
-    std::vector<bool> started(d3, false);
-    for (size_t t = 0; t < P.gpairs.size(); ++t) {
-      int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3;
-      if (!started[m3])
-        o.line(F("real t%d_%d = g[%d] * x%d_%d;", pi, m3, P.g_off + int(t), P.i_in, m1));
-      else
-        o.line(F("t%d_%d = fma(g[%d], x%d_%d, t%d_%d);", pi, m3, P.g_off + int(t), P.i_in, m1, pi, m3));
-      started[m3] = true;
-    }
-    bool first = true;
-    for (int m = 0; m < d3; ++m)
-      if (started[m]) {
-        if (first) o.line(F("real h%d = mb%d * t%d_%d;", pi, m, pi, m));
-        else o.line(F("h%d = fma(mb%d, t%d_%d, h%d);", pi, m, pi, m, pi));
-        first = false;
+  emit_recv_edge_loop(o, p, in_blocks_of(p, T.paths), "0", "1", [&] {
+    for (int v = 0; v < V; ++v) o.line(F("real v%d = R(0);", v));
+    int ai = 0;
+    for (int pi : T.paths) {
+      const Path& P = p.paths[pi];
+      const int s = K + P.l2 * P.l2;  // Y-bar slot of this path's SH block
+      std::vector<bool> started(d3, false);
+      for (size_t t = 0; t < P.gpairs.size(); ++t) {
+        int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3;
+        if (!started[m3])
+          o.line(F("real t%d_%d = g[%d] * x%d_%d;", pi, m3, P.g_off + int(t), P.i_in, m1));
+        else
+          o.line(F("t%d_%d = fma(g[%d], x%d_%d, t%d_%d);", pi, m3, P.g_off + int(t), P.i_in, m1, pi, m3));
+        started[m3] = true;
       }
-    emit_w(o, p, pi);
-    for (int q = 0; q < K; ++q) {
-      o.line(F("aa%d_%d = fma(f%d, h%d, aa%d_%d);", pi, q, q, pi, pi, q));
-      o.line(F("v%d = fma(a%d_%d, h%d, v%d);", q, pi, q, pi, q));
+      bool first = true;
+      for (int m = 0; m < d3; ++m)
+        if (started[m]) {
+          if (first) o.line(F("real h%d = mb%d * t%d_%d;", pi, m, pi, m));
+          else o.line(F("h%d = fma(mb%d, t%d_%d, h%d);", pi, m, pi, m, pi));
+          first = false;
+        }
+      emit_w(o, p, pi);
+      for (int q = 0; q < K; ++q, ++ai) {
+        o.line(F("aa%d = fma(f%d, h%d, aa%d);", ai, q, pi, ai));
+        o.line(F("v%d = fma(a%d_%d, h%d, v%d);", q, pi, q, pi, q));
+      }
+      std::set<int> m3used;
+      for (auto& gp : P.gpairs) m3used.insert(gp.m3);
+      for (int m : m3used) o.line(F("const real wm%d_%d = w%d * mb%d;", pi, m, pi, m));
+      for (auto& gp : P.gpairs) {
+        o.line(F("{ const real z = x%d_%d * wm%d_%d;", P.i_in, gp.m1, pi, gp.m3));
+        for (auto& t : gp.terms)
+          o.line(F("  v%d = fma(%s, z, v%d);", s + t.first, lit(t.second).c_str(), s + t.first));
+        o.line("}");
+      }
     }
-    std::set<int> m3used;
-    for (auto& gp : P.gpairs) m3used.insert(gp.m3);
-    for (int m : m3used) o.line(F("const real wm%d_%d = w%d * mb%d;", pi, m, pi, m));
-    for (auto& gp : P.gpairs) {
-      o.line(F("{ const real z = x%d_%d * wm%d_%d;", P.i_in, gp.m1, pi, gp.m3));
-      for (auto& t : gp.terms) o.line(F("  v%d = fma(%s, z, v%d);", s + t.first, lit(t.second).c_str(), s + t.first));
-      o.line("}");
-    }
-  }
-  // Transpose-reduce the V partial sums over the 64 lanes.
-  const int H = V / 2, Q = V / 4;
-  for (int k = 0; k < H; ++k) o.line(F("swap32(v%d, v%d); v%d += v%d;", k, k + H, k, k + H));
-  for (int k = 0; k < Q; ++k) o.line(F("swap16(v%d, v%d); v%d += v%d;", k, k + Q, k, k + Q));
-  for (int k = 0; k < Q; ++k) o.line(F("v%d = rowsum(v%d);", k, k));
-  o.open("if ((lane & 15) == 0)");
-  o.line(F("real* __restrict__ dst = ep + (i64)(e - e_base) * %d + %d + (lane >> 4) * %d;", ROW, ti * V, Q));
-  for (int k = 0; k < Q; ++k) o.line(F("dst[%d] = v%d;", k, k));
-  o.close();
-  o.close();  // edges
-  o.close();  // nodes
-  o.open(F("if (u < %d)", MUL));
+    // Transpose-reduce the V partial sums over the 64 lanes.
+    const int H = V / 2, Q = V / 4;
+    const bool f64 = p.dtype == CGTP_F64;
+    std::vector<std::pair<std::string, std::string>> pr;
+    for (int k = 0; k < H; ++k) pr.push_back({F("v%d", k), F("v%d", k + H)});
+    emit_swaps(o, pr, 32, f64);
+    for (int k = 0; k < H; ++k) o.line(F("v%d += v%d;", k, k + H));
+    pr.clear();
+    for (int k = 0; k < Q; ++k) pr.push_back({F("v%d", k), F("v%d", k + Q)});
+    emit_swaps(o, pr, 16, f64);
+    for (int k = 0; k < Q; ++k) o.line(F("v%d += v%d;", k, k + Q));
+    for (int k = 0; k < Q; ++k) o.line(F("v%d = rowsum(v%d);", k, k));
+    o.open("if ((lane & 15) == 0)");
+    o.line(F("real* __restrict__ dst = ep + (i64)(%d + (lane >> 4) * %d) * eps + (e - e_base);", ti * V, Q));
+    for (int k = 0; k < Q; ++k) o.line(F("dst[(i64)%d * eps] = v%d;", k, k));
+    o.close();
+  });
+  o.close();  // node >= 0
+  emit_wave_combine(o, "aa", int(aa.size()), kRecvGroup);
+  o.open(F("if (w == 0 && u < %d)", MUL));
   o.line(F("real* __restrict__ dst = ap + (i64)slot * %d + u;", K * p.n_w));
+  int ai = 0;
   for (int pi : T.paths)
-    for (int q = 0; q < K; ++q)
-      o.line(F("dst[%d] += aa%d_%d;", q * p.n_w + p.paths[pi].w_off, pi, q));
+    for (int q = 0; q < K; ++q, ++ai) o.line(F("dst[%d] += aa%d;", q * p.n_w + p.paths[pi].w_off, ai));
   o.close();
   o.close();
 }
 
-// Receiver ranges of R nodes per wave: block b -> XCD b & 7, and inside it (task, range).
-void emit_recv_dispatch(Out& o, int ntask) {
-  o.line("extern \"C\" __global__ void __launch_bounds__(64)");
-  o.open(std::string("cgtp_bwd_recv(") + kRecvArgs + ", int i0, int nrec, int per, int nch, int rpw, int e_base)");
+// kRecvGroup consecutive receivers (one wave each) per workgroup: block b -> XCD b & 7, and
+// inside it (task, group of receivers); the group is the A-bar partial slot.
+void emit_recv_dispatch(Out& o, const Plan& p, int ntask) {
+  int amax = 0;
+  for (const Task& t : recv_backward_tasks(p)) amax = std::max(amax, int(t.paths.size()) * p.K);
+  o.line(F("extern \"C\" __global__ void __launch_bounds__(%d)", 64 * kRecvGroup));
+  o.open(std::string("cgtp_bwd_recv(") + kRecvArgs + ", int i0, int nrec, int per, int nch, int e_base, int eps)");
+  o.line(F("__shared__ real sm[%d];", (kRecvGroup - 1) * amax * 64));
   o.line("const int b = (int)blockIdx.x;");
   o.line("const int xcd = b & 7, s = b >> 3;");
   o.line("const int t = s / nch, c = s - t * nch;");
-  o.line("const int lo = xcd * per + c * rpw;");
-  o.line("int hi = lo + rpw; if (hi > (xcd + 1) * per) hi = (xcd + 1) * per; if (hi > nrec) hi = nrec;");
+  o.line(F("const int lo = xcd * per + c * %d;", kRecvGroup));
+  o.line(F("int hi = lo + %d; if (hi > (xcd + 1) * per) hi = (xcd + 1) * per; if (hi > nrec) hi = nrec;", kRecvGroup));
   o.line("if (lo >= hi) return;");
+  o.line("const int r = lo + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
+  o.line("const int node = r < hi ? i0 + r : -1;");
   o.line("const int slot = xcd * nch + c;");
   o.open("switch (t)");
   for (int k = 0; k < ntask; ++k)
-    o.line(F("case %d: bwr_t%d(x, phi, A, G, row_ptr, col, gout, ep, ap, i0 + lo, i0 + hi, e_base, slot); break;",
-             k, k));
+    o.line(F("case %d: bwr_t%d(x, phi, A, G, row_ptr, col, gout, ep, ap, sm, node, e_base, eps, slot); break;", k, k));
   o.line("default: break;");
   o.close();
   o.close();
@@ -514,29 +627,44 @@ const char* kSrcArgs =
     " const int* __restrict__ src_edge, real* __restrict__ gx";
 
 // Source-major x-bar of task (input block b, channel block cb) for one sender (Eq. 21):
-// x-bar_j[m1] = sum over out-edges, paths of w_pi sum_m3 G[m1,m3] mbar_i[m3].
+// x-bar_j[m1] = sum over out-edges, paths of w_pi sum_m3 G[m1,m3] mbar_i[m3].  The out-edges are
+// dealt round-robin to the kSrcSplit waves of the workgroup (partials combined in LDS); the
+// receivers' mbar rows of the next edge are loaded one edge ahead.
 void emit_bwd_src_task(Out& o, const Plan& p, int ti, const Task& T) {
   const Block& IB = p.in[T.group];
   const int d1 = IB.dim(), MUL = IB.mul, K = p.K;
-  o.open(F("DEV void bws_t%d(%s, int node, int e_base, int accumulate)", ti, kSrcArgs));
-  o.line(F("const int u = %d + (int)threadIdx.x;", T.cb * 64));
+  o.open(F("DEV void bws_t%d(%s, real* sm, int node, int e_base, int accumulate)", ti, kSrcArgs));
+  o.line("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
+  o.line(F("const int u = %d + lane;", T.cb * 64));
   o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
   for (int m = 0; m < d1; ++m) o.line(F("real acc%d = R(0);", m));
   o.line("const int s0 = src_ptr[node], s1 = src_ptr[node + 1];");
   for (const auto& S : subsets(p, T.paths)) {
     o.open("");
     emit_a_loads(o, p, S);
-    o.open("for (int k = s0; k < s1; ++k)");
-    o.line("const int e = src_edge[k];");
-    o.line("const int i = recv[e];");
+    const auto obs = out_blocks_of(p, S);
+    o.line("int k = s0 + w;");
+    o.open("if (k < s1)");
+    o.line("int en = src_edge[k];");
+    o.line("int in_ = recv[en];");
+    for (int ob : obs) {
+      const Block& B = p.out[ob];
+      for (int m = 0; m < B.dim(); ++m)
+        o.line(F("real mn%d_%d = gout[(i64)in_ * %d + %d + uc];", ob, m, p.c_out, B.offset + m * B.mul));
+    }
+    o.open(F("for (; k < s1; k += %d)", kSrcSplit));
+    o.line("const int e = en;");
+    for (int ob : obs)
+      for (int m = 0; m < p.out[ob].dim(); ++m) o.line(F("const real mb%d_%d = mn%d_%d;", ob, m, ob, m));
+    o.line(F("{ const int kn = k + %d; en = src_edge[kn < s1 ? kn : k]; in_ = recv[en]; }", kSrcSplit));
+    for (int ob : obs) {
+      const Block& B = p.out[ob];
+      for (int m = 0; m < B.dim(); ++m)
+        o.line(F("mn%d_%d = gout[(i64)in_ * %d + %d + uc];", ob, m, p.c_out, B.offset + m * B.mul));
+    }
     o.line(F("const real* __restrict__ ph = phi + (i64)e * %d;", K));
     o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", p.g_stride));
-    o.line(F("const real* __restrict__ gi = gout + (i64)i * %d + uc;", p.c_out));
     for (int q = 0; q < K; ++q) o.line(F("const real f%d = ph[%d];", q, q));
-    for (int ob : out_blocks_of(p, S)) {
-      const Block& B = p.out[ob];
-      for (int m = 0; m < B.dim(); ++m) o.line(F("const real mb%d_%d = gi[%d];", ob, m, B.offset + m * B.mul));
-    }
     for (int pi : S) {
       const Path& P = p.paths[pi];
       const int d3 = 2 * P.l3 + 1;
@@ -562,8 +690,10 @@ void emit_bwd_src_task(Out& o, const Plan& p, int ti, const Task& T) {
     }
     o.close();
     o.close();
+    o.close();
   }
-  o.open(F("if (u < %d)", MUL));
+  emit_wave_combine(o, "acc", d1, kSrcSplit);
+  o.open(F("if (w == 0 && u < %d)", MUL));
   o.line(F("real* __restrict__ dst = gx + (i64)node * %d + %d + u;", p.c_in, IB.offset));
   o.open("if (accumulate)");
   for (int m = 0; m < d1; ++m) o.line(F("dst[%d] += acc%d;", m * MUL, m));
@@ -575,9 +705,10 @@ void emit_bwd_src_task(Out& o, const Plan& p, int ti, const Task& T) {
   o.close();
 }
 
-void emit_src_dispatch(Out& o, int ntask) {
-  o.line("extern \"C\" __global__ void __launch_bounds__(64)");
+void emit_src_dispatch(Out& o, const Plan& p, int ntask) {
+  o.line(F("extern \"C\" __global__ void __launch_bounds__(%d)", 64 * kSrcSplit));
   o.open(std::string("cgtp_bwd_src(") + kSrcArgs + ", int nrec, int per, int e_base, int accumulate)");
+  o.line(F("__shared__ real sm[%d];", (kSrcSplit - 1) * max_in_dim(p) * 64));
   o.line("const int b = (int)blockIdx.x;");
   o.line("const int xcd = b & 7, s = b >> 3;");
   o.line("const int t = s / per, il = s - t * per;");
@@ -585,8 +716,8 @@ void emit_src_dispatch(Out& o, int ntask) {
   o.line("if (node >= nrec) return;");
   o.open("switch (t)");
   for (int k = 0; k < ntask; ++k)
-    o.line(F("case %d: bws_t%d(phi, A, G, gout, recv, src_ptr, src_edge, gx, node, e_base, accumulate); break;", k,
-             k));
+    o.line(F("case %d: bws_t%d(phi, A, G, gout, recv, src_ptr, src_edge, gx, sm, node, e_base, accumulate); break;",
+             k, k));
   o.line("default: break;");
   o.close();
   o.close();
@@ -595,18 +726,19 @@ void emit_src_dispatch(Out& o, int ntask) {
 // Per-edge finalisation: phi-bar and Y-bar = fixed-order sums of the task partials, then the
 // edge-vector gradient e-bar = J_Y(r)^T Y-bar with J_Y = (I - n n^T) dY/dn / |r|.
 void emit_edge_final(Out& o, const Plan& p, int ntask, int V) {
-  const int K = p.K, ROW = ntask * V;
+  const int K = p.K;
   o.line("extern \"C\" __global__ void __launch_bounds__(256)");
   o.open("cgtp_edge_final(const real* __restrict__ pos, const real* __restrict__ shift, const int* __restrict__ recv,"
-         " const int* __restrict__ send, const real* __restrict__ ep, int e0, int e1, real* __restrict__ gphi,"
-         " real* __restrict__ gev)");
+         " const int* __restrict__ send, const real* __restrict__ ep, int e0, int e1, int eps,"
+         " real* __restrict__ gphi, real* __restrict__ gev)");
   o.line("const int e = e0 + (int)(blockIdx.x * 256 + threadIdx.x);");
   o.line("if (e >= e1) return;");
-  o.line(F("const real* __restrict__ row = ep + (i64)(e - e0) * %d;", ROW));
+  o.line("const real* __restrict__ col0 = ep + (e - e0);");
+  o.line("#define ROWV(k) col0[(i64)(k) * eps]");
   o.open("if (gphi)");
   for (int q = 0; q < K; ++q) {
-    std::string ex = F("row[%d]", q);
-    for (int t = 1; t < ntask; ++t) ex += F(" + row[%d]", t * V + q);
+    std::string ex = F("ROWV(%d)", q);
+    for (int t = 1; t < ntask; ++t) ex += F(" + ROWV(%d)", t * V + q);
     o.line(F("gphi[(i64)e * %d + %d] = ", K, q) + ex + ";");
   }
   o.close();
@@ -618,8 +750,8 @@ void emit_edge_final(Out& o, const Plan& p, int ntask, int V) {
   o.line("sh_eval<D3>(D3(nx, R(1), R(0), R(0)), D3(ny, R(0), R(1), R(0)), D3(nz, R(0), R(0), R(1)), Y);");
   o.line("real gx = R(0), gy = R(0), gz = R(0);");
   for (int m = 0; m < p.sh_dim; ++m) {
-    std::string ex = F("row[%d]", K + m);
-    for (int t = 1; t < ntask; ++t) ex += F(" + row[%d]", t * V + K + m);
+    std::string ex = F("ROWV(%d)", K + m);
+    for (int t = 1; t < ntask; ++t) ex += F(" + ROWV(%d)", t * V + K + m);
     o.line(F("{ const real yb = ") + ex + F("; gx = fma(yb, Y[%d].x, gx); gy = fma(yb, Y[%d].y, gy);"
                                              " gz = fma(yb, Y[%d].z, gz); }", m, m, m));
   }
@@ -627,34 +759,52 @@ void emit_edge_final(Out& o, const Plan& p, int ntask, int V) {
   o.line("gev[3 * (i64)e] = (gx - nx * d) * inv;");
   o.line("gev[3 * (i64)e + 1] = (gy - ny * d) * inv;");
   o.line("gev[3 * (i64)e + 2] = (gz - nz * d) * inv;");
+  o.line("#undef ROWV");
   o.close();
 }
 
 void emit_small_kernels(Out& o) {
-  // pos-bar_i = sum over out-edges of e-bar - sum over in-edges of e-bar (fixed CSR order).
-  o.line("extern \"C\" __global__ void __launch_bounds__(256)");
+  // Sum over the 64 lanes of a wave, the same value in every lane (fixed order).
+  o.line("DEV real wave_total(real v) {");
+  o.line("  v = rowsum(v);");
+  o.line("  return (__shfl_rd(v, 0) + __shfl_rd(v, 16)) + (__shfl_rd(v, 32) + __shfl_rd(v, 48));");
+  o.line("}");
+  // pos-bar_i = sum over out-edges of e-bar - sum over in-edges of e-bar; one wave per node, lanes
+  // stride the edge lists, then a fixed-order wave reduction.
+  o.line("extern \"C\" __global__ void __launch_bounds__(64)");
   o.open("cgtp_pos_grad(const real* __restrict__ gev, const int* __restrict__ row_ptr,"
          " const int* __restrict__ src_ptr, const int* __restrict__ src_edge, int n, real* __restrict__ gpos)");
-  o.line("const int i = (int)(blockIdx.x * 256 + threadIdx.x);");
+  o.line("const int i = (int)blockIdx.x, lane = (int)threadIdx.x;");
   o.line("if (i >= n) return;");
   o.line("real sx = R(0), sy = R(0), sz = R(0);");
-  o.open("for (int k = src_ptr[i]; k < src_ptr[i + 1]; ++k)");
+  o.open("for (int k = src_ptr[i] + lane; k < src_ptr[i + 1]; k += 64)");
   o.line("const i64 e = src_edge[k];");
   o.line("sx += gev[3 * e]; sy += gev[3 * e + 1]; sz += gev[3 * e + 2];");
   o.close();
-  o.open("for (i64 e = row_ptr[i]; e < row_ptr[i + 1]; ++e)");
-  o.line("sx -= gev[3 * e]; sy -= gev[3 * e + 1]; sz -= gev[3 * e + 2];");
+  o.open("for (int e = row_ptr[i] + lane; e < row_ptr[i + 1]; e += 64)");
+  o.line("sx -= gev[3 * (i64)e]; sy -= gev[3 * (i64)e + 1]; sz -= gev[3 * (i64)e + 2];");
   o.close();
-  o.line("gpos[3 * (i64)i] = sx; gpos[3 * (i64)i + 1] = sy; gpos[3 * (i64)i + 2] = sz;");
+  o.line("sx = wave_total(sx); sy = wave_total(sy); sz = wave_total(sz);");
+  o.line("if (lane == 0) { gpos[3 * (i64)i] = sx; gpos[3 * (i64)i + 1] = sy; gpos[3 * (i64)i + 2] = sz; }");
   o.close();
-  // A-bar = sum over wave slots of the partials, slot order fixed.
+  // A-bar = sum over wave slots of the partials: block = 64 outputs x 4 slot quarters, combined in
+  // LDS in a fixed order.
   o.line("extern \"C\" __global__ void __launch_bounds__(256)");
   o.open("cgtp_a_reduce(const real* __restrict__ ap, int nslot, int n, real* __restrict__ gA)");
-  o.line("const int k = (int)(blockIdx.x * 256 + threadIdx.x);");
-  o.line("if (k >= n) return;");
-  o.line("real s = R(0);");
-  o.line("for (int w = 0; w < nslot; ++w) s += ap[(i64)w * n + k];");
-  o.line("gA[k] = s;");
+  o.line("__shared__ real part[4][64];");
+  o.line("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
+  o.line("const int k = (int)blockIdx.x * 64 + lane;");
+  o.line("const int q = (nslot + 3) / 4, s0 = w * q, s1 = min(nslot, s0 + q);");
+  o.line("real a0 = R(0), a1 = R(0), a2 = R(0), a3 = R(0);");
+  o.open("if (k < n)");
+  o.line("int s = s0;");
+  o.line("for (; s + 3 < s1; s += 4) { a0 += ap[(i64)s * n + k]; a1 += ap[(i64)(s + 1) * n + k];"
+         " a2 += ap[(i64)(s + 2) * n + k]; a3 += ap[(i64)(s + 3) * n + k]; }");
+  o.line("for (; s < s1; ++s) a0 += ap[(i64)s * n + k];");
+  o.close();
+  o.line("part[w][lane] = (a0 + a1) + (a2 + a3);");
+  o.line("__syncthreads();");
+  o.line("if (w == 0 && k < n) gA[k] = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);");
   o.close();
 }
 
@@ -709,7 +859,7 @@ std::string generate_source(const Plan& p, const std::string& family, std::strin
       if (streamed) emit_fwd_streamed_task(o, p, k, tasks[k]);
       else emit_fwd_task(o, p, k, tasks[k]);
     }
-    emit_node_dispatch(o, streamed ? "cgtp_fwd_streamed" : "cgtp_fwd", kFwdArgs, streamed ? "fwds_t" : "fwd_t",
+    emit_node_dispatch(o, p, streamed ? "cgtp_fwd_streamed" : "cgtp_fwd", kFwdArgs, streamed ? "fwds_t" : "fwd_t",
                        int(tasks.size()));
     return o.s.str();
   }
@@ -720,10 +870,10 @@ std::string generate_source(const Plan& p, const std::string& family, std::strin
     const int V = edge_partial_width(p);
     auto rt = recv_backward_tasks(p);
     for (int k = 0; k < int(rt.size()); ++k) emit_bwd_recv_task(o, p, k, rt[k], V);
-    emit_recv_dispatch(o, int(rt.size()));
+    emit_recv_dispatch(o, p, int(rt.size()));
     auto st = source_tasks(p);
     for (int k = 0; k < int(st.size()); ++k) emit_bwd_src_task(o, p, k, st[k]);
-    emit_src_dispatch(o, int(st.size()));
+    emit_src_dispatch(o, p, int(st.size()));
     emit_edge_final(o, p, int(rt.size()), V);
     emit_small_kernels(o);
     return o.s.str();
