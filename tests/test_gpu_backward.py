@@ -106,3 +106,10 @@ def test_backward_config2_full_size():
     err = rel_err(got["A"], full["A"].numpy())
     print(f"config 2 grad A (full): rel err {err:.3e}", flush=True)
     assert err <= TOL["float32"]
+
+
+def test_backward_config5_reduced_full():
+    """l <= 6, 32 channels, 16 radial functions, 200 atoms: every gradient in full."""
+    case = make_case(5, n_nodes=200)
+    g = _gpu(case)
+    _compare(g.backward(), _oracle_full(case), "float32", label="config 5 reduced")

@@ -115,3 +115,29 @@ def test_forward_empty_graph_gives_zeros():
     A = torch.randn(4, plan.info["n_weights"], **dev)
     out = c.forward(x, pos, None, phi, A)
     assert torch.count_nonzero(out).item() == 0
+
+
+def test_forward_config5_reduced_full():
+    """l <= 6, 32 channels (half-masked waves), 16 Gaussian radial functions, 200 atoms."""
+    from clebsch_gordan_tensor_receiver_amd import _lib
+    from tests.gpu_helpers import TOL, rel_err
+    case = make_case(5, n_nodes=200)
+    g = _gpu(case)
+    ref = conv.forward_conventional(case.problem, case.x, case.edge_vec, case.recv, case.send, case.phi,
+                                    case.A).numpy()
+    for sch, name in ((_lib.CONVENTIONAL, "conventional"), (_lib.STREAMED, "streamed")):
+        out = g.forward(sch).cpu().numpy()
+        err = rel_err(out, ref)
+        print(f"config 5 reduced {name} rel err {err:.3e}", flush=True)
+        assert err <= TOL["float32"]
+
+
+def test_forward_config5_full_size_sampled():
+    from tests.gpu_helpers import TOL, rel_err
+    case = make_case(5)
+    g = _gpu(case)
+    out = g.forward().cpu().numpy()
+    rows = _sample_receivers(case, 24, seed=5)
+    err = rel_err(out[rows], _oracle_rows(case, rows))
+    print(f"config 5 sampled rel err {err:.3e}", flush=True)
+    assert err <= TOL["float32"]
