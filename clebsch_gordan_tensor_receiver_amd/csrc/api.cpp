@@ -11,6 +11,7 @@
 #include "graph.hpp"
 #include "kernels.hpp"
 #include "plan.hpp"
+#include "uvw_launch.hpp"
 
 struct cgtp_plan_s {
   cgtp::Plan p;
@@ -97,6 +98,23 @@ BwdLayout bwd_layout(const cgtp::Plan& p, const cgtp::Graph& g) {
   off += align256(size_t(std::max(g.e, 1)) * 3 * p.elem());
   L.total = off;
   return L;
+}
+
+// Feature blocks that no path reaches (output side) or leaves (input side) are not written by
+// the kernels; zero the whole tensor first when such a block exists.
+cgtp_status_t zero_unreached(cgtp::Plan& p, void* buf, int n, bool out_side, hipStream_t s, std::string* err) {
+  const auto& blocks = out_side ? p.out : p.in;
+  const auto& by = out_side ? p.by_out : p.by_in;
+  bool any = false;
+  for (size_t k = 0; k < blocks.size(); ++k) any = any || by[k].empty();
+  if (!any) return CGTP_OK;
+  const char* fam = p.mode == CGTP_CHANNELWISE ? "fwd" : "uvw_fwd";
+  hipFunction_t kz;
+  cgtp_status_t st = cgtp::get_kernel(p, fam, "cgtp_fill_zero", &kz, err);
+  if (st != CGTP_OK) return st;
+  long long cnt = (long long)n * (out_side ? p.c_out : p.c_in);
+  void* a[] = {&buf, &cnt};
+  return cgtp::launch(kz, unsigned((cnt + 255) / 256), 256, 0, s, a, err);
 }
 
 }  // namespace
@@ -199,6 +217,9 @@ cgtp_status_t cgtp_plan_compile(cgtp_plan_t plan, int ops) {
       fams.push_back("fwds");
     }
     if (ops & (1 << CGTP_OP_BACKWARD)) fams.push_back("bwd");
+  } else {
+    if (ops & (1 << CGTP_OP_FORWARD)) fams.push_back("uvw_fwd");
+    if (ops & (1 << CGTP_OP_BACKWARD)) fams.push_back("uvw_bwd");
   }
   for (auto& f : fams) {
     cgtp_status_t st = cgtp::compile_family(plan->p, f, &err);
@@ -271,6 +292,11 @@ cgtp_status_t cgtp_workspace_size(cgtp_plan_t plan, cgtp_graph_t g, cgtp_op_t op
   const cgtp::Plan& p = plan->p;
   const cgtp::Graph& G = g->g;
   size_t need = 0;
+  if (p.mode == CGTP_FULLY_CONNECTED) {
+    if (op == CGTP_OP_DOUBLE_BACKWARD) return fail(CGTP_ERR_UNSUPPORTED, "double backward is channelwise only");
+    *bytes = std::max<size_t>(cgtp::uvw_workspace(p, G, op), 256);
+    return ok();
+  }
   if (op == CGTP_OP_FORWARD) {
     auto ch = G.chunks(g_chunk_edges(p, G));
     need = align256(size_t(max_chunk_edges(G, ch)) * size_t(p.g_stride) * p.elem());
@@ -291,7 +317,6 @@ cgtp_status_t cgtp_conv_forward(cgtp_plan_t plan, cgtp_graph_t g, cgtp_schedule_
   if (schedule != CGTP_STREAMED && schedule != CGTP_CONVENTIONAL) return fail(CGTP_ERR_INVALID_ARG, "bad schedule");
   cgtp::Plan& p = plan->p;
   cgtp::Graph& G = g->g;
-  if (p.mode != CGTP_CHANNELWISE) return fail(CGTP_ERR_UNSUPPORTED, "fully connected forward not built yet");
   size_t need = 0;
   cgtp_workspace_size(plan, g, CGTP_OP_FORWARD, &need);
   if (ws_bytes < need || (!workspace && need > 0)) return fail(CGTP_ERR_WORKSPACE, "workspace too small");
@@ -299,6 +324,15 @@ cgtp_status_t cgtp_conv_forward(cgtp_plan_t plan, cgtp_graph_t g, cgtp_schedule_
   cgtp::DeviceGraph d;
   cgtp_status_t st = cgtp::device_graph(G, &d, &err);
   if (st != CGTP_OK) return fail(st, err);
+  hipStream_t s0 = static_cast<hipStream_t>(stream);
+  if ((st = zero_unreached(p, out, G.n, true, s0, &err)) != CGTP_OK) return fail(st, err);
+  if (p.mode == CGTP_FULLY_CONNECTED) {
+    if (schedule != CGTP_STREAMED)
+      return fail(CGTP_ERR_UNSUPPORTED, "fully connected mode runs the streamed schedule only: the conventional one "
+                                        "would materialise E x N_w edge weights");
+    st = cgtp::uvw_forward(p, G, d, x, pos, shift, phi, A, out, workspace, s0, &err);
+    return st == CGTP_OK ? ok() : fail(st, err);
+  }
   const char* fam = schedule == CGTP_STREAMED ? "fwds" : "fwd";
   hipFunction_t kprep, kfwd;
   if ((st = cgtp::get_kernel(p, fam, "cgtp_prep", &kprep, &err)) != CGTP_OK) return fail(st, err);
@@ -338,14 +372,22 @@ cgtp_status_t cgtp_conv_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x
   if (!x || !pos || !phi || !A || !grad_out) return fail(CGTP_ERR_INVALID_ARG, "null input tensor");
   cgtp::Plan& p = plan->p;
   cgtp::Graph& G = g->g;
-  if (p.mode != CGTP_CHANNELWISE) return fail(CGTP_ERR_UNSUPPORTED, "fully connected backward not built yet");
   if (!grad_x && !grad_pos && !grad_edge_vec && !grad_phi && !grad_A) return ok();
-  BwdLayout L = bwd_layout(p, G);
-  if (!workspace || ws_bytes < L.total) return fail(CGTP_ERR_WORKSPACE, "workspace too small");
+  size_t need = 0;
+  cgtp_workspace_size(plan, g, CGTP_OP_BACKWARD, &need);
+  if (!workspace || ws_bytes < need) return fail(CGTP_ERR_WORKSPACE, "workspace too small");
   std::string err;
   cgtp::DeviceGraph d;
   cgtp_status_t st = cgtp::device_graph(G, &d, &err);
   if (st != CGTP_OK) return fail(st, err);
+  if (grad_x && (st = zero_unreached(p, grad_x, G.n, false, static_cast<hipStream_t>(stream), &err)) != CGTP_OK)
+    return fail(st, err);
+  if (p.mode == CGTP_FULLY_CONNECTED) {
+    st = cgtp::uvw_backward(p, G, d, nullptr, x, pos, shift, phi, A, grad_out, grad_x, grad_pos, grad_edge_vec,
+                            grad_phi, grad_A, workspace, static_cast<hipStream_t>(stream), &err);
+    return st == CGTP_OK ? ok() : fail(st, err);
+  }
+  BwdLayout L = bwd_layout(p, G);
   const cgtp::SourceViews* views = nullptr;
   if (grad_x && (st = cgtp::source_views(G, L.cap, &views, &err)) != CGTP_OK) return fail(st, err);
   hipFunction_t kzero, kprep, krecv, ksrc, kfinal, kpos, kred;

@@ -27,46 +27,19 @@
 //   a_reduce:                   fixed-order sum of the per-wave A-bar partials.
 #include <algorithm>
 #include <cmath>
-#include <cstdarg>
+
 #include <cstdio>
 #include <functional>
 #include <numeric>
 #include <set>
 #include <sstream>
 
+#include "codegen.hpp"
 #include "kernels.hpp"
 #include "plan.hpp"
 
 namespace cgtp {
-namespace {
-
-std::string F(const char* fmt, ...) {
-  char buf[2048];
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
-  va_end(ap);
-  return buf;
-}
-
-std::string lit(double v) { return F("R(%.17g)", v); }
-
-struct Out {
-  std::ostringstream s;
-  int ind = 0;
-  void line(const std::string& t) {
-    for (int k = 0; k < ind; ++k) s << "  ";
-    s << t << "\n";
-  }
-  void open(const std::string& t) {
-    line(t + " {");
-    ++ind;
-  }
-  void close(const std::string& t = "}") {
-    --ind;
-    line(t);
-  }
-};
+namespace gen {
 
 long double dfact(int n) {  // n!!
   long double r = 1;
@@ -305,7 +278,8 @@ constexpr int kRecvGroup = 4;  // receivers (one wave each) per workgroup in the
 // pipelining), so their latency overlaps the arithmetic of the current edge.  The body sees
 // e, j, g (G row), f<q> (phi) and x<b>_<m>.
 void emit_recv_edge_loop(Out& o, const Plan& p, const std::vector<int>& blocks, const std::string& start,
-                         const std::string& stride, const std::function<void()>& body) {
+                         const std::string& stride, const std::function<void()>& body, bool block_uc) {
+  auto ucn = [&](int b) { return block_uc ? F("uc%d", b) : std::string("uc"); };
   o.open("");
   o.line("int e = e0 + " + start + ";");
   o.open("if (e < e1)");
@@ -313,7 +287,7 @@ void emit_recv_edge_loop(Out& o, const Plan& p, const std::vector<int>& blocks, 
   for (int b : blocks) {
     const Block& B = p.in[b];
     for (int m = 0; m < B.dim(); ++m)
-      o.line(F("real xn%d_%d = x[(i64)jn * %d + %d + uc];", b, m, p.c_in, B.offset + m * B.mul));
+      o.line(F("real xn%d_%d = x[(i64)jn * %d + %d + %s];", b, m, p.c_in, B.offset + m * B.mul, ucn(b).c_str()));
   }
   o.open("for (; e < e1; e += " + stride + ")");
   o.line("const int j = jn;");
@@ -323,7 +297,7 @@ void emit_recv_edge_loop(Out& o, const Plan& p, const std::vector<int>& blocks, 
   for (int b : blocks) {
     const Block& B = p.in[b];
     for (int m = 0; m < B.dim(); ++m)
-      o.line(F("xn%d_%d = x[(i64)jn * %d + %d + uc];", b, m, p.c_in, B.offset + m * B.mul));
+      o.line(F("xn%d_%d = x[(i64)jn * %d + %d + %s];", b, m, p.c_in, B.offset + m * B.mul, ucn(b).c_str()));
   }
   o.line(F("const real* __restrict__ ph = phi + (i64)e * %d;", p.K));
   o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", p.g_stride));
@@ -808,7 +782,9 @@ void emit_small_kernels(Out& o) {
   o.close();
 }
 
-}  // namespace
+}  // namespace gen
+
+using namespace gen;
 
 std::vector<Task> forward_tasks(const Plan& p) {
   std::vector<int> order(p.out.size());
@@ -845,10 +821,7 @@ int edge_partial_width(const Plan& p) { return (p.K + p.sh_dim + 3) / 4 * 4; }
 
 std::string generate_source(const Plan& p, const std::string& family, std::string* err) {
   Out o;
-  if (p.mode != CGTP_CHANNELWISE) {
-    *err = "fully connected kernels are not generated yet";
-    return "";
-  }
+  if (p.mode != CGTP_CHANNELWISE) return generate_uvw_source(p, family, err);
   if (family == "fwd" || family == "fwds") {
     prelude(o, p, false, false);
     emit_sh(o, p.lmax);
@@ -862,6 +835,10 @@ std::string generate_source(const Plan& p, const std::string& family, std::strin
     emit_node_dispatch(o, p, streamed ? "cgtp_fwd_streamed" : "cgtp_fwd", kFwdArgs, streamed ? "fwds_t" : "fwd_t",
                        int(tasks.size()));
     return o.s.str();
+  }
+  if (family == "uvw_fwd" || family == "uvw_bwd") {
+    *err = "fully connected families are generated by generate_uvw_source";
+    return "";
   }
   if (family == "bwd") {
     prelude(o, p, true, true);

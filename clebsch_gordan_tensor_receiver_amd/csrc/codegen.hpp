@@ -1,0 +1,67 @@
+// Internal helpers shared by the kernel source generators (codegen.cpp: channelwise kernels and
+// the shared edge/SH kernels; codegen_uvw.cpp: fully connected kernels).
+#pragma once
+
+#include <cstdarg>
+#include <cstdio>
+#include <functional>
+#include <sstream>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "kernels.hpp"
+#include "plan.hpp"
+
+namespace cgtp {
+namespace gen {
+
+inline std::string F(const char* fmt, ...) {
+  char buf[4096];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  return buf;
+}
+
+inline std::string lit(double v) { return F("R(%.17g)", v); }
+
+// Indented source text.
+struct Out {
+  std::ostringstream s;
+  int ind = 0;
+  void line(const std::string& t) {
+    for (int k = 0; k < ind; ++k) s << "  ";
+    s << t << "\n";
+  }
+  void open(const std::string& t) {
+    line(t + " {");
+    ++ind;
+  }
+  void close(const std::string& t = "}") {
+    --ind;
+    line(t);
+  }
+};
+
+std::vector<std::vector<int>> subsets(const Plan& p, const std::vector<int>& paths);
+void prelude(Out& o, const Plan& p, bool dual, bool reduce);
+void emit_sh(Out& o, int L);
+void emit_edge_vector(Out& o);
+void emit_prep(Out& o, const Plan& p);
+std::vector<int> in_blocks_of(const Plan& p, const std::vector<int>& paths);
+std::vector<int> out_blocks_of(const Plan& p, const std::vector<int>& paths);
+void emit_recv_edge_loop(Out& o, const Plan& p, const std::vector<int>& blocks, const std::string& start,
+                         const std::string& stride, const std::function<void()>& body, bool block_uc = false);
+void emit_wave_combine(Out& o, const std::string& prefix, int n, int nw);
+void emit_swaps(Out& o, const std::vector<std::pair<std::string, std::string>>& pairs, int width, bool f64);
+void emit_edge_final(Out& o, const Plan& p, int ntask, int V);
+void emit_small_kernels(Out& o);
+
+}  // namespace gen
+
+// Fully connected (uvw) kernel families "uvw_fwd" and "uvw_bwd".
+std::string generate_uvw_source(const Plan& p, const std::string& family, std::string* err);
+
+}  // namespace cgtp

@@ -1,0 +1,618 @@
+// Fully connected (uvw) kernels: the streamed schedule of Sobek section 4.2-4.3.
+//
+// Forward (Eqs. 32-35), per output block g:
+//   uvw_state (lane = input channel u): S_i[(m3)][(pi, q, u)] = sum_j phi_ij,q C_pi,u,m3(x_j, Y_ij),
+//       accumulated in registers over the receiver's edges, written as rows of a receiver-chunk
+//       matrix S_g (rows (i, m3), columns (pi, q, u));
+//   gemm_fwd_g (MFMA): m_g = S_g A_g with A_g[(pi, q, u)][w] = A[q, w_off_pi + u C_out + w].
+// Backward (Eq. 36 and its edge/source parts), per receiver chunk:
+//   uvw_state again (S), gemm_sbar_g: Sbar_g = mbar_g A_g^T, gemm_abar_g: A-bar_g += S_g^T mbar_g
+//   (split over rows, partials summed in a fixed order);
+//   uvw_edge (lane = u): per edge phi-bar_q = sum Sbar[q] C and Y-bar from
+//   Cbar[m3] = sum_q phi_q Sbar[q][m3], reduced over channels; edge_final and pos_grad as in the
+//   channelwise path.
+// and per sender chunk (x-bar without edge-sized buffers): the source-side state
+//   Z_j[(m1)][(pi, q, w)] = sum_{e: j -> i} phi_e,q sum_m3 G_e[m1, m3] mbar_i[m3][w]
+//   (uvw_zstate, lane = output channel w, over the source CSR), then gemm_xbar_b:
+//   x-bar_j[m1][u] = sum_{(pi, q, w)} Z_j[m1][(pi, q, w)] A[q, w_off_pi + u C_out + w].
+#include <algorithm>
+#include <set>
+
+#include "codegen.hpp"
+
+namespace cgtp {
+
+using namespace gen;
+
+namespace {
+
+constexpr int kStateBudget = 128;  // receiver/source state registers per lane per task
+
+struct Side {                 // one output block (receiver side) or input block (source side)
+  int blk;                    // block index
+  std::vector<int> paths;
+  int d;                      // 2l + 1 of the block
+  int mul;                    // channels of the block
+  std::vector<int> col_off;   // per path: first column of the path in a state row
+  std::vector<int> cmul;      // per path: channels along the state columns (mul_in or mul_out)
+  int D = 0, ld = 0;          // columns and padded row stride
+};
+
+std::vector<Side> recv_sides(const Plan& p) {
+  std::vector<Side> v;
+  for (int k = 0; k < int(p.out.size()); ++k) {
+    if (p.by_out[k].empty()) continue;
+    Side s{k, p.by_out[k], p.out[k].dim(), p.out[k].mul, {}, {}};
+    for (int pi : s.paths) {
+      s.col_off.push_back(s.D);
+      s.cmul.push_back(p.in[p.paths[pi].i_in].mul);
+      s.D += p.K * p.in[p.paths[pi].i_in].mul;
+    }
+    s.ld = (s.D + 3) / 4 * 4;
+    v.push_back(s);
+  }
+  return v;
+}
+
+std::vector<Side> send_sides(const Plan& p) {
+  std::vector<Side> v;
+  for (int k = 0; k < int(p.in.size()); ++k) {
+    if (p.by_in[k].empty()) continue;
+    Side s{k, p.by_in[k], p.in[k].dim(), p.in[k].mul, {}, {}};
+    for (int pi : s.paths) {
+      s.col_off.push_back(s.D);
+      s.cmul.push_back(p.out[p.paths[pi].i_out].mul);
+      s.D += p.K * p.out[p.paths[pi].i_out].mul;
+    }
+    s.ld = (s.D + 3) / 4 * 4;
+    v.push_back(s);
+  }
+  return v;
+}
+
+struct StateTask {
+  int side;                  // index into recv_sides / send_sides
+  std::vector<int> idx;      // indices into side.paths
+  int cb;
+};
+
+std::vector<StateTask> state_tasks(const Plan& p, const std::vector<Side>& sides, int budget_per_path_fn(const Plan&, const Side&, int)) {
+  std::vector<StateTask> t;
+  for (int s = 0; s < int(sides.size()); ++s) {
+    const Side& S = sides[s];
+    std::vector<std::vector<int>> groups;
+    int used = 0;
+    for (int k = 0; k < int(S.paths.size()); ++k) {
+      int cost = budget_per_path_fn(p, S, k);
+      if (groups.empty() || used + cost > kStateBudget) {
+        groups.push_back({});
+        used = 0;
+      }
+      groups.back().push_back(k);
+      used += cost;
+    }
+    for (auto& g : groups) {
+      int mmax = 0;
+      for (int k : g) mmax = std::max(mmax, S.cmul[k]);
+      for (int cb = 0; cb < (mmax + 63) / 64; ++cb) t.push_back({s, g, cb});
+    }
+  }
+  return t;
+}
+
+int recv_state_cost(const Plan& p, const Side& S, int) { return p.K * S.d; }
+int send_state_cost(const Plan& p, const Side& S, int) { return p.K * S.d; }
+
+// Row offset in A of column c of a receiver-side state (pi, q, u): q N_w + w_off + u C_out.
+void emit_brow(Out& o, const Plan& p, const Side& S, const std::string& name) {
+  o.open("DEV i64 " + name + "(int c)");
+  for (size_t k = 0; k < S.paths.size(); ++k) {
+    const Path& P = p.paths[S.paths[k]];
+    const int mul_in = S.cmul[k], mul_out = p.out[P.i_out].mul;
+    const int hi = S.col_off[k] + p.K * mul_in;
+    o.line(F("if (c < %d) { const int r = c - %d, q = r / %d, u = r - q * %d;"
+             " return (i64)q * %d + %d + (i64)u * %d; }",
+             hi, S.col_off[k], mul_in, mul_in, p.n_w, P.w_off, mul_out));
+  }
+  o.line("return 0;");
+  o.close();
+}
+
+// Row base and channel stride in A of column c of a source-side state (pi, q, w):
+// A[q, w_off + u C_out + w] = base + u * stride.
+void emit_bz(Out& o, const Plan& p, const Side& S, const std::string& name) {
+  o.open("DEV i64 " + name + "(int c, int& stride)");
+  for (size_t k = 0; k < S.paths.size(); ++k) {
+    const Path& P = p.paths[S.paths[k]];
+    const int mul_out = S.cmul[k];
+    const int hi = S.col_off[k] + p.K * mul_out;
+    o.line(F("if (c < %d) { const int r = c - %d, q = r / %d, w = r - q * %d; stride = %d;"
+             " return (i64)q * %d + %d + w; }",
+             hi, S.col_off[k], mul_out, mul_out, mul_out, p.n_w, P.w_off));
+  }
+  o.line("stride = 0; return 0;");
+  o.close();
+}
+
+struct GemmSpec {
+  std::string name, args, a_at, b_at, store;
+  int N;
+  bool a_kfast, b_kfast, split;
+};
+
+// LDS-tiled MFMA GEMM: 64 x 64 output tile per 4-wave workgroup, K staged 32 at a time, each wave
+// a 32 x 32 quarter as 2 x 2 MFMA 16x16x4 tiles.  C[r][c] = sum_k A(r, k) B(k, c) over
+// k in [kb, ke); `store` writes value v at (r, c).
+void emit_gemm(Out& o, const GemmSpec& g) {
+  o.line("extern \"C\" __global__ void __launch_bounds__(256)");
+  o.open(g.name + "(" + g.args + ", int M, int Kd, int kper)");
+  o.line("__shared__ real As[64 * 34];");
+  o.line("__shared__ real Bs[32 * 80];");
+  o.line("const int tid = (int)threadIdx.x, lane = tid & 63, wv = tid >> 6;");
+  o.line("const int r0 = (int)blockIdx.x * 64, c0 = (int)blockIdx.y * 64;");
+  if (g.split) {
+    o.line("const int kb = (int)blockIdx.z * kper, ke = min(Kd, kb + kper);");
+  } else {
+    o.line("const int kb = 0, ke = Kd; (void)kper;");
+  }
+  o.line("acc4 a00 = {0, 0, 0, 0}, a01 = {0, 0, 0, 0}, a10 = {0, 0, 0, 0}, a11 = {0, 0, 0, 0};");
+  o.open("for (int k0 = kb; k0 < ke; k0 += 32)");
+  o.open("for (int t = 0; t < 8; ++t)");
+  o.line("const int id = t * 256 + tid;");
+  o.line(g.a_kfast ? "const int rr = id >> 5, kk = id & 31;" : "const int rr = id & 63, kk = id >> 6;");
+  o.line("const int r = r0 + rr, k = k0 + kk;");
+  o.line("As[rr * 34 + kk] = (r < M && k < ke) ? (" + g.a_at + ") : R(0);");
+  o.close();
+  o.open("for (int t = 0; t < 8; ++t)");
+  o.line("const int id = t * 256 + tid;");
+  o.line(g.b_kfast ? "const int cc = id >> 5, kk = id & 31;" : "const int cc = id & 63, kk = id >> 6;");
+  o.line("const int c = c0 + cc, k = k0 + kk;");
+  o.line(F("Bs[kk * 80 + cc] = (k < ke && c < %d) ? (", g.N) + g.b_at + ") : R(0);");
+  o.close();
+  o.line("__syncthreads();");
+  o.open("for (int s = 0; s < 8; ++s)");
+  o.line("const int ka = s * 4 + (lane >> 4);");
+  o.line("const real x0 = As[(32 * (wv >> 1) + (lane & 15)) * 34 + ka];");
+  o.line("const real x1 = As[(32 * (wv >> 1) + 16 + (lane & 15)) * 34 + ka];");
+  o.line("const real y0 = Bs[ka * 80 + 32 * (wv & 1) + (lane & 15)];");
+  o.line("const real y1 = Bs[ka * 80 + 32 * (wv & 1) + 16 + (lane & 15)];");
+  o.line("a00 = MFMA(x0, y0, a00); a01 = MFMA(x0, y1, a01); a10 = MFMA(x1, y0, a10); a11 = MFMA(x1, y1, a11);");
+  o.close();
+  o.line("__syncthreads();");
+  o.close();
+  o.open("for (int q = 0; q < 4; ++q)");
+  o.line("const int wr = q >> 1, wc = q & 1;");
+  o.line("const acc4 acc = q == 0 ? a00 : (q == 1 ? a01 : (q == 2 ? a10 : a11));");
+  o.open("for (int rr = 0; rr < 4; ++rr)");
+  // Accumulator layout: lane l, element rr holds row 4 (l / 16) + rr (f32) or 4 rr + l / 16 (f64).
+  o.line("const int r = r0 + 32 * (wv >> 1) + 16 * wr + ROWOF(lane, rr);");
+  o.line("const int c = c0 + 32 * (wv & 1) + 16 * wc + (lane & 15);");
+  o.line(F("if (r < M && c < %d) { const real v = acc[rr]; ", g.N) + g.store + " }");
+  o.close();
+  o.close();
+  o.close();
+}
+
+void uvw_prelude_extra(Out& o, const Plan& p) {
+  if (p.dtype == CGTP_F64) {
+    o.line("typedef double acc4 __attribute__((ext_vector_type(4)));");
+    o.line("#define MFMA(a, b, c) __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0)");
+    o.line("#define ROWOF(lane, rr) (4 * (rr) + ((lane) >> 4))");
+  } else {
+    o.line("typedef float acc4 __attribute__((ext_vector_type(4)));");
+    o.line("#define MFMA(a, b, c) __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0)");
+    o.line("#define ROWOF(lane, rr) (4 * ((lane) >> 4) + (rr))");
+  }
+}
+
+const char* kStateArgs =
+    "const real* __restrict__ x, const real* __restrict__ phi, const real* __restrict__ G,"
+    " const int* __restrict__ row_ptr, const int* __restrict__ col, real* __restrict__ S";
+
+// Receiver state of task T for one receiver (Sobek Eq. 33): rows (il, m3), columns (pi, q, u).
+void emit_state_task(Out& o, const Plan& p, const std::vector<Side>& sides, int ti, const StateTask& T,
+                     const std::vector<size_t>& side_off, long long node_stride) {
+  const Side& S = sides[T.side];
+  const int K = p.K, d3 = S.d;
+  std::vector<int> paths;
+  for (int k : T.idx) paths.push_back(S.paths[k]);
+  o.open(F("DEV void uvs_t%d(%s, int node, int il, int e_base)", ti, kStateArgs));
+  o.line("const int lane = (int)threadIdx.x & 63;");
+  o.line(F("const int u = %d + lane;", T.cb * 64));
+  for (int b : in_blocks_of(p, paths)) o.line(F("const int uc%d = u < %d ? u : %d;", b, p.in[b].mul, p.in[b].mul - 1));
+  for (int pi : paths)
+    for (int q = 0; q < K; ++q)
+      for (int m = 0; m < d3; ++m) o.line(F("real s%d_%d_%d = R(0);", pi, q, m));
+  o.line("const int e0 = row_ptr[node], e1 = row_ptr[node + 1];");
+  emit_recv_edge_loop(o, p, in_blocks_of(p, paths), "0", "1", [&] {
+    for (int pi : paths) {
+      const Path& P = p.paths[pi];
+      std::vector<bool> started(d3, false);
+      for (size_t t = 0; t < P.gpairs.size(); ++t) {
+        int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3;
+        if (!started[m3])
+          o.line(F("real t%d_%d = g[%d] * x%d_%d;", pi, m3, P.g_off + int(t), P.i_in, m1));
+        else
+          o.line(F("t%d_%d = fma(g[%d], x%d_%d, t%d_%d);", pi, m3, P.g_off + int(t), P.i_in, m1, pi, m3));
+        started[m3] = true;
+      }
+      for (int q = 0; q < K; ++q)
+        for (int m = 0; m < d3; ++m)
+          if (started[m]) o.line(F("s%d_%d_%d = fma(f%d, t%d_%d, s%d_%d_%d);", pi, q, m, q, pi, m, pi, q, m));
+    }
+  }, true);
+  for (size_t kk = 0; kk < T.idx.size(); ++kk) {
+    const int k = T.idx[kk], pi = S.paths[k], mul = S.cmul[k];
+    o.open(F("if (u < %d)", mul));
+    o.line(F("real* __restrict__ dst = S + %zu + (i64)il * %lld + %d + u;", side_off[T.side], node_stride, S.col_off[k]));
+    for (int q = 0; q < K; ++q)
+      for (int m = 0; m < d3; ++m) o.line(F("dst[%d] = s%d_%d_%d;", m * S.ld + q * mul, pi, q, m));
+    o.close();
+  }
+  o.close();
+}
+
+// One wave per (task, receiver); XCD-contiguous receiver ranges as in the channelwise forward.
+void emit_state_dispatch(Out& o, int ntask) {
+  o.line("extern \"C\" __global__ void __launch_bounds__(64)");
+  o.open(std::string("cgtp_uvw_state(") + kStateArgs + ", int i0, int nrec, int per, int e_base)");
+  o.line("const int b = (int)blockIdx.x;");
+  o.line("const int xcd = b & 7, s = b >> 3;");
+  o.line("const int t = s / per, il = xcd * per + (s - t * per);");
+  o.line("if (il >= nrec) return;");
+  o.open("switch (t)");
+  for (int k = 0; k < ntask; ++k) o.line(F("case %d: uvs_t%d(x, phi, G, row_ptr, col, S, i0 + il, il, e_base); break;", k, k));
+  o.line("default: break;");
+  o.close();
+  o.close();
+}
+
+const char* kEdgeArgs =
+    "const real* __restrict__ x, const real* __restrict__ phi, const real* __restrict__ G,"
+    " const int* __restrict__ row_ptr, const int* __restrict__ col, const real* __restrict__ Sb,"
+    " real* __restrict__ ep";
+
+// Per-edge backward of task T (receiver side): phi-bar_q = sum_{pi,m3} Sbar[pi][q][m3] C_pi[m3] and
+// Y-bar from Cbar[pi][m3] = sum_q phi_q Sbar[pi][q][m3], both reduced over the channels of the wave
+// into the edge's partial columns of task ti.
+void emit_edge_task(Out& o, const Plan& p, const std::vector<Side>& sides, int ti, const StateTask& T,
+                    const std::vector<size_t>& side_off, long long node_stride, int V) {
+  const Side& S = sides[T.side];
+  const int K = p.K, d3 = S.d;
+  std::vector<int> paths;
+  for (int k : T.idx) paths.push_back(S.paths[k]);
+  o.open(F("DEV void uve_t%d(%s, int node, int il, int e_base, int eps)", ti, kEdgeArgs));
+  o.line("const int lane = (int)threadIdx.x & 63;");
+  o.line(F("const int u = %d + lane;", T.cb * 64));
+  for (int b : in_blocks_of(p, paths)) o.line(F("const int uc%d = u < %d ? u : %d;", b, p.in[b].mul, p.in[b].mul - 1));
+  for (size_t kk = 0; kk < T.idx.size(); ++kk) {
+    const int k = T.idx[kk], pi = S.paths[k], mul = S.cmul[k];
+    o.line(F("const real* __restrict__ sr%d = Sb + %zu + (i64)il * %lld + %d + (u < %d ? u : 0);", pi,
+             side_off[T.side], node_stride, S.col_off[k], mul));
+    for (int q = 0; q < K; ++q)
+      for (int m = 0; m < d3; ++m)
+        o.line(F("const real sb%d_%d_%d = u < %d ? sr%d[%d] : R(0);", pi, q, m, mul, pi, m * S.ld + q * mul));
+  }
+  o.line("const int e0 = row_ptr[node], e1 = row_ptr[node + 1];");
+  emit_recv_edge_loop(o, p, in_blocks_of(p, paths), "0", "1", [&] {
+    for (int v = 0; v < V; ++v) o.line(F("real v%d = R(0);", v));
+    for (int pi : paths) {
+      const Path& P = p.paths[pi];
+      const int s = K + P.l2 * P.l2;
+      std::vector<bool> started(d3, false);
+      for (size_t t = 0; t < P.gpairs.size(); ++t) {
+        int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3;
+        if (!started[m3])
+          o.line(F("real t%d_%d = g[%d] * x%d_%d;", pi, m3, P.g_off + int(t), P.i_in, m1));
+        else
+          o.line(F("t%d_%d = fma(g[%d], x%d_%d, t%d_%d);", pi, m3, P.g_off + int(t), P.i_in, m1, pi, m3));
+        started[m3] = true;
+      }
+      for (int q = 0; q < K; ++q)
+        for (int m = 0; m < d3; ++m)
+          if (started[m]) o.line(F("v%d = fma(sb%d_%d_%d, t%d_%d, v%d);", q, pi, q, m, pi, m, q));
+      std::set<int> m3used;
+      for (auto& gp : P.gpairs) m3used.insert(gp.m3);
+      for (int m : m3used) {
+        o.line(F("real cb%d_%d = f0 * sb%d_0_%d;", pi, m, pi, m));
+        for (int q = 1; q < K; ++q) o.line(F("cb%d_%d = fma(f%d, sb%d_%d_%d, cb%d_%d);", pi, m, q, pi, q, m, pi, m));
+      }
+      for (auto& gp : P.gpairs) {
+        o.line(F("{ const real z = x%d_%d * cb%d_%d;", P.i_in, gp.m1, pi, gp.m3));
+        for (auto& t : gp.terms)
+          o.line(F("  v%d = fma(%s, z, v%d);", s + t.first, lit(t.second).c_str(), s + t.first));
+        o.line("}");
+      }
+    }
+    const int H = V / 2, Q = V / 4;
+    const bool f64 = p.dtype == CGTP_F64;
+    std::vector<std::pair<std::string, std::string>> pr;
+    for (int k = 0; k < H; ++k) pr.push_back({F("v%d", k), F("v%d", k + H)});
+    emit_swaps(o, pr, 32, f64);
+    for (int k = 0; k < H; ++k) o.line(F("v%d += v%d;", k, k + H));
+    pr.clear();
+    for (int k = 0; k < Q; ++k) pr.push_back({F("v%d", k), F("v%d", k + Q)});
+    emit_swaps(o, pr, 16, f64);
+    for (int k = 0; k < Q; ++k) o.line(F("v%d += v%d;", k, k + Q));
+    for (int k = 0; k < Q; ++k) o.line(F("v%d = rowsum(v%d);", k, k));
+    o.open("if ((lane & 15) == 0)");
+    o.line(F("real* __restrict__ dst = ep + (i64)(%d + (lane >> 4) * %d) * eps + (e - e_base);", ti * V, Q));
+    for (int k = 0; k < Q; ++k) o.line(F("dst[(i64)%d * eps] = v%d;", k, k));
+    o.close();
+  }, true);
+  o.close();
+}
+
+void emit_edge_dispatch(Out& o, int ntask) {
+  o.line("extern \"C\" __global__ void __launch_bounds__(64)");
+  o.open(std::string("cgtp_uvw_edge(") + kEdgeArgs + ", int i0, int nrec, int per, int e_base, int eps)");
+  o.line("const int b = (int)blockIdx.x;");
+  o.line("const int xcd = b & 7, s = b >> 3;");
+  o.line("const int t = s / per, il = xcd * per + (s - t * per);");
+  o.line("if (il >= nrec) return;");
+  o.open("switch (t)");
+  for (int k = 0; k < ntask; ++k)
+    o.line(F("case %d: uve_t%d(x, phi, G, row_ptr, col, Sb, ep, i0 + il, il, e_base, eps); break;", k, k));
+  o.line("default: break;");
+  o.close();
+  o.close();
+}
+
+const char* kZArgs =
+    "const real* __restrict__ phi, const real* __restrict__ G, const real* __restrict__ gout,"
+    " const int* __restrict__ recv, const int* __restrict__ src_ptr, const int* __restrict__ src_edge,"
+    " real* __restrict__ Z";
+
+// Source-side state of task T for one sender j: rows (jl, m1), columns (pi, q, w), with G rows
+// stored in source-CSR order (row k - k_base for out-edge position k).
+void emit_zstate_task(Out& o, const Plan& p, const std::vector<Side>& sides, int ti, const StateTask& T,
+                      const std::vector<size_t>& side_off, long long node_stride) {
+  const Side& S = sides[T.side];
+  const int K = p.K, d1 = S.d;
+  std::vector<int> paths;
+  for (int k : T.idx) paths.push_back(S.paths[k]);
+  const auto obs = out_blocks_of(p, paths);
+  o.open(F("DEV void uvz_t%d(%s, int node, int jl, int k_base)", ti, kZArgs));
+  o.line("const int lane = (int)threadIdx.x & 63;");
+  o.line(F("const int w = %d + lane;", T.cb * 64));
+  for (int ob : obs) o.line(F("const int wc%d = w < %d ? w : %d;", ob, p.out[ob].mul, p.out[ob].mul - 1));
+  for (int pi : paths)
+    for (int q = 0; q < K; ++q)
+      for (int m = 0; m < d1; ++m) o.line(F("real z%d_%d_%d = R(0);", pi, q, m));
+  o.line("const int s0 = src_ptr[node], s1 = src_ptr[node + 1];");
+  o.open("if (s0 < s1)");
+  o.line("int en = src_edge[s0];");
+  o.line("int in_ = recv[en];");
+  for (int ob : obs) {
+    const Block& B = p.out[ob];
+    for (int m = 0; m < B.dim(); ++m)
+      o.line(F("real mn%d_%d = gout[(i64)in_ * %d + %d + wc%d];", ob, m, p.c_out, B.offset + m * B.mul, ob));
+  }
+  o.open("for (int k = s0; k < s1; ++k)");
+  o.line("const int e = en;");
+  for (int ob : obs)
+    for (int m = 0; m < p.out[ob].dim(); ++m) o.line(F("const real mb%d_%d = mn%d_%d;", ob, m, ob, m));
+  o.line("{ const int kn = k + 1; en = src_edge[kn < s1 ? kn : k]; in_ = recv[en]; }");
+  for (int ob : obs) {
+    const Block& B = p.out[ob];
+    for (int m = 0; m < B.dim(); ++m)
+      o.line(F("mn%d_%d = gout[(i64)in_ * %d + %d + wc%d];", ob, m, p.c_out, B.offset + m * B.mul, ob));
+  }
+  o.line(F("const real* __restrict__ ph = phi + (i64)e * %d;", K));
+  o.line(F("const real* __restrict__ g = G + (i64)(k - k_base) * %d;", p.g_stride));
+  for (int q = 0; q < K; ++q) o.line(F("const real f%d = ph[%d];", q, q));
+  for (int pi : paths) {
+    const Path& P = p.paths[pi];
+    std::vector<bool> started(d1, false);
+    for (size_t t = 0; t < P.gpairs.size(); ++t) {
+      int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3;
+      if (!started[m1])
+        o.line(F("real b%d_%d = g[%d] * mb%d_%d;", pi, m1, P.g_off + int(t), P.i_out, m3));
+      else
+        o.line(F("b%d_%d = fma(g[%d], mb%d_%d, b%d_%d);", pi, m1, P.g_off + int(t), P.i_out, m3, pi, m1));
+      started[m1] = true;
+    }
+    for (int q = 0; q < K; ++q)
+      for (int m = 0; m < d1; ++m)
+        if (started[m]) o.line(F("z%d_%d_%d = fma(f%d, b%d_%d, z%d_%d_%d);", pi, q, m, q, pi, m, pi, q, m));
+  }
+  o.close();
+  o.close();
+  for (size_t kk = 0; kk < T.idx.size(); ++kk) {
+    const int k = T.idx[kk], pi = S.paths[k], mul = S.cmul[k];
+    o.open(F("if (w < %d)", mul));
+    o.line(F("real* __restrict__ dst = Z + %zu + (i64)jl * %lld + %d + w;", side_off[T.side], node_stride, S.col_off[k]));
+    for (int q = 0; q < K; ++q)
+      for (int m = 0; m < d1; ++m) o.line(F("dst[%d] = z%d_%d_%d;", m * S.ld + q * mul, pi, q, m));
+    o.close();
+  }
+  o.close();
+}
+
+void emit_zstate_dispatch(Out& o, int ntask) {
+  o.line("extern \"C\" __global__ void __launch_bounds__(64)");
+  o.open(std::string("cgtp_uvw_zstate(") + kZArgs + ", int j0, int njs, int per, int k_base)");
+  o.line("const int b = (int)blockIdx.x;");
+  o.line("const int xcd = b & 7, s = b >> 3;");
+  o.line("const int t = s / per, jl = xcd * per + (s - t * per);");
+  o.line("if (jl >= njs) return;");
+  o.open("switch (t)");
+  for (int k = 0; k < ntask; ++k)
+    o.line(F("case %d: uvz_t%d(phi, G, gout, recv, src_ptr, src_edge, Z, j0 + jl, jl, k_base); break;", k, k));
+  o.line("default: break;");
+  o.close();
+  o.close();
+}
+
+// G rows of the out-edges at source-CSR positions [k0, k1) (row k - k0 for edge src_edge[k]).
+void emit_prep_src(Out& o, const Plan& p) {
+  o.line("extern \"C\" __global__ void __launch_bounds__(64)");
+  o.open("cgtp_prep_src(const real* __restrict__ pos, const real* __restrict__ shift, const int* __restrict__ recv,"
+         " const int* __restrict__ send, const int* __restrict__ src_edge, int k0, int k1, real* __restrict__ G)");
+  o.line("const int k = k0 + (int)(blockIdx.x * 64 + threadIdx.x);");
+  o.line("if (k >= k1) return;");
+  o.line("const int e = src_edge[k];");
+  emit_edge_vector(o);
+  o.line("const real inv = R(1) / sqrt(rx * rx + ry * ry + rz * rz);");
+  o.line(F("real Y[%d];", p.sh_dim));
+  o.line("sh_eval<real>(rx * inv, ry * inv, rz * inv, Y);");
+  o.line(F("real* __restrict__ dst = G + (i64)(k - k0) * %d;", p.g_stride));
+  int n = 0;
+  for (const Path& P : p.paths) {
+    int s = P.l2 * P.l2;
+    for (const GPair& gp : P.gpairs) {
+      std::string ex;
+      for (auto& t : gp.terms) {
+        if (!ex.empty()) ex += " + ";
+        ex += lit(t.second) + " * Y[" + std::to_string(s + t.first) + "]";
+      }
+      o.line(F("dst[%d] = ", n++) + ex + ";");
+    }
+  }
+  o.close();
+}
+
+// Per-node layout of a state: sides back to back, side g holding d_g rows of ld_g values.
+std::vector<size_t> side_offsets(const std::vector<Side>& sides, long long* stride) {
+  std::vector<size_t> off;
+  size_t acc = 0;
+  for (auto& s : sides) {
+    off.push_back(acc);
+    acc += size_t(s.d) * size_t(s.ld);
+  }
+  *stride = (long long)acc;
+  return off;
+}
+
+// Address of row r (node r / d, component r % d), column `col` of side s of a per-node state.
+std::string state_at(const std::string& base, const Side& s, size_t off, long long stride, const std::string& r,
+                     const std::string& col) {
+  return F("%s[(i64)(%s / %d) * %lld + %zu + (%s %% %d) * %d + %s]", base.c_str(), r.c_str(), s.d, stride, off,
+           r.c_str(), s.d, s.ld, col.c_str());
+}
+
+}  // namespace
+
+// Layout facts the launcher needs (columns, strides, task counts).
+UvwLayout uvw_layout(const Plan& p) {
+  UvwLayout L;
+  auto rs = recv_sides(p), ss = send_sides(p);
+  for (auto& s : rs) L.recv.push_back({s.blk, s.d, s.mul, s.D, s.ld});
+  for (auto& s : ss) L.send.push_back({s.blk, s.d, s.mul, s.D, s.ld});
+  side_offsets(rs, &L.recv_stride);
+  side_offsets(ss, &L.send_stride);
+  L.n_state_tasks = int(state_tasks(p, rs, recv_state_cost).size());
+  L.n_z_tasks = int(state_tasks(p, ss, send_state_cost).size());
+  return L;
+}
+
+std::string generate_uvw_source(const Plan& p, const std::string& family, std::string* err) {
+  if (family != "uvw_fwd" && family != "uvw_bwd") {
+    *err = "the fully connected mode supports the streamed schedule only (family " + family + ")";
+    return "";
+  }
+  const bool bwd = family == "uvw_bwd";
+  Out o;
+  prelude(o, p, bwd, bwd);
+  uvw_prelude_extra(o, p);
+  emit_sh(o, p.lmax);
+  emit_prep(o, p);
+  auto rs = recv_sides(p);
+  long long RS = 0;
+  const std::vector<size_t> roff = side_offsets(rs, &RS);
+  auto st = state_tasks(p, rs, recv_state_cost);
+  for (int k = 0; k < int(st.size()); ++k) emit_state_task(o, p, rs, k, st[k], roff, RS);
+  emit_state_dispatch(o, int(st.size()));
+  for (auto& s : rs) {
+    emit_brow(o, p, s, F("brow%d", s.blk));
+  }
+  if (!bwd) {
+    for (size_t gi = 0; gi < rs.size(); ++gi) {
+      const Side& s = rs[gi];
+      const Block& OB = p.out[s.blk];
+      GemmSpec g;
+      g.name = F("cgtp_gemm_fwd%d", s.blk);
+      g.args = "const real* __restrict__ S, const real* __restrict__ A, real* __restrict__ out, int i0";
+      g.a_at = state_at("S", s, roff[gi], RS, "r", "k");
+      g.b_at = F("A[brow%d(k) + c]", s.blk);
+      g.store = F("out[(i64)(i0 + r / %d) * %d + %d + (r %% %d) * %d + c] = v;", s.d, p.c_out, OB.offset, s.d, OB.mul);
+      g.N = OB.mul;
+      g.a_kfast = true;
+      g.b_kfast = false;
+      g.split = false;
+      emit_gemm(o, g);
+    }
+    return o.s.str();
+  }
+  // ---- backward
+  for (size_t gi = 0; gi < rs.size(); ++gi) {
+    const Side& s = rs[gi];
+    const Block& OB = p.out[s.blk];
+    GemmSpec g;  // Sbar = mbar A^T
+    g.name = F("cgtp_gemm_sbar%d", s.blk);
+    g.args = "const real* __restrict__ gout, const real* __restrict__ A, real* __restrict__ Sb, int i0";
+    g.a_at = F("gout[(i64)(i0 + r / %d) * %d + %d + (r %% %d) * %d + k]", s.d, p.c_out, OB.offset, s.d, OB.mul);
+    g.b_at = F("A[brow%d(c) + k]", s.blk);
+    g.store = state_at("Sb", s, roff[gi], RS, "r", "c") + " = v;";
+    g.N = s.D;
+    g.a_kfast = true;
+    g.b_kfast = true;
+    g.split = false;
+    emit_gemm(o, g);
+    GemmSpec h;  // A-bar partials = S^T mbar over a slice of rows
+    h.name = F("cgtp_gemm_abar%d", s.blk);
+    h.args = "const real* __restrict__ S, const real* __restrict__ gout, real* __restrict__ part, int i0";
+    h.a_at = state_at("S", s, roff[gi], RS, "k", "r");
+    h.b_at = F("gout[(i64)(i0 + k / %d) * %d + %d + (k %% %d) * %d + c]", s.d, p.c_out, OB.offset, s.d, OB.mul);
+    h.store = F("part[(i64)blockIdx.z * %lld + (i64)r * %d + c] = v;", (long long)s.D * OB.mul, OB.mul);
+    h.N = OB.mul;
+    h.a_kfast = false;
+    h.b_kfast = false;
+    h.split = true;
+    emit_gemm(o, h);
+    // A-bar += sum over row slices (fixed order), scattered into the layout of A.
+    o.line("extern \"C\" __global__ void __launch_bounds__(256)");
+    o.open(F("cgtp_abar_accum%d(const real* __restrict__ part, int nsplit, real* __restrict__ gA)", s.blk));
+    o.line(F("const int id = (int)(blockIdx.x * 256 + threadIdx.x);"));
+    o.line(F("if (id >= %d) return;", s.D * OB.mul));
+    o.line(F("const int r = id / %d, c = id - r * %d;", OB.mul, OB.mul));
+    o.line("real acc = R(0);");
+    o.line(F("for (int k = 0; k < nsplit; ++k) acc += part[(i64)k * %d + id];", s.D * OB.mul));
+    o.line(F("gA[brow%d(r) + c] += acc;", s.blk));
+    o.close();
+  }
+  const int V = edge_partial_width(p);
+  for (int k = 0; k < int(st.size()); ++k) emit_edge_task(o, p, rs, k, st[k], roff, RS, V);
+  emit_edge_dispatch(o, int(st.size()));
+  emit_edge_final(o, p, int(st.size()), V);
+  emit_small_kernels(o);
+  // source side
+  emit_prep_src(o, p);
+  auto ss = send_sides(p);
+  auto zt = state_tasks(p, ss, send_state_cost);
+  long long ZS = 0;
+  const std::vector<size_t> zoff = side_offsets(ss, &ZS);
+  for (int k = 0; k < int(zt.size()); ++k) emit_zstate_task(o, p, ss, k, zt[k], zoff, ZS);
+  emit_zstate_dispatch(o, int(zt.size()));
+  for (size_t bi = 0; bi < ss.size(); ++bi) {
+    const Side& s = ss[bi];
+    const Block& IB = p.in[s.blk];
+    emit_bz(o, p, s, F("bz%d", s.blk));
+    GemmSpec g;  // x-bar = Z A (contracting (pi, q, w))
+    g.name = F("cgtp_gemm_xbar%d", s.blk);
+    g.args = "const real* __restrict__ Z, const real* __restrict__ A, real* __restrict__ gx, int j0";
+    g.a_at = state_at("Z", s, zoff[bi], ZS, "r", "k");
+    g.b_at = F("bx%d(A, k, c)", s.blk);
+    g.store = F("gx[(i64)(j0 + r / %d) * %d + %d + (r %% %d) * %d + c] = v;", s.d, p.c_in, IB.offset, s.d, IB.mul);
+    g.N = IB.mul;
+    g.a_kfast = true;
+    g.b_kfast = true;
+    g.split = false;
+    o.line(F("DEV real bx%d(const real* __restrict__ A, int k, int c) { int st; const i64 b = bz%d(k, st);"
+             " return A[b + (i64)c * st]; }", s.blk, s.blk));
+    emit_gemm(o, g);
+  }
+  return o.s.str();
+}
+
+}  // namespace cgtp

@@ -46,6 +46,19 @@ std::vector<Task> source_tasks(const Plan& p);
 // Y-bar partials), padded to a multiple of 4.
 int edge_partial_width(const Plan& p);
 
+// Fully connected layout: per output block (receiver side) and input block (source side) the
+// state width D (columns (path, q, channel)) and padded row stride ld; per node the sides are
+// stored back to back (recv_stride / send_stride elements per node).
+struct UvwSideInfo {
+  int blk, d, mul, D, ld;
+};
+struct UvwLayout {
+  std::vector<UvwSideInfo> recv, send;
+  int n_state_tasks = 0, n_z_tasks = 0;
+  long long recv_stride = 0, send_stride = 0;
+};
+UvwLayout uvw_layout(const Plan& p);
+
 // Compile (once) and fetch a kernel of a family on the current device.
 cgtp_status_t get_kernel(Plan& p, const std::string& family, const std::string& name, hipFunction_t* f,
                          std::string* err);

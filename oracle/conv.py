@@ -188,3 +188,29 @@ def backward(problem: Problem, x, edge_vec, recv, send, phi, A, grad_out,
     gpos.index_add_(0, send, ge)
     gpos.index_add_(0, recv, -ge)
     return dict(x=gx, edge_vec=ge, pos=gpos, phi=gphi, A=gA, Y=gY)
+
+
+def grad_A_streamed(problem: Problem, x, edge_vec, recv, send, phi, grad_out, n_nodes: Optional[int] = None,
+                    paths=None):
+    """Sobek Eq. 36: A-bar = S^T mbar with the receiver state S of Eq. 33 (per path).
+
+    ``paths`` (indices) restricts the result to those paths' columns, concatenated in order.
+    """
+    x, phi, gout = _t(x), _t(phi), _t(grad_out)
+    recv, send = _idx(recv), _idx(send)
+    N = x.shape[0] if n_nodes is None else n_nodes
+    K = phi.shape[1]
+    Y = spherical_harmonics(problem, edge_vec)
+    cols = []
+    for p in problem.paths:
+        if paths is not None and p.index not in paths:
+            continue
+        bi, bo = problem.irreps_in[p.i_in], problem.irreps_out[p.i_out]
+        S = receiver_state(problem, p, x, Y, recv, send, phi, N)     # (N, K, d3, C_in)
+        mb = _block(gout, bo)                                         # (N, d3, C_out)
+        if problem.mode == "uvu":
+            g = torch.einsum("iqcu,icu->qu", S, mb)
+        else:
+            g = torch.einsum("iqcu,icw->quw", S, mb).reshape(K, -1)
+        cols.append(g)
+    return torch.cat(cols, dim=1)

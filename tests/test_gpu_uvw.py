@@ -1,0 +1,129 @@
+"""Fully connected (uvw) streamed convolution: parity of the HIP path with the oracle (MI355X)."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import conv
+from tests.oracle_helpers import make_case
+
+pytestmark = pytest.mark.gpu
+
+KEYS = ("x", "pos", "edge_vec", "phi", "A")
+RAGGED = dict(irreps_in="4x0e+3x1o+2x2e", irreps_out="3x0e+2x1o+5x2e", mode="uvw")
+CFG4_SMALL = 512
+
+
+def _gpu(case):
+    from tests.gpu_helpers import GpuCase
+    return GpuCase(case)
+
+
+def _compare(got, ref, dtype, keys=KEYS, label=""):
+    from tests.gpu_helpers import TOL, rel_err
+    for k in keys:
+        err = rel_err(got[k].cpu().numpy(), ref[k].numpy())
+        print(f"{label} grad {k}: rel err {err:.3e}", flush=True)
+        assert err <= TOL[dtype], (k, err)
+
+
+@pytest.mark.parametrize("dtype", ["float64", "float32"])
+def test_uvw_ragged_forward_backward(dtype):
+    from clebsch_gordan_tensor_receiver_amd import _lib
+    from tests.gpu_helpers import TOL, rel_err
+    case = make_case(1, irreps_override=RAGGED, dtype=dtype)
+    g = _gpu(case)
+    out = g.forward(_lib.STREAMED).cpu().numpy()
+    ref = conv.forward_conventional(case.problem, case.x, case.edge_vec, case.recv, case.send, case.phi,
+                                    case.A).numpy()
+    err = rel_err(out, ref)
+    print(f"uvw ragged {dtype} forward rel err {err:.3e}", flush=True)
+    assert err <= TOL[dtype]
+    ref_b = conv.backward(case.problem, case.x, case.edge_vec, case.recv, case.send, case.phi, case.A,
+                          case.grad_out)
+    _compare(g.backward(), ref_b, dtype, label=f"uvw ragged {dtype}")
+
+
+def test_uvw_conventional_is_refused():
+    from clebsch_gordan_tensor_receiver_amd import _lib
+    case = make_case(1, irreps_override=RAGGED, dtype="float32")
+    g = _gpu(case)
+    with pytest.raises(_lib.CgtpError) as ei:
+        g.forward(_lib.CONVENTIONAL)
+    assert ei.value.status == 2
+
+
+def test_uvw_chunked_scratch():
+    # A small scratch budget forces many receiver and sender chunks.
+    from clebsch_gordan_tensor_receiver_amd import _lib
+    from tests.gpu_helpers import TOL, rel_err
+    case = make_case(1, irreps_override=RAGGED, dtype="float64")
+    g = _gpu(case)
+    g.plan.set_scratch_budget(64 << 10)
+    out = g.forward(_lib.STREAMED).cpu().numpy()
+    ref = conv.forward_conventional(case.problem, case.x, case.edge_vec, case.recv, case.send, case.phi,
+                                    case.A).numpy()
+    assert rel_err(out, ref) <= TOL["float64"]
+    ref_b = conv.backward(case.problem, case.x, case.edge_vec, case.recv, case.send, case.phi, case.A,
+                          case.grad_out)
+    _compare(g.backward(), ref_b, "float64", label="uvw chunked")
+
+
+def test_uvw_config4_irreps_reduced_graph():
+    """64x(0e,1o,2e) fully connected, SH lmax 2, on a 512-atom box at the same density (fp32)."""
+    from clebsch_gordan_tensor_receiver_amd import _lib
+    from tests.gpu_helpers import TOL, rel_err
+    case = make_case(4, n_nodes=CFG4_SMALL)
+    g = _gpu(case)
+    out = g.forward(_lib.STREAMED).cpu().numpy()
+    ref = conv.forward_streamed(case.problem, case.x, case.edge_vec, case.recv, case.send, case.phi,
+                                case.A).numpy()
+    err = rel_err(out, ref)
+    print(f"config 4 reduced forward rel err {err:.3e}", flush=True)
+    assert err <= TOL["float32"]
+    ref_b = conv.backward(case.problem, case.x, case.edge_vec, case.recv, case.send, case.phi, case.A,
+                          case.grad_out)
+    _compare(g.backward(), ref_b, "float32", label="config 4 reduced")
+
+
+def test_uvw_config4_full_size_sampled():
+    """16,384 atoms, ~857k edges: sampled receivers/senders/edges and A-bar in full (Eq. 36)."""
+    from clebsch_gordan_tensor_receiver_amd import _lib
+    from tests.gpu_helpers import TOL, rel_err
+    case = make_case(4)
+    g = _gpu(case)
+    out = g.forward(_lib.STREAMED).cpu().numpy()
+    got = {k: v.cpu().numpy() for k, v in g.backward().items()}
+    rng = np.random.default_rng(44)
+    nodes = np.unique(np.concatenate([rng.choice(case.n_nodes, 12, replace=False), [0, case.n_nodes - 1]]))
+    keep_r = np.isin(case.recv, nodes)
+    ev = case.edge_vec[torch.as_tensor(np.nonzero(keep_r)[0])]
+    m = conv.forward_conventional(case.problem, case.x, ev, case.recv[keep_r], case.send[keep_r],
+                                  case.phi[keep_r], case.A).numpy()
+    err = rel_err(out[nodes], m[nodes])
+    print(f"config 4 sampled forward rel err {err:.3e}", flush=True)
+    assert err <= TOL["float32"]
+    keep = np.isin(case.send, nodes) | keep_r
+    idx = np.nonzero(keep)[0]
+    sub = conv.backward(case.problem, case.x, case.edge_vec[torch.as_tensor(idx)], case.recv[keep],
+                        case.send[keep], case.phi[keep], case.A, case.grad_out, n_nodes=case.n_nodes)
+    checks = {"x": (got["x"][nodes], sub["x"].numpy()[nodes]),
+              "pos": (got["pos"][nodes], sub["pos"].numpy()[nodes]),
+              "edge_vec": (got["edge_vec"][idx], sub["edge_vec"].numpy()),
+              "phi": (got["phi"][idx], sub["phi"].numpy())}
+    for k, (a, b) in checks.items():
+        err = rel_err(a, b)
+        print(f"config 4 sampled grad {k}: rel err {err:.3e}", flush=True)
+        assert err <= TOL["float32"], (k, err)
+    # A-bar sums over every edge: check the columns of two paths (into 0e and into 2e) in full.
+    pick = [0, len(case.problem.paths) - 1]
+    gA = conv.grad_A_streamed(case.problem, case.x, case.edge_vec, case.recv, case.send, case.phi, case.grad_out,
+                              paths=pick)
+    cols = np.concatenate([np.arange(case.problem.paths[k].weight_offset,
+                                     case.problem.paths[k].weight_offset + case.problem.paths[k].n_weights)
+                           for k in pick])
+    err = rel_err(got["A"][:, cols], gA.numpy())
+    print(f"config 4 grad A (paths {pick}, all edges, Eq. 36): rel err {err:.3e}", flush=True)
+    assert err <= TOL["float32"]

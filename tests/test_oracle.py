@@ -362,3 +362,15 @@ def test_sh_gradient_complex_step():
         rc[:, d] += 1j * h
         dY = sh.sh(LMAX, torch.as_tensor(rc)).numpy().imag / h
         np.testing.assert_allclose((dY * v).sum(1), got[:, d], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("mode", ["uvu", "uvw"])
+def test_grad_A_streamed_equals_edge_form(mode):
+    # Sobek Eq. 36 (A-bar = S^T mbar) and Eq. 19 (A-bar = sum_e phi h) agree.
+    ov = dict(irreps_in="3x0e+2x1o+2x2e", irreps_out="3x0e+2x1o+2x2e", mode=mode)
+    if mode == "uvw":
+        ov["irreps_out"] = "2x0e+3x1o+1x2e"
+    c = make_case(1, irreps_override=ov)
+    a = conv.backward(c.problem, c.x, c.edge_vec, c.recv, c.send, c.phi, c.A, c.grad_out)["A"]
+    b = conv.grad_A_streamed(c.problem, c.x, c.edge_vec, c.recv, c.send, c.phi, c.grad_out)
+    assert (a - b).abs().max().item() <= 1e-12 * a.abs().max().item()
