@@ -214,3 +214,109 @@ def grad_A_streamed(problem: Problem, x, edge_vec, recv, send, phi, grad_out, n_
             g = torch.einsum("iqcu,icw->quw", S, mb).reshape(K, -1)
         cols.append(g)
     return torch.cat(cols, dim=1)
+
+
+def _sh_jvp(problem: Problem, edge_vec, v_e: torch.Tensor) -> torch.Tensor:
+    """Ydot = J_Y(r) v_e: directional derivative of the harmonics along v_e (per edge)."""
+    r = _t(edge_vec).clone().requires_grad_(True)
+    Y = _sh.sh(problem.lmax_sh, r)
+    u = torch.zeros_like(Y, requires_grad=True)
+    (g,) = torch.autograd.grad(Y, r, grad_outputs=u, create_graph=True)   # J^T u, linear in u
+    (jv,) = torch.autograd.grad(g, u, grad_outputs=_t(v_e))               # J v
+    return jv.detach()
+
+
+def _sh_hvp(problem: Problem, edge_vec, v_e: torch.Tensor, Ybar: torch.Tensor) -> torch.Tensor:
+    """grad_r < J_Y(r) v_e, Ybar >: the second-derivative term of the edge-vector double backward."""
+    r = _t(edge_vec).clone().requires_grad_(True)
+    Y = _sh.sh(problem.lmax_sh, r)
+    (g,) = torch.autograd.grad(Y, r, grad_outputs=_t(Ybar), create_graph=True)  # J^T Ybar
+    (h,) = torch.autograd.grad(g, r, grad_outputs=_t(v_e))                     # d/dr <J^T Ybar, v_e>
+    return h.detach()
+
+
+def double_backward(problem: Problem, x, edge_vec, recv, send, phi, A, grad_out, v_x=None, v_e=None,
+                    v_phi=None, v_A=None, n_nodes: Optional[int] = None,
+                    edge_chunk: int = 1 << 14) -> Dict[str, torch.Tensor]:
+    """Vector-Jacobian product of the backward map (x, r, phi, A, mbar) -> (xbar, ebar, phibar, Abar).
+
+    With the directions xdot = v_x, rdot = v_e, phidot = v_phi, Adot = v_A (Sobek section 3.3):
+      wdot = phidot A + phi Adot (Eq. 23), Tdot = D_x T[xdot] + D_Y T[Ydot], Ydot = J_Y(r) rdot (Eq. 24),
+      mdot = sum (wdot T + w Tdot) (Eq. 25), hdot = <mbar, Tdot> (+ <mbardot, T>, no mbar direction here),
+      Abar-dot = sum phidot h + phi hdot (Eq. 26), phibar-dot = sum Adot h + A hdot (Eq. 27),
+      xbar-dot = sum wdot B^x + w Bdot^x with Bdot^x = D_x T(., Ydot)* mbar (Eq. 30),
+      Ybar-dot = sum wdot B^Y + w Bdot^Y with Bdot^Y = D_Y T(xdot, .)* mbar (Eq. 31).
+    The VJP with respect to mbar is mdot; with respect to r it is J_Y^T Ybar-dot plus the curvature
+    term grad_r <J_Y(r) rdot, Ybar> with the first-order Ybar of Eq. 22.
+    Missing directions are zero.
+    """
+    x, phi, A, gout = _t(x), _t(phi), _t(A), _t(grad_out)
+    recv, send = _idx(recv), _idx(send)
+    N = x.shape[0] if n_nodes is None else n_nodes
+    E, K = recv.shape[0], phi.shape[1]
+    vx = torch.zeros_like(x) if v_x is None else _t(v_x)
+    ve = torch.zeros(E, 3, dtype=_F64) if v_e is None else _t(v_e)
+    vphi = torch.zeros_like(phi) if v_phi is None else _t(v_phi)
+    vA = torch.zeros_like(A) if v_A is None else _t(v_A)
+    Y = spherical_harmonics(problem, edge_vec)
+    Yd = _sh_jvp(problem, edge_vec, ve)
+    gg = dict(x=torch.zeros_like(x), phi=torch.zeros(E, K, dtype=_F64), A=torch.zeros_like(A),
+              grad_out=torch.zeros(N, problem.c_out, dtype=_F64))
+    Ybar_d = torch.zeros(E, problem.sh_dim, dtype=_F64)   # Ybar-dot (Eq. 31)
+    Ybar_w = torch.zeros(E, problem.sh_dim, dtype=_F64)   # first-order Ybar (Eq. 22)
+    for p in problem.paths:
+        bi, bs, bo = problem.irreps_in[p.i_in], problem.irreps_sh[p.i_sh], problem.irreps_out[p.i_out]
+        c = _coupling(p)
+        sl_w = slice(p.weight_offset, p.weight_offset + p.n_weights)
+        Ap, vAp = A[:, sl_w], vA[:, sl_w]
+        gAp = torch.zeros_like(Ap)
+        gxb = torch.zeros(x.shape[0], bi.dim, bi.mul, dtype=_F64)
+        mdot = torch.zeros(N, bo.dim, bo.mul, dtype=_F64)
+        for s in range(0, E, edge_chunk):
+            sl = slice(s, min(E, s + edge_chunk))
+            rs, ss = recv[sl], send[sl]
+            Yb = Y[sl, bs.offset:bs.offset + bs.dim]
+            Ydb = Yd[sl, bs.offset:bs.offset + bs.dim]
+            xj = _block(x, bi)[ss]
+            vxj = _block(vx, bi)[ss]
+            mb = _block(gout, bo)[rs]
+            T = torch.einsum("abc,eau,eb->ecu", c, xj, Yb)
+            Tdot = torch.einsum("abc,eau,eb->ecu", c, xj, Ydb) + torch.einsum("abc,eau,eb->ecu", c, vxj, Yb)
+            W = phi[sl] @ Ap
+            Wd = vphi[sl] @ Ap + phi[sl] @ vAp
+            if problem.mode == "uvu":
+                h = (mb * T).sum(1)
+                hd = (mb * Tdot).sum(1)
+                mdot.index_add_(0, rs, Wd[:, None, :] * T + W[:, None, :] * Tdot)              # Eq. 25
+                Bx = torch.einsum("abc,eb,ecu->eau", c, Yb, mb)
+                Bxd = torch.einsum("abc,eb,ecu->eau", c, Ydb, mb)
+                gxb.index_add_(0, ss, Wd[:, None, :] * Bx + W[:, None, :] * Bxd)               # Eq. 30
+                Ybar_d[sl, bs.offset:bs.offset + bs.dim] += (
+                    torch.einsum("abc,eau,ecu,eu->eb", c, xj, mb, Wd)
+                    + torch.einsum("abc,eau,ecu,eu->eb", c, vxj, mb, W))                       # Eq. 31
+                Ybar_w[sl, bs.offset:bs.offset + bs.dim] += torch.einsum("abc,eau,ecu,eu->eb", c, xj, mb, W)
+            else:
+                W = W.reshape(-1, bi.mul, bo.mul)
+                Wd = Wd.reshape(-1, bi.mul, bo.mul)
+                h = torch.einsum("ecw,ecu->euw", mb, T).reshape(-1, p.n_weights)
+                hd = torch.einsum("ecw,ecu->euw", mb, Tdot).reshape(-1, p.n_weights)
+                mdot.index_add_(0, rs, torch.einsum("euw,ecu->ecw", Wd, T) + torch.einsum("euw,ecu->ecw", W, Tdot))
+                Bx = torch.einsum("abc,eb,ecw->eaw", c, Yb, mb)
+                Bxd = torch.einsum("abc,eb,ecw->eaw", c, Ydb, mb)
+                gxb.index_add_(0, ss, torch.einsum("euw,eaw->eau", Wd, Bx) + torch.einsum("euw,eaw->eau", W, Bxd))
+                Ybar_d[sl, bs.offset:bs.offset + bs.dim] += (
+                    torch.einsum("abc,eau,ecw,euw->eb", c, xj, mb, Wd)
+                    + torch.einsum("abc,eau,ecw,euw->eb", c, vxj, mb, W))
+                Ybar_w[sl, bs.offset:bs.offset + bs.dim] += torch.einsum("abc,eau,ecw,euw->eb", c, xj, mb, W)
+            gAp += vphi[sl].T @ h + phi[sl].T @ hd                                             # Eq. 26
+            gg["phi"][sl] += h @ vAp.T + hd @ Ap.T                                             # Eq. 27
+        gg["A"][:, sl_w] = gAp
+        gg["x"][:, bi.offset:bi.offset + bi.size] += gxb.reshape(x.shape[0], -1)
+        gg["grad_out"][:, bo.offset:bo.offset + bo.size] += mdot.reshape(N, -1)
+    ge = _sh_vjp(problem, edge_vec, Ybar_d) + _sh_hvp(problem, edge_vec, ve, Ybar_w)
+    gpos = torch.zeros(N, 3, dtype=_F64)
+    gpos.index_add_(0, send, ge)
+    gpos.index_add_(0, recv, -ge)
+    gg["edge_vec"] = ge
+    gg["pos"] = gpos
+    return gg

@@ -374,3 +374,76 @@ def test_grad_A_streamed_equals_edge_form(mode):
     a = conv.backward(c.problem, c.x, c.edge_vec, c.recv, c.send, c.phi, c.A, c.grad_out)["A"]
     b = conv.grad_A_streamed(c.problem, c.x, c.edge_vec, c.recv, c.send, c.phi, c.grad_out)
     assert (a - b).abs().max().item() <= 1e-12 * a.abs().max().item()
+
+
+def _dbl_case(mode, n_nodes=10):
+    ov = dict(irreps_in="2x0e+2x1o+2x2e", irreps_out="2x0e+2x1o+2x2e", irreps_sh=_sh_str(2), mode=mode)
+    c = make_case(1, irreps_override=ov, n_nodes=n_nodes)
+    g = np.random.default_rng(31)
+    v = dict(v_x=g.normal(size=c.x.shape), v_e=g.normal(size=(len(c.recv), 3)), v_phi=g.normal(size=c.phi.shape),
+             v_A=g.normal(size=c.A.shape))
+    return c, v
+
+
+@pytest.mark.parametrize("mode", ["uvu", "uvw"])
+def test_double_backward_matches_autograd(mode):
+    # Independent route: torch autograd of the oracle forward, differentiated twice.
+    c, v = _dbl_case(mode)
+    x = torch.tensor(c.x, requires_grad=True)
+    pos = torch.tensor(c.pos, requires_grad=True)
+    phi = torch.tensor(c.phi, requires_grad=True)
+    A = torch.tensor(c.A, requires_grad=True)
+    mbar = torch.tensor(c.grad_out, requires_grad=True)
+    ev = conv.edge_vectors(pos, c.shift, c.recv, c.send)
+    m = conv.forward_conventional(c.problem, x, ev, c.recv, c.send, phi, A)
+    gx, gev, gphi, gA = torch.autograd.grad((m * mbar).sum(), (x, ev, phi, A), create_graph=True)
+    s = ((gx * torch.as_tensor(v["v_x"])).sum() + (gev * torch.as_tensor(v["v_e"])).sum()
+         + (gphi * torch.as_tensor(v["v_phi"])).sum() + (gA * torch.as_tensor(v["v_A"])).sum())
+    rx, rpos, rphi, rA, rm = torch.autograd.grad(s, (x, pos, phi, A, mbar))
+    got = conv.double_backward(c.problem, c.x, c.edge_vec, c.recv, c.send, c.phi, c.A, c.grad_out, **v)
+    for k, ref in (("x", rx), ("pos", rpos), ("phi", rphi), ("A", rA), ("grad_out", rm)):
+        np.testing.assert_allclose(got[k].numpy(), ref.numpy(), atol=1e-11 * max(1.0, ref.abs().max().item()))
+
+
+def test_double_backward_matches_finite_differences_of_backward():
+    # <gg_theta, d> = d/dt <v, B(theta + t d)> at t = 0, by central differences of the oracle backward.
+    c, v = _dbl_case("uvu")
+    gg = conv.double_backward(c.problem, c.x, c.edge_vec, c.recv, c.send, c.phi, c.A, c.grad_out, **v)
+    rng = np.random.default_rng(32)
+    d = dict(x=rng.normal(size=c.x.shape), pos=rng.normal(size=c.pos.shape), phi=rng.normal(size=c.phi.shape),
+             A=rng.normal(size=c.A.shape), mbar=rng.normal(size=c.grad_out.shape))
+
+    def pairing(t):
+        x = c.x + t * d["x"]
+        pos = c.pos + t * d["pos"]
+        phi = c.phi + t * d["phi"]
+        A = c.A + t * d["A"]
+        mb = c.grad_out + t * d["mbar"]
+        ev = conv.edge_vectors(pos, c.shift, c.recv, c.send)
+        b = conv.backward(c.problem, x, ev, c.recv, c.send, phi, A, mb)
+        return float((b["x"].numpy() * v["v_x"]).sum() + (b["edge_vec"].numpy() * v["v_e"]).sum()
+                     + (b["phi"].numpy() * v["v_phi"]).sum() + (b["A"].numpy() * v["v_A"]).sum())
+
+    h = 1e-5
+    fd = (pairing(h) - pairing(-h)) / (2 * h)
+    an = float((gg["x"].numpy() * d["x"]).sum() + (gg["pos"].numpy() * d["pos"]).sum()
+               + (gg["phi"].numpy() * d["phi"]).sum() + (gg["A"].numpy() * d["A"]).sum()
+               + (gg["grad_out"].numpy() * d["mbar"]).sum())
+    assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (fd, an)
+
+
+def test_double_backward_second_order_symmetry():
+    # With mbar fixed, gg_theta = H v for the Hessian H of L = <mbar, m>: <H v1, v2> = <H v2, v1>.
+    c, v1 = _dbl_case("uvu")
+    rng = np.random.default_rng(33)
+    v2 = dict(v_x=rng.normal(size=c.x.shape), v_e=rng.normal(size=(len(c.recv), 3)),
+              v_phi=rng.normal(size=c.phi.shape), v_A=rng.normal(size=c.A.shape))
+    g1 = conv.double_backward(c.problem, c.x, c.edge_vec, c.recv, c.send, c.phi, c.A, c.grad_out, **v1)
+    g2 = conv.double_backward(c.problem, c.x, c.edge_vec, c.recv, c.send, c.phi, c.A, c.grad_out, **v2)
+
+    def pair(g, v):
+        return float((g["x"].numpy() * v["v_x"]).sum() + (g["edge_vec"].numpy() * v["v_e"]).sum()
+                     + (g["phi"].numpy() * v["v_phi"]).sum() + (g["A"].numpy() * v["v_A"]).sum())
+
+    a, b = pair(g1, v2), pair(g2, v1)
+    assert abs(a - b) <= 1e-10 * max(1.0, abs(a))
