@@ -25,7 +25,7 @@ EXPORTED = [
     "cgtp_plan_create", "cgtp_plan_destroy", "cgtp_plan_info", "cgtp_plan_path", "cgtp_plan_cg_table",
     "cgtp_plan_compile", "cgtp_plan_set_scratch_budget", "cgtp_graph_build", "cgtp_graph_export",
     "cgtp_graph_dims", "cgtp_graph_upload", "cgtp_graph_destroy", "cgtp_workspace_size",
-    "cgtp_conv_forward", "cgtp_conv_backward", "cgtp_check_edges", "cgtp_error_string", "cgtp_last_error",
+    "cgtp_conv_forward", "cgtp_conv_backward", "cgtp_conv_double_backward", "cgtp_check_edges", "cgtp_error_string", "cgtp_last_error",
     "cgtp_profile_begin", "cgtp_profile_end", "cgtp_profile_count", "cgtp_profile_get",
 ]
 
@@ -70,6 +70,7 @@ def load() -> ctypes.CDLL:
         "cgtp_workspace_size": [P, P, I, ctypes.POINTER(Z)],
         "cgtp_conv_forward": [P, P, I, V, V, V, V, V, V, V, Z, V],
         "cgtp_conv_backward": [P, P, V, V, V, V, V, V, V, V, V, V, V, V, Z, V],
+        "cgtp_conv_double_backward": [P, P] + [V] * 18 + [Z, V],
         "cgtp_check_edges": [P, P, V, V, V, Z, V, ctypes.POINTER(ctypes.c_int)],
         "cgtp_profile_begin": [],
         "cgtp_profile_end": [],
@@ -240,6 +241,16 @@ def conv_backward(plan: Plan, graph: Graph, x, pos, shift, phi, A, grad_out, gra
                                     workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+def conv_double_backward(plan: Plan, graph: Graph, x, pos, shift, phi, A, grad_out, v_x=None, v_pos=None,
+                         v_edge_vec=None, v_phi=None, v_A=None, gg_x=None, gg_pos=None, gg_edge_vec=None,
+                         gg_phi=None, gg_A=None, gg_grad_out=None, workspace=None, stream=None):
+    check(load().cgtp_conv_double_backward(
+        plan.handle, graph.handle, _ptr(x), _ptr(pos), _ptr(shift), _ptr(phi), _ptr(A), _ptr(grad_out),
+        _ptr(v_x), _ptr(v_pos), _ptr(v_edge_vec), _ptr(v_phi), _ptr(v_A), _ptr(gg_x), _ptr(gg_pos),
+        _ptr(gg_edge_vec), _ptr(gg_phi), _ptr(gg_A), _ptr(gg_grad_out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
 class Convolution:
     """A plan, a graph and a workspace bound together, called with torch device tensors.
 
@@ -284,4 +295,25 @@ class Convolution:
         conv_backward(self.plan, self.graph, x, pos, shift, phi, A, grad_out, grad_x=outs["x"], grad_pos=outs["pos"],
                       grad_edge_vec=outs["edge_vec"], grad_phi=outs["phi"], grad_A=outs["A"],
                       workspace=self.workspace(OP_BACKWARD))
+        return {k: v for k, v in outs.items() if v is not None}
+
+    def double_backward(self, x, pos, shift, phi, A, grad_out, v_x=None, v_pos=None, v_edge_vec=None, v_phi=None,
+                        v_A=None, want=("x", "pos", "edge_vec", "phi", "A", "grad_out")):
+        """Gradients of <v, backward(x, r, phi, A, grad_out)> with respect to every backward input."""
+        import torch
+        n, e = self.graph.n_nodes, self.graph.n_edges
+        info = self.plan.info
+        dt = dict(dtype=self.torch_dtype, device="cuda")
+        outs = dict(
+            x=torch.empty((n, info["c_in"]), **dt) if "x" in want else None,
+            pos=torch.empty((n, 3), **dt) if "pos" in want else None,
+            edge_vec=torch.empty((max(e, 1), 3), **dt) if "edge_vec" in want else None,
+            phi=torch.empty((max(e, 1), info["num_radial"]), **dt) if "phi" in want else None,
+            A=torch.empty((info["num_radial"], info["n_weights"]), **dt) if "A" in want else None,
+            grad_out=torch.empty((n, info["c_out"]), **dt) if "grad_out" in want else None,
+        )
+        conv_double_backward(self.plan, self.graph, x, pos, shift, phi, A, grad_out, v_x=v_x, v_pos=v_pos,
+                             v_edge_vec=v_edge_vec, v_phi=v_phi, v_A=v_A, gg_x=outs["x"], gg_pos=outs["pos"],
+                             gg_edge_vec=outs["edge_vec"], gg_phi=outs["phi"], gg_A=outs["A"],
+                             gg_grad_out=outs["grad_out"], workspace=self.workspace(OP_DOUBLE_BACKWARD))
         return {k: v for k, v in outs.items() if v is not None}

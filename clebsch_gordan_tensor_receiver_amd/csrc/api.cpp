@@ -100,6 +100,38 @@ BwdLayout bwd_layout(const cgtp::Plan& p, const cgtp::Graph& g) {
   return L;
 }
 
+// Workspace plan of a double-backward call: G and Gdot rows (2 g_stride per edge), the edge
+// partials of the receiver pass, A-bar-dot slots and an edge-vector buffer.
+BwdLayout dbl_layout(const cgtp::Plan& p, const cgtp::Graph& g) {
+  BwdLayout L;
+  L.ntask_r = int(cgtp::recv_backward_tasks(p).size());
+  L.ntask_s = int(cgtp::source_tasks(p).size());
+  L.V = cgtp::dbl_partial_width(p);
+  L.row = L.ntask_r * L.V;
+  long long row_bytes = (long long)(2 * p.g_stride + L.row) * (long long)p.elem();
+  L.cap = std::max<long long>(std::max<long long>(1, (long long)(p.scratch_budget / size_t(row_bytes))),
+                              g.max_in_degree);
+  L.chunks = g.chunks(L.cap);
+  long long emax = std::max<long long>(1, max_chunk_edges(g, L.chunks));
+  L.emax = emax;
+  for (auto& c : L.chunks) {
+    int per, nch;
+    chunk_geometry(c.second - c.first, &per, &nch);
+    L.nslot = std::max(L.nslot, 8 * nch);
+  }
+  size_t off = 0;
+  L.g_off = off;
+  off += align256(size_t(emax) * size_t(2 * p.g_stride) * p.elem());
+  L.ep_off = off;
+  off += align256(size_t(emax) * size_t(L.row) * p.elem());
+  L.ap_off = off;
+  off += align256(size_t(L.nslot) * size_t(p.K) * size_t(p.n_w) * p.elem());
+  L.gev_off = off;
+  off += align256(size_t(std::max(g.e, 1)) * 3 * p.elem());
+  L.total = off;
+  return L;
+}
+
 // Feature blocks that no path reaches (output side) or leaves (input side) are not written by
 // the kernels; zero the whole tensor first when such a block exists.
 cgtp_status_t zero_unreached(cgtp::Plan& p, void* buf, int n, bool out_side, hipStream_t s, std::string* err) {
@@ -217,7 +249,10 @@ cgtp_status_t cgtp_plan_compile(cgtp_plan_t plan, int ops) {
       fams.push_back("fwds");
     }
     if (ops & (1 << CGTP_OP_BACKWARD)) fams.push_back("bwd");
+    if (ops & (1 << CGTP_OP_DOUBLE_BACKWARD)) fams.push_back("dbl");
   } else {
+    if (ops & (1 << CGTP_OP_DOUBLE_BACKWARD))
+      return fail(CGTP_ERR_UNSUPPORTED, "double backward is channelwise only");
     if (ops & (1 << CGTP_OP_FORWARD)) fams.push_back("uvw_fwd");
     if (ops & (1 << CGTP_OP_BACKWARD)) fams.push_back("uvw_bwd");
   }
@@ -303,7 +338,7 @@ cgtp_status_t cgtp_workspace_size(cgtp_plan_t plan, cgtp_graph_t g, cgtp_op_t op
   } else if (op == CGTP_OP_BACKWARD) {
     need = bwd_layout(p, G).total;
   } else {
-    return fail(CGTP_ERR_UNSUPPORTED, "double backward is not built yet");
+    need = dbl_layout(p, G).total;
   }
   *bytes = std::max<size_t>(need, 256);
   return ok();
@@ -455,6 +490,122 @@ cgtp_status_t cgtp_conv_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x
   if (grad_A) {
     int n = p.K * p.n_w, ns = L.nslot;
     void* a[] = {&ap, &ns, &n, &grad_A};
+    if ((st = cgtp::launch(kred, unsigned((n + 63) / 64), 256, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
+  }
+  return ok();
+}
+
+cgtp_status_t cgtp_conv_double_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x, const void* pos,
+                                        const void* shift, const void* phi, const void* A, const void* grad_out,
+                                        const void* v_x, const void* v_pos, const void* v_edge_vec,
+                                        const void* v_phi, const void* v_A, void* gg_x, void* gg_pos,
+                                        void* gg_edge_vec, void* gg_phi, void* gg_A, void* gg_grad_out,
+                                        void* workspace, size_t ws_bytes, void* stream) {
+  if (!plan || !g) return fail(CGTP_ERR_INVALID_ARG, "null plan or graph");
+  if (!x || !pos || !phi || !A || !grad_out) return fail(CGTP_ERR_INVALID_ARG, "null input tensor");
+  cgtp::Plan& p = plan->p;
+  cgtp::Graph& G = g->g;
+  if (p.mode != CGTP_CHANNELWISE) return fail(CGTP_ERR_UNSUPPORTED, "double backward is channelwise only");
+  if (!gg_x && !gg_pos && !gg_edge_vec && !gg_phi && !gg_A && !gg_grad_out) return ok();
+  size_t need = 0;
+  cgtp_status_t st = cgtp_workspace_size(plan, g, CGTP_OP_DOUBLE_BACKWARD, &need);
+  if (st != CGTP_OK) return st;
+  if (!workspace || ws_bytes < need) return fail(CGTP_ERR_WORKSPACE, "workspace too small");
+  std::string err;
+  cgtp::DeviceGraph d;
+  if ((st = cgtp::device_graph(G, &d, &err)) != CGTP_OK) return fail(st, err);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (gg_x && (st = zero_unreached(p, gg_x, G.n, false, s, &err)) != CGTP_OK) return fail(st, err);
+  if (gg_grad_out && (st = zero_unreached(p, gg_grad_out, G.n, true, s, &err)) != CGTP_OK) return fail(st, err);
+  BwdLayout L = dbl_layout(p, G);
+  const cgtp::SourceViews* views = nullptr;
+  if (gg_x && (st = cgtp::source_views(G, L.cap, &views, &err)) != CGTP_OK) return fail(st, err);
+  hipFunction_t kzero, kprep, kfwd, krecv, ksrc, kfinal, kpos, kred;
+  const char* fam = "dbl";
+  if ((st = cgtp::get_kernel(p, fam, "cgtp_fill_zero", &kzero, &err)) != CGTP_OK ||
+      (st = cgtp::get_kernel(p, fam, "cgtp_prep2", &kprep, &err)) != CGTP_OK ||
+      (st = cgtp::get_kernel(p, fam, "cgtp_dfwd", &kfwd, &err)) != CGTP_OK ||
+      (st = cgtp::get_kernel(p, fam, "cgtp_drecv", &krecv, &err)) != CGTP_OK ||
+      (st = cgtp::get_kernel(p, fam, "cgtp_dsrc", &ksrc, &err)) != CGTP_OK ||
+      (st = cgtp::get_kernel(p, fam, "cgtp_dedge_final", &kfinal, &err)) != CGTP_OK ||
+      (st = cgtp::get_kernel(p, fam, "cgtp_pos_grad", &kpos, &err)) != CGTP_OK ||
+      (st = cgtp::get_kernel(p, fam, "cgtp_a_reduce", &kred, &err)) != CGTP_OK)
+    return fail(st, err);
+  // A missing direction is read from a primal array of the same shape with a zero scale.
+  const bool f64 = p.dtype == CGTP_F64;
+  double sxd = v_x ? 1.0 : 0.0, sphid = v_phi ? 1.0 : 0.0, sAd = v_A ? 1.0 : 0.0;
+  float sxf = float(sxd), sphif = float(sphid), sAf = float(sAd);
+  void* psx = f64 ? (void*)&sxd : (void*)&sxf;
+  void* psphi = f64 ? (void*)&sphid : (void*)&sphif;
+  void* psA = f64 ? (void*)&sAd : (void*)&sAf;
+  const void* vx = v_x ? v_x : x;
+  const void* vphi = v_phi ? v_phi : phi;
+  const void* vA = v_A ? v_A : A;
+  char* ws = static_cast<char*>(workspace);
+  void* Gb = ws + L.g_off;
+  void* ep = ws + L.ep_off;
+  void* ap = ws + L.ap_off;
+  void* gev = gg_edge_vec ? gg_edge_vec : static_cast<void*>(ws + L.gev_off);
+  const bool need_edge = gg_edge_vec || gg_pos || gg_phi;
+  void* gev_arg = (gg_edge_vec || gg_pos) ? gev : nullptr;
+  if (gg_A) {
+    long long n = (long long)L.nslot * p.K * p.n_w;
+    void* a[] = {&ap, &n};
+    if ((st = cgtp::launch(kzero, unsigned((n + 255) / 256), 256, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
+  }
+  const int nt_f = int(cgtp::forward_tasks(p).size()), nt_r = L.ntask_r, nt_s = L.ntask_s;
+  int eps = int(L.emax);
+  for (size_t c = 0; c < L.chunks.size(); ++c) {
+    int i0 = L.chunks[c].first, nrec = L.chunks[c].second - L.chunks[c].first;
+    int e0 = G.row_ptr[L.chunks[c].first], e1 = G.row_ptr[L.chunks[c].second];
+    if (e1 > e0) {
+      void* a[] = {(void*)&pos, (void*)&shift, (void*)&d.recv, (void*)&d.col, (void*)&v_edge_vec, (void*)&v_pos,
+                   &e0, &e1, &Gb};
+      if ((st = cgtp::launch(kprep, unsigned((e1 - e0 + 63) / 64), 64, 0, s, a, &err)) != CGTP_OK)
+        return fail(st, err);
+    }
+    void* out_arg = gg_grad_out;
+    void* common[] = {(void*)&x, (void*)&vx, (void*)&phi, (void*)&vphi, (void*)&A, (void*)&vA, &Gb,
+                      (void*)&d.row_ptr, (void*)&d.col, (void*)&grad_out, &out_arg, &ep, &ap, psx, psphi, psA};
+    if (gg_grad_out) {
+      int per = (nrec + 7) / 8;
+      void* a[20];
+      std::copy(common, common + 16, a);
+      a[16] = &i0; a[17] = &nrec; a[18] = &per; a[19] = &e0;
+      if ((st = cgtp::launch(kfwd, unsigned(8 * nt_f * per), 64, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
+    }
+    if (need_edge || gg_A) {
+      int per, nch;
+      chunk_geometry(nrec, &per, &nch);
+      void* a[22];
+      std::copy(common, common + 16, a);
+      a[16] = &i0; a[17] = &nrec; a[18] = &per; a[19] = &nch; a[20] = &e0; a[21] = &eps;
+      if ((st = cgtp::launch(krecv, unsigned(8 * nt_r * nch), 64 * kRecvGroup, 0, s, a, &err)) != CGTP_OK)
+        return fail(st, err);
+    }
+    if (gg_x) {
+      int n = G.n, per = (G.n + 7) / 8, acc = c > 0 ? 1 : 0;
+      void* sp = static_cast<int32_t*>(views->base) + views->ptr_off[c];
+      void* se = static_cast<int32_t*>(views->base) + views->edge_off[c];
+      void* a[] = {(void*)&phi, (void*)&vphi, (void*)&A, (void*)&vA, &Gb, (void*)&grad_out, (void*)&d.recv, &sp, &se,
+                   &gg_x, psphi, psA, &n, &per, &e0, &acc};
+      if ((st = cgtp::launch(ksrc, unsigned(8 * nt_s * per), 64, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
+    }
+    if (need_edge && e1 > e0) {
+      void* a[] = {(void*)&pos, (void*)&shift, (void*)&d.recv, (void*)&d.col, (void*)&v_edge_vec, (void*)&v_pos,
+                   &ep, &e0, &e1, &eps, &gg_phi, &gev_arg};
+      if ((st = cgtp::launch(kfinal, unsigned((e1 - e0 + 63) / 64), 64, 0, s, a, &err)) != CGTP_OK)
+        return fail(st, err);
+    }
+  }
+  if (gg_pos) {
+    int n = G.n;
+    void* a[] = {&gev, (void*)&d.row_ptr, (void*)&d.src_ptr, (void*)&d.src_edge, &n, &gg_pos};
+    if ((st = cgtp::launch(kpos, unsigned(n), 64, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
+  }
+  if (gg_A) {
+    int n = p.K * p.n_w, ns = L.nslot;
+    void* a[] = {&ap, &ns, &n, &gg_A};
     if ((st = cgtp::launch(kred, unsigned((n + 63) / 64), 256, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
   }
   return ok();

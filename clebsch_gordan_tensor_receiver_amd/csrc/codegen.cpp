@@ -836,6 +836,7 @@ std::string generate_source(const Plan& p, const std::string& family, std::strin
                        int(tasks.size()));
     return o.s.str();
   }
+  if (family == "dbl") return generate_dbl_source(p, err);
   if (family == "uvw_fwd" || family == "uvw_bwd") {
     *err = "fully connected families are generated by generate_uvw_source";
     return "";

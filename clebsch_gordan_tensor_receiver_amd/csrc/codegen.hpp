@@ -61,6 +61,9 @@ void emit_small_kernels(Out& o);
 
 }  // namespace gen
 
+// Channelwise double backward (family "dbl").
+std::string generate_dbl_source(const Plan& p, std::string* err);
+
 // Fully connected (uvw) kernel families "uvw_fwd" and "uvw_bwd".
 std::string generate_uvw_source(const Plan& p, const std::string& family, std::string* err);
 

@@ -1,0 +1,520 @@
+// Double backward of the channelwise convolution: the vector-Jacobian product of the backward map
+// (x, r, phi, A, mbar) -> (x-bar, e-bar, phi-bar, A-bar) for cotangent directions
+// (xdot, rdot, phidot, Adot) = (v_x, v_e, v_phi, v_A), following Sobek section 3.3 (Eqs. 23-31):
+//   wdot = phidot A + phi Adot,  Ydot = J_Y(r) rdot,  Gdot[m1,m3] = sum_m2 c Ydot[m2],
+//   Tdot = Gdot x + G xdot,  hdot = <mbar, Tdot>.
+// Kernels (one family "dbl"):
+//   prep2      (lane = edge):    G and Gdot rows (Ydot from a dual-number pass of the harmonics);
+//   dfwd       (lane = channel): mdot_i = sum_j sum_pi (wdot T + w Tdot)         -> d/d mbar;
+//   drecv      (lane = channel): A-bar-dot = sum_e phidot h + phi hdot (registers, Eq. 26) and per
+//                                edge phi-bar-dot = sum Adot h + A hdot (Eq. 27), Y-bar-dot
+//                                (Eq. 31) and the first-order Y-bar (Eq. 22), channel-reduced;
+//   dsrc       (lane = channel): x-bar-dot_j = sum_out-edges sum_pi wdot G^T mbar + w Gdot^T mbar;
+//   dedge_final(lane = edge):    e-bar-dot = J_Y^T Y-bar-dot + grad_r <J_Y(r) rdot, Y-bar> with the
+//                                curvature term from nested dual numbers.
+// A missing direction is read from its primal array with a zero scale, so every load stays in
+// bounds; rdot = v_edge_vec + v_pos[send] - v_pos[recv] (either part optional).
+#include <algorithm>
+#include <cmath>
+#include <set>
+
+#include "codegen.hpp"
+
+namespace cgtp {
+
+using namespace gen;
+
+namespace {
+
+long double dfact2(int n) {
+  long double r = 1;
+  for (int k = n; k > 1; k -= 2) r *= k;
+  return r;
+}
+long double fct2(int n) {
+  long double r = 1;
+  for (int k = 2; k <= n; ++k) r *= k;
+  return r;
+}
+
+void dual_types(Out& o) {
+  // D1: value and one directional derivative.  DD: a D3 value plus epsilon times a D3 (the
+  // directional derivative of a gradient-carrying value).
+  o.line("struct D1 { real v, d; __device__ D1() {} __device__ D1(real c) : v(c), d(0) {}"
+         " __device__ D1(real a, real b) : v(a), d(b) {} };");
+  o.line("DEV D1 operator+(D1 a, D1 b) { return D1(a.v + b.v, a.d + b.d); }");
+  o.line("DEV D1 operator-(D1 a, D1 b) { return D1(a.v - b.v, a.d - b.d); }");
+  o.line("DEV D1 operator*(D1 a, D1 b) { return D1(a.v * b.v, a.d * b.v + a.v * b.d); }");
+  o.line("DEV D1 operator*(real c, D1 b) { return D1(c * b.v, c * b.d); }");
+  o.line("struct DD { D3 a, b; __device__ DD() {} __device__ DD(real c) : a(c), b(R(0)) {}"
+         " __device__ DD(D3 x, D3 y) : a(x), b(y) {} };");
+  o.line("DEV DD operator+(DD x, DD y) { return DD(x.a + y.a, x.b + y.b); }");
+  o.line("DEV DD operator-(DD x, DD y) { return DD(x.a - y.a, x.b - y.b); }");
+  o.line("DEV DD operator*(DD x, DD y) { return DD(x.a * y.a, x.a * y.b + x.b * y.a); }");
+  o.line("DEV DD operator*(real c, DD y) { return DD(c * y.a, c * y.b); }");
+}
+
+// Real spherical harmonics (as in sh_eval) evaluated in type S and contracted on the fly:
+// acc_k += weight_k(idx) * Y_idx for each accumulator; emitted column by column in m so that the
+// Legendre intermediates die early.
+void emit_sh_contract(Out& o, int L, const std::string& S, const std::string& xs, const std::string& ys,
+                      const std::string& zs,
+                      const std::vector<std::pair<std::string, std::function<std::string(int)>>>& accs) {
+  o.open("");
+  o.line(S + " a0 = " + S + "(R(1)), b0 = " + S + "(R(0));");
+  o.line(S + " sx = " + xs + ", sy = " + ys + ", sz = " + zs + ";");
+  for (int m = 1; m <= L; ++m)
+    o.line(F("%s a%d = sx * a%d - sy * b%d, b%d = sx * b%d + sy * a%d;", S.c_str(), m, m - 1, m - 1, m, m - 1,
+             m - 1));
+  auto emit_y = [&](int l, int m, const std::string& q) {
+    long double nrm = std::sqrt((2.0L * l + 1) * fct2(l - m) / fct2(l + m));
+    if (m == 0) {
+      for (auto& a : accs)
+        o.line(F("%s = %s + (%s * %s) * %s;", a.first.c_str(), a.first.c_str(), a.second(l * l + l).c_str(),
+                 lit(double(nrm)).c_str(), q.c_str()));
+    } else {
+      double c = double(nrm * std::sqrt(2.0L));
+      for (auto& a : accs) {
+        o.line(F("%s = %s + (%s * %s) * (%s * a%d);", a.first.c_str(), a.first.c_str(),
+                 a.second(l * l + l + m).c_str(), lit(c).c_str(), q.c_str(), m));
+        o.line(F("%s = %s + (%s * %s) * (%s * b%d);", a.first.c_str(), a.first.c_str(),
+                 a.second(l * l + l - m).c_str(), lit(c).c_str(), q.c_str(), m));
+      }
+    }
+  };
+  for (int m = 0; m <= L; ++m) {
+    o.open("");
+    o.line(F("%s q%d_%d = %s(%s);", S.c_str(), m, m, S.c_str(), lit(double(dfact2(2 * m - 1))).c_str()));
+    emit_y(m, m, F("q%d_%d", m, m));
+    if (m + 1 <= L) {
+      o.line(F("%s q%d_%d = %s * (sz * q%d_%d);", S.c_str(), m + 1, m, lit(2.0 * m + 1).c_str(), m, m));
+      emit_y(m + 1, m, F("q%d_%d", m + 1, m));
+    }
+    for (int l = m + 2; l <= L; ++l) {
+      o.line(F("%s q%d_%d = %s * (sz * q%d_%d) - %s * q%d_%d;", S.c_str(), l, m, lit(double(2 * l - 1) / (l - m)).c_str(),
+               l - 1, m, lit(double(l + m - 1) / (l - m)).c_str(), l - 2, m));
+      emit_y(l, m, F("q%d_%d", l, m));
+    }
+    o.close();
+  }
+  o.close();
+}
+
+// Effective edge-vector direction rdot of sorted edge e (ri, sj in scope) into vex, vey, vez.
+void emit_edge_direction(Out& o) {
+  o.line("real vex = R(0), vey = R(0), vez = R(0);");
+  o.line("if (vev) { vex = vev[3 * (i64)e]; vey = vev[3 * (i64)e + 1]; vez = vev[3 * (i64)e + 2]; }");
+  o.line("if (vpos) { vex += vpos[3 * (i64)sj] - vpos[3 * (i64)ri]; vey += vpos[3 * (i64)sj + 1] - vpos[3 * (i64)ri + 1];"
+         " vez += vpos[3 * (i64)sj + 2] - vpos[3 * (i64)ri + 2]; }");
+}
+
+// prep2: G (columns 0..g_stride) and Gdot (columns g_stride..2 g_stride) of every edge of [e0, e1).
+void emit_prep2(Out& o, const Plan& p) {
+  o.line("extern \"C\" __global__ void __launch_bounds__(64)");
+  o.open("cgtp_prep2(const real* __restrict__ pos, const real* __restrict__ shift, const int* __restrict__ recv,"
+         " const int* __restrict__ send, const real* __restrict__ vev, const real* __restrict__ vpos, int e0,"
+         " int e1, real* __restrict__ G)");
+  o.line("const int e = e0 + (int)(blockIdx.x * 64 + threadIdx.x);");
+  o.line("if (e >= e1) return;");
+  emit_edge_vector(o);
+  emit_edge_direction(o);
+  o.line("const real inv = R(1) / sqrt(rx * rx + ry * ry + rz * rz);");
+  o.line("const real nx = rx * inv, ny = ry * inv, nz = rz * inv;");
+  o.line("const real nv = nx * vex + ny * vey + nz * vez;");
+  o.line("const real dx = (vex - nx * nv) * inv, dy = (vey - ny * nv) * inv, dz = (vez - nz * nv) * inv;");
+  o.line(F("D1 Y[%d];", p.sh_dim));
+  o.line("sh_eval<D1>(D1(nx, dx), D1(ny, dy), D1(nz, dz), Y);");
+  o.line(F("real* __restrict__ dst = G + (i64)(e - e0) * %d;", 2 * p.g_stride));
+  int n = 0;
+  for (const Path& P : p.paths) {
+    int s = P.l2 * P.l2;
+    for (const GPair& gp : P.gpairs) {
+      std::string ev, ed;
+      for (auto& t : gp.terms) {
+        if (!ev.empty()) {
+          ev += " + ";
+          ed += " + ";
+        }
+        ev += lit(t.second) + " * Y[" + std::to_string(s + t.first) + "].v";
+        ed += lit(t.second) + " * Y[" + std::to_string(s + t.first) + "].d";
+      }
+      o.line(F("dst[%d] = ", n) + ev + ";");
+      o.line(F("dst[%d] = ", n + p.g_stride) + ed + ";");
+      ++n;
+    }
+  }
+  o.close();
+}
+
+const char* kDArgs =
+    "const real* __restrict__ x, const real* __restrict__ vx, const real* __restrict__ phi,"
+    " const real* __restrict__ vphi, const real* __restrict__ A, const real* __restrict__ vA,"
+    " const real* __restrict__ G, const int* __restrict__ row_ptr, const int* __restrict__ col,"
+    " const real* __restrict__ gout, real* __restrict__ out, real* __restrict__ ep, real* __restrict__ ap,"
+    " real sx, real sphi, real sA";
+
+// Edge loop over the receiver's in-edges (one wave); loads x and xdot rows, phi and phidot, the G
+// and Gdot rows.  Body sees e, g (G row), gd (Gdot row), f<q>, fd<q>, x<b>_<m>, xd<b>_<m>.
+void emit_dedge_loop(Out& o, const Plan& p, const std::vector<int>& blocks, const std::function<void()>& body) {
+  o.open("for (int e = e0; e < e1; ++e)");
+  o.line("const int j = col[e];");
+  o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", 2 * p.g_stride));
+  o.line(F("const real* __restrict__ gd = g + %d;", p.g_stride));
+  o.line(F("const real* __restrict__ ph = phi + (i64)e * %d;", p.K));
+  o.line(F("const real* __restrict__ phd = vphi + (i64)e * %d;", p.K));
+  for (int q = 0; q < p.K; ++q) o.line(F("const real f%d = ph[%d], fd%d = sphi * phd[%d];", q, q, q, q));
+  for (int b : blocks) {
+    const Block& B = p.in[b];
+    for (int m = 0; m < B.dim(); ++m) {
+      o.line(F("const real x%d_%d = x[(i64)j * %d + %d + uc];", b, m, p.c_in, B.offset + m * B.mul));
+      o.line(F("const real xd%d_%d = sx * vx[(i64)j * %d + %d + uc];", b, m, p.c_in, B.offset + m * B.mul));
+    }
+  }
+  body();
+  o.close();
+}
+
+void emit_da_loads(Out& o, const Plan& p, const std::vector<int>& paths) {
+  for (int pi : paths) {
+    const Path& P = p.paths[pi];
+    for (int q = 0; q < p.K; ++q) {
+      o.line(F("const real a%d_%d = A[%d + uc];", pi, q, q * p.n_w + P.w_off));
+      o.line(F("const real ad%d_%d = sA * vA[%d + uc];", pi, q, q * p.n_w + P.w_off));
+    }
+  }
+}
+
+// w and wdot of path pi.
+void emit_wwd(Out& o, const Plan& p, int pi) {
+  o.line(F("real w%d = f0 * a%d_0;", pi, pi));
+  o.line(F("real wd%d = fma(fd0, a%d_0, f0 * ad%d_0);", pi, pi, pi));
+  for (int q = 1; q < p.K; ++q) {
+    o.line(F("w%d = fma(f%d, a%d_%d, w%d);", pi, q, pi, q, pi));
+    o.line(F("wd%d = fma(fd%d, a%d_%d, fma(f%d, ad%d_%d, wd%d));", pi, q, pi, q, q, pi, q, pi));
+  }
+}
+
+// T[m3] = G x and Tdot[m3] = Gdot x + G xdot of path pi, names t<pi>_<m3>, td<pi>_<m3>.
+std::vector<bool> emit_t_td(Out& o, const Plan& p, int pi, int d3) {
+  const Path& P = p.paths[pi];
+  std::vector<bool> started(d3, false);
+  for (size_t t = 0; t < P.gpairs.size(); ++t) {
+    int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3, gi = P.g_off + int(t);
+    if (!started[m3]) {
+      o.line(F("real t%d_%d = g[%d] * x%d_%d;", pi, m3, gi, P.i_in, m1));
+      o.line(F("real td%d_%d = fma(gd[%d], x%d_%d, g[%d] * xd%d_%d);", pi, m3, gi, P.i_in, m1, gi, P.i_in, m1));
+    } else {
+      o.line(F("t%d_%d = fma(g[%d], x%d_%d, t%d_%d);", pi, m3, gi, P.i_in, m1, pi, m3));
+      o.line(F("td%d_%d = fma(gd[%d], x%d_%d, fma(g[%d], xd%d_%d, td%d_%d));", pi, m3, gi, P.i_in, m1, gi, P.i_in,
+               m1, pi, m3));
+    }
+    started[m3] = true;
+  }
+  return started;
+}
+
+// mdot of task (output block k, channel block) for one receiver (Eq. 25).
+void emit_dfwd_task(Out& o, const Plan& p, int ti, const Task& T) {
+  const Block& OB = p.out[T.group];
+  const int d3 = OB.dim(), MUL = OB.mul;
+  o.open(F("DEV void dfw_t%d(%s, int node, int e_base)", ti, kDArgs));
+  o.line(F("const int u = %d + (int)threadIdx.x;", T.cb * 64));
+  o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
+  for (int m = 0; m < d3; ++m) o.line(F("real acc%d = R(0);", m));
+  o.line("const int e0 = row_ptr[node], e1 = row_ptr[node + 1];");
+  for (const auto& S : subsets(p, T.paths)) {
+    o.open("");
+    emit_da_loads(o, p, S);
+    emit_dedge_loop(o, p, in_blocks_of(p, S), [&] {
+      for (int pi : S) {
+        emit_wwd(o, p, pi);
+        auto started = emit_t_td(o, p, pi, d3);
+        for (int m = 0; m < d3; ++m)
+          if (started[m]) o.line(F("acc%d = fma(wd%d, t%d_%d, fma(w%d, td%d_%d, acc%d));", m, pi, pi, m, pi, pi, m, m));
+      }
+    });
+    o.close();
+  }
+  o.open(F("if (u < %d)", MUL));
+  o.line(F("real* __restrict__ dst = out + (i64)node * %d + %d + u;", p.c_out, OB.offset));
+  for (int m = 0; m < d3; ++m) o.line(F("dst[%d] = acc%d;", m * MUL, m));
+  o.close();
+  o.close();
+}
+
+// Receiver-major part of task (output block k, path subset, channel block) for one receiver per wave.
+// Edge partial columns of the task: [0, K) phi-bar-dot, [K, K+Yd) Y-bar-dot, [K+Yd, K+2Yd) Y-bar.
+void emit_drecv_task(Out& o, const Plan& p, int ti, const Task& T, int V) {
+  const Block& OB = p.out[T.group];
+  const int d3 = OB.dim(), MUL = OB.mul, K = p.K, Yd = p.sh_dim;
+  o.open(F("DEV void drc_t%d(%s, real* sm, int node, int e_base, int eps, int slot)", ti, kDArgs));
+  o.line("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
+  o.line(F("const int u = %d + lane;", T.cb * 64));
+  o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
+  emit_da_loads(o, p, T.paths);
+  int na = 0;
+  for (size_t k = 0; k < T.paths.size() * size_t(K); ++k) o.line(F("real aa%d = R(0);", na++));
+  o.open("if (node >= 0)");
+  o.line(F("const real* __restrict__ gr = gout + (i64)node * %d + %d + uc;", p.c_out, OB.offset));
+  for (int m = 0; m < d3; ++m) o.line(F("const real mb%d = u < %d ? gr[%d] : R(0);", m, MUL, m * MUL));
+  o.line("const int e0 = row_ptr[node], e1 = row_ptr[node + 1];");
+  emit_dedge_loop(o, p, in_blocks_of(p, T.paths), [&] {
+    for (int v = 0; v < V; ++v) o.line(F("real v%d = R(0);", v));
+    int ai = 0;
+    for (int pi : T.paths) {
+      const Path& P = p.paths[pi];
+      const int sd = K + P.l2 * P.l2, sw = K + Yd + P.l2 * P.l2;
+      emit_wwd(o, p, pi);
+      auto started = emit_t_td(o, p, pi, d3);
+      bool first = true;
+      for (int m = 0; m < d3; ++m)
+        if (started[m]) {
+          if (first) {
+            o.line(F("real h%d = mb%d * t%d_%d;", pi, m, pi, m));
+            o.line(F("real hd%d = mb%d * td%d_%d;", pi, m, pi, m));
+          } else {
+            o.line(F("h%d = fma(mb%d, t%d_%d, h%d);", pi, m, pi, m, pi));
+            o.line(F("hd%d = fma(mb%d, td%d_%d, hd%d);", pi, m, pi, m, pi));
+          }
+          first = false;
+        }
+      for (int q = 0; q < K; ++q, ++ai) {
+        o.line(F("aa%d = fma(fd%d, h%d, fma(f%d, hd%d, aa%d));", ai, q, pi, q, pi, ai));
+        o.line(F("v%d = fma(ad%d_%d, h%d, fma(a%d_%d, hd%d, v%d));", q, pi, q, pi, pi, q, pi, q));
+      }
+      const int d1 = 2 * P.l1 + 1;
+      for (int m = 0; m < d1; ++m)
+        o.line(F("const real s%d_%d = fma(wd%d, x%d_%d, w%d * xd%d_%d);", pi, m, pi, P.i_in, m, pi, P.i_in, m));
+      std::set<int> m3used;
+      for (auto& gp : P.gpairs) m3used.insert(gp.m3);
+      for (int m : m3used) o.line(F("const real wm%d_%d = w%d * mb%d;", pi, m, pi, m));
+      for (auto& gp : P.gpairs) {
+        o.line(F("{ const real z = s%d_%d * mb%d, zw = x%d_%d * wm%d_%d;", pi, gp.m1, gp.m3, P.i_in, gp.m1, pi, gp.m3));
+        for (auto& t : gp.terms) {
+          o.line(F("  v%d = fma(%s, z, v%d);", sd + t.first, lit(t.second).c_str(), sd + t.first));
+          o.line(F("  v%d = fma(%s, zw, v%d);", sw + t.first, lit(t.second).c_str(), sw + t.first));
+        }
+        o.line("}");
+      }
+    }
+    const int H = V / 2, Q = V / 4;
+    const bool f64 = p.dtype == CGTP_F64;
+    std::vector<std::pair<std::string, std::string>> pr;
+    for (int k = 0; k < H; ++k) pr.push_back({F("v%d", k), F("v%d", k + H)});
+    emit_swaps(o, pr, 32, f64);
+    for (int k = 0; k < H; ++k) o.line(F("v%d += v%d;", k, k + H));
+    pr.clear();
+    for (int k = 0; k < Q; ++k) pr.push_back({F("v%d", k), F("v%d", k + Q)});
+    emit_swaps(o, pr, 16, f64);
+    for (int k = 0; k < Q; ++k) o.line(F("v%d += v%d;", k, k + Q));
+    for (int k = 0; k < Q; ++k) o.line(F("v%d = rowsum(v%d);", k, k));
+    o.open("if ((lane & 15) == 0)");
+    o.line(F("real* __restrict__ dst = ep + (i64)(%d + (lane >> 4) * %d) * eps + (e - e_base);", ti * V, Q));
+    for (int k = 0; k < Q; ++k) o.line(F("dst[(i64)%d * eps] = v%d;", k, k));
+    o.close();
+  });
+  o.close();
+  emit_wave_combine(o, "aa", na, 4);
+  o.open(F("if (w == 0 && u < %d)", MUL));
+  o.line(F("real* __restrict__ dst = ap + (i64)slot * %d + u;", K * p.n_w));
+  int ai = 0;
+  for (int pi : T.paths)
+    for (int q = 0; q < K; ++q, ++ai) o.line(F("dst[%d] += aa%d;", q * p.n_w + p.paths[pi].w_off, ai));
+  o.close();
+  o.close();
+}
+
+const char* kDSrcArgs =
+    "const real* __restrict__ phi, const real* __restrict__ vphi, const real* __restrict__ A,"
+    " const real* __restrict__ vA, const real* __restrict__ G, const real* __restrict__ gout,"
+    " const int* __restrict__ recv, const int* __restrict__ src_ptr, const int* __restrict__ src_edge,"
+    " real* __restrict__ gx, real sphi, real sA";
+
+// x-bar-dot of task (input block b, channel block) for one sender (Eq. 30).
+void emit_dsrc_task(Out& o, const Plan& p, int ti, const Task& T) {
+  const Block& IB = p.in[T.group];
+  const int d1 = IB.dim(), MUL = IB.mul, K = p.K;
+  o.open(F("DEV void dsr_t%d(%s, int node, int e_base, int accumulate)", ti, kDSrcArgs));
+  o.line(F("const int u = %d + (int)threadIdx.x;", T.cb * 64));
+  o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
+  for (int m = 0; m < d1; ++m) o.line(F("real acc%d = R(0);", m));
+  o.line("const int s0 = src_ptr[node], s1 = src_ptr[node + 1];");
+  for (const auto& S : subsets(p, T.paths)) {
+    o.open("");
+    emit_da_loads(o, p, S);
+    o.open("for (int k = s0; k < s1; ++k)");
+    o.line("const int e = src_edge[k];");
+    o.line("const int i = recv[e];");
+    o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", 2 * p.g_stride));
+    o.line(F("const real* __restrict__ gd = g + %d;", p.g_stride));
+    o.line(F("const real* __restrict__ ph = phi + (i64)e * %d;", K));
+    o.line(F("const real* __restrict__ phd = vphi + (i64)e * %d;", K));
+    for (int q = 0; q < K; ++q) o.line(F("const real f%d = ph[%d], fd%d = sphi * phd[%d];", q, q, q, q));
+    o.line(F("const real* __restrict__ gi = gout + (i64)i * %d + uc;", p.c_out));
+    for (int ob : out_blocks_of(p, S)) {
+      const Block& B = p.out[ob];
+      for (int m = 0; m < B.dim(); ++m) o.line(F("const real mb%d_%d = gi[%d];", ob, m, B.offset + m * B.mul));
+    }
+    for (int pi : S) {
+      const Path& P = p.paths[pi];
+      emit_wwd(o, p, pi);
+      std::vector<bool> started(d1, false);
+      for (size_t t = 0; t < P.gpairs.size(); ++t) {
+        int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3, gi2 = P.g_off + int(t);
+        if (!started[m1]) {
+          o.line(F("real b%d_%d = g[%d] * mb%d_%d;", pi, m1, gi2, P.i_out, m3));
+          o.line(F("real bd%d_%d = gd[%d] * mb%d_%d;", pi, m1, gi2, P.i_out, m3));
+        } else {
+          o.line(F("b%d_%d = fma(g[%d], mb%d_%d, b%d_%d);", pi, m1, gi2, P.i_out, m3, pi, m1));
+          o.line(F("bd%d_%d = fma(gd[%d], mb%d_%d, bd%d_%d);", pi, m1, gi2, P.i_out, m3, pi, m1));
+        }
+        started[m1] = true;
+      }
+      for (int m = 0; m < d1; ++m)
+        if (started[m]) o.line(F("acc%d = fma(wd%d, b%d_%d, fma(w%d, bd%d_%d, acc%d));", m, pi, pi, m, pi, pi, m, m));
+    }
+    o.close();
+    o.close();
+  }
+  o.open(F("if (u < %d)", MUL));
+  o.line(F("real* __restrict__ dst = gx + (i64)node * %d + %d + u;", p.c_in, IB.offset));
+  o.open("if (accumulate)");
+  for (int m = 0; m < d1; ++m) o.line(F("dst[%d] += acc%d;", m * MUL, m));
+  o.close("} else {");
+  ++o.ind;
+  for (int m = 0; m < d1; ++m) o.line(F("dst[%d] = acc%d;", m * MUL, m));
+  o.close();
+  o.close();
+  o.close();
+}
+
+// Edge finalisation: phi-bar-dot sums, e-bar-dot = J^T Ybar_d + the curvature term.
+void emit_dedge_final(Out& o, const Plan& p, int ntask, int V) {
+  const int K = p.K, Yd = p.sh_dim;
+  o.line("extern \"C\" __global__ void __launch_bounds__(64)");
+  o.open("cgtp_dedge_final(const real* __restrict__ pos, const real* __restrict__ shift, const int* __restrict__ recv,"
+         " const int* __restrict__ send, const real* __restrict__ vev, const real* __restrict__ vpos,"
+         " const real* __restrict__ ep, int e0, int e1, int eps, real* __restrict__ gphi, real* __restrict__ gev)");
+  o.line("const int e = e0 + (int)(blockIdx.x * 64 + threadIdx.x);");
+  o.line("if (e >= e1) return;");
+  o.line("const real* __restrict__ col0 = ep + (e - e0);");
+  o.line("#define ROWV(k) col0[(i64)(k) * eps]");
+  auto sum_col = [&](int k) {
+    std::string ex = F("ROWV(%d)", k);
+    for (int t = 1; t < ntask; ++t) ex += F(" + ROWV(%d)", t * V + k);
+    return ex;
+  };
+  o.open("if (gphi)");
+  for (int q = 0; q < K; ++q) o.line(F("gphi[(i64)e * %d + %d] = ", K, q) + sum_col(q) + ";");
+  o.close();
+  o.line("if (!gev) return;");
+  emit_edge_vector(o);
+  emit_edge_direction(o);
+  o.line("const real inv = R(1) / sqrt(rx * rx + ry * ry + rz * rz);");
+  o.line("const real nx = rx * inv, ny = ry * inv, nz = rz * inv;");
+  o.line("const real nv = nx * vex + ny * vey + nz * vez;");
+  o.line("const real dx = (vex - nx * nv) * inv, dy = (vey - ny * nv) * inv, dz = (vez - nz * nv) * inv;");
+  o.line(F("real ybd[%d], ybw[%d];", Yd, Yd));
+  for (int m = 0; m < Yd; ++m) {
+    o.line(F("ybd[%d] = ", m) + sum_col(K + m) + ";");
+    o.line(F("ybw[%d] = ", m) + sum_col(K + Yd + m) + ";");
+  }
+  o.line("DD accw(R(0));");
+  o.line("DD accd(R(0));");
+  emit_sh_contract(o, p.lmax, "DD", "DD(D3(nx, R(1), R(0), R(0)), D3(dx, R(0), R(0), R(0)))",
+                   "DD(D3(ny, R(0), R(1), R(0)), D3(dy, R(0), R(0), R(0)))",
+                   "DD(D3(nz, R(0), R(0), R(1)), D3(dz, R(0), R(0), R(0)))",
+                   {{"accw", [](int i) { return F("ybw[%d]", i); }}, {"accd", [](int i) { return F("ybd[%d]", i); }}});
+  // J^T Ybar_d = Pi p_d / rho with p_d the gradient of sum Ybar_d P at n.
+  o.line("real px = accd.a.x, py = accd.a.y, pz = accd.a.z;");
+  o.line("real pn = nx * px + ny * py + nz * pz;");
+  o.line("real gx = (px - nx * pn) * inv, gy = (py - ny * pn) * inv, gz = (pz - nz * pn) * inv;");
+  // Curvature: H v = [-dn (n.p) - n (dn.p) + Pi (H_P dn)] / rho - Pi p (n.v) / rho^2, p, H_P dn of sum Ybar_w P.
+  o.line("const real wx = accw.a.x, wy = accw.a.y, wz = accw.a.z;");
+  o.line("const real hx = accw.b.x, hy = accw.b.y, hz = accw.b.z;");
+  o.line("const real np_ = nx * wx + ny * wy + nz * wz, dp = dx * wx + dy * wy + dz * wz;");
+  o.line("const real nh = nx * hx + ny * hy + nz * hz;");
+  o.line("gx += (-dx * np_ - nx * dp + (hx - nx * nh)) * inv - (wx - nx * np_) * nv * inv * inv;");
+  o.line("gy += (-dy * np_ - ny * dp + (hy - ny * nh)) * inv - (wy - ny * np_) * nv * inv * inv;");
+  o.line("gz += (-dz * np_ - nz * dp + (hz - nz * nh)) * inv - (wz - nz * np_) * nv * inv * inv;");
+  o.line("gev[3 * (i64)e] = gx; gev[3 * (i64)e + 1] = gy; gev[3 * (i64)e + 2] = gz;");
+  o.line("#undef ROWV");
+  o.close();
+}
+
+}  // namespace
+
+int dbl_partial_width(const Plan& p) { return (p.K + 2 * p.sh_dim + 3) / 4 * 4; }
+
+std::string generate_dbl_source(const Plan& p, std::string* err) {
+  if (p.mode != CGTP_CHANNELWISE) {
+    *err = "the double backward is generated for the channelwise mode";
+    return "";
+  }
+  Out o;
+  prelude(o, p, true, true);
+  dual_types(o);
+  emit_sh(o, p.lmax);
+  emit_prep2(o, p);
+  auto ft = forward_tasks(p);
+  for (int k = 0; k < int(ft.size()); ++k) emit_dfwd_task(o, p, k, ft[k]);
+  o.line("extern \"C\" __global__ void __launch_bounds__(64)");
+  o.open(std::string("cgtp_dfwd(") + kDArgs + ", int i0, int nrec, int per, int e_base)");
+  o.line("const int b = (int)blockIdx.x;");
+  o.line("const int xcd = b & 7, s = b >> 3;");
+  o.line("const int t = s / per, i = xcd * per + (s - t * per);");
+  o.line("if (i >= nrec) return;");
+  o.open("switch (t)");
+  for (int k = 0; k < int(ft.size()); ++k)
+    o.line(F("case %d: dfw_t%d(x, vx, phi, vphi, A, vA, G, row_ptr, col, gout, out, ep, ap, sx, sphi, sA, i0 + i, e_base);"
+             " break;", k, k));
+  o.line("default: break;");
+  o.close();
+  o.close();
+  const int V = dbl_partial_width(p);
+  auto rt = recv_backward_tasks(p);
+  int amax = 0;
+  for (int k = 0; k < int(rt.size()); ++k) {
+    emit_drecv_task(o, p, k, rt[k], V);
+    amax = std::max(amax, int(rt[k].paths.size()) * p.K);
+  }
+  o.line("extern \"C\" __global__ void __launch_bounds__(256)");
+  o.open(std::string("cgtp_drecv(") + kDArgs + ", int i0, int nrec, int per, int nch, int e_base, int eps)");
+  o.line(F("__shared__ real sm[%d];", 3 * amax * 64));
+  o.line("const int b = (int)blockIdx.x;");
+  o.line("const int xcd = b & 7, s = b >> 3;");
+  o.line("const int t = s / nch, c = s - t * nch;");
+  o.line("const int lo = xcd * per + c * 4;");
+  o.line("int hi = lo + 4; if (hi > (xcd + 1) * per) hi = (xcd + 1) * per; if (hi > nrec) hi = nrec;");
+  o.line("if (lo >= hi) return;");
+  o.line("const int r = lo + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
+  o.line("const int node = r < hi ? i0 + r : -1;");
+  o.line("const int slot = xcd * nch + c;");
+  o.open("switch (t)");
+  for (int k = 0; k < int(rt.size()); ++k)
+    o.line(F("case %d: drc_t%d(x, vx, phi, vphi, A, vA, G, row_ptr, col, gout, out, ep, ap, sx, sphi, sA, sm, node,"
+             " e_base, eps, slot); break;", k, k));
+  o.line("default: break;");
+  o.close();
+  o.close();
+  auto st = source_tasks(p);
+  for (int k = 0; k < int(st.size()); ++k) emit_dsrc_task(o, p, k, st[k]);
+  o.line("extern \"C\" __global__ void __launch_bounds__(64)");
+  o.open(std::string("cgtp_dsrc(") + kDSrcArgs + ", int nrec, int per, int e_base, int accumulate)");
+  o.line("const int b = (int)blockIdx.x;");
+  o.line("const int xcd = b & 7, s = b >> 3;");
+  o.line("const int t = s / per, node = xcd * per + (s - t * per);");
+  o.line("if (node >= nrec) return;");
+  o.open("switch (t)");
+  for (int k = 0; k < int(st.size()); ++k)
+    o.line(F("case %d: dsr_t%d(phi, vphi, A, vA, G, gout, recv, src_ptr, src_edge, gx, sphi, sA, node, e_base,"
+             " accumulate); break;", k, k));
+  o.line("default: break;");
+  o.close();
+  o.close();
+  emit_dedge_final(o, p, int(rt.size()), V);
+  emit_small_kernels(o);
+  return o.s.str();
+}
+
+}  // namespace cgtp

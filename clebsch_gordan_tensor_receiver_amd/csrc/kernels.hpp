@@ -45,6 +45,9 @@ std::vector<Task> source_tasks(const Plan& p);
 // Values per edge and task written by the receiver backward (phi-bar partials then
 // Y-bar partials), padded to a multiple of 4.
 int edge_partial_width(const Plan& p);
+// Values per edge and task written by the double backward's receiver pass (phi-bar-dot, then
+// Y-bar-dot, then the first-order Y-bar), padded to a multiple of 4.
+int dbl_partial_width(const Plan& p);
 
 // Fully connected layout: per output block (receiver side) and input block (source side) the
 // state width D (columns (path, q, channel)) and padded row stride ld; per node the sides are

@@ -163,6 +163,27 @@ cgtp_status_t cgtp_conv_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x
                                  void* grad_x, void* grad_pos, void* grad_edge_vec, void* grad_phi,
                                  void* grad_A, void* workspace, size_t ws_bytes, void* stream);
 
+/* Double backward (channelwise mode only): the vector-Jacobian product of the backward map
+ * (x, r, phi, A, grad_out) -> (grad_x, grad_edge_vec, grad_phi, grad_A) along the cotangent
+ * directions (v_x, v_edge, v_phi, v_A), i.e. the gradient of
+ *   <v_x, grad_x> + <v_edge, grad_edge_vec> + <v_phi, grad_phi> + <v_A, grad_A>
+ * with respect to every input of the backward (Sobek section 3.3, Eqs. 23-31, which state the
+ * same derivatives in tangent form).  Inputs as in cgtp_conv_backward; directions, each
+ * optional (NULL = zero): v_x (N x C_in), v_pos (N x 3; a direction of the positions, entering
+ * through the edge vectors as v_pos[send] - v_pos[recv]), v_edge_vec (E x 3, receiver-sorted),
+ * v_phi (E x K), v_A (K x N_w).  Outputs, each optional and overwritten: gg_x (N x C_in),
+ * gg_pos (N x 3, out-edge minus in-edge sums of gg_edge_vec), gg_edge_vec (E x 3), gg_phi
+ * (E x K), gg_A (K x N_w) and gg_grad_out (N x C_out, the derivative with respect to grad_out,
+ * which is the tangent of the forward output).  Fixed-order reductions: bitwise repeatable.
+ * UNSUPPORTED for the fully connected mode. */
+cgtp_status_t cgtp_conv_double_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x, const void* pos,
+                                        const void* shift, const void* phi, const void* A,
+                                        const void* grad_out, const void* v_x, const void* v_pos,
+                                        const void* v_edge_vec, const void* v_phi, const void* v_A,
+                                        void* gg_x, void* gg_pos, void* gg_edge_vec, void* gg_phi,
+                                        void* gg_A, void* gg_grad_out, void* workspace, size_t ws_bytes,
+                                        void* stream);
+
 /* Check on the device that no edge has zero length.  Synchronises `stream`.  Returns
  * DEGENERATE_EDGE (and the first offending sorted edge in *first_bad, else -1). */
 cgtp_status_t cgtp_check_edges(cgtp_plan_t plan, cgtp_graph_t g, const void* pos, const void* shift,

@@ -48,6 +48,13 @@ class GpuCase:
     def backward(self, **kw):
         return self.conv.backward(self.x, self.pos, self.shift, self.phi, self.A, self.grad_out, **kw)
 
+    def double_backward(self, dirs: dict, **kw):
+        """dirs: host arrays v_x, v_pos, v_edge_vec, v_phi, v_A (receiver-sorted edges); missing = zero."""
+        dt = torch.float64 if self.case.dtype == "float64" else torch.float32
+        dev = {k: (torch.tensor(v, dtype=dt, device="cuda").contiguous() if v is not None else None)
+               for k, v in dirs.items()}
+        return self.conv.double_backward(self.x, self.pos, self.shift, self.phi, self.A, self.grad_out, **dev, **kw)
+
 
 def _irreps(blocks) -> str:
     return "+".join(f"{b.mul}x{b.l}{'e' if b.parity > 0 else 'o'}" for b in blocks)

@@ -100,3 +100,31 @@ def rotate_features(blocks, feat: np.ndarray, R: np.ndarray, improper: bool = Fa
         v = feat[:, b.offset:b.offset + b.size].reshape(-1, b.dim, b.mul)
         out[:, b.offset:b.offset + b.size] = np.einsum("ab,nbu->nau", D, v).reshape(len(feat), -1)
     return out
+
+
+def make_directions(case: Case) -> dict:
+    """Seeded cotangent directions of the double backward, N(0, 1), rounded to the case's dtype.
+
+    Per-edge directions are drawn in the generator's edge order and permuted into receiver-sorted
+    order like phi.  v_e is the effective edge-vector direction v_edge_vec + v_pos[send] - v_pos[recv]
+    that the oracle takes.
+    """
+    c = case
+    E = len(c.recv)
+    v = dict(
+        v_x=normal_tensor(c.config, 4, c.x.shape, dtype=c.dtype),
+        v_pos=normal_tensor(c.config, 5, c.pos.shape, dtype=c.dtype),
+        v_edge_vec=normal_tensor(c.config, 6, (E, 3), dtype=c.dtype)[c.perm],
+        v_phi=normal_tensor(c.config, 7, c.phi.shape, dtype=c.dtype)[c.perm],
+        v_A=normal_tensor(c.config, 9, c.A.shape, dtype=c.dtype),
+    )
+    return v
+
+
+def effective_edge_direction(case: Case, v_edge_vec=None, v_pos=None) -> np.ndarray:
+    e = np.zeros((len(case.recv), 3))
+    if v_edge_vec is not None:
+        e = e + v_edge_vec
+    if v_pos is not None:
+        e = e + v_pos[case.send] - v_pos[case.recv]
+    return e

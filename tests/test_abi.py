@@ -1,0 +1,193 @@
+"""Host-side checks of the C-ABI library (no GPU): exported symbols, plan tables against the
+oracle's Clebsch-Gordan tensors and path enumeration, the CSR against the oracle's sort, and the
+status codes of invalid calls."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import cg, csr
+from oracle.irreps import make_problem
+from workloads import make_workload
+from workloads.graphs import CONFIGS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cgtp.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from clebsch_gordan_tensor_receiver_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from clebsch_gordan_tensor_receiver_amd import build
+        build.build()
+    return _lib
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cgtp_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("cgtp_plan_create", "cgtp_graph_build", "cgtp_workspace_size", "cgtp_conv_forward",
+              "cgtp_conv_backward", "cgtp_conv_double_backward", "cgtp_error_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    so = lib.load()
+    for n in _declared():
+        assert hasattr(so, n), n
+    assert sorted(lib.EXPORTED) == sorted(_declared())
+
+
+@pytest.mark.parametrize("config", sorted(CONFIGS))
+def test_plan_matches_oracle_paths_and_cg(lib, config):
+    s = CONFIGS[config]
+    plan = lib.Plan(s["irreps_in"], s["irreps_sh"], s["irreps_out"], s["mode"], s["dtype"], s["K"])
+    prob = make_problem(s["irreps_in"], s["irreps_sh"], s["irreps_out"], s["mode"])
+    info = plan.info
+    assert info["n_paths"] == len(prob.paths)
+    assert info["n_weights"] == prob.n_weights
+    assert (info["c_in"], info["c_out"], info["sh_dim"]) == (prob.c_in, prob.c_out, prob.sh_dim)
+    assert info["num_radial"] == s["K"]
+    nnz = 0
+    for k, P in enumerate(prob.paths):
+        d = plan.path(k)
+        assert (d["i_in"], d["i_sh"], d["i_out"], d["l1"], d["l2"], d["l3"]) == (P.i_in, P.i_sh, P.i_out, P.l1, P.l2,
+                                                                                  P.l3)
+        assert (d["weight_offset"], d["n_weights"]) == (P.weight_offset, P.n_weights)
+        idx, val = plan.cg_table(k)
+        ref = cg.sparse_terms(P.l1, P.l2, P.l3)
+        assert [tuple(r) for r in idx.tolist()] == [t[:3] for t in ref], k
+        assert np.abs(val - np.array([t[3] for t in ref])).max() <= 1e-15
+        nnz += len(ref)
+    assert info["cg_nnz"] == nnz
+
+
+def test_survey_table_counts(lib):
+    # Path counts, weight counts and widths of the five workloads, as tabulated from the path rule.
+    want = {1: (7, 56, 32, 72, 9), 2: (17, 2176, 1152, 2048, 16), 3: (17, 1088, 576, 1024, 16),
+            4: (11, 45056, 576, 576, 9), 5: (106, 3392, 1568, 1568, 49)}
+    for c, (P, nw, cin, cout, yd) in want.items():
+        s = CONFIGS[c]
+        info = lib.Plan(s["irreps_in"], s["irreps_sh"], s["irreps_out"], s["mode"], s["dtype"], s["K"]).info
+        assert (info["n_paths"], info["n_weights"], info["c_in"], info["c_out"], info["sh_dim"]) == (P, nw, cin, cout,
+                                                                                                      yd), c
+
+
+def _graph_vs_oracle(lib, n, recv, send, image):
+    g = lib.Graph(n, recv, send, image)
+    perm, row_ptr, col = csr.receiver_csr(n, recv, send, image)
+    rp, c, sp, se = g.export()
+    assert np.array_equal(g.perm, perm)
+    assert np.array_equal(rp, row_ptr)
+    assert np.array_equal(c, col)
+    src_ptr, src_edge = csr.source_csr(n, col)
+    assert np.array_equal(sp, src_ptr)
+    assert np.array_equal(se, src_edge)
+
+
+@pytest.mark.parametrize("config", [1, 2])
+def test_graph_csr_bit_exact(lib, config):
+    w = make_workload(config)
+    _graph_vs_oracle(lib, w.n_nodes, w.recv, w.send, w.image)
+
+
+def test_graph_edge_cases(lib):
+    rng = np.random.default_rng(5)
+    # Isolated nodes, repeated (recv, send) pairs told apart by the image index, self-loops of
+    # periodic images, and ties broken by the input index.
+    n = 9
+    recv = rng.integers(0, 5, size=60).astype(np.int32)
+    send = rng.integers(0, 5, size=60).astype(np.int32)
+    image = rng.integers(-1, 2, size=(60, 3)).astype(np.int32)
+    _graph_vs_oracle(lib, n, recv, send, image)
+    _graph_vs_oracle(lib, n, recv, send, None)
+    # Duplicate edges with identical keys keep their input order.
+    _graph_vs_oracle(lib, 3, np.array([1, 1, 1, 0], np.int32), np.array([2, 2, 2, 2], np.int32), None)
+    # No edges at all.
+    g = lib.Graph(4, np.zeros(0, np.int32), np.zeros(0, np.int32))
+    rp, c, sp, se = g.export()
+    assert rp.tolist() == [0] * 5 and sp.tolist() == [0] * 5 and len(c) == 0 and len(se) == 0
+
+
+def _status(fn):
+    from clebsch_gordan_tensor_receiver_amd._lib import CgtpError
+    with pytest.raises(CgtpError) as e:
+        fn()
+    return e.value.status
+
+
+INVALID_ARG, UNSUPPORTED, WORKSPACE = 1, 2, 3
+
+
+def test_invalid_plans_are_rejected(lib):
+    mk = lib.Plan
+    assert _status(lambda: mk("8x0e+bad", "1x0e+1x1o", "8x0e", "uvu")) == INVALID_ARG
+    assert _status(lambda: mk("8x0e", "1x0e+1x2e", "8x0e", "uvu")) == INVALID_ARG      # SH degrees not 0..L
+    assert _status(lambda: mk("8x0e", "1x0e+1x1e", "8x0e", "uvu")) == INVALID_ARG      # SH parity
+    assert _status(lambda: mk("8x0e", "1x0e", "8x0e", "uvu", num_radial=0)) == INVALID_ARG
+    assert _status(lambda: mk("8x0e", "1x0e", "8x1o", "uvu")) == UNSUPPORTED           # no admissible path
+    assert _status(lambda: mk("8x0e", "1x0e", "4x0e", "uvu")) == UNSUPPORTED           # uvu needs mul_in = mul_out
+    sh7 = "+".join(f"1x{l}{'e' if l % 2 == 0 else 'o'}" for l in range(8))
+    assert _status(lambda: mk("8x0e", sh7, "8x0e", "uvu")) == UNSUPPORTED              # degrees above 6
+
+
+def test_invalid_graphs_are_rejected(lib):
+    i32 = lambda *v: np.array(v, np.int32)  # noqa: E731
+    assert _status(lambda: lib.Graph(0, i32(), i32())) == INVALID_ARG
+    assert _status(lambda: lib.Graph(3, i32(0, 3), i32(1, 1))) == INVALID_ARG
+    assert _status(lambda: lib.Graph(3, i32(0, 1), i32(-1, 1))) == INVALID_ARG
+
+
+def test_host_validation_before_any_device_work(lib):
+    so = lib.load()
+    plan = lib.Plan("8x0e+8x1o", "1x0e+1x1o", "8x0e+8x1o", "uvu", "float64", 4)
+    uvw = lib.Plan("8x0e+8x1o", "1x0e+1x1o", "8x0e+8x1o", "uvw", "float64", 4)
+    g = lib.Graph(3, np.array([0, 1], np.int32), np.array([1, 2], np.int32))
+    n = ctypes.c_size_t()
+    assert so.cgtp_workspace_size(plan.handle, g.handle, 2, ctypes.byref(n)) == 0 and n.value >= 256
+    assert so.cgtp_workspace_size(uvw.handle, g.handle, 2, ctypes.byref(n)) == UNSUPPORTED
+    assert so.cgtp_plan_compile(uvw.handle, 1 << 2) == UNSUPPORTED
+    nul = [None] * 10
+    assert so.cgtp_conv_forward(plan.handle, g.handle, 0, *[None] * 6, None, 0, None) == INVALID_ARG
+    assert so.cgtp_conv_forward(plan.handle, g.handle, 7, *[1] * 6, None, 0, None) == INVALID_ARG  # bad schedule
+    assert so.cgtp_conv_backward(plan.handle, g.handle, *nul, None, None, 0, None) == INVALID_ARG
+    assert so.cgtp_conv_double_backward(plan.handle, g.handle, *[None] * 18, 0, None) == INVALID_ARG
+    assert so.cgtp_conv_double_backward(uvw.handle, g.handle, *[1] * 6, *[None] * 12, 0, None) == UNSUPPORTED
+    # Workspace smaller than cgtp_workspace_size: refused before touching the device.
+    assert so.cgtp_conv_backward(plan.handle, g.handle, *[1] * 6, 1, None, None, None, None, 1, 16, None) == WORKSPACE
+    assert so.cgtp_conv_double_backward(plan.handle, g.handle, *[1] * 6, *[None] * 5, 1, *[None] * 5, 1, 16,
+                                        None) == WORKSPACE
+    assert so.cgtp_plan_set_scratch_budget(plan.handle, 16) == INVALID_ARG
+    assert so.cgtp_plan_path(plan.handle, 99, (ctypes.c_int32 * 9)()) == INVALID_ARG
+    assert so.cgtp_error_string(WORKSPACE) == b"workspace too small"
+
+
+def test_workspace_is_bounded_by_the_scratch_budget(lib):
+    s = CONFIGS[2]
+    w = make_workload(2)
+    plan = lib.Plan(s["irreps_in"], s["irreps_sh"], s["irreps_out"], s["mode"], s["dtype"], s["K"])
+    g = lib.Graph(w.n_nodes, w.recv, w.send, w.image)
+    big = [lib.workspace_size(plan, g, op) for op in (0, 1, 2)]
+    plan.set_scratch_budget(1 << 20)
+    small = [lib.workspace_size(plan, g, op) for op in (0, 1, 2)]
+    for b, sm in zip(big, small):
+        assert sm < b
+    # Budget plus the O(N + E + parameter) terms: A-bar partial slots (8 per XCD group of 4
+    # receivers at most), one edge-vector buffer and alignment.  Never E x N_w.
+    E, N = g.n_edges, g.n_nodes
+    K, nw = plan.info["num_radial"], plan.info["n_weights"]
+    nslot = 8 * (((N + 7) // 8 + 3) // 4)
+    for sm in small:
+        assert sm <= (1 << 20) + 4 * (nslot * K * nw + 3 * E) + 1024
+        assert sm < E * nw * 4
