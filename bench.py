@@ -62,6 +62,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--profile-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain device copy of known size (calibrates the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -77,6 +79,8 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        return copy_probe(torch)
     spec = CONFIGS[CONFIG]
     w = make_workload(CONFIG)
     plan = cg.Plan(spec["irreps_in"], spec["irreps_sh"], spec["irreps_out"], spec["mode"], spec["dtype"], spec["K"])
@@ -170,6 +174,22 @@ def main() -> int:
     if not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity"] = cpu_baseline(w, plan, perm, x_h, A_h, g_h, out, grads)
     print(json.dumps(result), flush=True)
+    return 0
+
+
+COPY_BYTES = 256 << 20
+
+
+def copy_probe(torch) -> int:
+    """Five copies of a 256 MiB buffer: each reads and writes COPY_BYTES of HBM.  The FETCH_SIZE and
+    WRITE_SIZE counters of these dispatches, divided by COPY_BYTES, give the factors that turn the
+    counters of the convolution kernels into bytes."""
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": COPY_BYTES, "launches": 5}), flush=True)
     return 0
 
 

@@ -2,7 +2,7 @@
 
 Every random draw comes from a NumPy PCG64 generator seeded with
 ``1000 * config + stream`` (stream 0 positions, 1 node features, 2 radial
-matrix A, 3 output cotangent, 4..7 double-backward directions, 8 edge-order
+matrix A, 3 output cotangent, 4..7 and 9 double-backward directions, 8 edge-order
 shuffle).  The five configurations are:
 
 1. 64 uniform atoms in a 6 A periodic cube, cutoff 3 A, 8x0e+8x1o -> 8x0e+8x1o+8x2e,
