@@ -33,26 +33,37 @@ PEAK_FP32_ALU_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 PEAK_FP64_ALU_TFLOPS = 78.6
 
 
-def algorithmic_fma_per_edge(plan):
-    """Per-edge FMA counts of each kernel, from the plan's paths and CG tables."""
+def algorithmic_fma(plan, n_edges: int, n_nodes: int):
+    """FMA per launch of each kernel (one launch covers every edge), from the plan's path table.
+
+    Per path pi with C channels, K radial functions, gnz (m1, m3) pairs, p12 (m1, m2) pairs,
+    nnz CG terms and component counts d1, d2, d3:
+      forward     C (K + gnz + min(d1, d3)) per edge (w = phi A, T = G x, w applied on the smaller side)
+      source bwd  the same per edge (x-bar = w G^T mbar)
+      receiver bwd the cheaper of two exact forms: with T = G x, C (2 gnz + 3K + d3) per edge plus
+                  2 nnz per edge for Y-bar; or folded through R = sum c mbar (formed once per receiver,
+                  C nnz), C (p12 + 2 d2 + 3K) per edge (Q = x R, h = Y.Q, Y-bar += w Q, and the three K
+                  contractions w, phi-bar, A-bar)
+      prep        nnz per edge (G = sum c Y)
+    """
     K = plan.info["num_radial"]
-    mul_in = {}
-    fwd = recv = src = 0
-    nnz_total = 0
+    E, N = n_edges, n_nodes
+    deg = E / max(N, 1)
+    fwd = recv = prep = 0.0
     for k in range(plan.info["n_paths"]):
         d = plan.path(k)
         idx, _ = plan.cg_table(k)
         gnz = len({(int(a), int(c)) for a, _, c in idx})
+        p12 = len({(int(a), int(b)) for a, b, _ in idx})
         nnz = len(idx)
-        nnz_total += nnz
-        d1, d3 = 2 * d["l1"] + 1, 2 * d["l3"] + 1
+        d1, d2, d3 = 2 * d["l1"] + 1, 2 * d["l2"] + 1, 2 * d["l3"] + 1
         C = d["n_weights"]  # channelwise: one weight per channel
         fwd += C * (K + gnz + min(d1, d3))
-        src += C * (K + gnz + min(d1, d3))
-        recv += C * (2 * gnz + 3 * K + d3)
-        mul_in[k] = C
-    recv += 2 * nnz_total
-    return {"cgtp_fwd": fwd, "cgtp_prep": nnz_total, "cgtp_bwd_recv": recv, "cgtp_bwd_src": src}
+        plain = C * (2 * gnz + 3 * K + d3) + 2 * nnz
+        fold = C * (p12 + 2 * d2 + 3 * K) + C * nnz / deg
+        recv += min(plain, fold)
+        prep += nnz
+    return {"cgtp_fwd": fwd * E, "cgtp_prep": prep * E, "cgtp_bwd_recv": recv * E, "cgtp_bwd_src": fwd * E}
 
 
 def main() -> int:
@@ -132,13 +143,13 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
     prof = cg._lib.profile_end()
-    fma = algorithmic_fma_per_edge(plan)
+    fma = algorithmic_fma(plan, E, w.n_nodes)
     kernels = {}
     for name, (n, ms) in prof.items():
         avg_us = 1e3 * ms / n
         entry = {"launches_per_step": n / args.profile_steps, "avg_us": round(avg_us, 2)}
         if name in fma:
-            flop = 2.0 * fma[name] * E  # one launch covers every edge (single receiver chunk)
+            flop = 2.0 * fma[name]  # one launch covers every edge (single receiver chunk)
             entry["tflops"] = round(flop / (avg_us * 1e-6) / 1e12, 3)
         kernels[name] = entry
     dominant = max(prof, key=lambda k: prof[k][1])
@@ -147,7 +158,7 @@ def main() -> int:
     roofline = {"kernel": dominant, "bound": "alu", "achieved": achieved, "peak": round(PEAK_FP32_ALU_TFLOPS, 1),
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_ALU_TFLOPS, 4) if achieved else None,
                 "traffic": None}
-    step_flop = 2.0 * E * (fma["cgtp_fwd"] + 2 * fma["cgtp_prep"] + fma["cgtp_bwd_recv"] + fma["cgtp_bwd_src"])
+    step_flop = 2.0 * (fma["cgtp_fwd"] + 2 * fma["cgtp_prep"] + fma["cgtp_bwd_recv"] + fma["cgtp_bwd_src"])
 
     result = {
         "metric": "edges/sec for CGTP conv fwd+bwd, MACE-like irreps, fp32",

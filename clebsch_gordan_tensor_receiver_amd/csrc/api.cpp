@@ -76,7 +76,8 @@ BwdLayout bwd_layout(const cgtp::Plan& p, const cgtp::Graph& g) {
   L.ntask_s = int(cgtp::source_tasks(p).size());
   L.V = cgtp::edge_partial_width(p);
   L.row = L.ntask_r * L.V;
-  long long row_bytes = (long long)(p.g_stride + L.row) * (long long)p.elem();
+  const int grow = cgtp::bwd_row_stride(p);
+  long long row_bytes = (long long)(grow + L.row) * (long long)p.elem();
   L.cap = std::max<long long>(std::max<long long>(1, (long long)(p.scratch_budget / size_t(row_bytes))),
                               g.max_in_degree);
   L.chunks = g.chunks(L.cap);
@@ -89,7 +90,7 @@ BwdLayout bwd_layout(const cgtp::Plan& p, const cgtp::Graph& g) {
   }
   size_t off = 0;
   L.g_off = off;
-  off += align256(size_t(emax) * size_t(p.g_stride) * p.elem());
+  off += align256(size_t(emax) * size_t(grow) * p.elem());
   L.ep_off = off;
   off += align256(size_t(emax) * size_t(L.row) * p.elem());
   L.ap_off = off;
@@ -104,7 +105,7 @@ BwdLayout bwd_layout(const cgtp::Plan& p, const cgtp::Graph& g) {
 // partials of the receiver pass, A-bar-dot slots and an edge-vector buffer.
 BwdLayout dbl_layout(const cgtp::Plan& p, const cgtp::Graph& g) {
   BwdLayout L;
-  L.ntask_r = int(cgtp::recv_backward_tasks(p).size());
+  L.ntask_r = int(cgtp::dbl_recv_tasks(p).size());
   L.ntask_s = int(cgtp::source_tasks(p).size());
   L.V = cgtp::dbl_partial_width(p);
   L.row = L.ntask_r * L.V;

@@ -30,6 +30,7 @@
 
 #include <cstdio>
 #include <functional>
+#include <map>
 #include <numeric>
 #include <set>
 #include <sstream>
@@ -158,8 +159,9 @@ void emit_edge_vector(Out& o) {
 // prep: lane = edge, one wave per 64 edges; writes the G row of every edge of [e0, e1) at
 // G + (e - e0) * stride.  Rows are produced 64 values at a time into an LDS tile and copied out
 // with 16-byte stores in which 16 lanes cover 256 contiguous bytes of one row.
-void emit_prep(Out& o, const Plan& p) {
+void emit_prep(Out& o, const Plan& p, bool with_y) {
   const int per = p.dtype == CGTP_F64 ? 2 : 4;  // values per 16-byte unit
+  const int stride = with_y ? bwd_row_stride(p) : p.g_stride;
   const int block_vals = 16 * per;             // values per tile column block
   o.line("extern \"C\" __global__ void __launch_bounds__(64)");
   o.open("cgtp_prep(const real* __restrict__ pos, const real* __restrict__ shift, const int* __restrict__ recv,"
@@ -185,9 +187,12 @@ void emit_prep(Out& o, const Plan& p) {
     }
   }
   while (int(vals.size()) < p.g_stride) vals.push_back("R(0)");
-  const int nblocks = (p.g_stride + block_vals - 1) / block_vals;
+  if (with_y)
+    for (int m = 0; m < p.sh_dim; ++m) vals.push_back(F("Y[%d]", m));
+  while (int(vals.size()) < stride) vals.push_back("R(0)");
+  const int nblocks = (stride + block_vals - 1) / block_vals;
   for (int b = 0; b < nblocks; ++b) {
-    const int v0 = b * block_vals, nv = std::min(block_vals, p.g_stride - v0) / per;
+    const int v0 = b * block_vals, nv = std::min(block_vals, stride - v0) / per;
     o.open("");
     for (int k = 0; k < nv; ++k) {
       std::string v;
@@ -198,7 +203,7 @@ void emit_prep(Out& o, const Plan& p) {
     o.open("for (int it = 0; it < 16; ++it)");
     o.line("const int row = it * 4 + (lane >> 4), c = lane & 15;");
     o.line(F("if (eb + row < e1 && c < %d) ((V4*)(G + (i64)(eb + row - e0) * %d + %d))[c] = tile[row * 17 + c];", nv,
-             p.g_stride, v0));
+             stride, v0));
     o.close();
     o.line("__syncthreads();");
     o.close();
@@ -278,8 +283,10 @@ constexpr int kRecvGroup = 4;  // receivers (one wave each) per workgroup in the
 // pipelining), so their latency overlaps the arithmetic of the current edge.  The body sees
 // e, j, g (G row), f<q> (phi) and x<b>_<m>.
 void emit_recv_edge_loop(Out& o, const Plan& p, const std::vector<int>& blocks, const std::string& start,
-                         const std::string& stride, const std::function<void()>& body, bool block_uc) {
+                         const std::string& stride, const std::function<void()>& body, bool block_uc,
+                         int row_stride) {
   auto ucn = [&](int b) { return block_uc ? F("uc%d", b) : std::string("uc"); };
+  if (row_stride <= 0) row_stride = p.g_stride;
   o.open("");
   o.line("int e = e0 + " + start + ";");
   o.open("if (e < e1)");
@@ -300,7 +307,7 @@ void emit_recv_edge_loop(Out& o, const Plan& p, const std::vector<int>& blocks, 
       o.line(F("xn%d_%d = x[(i64)jn * %d + %d + %s];", b, m, p.c_in, B.offset + m * B.mul, ucn(b).c_str()));
   }
   o.line(F("const real* __restrict__ ph = phi + (i64)e * %d;", p.K));
-  o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", p.g_stride));
+  o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", row_stride));
   for (int q = 0; q < p.K; ++q) o.line(F("const real f%d = ph[%d];", q, q));
   o.line("(void)j;");
   body();
@@ -481,15 +488,39 @@ const char* kRecvArgs =
     " const real* __restrict__ G, const int* __restrict__ row_ptr, const int* __restrict__ col,"
     " const real* __restrict__ gout, real* __restrict__ ep, real* __restrict__ ap";
 
+// (m1, m2) pairs of a path's CG tensor with their (m3, c) terms: R[m1, m2] = sum_m3 c mbar[m3].
+std::vector<std::pair<std::pair<int, int>, std::vector<std::pair<int, double>>>> m12_pairs(const Path& P) {
+  std::vector<std::pair<std::pair<int, int>, std::vector<std::pair<int, double>>>> v;
+  for (const CGTerm& t : P.terms) {
+    std::pair<int, int> key{t.m1, t.m2};
+    auto it = std::find_if(v.begin(), v.end(), [&](const auto& e) { return e.first == key; });
+    if (it == v.end()) {
+      v.push_back({key, {}});
+      it = v.end() - 1;
+    }
+    it->second.push_back({t.m3, t.c});
+  }
+  return v;
+}
+
+// A path of the receiver backward runs in "receiver-folded" form when its (m1, m2) table fits the
+// register budget: R = sum_m3 c mbar[m3] is formed once per receiver, and per edge
+// Q[m2] = sum_m1 x[m1] R[m1, m2] gives both h = sum_m2 Y[m2] Q[m2] (Eq. 18) and the Y-bar
+// partials w Q[m2] (Eq. 22) without forming T = G x.
+constexpr int kFoldMax = 48;     // largest (m1, m2) table kept in registers
+constexpr int kRecvBudget = 176;  // registers per lane for A, the A-bar accumulators and R of one task
+
+bool folded(const Path& P) { return int(m12_pairs(P).size()) <= kFoldMax; }
+
 // Receiver-major backward of task (output block k, path subset, channel block) for one receiver
 // per wave (node < 0: no receiver).  Per edge: h_pi = <mbar, T_pi> (Eq. 18), phi-bar partials
 // sum_pi A h (Eq. 20) and Y-bar partials sum_pi w sum c x mbar (Eq. 22), reduced over the 64
 // channels of the wave and stored in slot `ti` of the edge's partial column.  A-bar = sum_e phi h
 // (Eq. 19) accumulates in registers, is combined over the kRecvGroup waves of the workgroup in
-// LDS and added to the workgroup's partial slot.
+// LDS and added to the workgroup's partial slot.  Folded paths read Y from the edge's workspace
+// row (after the G values); the others contract G as in the forward.
 void emit_bwd_recv_task(Out& o, const Plan& p, int ti, const Task& T, int V) {
-  const Block& OB = p.out[T.group];
-  const int d3 = OB.dim(), MUL = OB.mul, K = p.K;
+  const int MUL = p.out[p.paths[T.paths[0]].i_out].mul, K = p.K;
   o.open(F("DEV void bwr_t%d(%s, real* sm, int node, int e_base, int eps, int slot)", ti, kRecvArgs));
   o.line("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
   o.line(F("const int u = %d + lane;", T.cb * 64));
@@ -502,15 +533,56 @@ void emit_bwd_recv_task(Out& o, const Plan& p, int ti, const Task& T, int V) {
       aa.push_back(F("aa%d", int(aa.size())));
     }
   o.open("if (node >= 0)");
-  o.line(F("const real* __restrict__ gr = gout + (i64)node * %d + %d + uc;", p.c_out, OB.offset));
-  for (int m = 0; m < d3; ++m) o.line(F("const real mb%d = u < %d ? gr[%d] : R(0);", m, MUL, m * MUL));
+  o.line(F("const real* __restrict__ gr = gout + (i64)node * %d + uc;", p.c_out));
+  for (int ob : out_blocks_of(p, T.paths)) {
+    const Block& OB = p.out[ob];
+    for (int m = 0; m < OB.dim(); ++m)
+      o.line(F("const real mb%d_%d = u < %d ? gr[%d] : R(0);", ob, m, MUL, OB.offset + m * MUL));
+  }
+  for (int pi : T.paths) {
+    const Path& P = p.paths[pi];
+    if (!folded(P)) continue;
+    for (auto& pr : m12_pairs(P)) {
+      std::string ex;
+      for (auto& t : pr.second)
+        ex += (ex.empty() ? "" : " + ") + lit(t.second) + F(" * mb%d_%d", P.i_out, t.first);
+      o.line(F("const real r%d_%d_%d = ", pi, pr.first.first, pr.first.second) + ex + ";");
+    }
+  }
   o.line("const int e0 = row_ptr[node], e1 = row_ptr[node + 1];");
+  const int yoff = p.g_stride;  // Y values follow the G values in a workspace row
   emit_recv_edge_loop(o, p, in_blocks_of(p, T.paths), "0", "1", [&] {
     for (int v = 0; v < V; ++v) o.line(F("real v%d = R(0);", v));
     int ai = 0;
     for (int pi : T.paths) {
       const Path& P = p.paths[pi];
       const int s = K + P.l2 * P.l2;  // Y-bar slot of this path's SH block
+      const int d2 = 2 * P.l2 + 1;
+      emit_w(o, p, pi);
+      if (folded(P)) {
+        std::vector<bool> qs(d2, false);
+        for (auto& pr : m12_pairs(P)) {
+          int m1 = pr.first.first, m2 = pr.first.second;
+          if (!qs[m2]) o.line(F("real q%d_%d = x%d_%d * r%d_%d_%d;", pi, m2, P.i_in, m1, pi, m1, m2));
+          else o.line(F("q%d_%d = fma(x%d_%d, r%d_%d_%d, q%d_%d);", pi, m2, P.i_in, m1, pi, m1, m2, pi, m2));
+          qs[m2] = true;
+        }
+        bool first = true;
+        for (int m = 0; m < d2; ++m)
+          if (qs[m]) {
+            if (first) o.line(F("real h%d = g[%d] * q%d_%d;", pi, yoff + P.l2 * P.l2 + m, pi, m));
+            else o.line(F("h%d = fma(g[%d], q%d_%d, h%d);", pi, yoff + P.l2 * P.l2 + m, pi, m, pi));
+            first = false;
+          }
+        for (int q = 0; q < K; ++q, ++ai) {
+          o.line(F("aa%d = fma(f%d, h%d, aa%d);", ai, q, pi, ai));
+          o.line(F("v%d = fma(a%d_%d, h%d, v%d);", q, pi, q, pi, q));
+        }
+        for (int m = 0; m < d2; ++m)
+          if (qs[m]) o.line(F("v%d = fma(w%d, q%d_%d, v%d);", s + m, pi, pi, m, s + m));
+        continue;
+      }
+      const int d3 = 2 * P.l3 + 1, ob = P.i_out;
       std::vector<bool> started(d3, false);
       for (size_t t = 0; t < P.gpairs.size(); ++t) {
         int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3;
@@ -523,18 +595,17 @@ void emit_bwd_recv_task(Out& o, const Plan& p, int ti, const Task& T, int V) {
       bool first = true;
       for (int m = 0; m < d3; ++m)
         if (started[m]) {
-          if (first) o.line(F("real h%d = mb%d * t%d_%d;", pi, m, pi, m));
-          else o.line(F("h%d = fma(mb%d, t%d_%d, h%d);", pi, m, pi, m, pi));
+          if (first) o.line(F("real h%d = mb%d_%d * t%d_%d;", pi, ob, m, pi, m));
+          else o.line(F("h%d = fma(mb%d_%d, t%d_%d, h%d);", pi, ob, m, pi, m, pi));
           first = false;
         }
-      emit_w(o, p, pi);
       for (int q = 0; q < K; ++q, ++ai) {
         o.line(F("aa%d = fma(f%d, h%d, aa%d);", ai, q, pi, ai));
         o.line(F("v%d = fma(a%d_%d, h%d, v%d);", q, pi, q, pi, q));
       }
       std::set<int> m3used;
       for (auto& gp : P.gpairs) m3used.insert(gp.m3);
-      for (int m : m3used) o.line(F("const real wm%d_%d = w%d * mb%d;", pi, m, pi, m));
+      for (int m : m3used) o.line(F("const real wm%d_%d = w%d * mb%d_%d;", pi, m, pi, ob, m));
       for (auto& gp : P.gpairs) {
         o.line(F("{ const real z = x%d_%d * wm%d_%d;", P.i_in, gp.m1, pi, gp.m3));
         for (auto& t : gp.terms)
@@ -558,7 +629,7 @@ void emit_bwd_recv_task(Out& o, const Plan& p, int ti, const Task& T, int V) {
     o.line(F("real* __restrict__ dst = ep + (i64)(%d + (lane >> 4) * %d) * eps + (e - e_base);", ti * V, Q));
     for (int k = 0; k < Q; ++k) o.line(F("dst[(i64)%d * eps] = v%d;", k, k));
     o.close();
-  });
+  }, false, bwd_row_stride(p));
   o.close();  // node >= 0
   emit_wave_combine(o, "aa", int(aa.size()), kRecvGroup);
   o.open(F("if (w == 0 && u < %d)", MUL));
@@ -637,7 +708,7 @@ void emit_bwd_src_task(Out& o, const Plan& p, int ti, const Task& T) {
         o.line(F("mn%d_%d = gout[(i64)in_ * %d + %d + uc];", ob, m, p.c_out, B.offset + m * B.mul));
     }
     o.line(F("const real* __restrict__ ph = phi + (i64)e * %d;", K));
-    o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", p.g_stride));
+    o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", bwd_row_stride(p)));
     for (int q = 0; q < K; ++q) o.line(F("const real f%d = ph[%d];", q, q));
     for (int pi : S) {
       const Path& P = p.paths[pi];
@@ -801,11 +872,56 @@ std::vector<Task> forward_tasks(const Plan& p) {
 }
 
 std::vector<Task> recv_backward_tasks(const Plan& p) {
+  // Paths of every output block with the same multiplicity and 64-channel block are packed into
+  // as few tasks as the register budget allows (first-fit, heaviest first): each task reduces its
+  // per-edge partial sums over the channels once, however many output blocks it covers.  The
+  // budget counts, per path, A and the A-bar accumulators (2K) plus the R table of folded paths.
+  auto regs = [&](int pi) {
+    const Path& P = p.paths[pi];
+    return 2 * p.K + (folded(P) ? int(m12_pairs(P).size()) : 2 * P.l3 + 1);
+  };
+  std::map<std::pair<int, int>, std::vector<int>> by_key;  // (mul, channel block) -> paths
+  for (int pi = 0; pi < int(p.paths.size()); ++pi) {
+    const int mul = p.out[p.paths[pi].i_out].mul;
+    for (int cb = 0; cb * 64 < mul; ++cb) by_key[{mul, cb}].push_back(pi);
+  }
+  std::vector<std::pair<int, Task>> tasks;  // (cost, task)
+  for (auto& kv : by_key) {
+    std::vector<int> order = kv.second;
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return regs(a) > regs(b); });
+    std::vector<Task> bins;
+    std::vector<int> used;
+    for (int pi : order) {
+      size_t b = 0;
+      while (b < bins.size() && used[b] + regs(pi) > kRecvBudget) ++b;
+      if (b == bins.size()) {
+        bins.push_back({p.paths[pi].i_out, kv.first.second, {}});
+        used.push_back(0);
+      }
+      bins[b].paths.push_back(pi);
+      used[b] += regs(pi);
+    }
+    for (Task& t : bins) {
+      std::sort(t.paths.begin(), t.paths.end());
+      int cost = 0;
+      for (int pi : t.paths) cost += path_cost(p, p.paths[pi]);
+      tasks.push_back({cost, t});
+    }
+  }
+  std::stable_sort(tasks.begin(), tasks.end(), [](const auto& a, const auto& b) { return a.first > b.first; });
+  std::vector<Task> t;
+  for (auto& c : tasks) t.push_back(c.second);
+  return t;
+}
+
+std::vector<Task> dbl_recv_tasks(const Plan& p) {
   std::vector<Task> t;
   for (const Task& f : forward_tasks(p))
     for (const auto& S : subsets(p, f.paths)) t.push_back({f.group, f.cb, S});
   return t;
 }
+
+int bwd_row_stride(const Plan& p) { return (p.g_stride + p.sh_dim + 3) / 4 * 4; }
 
 std::vector<Task> source_tasks(const Plan& p) {
   std::vector<Task> t;
@@ -844,7 +960,7 @@ std::string generate_source(const Plan& p, const std::string& family, std::strin
   if (family == "bwd") {
     prelude(o, p, true, true);
     emit_sh(o, p.lmax);
-    emit_prep(o, p);
+    emit_prep(o, p, true);
     const int V = edge_partial_width(p);
     auto rt = recv_backward_tasks(p);
     for (int k = 0; k < int(rt.size()); ++k) emit_bwd_recv_task(o, p, k, rt[k], V);

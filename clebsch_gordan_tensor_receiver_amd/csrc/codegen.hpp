@@ -49,11 +49,12 @@ std::vector<std::vector<int>> subsets(const Plan& p, const std::vector<int>& pat
 void prelude(Out& o, const Plan& p, bool dual, bool reduce);
 void emit_sh(Out& o, int L);
 void emit_edge_vector(Out& o);
-void emit_prep(Out& o, const Plan& p);
+void emit_prep(Out& o, const Plan& p, bool with_y = false);
 std::vector<int> in_blocks_of(const Plan& p, const std::vector<int>& paths);
 std::vector<int> out_blocks_of(const Plan& p, const std::vector<int>& paths);
 void emit_recv_edge_loop(Out& o, const Plan& p, const std::vector<int>& blocks, const std::string& start,
-                         const std::string& stride, const std::function<void()>& body, bool block_uc = false);
+                         const std::string& stride, const std::function<void()>& body, bool block_uc = false,
+                         int row_stride = 0);
 void emit_wave_combine(Out& o, const std::string& prefix, int n, int nw);
 void emit_swaps(Out& o, const std::vector<std::pair<std::string, std::string>>& pairs, int width, bool f64);
 void emit_edge_final(Out& o, const Plan& p, int ntask, int V);

@@ -472,7 +472,7 @@ std::string generate_dbl_source(const Plan& p, std::string* err) {
   o.close();
   o.close();
   const int V = dbl_partial_width(p);
-  auto rt = recv_backward_tasks(p);
+  auto rt = dbl_recv_tasks(p);
   int amax = 0;
   for (int k = 0; k < int(rt.size()); ++k) {
     emit_drecv_task(o, p, k, rt[k], V);

@@ -41,7 +41,11 @@ struct Task {
 };
 std::vector<Task> forward_tasks(const Plan& p);
 std::vector<Task> recv_backward_tasks(const Plan& p);
+std::vector<Task> dbl_recv_tasks(const Plan& p);
 std::vector<Task> source_tasks(const Plan& p);
+// Values per edge in the backward's workspace rows: the G row (g_stride values) followed by the
+// spherical harmonics Y (sh_dim values), padded to a multiple of 4.
+int bwd_row_stride(const Plan& p);
 // Values per edge and task written by the receiver backward (phi-bar partials then
 // Y-bar partials), padded to a multiple of 4.
 int edge_partial_width(const Plan& p);
