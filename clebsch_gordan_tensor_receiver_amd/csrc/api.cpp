@@ -74,8 +74,8 @@ BwdLayout bwd_layout(const cgtp::Plan& p, const cgtp::Graph& g) {
   BwdLayout L;
   L.ntask_r = int(cgtp::recv_backward_tasks(p).size());
   L.ntask_s = int(cgtp::source_tasks(p).size());
-  L.V = cgtp::edge_partial_width(p);
-  L.row = L.ntask_r * L.V;
+  L.V = 0;
+  L.row = cgtp::recv_partial_row(p);
   const int grow = cgtp::bwd_row_stride(p);
   long long row_bytes = (long long)(grow + L.row) * (long long)p.elem();
   L.cap = std::max<long long>(std::max<long long>(1, (long long)(p.scratch_budget / size_t(row_bytes))),

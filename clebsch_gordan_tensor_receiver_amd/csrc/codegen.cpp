@@ -316,6 +316,46 @@ void emit_recv_edge_loop(Out& o, const Plan& p, const std::vector<int>& blocks, 
   o.close();
 }
 
+// Loop over all in-edges of a receiver (`e0`, `e1` in scope), unrolled by two so that the rows x_j
+// prefetched one edge ahead alternate between two register sets (no copies between iterations).
+// The body sees e, g (workspace row of `row_stride` values), f<q> (phi) and x<b>_<m>.
+void emit_recv_edge_loop2(Out& o, const Plan& p, const std::vector<int>& blocks, int row_stride,
+                          const std::function<void()>& body) {
+  auto xrow = [&](const char* set) {
+    for (int b : blocks) {
+      const Block& B = p.in[b];
+      for (int m = 0; m < B.dim(); ++m)
+        o.line(F("%s%d_%d = x[(i64)jn * %d + %d + uc];", set, b, m, p.c_in, B.offset + m * B.mul));
+    }
+  };
+  auto half = [&](const char* cur, const char* next) {
+    o.open("");
+    o.line("{ const int en = e + 1; jn = col[en < e1 ? en : e]; }");
+    xrow(next);
+    for (int b : blocks)
+      for (int m = 0; m < p.in[b].dim(); ++m) o.line(F("const real x%d_%d = %s%d_%d;", b, m, cur, b, m));
+    o.line(F("const real* __restrict__ ph = phi + (i64)e * %d;", p.K));
+    o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", row_stride));
+    for (int q = 0; q < p.K; ++q) o.line(F("const real f%d = ph[%d];", q, q));
+    body();
+    o.close();
+    o.line("if (++e >= e1) break;");
+  };
+  o.open("");
+  o.line("int e = e0;");
+  o.open("if (e < e1)");
+  o.line("int jn = col[e];");
+  for (int b : blocks)
+    for (int m = 0; m < p.in[b].dim(); ++m) o.line(F("real xa%d_%d, xb%d_%d;", b, m, b, m));
+  xrow("xa");
+  o.open("for (;;)");
+  half("xa", "xb");
+  half("xb", "xa");
+  o.close();
+  o.close();
+  o.close();
+}
+
 // Combine per-wave partial sums acc<m> (m < n) of the waves of a workgroup through LDS in a fixed
 // order; afterwards wave 0 holds the total.  `sm` must hold (nw - 1) * n * 64 values.
 void emit_wave_combine(Out& o, const std::string& prefix, int n, int nw) {
@@ -519,8 +559,11 @@ bool folded(const Path& P) { return int(m12_pairs(P).size()) <= kFoldMax; }
 // (Eq. 19) accumulates in registers, is combined over the kRecvGroup waves of the workgroup in
 // LDS and added to the workgroup's partial slot.  Folded paths read Y from the edge's workspace
 // row (after the G values); the others contract G as in the forward.
-void emit_bwd_recv_task(Out& o, const Plan& p, int ti, const Task& T, int V) {
+void emit_bwd_recv_task(Out& o, const Plan& p, int ti, const Task& T, int col_off, int row) {
   const int MUL = p.out[p.paths[T.paths[0]].i_out].mul, K = p.K;
+  const std::vector<int> ycols = recv_task_ycols(p, T);
+  const int V = recv_task_width(p, T);
+  auto ycol = [&](int y) { return K + int(std::find(ycols.begin(), ycols.end(), y) - ycols.begin()); };
   o.open(F("DEV void bwr_t%d(%s, real* sm, int node, int e_base, int eps, int slot)", ti, kRecvArgs));
   o.line("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
   o.line(F("const int u = %d + lane;", T.cb * 64));
@@ -551,7 +594,7 @@ void emit_bwd_recv_task(Out& o, const Plan& p, int ti, const Task& T, int V) {
   }
   o.line("const int e0 = row_ptr[node], e1 = row_ptr[node + 1];");
   const int yoff = p.g_stride;  // Y values follow the G values in a workspace row
-  emit_recv_edge_loop(o, p, in_blocks_of(p, T.paths), "0", "1", [&] {
+  emit_recv_edge_loop2(o, p, in_blocks_of(p, T.paths), bwd_row_stride(p), [&] {
     for (int v = 0; v < V; ++v) o.line(F("real v%d = R(0);", v));
     int ai = 0;
     for (int pi : T.paths) {
@@ -579,7 +622,7 @@ void emit_bwd_recv_task(Out& o, const Plan& p, int ti, const Task& T, int V) {
           o.line(F("v%d = fma(a%d_%d, h%d, v%d);", q, pi, q, pi, q));
         }
         for (int m = 0; m < d2; ++m)
-          if (qs[m]) o.line(F("v%d = fma(w%d, q%d_%d, v%d);", s + m, pi, pi, m, s + m));
+          if (qs[m]) o.line(F("v%d = fma(w%d, q%d_%d, v%d);", ycol(s - K + m), pi, pi, m, ycol(s - K + m)));
         continue;
       }
       const int d3 = 2 * P.l3 + 1, ob = P.i_out;
@@ -609,11 +652,13 @@ void emit_bwd_recv_task(Out& o, const Plan& p, int ti, const Task& T, int V) {
       for (auto& gp : P.gpairs) {
         o.line(F("{ const real z = x%d_%d * wm%d_%d;", P.i_in, gp.m1, pi, gp.m3));
         for (auto& t : gp.terms)
-          o.line(F("  v%d = fma(%s, z, v%d);", s + t.first, lit(t.second).c_str(), s + t.first));
+          o.line(F("  v%d = fma(%s, z, v%d);", ycol(s - K + t.first), lit(t.second).c_str(), ycol(s - K + t.first)));
         o.line("}");
       }
     }
-    // Transpose-reduce the V partial sums over the 64 lanes.
+    // Transpose-reduce the V partial sums over the 64 lanes: afterwards lane group r = lane / 16
+    // holds columns r Q .. r Q + Q - 1 in v0 .. v(Q-1).  The empty asm keeps the row sums in all
+    // lanes, so that their last DPP step is not moved under the store's lane mask.
     const int H = V / 2, Q = V / 4;
     const bool f64 = p.dtype == CGTP_F64;
     std::vector<std::pair<std::string, std::string>> pr;
@@ -624,12 +669,12 @@ void emit_bwd_recv_task(Out& o, const Plan& p, int ti, const Task& T, int V) {
     for (int k = 0; k < Q; ++k) pr.push_back({F("v%d", k), F("v%d", k + Q)});
     emit_swaps(o, pr, 16, f64);
     for (int k = 0; k < Q; ++k) o.line(F("v%d += v%d;", k, k + Q));
-    for (int k = 0; k < Q; ++k) o.line(F("v%d = rowsum(v%d);", k, k));
+    for (int k = 0; k < Q; ++k) o.line(F("v%d = rowsum(v%d); asm volatile(\"\" : \"+v\"(v%d));", k, k, k));
     o.open("if ((lane & 15) == 0)");
-    o.line(F("real* __restrict__ dst = ep + (i64)(%d + (lane >> 4) * %d) * eps + (e - e_base);", ti * V, Q));
-    for (int k = 0; k < Q; ++k) o.line(F("dst[(i64)%d * eps] = v%d;", k, k));
+    o.line(F("real* __restrict__ dst = ep + (i64)(e - e_base) * %d + %d + (lane >> 4) * %d;", row, col_off, Q));
+    for (int k = 0; k < Q; ++k) o.line(F("dst[%d] = v%d;", k, k));
     o.close();
-  }, false, bwd_row_stride(p));
+  });
   o.close();  // node >= 0
   emit_wave_combine(o, "aa", int(aa.size()), kRecvGroup);
   o.open(F("if (w == 0 && u < %d)", MUL));
@@ -808,6 +853,55 @@ void emit_edge_final(Out& o, const Plan& p, int ntask, int V) {
   o.close();
 }
 
+// Edge finalisation of the channelwise backward: the edge's partial row holds, task after task,
+// K phi-bar partials and the task's Y-bar columns; sums run over the tasks in a fixed order, then
+// e-bar = J_Y(r)^T Y-bar with J_Y = (I - n n^T) dY/dn / |r|.
+void emit_recv_edge_final(Out& o, const Plan& p, const std::vector<Task>& tasks) {
+  const int K = p.K, row = recv_partial_row(p);
+  std::vector<int> off;
+  for (int k = 0, c = 0; k < int(tasks.size()); c += recv_task_width(p, tasks[k]), ++k) off.push_back(c);
+  o.line("extern \"C\" __global__ void __launch_bounds__(256)");
+  o.open("cgtp_edge_final(const real* __restrict__ pos, const real* __restrict__ shift, const int* __restrict__ recv,"
+         " const int* __restrict__ send, const real* __restrict__ ep, int e0, int e1, int eps,"
+         " real* __restrict__ gphi, real* __restrict__ gev)");
+  o.line("(void)eps;");
+  o.line("const int e = e0 + (int)(blockIdx.x * 256 + threadIdx.x);");
+  o.line("if (e >= e1) return;");
+  o.line(F("const real* __restrict__ rw = ep + (i64)(e - e0) * %d;", row));
+  o.open("if (gphi)");
+  for (int q = 0; q < K; ++q) {
+    std::string ex;
+    for (size_t t = 0; t < tasks.size(); ++t) ex += (t ? " + " : "") + F("rw[%d]", off[t] + q);
+    o.line(F("gphi[(i64)e * %d + %d] = ", K, q) + ex + ";");
+  }
+  o.close();
+  o.line("if (!gev) return;");
+  emit_edge_vector(o);
+  o.line("const real inv = R(1) / sqrt(rx * rx + ry * ry + rz * rz);");
+  o.line("const real nx = rx * inv, ny = ry * inv, nz = rz * inv;");
+  o.line(F("D3 Y[%d];", p.sh_dim));
+  o.line("sh_eval<D3>(D3(nx, R(1), R(0), R(0)), D3(ny, R(0), R(1), R(0)), D3(nz, R(0), R(0), R(1)), Y);");
+  o.line("real gx = R(0), gy = R(0), gz = R(0);");
+  std::vector<std::vector<int>> yc;
+  for (const Task& t : tasks) yc.push_back(recv_task_ycols(p, t));
+  for (int m = 0; m < p.sh_dim; ++m) {
+    std::string ex;
+    for (size_t t = 0; t < tasks.size(); ++t) {
+      auto it = std::find(yc[t].begin(), yc[t].end(), m);
+      if (it == yc[t].end()) continue;
+      ex += (ex.empty() ? "" : " + ") + F("rw[%d]", off[t] + K + int(it - yc[t].begin()));
+    }
+    if (ex.empty()) continue;
+    o.line(F("{ const real yb = ") + ex + F("; gx = fma(yb, Y[%d].x, gx); gy = fma(yb, Y[%d].y, gy);"
+                                           " gz = fma(yb, Y[%d].z, gz); }", m, m, m));
+  }
+  o.line("const real d = nx * gx + ny * gy + nz * gz;");
+  o.line("gev[3 * (i64)e] = (gx - nx * d) * inv;");
+  o.line("gev[3 * (i64)e + 1] = (gy - ny * d) * inv;");
+  o.line("gev[3 * (i64)e + 2] = (gz - nz * d) * inv;");
+  o.close();
+}
+
 void emit_small_kernels(Out& o) {
   // Sum over the 64 lanes of a wave, the same value in every lane (fixed order).
   o.line("DEV real wave_total(real v) {");
@@ -885,6 +979,7 @@ std::vector<Task> recv_backward_tasks(const Plan& p) {
     const int mul = p.out[p.paths[pi].i_out].mul;
     for (int cb = 0; cb * 64 < mul; ++cb) by_key[{mul, cb}].push_back(pi);
   }
+  const int budget = p.dtype == CGTP_F64 ? kRecvBudget / 2 : kRecvBudget;  // 64-bit values take two registers
   std::vector<std::pair<int, Task>> tasks;  // (cost, task)
   for (auto& kv : by_key) {
     std::vector<int> order = kv.second;
@@ -893,7 +988,7 @@ std::vector<Task> recv_backward_tasks(const Plan& p) {
     std::vector<int> used;
     for (int pi : order) {
       size_t b = 0;
-      while (b < bins.size() && used[b] + regs(pi) > kRecvBudget) ++b;
+      while (b < bins.size() && used[b] + regs(pi) > budget) ++b;
       if (b == bins.size()) {
         bins.push_back({p.paths[pi].i_out, kv.first.second, {}});
         used.push_back(0);
@@ -922,6 +1017,23 @@ std::vector<Task> dbl_recv_tasks(const Plan& p) {
 }
 
 int bwd_row_stride(const Plan& p) { return (p.g_stride + p.sh_dim + 3) / 4 * 4; }
+
+std::vector<int> recv_task_ycols(const Plan& p, const Task& T) {
+  std::set<int> s;
+  for (int pi : T.paths) {
+    const Path& P = p.paths[pi];
+    for (const CGTerm& t : P.terms) s.insert(P.l2 * P.l2 + t.m2);
+  }
+  return std::vector<int>(s.begin(), s.end());
+}
+
+int recv_task_width(const Plan& p, const Task& T) { return (p.K + int(recv_task_ycols(p, T).size()) + 3) / 4 * 4; }
+
+int recv_partial_row(const Plan& p) {
+  int r = 0;
+  for (const Task& t : recv_backward_tasks(p)) r += recv_task_width(p, t);
+  return r;
+}
 
 std::vector<Task> source_tasks(const Plan& p) {
   std::vector<Task> t;
@@ -961,14 +1073,15 @@ std::string generate_source(const Plan& p, const std::string& family, std::strin
     prelude(o, p, true, true);
     emit_sh(o, p.lmax);
     emit_prep(o, p, true);
-    const int V = edge_partial_width(p);
     auto rt = recv_backward_tasks(p);
-    for (int k = 0; k < int(rt.size()); ++k) emit_bwd_recv_task(o, p, k, rt[k], V);
+    const int row = recv_partial_row(p);
+    for (int k = 0, off = 0; k < int(rt.size()); off += recv_task_width(p, rt[k]), ++k)
+      emit_bwd_recv_task(o, p, k, rt[k], off, row);
     emit_recv_dispatch(o, p, int(rt.size()));
     auto st = source_tasks(p);
     for (int k = 0; k < int(st.size()); ++k) emit_bwd_src_task(o, p, k, st[k]);
     emit_src_dispatch(o, p, int(st.size()));
-    emit_edge_final(o, p, int(rt.size()), V);
+    emit_recv_edge_final(o, p, rt);
     emit_small_kernels(o);
     return o.s.str();
   }

@@ -58,6 +58,7 @@ void emit_recv_edge_loop(Out& o, const Plan& p, const std::vector<int>& blocks, 
 void emit_wave_combine(Out& o, const std::string& prefix, int n, int nw);
 void emit_swaps(Out& o, const std::vector<std::pair<std::string, std::string>>& pairs, int width, bool f64);
 void emit_edge_final(Out& o, const Plan& p, int ntask, int V);
+void emit_recv_edge_final(Out& o, const Plan& p, const std::vector<Task>& tasks);
 void emit_small_kernels(Out& o);
 
 }  // namespace gen

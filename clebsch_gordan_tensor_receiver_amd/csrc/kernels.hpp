@@ -46,6 +46,12 @@ std::vector<Task> source_tasks(const Plan& p);
 // Values per edge in the backward's workspace rows: the G row (g_stride values) followed by the
 // spherical harmonics Y (sh_dim values), padded to a multiple of 4.
 int bwd_row_stride(const Plan& p);
+// Receiver-backward edge partials: per task, K phi-bar partials then the Y-bar columns the task's
+// paths touch (recv_task_ycols), padded to a multiple of 4; one row of recv_partial_row values
+// per edge, tasks in order.
+std::vector<int> recv_task_ycols(const Plan& p, const Task& T);
+int recv_task_width(const Plan& p, const Task& T);
+int recv_partial_row(const Plan& p);
 // Values per edge and task written by the receiver backward (phi-bar partials then
 // Y-bar partials), padded to a multiple of 4.
 int edge_partial_width(const Plan& p);
