@@ -92,7 +92,7 @@ BwdLayout bwd_layout(const cgtp::Plan& p, const cgtp::Graph& g) {
   L.g_off = off;
   off += align256(size_t(emax) * size_t(grow) * p.elem());
   L.ep_off = off;
-  off += align256(size_t(emax) * size_t(L.row) * p.elem());
+  off += align256(size_t((emax + 63) / 64 * 64) * size_t(L.row) * p.elem());  // tiles of 64 edges
   L.ap_off = off;
   off += align256(size_t(L.nslot) * size_t(p.K) * size_t(p.n_w) * p.elem());
   L.gev_off = off;
@@ -479,7 +479,7 @@ cgtp_status_t cgtp_conv_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x
     if (need_edge && e1 > e0) {
       void* a[] = {(void*)&pos, (void*)&shift, (void*)&d.recv, (void*)&d.col, &ep, &e0, &e1, &eps, &grad_phi,
                    &gev_arg};
-      if ((st = cgtp::launch(kfinal, unsigned((e1 - e0 + 255) / 256), 256, 0, s, a, &err)) != CGTP_OK)
+      if ((st = cgtp::launch(kfinal, unsigned((e1 - e0 + 63) / 64), 64, 0, s, a, &err)) != CGTP_OK)
         return fail(st, err);
     }
   }

@@ -56,6 +56,19 @@ long double fct(int n) {
 // Register budget: A coefficients held per lane for one subset of paths.
 constexpr int kRegBudget = 64;
 
+// Split a task's paths into consecutive subsets whose A coefficients (K per path) fit `avail`
+// registers; each subset re-walks the edge list (only tasks of one oversized block need more
+// than one).
+std::vector<std::vector<int>> a_subsets(const Plan& p, const std::vector<int>& paths, int avail) {
+  std::vector<std::vector<int>> out;
+  const int per = std::max(1, avail / std::max(1, p.K * (p.dtype == CGTP_F64 ? 2 : 1)));
+  for (int pi : paths) {
+    if (out.empty() || int(out.back().size()) >= per) out.push_back({});
+    out.back().push_back(pi);
+  }
+  return out;
+}
+
 std::vector<std::vector<int>> subsets(const Plan& p, const std::vector<int>& paths) {
   std::vector<std::vector<int>> out;
   for (int pi : paths) {
@@ -245,14 +258,16 @@ void emit_w(Out& o, const Plan& p, int pi) {
   for (int q = 1; q < p.K; ++q) o.line(F("w%d = fma(f%d, a%d_%d, w%d);", pi, q, pi, q, pi));
 }
 
-// acc<m3> += w * sum_m1 G[m1,m3] x[m1] for path pi, choosing where to apply w by cost.
-void emit_path_accumulate(Out& o, const Plan& p, int pi) {
+// acc<m3> += w * sum_m1 G[m1,m3] x[m1] for path pi, choosing where to apply w by cost.  The
+// accumulators are named <acc><m3>.
+void emit_path_accumulate(Out& o, const Plan& p, int pi, const std::string& acc = "acc") {
   const Path& P = p.paths[pi];
   const int d1 = 2 * P.l1 + 1, d3 = 2 * P.l3 + 1;
+  const char* A = acc.c_str();
   if (d1 <= d3) {
     for (int m = 0; m < d1; ++m) o.line(F("const real s%d_%d = w%d * x%d_%d;", pi, m, pi, P.i_in, m));
     for (size_t t = 0; t < P.gpairs.size(); ++t)
-      o.line(F("acc%d = fma(g[%d], s%d_%d, acc%d);", P.gpairs[t].m3, P.g_off + int(t), pi, P.gpairs[t].m1,
+      o.line(F("%s%d = fma(g[%d], s%d_%d, %s%d);", A, P.gpairs[t].m3, P.g_off + int(t), pi, P.gpairs[t].m1, A,
                P.gpairs[t].m3));
   } else {
     std::vector<bool> started(d3, false);
@@ -265,7 +280,7 @@ void emit_path_accumulate(Out& o, const Plan& p, int pi) {
       started[m3] = true;
     }
     for (int m = 0; m < d3; ++m)
-      if (started[m]) o.line(F("acc%d = fma(w%d, t%d_%d, acc%d);", m, pi, pi, m, m));
+      if (started[m]) o.line(F("%s%d = fma(w%d, t%d_%d, %s%d);", A, m, pi, pi, m, A, m));
   }
 }
 
@@ -370,34 +385,54 @@ void emit_wave_combine(Out& o, const std::string& prefix, int n, int nw) {
   o.close();
 }
 
+// emit_wave_combine over an explicit list of accumulator names.
+void emit_wave_combine_names(Out& o, const std::vector<std::string>& names, int nw) {
+  const int n = int(names.size());
+  o.open("if (w != 0)");
+  for (int m = 0; m < n; ++m) o.line(F("sm[((w - 1) * %d + %d) * 64 + lane] = %s;", n, m, names[m].c_str()));
+  o.close();
+  o.line("__syncthreads();");
+  o.open("if (w == 0)");
+  for (int k = 1; k < nw; ++k)
+    for (int m = 0; m < n; ++m) o.line(F("%s += sm[(%d * %d + %d) * 64 + lane];", names[m].c_str(), k - 1, n, m));
+  o.close();
+}
+
 // Channelwise conventional forward of task (output block k, channel block cb) for one receiver;
 // the receiver's edges are dealt round-robin to the kFwdSplit waves of the workgroup and their
 // partial sums combined in LDS.  Paths are processed in register-budgeted subsets, each
 // re-walking the edges.
 void emit_fwd_task(Out& o, const Plan& p, int ti, const Task& T) {
-  const Block& OB = p.out[T.group];
-  const int d3 = OB.dim(), MUL = OB.mul;
+  const int MUL = p.out[p.paths[T.paths[0]].i_out].mul;
+  const std::vector<int> obs = out_blocks_of(p, T.paths);
   o.open(F("DEV void fwd_t%d(%s, real* sm, int node, int e_base)", ti, kFwdArgs));
   o.line("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
   o.line(F("const int u = %d + lane;", T.cb * 64));
   o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
-  for (int m = 0; m < d3; ++m) o.line(F("real acc%d = R(0);", m));
+  std::vector<std::string> accs;
+  for (int ob : obs)
+    for (int m = 0; m < p.out[ob].dim(); ++m) {
+      accs.push_back(F("acc%d_%d", ob, m));
+      o.line("real " + accs.back() + " = R(0);");
+    }
   o.line("const int e0 = row_ptr[node], e1 = row_ptr[node + 1];");
-  for (const auto& S : subsets(p, T.paths)) {
+  for (const auto& S : a_subsets(p, T.paths, kRegBudget)) {
     o.open("");
     emit_a_loads(o, p, S);
     emit_recv_edge_loop(o, p, in_blocks_of(p, S), "w", std::to_string(kFwdSplit), [&] {
       for (int pi : S) {
         emit_w(o, p, pi);
-        emit_path_accumulate(o, p, pi);
+        emit_path_accumulate(o, p, pi, F("acc%d_", p.paths[pi].i_out));
       }
     });
     o.close();
   }
-  emit_wave_combine(o, "acc", d3, kFwdSplit);
+  emit_wave_combine_names(o, accs, kFwdSplit);
   o.open(F("if (w == 0 && u < %d)", MUL));
-  o.line(F("real* __restrict__ dst = out + (i64)node * %d + %d + u;", p.c_out, OB.offset));
-  for (int m = 0; m < d3; ++m) o.line(F("dst[%d] = acc%d;", m * MUL, m));
+  o.line(F("real* __restrict__ dst = out + (i64)node * %d + u;", p.c_out));
+  for (int ob : obs)
+    for (int m = 0; m < p.out[ob].dim(); ++m)
+      o.line(F("dst[%d] = acc%d_%d;", p.out[ob].offset + m * MUL, ob, m));
   o.close();
   o.close();
 }
@@ -463,10 +498,10 @@ int max_in_dim(const Plan& p) {
 // neighbours, whose senders' rows then stay in that XCD's L2) and runs the tasks in decreasing
 // cost order inside it (LunaTP section 4.2, task ordering).
 void emit_node_dispatch(Out& o, const Plan& p, const std::string& kname, const std::string& args,
-                        const std::string& call, int ntask) {
+                        const std::string& call, int ntask, int nacc) {
   o.line(F("extern \"C\" __global__ void __launch_bounds__(%d)", 64 * kFwdSplit));
   o.open(kname + "(" + args + ", int i0, int nrec, int per, int e_base)");
-  o.line(F("__shared__ real sm[%d];", (kFwdSplit - 1) * max_out_dim(p) * 64));
+  o.line(F("__shared__ real sm[%d];", (kFwdSplit - 1) * nacc * 64));
   o.line("const int b = (int)blockIdx.x;");
   o.line("const int xcd = b & 7, s = b >> 3;");
   o.line("const int t = s / per, il = s - t * per;");
@@ -671,8 +706,9 @@ void emit_bwd_recv_task(Out& o, const Plan& p, int ti, const Task& T, int col_of
     for (int k = 0; k < Q; ++k) o.line(F("v%d += v%d;", k, k + Q));
     for (int k = 0; k < Q; ++k) o.line(F("v%d = rowsum(v%d); asm volatile(\"\" : \"+v\"(v%d));", k, k, k));
     o.open("if ((lane & 15) == 0)");
-    o.line(F("real* __restrict__ dst = ep + (i64)(e - e_base) * %d + %d + (lane >> 4) * %d;", row, col_off, Q));
-    for (int k = 0; k < Q; ++k) o.line(F("dst[%d] = v%d;", k, k));
+    o.line(F("real* __restrict__ dst = ep + ((i64)((e - e_base) >> 6) * %d + %d + (lane >> 4) * %d) * 64"
+             " + ((e - e_base) & 63);", row, col_off, Q));
+    for (int k = 0; k < Q; ++k) o.line(F("dst[%d] = v%d;", 64 * k, k));
     o.close();
   });
   o.close();  // node >= 0
@@ -721,84 +757,97 @@ const char* kSrcArgs =
 // dealt round-robin to the kSrcSplit waves of the workgroup (partials combined in LDS); the
 // receivers' mbar rows of the next edge are loaded one edge ahead.
 void emit_bwd_src_task(Out& o, const Plan& p, int ti, const Task& T) {
-  const Block& IB = p.in[T.group];
-  const int d1 = IB.dim(), MUL = IB.mul, K = p.K;
+  const int MUL = p.in[p.paths[T.paths[0]].i_in].mul, K = p.K;
+  const std::vector<int> ibs = in_blocks_of(p, T.paths);
   o.open(F("DEV void bws_t%d(%s, real* sm, int node, int e_base, int accumulate)", ti, kSrcArgs));
   o.line("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
   o.line(F("const int u = %d + lane;", T.cb * 64));
   o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
-  for (int m = 0; m < d1; ++m) o.line(F("real acc%d = R(0);", m));
+  std::vector<std::string> accs;
+  for (int ib : ibs)
+    for (int m = 0; m < p.in[ib].dim(); ++m) {
+      accs.push_back(F("acc%d_%d", ib, m));
+      o.line("real " + accs.back() + " = R(0);");
+    }
   o.line("const int s0 = src_ptr[node], s1 = src_ptr[node + 1];");
-  for (const auto& S : subsets(p, T.paths)) {
-    o.open("");
-    emit_a_loads(o, p, S);
-    const auto obs = out_blocks_of(p, S);
-    o.line("int k = s0 + w;");
-    o.open("if (k < s1)");
-    o.line("int en = src_edge[k];");
-    o.line("int in_ = recv[en];");
-    for (int ob : obs) {
-      const Block& B = p.out[ob];
-      for (int m = 0; m < B.dim(); ++m)
-        o.line(F("real mn%d_%d = gout[(i64)in_ * %d + %d + uc];", ob, m, p.c_out, B.offset + m * B.mul));
-    }
-    o.open(F("for (; k < s1; k += %d)", kSrcSplit));
-    o.line("const int e = en;");
-    for (int ob : obs)
-      for (int m = 0; m < p.out[ob].dim(); ++m) o.line(F("const real mb%d_%d = mn%d_%d;", ob, m, ob, m));
-    o.line(F("{ const int kn = k + %d; en = src_edge[kn < s1 ? kn : k]; in_ = recv[en]; }", kSrcSplit));
-    for (int ob : obs) {
-      const Block& B = p.out[ob];
-      for (int m = 0; m < B.dim(); ++m)
-        o.line(F("mn%d_%d = gout[(i64)in_ * %d + %d + uc];", ob, m, p.c_out, B.offset + m * B.mul));
-    }
-    o.line(F("const real* __restrict__ ph = phi + (i64)e * %d;", K));
-    o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", bwd_row_stride(p)));
-    for (int q = 0; q < K; ++q) o.line(F("const real f%d = ph[%d];", q, q));
-    for (int pi : S) {
-      const Path& P = p.paths[pi];
-      const int d3 = 2 * P.l3 + 1;
-      emit_w(o, p, pi);
-      if (d3 <= d1) {
-        for (int m = 0; m < d3; ++m) o.line(F("const real s%d_%d = w%d * mb%d_%d;", pi, m, pi, P.i_out, m));
-        for (size_t t = 0; t < P.gpairs.size(); ++t)
-          o.line(F("acc%d = fma(g[%d], s%d_%d, acc%d);", P.gpairs[t].m1, P.g_off + int(t), pi, P.gpairs[t].m3,
-                   P.gpairs[t].m1));
-      } else {
-        std::vector<bool> started(d1, false);
-        for (size_t t = 0; t < P.gpairs.size(); ++t) {
-          int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3;
-          if (!started[m1])
-            o.line(F("real b%d_%d = g[%d] * mb%d_%d;", pi, m1, P.g_off + int(t), P.i_out, m3));
-          else
-            o.line(F("b%d_%d = fma(g[%d], mb%d_%d, b%d_%d);", pi, m1, P.g_off + int(t), P.i_out, m3, pi, m1));
-          started[m1] = true;
-        }
-        for (int m = 0; m < d1; ++m)
-          if (started[m]) o.line(F("acc%d = fma(w%d, b%d_%d, acc%d);", m, pi, pi, m, m));
-      }
-    }
-    o.close();
-    o.close();
-    o.close();
+  for (const auto& S : a_subsets(p, T.paths, kRegBudget)) {
+  o.open("");
+  emit_a_loads(o, p, S);
+  const auto obs = out_blocks_of(p, S);
+  o.line("int k = s0 + w;");
+  o.open("if (k < s1)");
+  o.line("int en = src_edge[k];");
+  o.line("int in_ = recv[en];");
+  for (int ob : obs) {
+    const Block& B = p.out[ob];
+    for (int m = 0; m < B.dim(); ++m)
+      o.line(F("real mn%d_%d = gout[(i64)in_ * %d + %d + uc];", ob, m, p.c_out, B.offset + m * B.mul));
   }
-  emit_wave_combine(o, "acc", d1, kSrcSplit);
+  o.open(F("for (; k < s1; k += %d)", kSrcSplit));
+  o.line("const int e = en;");
+  for (int ob : obs)
+    for (int m = 0; m < p.out[ob].dim(); ++m) o.line(F("const real mb%d_%d = mn%d_%d;", ob, m, ob, m));
+  o.line(F("{ const int kn = k + %d; en = src_edge[kn < s1 ? kn : k]; in_ = recv[en]; }", kSrcSplit));
+  for (int ob : obs) {
+    const Block& B = p.out[ob];
+    for (int m = 0; m < B.dim(); ++m)
+      o.line(F("mn%d_%d = gout[(i64)in_ * %d + %d + uc];", ob, m, p.c_out, B.offset + m * B.mul));
+  }
+  o.line(F("const real* __restrict__ ph = phi + (i64)e * %d;", K));
+  o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", bwd_row_stride(p)));
+  for (int q = 0; q < K; ++q) o.line(F("const real f%d = ph[%d];", q, q));
+  for (int pi : S) {
+    const Path& P = p.paths[pi];
+    const int d1 = 2 * P.l1 + 1, d3 = 2 * P.l3 + 1, ib = P.i_in;
+    emit_w(o, p, pi);
+    if (d3 <= d1) {
+      for (int m = 0; m < d3; ++m) o.line(F("const real s%d_%d = w%d * mb%d_%d;", pi, m, pi, P.i_out, m));
+      for (size_t t = 0; t < P.gpairs.size(); ++t)
+        o.line(F("acc%d_%d = fma(g[%d], s%d_%d, acc%d_%d);", ib, P.gpairs[t].m1, P.g_off + int(t), pi,
+                 P.gpairs[t].m3, ib, P.gpairs[t].m1));
+    } else {
+      std::vector<bool> started(d1, false);
+      for (size_t t = 0; t < P.gpairs.size(); ++t) {
+        int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3;
+        if (!started[m1])
+          o.line(F("real b%d_%d = g[%d] * mb%d_%d;", pi, m1, P.g_off + int(t), P.i_out, m3));
+        else
+          o.line(F("b%d_%d = fma(g[%d], mb%d_%d, b%d_%d);", pi, m1, P.g_off + int(t), P.i_out, m3, pi, m1));
+        started[m1] = true;
+      }
+      for (int m = 0; m < d1; ++m)
+        if (started[m]) o.line(F("acc%d_%d = fma(w%d, b%d_%d, acc%d_%d);", ib, m, pi, pi, m, ib, m));
+    }
+  }
+  o.close();
+  o.close();
+  o.close();
+  }
+  emit_wave_combine_names(o, accs, kSrcSplit);
   o.open(F("if (w == 0 && u < %d)", MUL));
-  o.line(F("real* __restrict__ dst = gx + (i64)node * %d + %d + u;", p.c_in, IB.offset));
+  o.line(F("real* __restrict__ dst = gx + (i64)node * %d + u;", p.c_in));
   o.open("if (accumulate)");
-  for (int m = 0; m < d1; ++m) o.line(F("dst[%d] += acc%d;", m * MUL, m));
+  for (int ib : ibs)
+    for (int m = 0; m < p.in[ib].dim(); ++m) o.line(F("dst[%d] += acc%d_%d;", p.in[ib].offset + m * MUL, ib, m));
   o.close("} else {");
   ++o.ind;
-  for (int m = 0; m < d1; ++m) o.line(F("dst[%d] = acc%d;", m * MUL, m));
+  for (int ib : ibs)
+    for (int m = 0; m < p.in[ib].dim(); ++m) o.line(F("dst[%d] = acc%d_%d;", p.in[ib].offset + m * MUL, ib, m));
   o.close();
   o.close();
   o.close();
 }
 
 void emit_src_dispatch(Out& o, const Plan& p, int ntask) {
+  int nacc = 1;
+  for (const Task& t : source_tasks(p)) {
+    int n = 0;
+    for (int ib : in_blocks_of(p, t.paths)) n += p.in[ib].dim();
+    nacc = std::max(nacc, n);
+  }
   o.line(F("extern \"C\" __global__ void __launch_bounds__(%d)", 64 * kSrcSplit));
   o.open(std::string("cgtp_bwd_src(") + kSrcArgs + ", int nrec, int per, int e_base, int accumulate)");
-  o.line(F("__shared__ real sm[%d];", (kSrcSplit - 1) * max_in_dim(p) * 64));
+  o.line(F("__shared__ real sm[%d];", (kSrcSplit - 1) * nacc * 64));
   o.line("const int b = (int)blockIdx.x;");
   o.line("const int xcd = b & 7, s = b >> 3;");
   o.line("const int t = s / per, il = s - t * per;");
@@ -855,23 +904,27 @@ void emit_edge_final(Out& o, const Plan& p, int ntask, int V) {
 
 // Edge finalisation of the channelwise backward: the edge's partial row holds, task after task,
 // K phi-bar partials and the task's Y-bar columns; sums run over the tasks in a fixed order, then
-// e-bar = J_Y(r)^T Y-bar with J_Y = (I - n n^T) dY/dn / |r|.
+// e-bar = J_Y(r)^T Y-bar with J_Y = (I - n n^T) dY/dn / |r|.  Partial rows are stored in tiles of
+// 64 edges, column-major inside a tile: column c of edge e sits at
+// ((e / 64) row + c) 64 + e mod 64, so that both the receiver pass (one base address, immediate
+// offsets) and this kernel (lane = edge) access them contiguously.
 void emit_recv_edge_final(Out& o, const Plan& p, const std::vector<Task>& tasks) {
   const int K = p.K, row = recv_partial_row(p);
   std::vector<int> off;
   for (int k = 0, c = 0; k < int(tasks.size()); c += recv_task_width(p, tasks[k]), ++k) off.push_back(c);
-  o.line("extern \"C\" __global__ void __launch_bounds__(256)");
+  o.line("extern \"C\" __global__ void __launch_bounds__(64)");
   o.open("cgtp_edge_final(const real* __restrict__ pos, const real* __restrict__ shift, const int* __restrict__ recv,"
          " const int* __restrict__ send, const real* __restrict__ ep, int e0, int e1, int eps,"
          " real* __restrict__ gphi, real* __restrict__ gev)");
   o.line("(void)eps;");
-  o.line("const int e = e0 + (int)(blockIdx.x * 256 + threadIdx.x);");
+  o.line("const int e = e0 + (int)(blockIdx.x * 64 + threadIdx.x);");
   o.line("if (e >= e1) return;");
-  o.line(F("const real* __restrict__ rw = ep + (i64)(e - e0) * %d;", row));
+  o.line(F("const real* __restrict__ rw = ep + (i64)((e - e0) >> 6) * %d + ((e - e0) & 63);", 64 * row));
+  o.line("#define RW(c) rw[64 * (c)]");
   o.open("if (gphi)");
   for (int q = 0; q < K; ++q) {
     std::string ex;
-    for (size_t t = 0; t < tasks.size(); ++t) ex += (t ? " + " : "") + F("rw[%d]", off[t] + q);
+    for (size_t t = 0; t < tasks.size(); ++t) ex += (t ? " + " : "") + F("RW(%d)", off[t] + q);
     o.line(F("gphi[(i64)e * %d + %d] = ", K, q) + ex + ";");
   }
   o.close();
@@ -889,7 +942,7 @@ void emit_recv_edge_final(Out& o, const Plan& p, const std::vector<Task>& tasks)
     for (size_t t = 0; t < tasks.size(); ++t) {
       auto it = std::find(yc[t].begin(), yc[t].end(), m);
       if (it == yc[t].end()) continue;
-      ex += (ex.empty() ? "" : " + ") + F("rw[%d]", off[t] + K + int(it - yc[t].begin()));
+      ex += (ex.empty() ? "" : " + ") + F("RW(%d)", off[t] + K + int(it - yc[t].begin()));
     }
     if (ex.empty()) continue;
     o.line(F("{ const real yb = ") + ex + F("; gx = fma(yb, Y[%d].x, gx); gy = fma(yb, Y[%d].y, gy);"
@@ -899,6 +952,7 @@ void emit_recv_edge_final(Out& o, const Plan& p, const std::vector<Task>& tasks)
   o.line("gev[3 * (i64)e] = (gx - nx * d) * inv;");
   o.line("gev[3 * (i64)e + 1] = (gy - ny * d) * inv;");
   o.line("gev[3 * (i64)e + 2] = (gz - nz * d) * inv;");
+  o.line("#undef RW");
   o.close();
 }
 
@@ -1054,14 +1108,18 @@ std::string generate_source(const Plan& p, const std::string& family, std::strin
     prelude(o, p, false, false);
     emit_sh(o, p.lmax);
     emit_prep(o, p);
-    auto tasks = forward_tasks(p);
     bool streamed = family == "fwds";
+    auto tasks = forward_tasks(p);
+    int nacc = 1;
     for (int k = 0; k < int(tasks.size()); ++k) {
       if (streamed) emit_fwd_streamed_task(o, p, k, tasks[k]);
       else emit_fwd_task(o, p, k, tasks[k]);
+      int n = 0;
+      for (int ob : out_blocks_of(p, tasks[k].paths)) n += p.out[ob].dim();
+      nacc = std::max(nacc, n);
     }
     emit_node_dispatch(o, p, streamed ? "cgtp_fwd_streamed" : "cgtp_fwd", kFwdArgs, streamed ? "fwds_t" : "fwd_t",
-                       int(tasks.size()));
+                       int(tasks.size()), nacc);
     return o.s.str();
   }
   if (family == "dbl") return generate_dbl_source(p, err);
