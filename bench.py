@@ -1,22 +1,30 @@
 """Throughput of the Clebsch-Gordan tensor-product convolution on one MI355X.
 
-One step = forward + backward (gradients of x, phi, A and the positions) of the channelwise
-convolution on the 1,024-atom perturbed-diamond graph (cutoff 5 A, ~91k directed edges),
-128x0e+128x1o+128x2e -> 128x(0e,1o,2e,3o), SH lmax 3, 8 radial functions, float32, inputs
-resident in device memory.  Prints one JSON line:
+Default: one step = forward + backward (gradients of x, phi, A and the positions) of the
+channelwise convolution on the 1,024-atom perturbed-diamond graph (cutoff 5 A, ~91k directed
+edges), 128x0e+128x1o+128x2e -> 128x(0e,1o,2e,3o), SH lmax 3, 8 radial functions, float32,
+inputs resident in device memory.  Prints one JSON line:
 
-  metric / value / unit      edges per second of forward + backward (whole job, one GPU)
-  roofline                   the dominant kernel against the fp32 vector-ALU peak, from HIP
-                             events recorded around every launch inside this process
+  metric / value / unit      edges per second of the step (whole job, one GPU)
+  kernels                    per kernel: launches and time per step (HIP events recorded around
+                             every launch on its stream), algorithmic TFLOP/s where defined
+  roofline                   the dominant kernel against its peak (vector ALU or MFMA)
   cpu_baseline               the float64 CPU oracle on a bounded receiver slice of the same
                              workload, timed on this host (a reported baseline, not a target)
+
+``--workload N`` measures another of the five standard workloads with its own passes (1: both
+forward schedules; 3: forward, float64; 4: fully connected streamed forward + backward; 5:
+forward + backward + double backward); ``--copy-probe`` only runs a device copy of known size,
+which calibrates the HBM byte counters of rocprofv3.
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -26,44 +34,144 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-CONFIG = 2
-# Non-packed FP32 vector FMA peak: 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz.  The build
-# keeps packed FP32 off, so this (not the 157.3 TFLOP/s packed figure) bounds the VALU kernels.
-PEAK_FP32_ALU_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
-PEAK_FP64_ALU_TFLOPS = 78.6
+DEFAULT_WORKLOAD = 2
+# Vector-ALU FMA peak without packed FP32: 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz.  The
+# build keeps packed FP32 off, so this (not the 157.3 TFLOP/s packed figure) bounds the VALU
+# kernels; the fp64 vector peak is the same 78.6 TFLOP/s.  Dense MFMA: fp32 157.3, fp64 78.6.
+PEAK_ALU_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+PEAK_ALU_PACKED_FP32_TFLOPS = 157.3
+PEAK_MFMA_TFLOPS = {"float32": 157.3, "float64": 78.6}
+
+PASSES = {1: ("fwd", "fwds"), 2: ("fwd", "bwd"), 3: ("fwd",), 4: ("fwds", "bwd"), 5: ("fwd", "bwd", "dbl")}
+PASS_NAMES = {"fwd": "forward (conventional)", "fwds": "forward (streamed)", "bwd": "backward",
+              "dbl": "double backward"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cgtp_bwd_recv__diamond1024_uvu_l3_fp32__hbm_counters.md")
 
 
-def algorithmic_fma(plan, n_edges: int, n_nodes: int):
-    """FMA per launch of each kernel (one launch covers every edge), from the plan's path table.
+def _blocks(irreps: str):
+    out = []
+    for tok in irreps.split("+"):
+        m = re.fullmatch(r"(\d+)x(\d+)([eo])", tok.strip())
+        out.append((int(m.group(1)), int(m.group(2))))
+    return out
 
-    Per path pi with C channels, K radial functions, gnz (m1, m3) pairs, p12 (m1, m2) pairs,
-    nnz CG terms and component counts d1, d2, d3:
-      forward     C (K + gnz + min(d1, d3)) per edge (w = phi A, T = G x, w applied on the smaller side)
-      source bwd  the same per edge (x-bar = w G^T mbar)
-      receiver bwd the cheaper of two exact forms: with T = G x, C (2 gnz + 3K + d3) per edge plus
-                  2 nnz per edge for Y-bar; or folded through R = sum c mbar (formed once per receiver,
-                  C nnz), C (p12 + 2 d2 + 3K) per edge (Q = x R, h = Y.Q, Y-bar += w Q, and the three K
-                  contractions w, phi-bar, A-bar)
-      prep        nnz per edge (G = sum c Y)
-    """
-    K = plan.info["num_radial"]
-    E, N = n_edges, n_nodes
-    deg = E / max(N, 1)
-    fwd = recv = prep = 0.0
+
+def _path_table(plan):
+    rows = []
     for k in range(plan.info["n_paths"]):
         d = plan.path(k)
         idx, _ = plan.cg_table(k)
-        gnz = len({(int(a), int(c)) for a, _, c in idx})
-        p12 = len({(int(a), int(b)) for a, b, _ in idx})
-        nnz = len(idx)
-        d1, d2, d3 = 2 * d["l1"] + 1, 2 * d["l2"] + 1, 2 * d["l3"] + 1
-        C = d["n_weights"]  # channelwise: one weight per channel
-        fwd += C * (K + gnz + min(d1, d3))
-        plain = C * (2 * gnz + 3 * K + d3) + 2 * nnz
-        fold = C * (p12 + 2 * d2 + 3 * K) + C * nnz / deg
-        recv += min(plain, fold)
-        prep += nnz
-    return {"cgtp_fwd": fwd * E, "cgtp_prep": prep * E, "cgtp_bwd_recv": recv * E, "cgtp_bwd_src": fwd * E}
+        rows.append(dict(d, gnz=len({(int(a), int(c)) for a, _, c in idx}),
+                         p12=len({(int(a), int(b)) for a, b, _ in idx}), nnz=len(idx),
+                         d1=2 * d["l1"] + 1, d2=2 * d["l2"] + 1, d3=2 * d["l3"] + 1))
+    return rows
+
+
+def kernel_fma(plan, spec, n_edges: int, n_nodes: int, passes):
+    """Algorithmic FMA per step of each kernel, from the plan's path table.
+
+    Per path with C channels (uvu), K radial functions, gnz (m1, m3) pairs, p12 (m1, m2) pairs, nnz
+    CG terms and component counts d1, d2, d3, per edge:
+      prep            nnz (G = sum c Y), once per pass that needs it
+      fwd / bwd_src   C (K + gnz + min(d1, d3)): w = phi A, T = G x (or G^T mbar), w applied on the
+                      smaller side
+      fwd_streamed    C (gnz + K d3) per edge plus C K d3 per receiver (S, then S A)
+      bwd_recv        the cheaper exact form: C (2 gnz + 3K + d3) + 2 nnz with T = G x, or, folding
+                      R = sum c mbar once per receiver (C nnz), C (p12 + 2 d2 + 3K)
+      prep2           2 nnz (G and its tangent)
+      dfwd            C (3K + 3 gnz + 2 d3): w, wdot, T, Tdot, mdot
+      drecv           C (7K + 5 gnz + 2 d3 + 2 d1) + 2 nnz: the tangents of h, A-bar, phi-bar and
+                      Y-bar and the first-order Y-bar, as written in the method's equations
+      dsrc            C (3K + 2 gnz + 2 d1)
+    Fully connected (C_in, C_out per path):
+      uvw_state       C_in (gnz + K d3) per edge, in every pass that forms S
+      uvw_edge        C_in (gnz + 2 K d3 + nnz) per edge: T, phi-bar = sum Sbar T, Cbar = sum phi Sbar
+                      and the Y-bar contraction
+      uvw_zstate      C_out (gnz + K d1) per edge
+      gemm_fwd<g>, gemm_sbar<g>, gemm_abar<g>: (N d3_g) x C_out x sum_{paths into g} K C_in
+      gemm_xbar<b>    (N d1_b) x C_in x sum_{paths from b} K C_out
+    Kernels without an entry (edge finalisation, reductions) are reported by time only.
+    """
+    K, E, N = plan.info["num_radial"], n_edges, n_nodes
+    deg = E / max(N, 1)
+    rows = _path_table(plan)
+    f = {}
+
+    def add(name, v):
+        f[name] = f.get(name, 0.0) + v
+
+    if spec["mode"] == "uvu":
+        nnz = sum(r["nnz"] for r in rows)
+        fwd = sum(r["n_weights"] * (K + r["gnz"] + min(r["d1"], r["d3"])) for r in rows) * E
+        for ps in passes:
+            if ps in ("fwd", "fwds", "bwd"):
+                add("cgtp_prep", nnz * E)
+            if ps == "fwd":
+                add("cgtp_fwd", fwd)
+            if ps == "fwds":
+                add("cgtp_fwd_streamed", sum(r["n_weights"] * (r["gnz"] + K * r["d3"]) * E
+                                             + r["n_weights"] * K * r["d3"] * N for r in rows))
+            if ps == "bwd":
+                recv = 0.0
+                for r in rows:
+                    C = r["n_weights"]
+                    plain = C * (2 * r["gnz"] + 3 * K + r["d3"]) + 2 * r["nnz"]
+                    fold = C * (r["p12"] + 2 * r["d2"] + 3 * K) + C * r["nnz"] / deg
+                    recv += min(plain, fold)
+                add("cgtp_bwd_recv", recv * E)
+                add("cgtp_bwd_src", fwd)
+            if ps == "dbl":
+                add("cgtp_prep2", 2 * nnz * E)
+                add("cgtp_dfwd", sum(r["n_weights"] * (3 * K + 3 * r["gnz"] + 2 * r["d3"]) for r in rows) * E)
+                add("cgtp_drecv", (sum(r["n_weights"] * (7 * K + 5 * r["gnz"] + 2 * r["d3"] + 2 * r["d1"])
+                                       for r in rows) + 2 * nnz) * E)
+                add("cgtp_dsrc", sum(r["n_weights"] * (3 * K + 2 * r["gnz"] + 2 * r["d1"]) for r in rows) * E)
+        return f
+    bi, bo = _blocks(spec["irreps_in"]), _blocks(spec["irreps_out"])
+    state = sum(bi[r["i_in"]][0] * (r["gnz"] + K * r["d3"]) for r in rows) * E
+    for ps in passes:
+        if ps in ("fwds", "bwd"):
+            add("cgtp_uvw_state", state)
+        for g in sorted({r["i_out"] for r in rows}):
+            depth = sum(K * bi[r["i_in"]][0] for r in rows if r["i_out"] == g)
+            mac = N * (2 * bo[g][1] + 1) * bo[g][0] * depth
+            if ps == "fwds":
+                add(f"cgtp_gemm_fwd{g}", mac)
+            if ps == "bwd":
+                add(f"cgtp_gemm_sbar{g}", mac)
+                add(f"cgtp_gemm_abar{g}", mac)
+        if ps == "bwd":
+            add("cgtp_uvw_edge", sum(bi[r["i_in"]][0] * (r["gnz"] + 2 * K * r["d3"] + r["nnz"]) for r in rows) * E)
+            add("cgtp_uvw_zstate", sum(bo[r["i_out"]][0] * (r["gnz"] + K * r["d1"]) for r in rows) * E)
+            for b in sorted({r["i_in"] for r in rows}):
+                depth = sum(K * bo[r["i_out"]][0] for r in rows if r["i_in"] == b)
+                add(f"cgtp_gemm_xbar{b}", N * (2 * bi[b][1] + 1) * bi[b][0] * depth)
+    return f
+
+
+def generator_digest() -> str:
+    """Hash of the kernel generator sources: HBM counters are valid for the code they were taken on."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "clebsch_gordan_tensor_receiver_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.startswith("codegen") or name in ("plan.cpp", "plan.hpp", "kernels.hpp"):
+            with open(os.path.join(csrc, name), "rb") as fh:
+                h.update(name.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, if it was taken on the
+    current kernel generator (else None)."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    dig = re.search(r"generator digest: `([0-9a-f]+)`", text)
+    m = re.search(r"traffic bytes per launch of " + re.escape(kernel) + r": `([0-9.]+)`", text)
+    if not dig or not m or dig.group(1) != generator_digest():
+        return None
+    return float(m.group(1))
 
 
 def main() -> int:
@@ -72,6 +180,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--profile-steps", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD, choices=sorted(PASSES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of known size (calibrates the HBM byte counters)")
@@ -92,39 +201,57 @@ def main() -> int:
     torch.cuda.set_device(0)
     if args.copy_probe:
         return copy_probe(torch)
-    spec = CONFIGS[CONFIG]
-    w = make_workload(CONFIG)
-    plan = cg.Plan(spec["irreps_in"], spec["irreps_sh"], spec["irreps_out"], spec["mode"], spec["dtype"], spec["K"])
+    cfg = args.workload
+    passes = PASSES[cfg]
+    spec = CONFIGS[cfg]
+    w = make_workload(cfg)
+    dtype = spec["dtype"]
+    plan = cg.Plan(spec["irreps_in"], spec["irreps_sh"], spec["irreps_out"], spec["mode"], dtype, spec["K"])
     graph = cg.Graph(w.n_nodes, w.recv, w.send, w.image)
     perm = graph.perm
     info = plan.info
-    K = spec["K"]
-    dev = dict(dtype=torch.float32, device="cuda")
-    x_h = normal_tensor(CONFIG, 1, (w.n_nodes, info["c_in"]), dtype="float32")
-    A_h = normal_tensor(CONFIG, 2, (K, info["n_weights"]), std=1.0 / np.sqrt(K), dtype="float32")
-    g_h = normal_tensor(CONFIG, 3, (w.n_nodes, info["c_out"]), dtype="float32")
+    K, E, N = spec["K"], graph.n_edges, w.n_nodes
+    tdt = torch.float64 if dtype == "float64" else torch.float32
+    dev = dict(dtype=tdt, device="cuda")
+    rnd = (lambda a: a.astype(np.float32).astype(np.float64)) if dtype == "float32" else (lambda a: a)
+    x_h = normal_tensor(cfg, 1, (N, info["c_in"]), dtype=dtype)
+    A_h = normal_tensor(cfg, 2, (K, info["n_weights"]), std=1.0 / np.sqrt(K), dtype=dtype)
+    g_h = normal_tensor(cfg, 3, (N, info["c_out"]), dtype=dtype)
     x = torch.tensor(x_h, **dev)
     A = torch.tensor(A_h, **dev)
     gout = torch.tensor(g_h, **dev)
-    pos = torch.tensor(w.pos.astype(np.float32), **dev)
-    shift = torch.tensor(w.shift[perm].astype(np.float32), **dev).contiguous()
-    phi = torch.tensor(w.phi[perm].astype(np.float32), **dev).contiguous()
+    pos = torch.tensor(rnd(w.pos), **dev)
+    shift = torch.tensor(rnd(w.shift[perm]), **dev).contiguous()
+    phi = torch.tensor(rnd(w.phi[perm]), **dev).contiguous()
     conv = cg.Convolution(plan, graph)
-    plan.compile((cg.OP_FORWARD, cg.OP_BACKWARD))
+    ops = {"fwd": cg.OP_FORWARD, "fwds": cg.OP_FORWARD, "bwd": cg.OP_BACKWARD, "dbl": cg.OP_DOUBLE_BACKWARD}
+    plan.compile(tuple(sorted({ops[p] for p in passes})))
     graph.upload()
-    E = graph.n_edges
 
-    out = torch.empty((w.n_nodes, info["c_out"]), **dev)
+    out = torch.empty((N, info["c_out"]), **dev)
     grads = dict(x=torch.empty_like(x), pos=torch.empty_like(pos), edge_vec=torch.empty((E, 3), **dev),
                  phi=torch.empty_like(phi), A=torch.empty_like(A))
-    ws_f = conv.workspace(cg.OP_FORWARD)
-    ws_b = conv.workspace(cg.OP_BACKWARD)
+    ws = {p: conv.workspace(ops[p]) for p in passes}
+    if "dbl" in passes:
+        dirs = dict(v_x=torch.tensor(normal_tensor(cfg, 4, (N, info["c_in"]), dtype=dtype), **dev),
+                    v_pos=torch.tensor(normal_tensor(cfg, 5, (N, 3), dtype=dtype), **dev),
+                    v_edge_vec=torch.tensor(normal_tensor(cfg, 6, (E, 3), dtype=dtype)[perm], **dev).contiguous(),
+                    v_phi=torch.tensor(normal_tensor(cfg, 7, (E, K), dtype=dtype)[perm], **dev).contiguous(),
+                    v_A=torch.tensor(normal_tensor(cfg, 9, (K, info["n_weights"]), dtype=dtype), **dev))
+        gg = dict(gg_x=torch.empty_like(x), gg_pos=torch.empty_like(pos), gg_edge_vec=torch.empty((E, 3), **dev),
+                  gg_phi=torch.empty_like(phi), gg_A=torch.empty_like(A), gg_grad_out=torch.empty_like(out))
 
     def step():
-        cg.conv_forward(plan, graph, cg.CONVENTIONAL, x, pos, shift, phi, A, out, ws_f)
-        cg.conv_backward(plan, graph, x, pos, shift, phi, A, gout, grad_x=grads["x"], grad_pos=grads["pos"],
-                         grad_edge_vec=grads["edge_vec"], grad_phi=grads["phi"], grad_A=grads["A"],
-                         workspace=ws_b)
+        for ps in passes:
+            if ps in ("fwd", "fwds"):
+                sched = cg.CONVENTIONAL if ps == "fwd" else cg.STREAMED
+                cg.conv_forward(plan, graph, sched, x, pos, shift, phi, A, out, ws[ps])
+            elif ps == "bwd":
+                cg.conv_backward(plan, graph, x, pos, shift, phi, A, gout, grad_x=grads["x"], grad_pos=grads["pos"],
+                                 grad_edge_vec=grads["edge_vec"], grad_phi=grads["phi"], grad_A=grads["A"],
+                                 workspace=ws[ps])
+            else:
+                cg.conv_double_backward(plan, graph, x, pos, shift, phi, A, gout, **dirs, **gg, workspace=ws[ps])
 
     for _ in range(args.warmup):
         step()
@@ -137,31 +264,50 @@ def main() -> int:
     ms_per_step = 1e3 * elapsed / args.steps
     value = E * args.steps / elapsed
 
-    # Per-kernel durations from HIP events around each launch (separate region).
-    cg._lib.profile_begin()
-    for _ in range(args.profile_steps):
-        step()
-    torch.cuda.synchronize()
-    prof = cg._lib.profile_end()
-    fma = algorithmic_fma(plan, E, w.n_nodes)
-    kernels = {}
-    for name, (n, ms) in prof.items():
-        avg_us = 1e3 * ms / n
-        entry = {"launches_per_step": n / args.profile_steps, "avg_us": round(avg_us, 2)}
-        if name in fma:
-            flop = 2.0 * fma[name]  # one launch covers every edge (single receiver chunk)
-            entry["tflops"] = round(flop / (avg_us * 1e-6) / 1e12, 3)
-        kernels[name] = entry
-    dominant = max(prof, key=lambda k: prof[k][1])
-    d_entry = kernels[dominant]
-    achieved = d_entry.get("tflops")
-    roofline = {"kernel": dominant, "bound": "alu", "achieved": achieved, "peak": round(PEAK_FP32_ALU_TFLOPS, 1),
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_ALU_TFLOPS, 4) if achieved else None,
-                "traffic": None}
-    step_flop = 2.0 * (fma["cgtp_fwd"] + 2 * fma["cgtp_prep"] + fma["cgtp_bwd_recv"] + fma["cgtp_bwd_src"])
+    # Per-kernel durations from HIP events around each launch (a separate region).
+    result_kernels, roofline, step_fma = {}, None, 0.0
+    if args.profile_steps > 0:
+        cg._lib.profile_begin()
+        for _ in range(args.profile_steps):
+            step()
+        torch.cuda.synchronize()
+        prof = cg._lib.profile_end()
+        fma = kernel_fma(plan, spec, E, N, passes)
+        step_fma = sum(fma.values())
+        for name, (n, ms) in prof.items():
+            us_step = 1e3 * ms / args.profile_steps
+            entry = {"launches_per_step": n / args.profile_steps, "us_per_step": round(us_step, 2),
+                     "avg_us": round(1e3 * ms / n, 2)}
+            if name in fma:
+                entry["tflops"] = round(2.0 * fma[name] / (us_step * 1e-6) / 1e12, 3)
+            result_kernels[name] = entry
+        dominant = max(prof, key=lambda k: prof[k][1])
+        d = result_kernels[dominant]
+        mfma = dominant.startswith("cgtp_gemm")
+        peak = PEAK_MFMA_TFLOPS[dtype] if mfma else PEAK_ALU_TFLOPS
+        achieved = d.get("tflops")
+        roofline = {"kernel": dominant, "bound": "mfma" if mfma else "alu", "achieved": achieved,
+                    "peak": round(peak, 1), "unit": "TFLOP/s",
+                    "frac": round(achieved / peak, 4) if achieved else None,
+                    "traffic": recorded_traffic(dominant) if cfg == DEFAULT_WORKLOAD else None}
+        if not mfma and dtype == "float32" and achieved:
+            roofline["frac_of_packed_fp32_peak"] = round(achieved / PEAK_ALU_PACKED_FP32_TFLOPS, 4)
 
+    desc = {2: "1,024-atom perturbed diamond (4x4x8 cells, a=3.57 A, sigma 0.05 A), cutoff 5 A; "
+               "128x0e+128x1o+128x2e -> 128x0e+128x1o+128x2e+128x3o, SH lmax 3, channelwise, "
+               "8 Bessel radial functions",
+            1: "64 uniform atoms, 6 A periodic cube, cutoff 3 A; 8x0e+8x1o -> 8x0e+8x1o+8x2e, SH lmax 2, "
+               "channelwise, 8 Bessel radial functions",
+            3: "1,024-atom perturbed diamond, cutoff 5 A; 64x0e+64x1o+64x2e -> 64x0e+64x1o+64x2e+64x3o, "
+               "SH lmax 3, channelwise, 8 Bessel radial functions",
+            4: "16,384 uniform atoms at 0.1 /A^3, cutoff 5 A; 64x0e+64x1o+64x2e -> same, SH lmax 2, fully "
+               "connected (uvw), 8 Bessel radial functions",
+            5: "4,096 uniform atoms, 60 expected neighbours within 6 A; 32x(0e..6e) -> same, SH lmax 6, "
+               "channelwise, 16 Gaussian radial functions"}[cfg]
+    label = " + ".join(PASS_NAMES[p] for p in passes)
     result = {
-        "metric": "edges/sec for CGTP conv fwd+bwd, MACE-like irreps, fp32",
+        "metric": "edges/sec for CGTP conv fwd+bwd, MACE-like irreps, fp32" if cfg == DEFAULT_WORKLOAD
+        else f"edges/sec for CGTP conv {label}, {dtype}",
         "value": round(value, 1),
         "unit": "edges/s",
         "n_gpus": 1,
@@ -171,18 +317,16 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f64" if dtype == "float64" else "f32",
         "data": "synthetic",
-        "config": {"workload": "1,024-atom perturbed diamond (4x4x8 cells, a=3.57 A, sigma 0.05 A), cutoff 5 A; "
-                               "128x0e+128x1o+128x2e -> 128x0e+128x1o+128x2e+128x3o, SH lmax 3, channelwise, "
-                               "8 Bessel radial functions; forward + backward (x, phi, A, positions)",
-                   "n_nodes": w.n_nodes, "n_edges": E, "schedule": "conventional (per-edge weights in registers)"},
-        "gflops_algorithmic": round(step_flop / (ms_per_step * 1e-3) / 1e9, 1),
-        "kernels": kernels,
+        "config": {"workload": f"{desc}; {label}" + ("; gradients of x, phi, A and positions" if "bwd" in passes
+                                                     else ""),
+                   "n_nodes": N, "n_edges": E, "passes": list(passes)},
+        "gflops_algorithmic": round(2.0 * step_fma / (ms_per_step * 1e-3) / 1e9, 1) if step_fma else None,
+        "kernels": result_kernels,
         "roofline": roofline,
     }
-
-    if not args.no_cpu_baseline:
+    if cfg == DEFAULT_WORKLOAD and not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity"] = cpu_baseline(w, plan, perm, x_h, A_h, g_h, out, grads)
     print(json.dumps(result), flush=True)
     return 0

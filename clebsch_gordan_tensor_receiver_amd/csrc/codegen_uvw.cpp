@@ -193,6 +193,21 @@ void emit_gemm(Out& o, const GemmSpec& g) {
   o.close();
 }
 
+// Fixed-order sum of the split-K partials of a GEMM (part[z][r][c], z < nsplit) and the GEMM's
+// scatter store of the result.
+void emit_gemm_reduce(Out& o, const GemmSpec& g, const std::string& args) {
+  o.line("extern \"C\" __global__ void __launch_bounds__(256)");
+  o.open(g.name + "_reduce(const real* __restrict__ part, int nsplit, int M, " + args + ")");
+  o.line("const i64 id = (i64)blockIdx.x * 256 + threadIdx.x;");
+  o.line(F("const i64 MN = (i64)M * %d;", g.N));
+  o.line("if (id >= MN) return;");
+  o.line(F("const int r = (int)(id / %d), c = (int)(id - (i64)r * %d);", g.N, g.N));
+  o.line("real v = part[id];");
+  o.line("for (int z = 1; z < nsplit; ++z) v += part[(i64)z * MN + id];");
+  o.line(g.store);
+  o.close();
+}
+
 void uvw_prelude_extra(Out& o, const Plan& p) {
   if (p.dtype == CGTP_F64) {
     o.line("typedef double acc4 __attribute__((ext_vector_type(4)));");
@@ -532,15 +547,17 @@ std::string generate_uvw_source(const Plan& p, const std::string& family, std::s
       const Block& OB = p.out[s.blk];
       GemmSpec g;
       g.name = F("cgtp_gemm_fwd%d", s.blk);
-      g.args = "const real* __restrict__ S, const real* __restrict__ A, real* __restrict__ out, int i0";
+      g.args = "const real* __restrict__ S, const real* __restrict__ A, real* __restrict__ part, int i0";
       g.a_at = state_at("S", s, roff[gi], RS, "r", "k");
       g.b_at = F("A[brow%d(k) + c]", s.blk);
-      g.store = F("out[(i64)(i0 + r / %d) * %d + %d + (r %% %d) * %d + c] = v;", s.d, p.c_out, OB.offset, s.d, OB.mul);
+      g.store = F("part[(i64)blockIdx.z * M * %d + (i64)r * %d + c] = v;", OB.mul, OB.mul);
       g.N = OB.mul;
       g.a_kfast = true;
       g.b_kfast = false;
-      g.split = false;
+      g.split = true;
       emit_gemm(o, g);
+      g.store = F("out[(i64)(i0 + r / %d) * %d + %d + (r %% %d) * %d + c] = v;", s.d, p.c_out, OB.offset, s.d, OB.mul);
+      emit_gemm_reduce(o, g, "real* __restrict__ out, int i0");
     }
     return o.s.str();
   }
@@ -600,17 +617,19 @@ std::string generate_uvw_source(const Plan& p, const std::string& family, std::s
     emit_bz(o, p, s, F("bz%d", s.blk));
     GemmSpec g;  // x-bar = Z A (contracting (pi, q, w))
     g.name = F("cgtp_gemm_xbar%d", s.blk);
-    g.args = "const real* __restrict__ Z, const real* __restrict__ A, real* __restrict__ gx, int j0";
+    g.args = "const real* __restrict__ Z, const real* __restrict__ A, real* __restrict__ part, int j0";
     g.a_at = state_at("Z", s, zoff[bi], ZS, "r", "k");
     g.b_at = F("bx%d(A, k, c)", s.blk);
-    g.store = F("gx[(i64)(j0 + r / %d) * %d + %d + (r %% %d) * %d + c] = v;", s.d, p.c_in, IB.offset, s.d, IB.mul);
+    g.store = F("part[(i64)blockIdx.z * M * %d + (i64)r * %d + c] = v;", IB.mul, IB.mul);
     g.N = IB.mul;
     g.a_kfast = true;
     g.b_kfast = true;
-    g.split = false;
+    g.split = true;
     o.line(F("DEV real bx%d(const real* __restrict__ A, int k, int c) { int st; const i64 b = bz%d(k, st);"
              " return A[b + (i64)c * st]; }", s.blk, s.blk));
     emit_gemm(o, g);
+    g.store = F("gx[(i64)(j0 + r / %d) * %d + %d + (r %% %d) * %d + c] = v;", s.d, p.c_in, IB.offset, s.d, IB.mul);
+    emit_gemm_reduce(o, g, "real* __restrict__ gx, int j0");
   }
   return o.s.str();
 }

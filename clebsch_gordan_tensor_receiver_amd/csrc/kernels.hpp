@@ -90,5 +90,8 @@ std::vector<ProfileEntry> profile_entries();
 // Launch helper: args is an array of pointers to the kernel arguments.
 cgtp_status_t launch(hipFunction_t f, unsigned grid, unsigned block, unsigned shmem, hipStream_t s,
                      void** args, std::string* err);
+// Three-dimensional grid (also timed by the launch profiler).
+cgtp_status_t launch_grid(hipFunction_t f, unsigned gx, unsigned gy, unsigned gz, unsigned block, unsigned shmem,
+                          hipStream_t s, void** args, std::string* err);
 
 }  // namespace cgtp

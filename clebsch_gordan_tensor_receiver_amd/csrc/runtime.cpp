@@ -218,7 +218,12 @@ cgtp_status_t get_kernel(Plan& p, const std::string& family, const std::string& 
 
 cgtp_status_t launch(hipFunction_t f, unsigned grid, unsigned block, unsigned shmem, hipStream_t s, void** args,
                      std::string* err) {
-  if (grid == 0) return CGTP_OK;
+  return launch_grid(f, grid, 1, 1, block, shmem, s, args, err);
+}
+
+cgtp_status_t launch_grid(hipFunction_t f, unsigned gx, unsigned gy, unsigned gz, unsigned block, unsigned shmem,
+                          hipStream_t s, void** args, std::string* err) {
+  if (gx == 0 || gy == 0 || gz == 0) return CGTP_OK;
   hipEvent_t ea = nullptr, eb = nullptr;
   std::string pname;
   {
@@ -231,7 +236,7 @@ cgtp_status_t launch(hipFunction_t f, unsigned grid, unsigned block, unsigned sh
     }
   }
   if (ea) hipEventRecord(ea, s);
-  hipError_t e = hipModuleLaunchKernel(f, grid, 1, 1, block, 1, 1, shmem, s, args, nullptr);
+  hipError_t e = hipModuleLaunchKernel(f, gx, gy, gz, block, 1, 1, shmem, s, args, nullptr);
   if (eb) {
     hipEventRecord(eb, s);
     std::lock_guard<std::mutex> lock(g_prof_mu);

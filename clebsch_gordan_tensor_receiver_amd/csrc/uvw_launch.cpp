@@ -34,6 +34,26 @@ std::vector<std::pair<int, int>> ranges(int n, const std::vector<int32_t>& ptr, 
 }
 
 constexpr int kAbarSplit = 32;  // row slices of the A-bar GEMM per group (fixed-order partial sums)
+constexpr int kMaxSplit = 8;    // K slices of the forward and x-bar GEMMs (64 output columns: few row tiles)
+
+// K slices of a GEMM with M rows, N columns and depth Kd: enough workgroups to fill the chip
+// (about 1,024), slices of at least 128, at most kMaxSplit.  Returns the slice length in *kper.
+int gemm_split(int M, int N, int Kd, int* kper) {
+  const long long tiles = (long long)((M + 63) / 64) * ((N + 63) / 64);
+  int ns = int(std::min<long long>(kMaxSplit, std::max<long long>(1, (1024 + tiles - 1) / std::max(1LL, tiles))));
+  ns = std::max(1, std::min(ns, Kd / 128));
+  int kp = (Kd + ns - 1) / ns;
+  kp = (kp + 31) / 32 * 32;
+  *kper = kp;
+  return (Kd + kp - 1) / kp;
+}
+
+// Largest d x mul over the sides: rows per node times columns of a split-K partial.
+size_t max_side_cols(const std::vector<UvwSideInfo>& sides) {
+  size_t m = 1;
+  for (auto& s : sides) m = std::max(m, size_t(s.d) * size_t(s.mul));
+  return m;
+}
 
 struct UvwPlanB {
   UvwLayout L;
@@ -41,7 +61,8 @@ struct UvwPlanB {
   int V = 0, ep_row = 0;
   long long emax = 1, kmax = 1;
   int nmax = 1, jmax = 1;
-  size_t g_off = 0, s_off = 0, sb_off = 0, ep_off = 0, ap_off = 0, z_off = 0, gs_off = 0, gev_off = 0, total = 0;
+  size_t g_off = 0, s_off = 0, sb_off = 0, ep_off = 0, ap_off = 0, z_off = 0, xp_off = 0, gs_off = 0, gev_off = 0;
+  size_t total = 0;
 };
 
 UvwPlanB layout_bwd(const Plan& p, const Graph& g) {
@@ -57,7 +78,8 @@ UvwPlanB layout_bwd(const Plan& p, const Graph& g) {
     B.emax = std::max<long long>(B.emax, g.row_ptr[c.second] - g.row_ptr[c.first]);
     B.nmax = std::max(B.nmax, c.second - c.first);
   }
-  B.schunks = ranges(g.n, g.src_ptr, size_t(B.L.send_stride) * el, size_t(p.g_stride) * el, p.scratch_budget);
+  B.schunks = ranges(g.n, g.src_ptr, (size_t(B.L.send_stride) + kMaxSplit * max_side_cols(B.L.send)) * el,
+                     size_t(p.g_stride) * el, p.scratch_budget);
   for (auto& c : B.schunks) {
     B.kmax = std::max<long long>(B.kmax, g.src_ptr[c.second] - g.src_ptr[c.first]);
     B.jmax = std::max(B.jmax, c.second - c.first);
@@ -83,6 +105,8 @@ UvwPlanB layout_bwd(const Plan& p, const Graph& g) {
   off += al(size_t(B.kmax) * p.g_stride * el);
   B.z_off = off;
   off += al(size_t(B.jmax) * B.L.send_stride * el);
+  B.xp_off = off;
+  off += al(size_t(B.jmax) * kMaxSplit * max_side_cols(B.L.send) * el);
   size_t send_phase = off;
   B.gev_off = std::max(recv_phase, send_phase);
   B.total = B.gev_off + al(size_t(std::max(g.e, 1)) * 3 * el);
@@ -94,21 +118,23 @@ struct UvwPlanF {
   std::vector<std::pair<int, int>> chunks;
   long long emax = 1;
   int nmax = 1;
-  size_t g_off = 0, s_off = 0, total = 0;
+  size_t g_off = 0, s_off = 0, part_off = 0, total = 0;
 };
 
 UvwPlanF layout_fwd(const Plan& p, const Graph& g) {
   UvwPlanF F;
   F.L = uvw_layout(p);
   const size_t el = p.elem();
-  F.chunks = ranges(g.n, g.row_ptr, size_t(F.L.recv_stride) * el, size_t(p.g_stride) * el, p.scratch_budget);
+  F.chunks = ranges(g.n, g.row_ptr, (size_t(F.L.recv_stride) + kMaxSplit * max_side_cols(F.L.recv)) * el,
+                    size_t(p.g_stride) * el, p.scratch_budget);
   for (auto& c : F.chunks) {
     F.emax = std::max<long long>(F.emax, g.row_ptr[c.second] - g.row_ptr[c.first]);
     F.nmax = std::max(F.nmax, c.second - c.first);
   }
   F.g_off = 0;
   F.s_off = al(size_t(F.emax) * p.g_stride * el);
-  F.total = F.s_off + al(size_t(F.nmax) * F.L.recv_stride * el);
+  F.part_off = F.s_off + al(size_t(F.nmax) * F.L.recv_stride * el);
+  F.total = F.part_off + al(size_t(F.nmax) * kMaxSplit * max_side_cols(F.L.recv) * el);
   return F;
 }
 
@@ -116,13 +142,7 @@ unsigned cdiv(long long a, long long b) { return unsigned((a + b - 1) / b); }
 
 cgtp_status_t launch3(hipFunction_t f, unsigned gx, unsigned gy, unsigned gz, unsigned block, hipStream_t s,
                       void** args, std::string* err) {
-  if (gx == 0 || gy == 0 || gz == 0) return CGTP_OK;
-  hipError_t e = hipModuleLaunchKernel(f, gx, gy, gz, block, 1, 1, 0, s, args, nullptr);
-  if (e != hipSuccess) {
-    *err = std::string("hipModuleLaunchKernel: ") + hipGetErrorString(e);
-    return CGTP_ERR_HIP;
-  }
-  return CGTP_OK;
+  return launch_grid(f, gx, gy, gz, block, 0, s, args, err);
 }
 
 }  // namespace
@@ -140,14 +160,19 @@ cgtp_status_t uvw_forward(Plan& p, Graph& G, const DeviceGraph& d, const void* x
   if ((st = get_kernel(p, "uvw_fwd", "cgtp_prep", &kprep, err)) != CGTP_OK ||
       (st = get_kernel(p, "uvw_fwd", "cgtp_uvw_state", &kstate, err)) != CGTP_OK)
     return st;
-  std::vector<hipFunction_t> kg;
+  std::vector<hipFunction_t> kg, kr;
   for (auto& side : F.L.recv) {
-    hipFunction_t f;
-    if ((st = get_kernel(p, "uvw_fwd", "cgtp_gemm_fwd" + std::to_string(side.blk), &f, err)) != CGTP_OK) return st;
+    hipFunction_t f, r;
+    const std::string nm = "cgtp_gemm_fwd" + std::to_string(side.blk);
+    if ((st = get_kernel(p, "uvw_fwd", nm, &f, err)) != CGTP_OK ||
+        (st = get_kernel(p, "uvw_fwd", nm + "_reduce", &r, err)) != CGTP_OK)
+      return st;
     kg.push_back(f);
+    kr.push_back(r);
   }
   void* Gb = static_cast<char*>(workspace) + F.g_off;
   void* S = static_cast<char*>(workspace) + F.s_off;
+  void* part = static_cast<char*>(workspace) + F.part_off;
   for (auto& c : F.chunks) {
     int i0 = c.first, nrec = c.second - c.first;
     int e0 = G.row_ptr[c.first], e1 = G.row_ptr[c.second];
@@ -161,8 +186,12 @@ cgtp_status_t uvw_forward(Plan& p, Graph& G, const DeviceGraph& d, const void* x
     for (size_t gi = 0; gi < F.L.recv.size(); ++gi) {
       const auto& side = F.L.recv[gi];
       int M = nrec * side.d, Kd = side.D, kper = 0;
-      void* a[] = {&S, (void*)&A, &out, &i0, &M, &Kd, &kper};
-      if ((st = launch3(kg[gi], cdiv(M, 64), cdiv(side.mul, 64), 1, 256, s, a, err)) != CGTP_OK) return st;
+      int ns = gemm_split(M, side.mul, Kd, &kper);
+      void* a[] = {&S, (void*)&A, &part, &i0, &M, &Kd, &kper};
+      if ((st = launch3(kg[gi], cdiv(M, 64), cdiv(side.mul, 64), unsigned(ns), 256, s, a, err)) != CGTP_OK)
+        return st;
+      void* b[] = {&part, &ns, &M, &out, &i0};
+      if ((st = launch(kr[gi], cdiv((long long)M * side.mul, 256), 256, 0, s, b, err)) != CGTP_OK) return st;
     }
   }
   // Output blocks without paths stay untouched by the GEMMs: callers get zeros there.
@@ -199,10 +228,14 @@ cgtp_status_t uvw_backward(Plan& p, Graph& G, const DeviceGraph& d, const Source
     kab.push_back(f2);
     kacc.push_back(f3);
   }
+  std::vector<hipFunction_t> kxr;
   for (auto& side : B.L.send) {
-    hipFunction_t f;
-    if ((st = get_kernel(p, fam, "cgtp_gemm_xbar" + std::to_string(side.blk), &f, err)) != CGTP_OK) return st;
+    hipFunction_t f, r;
+    const std::string nm = "cgtp_gemm_xbar" + std::to_string(side.blk);
+    if ((st = get_kernel(p, fam, nm, &f, err)) != CGTP_OK || (st = get_kernel(p, fam, nm + "_reduce", &r, err)) != CGTP_OK)
+      return st;
     kxb.push_back(f);
+    kxr.push_back(r);
   }
   char* ws = static_cast<char*>(workspace);
   void* Gb = ws + B.g_off;
@@ -274,11 +307,16 @@ cgtp_status_t uvw_backward(Plan& p, Graph& G, const DeviceGraph& d, const Source
       void* b[] = {(void*)&phi, &Gs, (void*)&gout, (void*)&d.recv, (void*)&d.src_ptr, (void*)&d.src_edge, &Z, &j0,
                    &njs, &per, &k0};
       if ((st = launch(kz, unsigned(8 * B.L.n_z_tasks * per), 64, 0, s, b, err)) != CGTP_OK) return st;
+      void* xp = ws + B.xp_off;
       for (size_t bi = 0; bi < B.L.send.size(); ++bi) {
         const auto& side = B.L.send[bi];
         int M = njs * side.d, Kd = side.D, kper = 0;
-        void* a[] = {&Z, (void*)&A, &grad_x, &j0, &M, &Kd, &kper};
-        if ((st = launch3(kxb[bi], cdiv(M, 64), cdiv(side.mul, 64), 1, 256, s, a, err)) != CGTP_OK) return st;
+        int ns = gemm_split(M, side.mul, Kd, &kper);
+        void* a[] = {&Z, (void*)&A, &xp, &j0, &M, &Kd, &kper};
+        if ((st = launch3(kxb[bi], cdiv(M, 64), cdiv(side.mul, 64), unsigned(ns), 256, s, a, err)) != CGTP_OK)
+          return st;
+        void* b[] = {&xp, &ns, &M, &grad_x, &j0};
+        if ((st = launch(kxr[bi], cdiv((long long)M * side.mul, 256), 256, 0, s, b, err)) != CGTP_OK) return st;
       }
     }
   }
