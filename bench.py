@@ -181,6 +181,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--profile-steps", type=int, default=10)
     ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD, choices=sorted(PASSES))
+    ap.add_argument("--scratch-mib", type=int, default=0,
+                    help="scratch budget of the plan in MiB (0: the library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of known size (calibrates the HBM byte counters)")
@@ -207,6 +209,8 @@ def main() -> int:
     w = make_workload(cfg)
     dtype = spec["dtype"]
     plan = cg.Plan(spec["irreps_in"], spec["irreps_sh"], spec["irreps_out"], spec["mode"], dtype, spec["K"])
+    if args.scratch_mib > 0:
+        plan.set_scratch_budget(args.scratch_mib << 20)
     graph = cg.Graph(w.n_nodes, w.recv, w.send, w.image)
     perm = graph.perm
     info = plan.info
@@ -321,7 +325,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": f"{desc}; {label}" + ("; gradients of x, phi, A and positions" if "bwd" in passes
                                                      else ""),
-                   "n_nodes": N, "n_edges": E, "passes": list(passes)},
+                   "n_nodes": N, "n_edges": E, "passes": list(passes),
+                   "scratch_budget_mib": args.scratch_mib or 256},
         "gflops_algorithmic": round(2.0 * step_fma / (ms_per_step * 1e-3) / 1e9, 1) if step_fma else None,
         "kernels": result_kernels,
         "roofline": roofline,

@@ -53,8 +53,6 @@ long double fct(int n) {
   return r;
 }
 
-// Register budget: A coefficients held per lane for one subset of paths.
-constexpr int kRegBudget = 64;
 
 // Split a task's paths into consecutive subsets whose A coefficients (K per path) fit `avail`
 // registers; each subset re-walks the edge list (only tasks of one oversized block need more
@@ -76,6 +74,26 @@ std::vector<std::vector<int>> subsets(const Plan& p, const std::vector<int>& pat
     out.back().push_back(pi);
   }
   return out;
+}
+
+void emit_vz(Out& o, const Plan& p) {
+  if (p.vec_g) o.line("int vz; asm(\"v_mov_b32 %0, 0\" : \"=v\"(vz));");
+}
+
+void emit_gvec_loads(Out& o, const Plan& p, int pi, const std::string& row, const std::string& tag, bool vec) {
+  const Path& P = p.paths[pi];
+  if (!vec || !path_vec(P)) return;
+  const int per = p.dtype == CGTP_F64 ? 2 : 4;
+  const int n = (int(P.gpairs.size()) + per - 1) / per;
+  o.line(F("const V4* __restrict__ gv%s%d = (const V4*)(%s + %d) + vz;", tag.c_str(), pi, row.c_str(), P.g_off));
+  for (int c = 0; c < n; ++c) o.line(F("const V4 gq%s%d_%d = gv%s%d[%d];", tag.c_str(), pi, c, tag.c_str(), pi, c));
+}
+
+std::string gref(const Plan& p, int pi, int t, const std::string& row, const std::string& tag, bool vec) {
+  const Path& P = p.paths[pi];
+  if (!vec || !path_vec(P)) return F("%s[%d]", row.c_str(), P.g_off + t);
+  const int per = p.dtype == CGTP_F64 ? 2 : 4;
+  return F("gq%s%d_%d.%c", tag.c_str(), pi, t / per, "abcd"[t % per]);
 }
 
 void prelude(Out& o, const Plan& p, bool dual, bool reduce) {
@@ -187,19 +205,18 @@ void emit_prep(Out& o, const Plan& p, bool with_y) {
   o.line("const real inv = R(1) / sqrt(rx * rx + ry * ry + rz * rz);");
   o.line(F("real Y[%d];", p.sh_dim));
   o.line("sh_eval<real>(rx * inv, ry * inv, rz * inv, Y);");
-  std::vector<std::string> vals;
+  std::vector<std::string> vals(size_t(p.g_stride), "R(0)");
   for (const Path& P : p.paths) {
     int s = P.l2 * P.l2;
-    for (const GPair& gp : P.gpairs) {
+    for (size_t t = 0; t < P.gpairs.size(); ++t) {
       std::string ex;
-      for (auto& t : gp.terms) {
+      for (auto& tm : P.gpairs[t].terms) {
         if (!ex.empty()) ex += " + ";
-        ex += lit(t.second) + " * Y[" + std::to_string(s + t.first) + "]";
+        ex += lit(tm.second) + " * Y[" + std::to_string(s + tm.first) + "]";
       }
-      vals.push_back(ex);
+      vals[size_t(P.g_off) + t] = ex;
     }
   }
-  while (int(vals.size()) < p.g_stride) vals.push_back("R(0)");
   if (with_y)
     for (int m = 0; m < p.sh_dim; ++m) vals.push_back(F("Y[%d]", m));
   while (int(vals.size()) < stride) vals.push_back("R(0)");
@@ -264,19 +281,20 @@ void emit_path_accumulate(Out& o, const Plan& p, int pi, const std::string& acc 
   const Path& P = p.paths[pi];
   const int d1 = 2 * P.l1 + 1, d3 = 2 * P.l3 + 1;
   const char* A = acc.c_str();
+  auto G = [&](size_t t) { return gref(p, pi, int(t), "g", "", false); };
   if (d1 <= d3) {
     for (int m = 0; m < d1; ++m) o.line(F("const real s%d_%d = w%d * x%d_%d;", pi, m, pi, P.i_in, m));
     for (size_t t = 0; t < P.gpairs.size(); ++t)
-      o.line(F("%s%d = fma(g[%d], s%d_%d, %s%d);", A, P.gpairs[t].m3, P.g_off + int(t), pi, P.gpairs[t].m1, A,
+      o.line(F("%s%d = fma(%s, s%d_%d, %s%d);", A, P.gpairs[t].m3, G(t).c_str(), pi, P.gpairs[t].m1, A,
                P.gpairs[t].m3));
   } else {
     std::vector<bool> started(d3, false);
     for (size_t t = 0; t < P.gpairs.size(); ++t) {
       int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3;
       if (!started[m3])
-        o.line(F("real t%d_%d = g[%d] * x%d_%d;", pi, m3, P.g_off + int(t), P.i_in, m1));
+        o.line(F("real t%d_%d = %s * x%d_%d;", pi, m3, G(t).c_str(), P.i_in, m1));
       else
-        o.line(F("t%d_%d = fma(g[%d], x%d_%d, t%d_%d);", pi, m3, P.g_off + int(t), P.i_in, m1, pi, m3));
+        o.line(F("t%d_%d = fma(%s, x%d_%d, t%d_%d);", pi, m3, G(t).c_str(), P.i_in, m1, pi, m3));
       started[m3] = true;
     }
     for (int m = 0; m < d3; ++m)
@@ -407,6 +425,7 @@ void emit_fwd_task(Out& o, const Plan& p, int ti, const Task& T) {
   const std::vector<int> obs = out_blocks_of(p, T.paths);
   o.open(F("DEV void fwd_t%d(%s, real* sm, int node, int e_base)", ti, kFwdArgs));
   o.line("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
+  emit_vz(o, p);
   o.line(F("const int u = %d + lane;", T.cb * 64));
   o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
   std::vector<std::string> accs;
@@ -444,6 +463,7 @@ void emit_fwd_streamed_task(Out& o, const Plan& p, int ti, const Task& T) {
   const int d3 = OB.dim(), MUL = OB.mul, K = p.K;
   o.open(F("DEV void fwds_t%d(%s, real* sm, int node, int e_base)", ti, kFwdArgs));
   o.line("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
+  emit_vz(o, p);
   o.line(F("const int u = %d + lane;", T.cb * 64));
   o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
   for (int m = 0; m < d3; ++m) o.line(F("real acc%d = R(0);", m));
@@ -457,10 +477,11 @@ void emit_fwd_streamed_task(Out& o, const Plan& p, int ti, const Task& T) {
       std::vector<bool> started(d3, false);
       for (size_t t = 0; t < P.gpairs.size(); ++t) {
         int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3;
+        const std::string G = gref(p, pi, int(t), "g", "", false);
         if (!started[m3])
-          o.line(F("real c%d = g[%d] * x%d_%d;", m3, P.g_off + int(t), P.i_in, m1));
+          o.line(F("real c%d = %s * x%d_%d;", m3, G.c_str(), P.i_in, m1));
         else
-          o.line(F("c%d = fma(g[%d], x%d_%d, c%d);", m3, P.g_off + int(t), P.i_in, m1, m3));
+          o.line(F("c%d = fma(%s, x%d_%d, c%d);", m3, G.c_str(), P.i_in, m1, m3));
         started[m3] = true;
       }
       for (int q = 0; q < K; ++q)
@@ -601,6 +622,7 @@ void emit_bwd_recv_task(Out& o, const Plan& p, int ti, const Task& T, int col_of
   auto ycol = [&](int y) { return K + int(std::find(ycols.begin(), ycols.end(), y) - ycols.begin()); };
   o.open(F("DEV void bwr_t%d(%s, real* sm, int node, int e_base, int eps, int slot)", ti, kRecvArgs));
   o.line("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
+  emit_vz(o, p);
   o.line(F("const int u = %d + lane;", T.cb * 64));
   o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
   emit_a_loads(o, p, T.paths);
@@ -661,13 +683,15 @@ void emit_bwd_recv_task(Out& o, const Plan& p, int ti, const Task& T, int col_of
         continue;
       }
       const int d3 = 2 * P.l3 + 1, ob = P.i_out;
+      emit_gvec_loads(o, p, pi, "g", "");
       std::vector<bool> started(d3, false);
       for (size_t t = 0; t < P.gpairs.size(); ++t) {
         int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3;
+        const std::string G = gref(p, pi, int(t), "g", "");
         if (!started[m3])
-          o.line(F("real t%d_%d = g[%d] * x%d_%d;", pi, m3, P.g_off + int(t), P.i_in, m1));
+          o.line(F("real t%d_%d = %s * x%d_%d;", pi, m3, G.c_str(), P.i_in, m1));
         else
-          o.line(F("t%d_%d = fma(g[%d], x%d_%d, t%d_%d);", pi, m3, P.g_off + int(t), P.i_in, m1, pi, m3));
+          o.line(F("t%d_%d = fma(%s, x%d_%d, t%d_%d);", pi, m3, G.c_str(), P.i_in, m1, pi, m3));
         started[m3] = true;
       }
       bool first = true;
@@ -761,6 +785,7 @@ void emit_bwd_src_task(Out& o, const Plan& p, int ti, const Task& T) {
   const std::vector<int> ibs = in_blocks_of(p, T.paths);
   o.open(F("DEV void bws_t%d(%s, real* sm, int node, int e_base, int accumulate)", ti, kSrcArgs));
   o.line("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
+  emit_vz(o, p);
   o.line(F("const int u = %d + lane;", T.cb * 64));
   o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
   std::vector<std::string> accs;
@@ -800,19 +825,20 @@ void emit_bwd_src_task(Out& o, const Plan& p, int ti, const Task& T) {
     const Path& P = p.paths[pi];
     const int d1 = 2 * P.l1 + 1, d3 = 2 * P.l3 + 1, ib = P.i_in;
     emit_w(o, p, pi);
+    auto G = [&](size_t t) { return gref(p, pi, int(t), "g", "", false); };
     if (d3 <= d1) {
       for (int m = 0; m < d3; ++m) o.line(F("const real s%d_%d = w%d * mb%d_%d;", pi, m, pi, P.i_out, m));
       for (size_t t = 0; t < P.gpairs.size(); ++t)
-        o.line(F("acc%d_%d = fma(g[%d], s%d_%d, acc%d_%d);", ib, P.gpairs[t].m1, P.g_off + int(t), pi,
+        o.line(F("acc%d_%d = fma(%s, s%d_%d, acc%d_%d);", ib, P.gpairs[t].m1, G(t).c_str(), pi,
                  P.gpairs[t].m3, ib, P.gpairs[t].m1));
     } else {
       std::vector<bool> started(d1, false);
       for (size_t t = 0; t < P.gpairs.size(); ++t) {
         int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3;
         if (!started[m1])
-          o.line(F("real b%d_%d = g[%d] * mb%d_%d;", pi, m1, P.g_off + int(t), P.i_out, m3));
+          o.line(F("real b%d_%d = %s * mb%d_%d;", pi, m1, G(t).c_str(), P.i_out, m3));
         else
-          o.line(F("b%d_%d = fma(g[%d], mb%d_%d, b%d_%d);", pi, m1, P.g_off + int(t), P.i_out, m3, pi, m1));
+          o.line(F("b%d_%d = fma(%s, mb%d_%d, b%d_%d);", pi, m1, G(t).c_str(), P.i_out, m3, pi, m1));
         started[m1] = true;
       }
       for (int m = 0; m < d1; ++m)
@@ -1064,9 +1090,11 @@ std::vector<Task> recv_backward_tasks(const Plan& p) {
 }
 
 std::vector<Task> dbl_recv_tasks(const Plan& p) {
+  // Per path the receiver pass of the double backward holds A, its tangent and the A-bar tangent
+  // accumulators (3K values per lane).
   std::vector<Task> t;
   for (const Task& f : forward_tasks(p))
-    for (const auto& S : subsets(p, f.paths)) t.push_back({f.group, f.cb, S});
+    for (const auto& S : a_subsets(p, f.paths, 3 * kRegBudget / 2 / 3)) t.push_back({f.group, f.cb, S});
   return t;
 }
 

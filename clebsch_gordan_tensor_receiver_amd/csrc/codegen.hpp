@@ -46,6 +46,19 @@ struct Out {
 };
 
 std::vector<std::vector<int>> subsets(const Plan& p, const std::vector<int>& paths);
+// Consecutive subsets holding at most avail / K paths (A coefficients of K values per path).
+std::vector<std::vector<int>> a_subsets(const Plan& p, const std::vector<int>& paths, int avail);
+constexpr int kRegBudget = 64;  // registers per lane for A coefficients of one path subset
+
+// Folded coefficients of large paths (more than kVecGPairs pairs) are read with 16-byte vector
+// loads into VGPRs instead of scalar loads: `vz` is a per-lane zero the compiler cannot prove
+// uniform (declared by emit_vz in every task of a plan with such paths).
+inline bool path_vec(const Path& P) { return int(P.gpairs.size()) > kVecGPairs; }
+void emit_vz(Out& o, const Plan& p);
+// `vec` false: scalar loads whatever the path size (kernels where vector loads measured slower).
+void emit_gvec_loads(Out& o, const Plan& p, int pi, const std::string& row, const std::string& tag,
+                     bool vec = true);
+std::string gref(const Plan& p, int pi, int t, const std::string& row, const std::string& tag, bool vec = true);
 void prelude(Out& o, const Plan& p, bool dual, bool reduce);
 void emit_sh(Out& o, int L);
 void emit_edge_vector(Out& o);

@@ -125,9 +125,9 @@ void emit_prep2(Out& o, const Plan& p) {
   o.line(F("D1 Y[%d];", p.sh_dim));
   o.line("sh_eval<D1>(D1(nx, dx), D1(ny, dy), D1(nz, dz), Y);");
   o.line(F("real* __restrict__ dst = G + (i64)(e - e0) * %d;", 2 * p.g_stride));
-  int n = 0;
   for (const Path& P : p.paths) {
     int s = P.l2 * P.l2;
+    int n = P.g_off;
     for (const GPair& gp : P.gpairs) {
       std::string ev, ed;
       for (auto& t : gp.terms) {
@@ -197,16 +197,20 @@ void emit_wwd(Out& o, const Plan& p, int pi) {
 // T[m3] = G x and Tdot[m3] = Gdot x + G xdot of path pi, names t<pi>_<m3>, td<pi>_<m3>.
 std::vector<bool> emit_t_td(Out& o, const Plan& p, int pi, int d3) {
   const Path& P = p.paths[pi];
+  emit_gvec_loads(o, p, pi, "g", "");
+  emit_gvec_loads(o, p, pi, "gd", "d");
   std::vector<bool> started(d3, false);
   for (size_t t = 0; t < P.gpairs.size(); ++t) {
-    int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3, gi = P.g_off + int(t);
+    int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3;
+    const std::string G = gref(p, pi, int(t), "g", ""), Gd = gref(p, pi, int(t), "gd", "d");
     if (!started[m3]) {
-      o.line(F("real t%d_%d = g[%d] * x%d_%d;", pi, m3, gi, P.i_in, m1));
-      o.line(F("real td%d_%d = fma(gd[%d], x%d_%d, g[%d] * xd%d_%d);", pi, m3, gi, P.i_in, m1, gi, P.i_in, m1));
+      o.line(F("real t%d_%d = %s * x%d_%d;", pi, m3, G.c_str(), P.i_in, m1));
+      o.line(F("real td%d_%d = fma(%s, x%d_%d, %s * xd%d_%d);", pi, m3, Gd.c_str(), P.i_in, m1, G.c_str(), P.i_in,
+               m1));
     } else {
-      o.line(F("t%d_%d = fma(g[%d], x%d_%d, t%d_%d);", pi, m3, gi, P.i_in, m1, pi, m3));
-      o.line(F("td%d_%d = fma(gd[%d], x%d_%d, fma(g[%d], xd%d_%d, td%d_%d));", pi, m3, gi, P.i_in, m1, gi, P.i_in,
-               m1, pi, m3));
+      o.line(F("t%d_%d = fma(%s, x%d_%d, t%d_%d);", pi, m3, G.c_str(), P.i_in, m1, pi, m3));
+      o.line(F("td%d_%d = fma(%s, x%d_%d, fma(%s, xd%d_%d, td%d_%d));", pi, m3, Gd.c_str(), P.i_in, m1, G.c_str(),
+               P.i_in, m1, pi, m3));
     }
     started[m3] = true;
   }
@@ -218,11 +222,12 @@ void emit_dfwd_task(Out& o, const Plan& p, int ti, const Task& T) {
   const Block& OB = p.out[T.group];
   const int d3 = OB.dim(), MUL = OB.mul;
   o.open(F("DEV void dfw_t%d(%s, int node, int e_base)", ti, kDArgs));
+  emit_vz(o, p);
   o.line(F("const int u = %d + (int)threadIdx.x;", T.cb * 64));
   o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
   for (int m = 0; m < d3; ++m) o.line(F("real acc%d = R(0);", m));
   o.line("const int e0 = row_ptr[node], e1 = row_ptr[node + 1];");
-  for (const auto& S : subsets(p, T.paths)) {
+  for (const auto& S : a_subsets(p, T.paths, kRegBudget / 2)) {  // A and its tangent
     o.open("");
     emit_da_loads(o, p, S);
     emit_dedge_loop(o, p, in_blocks_of(p, S), [&] {
@@ -248,6 +253,7 @@ void emit_drecv_task(Out& o, const Plan& p, int ti, const Task& T, int V) {
   const Block& OB = p.out[T.group];
   const int d3 = OB.dim(), MUL = OB.mul, K = p.K, Yd = p.sh_dim;
   o.open(F("DEV void drc_t%d(%s, real* sm, int node, int e_base, int eps, int slot)", ti, kDArgs));
+  emit_vz(o, p);
   o.line("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
   o.line(F("const int u = %d + lane;", T.cb * 64));
   o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
@@ -335,6 +341,7 @@ void emit_dsrc_task(Out& o, const Plan& p, int ti, const Task& T) {
   const Block& IB = p.in[T.group];
   const int d1 = IB.dim(), MUL = IB.mul, K = p.K;
   o.open(F("DEV void dsr_t%d(%s, int node, int e_base, int accumulate)", ti, kDSrcArgs));
+  emit_vz(o, p);
   o.line(F("const int u = %d + (int)threadIdx.x;", T.cb * 64));
   o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
   for (int m = 0; m < d1; ++m) o.line(F("real acc%d = R(0);", m));
@@ -360,13 +367,14 @@ void emit_dsrc_task(Out& o, const Plan& p, int ti, const Task& T) {
       emit_wwd(o, p, pi);
       std::vector<bool> started(d1, false);
       for (size_t t = 0; t < P.gpairs.size(); ++t) {
-        int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3, gi2 = P.g_off + int(t);
+        int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3;
+        const std::string G = gref(p, pi, int(t), "g", "", false), Gd = gref(p, pi, int(t), "gd", "d", false);
         if (!started[m1]) {
-          o.line(F("real b%d_%d = g[%d] * mb%d_%d;", pi, m1, gi2, P.i_out, m3));
-          o.line(F("real bd%d_%d = gd[%d] * mb%d_%d;", pi, m1, gi2, P.i_out, m3));
+          o.line(F("real b%d_%d = %s * mb%d_%d;", pi, m1, G.c_str(), P.i_out, m3));
+          o.line(F("real bd%d_%d = %s * mb%d_%d;", pi, m1, Gd.c_str(), P.i_out, m3));
         } else {
-          o.line(F("b%d_%d = fma(g[%d], mb%d_%d, b%d_%d);", pi, m1, gi2, P.i_out, m3, pi, m1));
-          o.line(F("bd%d_%d = fma(gd[%d], mb%d_%d, bd%d_%d);", pi, m1, gi2, P.i_out, m3, pi, m1));
+          o.line(F("b%d_%d = fma(%s, mb%d_%d, b%d_%d);", pi, m1, G.c_str(), P.i_out, m3, pi, m1));
+          o.line(F("bd%d_%d = fma(%s, mb%d_%d, bd%d_%d);", pi, m1, Gd.c_str(), P.i_out, m3, pi, m1));
         }
         started[m1] = true;
       }

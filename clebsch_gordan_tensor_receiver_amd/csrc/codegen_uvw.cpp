@@ -472,9 +472,9 @@ void emit_prep_src(Out& o, const Plan& p) {
   o.line(F("real Y[%d];", p.sh_dim));
   o.line("sh_eval<real>(rx * inv, ry * inv, rz * inv, Y);");
   o.line(F("real* __restrict__ dst = G + (i64)(k - k0) * %d;", p.g_stride));
-  int n = 0;
   for (const Path& P : p.paths) {
     int s = P.l2 * P.l2;
+    int n = P.g_off;
     for (const GPair& gp : P.gpairs) {
       std::string ex;
       for (auto& t : gp.terms) {

@@ -237,14 +237,21 @@ cgtp_status_t build_plan(const char* irreps_in, const char* irreps_sh, const cha
             }
             if (!gp.terms.empty()) P.gpairs.push_back(gp);
           }
-        P.g_off = g_off;
-        g_off += int(P.gpairs.size());
         nnz += int(P.terms.size());
         p->paths.push_back(std::move(P));
       }
   if (p->paths.empty()) {
     *err = "no admissible path between these irreps";
     return CGTP_ERR_UNSUPPORTED;
+  }
+  // G layout: the paths' (m1, m3) pairs back to back.  Plans with large paths read those through
+  // 16-byte vector loads, so their path blocks start on multiples of 4 values.
+  p->vec_g = false;
+  for (const Path& P : p->paths) p->vec_g = p->vec_g || int(P.gpairs.size()) > kVecGPairs;
+  for (Path& P : p->paths) {
+    if (p->vec_g) g_off = (g_off + 3) / 4 * 4;
+    P.g_off = g_off;
+    g_off += int(P.gpairs.size());
   }
   p->n_w = w_off;
   p->g_width = g_off;

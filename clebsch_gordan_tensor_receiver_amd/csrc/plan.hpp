@@ -45,6 +45,10 @@ struct Path {
 // Kernel family state (compiled code objects and loaded modules per device).
 struct KernelSet;
 
+// Paths with more (m1, m3) pairs than this read their folded coefficients through vector loads
+// (the scalar register file cannot hold them per edge).
+constexpr int kVecGPairs = 48;
+
 struct Plan {
   std::vector<Block> in, sh, out;
   std::vector<Path> paths;
@@ -52,7 +56,8 @@ struct Plan {
   cgtp_dtype_t dtype;
   int K = 0;
   int c_in = 0, c_out = 0, sh_dim = 0, lmax = 0, n_w = 0;
-  int g_width = 0;     // folded coefficients per edge (sum over paths of gpairs)
+  int g_width = 0;     // folded coefficients per edge (sum over paths of gpairs, with alignment)
+  bool vec_g = false;  // some path has more than kVecGPairs pairs: path blocks are 4-aligned
   int g_stride = 0;    // padded row stride of G in elements
   int cg_nnz = 0;
   size_t scratch_budget = size_t(256) << 20;
