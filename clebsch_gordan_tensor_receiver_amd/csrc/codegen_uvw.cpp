@@ -142,12 +142,14 @@ struct GemmSpec {
 
 // LDS-tiled MFMA GEMM: 64 x 64 output tile per 4-wave workgroup, K staged 32 at a time, each wave
 // a 32 x 32 quarter as 2 x 2 MFMA 16x16x4 tiles.  C[r][c] = sum_k A(r, k) B(k, c) over
-// k in [kb, ke); `store` writes value v at (r, c).
+// k in [kb, ke); `store` writes value v at (r, c).  Two LDS buffers: the next K slice is loaded
+// into registers while the current one feeds the MFMAs, then stored to the other buffer, so one
+// barrier per slice suffices and the global loads overlap the matrix work.
 void emit_gemm(Out& o, const GemmSpec& g) {
   o.line("extern \"C\" __global__ void __launch_bounds__(256)");
   o.open(g.name + "(" + g.args + ", int M, int Kd, int kper)");
-  o.line("__shared__ real As[64 * 34];");
-  o.line("__shared__ real Bs[32 * 80];");
+  o.line("__shared__ real As[2][64 * 34];");
+  o.line("__shared__ real Bs[2][32 * 80];");
   o.line("const int tid = (int)threadIdx.x, lane = tid & 63, wv = tid >> 6;");
   o.line("const int r0 = (int)blockIdx.x * 64, c0 = (int)blockIdx.y * 64;");
   if (g.split) {
@@ -156,27 +158,58 @@ void emit_gemm(Out& o, const GemmSpec& g) {
     o.line("const int kb = 0, ke = Kd; (void)kper;");
   }
   o.line("acc4 a00 = {0, 0, 0, 0}, a01 = {0, 0, 0, 0}, a10 = {0, 0, 0, 0}, a11 = {0, 0, 0, 0};");
-  o.open("for (int k0 = kb; k0 < ke; k0 += 32)");
-  o.open("for (int t = 0; t < 8; ++t)");
-  o.line("const int id = t * 256 + tid;");
-  o.line(g.a_kfast ? "const int rr = id >> 5, kk = id & 31;" : "const int rr = id & 63, kk = id >> 6;");
-  o.line("const int r = r0 + rr, k = k0 + kk;");
-  o.line("As[rr * 34 + kk] = (r < M && k < ke) ? (" + g.a_at + ") : R(0);");
-  o.close();
-  o.open("for (int t = 0; t < 8; ++t)");
-  o.line("const int id = t * 256 + tid;");
-  o.line(g.b_kfast ? "const int cc = id >> 5, kk = id & 31;" : "const int cc = id & 63, kk = id >> 6;");
-  o.line("const int c = c0 + cc, k = k0 + kk;");
-  o.line(F("Bs[kk * 80 + cc] = (k < ke && c < %d) ? (", g.N) + g.b_at + ") : R(0);");
+  o.line("real ra[8], rb[8];");
+  // Global -> registers for the K slice starting at k0.
+  auto load = [&](const std::string& k0) {
+    o.open("");
+    o.line("const int k0_ = " + k0 + ";");
+    o.open("for (int t = 0; t < 8; ++t)");
+    o.line("const int id = t * 256 + tid;");
+    o.line(g.a_kfast ? "const int rr = id >> 5, kk = id & 31;" : "const int rr = id & 63, kk = id >> 6;");
+    o.line("const int r = r0 + rr, k = k0_ + kk;");
+    o.line("ra[t] = (r < M && k < ke) ? (" + g.a_at + ") : R(0);");
+    o.close();
+    o.open("for (int t = 0; t < 8; ++t)");
+    o.line("const int id = t * 256 + tid;");
+    o.line(g.b_kfast ? "const int cc = id >> 5, kk = id & 31;" : "const int cc = id & 63, kk = id >> 6;");
+    o.line("const int c = c0 + cc, k = k0_ + kk;");
+    o.line(F("rb[t] = (k < ke && c < %d) ? (", g.N) + g.b_at + ") : R(0);");
+    o.close();
+    o.close();
+  };
+  // Registers -> LDS buffer `buf`.
+  auto store = [&](const std::string& buf) {
+    o.open("for (int t = 0; t < 8; ++t)");
+    o.line("const int id = t * 256 + tid;");
+    o.line(g.a_kfast ? "const int rr = id >> 5, kk = id & 31;" : "const int rr = id & 63, kk = id >> 6;");
+    o.line("As[" + buf + "][rr * 34 + kk] = ra[t];");
+    o.close();
+    o.open("for (int t = 0; t < 8; ++t)");
+    o.line("const int id = t * 256 + tid;");
+    o.line(g.b_kfast ? "const int cc = id >> 5, kk = id & 31;" : "const int cc = id & 63, kk = id >> 6;");
+    o.line("Bs[" + buf + "][kk * 80 + cc] = rb[t];");
+    o.close();
+  };
+  o.open("if (kb < ke)");
+  load("kb");
+  store("0");
   o.close();
   o.line("__syncthreads();");
+  o.open("for (int k0 = kb, cur = 0; k0 < ke; k0 += 32, cur ^= 1)");
+  o.line("const bool more = k0 + 32 < ke;");
+  o.open("if (more)");
+  load("k0 + 32");
+  o.close();
   o.open("for (int s = 0; s < 8; ++s)");
   o.line("const int ka = s * 4 + (lane >> 4);");
-  o.line("const real x0 = As[(32 * (wv >> 1) + (lane & 15)) * 34 + ka];");
-  o.line("const real x1 = As[(32 * (wv >> 1) + 16 + (lane & 15)) * 34 + ka];");
-  o.line("const real y0 = Bs[ka * 80 + 32 * (wv & 1) + (lane & 15)];");
-  o.line("const real y1 = Bs[ka * 80 + 32 * (wv & 1) + 16 + (lane & 15)];");
+  o.line("const real x0 = As[cur][(32 * (wv >> 1) + (lane & 15)) * 34 + ka];");
+  o.line("const real x1 = As[cur][(32 * (wv >> 1) + 16 + (lane & 15)) * 34 + ka];");
+  o.line("const real y0 = Bs[cur][ka * 80 + 32 * (wv & 1) + (lane & 15)];");
+  o.line("const real y1 = Bs[cur][ka * 80 + 32 * (wv & 1) + 16 + (lane & 15)];");
   o.line("a00 = MFMA(x0, y0, a00); a01 = MFMA(x0, y1, a01); a10 = MFMA(x1, y0, a10); a11 = MFMA(x1, y1, a11);");
+  o.close();
+  o.open("if (more)");
+  store("cur ^ 1");
   o.close();
   o.line("__syncthreads();");
   o.close();
