@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(HERE, "libcgtp.so")
 CHANNELWISE, FULLY_CONNECTED = 0, 1
 F32, F64 = 0, 1
 STREAMED, CONVENTIONAL = 0, 1
+DEGENERATE_EDGE = 4
 OP_FORWARD, OP_BACKWARD, OP_DOUBLE_BACKWARD = 0, 1, 2
 
 EXPORTED = [
@@ -249,6 +250,17 @@ def conv_double_backward(plan: Plan, graph: Graph, x, pos, shift, phi, A, grad_o
         _ptr(v_x), _ptr(v_pos), _ptr(v_edge_vec), _ptr(v_phi), _ptr(v_A), _ptr(gg_x), _ptr(gg_pos),
         _ptr(gg_edge_vec), _ptr(gg_phi), _ptr(gg_A), _ptr(gg_grad_out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def check_edges(plan: Plan, graph: Graph, pos, shift, workspace, stream=None) -> int:
+    """Smallest receiver-sorted index of a zero-length edge, or -1 (synchronises the stream)."""
+    first = ctypes.c_int(-1)
+    st = load().cgtp_check_edges(plan.handle, graph.handle, _ptr(pos), _ptr(shift), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream), ctypes.byref(first))
+    if st == DEGENERATE_EDGE:
+        return int(first.value)
+    check(st)
+    return -1
 
 
 class Convolution:

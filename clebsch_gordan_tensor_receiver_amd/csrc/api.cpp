@@ -6,6 +6,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "cgtp.h"
 #include "graph.hpp"
@@ -614,8 +615,34 @@ cgtp_status_t cgtp_conv_double_backward(cgtp_plan_t plan, cgtp_graph_t g, const 
 
 cgtp_status_t cgtp_check_edges(cgtp_plan_t plan, cgtp_graph_t g, const void* pos, const void* shift, void* workspace,
                                size_t ws_bytes, void* stream, int* first_bad) {
-  (void)plan; (void)g; (void)pos; (void)shift; (void)workspace; (void)ws_bytes; (void)stream; (void)first_bad;
-  return fail(CGTP_ERR_UNSUPPORTED, "edge check not built yet");
+  if (!plan || !g || !pos || !first_bad) return fail(CGTP_ERR_INVALID_ARG, "null argument");
+  cgtp::Plan& p = plan->p;
+  cgtp::Graph& G = g->g;
+  *first_bad = -1;
+  if (G.e == 0) return ok();
+  const int nblk = (G.e + 255) / 256;
+  if (!workspace || ws_bytes < size_t(nblk) * sizeof(int))
+    return fail(CGTP_ERR_WORKSPACE, "workspace smaller than 4 bytes per 256 edges");
+  std::string err;
+  cgtp::DeviceGraph d;
+  cgtp_status_t st = cgtp::device_graph(G, &d, &err);
+  if (st != CGTP_OK) return fail(st, err);
+  hipFunction_t k;
+  const char* fam = p.mode == CGTP_CHANNELWISE ? "fwd" : "uvw_fwd";
+  if ((st = cgtp::get_kernel(p, fam, "cgtp_check_edges", &k, &err)) != CGTP_OK) return fail(st, err);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int ne = G.e;
+  void* a[] = {(void*)&pos, (void*)&shift, (void*)&d.recv, (void*)&d.col, &ne, &workspace};
+  if ((st = cgtp::launch(k, unsigned(nblk), 256, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
+  std::vector<int> h(size_t(nblk), 0);
+  if (hipMemcpyAsync(h.data(), workspace, h.size() * sizeof(int), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return fail(CGTP_ERR_HIP, "copying the edge check result failed");
+  int m = 0x7fffffff;
+  for (int v : h) m = std::min(m, v);
+  if (m == 0x7fffffff) return ok();
+  *first_bad = m;
+  return fail(CGTP_ERR_DEGENERATE_EDGE, "edge " + std::to_string(m) + " (receiver-sorted) has zero length");
 }
 
 }  // extern "C"

@@ -982,6 +982,29 @@ void emit_recv_edge_final(Out& o, const Plan& p, const std::vector<Task>& tasks)
   o.close();
 }
 
+// Zero-length edge check: per 256-edge block, the smallest sorted edge index whose vector
+// pos[send] - pos[recv] + shift is exactly zero (INT_MAX if none), reduced in LDS in a fixed order.
+void emit_check_edges(Out& o) {
+  o.line("extern \"C\" __global__ void __launch_bounds__(256)");
+  o.open("cgtp_check_edges(const real* __restrict__ pos, const real* __restrict__ shift, const int* __restrict__ recv,"
+         " const int* __restrict__ send, int n_edges, int* __restrict__ first)");
+  o.line("__shared__ int sm[256];");
+  o.line("const int tid = (int)threadIdx.x, e = (int)blockIdx.x * 256 + tid;");
+  o.line("int bad = 0x7fffffff;");
+  o.open("if (e < n_edges)");
+  emit_edge_vector(o);
+  o.line("if (rx * rx + ry * ry + rz * rz == R(0)) bad = e;");
+  o.close();
+  o.line("sm[tid] = bad;");
+  o.line("__syncthreads();");
+  o.open("for (int w = 128; w > 0; w >>= 1)");
+  o.line("if (tid < w) sm[tid] = min(sm[tid], sm[tid + w]);");
+  o.line("__syncthreads();");
+  o.close();
+  o.line("if (tid == 0) first[blockIdx.x] = sm[0];");
+  o.close();
+}
+
 void emit_small_kernels(Out& o) {
   // Sum over the 64 lanes of a wave, the same value in every lane (fixed order).
   o.line("DEV real wave_total(real v) {");
@@ -1136,6 +1159,7 @@ std::string generate_source(const Plan& p, const std::string& family, std::strin
     prelude(o, p, false, false);
     emit_sh(o, p.lmax);
     emit_prep(o, p);
+    emit_check_edges(o);
     bool streamed = family == "fwds";
     auto tasks = forward_tasks(p);
     int nacc = 1;

@@ -73,6 +73,7 @@ void emit_swaps(Out& o, const std::vector<std::pair<std::string, std::string>>& 
 void emit_edge_final(Out& o, const Plan& p, int ntask, int V);
 void emit_recv_edge_final(Out& o, const Plan& p, const std::vector<Task>& tasks);
 void emit_small_kernels(Out& o);
+void emit_check_edges(Out& o);
 
 }  // namespace gen
 

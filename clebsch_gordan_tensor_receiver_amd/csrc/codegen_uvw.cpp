@@ -565,6 +565,7 @@ std::string generate_uvw_source(const Plan& p, const std::string& family, std::s
   uvw_prelude_extra(o, p);
   emit_sh(o, p.lmax);
   emit_prep(o, p);
+  if (!bwd) emit_check_edges(o);
   auto rs = recv_sides(p);
   long long RS = 0;
   const std::vector<size_t> roff = side_offsets(rs, &RS);

@@ -184,8 +184,12 @@ cgtp_status_t cgtp_conv_double_backward(cgtp_plan_t plan, cgtp_graph_t g, const 
                                         void* gg_A, void* gg_grad_out, void* workspace, size_t ws_bytes,
                                         void* stream);
 
-/* Check on the device that no edge has zero length.  Synchronises `stream`.  Returns
- * DEGENERATE_EDGE (and the first offending sorted edge in *first_bad, else -1). */
+/* Check on the device that no edge vector pos[send] - pos[recv] + shift is exactly zero (such an
+ * edge has no direction, so its spherical harmonics are undefined).  workspace: device memory of
+ * at least 4 bytes per 256 edges (any forward workspace of the plan serves).  Synchronises
+ * `stream`.  *first_bad receives the smallest receiver-sorted index of a zero-length edge, else -1;
+ * the status is then DEGENERATE_EDGE, else OK.  INVALID_ARG for null plan, graph, pos or
+ * first_bad; WORKSPACE if the workspace is too small. */
 cgtp_status_t cgtp_check_edges(cgtp_plan_t plan, cgtp_graph_t g, const void* pos, const void* shift,
                                void* workspace, size_t ws_bytes, void* stream, int* first_bad);
 

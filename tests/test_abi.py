@@ -168,6 +168,10 @@ def test_host_validation_before_any_device_work(lib):
     assert so.cgtp_conv_backward(plan.handle, g.handle, *[1] * 6, 1, None, None, None, None, 1, 16, None) == WORKSPACE
     assert so.cgtp_conv_double_backward(plan.handle, g.handle, *[1] * 6, *[None] * 5, 1, *[None] * 5, 1, 16,
                                         None) == WORKSPACE
+    first = ctypes.c_int(7)
+    assert so.cgtp_check_edges(plan.handle, g.handle, None, None, None, 0, None, ctypes.byref(first)) == INVALID_ARG
+    assert so.cgtp_check_edges(plan.handle, g.handle, 1, None, 1, 2, None, ctypes.byref(first)) == WORKSPACE
+    assert so.cgtp_check_edges(plan.handle, g.handle, 1, None, 1, 2, None, None) == INVALID_ARG
     assert so.cgtp_plan_set_scratch_budget(plan.handle, 16) == INVALID_ARG
     assert so.cgtp_plan_path(plan.handle, 99, (ctypes.c_int32 * 9)()) == INVALID_ARG
     assert so.cgtp_error_string(WORKSPACE) == b"workspace too small"

@@ -1,0 +1,129 @@
+"""Degenerate inputs on the GPU: zero-length edges, empty edge lists, receivers without edges,
+a single atom whose only neighbours are its own periodic images (needs an MI355X)."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import conv
+from oracle.irreps import make_problem
+from tests.oracle_helpers import make_case
+
+pytestmark = pytest.mark.gpu
+
+IRREPS = dict(irreps_in="16x0e+16x1o", irreps_sh="1x0e+1x1o+1x2e", irreps_out="16x0e+16x1o+16x2e")
+
+
+def _plan(dtype="float64", K=4):
+    from clebsch_gordan_tensor_receiver_amd import _lib
+    return _lib.Plan(IRREPS["irreps_in"], IRREPS["irreps_sh"], IRREPS["irreps_out"], "uvu", dtype, K)
+
+
+def _inputs(n, recv, send, shift, K, seed, dtype=torch.float64):
+    g = np.random.default_rng(seed)
+    prob = make_problem(IRREPS["irreps_in"], IRREPS["irreps_sh"], IRREPS["irreps_out"], "uvu")
+    d = dict(x=g.normal(size=(n, prob.c_in)), pos=g.uniform(0, 4, size=(n, 3)),
+             phi=g.normal(size=(len(recv), K)), A=g.normal(size=(K, prob.n_weights)) / np.sqrt(K),
+             grad_out=g.normal(size=(n, prob.c_out)), shift=np.asarray(shift, dtype=np.float64).reshape(-1, 3))
+    return prob, d
+
+
+def _run(plan, n, recv, send, d, want_bwd=True):
+    from clebsch_gordan_tensor_receiver_amd import _lib
+    graph = _lib.Graph(n, np.asarray(recv, np.int32), np.asarray(send, np.int32))
+    perm = graph.perm
+    conv_ = _lib.Convolution(plan, graph)
+    dev = dict(dtype=torch.float64, device="cuda")
+    t = {k: torch.tensor(v, **dev) for k, v in d.items() if k not in ("phi", "shift")}
+    E = len(recv)
+    phi = torch.tensor(d["phi"][perm] if E else np.zeros((1, d["phi"].shape[1])), **dev).contiguous()
+    shift = torch.tensor(d["shift"][perm] if E else np.zeros((1, 3)), **dev).contiguous()
+    out = conv_.forward(t["x"], t["pos"], shift, phi, t["A"])
+    grads = conv_.backward(t["x"], t["pos"], shift, phi, t["A"], t["grad_out"]) if want_bwd else None
+    return graph, perm, out, grads
+
+
+def test_check_edges_clean_graph():
+    from clebsch_gordan_tensor_receiver_amd import _lib
+    from tests.gpu_helpers import GpuCase
+    case = make_case(1)
+    g = GpuCase(case)
+    ws = g.conv.workspace(_lib.OP_FORWARD)
+    assert _lib.check_edges(g.plan, g.graph, g.pos, g.shift, ws) == -1
+
+
+def test_check_edges_finds_first_zero_length_edge():
+    from clebsch_gordan_tensor_receiver_amd import _lib
+    n = 6
+    rng = np.random.default_rng(3)
+    pos = rng.uniform(0, 5, size=(n, 3))
+    pos[4] = pos[1]          # atoms 1 and 4 coincide: edges 1 <- 4 and 4 <- 1 have zero length
+    recv, send = zip(*[(i, j) for i in range(n) for j in range(n) if i != j])
+    recv, send = np.array(recv, np.int32), np.array(send, np.int32)
+    plan = _plan()
+    graph = _lib.Graph(n, recv, send)
+    perm = graph.perm
+    vec = pos[send[perm]] - pos[recv[perm]]
+    expect = int(np.nonzero((vec ** 2).sum(1) == 0.0)[0].min())
+    dev = dict(dtype=torch.float64, device="cuda")
+    ws = torch.empty(4096, dtype=torch.uint8, device="cuda")
+    got = _lib.check_edges(plan, graph, torch.tensor(pos, **dev), torch.zeros((len(recv), 3), **dev), ws)
+    print(f"first zero-length edge {got} (expected {expect})", flush=True)
+    assert got == expect
+
+
+def test_empty_edge_list():
+    K = 4
+    n = 5
+    prob, d = _inputs(n, [], [], np.zeros((0, 3)), K, seed=4)
+    graph, perm, out, grads = _run(_plan(K=K), n, [], [], d)
+    assert out.shape == (n, prob.c_out) and float(out.abs().max()) == 0.0
+    for k in ("x", "pos", "A"):
+        assert float(grads[k].abs().max()) == 0.0, k
+
+
+def test_receivers_without_edges():
+    # A small random graph in which receivers 0, 5 and 9 have no incoming edges and 9 sends none.
+    from tests.gpu_helpers import TOL, rel_err
+    K, n = 4, 10
+    rng = np.random.default_rng(5)
+    pairs = [(i, j) for i in range(n) for j in range(n - 1) if i != j and i not in (0, 5, 9) and rng.random() < 0.5]
+    recv = np.array([p[0] for p in pairs], np.int32)
+    send = np.array([p[1] for p in pairs], np.int32)
+    prob, d = _inputs(n, recv, send, np.zeros((len(recv), 3)), K, seed=6)
+    graph, perm, out, grads = _run(_plan(K=K), n, recv, send, d)
+    ev = conv.edge_vectors(d["pos"], d["shift"][perm], recv[perm], send[perm])
+    ref = conv.forward_conventional(prob, d["x"], ev, recv[perm], send[perm], d["phi"][perm], d["A"]).numpy()
+    assert rel_err(out.cpu().numpy(), ref) <= TOL["float64"]
+    assert float(out[[0, 5, 9]].abs().max()) == 0.0
+    b = conv.backward(prob, d["x"], ev, recv[perm], send[perm], d["phi"][perm], d["A"], d["grad_out"], n_nodes=n)
+    for k in ("x", "pos", "edge_vec", "phi", "A"):
+        err = rel_err(grads[k].cpu().numpy()[:len(b[k])], b[k].numpy())
+        print(f"isolated receivers grad {k}: {err:.3e}", flush=True)
+        assert err <= TOL["float64"], k
+    assert float(grads["x"][9].abs().max()) == 0.0
+
+
+def test_single_atom_periodic_images():
+    # One atom in a 1.5 A periodic cube with cutoff 3 A: every edge joins the atom to one of its
+    # own images, so every edge is a self-loop with a non-zero shift.
+    from tests.gpu_helpers import GpuCase, TOL, rel_err
+    case = make_case(1, n_nodes=1, irreps_override=IRREPS)
+    assert case.n_nodes == 1 and len(case.recv) > 0 and np.all(case.recv == case.send)
+    g = GpuCase(case)
+    out = g.forward().cpu().numpy()
+    ref = conv.forward_conventional(case.problem, case.x, case.edge_vec, case.recv, case.send, case.phi,
+                                    case.A).numpy()
+    assert rel_err(out, ref) <= TOL["float64"]
+    got = g.backward()
+    b = conv.backward(case.problem, case.x, case.edge_vec, case.recv, case.send, case.phi, case.A, case.grad_out)
+    for k in ("x", "pos", "edge_vec", "phi", "A"):
+        err = rel_err(got[k].cpu().numpy(), b[k].numpy())
+        print(f"single atom grad {k}: {err:.3e}", flush=True)
+        # pos-bar of a lone atom is the sum of +e-bar and -e-bar over its self-loops: exactly 0
+        if k == "pos":
+            assert float(np.abs(got[k].cpu().numpy()).max()) <= 1e-12
+        else:
+            assert err <= TOL["float64"], k
