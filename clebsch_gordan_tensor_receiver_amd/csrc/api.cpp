@@ -108,8 +108,8 @@ BwdLayout dbl_layout(const cgtp::Plan& p, const cgtp::Graph& g) {
   BwdLayout L;
   L.ntask_r = int(cgtp::dbl_recv_tasks(p).size());
   L.ntask_s = int(cgtp::source_tasks(p).size());
-  L.V = cgtp::dbl_partial_width(p);
-  L.row = L.ntask_r * L.V;
+  L.V = 0;
+  L.row = cgtp::dbl_partial_row(p);
   long long row_bytes = (long long)(2 * p.g_stride + L.row) * (long long)p.elem();
   L.cap = std::max<long long>(std::max<long long>(1, (long long)(p.scratch_budget / size_t(row_bytes))),
                               g.max_in_degree);
@@ -125,7 +125,7 @@ BwdLayout dbl_layout(const cgtp::Plan& p, const cgtp::Graph& g) {
   L.g_off = off;
   off += align256(size_t(emax) * size_t(2 * p.g_stride) * p.elem());
   L.ep_off = off;
-  off += align256(size_t(emax) * size_t(L.row) * p.elem());
+  off += align256(size_t((emax + 63) / 64 * 64) * size_t(L.row) * p.elem());  // tiles of 64 edges
   L.ap_off = off;
   off += align256(size_t(L.nslot) * size_t(p.K) * size_t(p.n_w) * p.elem());
   L.gev_off = off;

@@ -26,6 +26,11 @@ using namespace gen;
 
 namespace {
 
+// A and A-tangent registers per lane of one path subset in the double backward's forward-tangent
+// and source passes (K values each per path).
+constexpr int kDfwdRegs = 32;
+constexpr int kDsrcRegs = 16;
+
 long double dfact2(int n) {
   long double r = 1;
   for (int k = n; k > 1; k -= 2) r *= k;
@@ -227,7 +232,7 @@ void emit_dfwd_task(Out& o, const Plan& p, int ti, const Task& T) {
   o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
   for (int m = 0; m < d3; ++m) o.line(F("real acc%d = R(0);", m));
   o.line("const int e0 = row_ptr[node], e1 = row_ptr[node + 1];");
-  for (const auto& S : a_subsets(p, T.paths, kRegBudget / 2)) {  // A and its tangent
+  for (const auto& S : a_subsets(p, T.paths, kDfwdRegs)) {  // A and its tangent
     o.open("");
     emit_da_loads(o, p, S);
     emit_dedge_loop(o, p, in_blocks_of(p, S), [&] {
@@ -249,9 +254,14 @@ void emit_dfwd_task(Out& o, const Plan& p, int ti, const Task& T) {
 
 // Receiver-major part of task (output block k, path subset, channel block) for one receiver per wave.
 // Edge partial columns of the task: [0, K) phi-bar-dot, [K, K+Yd) Y-bar-dot, [K+Yd, K+2Yd) Y-bar.
-void emit_drecv_task(Out& o, const Plan& p, int ti, const Task& T, int V) {
+void emit_drecv_task(Out& o, const Plan& p, int ti, const Task& T, int col_off, int row) {
   const Block& OB = p.out[T.group];
-  const int d3 = OB.dim(), MUL = OB.mul, K = p.K, Yd = p.sh_dim;
+  const int d3 = OB.dim(), MUL = OB.mul, K = p.K;
+  const std::vector<int> yc = recv_task_ycols(p, T);
+  const int ny = int(yc.size()), V = dbl_task_width(p, T);
+  // Columns: K phi-bar-dot partials, then Y-bar-dot and first-order Y-bar over the task's Y entries.
+  auto cd = [&](int y) { return K + int(std::find(yc.begin(), yc.end(), y) - yc.begin()); };
+  auto cw = [&](int y) { return cd(y) + ny; };
   o.open(F("DEV void drc_t%d(%s, real* sm, int node, int e_base, int eps, int slot)", ti, kDArgs));
   emit_vz(o, p);
   o.line("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
@@ -269,7 +279,7 @@ void emit_drecv_task(Out& o, const Plan& p, int ti, const Task& T, int V) {
     int ai = 0;
     for (int pi : T.paths) {
       const Path& P = p.paths[pi];
-      const int sd = K + P.l2 * P.l2, sw = K + Yd + P.l2 * P.l2;
+      const int y0 = P.l2 * P.l2;
       emit_wwd(o, p, pi);
       auto started = emit_t_td(o, p, pi, d3);
       bool first = true;
@@ -297,8 +307,8 @@ void emit_drecv_task(Out& o, const Plan& p, int ti, const Task& T, int V) {
       for (auto& gp : P.gpairs) {
         o.line(F("{ const real z = s%d_%d * mb%d, zw = x%d_%d * wm%d_%d;", pi, gp.m1, gp.m3, P.i_in, gp.m1, pi, gp.m3));
         for (auto& t : gp.terms) {
-          o.line(F("  v%d = fma(%s, z, v%d);", sd + t.first, lit(t.second).c_str(), sd + t.first));
-          o.line(F("  v%d = fma(%s, zw, v%d);", sw + t.first, lit(t.second).c_str(), sw + t.first));
+          o.line(F("  v%d = fma(%s, z, v%d);", cd(y0 + t.first), lit(t.second).c_str(), cd(y0 + t.first)));
+          o.line(F("  v%d = fma(%s, zw, v%d);", cw(y0 + t.first), lit(t.second).c_str(), cw(y0 + t.first)));
         }
         o.line("}");
       }
@@ -313,10 +323,11 @@ void emit_drecv_task(Out& o, const Plan& p, int ti, const Task& T, int V) {
     for (int k = 0; k < Q; ++k) pr.push_back({F("v%d", k), F("v%d", k + Q)});
     emit_swaps(o, pr, 16, f64);
     for (int k = 0; k < Q; ++k) o.line(F("v%d += v%d;", k, k + Q));
-    for (int k = 0; k < Q; ++k) o.line(F("v%d = rowsum(v%d);", k, k));
+    for (int k = 0; k < Q; ++k) o.line(F("v%d = rowsum(v%d); asm volatile(\"\" : \"+v\"(v%d));", k, k, k));
     o.open("if ((lane & 15) == 0)");
-    o.line(F("real* __restrict__ dst = ep + (i64)(%d + (lane >> 4) * %d) * eps + (e - e_base);", ti * V, Q));
-    for (int k = 0; k < Q; ++k) o.line(F("dst[(i64)%d * eps] = v%d;", k, k));
+    o.line(F("real* __restrict__ dst = ep + ((i64)((e - e_base) >> 6) * %d + %d + (lane >> 4) * %d) * 64"
+             " + ((e - e_base) & 63);", row, col_off, Q));
+    for (int k = 0; k < Q; ++k) o.line(F("dst[%d] = v%d;", 64 * k, k));
     o.close();
   });
   o.close();
@@ -346,7 +357,7 @@ void emit_dsrc_task(Out& o, const Plan& p, int ti, const Task& T) {
   o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
   for (int m = 0; m < d1; ++m) o.line(F("real acc%d = R(0);", m));
   o.line("const int s0 = src_ptr[node], s1 = src_ptr[node + 1];");
-  for (const auto& S : subsets(p, T.paths)) {
+  for (const auto& S : a_subsets(p, T.paths, kDsrcRegs)) {
     o.open("");
     emit_da_loads(o, p, S);
     o.open("for (int k = s0; k < s1; ++k)");
@@ -397,23 +408,40 @@ void emit_dsrc_task(Out& o, const Plan& p, int ti, const Task& T) {
 }
 
 // Edge finalisation: phi-bar-dot sums, e-bar-dot = J^T Ybar_d + the curvature term.
-void emit_dedge_final(Out& o, const Plan& p, int ntask, int V) {
-  const int K = p.K, Yd = p.sh_dim;
+void emit_dedge_final(Out& o, const Plan& p, const std::vector<Task>& tasks) {
+  const int K = p.K, Yd = p.sh_dim, row = dbl_partial_row(p);
+  std::vector<int> off;
+  std::vector<std::vector<int>> yc;
+  for (int k = 0, c = 0; k < int(tasks.size()); c += dbl_task_width(p, tasks[k]), ++k) {
+    off.push_back(c);
+    yc.push_back(recv_task_ycols(p, tasks[k]));
+  }
   o.line("extern \"C\" __global__ void __launch_bounds__(64)");
   o.open("cgtp_dedge_final(const real* __restrict__ pos, const real* __restrict__ shift, const int* __restrict__ recv,"
          " const int* __restrict__ send, const real* __restrict__ vev, const real* __restrict__ vpos,"
          " const real* __restrict__ ep, int e0, int e1, int eps, real* __restrict__ gphi, real* __restrict__ gev)");
   o.line("const int e = e0 + (int)(blockIdx.x * 64 + threadIdx.x);");
   o.line("if (e >= e1) return;");
-  o.line("const real* __restrict__ col0 = ep + (e - e0);");
-  o.line("#define ROWV(k) col0[(i64)(k) * eps]");
-  auto sum_col = [&](int k) {
-    std::string ex = F("ROWV(%d)", k);
-    for (int t = 1; t < ntask; ++t) ex += F(" + ROWV(%d)", t * V + k);
-    return ex;
+  o.line("(void)eps;");
+  o.line(F("const real* __restrict__ rw = ep + (i64)((e - e0) >> 6) * %d + ((e - e0) & 63);", 64 * row));
+  o.line("#define ROWV(k) rw[64 * (k)]");
+  // Sum of one kind of column over the tasks in order; `shift` 0: Y-bar-dot, 1: first-order Y-bar.
+  auto sum_y = [&](int y, int shift) {
+    std::string ex;
+    for (size_t t = 0; t < tasks.size(); ++t) {
+      auto it = std::find(yc[t].begin(), yc[t].end(), y);
+      if (it == yc[t].end()) continue;
+      const int c = off[t] + K + int(it - yc[t].begin()) + shift * int(yc[t].size());
+      ex += (ex.empty() ? "" : " + ") + F("ROWV(%d)", c);
+    }
+    return ex.empty() ? std::string("R(0)") : ex;
   };
   o.open("if (gphi)");
-  for (int q = 0; q < K; ++q) o.line(F("gphi[(i64)e * %d + %d] = ", K, q) + sum_col(q) + ";");
+  for (int q = 0; q < K; ++q) {
+    std::string ex;
+    for (size_t t = 0; t < tasks.size(); ++t) ex += (t ? " + " : "") + F("ROWV(%d)", off[t] + q);
+    o.line(F("gphi[(i64)e * %d + %d] = ", K, q) + ex + ";");
+  }
   o.close();
   o.line("if (!gev) return;");
   emit_edge_vector(o);
@@ -424,8 +452,8 @@ void emit_dedge_final(Out& o, const Plan& p, int ntask, int V) {
   o.line("const real dx = (vex - nx * nv) * inv, dy = (vey - ny * nv) * inv, dz = (vez - nz * nv) * inv;");
   o.line(F("real ybd[%d], ybw[%d];", Yd, Yd));
   for (int m = 0; m < Yd; ++m) {
-    o.line(F("ybd[%d] = ", m) + sum_col(K + m) + ";");
-    o.line(F("ybw[%d] = ", m) + sum_col(K + Yd + m) + ";");
+    o.line(F("ybd[%d] = ", m) + sum_y(m, 0) + ";");
+    o.line(F("ybw[%d] = ", m) + sum_y(m, 1) + ";");
   }
   o.line("DD accw(R(0));");
   o.line("DD accd(R(0));");
@@ -452,7 +480,15 @@ void emit_dedge_final(Out& o, const Plan& p, int ntask, int V) {
 
 }  // namespace
 
-int dbl_partial_width(const Plan& p) { return (p.K + 2 * p.sh_dim + 3) / 4 * 4; }
+int dbl_task_width(const Plan& p, const Task& T) {
+  return (p.K + 2 * int(recv_task_ycols(p, T).size()) + 3) / 4 * 4;
+}
+
+int dbl_partial_row(const Plan& p) {
+  int r = 0;
+  for (const Task& t : dbl_recv_tasks(p)) r += dbl_task_width(p, t);
+  return r;
+}
 
 std::string generate_dbl_source(const Plan& p, std::string* err) {
   if (p.mode != CGTP_CHANNELWISE) {
@@ -479,11 +515,11 @@ std::string generate_dbl_source(const Plan& p, std::string* err) {
   o.line("default: break;");
   o.close();
   o.close();
-  const int V = dbl_partial_width(p);
   auto rt = dbl_recv_tasks(p);
+  const int row = dbl_partial_row(p);
   int amax = 0;
-  for (int k = 0; k < int(rt.size()); ++k) {
-    emit_drecv_task(o, p, k, rt[k], V);
+  for (int k = 0, off = 0; k < int(rt.size()); off += dbl_task_width(p, rt[k]), ++k) {
+    emit_drecv_task(o, p, k, rt[k], off, row);
     amax = std::max(amax, int(rt[k].paths.size()) * p.K);
   }
   o.line("extern \"C\" __global__ void __launch_bounds__(256)");
@@ -520,7 +556,7 @@ std::string generate_dbl_source(const Plan& p, std::string* err) {
   o.line("default: break;");
   o.close();
   o.close();
-  emit_dedge_final(o, p, int(rt.size()), V);
+  emit_dedge_final(o, p, rt);
   emit_small_kernels(o);
   return o.s.str();
 }

@@ -55,9 +55,11 @@ int recv_partial_row(const Plan& p);
 // Values per edge and task written by the receiver backward (phi-bar partials then
 // Y-bar partials), padded to a multiple of 4.
 int edge_partial_width(const Plan& p);
-// Values per edge and task written by the double backward's receiver pass (phi-bar-dot, then
-// Y-bar-dot, then the first-order Y-bar), padded to a multiple of 4.
-int dbl_partial_width(const Plan& p);
+// Double backward's receiver pass: per task, K phi-bar-dot partials, then the Y-bar-dot and the
+// first-order Y-bar columns of the task's Y entries, padded to a multiple of 4; one row of
+// dbl_partial_row values per edge in 64-edge tiles (as the first-order backward).
+int dbl_task_width(const Plan& p, const Task& T);
+int dbl_partial_row(const Plan& p);
 
 // Fully connected layout: per output block (receiver side) and input block (source side) the
 // state width D (columns (path, q, channel)) and padded row stride ld; per node the sides are
