@@ -308,6 +308,7 @@ const char* kFwdArgs =
     " real* __restrict__ out";
 
 constexpr int kFwdSplit = 2;   // waves sharing one receiver's edge list in the forward
+constexpr bool kLanePrefetch = false;  // gather the next edge's row one edge ahead
 constexpr int kSrcSplit = 2;   // waves sharing one sender's edge list in the source backward
 constexpr int kRecvGroup = 4;  // receivers (one wave each) per workgroup in the receiver backward
 
@@ -320,29 +321,40 @@ void emit_recv_edge_loop(Out& o, const Plan& p, const std::vector<int>& blocks, 
                          int row_stride) {
   auto ucn = [&](int b) { return block_uc ? F("uc%d", b) : std::string("uc"); };
   if (row_stride <= 0) row_stride = p.g_stride;
+  auto xrow = [&](const char* pre, const char* j, const char* type) {
+    for (int b : blocks) {
+      const Block& B = p.in[b];
+      for (int m = 0; m < B.dim(); ++m)
+        o.line(F("%s%s%d_%d = x[(i64)%s * %d + %d + %s];", type, pre, b, m, j, p.c_in, B.offset + m * B.mul,
+                 ucn(b).c_str()));
+    }
+  };
+  // The sender indices of up to 64 of the wave's edges are loaded at once, one per lane, and
+  // taken one by one with readlane: no scalar-load round trip before each edge's row gather.
   o.open("");
-  o.line("int e = e0 + " + start + ";");
-  o.open("if (e < e1)");
-  o.line("int jn = col[e];");
-  for (int b : blocks) {
-    const Block& B = p.in[b];
-    for (int m = 0; m < B.dim(); ++m)
-      o.line(F("real xn%d_%d = x[(i64)jn * %d + %d + %s];", b, m, p.c_in, B.offset + m * B.mul, ucn(b).c_str()));
+  o.line("const int li_ = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));");
+  o.open("for (int eb_ = e0 + " + start + "; eb_ < e1; eb_ += 64 * " + stride + ")");
+  o.line("const int el_ = eb_ + li_ * " + stride + ";");
+  o.line("const int cl_ = col[el_ < e1 ? el_ : eb_];");
+  o.line("const int ne_ = min(64, (e1 - eb_ + " + stride + " - 1) / " + stride + ");");
+  if (kLanePrefetch) {
+    o.line("int jn = __builtin_amdgcn_readlane(cl_, 0);");
+    xrow("xn", "jn", "real ");
   }
-  o.open("for (; e < e1; e += " + stride + ")");
-  o.line("const int j = jn;");
-  for (int b : blocks)
-    for (int m = 0; m < p.in[b].dim(); ++m) o.line(F("const real x%d_%d = xn%d_%d;", b, m, b, m));
-  o.line("{ const int en = e + " + stride + "; jn = col[en < e1 ? en : e]; }");
-  for (int b : blocks) {
-    const Block& B = p.in[b];
-    for (int m = 0; m < B.dim(); ++m)
-      o.line(F("xn%d_%d = x[(i64)jn * %d + %d + %s];", b, m, p.c_in, B.offset + m * B.mul, ucn(b).c_str()));
+  o.open("for (int k_ = 0; k_ < ne_; ++k_)");
+  o.line("const int e = eb_ + k_ * " + stride + ";");
+  if (kLanePrefetch) {
+    for (int b : blocks)
+      for (int m = 0; m < p.in[b].dim(); ++m) o.line(F("const real x%d_%d = xn%d_%d;", b, m, b, m));
+    o.line("jn = __builtin_amdgcn_readlane(cl_, k_ + 1 < ne_ ? k_ + 1 : k_);");
+    xrow("xn", "jn", "");
+  } else {
+    o.line("const int j = __builtin_amdgcn_readlane(cl_, k_);");
+    xrow("x", "j", "const real ");
   }
   o.line(F("const real* __restrict__ ph = phi + (i64)e * %d;", p.K));
   o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", row_stride));
   for (int q = 0; q < p.K; ++q) o.line(F("const real f%d = ph[%d];", q, q));
-  o.line("(void)j;");
   body();
   o.close();
   o.close();
@@ -799,24 +811,34 @@ void emit_bwd_src_task(Out& o, const Plan& p, int ti, const Task& T) {
   o.open("");
   emit_a_loads(o, p, S);
   const auto obs = out_blocks_of(p, S);
-  o.line("int k = s0 + w;");
-  o.open("if (k < s1)");
-  o.line("int en = src_edge[k];");
-  o.line("int in_ = recv[en];");
-  for (int ob : obs) {
-    const Block& B = p.out[ob];
-    for (int m = 0; m < B.dim(); ++m)
-      o.line(F("real mn%d_%d = gout[(i64)in_ * %d + %d + uc];", ob, m, p.c_out, B.offset + m * B.mul));
+  auto mrow = [&](const char* pre, const char* i, const char* type) {
+    for (int ob : obs) {
+      const Block& B = p.out[ob];
+      for (int m = 0; m < B.dim(); ++m)
+        o.line(F("%s%s%d_%d = gout[(i64)%s * %d + %d + uc];", type, pre, ob, m, i, p.c_out, B.offset + m * B.mul));
+    }
+  };
+  // Edge ids and their receivers for up to 64 of the wave's out-edges, one per lane, taken one
+  // by one with readlane (no dependent scalar loads before each edge's gather).
+  o.open(F("for (int kb_ = s0 + w; kb_ < s1; kb_ += %d)", 64 * kSrcSplit));
+  o.line(F("const int kl_ = kb_ + lane * %d;", kSrcSplit));
+  o.line("const int el_ = src_edge[kl_ < s1 ? kl_ : kb_];");
+  o.line("const int il_ = recv[el_];");
+  o.line(F("const int ne_ = min(64, (s1 - kb_ + %d) / %d);", kSrcSplit - 1, kSrcSplit));
+  if (kLanePrefetch) {
+    o.line("int in_ = __builtin_amdgcn_readlane(il_, 0);");
+    mrow("mn", "in_", "real ");
   }
-  o.open(F("for (; k < s1; k += %d)", kSrcSplit));
-  o.line("const int e = en;");
-  for (int ob : obs)
-    for (int m = 0; m < p.out[ob].dim(); ++m) o.line(F("const real mb%d_%d = mn%d_%d;", ob, m, ob, m));
-  o.line(F("{ const int kn = k + %d; en = src_edge[kn < s1 ? kn : k]; in_ = recv[en]; }", kSrcSplit));
-  for (int ob : obs) {
-    const Block& B = p.out[ob];
-    for (int m = 0; m < B.dim(); ++m)
-      o.line(F("mn%d_%d = gout[(i64)in_ * %d + %d + uc];", ob, m, p.c_out, B.offset + m * B.mul));
+  o.open("for (int k_ = 0; k_ < ne_; ++k_)");
+  o.line("const int e = __builtin_amdgcn_readlane(el_, k_);");
+  if (kLanePrefetch) {
+    for (int ob : obs)
+      for (int m = 0; m < p.out[ob].dim(); ++m) o.line(F("const real mb%d_%d = mn%d_%d;", ob, m, ob, m));
+    o.line("in_ = __builtin_amdgcn_readlane(il_, k_ + 1 < ne_ ? k_ + 1 : k_);");
+    mrow("mn", "in_", "");
+  } else {
+    o.line("const int i_ = __builtin_amdgcn_readlane(il_, k_);");
+    mrow("mb", "i_", "const real ");
   }
   o.line(F("const real* __restrict__ ph = phi + (i64)e * %d;", K));
   o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", bwd_row_stride(p)));
@@ -1054,7 +1076,7 @@ void emit_small_kernels(Out& o) {
 
 using namespace gen;
 
-std::vector<Task> forward_tasks(const Plan& p) {
+static std::vector<Task> make_forward_tasks(const Plan& p) {
   std::vector<int> order(p.out.size());
   std::iota(order.begin(), order.end(), 0);
   std::stable_sort(order.begin(), order.end(),
@@ -1068,7 +1090,7 @@ std::vector<Task> forward_tasks(const Plan& p) {
   return t;
 }
 
-std::vector<Task> recv_backward_tasks(const Plan& p) {
+static std::vector<Task> make_recv_backward_tasks(const Plan& p) {
   // Paths of every output block with the same multiplicity and 64-channel block are packed into
   // as few tasks as the register budget allows (first-fit, heaviest first): each task reduces its
   // per-edge partial sums over the channels once, however many output blocks it covers.  The
@@ -1112,11 +1134,11 @@ std::vector<Task> recv_backward_tasks(const Plan& p) {
   return t;
 }
 
-std::vector<Task> dbl_recv_tasks(const Plan& p) {
+static std::vector<Task> make_dbl_recv_tasks(const Plan& p) {
   // Per path the receiver pass of the double backward holds A, its tangent and the A-bar tangent
   // accumulators (3K values per lane).
   std::vector<Task> t;
-  for (const Task& f : forward_tasks(p))
+  for (const Task& f : make_forward_tasks(p))
     for (const auto& S : a_subsets(p, f.paths, 3 * kRegBudget / 2 / 3)) t.push_back({f.group, f.cb, S});
   return t;
 }
@@ -1134,13 +1156,11 @@ std::vector<int> recv_task_ycols(const Plan& p, const Task& T) {
 
 int recv_task_width(const Plan& p, const Task& T) { return (p.K + int(recv_task_ycols(p, T).size()) + 3) / 4 * 4; }
 
-int recv_partial_row(const Plan& p) {
-  int r = 0;
-  for (const Task& t : recv_backward_tasks(p)) r += recv_task_width(p, t);
-  return r;
-}
+int recv_partial_row(const Plan& p) { return task_tables(p).recv_row; }
 
-std::vector<Task> source_tasks(const Plan& p) {
+
+
+static std::vector<Task> make_source_tasks(const Plan& p) {
   std::vector<Task> t;
   for (int k = 0; k < int(p.in.size()); ++k) {
     if (p.by_in[k].empty()) continue;
@@ -1149,6 +1169,25 @@ std::vector<Task> source_tasks(const Plan& p) {
   }
   return t;
 }
+
+const TaskTables& task_tables(const Plan& p) {
+  std::call_once(p.tables_once, [&p] {
+    auto t = std::make_unique<TaskTables>();
+    t->fwd = make_forward_tasks(p);
+    t->recv = make_recv_backward_tasks(p);
+    t->dbl_recv = make_dbl_recv_tasks(p);
+    t->src = make_source_tasks(p);
+    for (const Task& k : t->recv) t->recv_row += recv_task_width(p, k);
+    for (const Task& k : t->dbl_recv) t->dbl_row += dbl_task_width(p, k);
+    p.tables = std::move(t);
+  });
+  return *p.tables;
+}
+
+const std::vector<Task>& forward_tasks(const Plan& p) { return task_tables(p).fwd; }
+const std::vector<Task>& recv_backward_tasks(const Plan& p) { return task_tables(p).recv; }
+const std::vector<Task>& dbl_recv_tasks(const Plan& p) { return task_tables(p).dbl_recv; }
+const std::vector<Task>& source_tasks(const Plan& p) { return task_tables(p).src; }
 
 int edge_partial_width(const Plan& p) { return (p.K + p.sh_dim + 3) / 4 * 4; }
 

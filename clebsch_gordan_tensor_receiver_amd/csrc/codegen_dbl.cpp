@@ -484,11 +484,7 @@ int dbl_task_width(const Plan& p, const Task& T) {
   return (p.K + 2 * int(recv_task_ycols(p, T).size()) + 3) / 4 * 4;
 }
 
-int dbl_partial_row(const Plan& p) {
-  int r = 0;
-  for (const Task& t : dbl_recv_tasks(p)) r += dbl_task_width(p, t);
-  return r;
-}
+int dbl_partial_row(const Plan& p) { return task_tables(p).dbl_row; }
 
 std::string generate_dbl_source(const Plan& p, std::string* err) {
   if (p.mode != CGTP_CHANNELWISE) {

@@ -39,10 +39,12 @@ struct Task {
   int cb;                 // 64-channel block
   std::vector<int> paths; // paths handled (receiver backward: one register-budgeted subset)
 };
-std::vector<Task> forward_tasks(const Plan& p);
-std::vector<Task> recv_backward_tasks(const Plan& p);
-std::vector<Task> dbl_recv_tasks(const Plan& p);
-std::vector<Task> source_tasks(const Plan& p);
+// The task lists below are derived from the plan alone; they are built once per plan, on first
+// use (every call's host side reads them), and returned by reference.
+const std::vector<Task>& forward_tasks(const Plan& p);
+const std::vector<Task>& recv_backward_tasks(const Plan& p);
+const std::vector<Task>& dbl_recv_tasks(const Plan& p);
+const std::vector<Task>& source_tasks(const Plan& p);
 // Values per edge in the backward's workspace rows: the G row (g_stride values) followed by the
 // spherical harmonics Y (sh_dim values), padded to a multiple of 4.
 int bwd_row_stride(const Plan& p);
@@ -60,6 +62,12 @@ int edge_partial_width(const Plan& p);
 // dbl_partial_row values per edge in 64-edge tiles (as the first-order backward).
 int dbl_task_width(const Plan& p, const Task& T);
 int dbl_partial_row(const Plan& p);
+
+struct TaskTables {
+  std::vector<Task> fwd, recv, dbl_recv, src;
+  int recv_row = 0, dbl_row = 0;
+};
+const TaskTables& task_tables(const Plan& p);
 
 // Fully connected layout: per output block (receiver side) and input block (source side) the
 // state width D (columns (path, q, channel)) and padded row stride ld; per node the sides are

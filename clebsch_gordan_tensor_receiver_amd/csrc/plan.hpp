@@ -44,6 +44,7 @@ struct Path {
 
 // Kernel family state (compiled code objects and loaded modules per device).
 struct KernelSet;
+struct TaskTables;
 
 // Paths with more (m1, m3) pairs than this read their folded coefficients through vector loads
 // (the scalar register file cannot hold them per edge).
@@ -66,6 +67,8 @@ struct Plan {
   std::string key;     // canonical description used to name and cache kernels
   std::unique_ptr<KernelSet> kernels;
   std::mutex mu;
+  mutable std::once_flag tables_once;              // task lists (kernels.hpp), built on first use
+  mutable std::unique_ptr<TaskTables> tables;
   size_t elem() const { return dtype == CGTP_F64 ? 8 : 4; }
   ~Plan();
 };
