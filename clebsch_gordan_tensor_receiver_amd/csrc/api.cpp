@@ -377,8 +377,8 @@ cgtp_status_t cgtp_conv_forward(cgtp_plan_t plan, cgtp_graph_t g, cgtp_schedule_
       CGTP_OK)
     return fail(st, err);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  auto tasks = cgtp::forward_tasks(p);
-  int ntask = int(tasks.size());
+  const cgtp::TaskGroups tg = cgtp::task_groups(cgtp::forward_tasks(p));
+  const int ngroup = int(tg.tasks.size());
   void* G_ws = workspace;
   for (auto& c : G.chunks(g_chunk_edges(p, G))) {
     int i0 = c.first, nrec = c.second - c.first;
@@ -390,7 +390,7 @@ cgtp_status_t cgtp_conv_forward(cgtp_plan_t plan, cgtp_graph_t g, cgtp_schedule_
     }
     int per = (nrec + 7) / 8;
     void* b[] = {(void*)&x, (void*)&phi, (void*)&A, &G_ws, (void*)&d.row_ptr, (void*)&d.col, &out, &i0, &nrec, &per, &e0};
-    if ((st = cgtp::launch(kfwd, unsigned(8 * ntask * per), 64 * kFwdSplit, 0, s, b, &err)) != CGTP_OK)
+    if ((st = cgtp::launch(kfwd, unsigned(8 * ngroup * per), 64 * kFwdSplit * tg.ncb, 0, s, b, &err)) != CGTP_OK)
       return fail(st, err);
   }
   return ok();
@@ -450,7 +450,8 @@ cgtp_status_t cgtp_conv_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x
     void* a[] = {&ap, &n};
     if ((st = cgtp::launch(kzero, unsigned((n + 255) / 256), 256, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
   }
-  const int nt_r = L.ntask_r, nt_s = L.ntask_s;
+  const int nt_r = L.ntask_r;
+  const cgtp::TaskGroups tsrc = cgtp::task_groups(cgtp::source_tasks(p));
   int eps = int(L.emax);
   for (size_t c = 0; c < L.chunks.size(); ++c) {
     int i0 = L.chunks[c].first, nrec = L.chunks[c].second - L.chunks[c].first;
@@ -474,7 +475,8 @@ cgtp_status_t cgtp_conv_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x
       void* se = static_cast<int32_t*>(views->base) + views->edge_off[c];
       void* a[] = {(void*)&phi, (void*)&A, &Gb, (void*)&grad_out, (void*)&d.recv, &sp, &se, &grad_x, &n, &per, &e0,
                    &acc};
-      if ((st = cgtp::launch(ksrc, unsigned(8 * nt_s * per), 64 * kSrcSplit, 0, s, a, &err)) != CGTP_OK)
+      if ((st = cgtp::launch(ksrc, unsigned(8 * tsrc.tasks.size() * per), 64 * kSrcSplit * tsrc.ncb, 0, s, a, &err)) !=
+          CGTP_OK)
         return fail(st, err);
     }
     if (need_edge && e1 > e0) {

@@ -436,7 +436,8 @@ void emit_fwd_task(Out& o, const Plan& p, int ti, const Task& T) {
   const int MUL = p.out[p.paths[T.paths[0]].i_out].mul;
   const std::vector<int> obs = out_blocks_of(p, T.paths);
   o.open(F("DEV void fwd_t%d(%s, real* sm, int node, int e_base)", ti, kFwdArgs));
-  o.line("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
+  o.line(F("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) %% %d;",
+           kFwdSplit));
   emit_vz(o, p);
   o.line(F("const int u = %d + lane;", T.cb * 64));
   o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
@@ -474,7 +475,8 @@ void emit_fwd_streamed_task(Out& o, const Plan& p, int ti, const Task& T) {
   const Block& OB = p.out[T.group];
   const int d3 = OB.dim(), MUL = OB.mul, K = p.K;
   o.open(F("DEV void fwds_t%d(%s, real* sm, int node, int e_base)", ti, kFwdArgs));
-  o.line("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
+  o.line(F("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) %% %d;",
+           kFwdSplit));
   emit_vz(o, p);
   o.line(F("const int u = %d + lane;", T.cb * 64));
   o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
@@ -530,22 +532,35 @@ int max_in_dim(const Plan& p) {
 // round-robin by the hardware; this mapping gives each XCD a contiguous receiver range (spatial
 // neighbours, whose senders' rows then stay in that XCD's L2) and runs the tasks in decreasing
 // cost order inside it (LunaTP section 4.2, task ordering).
+// Switch of a grouped dispatch: wave set `cb` of group `t` runs task tasks[t][cb]; the waves of
+// a missing channel block only take part in the one workgroup barrier every task function has.
+void emit_group_switch(Out& o, const TaskGroups& tg, const std::string& call_fmt) {
+  o.open(F("switch (t * %d + cb)", tg.ncb));
+  for (int t = 0; t < int(tg.tasks.size()); ++t)
+    for (int c = 0; c < int(tg.tasks[t].size()); ++c) {
+      std::string call = call_fmt;
+      for (size_t at; (at = call.find("%T")) != std::string::npos;) call.replace(at, 2, std::to_string(tg.tasks[t][c]));
+      o.line(F("case %d: ", t * tg.ncb + c) + call + " break;");
+    }
+  o.line("default: __syncthreads(); break;");
+  o.close();
+}
+
 void emit_node_dispatch(Out& o, const Plan& p, const std::string& kname, const std::string& args,
-                        const std::string& call, int ntask, int nacc) {
-  o.line(F("extern \"C\" __global__ void __launch_bounds__(%d)", 64 * kFwdSplit));
+                        const std::string& call, const TaskGroups& tg, int nacc) {
+  const int slice = (kFwdSplit - 1) * nacc * 64;
+  o.line(F("extern \"C\" __global__ void __launch_bounds__(%d)", 64 * kFwdSplit * tg.ncb));
   o.open(kname + "(" + args + ", int i0, int nrec, int per, int e_base)");
-  o.line(F("__shared__ real sm[%d];", (kFwdSplit - 1) * nacc * 64));
+  o.line(F("__shared__ real sm[%d];", std::max(1, tg.ncb * slice)));
   o.line("const int b = (int)blockIdx.x;");
   o.line("const int xcd = b & 7, s = b >> 3;");
   o.line("const int t = s / per, il = s - t * per;");
   o.line("const int i = xcd * per + il;");
   o.line("if (i >= nrec) return;");
   o.line("const int node = i0 + i;");
-  o.open("switch (t)");
-  for (int k = 0; k < ntask; ++k)
-    o.line(F("case %d: %s%d(x, phi, A, G, row_ptr, col, out, sm, node, e_base); break;", k, call.c_str(), k));
-  o.line("default: break;");
-  o.close();
+  o.line(F("const int cb = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) / %d;", kFwdSplit));
+  o.line(F("real* const smc = sm + cb * %d;", slice));
+  emit_group_switch(o, tg, call + "%T(x, phi, A, G, row_ptr, col, out, smc, node, e_base);");
   o.close();
 }
 
@@ -796,7 +811,8 @@ void emit_bwd_src_task(Out& o, const Plan& p, int ti, const Task& T) {
   const int MUL = p.in[p.paths[T.paths[0]].i_in].mul, K = p.K;
   const std::vector<int> ibs = in_blocks_of(p, T.paths);
   o.open(F("DEV void bws_t%d(%s, real* sm, int node, int e_base, int accumulate)", ti, kSrcArgs));
-  o.line("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
+  o.line(F("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) %% %d;",
+           kSrcSplit));
   emit_vz(o, p);
   o.line(F("const int u = %d + lane;", T.cb * 64));
   o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
@@ -893,20 +909,20 @@ void emit_src_dispatch(Out& o, const Plan& p, int ntask) {
     for (int ib : in_blocks_of(p, t.paths)) n += p.in[ib].dim();
     nacc = std::max(nacc, n);
   }
-  o.line(F("extern \"C\" __global__ void __launch_bounds__(%d)", 64 * kSrcSplit));
+  const TaskGroups tg = task_groups(source_tasks(p));
+  (void)ntask;
+  const int slice = (kSrcSplit - 1) * nacc * 64;
+  o.line(F("extern \"C\" __global__ void __launch_bounds__(%d)", 64 * kSrcSplit * tg.ncb));
   o.open(std::string("cgtp_bwd_src(") + kSrcArgs + ", int nrec, int per, int e_base, int accumulate)");
-  o.line(F("__shared__ real sm[%d];", (kSrcSplit - 1) * nacc * 64));
+  o.line(F("__shared__ real sm[%d];", std::max(1, tg.ncb * slice)));
   o.line("const int b = (int)blockIdx.x;");
   o.line("const int xcd = b & 7, s = b >> 3;");
   o.line("const int t = s / per, il = s - t * per;");
   o.line("const int node = xcd * per + il;");
   o.line("if (node >= nrec) return;");
-  o.open("switch (t)");
-  for (int k = 0; k < ntask; ++k)
-    o.line(F("case %d: bws_t%d(phi, A, G, gout, recv, src_ptr, src_edge, gx, sm, node, e_base, accumulate); break;",
-             k, k));
-  o.line("default: break;");
-  o.close();
+  o.line(F("const int cb = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) / %d;", kSrcSplit));
+  o.line(F("real* const smc = sm + cb * %d;", slice));
+  emit_group_switch(o, tg, "bws_t%T(phi, A, G, gout, recv, src_ptr, src_edge, gx, smc, node, e_base, accumulate);");
   o.close();
 }
 
@@ -1184,6 +1200,24 @@ const TaskTables& task_tables(const Plan& p) {
   return *p.tables;
 }
 
+TaskGroups task_groups(const std::vector<Task>& tasks) {
+  TaskGroups g;
+  std::vector<int> key;  // group of each entry of g.tasks
+  for (int k = 0; k < int(tasks.size()); ++k) {
+    auto it = std::find(key.begin(), key.end(), tasks[k].group);
+    size_t at = it - key.begin();
+    if (it == key.end()) {
+      key.push_back(tasks[k].group);
+      g.tasks.emplace_back();
+    }
+    auto& v = g.tasks[at];
+    if (int(v.size()) <= tasks[k].cb) v.resize(tasks[k].cb + 1, -1);
+    v[tasks[k].cb] = k;
+    g.ncb = std::max(g.ncb, int(v.size()));
+  }
+  return g;
+}
+
 const std::vector<Task>& forward_tasks(const Plan& p) { return task_tables(p).fwd; }
 const std::vector<Task>& recv_backward_tasks(const Plan& p) { return task_tables(p).recv; }
 const std::vector<Task>& dbl_recv_tasks(const Plan& p) { return task_tables(p).dbl_recv; }
@@ -1210,7 +1244,7 @@ std::string generate_source(const Plan& p, const std::string& family, std::strin
       nacc = std::max(nacc, n);
     }
     emit_node_dispatch(o, p, streamed ? "cgtp_fwd_streamed" : "cgtp_fwd", kFwdArgs, streamed ? "fwds_t" : "fwd_t",
-                       int(tasks.size()), nacc);
+                       task_groups(tasks), nacc);
     return o.s.str();
   }
   if (family == "dbl") return generate_dbl_source(p, err);

@@ -45,6 +45,15 @@ const std::vector<Task>& forward_tasks(const Plan& p);
 const std::vector<Task>& recv_backward_tasks(const Plan& p);
 const std::vector<Task>& dbl_recv_tasks(const Plan& p);
 const std::vector<Task>& source_tasks(const Plan& p);
+// Task groups of a list: tasks sharing a feature block (`group`), in first-appearance order.
+// One workgroup runs all channel blocks of a group for one node, so that their waves, which read
+// the same coefficient rows edge by edge, share the CU's scalar cache.  `ncb` = the largest
+// channel-block count of a group (waves of a smaller group's missing blocks idle).
+struct TaskGroups {
+  int ncb = 1;
+  std::vector<std::vector<int>> tasks;  // per group: task index of channel block cb
+};
+TaskGroups task_groups(const std::vector<Task>& tasks);
 // Values per edge in the backward's workspace rows: the G row (g_stride values) followed by the
 // spherical harmonics Y (sh_dim values), padded to a multiple of 4.
 int bwd_row_stride(const Plan& p);
