@@ -51,7 +51,6 @@ long long max_chunk_edges(const cgtp::Graph& g, const std::vector<std::pair<int,
 }
 
 // Launch geometry shared with the generated kernels (codegen.cpp).
-constexpr int kFwdSplit = 2;    // waves per receiver in the forward
 constexpr int kSrcSplit = 2;    // waves per sender in the source backward
 constexpr int kRecvGroup = 4;   // receivers (one wave each) per workgroup in the receiver backward
 
@@ -390,7 +389,7 @@ cgtp_status_t cgtp_conv_forward(cgtp_plan_t plan, cgtp_graph_t g, cgtp_schedule_
     }
     int per = (nrec + 7) / 8;
     void* b[] = {(void*)&x, (void*)&phi, (void*)&A, &G_ws, (void*)&d.row_ptr, (void*)&d.col, &out, &i0, &nrec, &per, &e0};
-    if ((st = cgtp::launch(kfwd, unsigned(8 * ngroup * per), 64 * kFwdSplit * tg.ncb, 0, s, b, &err)) != CGTP_OK)
+    if ((st = cgtp::launch(kfwd, unsigned(8 * ngroup * per), 64 * cgtp::fwd_split(p) * tg.ncb, 0, s, b, &err)) != CGTP_OK)
       return fail(st, err);
   }
   return ok();

@@ -307,8 +307,8 @@ const char* kFwdArgs =
     " const real* __restrict__ G, const int* __restrict__ row_ptr, const int* __restrict__ col,"
     " real* __restrict__ out";
 
-constexpr int kFwdSplit = 2;   // waves sharing one receiver's edge list in the forward
 constexpr bool kLanePrefetch = false;  // gather the next edge's row one edge ahead
+constexpr int kFwdRegs = kRegBudget;   // A registers per lane of one path subset in the forward
 constexpr int kSrcSplit = 2;   // waves sharing one sender's edge list in the source backward
 constexpr int kRecvGroup = 4;  // receivers (one wave each) per workgroup in the receiver backward
 
@@ -429,7 +429,7 @@ void emit_wave_combine_names(Out& o, const std::vector<std::string>& names, int 
 }
 
 // Channelwise conventional forward of task (output block k, channel block cb) for one receiver;
-// the receiver's edges are dealt round-robin to the kFwdSplit waves of the workgroup and their
+// the receiver's edges are dealt round-robin to the fwd_split waves of the workgroup and their
 // partial sums combined in LDS.  Paths are processed in register-budgeted subsets, each
 // re-walking the edges.
 void emit_fwd_task(Out& o, const Plan& p, int ti, const Task& T) {
@@ -437,7 +437,7 @@ void emit_fwd_task(Out& o, const Plan& p, int ti, const Task& T) {
   const std::vector<int> obs = out_blocks_of(p, T.paths);
   o.open(F("DEV void fwd_t%d(%s, real* sm, int node, int e_base)", ti, kFwdArgs));
   o.line(F("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) %% %d;",
-           kFwdSplit));
+           fwd_split(p)));
   emit_vz(o, p);
   o.line(F("const int u = %d + lane;", T.cb * 64));
   o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
@@ -448,10 +448,10 @@ void emit_fwd_task(Out& o, const Plan& p, int ti, const Task& T) {
       o.line("real " + accs.back() + " = R(0);");
     }
   o.line("const int e0 = row_ptr[node], e1 = row_ptr[node + 1];");
-  for (const auto& S : a_subsets(p, T.paths, kRegBudget)) {
+  for (const auto& S : a_subsets(p, T.paths, kFwdRegs)) {
     o.open("");
     emit_a_loads(o, p, S);
-    emit_recv_edge_loop(o, p, in_blocks_of(p, S), "w", std::to_string(kFwdSplit), [&] {
+    emit_recv_edge_loop(o, p, in_blocks_of(p, S), "w", std::to_string(fwd_split(p)), [&] {
       for (int pi : S) {
         emit_w(o, p, pi);
         emit_path_accumulate(o, p, pi, F("acc%d_", p.paths[pi].i_out));
@@ -459,7 +459,7 @@ void emit_fwd_task(Out& o, const Plan& p, int ti, const Task& T) {
     });
     o.close();
   }
-  emit_wave_combine_names(o, accs, kFwdSplit);
+  emit_wave_combine_names(o, accs, fwd_split(p));
   o.open(F("if (w == 0 && u < %d)", MUL));
   o.line(F("real* __restrict__ dst = out + (i64)node * %d + u;", p.c_out));
   for (int ob : obs)
@@ -476,7 +476,7 @@ void emit_fwd_streamed_task(Out& o, const Plan& p, int ti, const Task& T) {
   const int d3 = OB.dim(), MUL = OB.mul, K = p.K;
   o.open(F("DEV void fwds_t%d(%s, real* sm, int node, int e_base)", ti, kFwdArgs));
   o.line(F("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) %% %d;",
-           kFwdSplit));
+           fwd_split(p)));
   emit_vz(o, p);
   o.line(F("const int u = %d + lane;", T.cb * 64));
   o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
@@ -487,7 +487,7 @@ void emit_fwd_streamed_task(Out& o, const Plan& p, int ti, const Task& T) {
     o.open("");
     for (int q = 0; q < K; ++q)
       for (int m = 0; m < d3; ++m) o.line(F("real S%d_%d = R(0);", q, m));
-    emit_recv_edge_loop(o, p, {P.i_in}, "w", std::to_string(kFwdSplit), [&] {
+    emit_recv_edge_loop(o, p, {P.i_in}, "w", std::to_string(fwd_split(p)), [&] {
       std::vector<bool> started(d3, false);
       for (size_t t = 0; t < P.gpairs.size(); ++t) {
         int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3;
@@ -508,7 +508,7 @@ void emit_fwd_streamed_task(Out& o, const Plan& p, int ti, const Task& T) {
     }
     o.close();
   }
-  emit_wave_combine(o, "acc", d3, kFwdSplit);
+  emit_wave_combine(o, "acc", d3, fwd_split(p));
   o.open(F("if (w == 0 && u < %d)", MUL));
   o.line(F("real* __restrict__ dst = out + (i64)node * %d + %d + u;", p.c_out, OB.offset));
   for (int m = 0; m < d3; ++m) o.line(F("dst[%d] = acc%d;", m * MUL, m));
@@ -528,7 +528,7 @@ int max_in_dim(const Plan& p) {
   return d;
 }
 
-// One receiver per workgroup of kFwdSplit waves.  Workgroups are spread over the 8 XCDs
+// One receiver per workgroup of fwd_split waves.  Workgroups are spread over the 8 XCDs
 // round-robin by the hardware; this mapping gives each XCD a contiguous receiver range (spatial
 // neighbours, whose senders' rows then stay in that XCD's L2) and runs the tasks in decreasing
 // cost order inside it (LunaTP section 4.2, task ordering).
@@ -548,8 +548,8 @@ void emit_group_switch(Out& o, const TaskGroups& tg, const std::string& call_fmt
 
 void emit_node_dispatch(Out& o, const Plan& p, const std::string& kname, const std::string& args,
                         const std::string& call, const TaskGroups& tg, int nacc) {
-  const int slice = (kFwdSplit - 1) * nacc * 64;
-  o.line(F("extern \"C\" __global__ void __launch_bounds__(%d)", 64 * kFwdSplit * tg.ncb));
+  const int slice = (fwd_split(p) - 1) * nacc * 64;
+  o.line(F("extern \"C\" __global__ void __launch_bounds__(%d)", 64 * fwd_split(p) * tg.ncb));
   o.open(kname + "(" + args + ", int i0, int nrec, int per, int e_base)");
   o.line(F("__shared__ real sm[%d];", std::max(1, tg.ncb * slice)));
   o.line("const int b = (int)blockIdx.x;");
@@ -558,7 +558,7 @@ void emit_node_dispatch(Out& o, const Plan& p, const std::string& kname, const s
   o.line("const int i = xcd * per + il;");
   o.line("if (i >= nrec) return;");
   o.line("const int node = i0 + i;");
-  o.line(F("const int cb = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) / %d;", kFwdSplit));
+  o.line(F("const int cb = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) / %d;", fwd_split(p)));
   o.line(F("real* const smc = sm + cb * %d;", slice));
   emit_group_switch(o, tg, call + "%T(x, phi, A, G, row_ptr, col, out, smc, node, e_base);");
   o.close();
@@ -1217,6 +1217,10 @@ TaskGroups task_groups(const std::vector<Task>& tasks) {
   }
   return g;
 }
+
+// Two waves split a receiver's edges in single precision; in double precision the latency of the
+// (twice as many) coefficient loads is better hidden by more receivers in flight.
+int fwd_split(const Plan& p) { return p.dtype == CGTP_F64 ? 1 : 2; }
 
 const std::vector<Task>& forward_tasks(const Plan& p) { return task_tables(p).fwd; }
 const std::vector<Task>& recv_backward_tasks(const Plan& p) { return task_tables(p).recv; }

@@ -26,7 +26,7 @@ using namespace gen;
 
 namespace {
 
-constexpr int kStateBudget = 128;  // receiver/source state registers per lane per task
+constexpr int kStateBudget = 96;   // receiver/source state registers per lane per task
 
 struct Side {                 // one output block (receiver side) or input block (source side)
   int blk;                    // block index
@@ -428,23 +428,20 @@ void emit_zstate_task(Out& o, const Plan& p, const std::vector<Side>& sides, int
     for (int q = 0; q < K; ++q)
       for (int m = 0; m < d1; ++m) o.line(F("real z%d_%d_%d = R(0);", pi, q, m));
   o.line("const int s0 = src_ptr[node], s1 = src_ptr[node + 1];");
-  o.open("if (s0 < s1)");
-  o.line("int en = src_edge[s0];");
-  o.line("int in_ = recv[en];");
+  // Edge ids and receivers of up to 64 out-edges, one per lane, taken one by one with readlane.
+  o.open("for (int kb_ = s0; kb_ < s1; kb_ += 64)");
+  o.line("const int kl_ = kb_ + lane;");
+  o.line("const int el_ = src_edge[kl_ < s1 ? kl_ : kb_];");
+  o.line("const int il_ = recv[el_];");
+  o.line("const int ne_ = min(64, s1 - kb_);");
+  o.open("for (int k_ = 0; k_ < ne_; ++k_)");
+  o.line("const int k = kb_ + k_;");
+  o.line("const int e = __builtin_amdgcn_readlane(el_, k_);");
+  o.line("const int i_ = __builtin_amdgcn_readlane(il_, k_);");
   for (int ob : obs) {
     const Block& B = p.out[ob];
     for (int m = 0; m < B.dim(); ++m)
-      o.line(F("real mn%d_%d = gout[(i64)in_ * %d + %d + wc%d];", ob, m, p.c_out, B.offset + m * B.mul, ob));
-  }
-  o.open("for (int k = s0; k < s1; ++k)");
-  o.line("const int e = en;");
-  for (int ob : obs)
-    for (int m = 0; m < p.out[ob].dim(); ++m) o.line(F("const real mb%d_%d = mn%d_%d;", ob, m, ob, m));
-  o.line("{ const int kn = k + 1; en = src_edge[kn < s1 ? kn : k]; in_ = recv[en]; }");
-  for (int ob : obs) {
-    const Block& B = p.out[ob];
-    for (int m = 0; m < B.dim(); ++m)
-      o.line(F("mn%d_%d = gout[(i64)in_ * %d + %d + wc%d];", ob, m, p.c_out, B.offset + m * B.mul, ob));
+      o.line(F("const real mb%d_%d = gout[(i64)i_ * %d + %d + wc%d];", ob, m, p.c_out, B.offset + m * B.mul, ob));
   }
   o.line(F("const real* __restrict__ ph = phi + (i64)e * %d;", K));
   o.line(F("const real* __restrict__ g = G + (i64)(k - k_base) * %d;", p.g_stride));

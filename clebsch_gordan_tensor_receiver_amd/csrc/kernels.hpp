@@ -54,6 +54,8 @@ struct TaskGroups {
   std::vector<std::vector<int>> tasks;  // per group: task index of channel block cb
 };
 TaskGroups task_groups(const std::vector<Task>& tasks);
+// Waves per (receiver, channel block) in the forward kernels: they deal the edges round-robin.
+int fwd_split(const Plan& p);
 // Values per edge in the backward's workspace rows: the G row (g_stride values) followed by the
 // spherical harmonics Y (sh_dim values), padded to a multiple of 4.
 int bwd_row_stride(const Plan& p);
