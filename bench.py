@@ -16,6 +16,11 @@ inputs resident in device memory.  Prints one JSON line:
 forward schedules; 3: forward, float64; 4: fully connected streamed forward + backward; 5:
 forward + backward + double backward); ``--copy-probe`` only runs a device copy of known size,
 which calibrates the HBM byte counters of rocprofv3.
+
+``--sweep degree|copies`` runs the scaling axes of the Sobek page's section 5.1 (fully connected
+irrep profiles 128/64, 128/64/64, 128/64/64/64; ``--profile L`` picks one): per point one JSON
+line with forward and backward time, edges/s, the library's workspace for each pass, the bytes
+a materialised E x N_w weight tensor would take, and the peak device allocation of the point.
 """
 
 from __future__ import annotations
@@ -186,6 +191,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of known size (calibrates the HBM byte counters)")
+    ap.add_argument("--sweep", choices=("degree", "copies"),
+                    help="scaling axis of the fully connected profiles (one JSON line per point)")
+    ap.add_argument("--profile", type=int, default=0, choices=(0, 1, 2, 3),
+                    help="irrep profile (L_max) of the sweep; 0: all three")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -203,6 +212,8 @@ def main() -> int:
     torch.cuda.set_device(0)
     if args.copy_probe:
         return copy_probe(torch)
+    if args.sweep:
+        return sweep(torch, cg, args)
     cfg = args.workload
     passes = PASSES[cfg]
     spec = CONFIGS[cfg]
@@ -334,6 +345,77 @@ def main() -> int:
     if cfg == DEFAULT_WORKLOAD and not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity"] = cpu_baseline(w, plan, perm, x_h, A_h, g_h, out, grads)
     print(json.dumps(result), flush=True)
+    return 0
+
+
+def sweep(torch, cg, args) -> int:
+    """Scaling axis `args.sweep` of the fully connected profiles: streamed forward and backward
+    (gradients of x, phi, A and positions) per point, timed separately with the library's default
+    scratch budget."""
+    from workloads import sweeps
+
+    points = sweeps.DEGREES if args.sweep == "degree" else sweeps.COPIES
+    profiles = [args.profile] if args.profile else sorted(sweeps.PROFILES)
+    steps, warmup = max(1, min(args.steps, 5)), max(1, min(args.warmup, 2))
+    for L in profiles:
+        s = sweeps.PROFILES[L]
+        plan = cg.Plan(s["irreps_in"], s["irreps_sh"], s["irreps_out"], s["mode"], s["dtype"], s["K"])
+        if args.scratch_mib > 0:
+            plan.set_scratch_budget(args.scratch_mib << 20)
+        plan.compile((cg.OP_FORWARD, cg.OP_BACKWARD))
+        info = plan.info
+        for pt in points:
+            g = sweeps.sweep_graph(args.sweep, pt)
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+            torch.cuda.reset_peak_memory_stats()
+            base = torch.cuda.memory_allocated()
+            graph = cg.Graph(g.n_nodes, g.recv, g.send, g.image)
+            perm = graph.perm
+            N, E = g.n_nodes, graph.n_edges
+            dev = dict(dtype=torch.float32, device="cuda")
+            x = torch.tensor(sweeps.normal(1, (N, info["c_in"])), **dev)
+            A = torch.tensor(sweeps.normal(2, (s["K"], info["n_weights"]), std=1.0 / np.sqrt(s["K"])), **dev)
+            gout = torch.tensor(sweeps.normal(3, (N, info["c_out"])), **dev)
+            r32 = lambda a: a.astype(np.float32)  # noqa: E731
+            pos = torch.tensor(r32(g.pos), **dev)
+            shift = torch.tensor(r32(g.shift[perm]), **dev).contiguous()
+            phi = torch.tensor(r32(g.phi[perm]), **dev).contiguous()
+            graph.upload()
+            conv = cg.Convolution(plan, graph)
+            ws_f, ws_b = conv.workspace(cg.OP_FORWARD), conv.workspace(cg.OP_BACKWARD)
+            out = torch.empty((N, info["c_out"]), **dev)
+            grads = dict(x=torch.empty_like(x), pos=torch.empty_like(pos), edge_vec=torch.empty((E, 3), **dev),
+                         phi=torch.empty_like(phi), A=torch.empty_like(A))
+
+            def fwd():
+                cg.conv_forward(plan, graph, cg.STREAMED, x, pos, shift, phi, A, out, ws_f)
+
+            def bwd():
+                cg.conv_backward(plan, graph, x, pos, shift, phi, A, gout, grad_x=grads["x"], grad_pos=grads["pos"],
+                                 grad_edge_vec=grads["edge_vec"], grad_phi=grads["phi"], grad_A=grads["A"],
+                                 workspace=ws_b)
+
+            times = {}
+            for name, fn in (("fwd", fwd), ("bwd", bwd)):
+                for _ in range(warmup):
+                    fn()
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(steps):
+                    fn()
+                torch.cuda.synchronize()
+                times[name] = (time.perf_counter() - t0) / steps
+            line = {"sweep": args.sweep, "point": pt, "profile": f"L{L} " + s["irreps_in"], "n_weights": info["n_weights"],
+                    "n_nodes": N, "n_edges": E, "mean_degree": round(E / N, 2), "cutoff_A": round(g.rc, 3),
+                    "fwd_ms": round(1e3 * times["fwd"], 3), "bwd_ms": round(1e3 * times["bwd"], 3),
+                    "edges_per_s_fwd_bwd": round(E / (times["fwd"] + times["bwd"]), 1),
+                    "workspace_fwd_bytes": int(ws_f.numel()), "workspace_bwd_bytes": int(ws_b.numel()),
+                    "materialized_W_fp32_bytes": 4 * E * info["n_weights"],
+                    "peak_alloc_bytes": int(torch.cuda.max_memory_allocated() - base),
+                    "scratch_budget_mib": args.scratch_mib or 256, "steps": steps}
+            print(json.dumps(line), flush=True)
+            del graph, conv, ws_f, ws_b, out, grads, x, A, gout, pos, shift, phi
     return 0
 
 

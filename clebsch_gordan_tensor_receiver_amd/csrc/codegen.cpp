@@ -404,6 +404,7 @@ void emit_recv_edge_loop2(Out& o, const Plan& p, const std::vector<int>& blocks,
 // Combine per-wave partial sums acc<m> (m < n) of the waves of a workgroup through LDS in a fixed
 // order; afterwards wave 0 holds the total.  `sm` must hold (nw - 1) * n * 64 values.
 void emit_wave_combine(Out& o, const std::string& prefix, int n, int nw) {
+  if (nw == 1) return;
   o.open("if (w != 0)");
   for (int m = 0; m < n; ++m) o.line(F("sm[((w - 1) * %d + %d) * 64 + lane] = %s%d;", n, m, prefix.c_str(), m));
   o.close();
@@ -417,6 +418,7 @@ void emit_wave_combine(Out& o, const std::string& prefix, int n, int nw) {
 
 // emit_wave_combine over an explicit list of accumulator names.
 void emit_wave_combine_names(Out& o, const std::vector<std::string>& names, int nw) {
+  if (nw == 1) return;
   const int n = int(names.size());
   o.open("if (w != 0)");
   for (int m = 0; m < n; ++m) o.line(F("sm[((w - 1) * %d + %d) * 64 + lane] = %s;", n, m, names[m].c_str()));
@@ -534,7 +536,7 @@ int max_in_dim(const Plan& p) {
 // cost order inside it (LunaTP section 4.2, task ordering).
 // Switch of a grouped dispatch: wave set `cb` of group `t` runs task tasks[t][cb]; the waves of
 // a missing channel block only take part in the one workgroup barrier every task function has.
-void emit_group_switch(Out& o, const TaskGroups& tg, const std::string& call_fmt) {
+void emit_group_switch(Out& o, const TaskGroups& tg, const std::string& call_fmt, bool barrier) {
   o.open(F("switch (t * %d + cb)", tg.ncb));
   for (int t = 0; t < int(tg.tasks.size()); ++t)
     for (int c = 0; c < int(tg.tasks[t].size()); ++c) {
@@ -542,7 +544,7 @@ void emit_group_switch(Out& o, const TaskGroups& tg, const std::string& call_fmt
       for (size_t at; (at = call.find("%T")) != std::string::npos;) call.replace(at, 2, std::to_string(tg.tasks[t][c]));
       o.line(F("case %d: ", t * tg.ncb + c) + call + " break;");
     }
-  o.line("default: __syncthreads(); break;");
+  o.line(barrier ? "default: __syncthreads(); break;" : "default: break;");
   o.close();
 }
 
@@ -560,7 +562,7 @@ void emit_node_dispatch(Out& o, const Plan& p, const std::string& kname, const s
   o.line("const int node = i0 + i;");
   o.line(F("const int cb = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) / %d;", fwd_split(p)));
   o.line(F("real* const smc = sm + cb * %d;", slice));
-  emit_group_switch(o, tg, call + "%T(x, phi, A, G, row_ptr, col, out, smc, node, e_base);");
+  emit_group_switch(o, tg, call + "%T(x, phi, A, G, row_ptr, col, out, smc, node, e_base);", fwd_split(p) > 1);
   o.close();
 }
 
@@ -922,7 +924,8 @@ void emit_src_dispatch(Out& o, const Plan& p, int ntask) {
   o.line("if (node >= nrec) return;");
   o.line(F("const int cb = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) / %d;", kSrcSplit));
   o.line(F("real* const smc = sm + cb * %d;", slice));
-  emit_group_switch(o, tg, "bws_t%T(phi, A, G, gout, recv, src_ptr, src_edge, gx, smc, node, e_base, accumulate);");
+  emit_group_switch(o, tg, "bws_t%T(phi, A, G, gout, recv, src_ptr, src_edge, gx, smc, node, e_base, accumulate);",
+                    kSrcSplit > 1);
   o.close();
 }
 

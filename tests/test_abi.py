@@ -195,3 +195,14 @@ def test_workspace_is_bounded_by_the_scratch_budget(lib):
     for sm in small:
         assert sm <= (1 << 20) + 4 * (nslot * K * nw + 3 * E) + 1024
         assert sm < E * nw * 4
+
+
+def test_sweep_profile_weight_counts(lib):
+    # Sobek, section 5.1 ("Representative irrep profiles"): the fully connected profiles 128/64,
+    # 128/64/64 and 128/64/64/64 have N_w = 36,864, 73,728 and 131,072 radial weights.
+    from workloads import sweeps
+    want = {1: 36864, 2: 73728, 3: 131072}
+    for L, s in sweeps.PROFILES.items():
+        info = lib.Plan(s["irreps_in"], s["irreps_sh"], s["irreps_out"], s["mode"], s["dtype"], s["K"]).info
+        assert info["n_weights"] == want[L], L
+        assert info["n_weights"] == make_problem(s["irreps_in"], s["irreps_sh"], s["irreps_out"], s["mode"]).n_weights

@@ -1,0 +1,121 @@
+"""Scaling sweeps shaped like the Sobek page's section 5.1 ("Scaling axes", "Representative irrep
+profiles"): inputs only, no convolution arithmetic.
+
+* Degree axis: one set of 2,048 uniform positions (periodic box at 0.1 atoms/A^3, Morton order);
+  the cutoff is chosen per point so that the expected receiver degree is 4 ... 1,023.
+* Graph-count axis: one 128-node graph of expected degree 32 (same density), repeated B = 2 ... 511
+  times as disjoint copies (node indices offset by 128 per copy).
+
+Both axes span about 8.2e3 to 2.1e6 directed edges.  The irrep profiles hold 128 scalar channels
+and 64 channels per non-scalar order, inputs equal to outputs with alternating parity, one SH copy
+per order up to L_max, fully connected paths and K = 16 radial functions (Gaussian basis), fp32.
+
+Seeds: PCG64(1000 * SWEEP_SEED + stream) with stream 0 positions, 1 node features, 2 radial
+matrix A, 3 output cotangent, 8 edge-order shuffle; the repeated graph draws its positions from
+stream 10.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+from .graphs import _morton_order, gaussian_basis, neighbour_list
+
+SWEEP_SEED = 61
+DENSITY = 0.1                     # atoms per cubic Angstrom
+K = 16
+DEGREES = (4, 8, 16, 32, 64, 128, 256, 512, 1023)
+COPIES = (2, 4, 8, 16, 32, 64, 128, 256, 511)
+
+
+def _alt(lmax: int, scalar_mul: int = 128, mul: int = 64) -> str:
+    parts = [f"{scalar_mul}x0e"] + [f"{mul}x{l}{'e' if l % 2 == 0 else 'o'}" for l in range(1, lmax + 1)]
+    return "+".join(parts)
+
+
+def _sh(lmax: int) -> str:
+    return "+".join(f"1x{l}{'e' if l % 2 == 0 else 'o'}" for l in range(lmax + 1))
+
+
+# L_max -> irreps of the "128/64", "128/64/64" and "128/64/64/64" profiles.
+PROFILES = {L: dict(irreps_in=_alt(L), irreps_sh=_sh(L), irreps_out=_alt(L), mode="uvw", dtype="float32", K=K)
+            for L in (1, 2, 3)}
+
+
+@dataclasses.dataclass
+class SweepGraph:
+    axis: str                # "degree" or "copies"
+    point: int               # target degree or copy count
+    n_nodes: int
+    recv: np.ndarray         # (E,) int32, seeded random order
+    send: np.ndarray
+    image: np.ndarray        # (E, 3) int32
+    shift: np.ndarray        # (E, 3) float64
+    pos: np.ndarray          # (N, 3) float64
+    box: np.ndarray
+    rc: float
+    phi: np.ndarray          # (E, K) float64
+
+    @property
+    def n_edges(self) -> int:
+        return int(self.recv.shape[0])
+
+    @property
+    def mean_degree(self) -> float:
+        return self.n_edges / self.n_nodes
+
+
+def _rng(stream: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(1000 * SWEEP_SEED + stream))
+
+
+def _cutoff(degree: float) -> float:
+    """Radius whose sphere holds `degree` atoms on average at DENSITY."""
+    return (3.0 * degree / (4.0 * math.pi * DENSITY)) ** (1.0 / 3.0)
+
+
+def _uniform(n: int, stream: int):
+    box = np.full(3, (n / DENSITY) ** (1.0 / 3.0))
+    pos = _rng(stream).uniform(0.0, 1.0, size=(n, 3)) * box
+    return pos[_morton_order(pos, box, _cutoff(32.0))], box
+
+
+def _finish(axis, point, pos, box, rc, recv, send, image) -> SweepGraph:
+    perm = _rng(8).permutation(len(recv))
+    recv, send, image = recv[perm], send[perm], image[perm]
+    shift = image.astype(np.float64) * box[None, :]
+    r = np.linalg.norm(pos[send] - pos[recv] + shift, axis=1)
+    return SweepGraph(axis, point, len(pos), recv, send, image, shift, pos, box, rc, gaussian_basis(r, rc, K))
+
+
+def degree_graph(degree: int) -> SweepGraph:
+    """Radius graph on 2,048 fixed positions with the cutoff of expected degree `degree`."""
+    pos, box = _uniform(2048, 0)
+    rc = _cutoff(degree)
+    recv, send, image = neighbour_list(pos, box, rc)
+    return _finish("degree", degree, pos, box, rc, recv, send, image)
+
+
+def copies_graph(copies: int) -> SweepGraph:
+    """`copies` disjoint copies of one 128-node graph of expected degree 32."""
+    pos1, box = _uniform(128, 10)
+    rc = _cutoff(32.0)
+    r1, s1, i1 = neighbour_list(pos1, box, rc)
+    off = (np.arange(copies, dtype=np.int64) * 128)[:, None]
+    recv = (r1[None, :] + off).reshape(-1).astype(np.int32)
+    send = (s1[None, :] + off).reshape(-1).astype(np.int32)
+    image = np.tile(i1, (copies, 1))
+    pos = np.tile(pos1, (copies, 1))  # copies share coordinates; they never exchange edges
+    return _finish("copies", copies, pos, box, rc, recv, send, image)
+
+
+def sweep_graph(axis: str, point: int) -> SweepGraph:
+    return degree_graph(point) if axis == "degree" else copies_graph(point)
+
+
+def normal(stream: int, shape, std: float = 1.0) -> np.ndarray:
+    """N(0, std^2) draws rounded to float32 (kept as float64)."""
+    return _rng(stream).normal(0.0, std, size=shape).astype(np.float32).astype(np.float64)
