@@ -195,6 +195,8 @@ def main() -> int:
                     help="scaling axis of the fully connected profiles (one JSON line per point)")
     ap.add_argument("--profile", type=int, default=0, choices=(0, 1, 2, 3),
                     help="irrep profile (L_max) of the sweep; 0: all three")
+    ap.add_argument("--points", default="",
+                    help="comma-separated sweep points (degrees or copy counts); default: the whole axis")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -355,6 +357,8 @@ def sweep(torch, cg, args) -> int:
     from workloads import sweeps
 
     points = sweeps.DEGREES if args.sweep == "degree" else sweeps.COPIES
+    if args.points:
+        points = [int(v) for v in args.points.split(",")]
     profiles = [args.profile] if args.profile else sorted(sweeps.PROFILES)
     steps, warmup = max(1, min(args.steps, 5)), max(1, min(args.warmup, 2))
     for L in profiles:
@@ -406,6 +410,13 @@ def sweep(torch, cg, args) -> int:
                     fn()
                 torch.cuda.synchronize()
                 times[name] = (time.perf_counter() - t0) / steps
+            kernels = {}
+            if args.profile_steps > 0:
+                cg._lib.profile_begin()
+                fwd()
+                bwd()
+                torch.cuda.synchronize()
+                kernels = {k: round(1e3 * ms, 1) for k, (n, ms) in cg._lib.profile_end().items()}
             line = {"sweep": args.sweep, "point": pt, "profile": f"L{L} " + s["irreps_in"], "n_weights": info["n_weights"],
                     "n_nodes": N, "n_edges": E, "mean_degree": round(E / N, 2), "cutoff_A": round(g.rc, 3),
                     "fwd_ms": round(1e3 * times["fwd"], 3), "bwd_ms": round(1e3 * times["bwd"], 3),
@@ -413,7 +424,7 @@ def sweep(torch, cg, args) -> int:
                     "workspace_fwd_bytes": int(ws_f.numel()), "workspace_bwd_bytes": int(ws_b.numel()),
                     "materialized_W_fp32_bytes": 4 * E * info["n_weights"],
                     "peak_alloc_bytes": int(torch.cuda.max_memory_allocated() - base),
-                    "scratch_budget_mib": args.scratch_mib or 256, "steps": steps}
+                    "scratch_budget_mib": args.scratch_mib or 256, "steps": steps, "kernel_us": kernels}
             print(json.dumps(line), flush=True)
             del graph, conv, ws_f, ws_b, out, grads, x, A, gout, pos, shift, phi
     return 0

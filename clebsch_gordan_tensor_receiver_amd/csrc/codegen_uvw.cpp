@@ -264,15 +264,19 @@ void emit_state_task(Out& o, const Plan& p, const std::vector<Side>& sides, int 
   const int K = p.K, d3 = S.d;
   std::vector<int> paths;
   for (int k : T.idx) paths.push_back(S.paths[k]);
-  o.open(F("DEV void uvs_t%d(%s, int node, int il, int e_base)", ti, kStateArgs));
+  o.open(F("DEV void uvs_t%d(%s, int node, int il, int e_base, int w, int nst, real* sm)", ti, kStateArgs));
   o.line("const int lane = (int)threadIdx.x & 63;");
   o.line(F("const int u = %d + lane;", T.cb * 64));
   for (int b : in_blocks_of(p, paths)) o.line(F("const int uc%d = u < %d ? u : %d;", b, p.in[b].mul, p.in[b].mul - 1));
+  std::vector<std::string> acc;
   for (int pi : paths)
     for (int q = 0; q < K; ++q)
-      for (int m = 0; m < d3; ++m) o.line(F("real s%d_%d_%d = R(0);", pi, q, m));
+      for (int m = 0; m < d3; ++m) {
+        acc.push_back(F("s%d_%d_%d", pi, q, m));
+        o.line("real " + acc.back() + " = R(0);");
+      }
   o.line("const int e0 = row_ptr[node], e1 = row_ptr[node + 1];");
-  emit_recv_edge_loop(o, p, in_blocks_of(p, paths), "0", "1", [&] {
+  emit_recv_edge_loop(o, p, in_blocks_of(p, paths), "w", "nst", [&] {
     for (int pi : paths) {
       const Path& P = p.paths[pi];
       std::vector<bool> started(d3, false);
@@ -289,6 +293,21 @@ void emit_state_task(Out& o, const Plan& p, const std::vector<Side>& sides, int 
           if (started[m]) o.line(F("s%d_%d_%d = fma(f%d, t%d_%d, s%d_%d_%d);", pi, q, m, q, pi, m, pi, q, m));
     }
   }, true);
+  // The nst waves of the workgroup took every nst-th edge: partial states summed in LDS in a fixed
+  // order (wave 0 first, then 1, ...).
+  const int n = int(acc.size());
+  o.open("if (nst > 1)");
+  o.open("if (w != 0)");
+  for (int m = 0; m < n; ++m) o.line(F("sm[((w - 1) * %d + %d) * 64 + lane] = %s;", n, m, acc[m].c_str()));
+  o.close();
+  o.line("__syncthreads();");
+  o.open("if (w == 0)");
+  o.open("for (int k = 1; k < nst; ++k)");
+  for (int m = 0; m < n; ++m) o.line(F("%s += sm[((k - 1) * %d + %d) * 64 + lane];", acc[m].c_str(), n, m));
+  o.close();
+  o.close();
+  o.close();
+  o.line("if (w != 0) return;");
   for (size_t kk = 0; kk < T.idx.size(); ++kk) {
     const int k = T.idx[kk], pi = S.paths[k], mul = S.cmul[k];
     o.open(F("if (u < %d)", mul));
@@ -301,15 +320,20 @@ void emit_state_task(Out& o, const Plan& p, const std::vector<Side>& sides, int 
 }
 
 // One wave per (task, receiver); XCD-contiguous receiver ranges as in the channelwise forward.
+// nst waves per workgroup split the receiver's edge list (nst = blockDim.x / 64, at most
+// kMaxStripes); their partial states meet in dynamic LDS of (nst - 1) x state_acc x 64 values.
 void emit_state_dispatch(Out& o, int ntask) {
-  o.line("extern \"C\" __global__ void __launch_bounds__(64)");
+  o.line(F("extern \"C\" __global__ void __launch_bounds__(%d)", 64 * kMaxStripes));
   o.open(std::string("cgtp_uvw_state(") + kStateArgs + ", int i0, int nrec, int per, int e_base)");
+  o.line("extern __shared__ real sm[];");
   o.line("const int b = (int)blockIdx.x;");
   o.line("const int xcd = b & 7, s = b >> 3;");
   o.line("const int t = s / per, il = xcd * per + (s - t * per);");
   o.line("if (il >= nrec) return;");
+  o.line("const int nst = (int)blockDim.x >> 6, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
   o.open("switch (t)");
-  for (int k = 0; k < ntask; ++k) o.line(F("case %d: uvs_t%d(x, phi, G, row_ptr, col, S, i0 + il, il, e_base); break;", k, k));
+  for (int k = 0; k < ntask; ++k)
+    o.line(F("case %d: uvs_t%d(x, phi, G, row_ptr, col, S, i0 + il, il, e_base, w, nst, sm); break;", k, k));
   o.line("default: break;");
   o.close();
   o.close();
@@ -329,7 +353,10 @@ void emit_edge_task(Out& o, const Plan& p, const std::vector<Side>& sides, int t
   const int K = p.K, d3 = S.d;
   std::vector<int> paths;
   for (int k : T.idx) paths.push_back(S.paths[k]);
-  o.open(F("DEV void uve_t%d(%s, int node, int il, int e_base, int eps)", ti, kEdgeArgs));
+  // NST = 1: one wave per receiver (constant stride, the common case); NST = 0: stride nst.
+  o.line("template <int NST>");
+  o.open(F("DEV void uve_t%d(%s, int node, int il, int e_base, int eps, int stripe, int nst)", ti, kEdgeArgs));
+  o.line("const int st_ = NST == 1 ? 0 : stripe, ns_ = NST == 1 ? 1 : nst;");
   o.line("const int lane = (int)threadIdx.x & 63;");
   o.line(F("const int u = %d + lane;", T.cb * 64));
   for (int b : in_blocks_of(p, paths)) o.line(F("const int uc%d = u < %d ? u : %d;", b, p.in[b].mul, p.in[b].mul - 1));
@@ -342,7 +369,7 @@ void emit_edge_task(Out& o, const Plan& p, const std::vector<Side>& sides, int t
         o.line(F("const real sb%d_%d_%d = u < %d ? sr%d[%d] : R(0);", pi, q, m, mul, pi, m * S.ld + q * mul));
   }
   o.line("const int e0 = row_ptr[node], e1 = row_ptr[node + 1];");
-  emit_recv_edge_loop(o, p, in_blocks_of(p, paths), "0", "1", [&] {
+  emit_recv_edge_loop(o, p, in_blocks_of(p, paths), "st_", "ns_", [&] {
     for (int v = 0; v < V; ++v) o.line(F("real v%d = R(0);", v));
     for (int pi : paths) {
       const Path& P = p.paths[pi];
@@ -391,19 +418,28 @@ void emit_edge_task(Out& o, const Plan& p, const std::vector<Side>& sides, int t
   o.close();
 }
 
+// One wave per (task, receiver, stripe): the nst stripes of a receiver take every nst-th edge
+// (per-edge outputs, nothing to combine).
 void emit_edge_dispatch(Out& o, int ntask) {
-  o.line("extern \"C\" __global__ void __launch_bounds__(64)");
-  o.open(std::string("cgtp_uvw_edge(") + kEdgeArgs + ", int i0, int nrec, int per, int e_base, int eps)");
-  o.line("const int b = (int)blockIdx.x;");
-  o.line("const int xcd = b & 7, s = b >> 3;");
-  o.line("const int t = s / per, il = xcd * per + (s - t * per);");
-  o.line("if (il >= nrec) return;");
-  o.open("switch (t)");
-  for (int k = 0; k < ntask; ++k)
-    o.line(F("case %d: uve_t%d(x, phi, G, row_ptr, col, Sb, ep, i0 + il, il, e_base, eps); break;", k, k));
-  o.line("default: break;");
-  o.close();
-  o.close();
+  // cgtp_uvw_edge: one wave per (task, receiver); cgtp_uvw_edge_striped: nst waves per receiver
+  // (separate kernels so that each gets its own register allocation).
+  for (int striped = 0; striped < 2; ++striped) {
+    o.line("extern \"C\" __global__ void __launch_bounds__(64)");
+    o.open(std::string(striped ? "cgtp_uvw_edge_striped(" : "cgtp_uvw_edge(") + kEdgeArgs +
+           ", int i0, int nrec, int per, int e_base, int eps, int nst)");
+    o.line("const int b = (int)blockIdx.x;");
+    o.line("const int xcd = b & 7, s = b >> 3;");
+    o.line("const int t = s / (per * nst), r = s - t * per * nst;");
+    o.line("const int il = xcd * per + r / nst, stripe = r - (r / nst) * nst;");
+    o.line("if (il >= nrec) return;");
+    o.open("switch (t)");
+    for (int k = 0; k < ntask; ++k)
+      o.line(F("case %d: uve_t%d<%d>(x, phi, G, row_ptr, col, Sb, ep, i0 + il, il, e_base, eps, stripe, nst); break;",
+               k, k, striped ? 0 : 1));
+    o.line("default: break;");
+    o.close();
+    o.close();
+  }
 }
 
 const char* kZArgs =
@@ -546,7 +582,9 @@ UvwLayout uvw_layout(const Plan& p) {
   for (auto& s : ss) L.send.push_back({s.blk, s.d, s.mul, s.D, s.ld});
   side_offsets(rs, &L.recv_stride);
   side_offsets(ss, &L.send_stride);
-  L.n_state_tasks = int(state_tasks(p, rs, recv_state_cost).size());
+  const auto st = state_tasks(p, rs, recv_state_cost);
+  L.n_state_tasks = int(st.size());
+  for (const StateTask& t : st) L.state_acc = std::max(L.state_acc, int(t.idx.size()) * p.K * rs[t.side].d);
   L.n_z_tasks = int(state_tasks(p, ss, send_state_cost).size());
   return L;
 }

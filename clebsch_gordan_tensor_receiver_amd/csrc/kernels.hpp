@@ -89,9 +89,12 @@ struct UvwSideInfo {
 struct UvwLayout {
   std::vector<UvwSideInfo> recv, send;
   int n_state_tasks = 0, n_z_tasks = 0;
+  int state_acc = 1;  // largest number of state accumulators of a receiver-state task (per lane)
   long long recv_stride = 0, send_stride = 0;
 };
 UvwLayout uvw_layout(const Plan& p);
+// Waves splitting one receiver's edge list in the fully connected state and edge kernels.
+constexpr int kMaxStripes = 4;
 
 // Compile (once) and fetch a kernel of a family on the current device.
 cgtp_status_t get_kernel(Plan& p, const std::string& family, const std::string& name, hipFunction_t* f,

@@ -55,6 +55,16 @@ size_t max_side_cols(const std::vector<UvwSideInfo>& sides) {
   return m;
 }
 
+// Waves per receiver for the state and edge kernels of a chunk: doubled (up to kMaxStripes) while
+// the chunk's (receiver, task) waves would not give every SIMD four; for the state kernel the
+// partial states of the extra waves must fit 64 KiB of LDS.
+int stripes(int nrec, int ntask, size_t lds_per_extra_wave) {
+  const long long waves = 8LL * ((nrec + 7) / 8) * ntask;
+  int n = 1;
+  while (n < kMaxStripes && waves * n < 4096 && size_t(2 * n - 1) * lds_per_extra_wave <= (64u << 10)) n *= 2;
+  return n;
+}
+
 struct UvwPlanB {
   UvwLayout L;
   std::vector<std::pair<int, int>> rchunks, schunks;
@@ -181,8 +191,12 @@ cgtp_status_t uvw_forward(Plan& p, Graph& G, const DeviceGraph& d, const void* x
       if ((st = launch(kprep, cdiv(e1 - e0, 64), 64, 0, s, a, err)) != CGTP_OK) return st;
     }
     int per = (nrec + 7) / 8;
+    const size_t lds_w = size_t(F.L.state_acc) * 64 * p.elem();
+    const int nst = stripes(nrec, F.L.n_state_tasks, lds_w);
     void* b[] = {(void*)&x, (void*)&phi, &Gb, (void*)&d.row_ptr, (void*)&d.col, &S, &i0, &nrec, &per, &e0};
-    if ((st = launch(kstate, unsigned(8 * F.L.n_state_tasks * per), 64, 0, s, b, err)) != CGTP_OK) return st;
+    if ((st = launch(kstate, unsigned(8 * F.L.n_state_tasks * per), 64 * nst, unsigned((nst - 1) * lds_w), s, b,
+                     err)) != CGTP_OK)
+      return st;
     for (size_t gi = 0; gi < F.L.recv.size(); ++gi) {
       const auto& side = F.L.recv[gi];
       int M = nrec * side.d, Kd = side.D, kper = 0;
@@ -206,11 +220,12 @@ cgtp_status_t uvw_backward(Plan& p, Graph& G, const DeviceGraph& d, const Source
   UvwPlanB B = layout_bwd(p, G);
   cgtp_status_t st;
   const char* fam = "uvw_bwd";
-  hipFunction_t kzero, kprep, kstate, kedge, kfinal, kpos, kprep_src, kz;
+  hipFunction_t kzero, kprep, kstate, kedge, kedge_s, kfinal, kpos, kprep_src, kz;
   if ((st = get_kernel(p, fam, "cgtp_fill_zero", &kzero, err)) != CGTP_OK ||
       (st = get_kernel(p, fam, "cgtp_prep", &kprep, err)) != CGTP_OK ||
       (st = get_kernel(p, fam, "cgtp_uvw_state", &kstate, err)) != CGTP_OK ||
       (st = get_kernel(p, fam, "cgtp_uvw_edge", &kedge, err)) != CGTP_OK ||
+      (st = get_kernel(p, fam, "cgtp_uvw_edge_striped", &kedge_s, err)) != CGTP_OK ||
       (st = get_kernel(p, fam, "cgtp_edge_final", &kfinal, err)) != CGTP_OK ||
       (st = get_kernel(p, fam, "cgtp_pos_grad", &kpos, err)) != CGTP_OK ||
       (st = get_kernel(p, fam, "cgtp_prep_src", &kprep_src, err)) != CGTP_OK ||
@@ -262,8 +277,12 @@ cgtp_status_t uvw_backward(Plan& p, Graph& G, const DeviceGraph& d, const Source
         if ((st = launch(kprep, cdiv(e1 - e0, 64), 64, 0, s, a, err)) != CGTP_OK) return st;
       }
       if (grad_A) {
+        const size_t lds_w = size_t(B.L.state_acc) * 64 * p.elem();
+        const int nst = stripes(nrec, B.L.n_state_tasks, lds_w);
         void* b[] = {(void*)&x, (void*)&phi, &Gb, (void*)&d.row_ptr, (void*)&d.col, &S, &i0, &nrec, &per, &e0};
-        if ((st = launch(kstate, unsigned(8 * B.L.n_state_tasks * per), 64, 0, s, b, err)) != CGTP_OK) return st;
+        if ((st = launch(kstate, unsigned(8 * B.L.n_state_tasks * per), 64 * nst, unsigned((nst - 1) * lds_w), s, b,
+                         err)) != CGTP_OK)
+          return st;
       }
       for (size_t gi = 0; gi < B.L.recv.size(); ++gi) {
         const auto& side = B.L.recv[gi];
@@ -284,9 +303,12 @@ cgtp_status_t uvw_backward(Plan& p, Graph& G, const DeviceGraph& d, const Source
         }
       }
       if (need_edge && e1 > e0) {
+        int nst = stripes(nrec, B.L.n_state_tasks, 0);
         void* a[] = {(void*)&x, (void*)&phi, &Gb, (void*)&d.row_ptr, (void*)&d.col, &Sb, &ep, &i0, &nrec, &per, &e0,
-                     &eps};
-        if ((st = launch(kedge, unsigned(8 * B.L.n_state_tasks * per), 64, 0, s, a, err)) != CGTP_OK) return st;
+                     &eps, &nst};
+        if ((st = launch(nst == 1 ? kedge : kedge_s, unsigned(8 * B.L.n_state_tasks * per * nst), 64, 0, s, a, err)) !=
+            CGTP_OK)
+          return st;
         void* b[] = {(void*)&pos, (void*)&shift, (void*)&d.recv, (void*)&d.col, &ep, &e0, &e1, &eps, &grad_phi,
                      &gev_arg};
         if ((st = launch(kfinal, cdiv(e1 - e0, 256), 256, 0, s, b, err)) != CGTP_OK) return st;
