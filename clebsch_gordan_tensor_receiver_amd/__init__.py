@@ -8,4 +8,5 @@ package holds its build step (``build``) and the ctypes binding (``_lib``).
 from . import _lib  # noqa: F401
 from ._lib import (CONVENTIONAL, STREAMED, OP_BACKWARD, OP_DOUBLE_BACKWARD, OP_FORWARD,  # noqa: F401
                    CgtpError, Convolution, Graph, Plan, check_edges, conv_backward, conv_double_backward, conv_forward,
+                   layout_convert,
                    workspace_size)

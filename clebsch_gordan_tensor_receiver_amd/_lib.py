@@ -26,7 +26,7 @@ EXPORTED = [
     "cgtp_plan_create", "cgtp_plan_destroy", "cgtp_plan_info", "cgtp_plan_path", "cgtp_plan_cg_table",
     "cgtp_plan_compile", "cgtp_plan_set_scratch_budget", "cgtp_graph_build", "cgtp_graph_export",
     "cgtp_graph_dims", "cgtp_graph_upload", "cgtp_graph_destroy", "cgtp_workspace_size",
-    "cgtp_conv_forward", "cgtp_conv_backward", "cgtp_conv_double_backward", "cgtp_check_edges", "cgtp_error_string", "cgtp_last_error",
+    "cgtp_conv_forward", "cgtp_conv_backward", "cgtp_conv_double_backward", "cgtp_check_edges", "cgtp_layout_convert", "cgtp_error_string", "cgtp_last_error",
     "cgtp_profile_begin", "cgtp_profile_end", "cgtp_profile_count", "cgtp_profile_get",
 ]
 
@@ -73,6 +73,7 @@ def load() -> ctypes.CDLL:
         "cgtp_conv_backward": [P, P, V, V, V, V, V, V, V, V, V, V, V, V, Z, V],
         "cgtp_conv_double_backward": [P, P] + [V] * 18 + [Z, V],
         "cgtp_check_edges": [P, P, V, V, V, Z, V, ctypes.POINTER(ctypes.c_int)],
+        "cgtp_layout_convert": [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, V, V, V],
         "cgtp_profile_begin": [],
         "cgtp_profile_end": [],
         "cgtp_profile_count": [],
@@ -250,6 +251,13 @@ def conv_double_backward(plan: Plan, graph: Graph, x, pos, shift, phi, A, grad_o
         _ptr(v_x), _ptr(v_pos), _ptr(v_edge_vec), _ptr(v_phi), _ptr(v_A), _ptr(gg_x), _ptr(gg_pos),
         _ptr(gg_edge_vec), _ptr(gg_phi), _ptr(gg_A), _ptr(gg_grad_out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def layout_convert(plan: Plan, side: int, direction: int, src, dst, stream=None) -> None:
+    """Feature layout conversion: side 0 input / 1 output features, direction 0 mul_ir -> ir_mul,
+    1 ir_mul -> mul_ir; src and dst are device tensors of shape (N, width)."""
+    check(load().cgtp_layout_convert(plan.handle, side, direction, int(src.shape[0]), _ptr(src), _ptr(dst),
+                                      _stream(stream)))
 
 
 def check_edges(plan: Plan, graph: Graph, pos, shift, workspace, stream=None) -> int:

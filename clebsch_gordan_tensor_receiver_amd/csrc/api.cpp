@@ -257,6 +257,7 @@ cgtp_status_t cgtp_plan_compile(cgtp_plan_t plan, int ops) {
     if (ops & (1 << CGTP_OP_FORWARD)) fams.push_back("uvw_fwd");
     if (ops & (1 << CGTP_OP_BACKWARD)) fams.push_back("uvw_bwd");
   }
+  if (ops & (1 << CGTP_OP_FORWARD)) fams.push_back("layout");  // boundary layout conversion
   for (auto& f : fams) {
     cgtp_status_t st = cgtp::compile_family(plan->p, f, &err);
     if (st != CGTP_OK) return fail(st, err);
@@ -644,6 +645,27 @@ cgtp_status_t cgtp_check_edges(cgtp_plan_t plan, cgtp_graph_t g, const void* pos
   if (m == 0x7fffffff) return ok();
   *first_bad = m;
   return fail(CGTP_ERR_DEGENERATE_EDGE, "edge " + std::to_string(m) + " (receiver-sorted) has zero length");
+}
+
+cgtp_status_t cgtp_layout_convert(cgtp_plan_t plan, int side, int direction, int n_nodes, const void* src, void* dst,
+                                  void* stream) {
+  if (!plan) return fail(CGTP_ERR_INVALID_ARG, "null plan");
+  if (side != 0 && side != 1) return fail(CGTP_ERR_INVALID_ARG, "side must be 0 (input) or 1 (output)");
+  if (direction != 0 && direction != 1) return fail(CGTP_ERR_INVALID_ARG, "direction must be 0 or 1");
+  if (n_nodes < 0) return fail(CGTP_ERR_INVALID_ARG, "negative node count");
+  if (n_nodes == 0) return ok();
+  if (!src || !dst) return fail(CGTP_ERR_INVALID_ARG, "null tensor argument");
+  if (src == dst) return fail(CGTP_ERR_INVALID_ARG, "src and dst must not overlap");
+  cgtp::Plan& p = plan->p;
+  std::string err;
+  hipFunction_t k;
+  cgtp_status_t st = cgtp::get_kernel(p, "layout", side == 0 ? "cgtp_layout_in" : "cgtp_layout_out", &k, &err);
+  if (st != CGTP_OK) return fail(st, err);
+  long long total = (long long)n_nodes * (side == 0 ? p.c_in : p.c_out);
+  int to_mul_ir = direction;
+  void* a[] = {(void*)&src, &dst, &total, &to_mul_ir};
+  st = cgtp::launch(k, unsigned((total + 255) / 256), 256, 0, static_cast<hipStream_t>(stream), a, &err);
+  return st == CGTP_OK ? ok() : fail(st, err);
 }
 
 }  // extern "C"

@@ -1232,8 +1232,36 @@ const std::vector<Task>& source_tasks(const Plan& p) { return task_tables(p).src
 
 int edge_partial_width(const Plan& p) { return (p.K + p.sh_dim + 3) / 4 * 4; }
 
+// Feature layout conversion of one side (in / out) between ir_mul (block offset + m C + u) and
+// mul_ir (block offset + u (2l+1) + m); one thread per element, reads or writes coalesced on the
+// ir_mul side.
+void emit_layout_kernel(Out& o, const std::vector<Block>& blocks, int width, const char* name) {
+  o.line("extern \"C\" __global__ void __launch_bounds__(256)");
+  o.open(std::string(name) + "(const real* __restrict__ src, real* __restrict__ dst, i64 total, int to_mul_ir)");
+  o.line("const i64 k = (i64)blockIdx.x * 256 + threadIdx.x;");
+  o.line("if (k >= total) return;");
+  o.line(F("const i64 n = k / %d;", width));
+  o.line(F("const int c = (int)(k - n * %d);", width));
+  o.line("int off, mul, dim;");
+  for (size_t b = 0; b < blocks.size(); ++b) {
+    const Block& B = blocks[b];
+    const std::string cond = b + 1 < blocks.size() ? F("if (c < %d) ", B.offset + B.size()) : std::string("");
+    o.line((b ? "else " : "") + cond + F("{ off = %d; mul = %d; dim = %d; }", B.offset, B.mul, B.dim()));
+  }
+  o.line("const int r = c - off, m = r / mul, u = r - m * mul;");
+  o.line(F("const i64 a = n * %d + c, t = n * %d + off + u * dim + m;", width, width));
+  o.line("if (to_mul_ir) dst[t] = src[a]; else dst[a] = src[t];");
+  o.close();
+}
+
 std::string generate_source(const Plan& p, const std::string& family, std::string* err) {
   Out o;
+  if (family == "layout") {
+    prelude(o, p, false, false);
+    emit_layout_kernel(o, p.in, p.c_in, "cgtp_layout_in");
+    emit_layout_kernel(o, p.out, p.c_out, "cgtp_layout_out");
+    return o.s.str();
+  }
   if (p.mode != CGTP_CHANNELWISE) return generate_uvw_source(p, family, err);
   if (family == "fwd" || family == "fwds") {
     prelude(o, p, false, false);

@@ -193,6 +193,20 @@ cgtp_status_t cgtp_conv_double_backward(cgtp_plan_t plan, cgtp_graph_t g, const 
 cgtp_status_t cgtp_check_edges(cgtp_plan_t plan, cgtp_graph_t g, const void* pos, const void* shift,
                                void* workspace, size_t ws_bytes, void* stream, int* first_bad);
 
+/* Feature layout conversion at the boundary.  The convolution entry points take node features
+ * in the ir_mul layout (Sobek section 4.4: within an irrep block of multiplicity C and dimension
+ * 2l+1 the component index m is the slower one, element offset + m C + u); libraries that store
+ * mul_ir (offset + u (2l+1) + m, channel index slower) convert with this call.
+ *   side       0: input features (N x C_in, the layout of x and grad_x); 1: output features
+ *              (N x C_out, the layout of the output and of grad_out)
+ *   direction  0: mul_ir -> ir_mul; 1: ir_mul -> mul_ir
+ *   src, dst   device pointers of n_nodes rows in the plan's dtype; caller-owned; must not
+ *              overlap (INVALID_ARG when src == dst)
+ * Asynchronous on `stream`; a pure permutation of the elements (bit-exact).  INVALID_ARG for a
+ * null plan or tensor, a side or direction other than 0/1, or n_nodes < 0. */
+cgtp_status_t cgtp_layout_convert(cgtp_plan_t plan, int side, int direction, int n_nodes, const void* src, void* dst,
+                                  void* stream);
+
 /* ---------------------------------------------------------------- launch timing */
 
 /* Start timing kernel launches: from now on every kernel the library launches (any plan, any
