@@ -24,7 +24,7 @@ OP_FORWARD, OP_BACKWARD, OP_DOUBLE_BACKWARD = 0, 1, 2
 
 EXPORTED = [
     "cgtp_plan_create", "cgtp_plan_destroy", "cgtp_plan_info", "cgtp_plan_path", "cgtp_plan_cg_table",
-    "cgtp_plan_compile", "cgtp_plan_set_scratch_budget", "cgtp_graph_build", "cgtp_graph_export",
+    "cgtp_plan_compile", "cgtp_plan_set_scratch_budget", "cgtp_plan_set_radial", "cgtp_graph_build", "cgtp_graph_export",
     "cgtp_graph_dims", "cgtp_graph_upload", "cgtp_graph_destroy", "cgtp_workspace_size",
     "cgtp_conv_forward", "cgtp_conv_backward", "cgtp_conv_double_backward", "cgtp_check_edges", "cgtp_layout_convert", "cgtp_error_string", "cgtp_last_error",
     "cgtp_profile_begin", "cgtp_profile_end", "cgtp_profile_count", "cgtp_profile_get",
@@ -63,6 +63,7 @@ def load() -> ctypes.CDLL:
         "cgtp_plan_cg_table": [P, I, ip, ctypes.POINTER(ctypes.c_double), I, ctypes.POINTER(ctypes.c_int)],
         "cgtp_plan_compile": [P, I],
         "cgtp_plan_set_scratch_budget": [P, Z],
+        "cgtp_plan_set_radial": [P, ctypes.c_int, ctypes.c_double],
         "cgtp_graph_build": [I, I, ip, ip, ip, ip, ctypes.POINTER(P)],
         "cgtp_graph_export": [P, ip, ip, ip, ip],
         "cgtp_graph_dims": [P, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)],
@@ -162,6 +163,11 @@ class Plan:
 
     def set_scratch_budget(self, nbytes: int) -> None:
         check(load().cgtp_plan_set_scratch_budget(self.handle, int(nbytes)))
+
+    def set_radial(self, kind: int, r_cut: float) -> None:
+        """Compute phi from |r| in the kernels (1 Bessel + envelope, 2 Gaussian, 0 none); the
+        convolution calls then take phi=None."""
+        check(load().cgtp_plan_set_radial(self.handle, int(kind), float(r_cut)))
 
 
 class Graph:

@@ -240,6 +240,22 @@ cgtp_status_t cgtp_plan_set_scratch_budget(cgtp_plan_t plan, size_t bytes) {
   return ok();
 }
 
+cgtp_status_t cgtp_plan_set_radial(cgtp_plan_t plan, int kind, double r_cut) {
+  if (!plan) return fail(CGTP_ERR_INVALID_ARG, "null plan");
+  if (kind < 0 || kind > 2) return fail(CGTP_ERR_INVALID_ARG, "radial kind must be 0, 1 or 2");
+  if (kind != 0 && !(r_cut > 0.0)) return fail(CGTP_ERR_INVALID_ARG, "cutoff radius must be positive");
+  if (kind == 2 && plan->p.K < 2) return fail(CGTP_ERR_INVALID_ARG, "the Gaussian basis needs K >= 2");
+  cgtp::Plan& p = plan->p;
+  std::lock_guard<std::mutex> lock(p.mu);
+  if (!p.kernels->families.empty())
+    return fail(CGTP_ERR_UNSUPPORTED, "set the radial basis before the plan's kernels are compiled");
+  p.radial = kind;
+  p.r_cut = kind ? r_cut : 0.0;
+  p.phi_off = p.g_width;
+  p.g_stride = (p.g_width + (kind ? p.K : 0) + 3) / 4 * 4;
+  return ok();
+}
+
 cgtp_status_t cgtp_plan_compile(cgtp_plan_t plan, int ops) {
   if (!plan) return fail(CGTP_ERR_INVALID_ARG, "null plan");
   std::string err;
@@ -350,9 +366,12 @@ cgtp_status_t cgtp_conv_forward(cgtp_plan_t plan, cgtp_graph_t g, cgtp_schedule_
                                 const void* pos, const void* shift, const void* phi, const void* A, void* out,
                                 void* workspace, size_t ws_bytes, void* stream) {
   if (!plan || !g) return fail(CGTP_ERR_INVALID_ARG, "null plan or graph");
-  if (!x || !pos || !phi || !A || !out) return fail(CGTP_ERR_INVALID_ARG, "null tensor argument");
+  if (!x || !pos || !A || !out) return fail(CGTP_ERR_INVALID_ARG, "null tensor argument");
   if (schedule != CGTP_STREAMED && schedule != CGTP_CONVENTIONAL) return fail(CGTP_ERR_INVALID_ARG, "bad schedule");
   cgtp::Plan& p = plan->p;
+  if ((phi == nullptr) != (p.radial != 0))
+    return fail(CGTP_ERR_INVALID_ARG, p.radial ? "phi must be NULL: the plan computes the radial basis"
+                                               : "null phi (the plan has no radial basis of its own)");
   cgtp::Graph& G = g->g;
   size_t need = 0;
   cgtp_workspace_size(plan, g, CGTP_OP_FORWARD, &need);
@@ -406,9 +425,12 @@ cgtp_status_t cgtp_conv_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x
                                  void* grad_edge_vec, void* grad_phi, void* grad_A, void* workspace, size_t ws_bytes,
                                  void* stream) {
   if (!plan || !g) return fail(CGTP_ERR_INVALID_ARG, "null plan or graph");
-  if (!x || !pos || !phi || !A || !grad_out) return fail(CGTP_ERR_INVALID_ARG, "null input tensor");
+  if (!x || !pos || !A || !grad_out) return fail(CGTP_ERR_INVALID_ARG, "null input tensor");
   cgtp::Plan& p = plan->p;
   cgtp::Graph& G = g->g;
+  if ((phi == nullptr) != (p.radial != 0))
+    return fail(CGTP_ERR_INVALID_ARG, p.radial ? "phi must be NULL: the plan computes the radial basis"
+                                               : "null phi (the plan has no radial basis of its own)");
   if (!grad_x && !grad_pos && !grad_edge_vec && !grad_phi && !grad_A) return ok();
   size_t need = 0;
   cgtp_workspace_size(plan, g, CGTP_OP_BACKWARD, &need);
@@ -510,6 +532,7 @@ cgtp_status_t cgtp_conv_double_backward(cgtp_plan_t plan, cgtp_graph_t g, const 
   cgtp::Plan& p = plan->p;
   cgtp::Graph& G = g->g;
   if (p.mode != CGTP_CHANNELWISE) return fail(CGTP_ERR_UNSUPPORTED, "double backward is channelwise only");
+  if (p.radial) return fail(CGTP_ERR_UNSUPPORTED, "double backward takes phi as an input (no fused radial basis)");
   if (!gg_x && !gg_pos && !gg_edge_vec && !gg_phi && !gg_A && !gg_grad_out) return ok();
   size_t need = 0;
   cgtp_status_t st = cgtp_workspace_size(plan, g, CGTP_OP_DOUBLE_BACKWARD, &need);

@@ -96,6 +96,37 @@ std::string gref(const Plan& p, int pi, int t, const std::string& row, const std
   return F("gq%s%d_%d.%c", tag.c_str(), pi, t / per, "abcd"[t % per]);
 }
 
+// Radial basis of |r| (plan.radial 1: Bessel with the p = 6 polynomial envelope, zero beyond the
+// cutoff; 2: Gaussians centred at k r_c / (K - 1) with width r_c / (K - 1)), with d/dr when df is
+// non-null.
+void emit_radial(Out& o, const Plan& p) {
+  const int K = p.K;
+  o.open("DEV void radial_eval(real r, real* f, real* df)");
+  if (p.radial == 1) {
+    o.line(F("const real rc = R(%.17g), d = r / rc;", p.r_cut));
+    o.line("const real d2 = d * d, d5 = d2 * d2 * d, d6 = d5 * d, d7 = d6 * d, d8 = d7 * d;");
+    o.line("const bool in = d < R(1);");
+    o.line("const real u = in ? R(1) - R(28) * d6 + R(48) * d7 - R(21) * d8 : R(0);");
+    o.line("const real du = in ? (R(-168) * d5 + R(336) * d6 - R(168) * d7) / rc : R(0);");
+    o.line(F("const real nrm = R(%.17g), ir = R(1) / r;", std::sqrt(2.0 / p.r_cut)));
+    o.open(F("for (int n = 0; n < %d; ++n)", K));
+    o.line(F("const real a = R(n + 1) * R(%.17g);", M_PI / p.r_cut));
+    o.line("const real sn = sin(a * r), cs = cos(a * r);");
+    o.line("const real b = nrm * sn * ir;");
+    o.line("f[n] = b * u;");
+    o.line("if (df) df[n] = nrm * (a * cs * r - sn) * ir * ir * u + b * du;");
+    o.close();
+  } else {
+    o.line(F("const real D = R(%.17g), inv2 = R(1) / (R(2) * D * D);", p.r_cut / (K - 1)));
+    o.open(F("for (int k = 0; k < %d; ++k)", K));
+    o.line("const real t = r - R(k) * D, g = exp(-t * t * inv2);");
+    o.line("f[k] = g;");
+    o.line("if (df) df[k] = -t * R(2) * inv2 * g;");
+    o.close();
+  }
+  o.close();
+}
+
 void prelude(Out& o, const Plan& p, bool dual, bool reduce) {
   const bool f64 = p.dtype == CGTP_F64;
   o.line(f64 ? "typedef double real;" : "typedef float real;");
@@ -145,6 +176,7 @@ void prelude(Out& o, const Plan& p, bool dual, bool reduce) {
     o.line("DEV real rowsum(real v) { v += dpp<0xB1>(v); v += dpp<0x4E>(v); v += dpp<0x141>(v);"
            " v += dpp<0x140>(v); return v; }");
   }
+  if (p.radial) emit_radial(o, p);
 }
 
 // Real spherical harmonics up to degree L, component normalised, as the three-term Legendre
@@ -202,10 +234,15 @@ void emit_prep(Out& o, const Plan& p, bool with_y) {
   o.line("const int eb = e0 + (int)blockIdx.x * 64;");
   o.line("const int e = min(eb + lane, e1 - 1);");
   emit_edge_vector(o);
-  o.line("const real inv = R(1) / sqrt(rx * rx + ry * ry + rz * rz);");
+  o.line("const real rr = sqrt(rx * rx + ry * ry + rz * rz), inv = R(1) / rr;");
   o.line(F("real Y[%d];", p.sh_dim));
   o.line("sh_eval<real>(rx * inv, ry * inv, rz * inv, Y);");
   std::vector<std::string> vals(size_t(p.g_stride), "R(0)");
+  if (p.radial) {
+    o.line(F("real fr[%d];", p.K));
+    o.line("radial_eval(rr, fr, nullptr);");
+    for (int q = 0; q < p.K; ++q) vals[size_t(p.phi_off + q)] = F("fr[%d]", q);
+  }
   for (const Path& P : p.paths) {
     int s = P.l2 * P.l2;
     for (size_t t = 0; t < P.gpairs.size(); ++t) {
@@ -316,6 +353,27 @@ constexpr int kRecvGroup = 4;  // receivers (one wave each) per workgroup in the
 // scope).  Rows x_j of the input blocks `blocks` are loaded one edge ahead (software
 // pipelining), so their latency overlaps the arithmetic of the current edge.  The body sees
 // e, j, g (G row), f<q> (phi) and x<b>_<m>.
+// sr = sum_q phi-bar_q dphi_q/dr at rr (the radial part of the edge-vector gradient is sr r-hat);
+// 0 when phi is an input.  `pb` names the phi-bar registers pb0..pb{K-1}.
+void emit_radial_term(Out& o, const Plan& p, const std::string& pb) {
+  if (!p.radial) {
+    o.line("const real sr = R(0);");
+    return;
+  }
+  o.line(F("real fr[%d], dfr[%d];", p.K, p.K));
+  o.line("radial_eval(rr, fr, dfr);");
+  std::string ex = F("%s0 * dfr[0]", pb.c_str());
+  for (int q = 1; q < p.K; ++q) ex += F(" + %s%d * dfr[%d]", pb.c_str(), q, q);
+  o.line("const real sr = " + ex + ";");
+}
+
+// Pointer to the K radial values of the current edge: the phi input, or the edge's G row
+// (`grow`) when the plan computes the basis itself.
+std::string phi_ptr(const Plan& p, const std::string& e, const std::string& grow) {
+  if (p.radial) return F("%s + %d", grow.c_str(), p.phi_off);
+  return F("phi + (i64)%s * %d", e.c_str(), p.K);
+}
+
 void emit_recv_edge_loop(Out& o, const Plan& p, const std::vector<int>& blocks, const std::string& start,
                          const std::string& stride, const std::function<void()>& body, bool block_uc,
                          int row_stride) {
@@ -352,8 +410,8 @@ void emit_recv_edge_loop(Out& o, const Plan& p, const std::vector<int>& blocks, 
     o.line("const int j = __builtin_amdgcn_readlane(cl_, k_);");
     xrow("x", "j", "const real ");
   }
-  o.line(F("const real* __restrict__ ph = phi + (i64)e * %d;", p.K));
   o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", row_stride));
+  o.line("const real* __restrict__ ph = " + phi_ptr(p, "e", "g") + ";");
   for (int q = 0; q < p.K; ++q) o.line(F("const real f%d = ph[%d];", q, q));
   body();
   o.close();
@@ -379,8 +437,8 @@ void emit_recv_edge_loop2(Out& o, const Plan& p, const std::vector<int>& blocks,
     xrow(next);
     for (int b : blocks)
       for (int m = 0; m < p.in[b].dim(); ++m) o.line(F("const real x%d_%d = %s%d_%d;", b, m, cur, b, m));
-    o.line(F("const real* __restrict__ ph = phi + (i64)e * %d;", p.K));
     o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", row_stride));
+    o.line("const real* __restrict__ ph = " + phi_ptr(p, "e", "g") + ";");
     for (int q = 0; q < p.K; ++q) o.line(F("const real f%d = ph[%d];", q, q));
     body();
     o.close();
@@ -858,8 +916,8 @@ void emit_bwd_src_task(Out& o, const Plan& p, int ti, const Task& T) {
     o.line("const int i_ = __builtin_amdgcn_readlane(il_, k_);");
     mrow("mb", "i_", "const real ");
   }
-  o.line(F("const real* __restrict__ ph = phi + (i64)e * %d;", K));
   o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", bwd_row_stride(p)));
+  o.line("const real* __restrict__ ph = " + phi_ptr(p, "e", "g") + ";");
   for (int q = 0; q < K; ++q) o.line(F("const real f%d = ph[%d];", q, q));
   for (int pi : S) {
     const Path& P = p.paths[pi];
@@ -941,16 +999,17 @@ void emit_edge_final(Out& o, const Plan& p, int ntask, int V) {
   o.line("if (e >= e1) return;");
   o.line("const real* __restrict__ col0 = ep + (e - e0);");
   o.line("#define ROWV(k) col0[(i64)(k) * eps]");
-  o.open("if (gphi)");
   for (int q = 0; q < K; ++q) {
     std::string ex = F("ROWV(%d)", q);
     for (int t = 1; t < ntask; ++t) ex += F(" + ROWV(%d)", t * V + q);
-    o.line(F("gphi[(i64)e * %d + %d] = ", K, q) + ex + ";");
+    o.line(F("const real pb%d = ", q) + ex + ";");
   }
+  o.open("if (gphi)");
+  for (int q = 0; q < K; ++q) o.line(F("gphi[(i64)e * %d + %d] = pb%d;", K, q, q));
   o.close();
   o.line("if (!gev) return;");
   emit_edge_vector(o);
-  o.line("const real inv = R(1) / sqrt(rx * rx + ry * ry + rz * rz);");
+  o.line("const real rr = sqrt(rx * rx + ry * ry + rz * rz), inv = R(1) / rr;");
   o.line("const real nx = rx * inv, ny = ry * inv, nz = rz * inv;");
   o.line(F("D3 Y[%d];", p.sh_dim));
   o.line("sh_eval<D3>(D3(nx, R(1), R(0), R(0)), D3(ny, R(0), R(1), R(0)), D3(nz, R(0), R(0), R(1)), Y);");
@@ -962,9 +1021,10 @@ void emit_edge_final(Out& o, const Plan& p, int ntask, int V) {
                                              " gz = fma(yb, Y[%d].z, gz); }", m, m, m));
   }
   o.line("const real d = nx * gx + ny * gy + nz * gz;");
-  o.line("gev[3 * (i64)e] = (gx - nx * d) * inv;");
-  o.line("gev[3 * (i64)e + 1] = (gy - ny * d) * inv;");
-  o.line("gev[3 * (i64)e + 2] = (gz - nz * d) * inv;");
+  emit_radial_term(o, p, "pb");
+  o.line("gev[3 * (i64)e] = (gx - nx * d) * inv + sr * nx;");
+  o.line("gev[3 * (i64)e + 1] = (gy - ny * d) * inv + sr * ny;");
+  o.line("gev[3 * (i64)e + 2] = (gz - nz * d) * inv + sr * nz;");
   o.line("#undef ROWV");
   o.close();
 }
@@ -988,16 +1048,17 @@ void emit_recv_edge_final(Out& o, const Plan& p, const std::vector<Task>& tasks)
   o.line("if (e >= e1) return;");
   o.line(F("const real* __restrict__ rw = ep + (i64)((e - e0) >> 6) * %d + ((e - e0) & 63);", 64 * row));
   o.line("#define RW(c) rw[64 * (c)]");
-  o.open("if (gphi)");
   for (int q = 0; q < K; ++q) {
     std::string ex;
     for (size_t t = 0; t < tasks.size(); ++t) ex += (t ? " + " : "") + F("RW(%d)", off[t] + q);
-    o.line(F("gphi[(i64)e * %d + %d] = ", K, q) + ex + ";");
+    o.line(F("const real pb%d = ", q) + ex + ";");
   }
+  o.open("if (gphi)");
+  for (int q = 0; q < K; ++q) o.line(F("gphi[(i64)e * %d + %d] = pb%d;", K, q, q));
   o.close();
   o.line("if (!gev) return;");
   emit_edge_vector(o);
-  o.line("const real inv = R(1) / sqrt(rx * rx + ry * ry + rz * rz);");
+  o.line("const real rr = sqrt(rx * rx + ry * ry + rz * rz), inv = R(1) / rr;");
   o.line("const real nx = rx * inv, ny = ry * inv, nz = rz * inv;");
   o.line(F("D3 Y[%d];", p.sh_dim));
   o.line("sh_eval<D3>(D3(nx, R(1), R(0), R(0)), D3(ny, R(0), R(1), R(0)), D3(nz, R(0), R(0), R(1)), Y);");
@@ -1016,9 +1077,10 @@ void emit_recv_edge_final(Out& o, const Plan& p, const std::vector<Task>& tasks)
                                            " gz = fma(yb, Y[%d].z, gz); }", m, m, m));
   }
   o.line("const real d = nx * gx + ny * gy + nz * gz;");
-  o.line("gev[3 * (i64)e] = (gx - nx * d) * inv;");
-  o.line("gev[3 * (i64)e + 1] = (gy - ny * d) * inv;");
-  o.line("gev[3 * (i64)e + 2] = (gz - nz * d) * inv;");
+  emit_radial_term(o, p, "pb");
+  o.line("gev[3 * (i64)e] = (gx - nx * d) * inv + sr * nx;");
+  o.line("gev[3 * (i64)e + 1] = (gy - ny * d) * inv + sr * ny;");
+  o.line("gev[3 * (i64)e + 2] = (gz - nz * d) * inv + sr * nz;");
   o.line("#undef RW");
   o.close();
 }

@@ -60,6 +60,10 @@ void emit_gvec_loads(Out& o, const Plan& p, int pi, const std::string& row, cons
                      bool vec = true);
 std::string gref(const Plan& p, int pi, int t, const std::string& row, const std::string& tag, bool vec = true);
 void prelude(Out& o, const Plan& p, bool dual, bool reduce);
+// Radial values of the current edge (the phi input or the edge's G row), and the radial part of
+// the edge-vector gradient (sr; needs rr = |r| and phi-bar registers <pb>0..K-1 in scope).
+std::string phi_ptr(const Plan& p, const std::string& e, const std::string& grow);
+void emit_radial_term(Out& o, const Plan& p, const std::string& pb);
 void emit_sh(Out& o, int L);
 void emit_edge_vector(Out& o);
 void emit_prep(Out& o, const Plan& p, bool with_y = false);

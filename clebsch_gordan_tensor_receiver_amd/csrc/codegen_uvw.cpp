@@ -479,8 +479,8 @@ void emit_zstate_task(Out& o, const Plan& p, const std::vector<Side>& sides, int
     for (int m = 0; m < B.dim(); ++m)
       o.line(F("const real mb%d_%d = gout[(i64)i_ * %d + %d + wc%d];", ob, m, p.c_out, B.offset + m * B.mul, ob));
   }
-  o.line(F("const real* __restrict__ ph = phi + (i64)e * %d;", K));
   o.line(F("const real* __restrict__ g = G + (i64)(k - k_base) * %d;", p.g_stride));
+  o.line("const real* __restrict__ ph = " + phi_ptr(p, "e", "g") + ";");
   for (int q = 0; q < K; ++q) o.line(F("const real f%d = ph[%d];", q, q));
   for (int pi : paths) {
     const Path& P = p.paths[pi];
@@ -534,10 +534,15 @@ void emit_prep_src(Out& o, const Plan& p) {
   o.line("if (k >= k1) return;");
   o.line("const int e = src_edge[k];");
   emit_edge_vector(o);
-  o.line("const real inv = R(1) / sqrt(rx * rx + ry * ry + rz * rz);");
+  o.line("const real rr = sqrt(rx * rx + ry * ry + rz * rz), inv = R(1) / rr;");
   o.line(F("real Y[%d];", p.sh_dim));
   o.line("sh_eval<real>(rx * inv, ry * inv, rz * inv, Y);");
   o.line(F("real* __restrict__ dst = G + (i64)(k - k0) * %d;", p.g_stride));
+  if (p.radial) {
+    o.line(F("real fr[%d];", p.K));
+    o.line("radial_eval(rr, fr, nullptr);");
+    for (int q = 0; q < p.K; ++q) o.line(F("dst[%d] = fr[%d];", p.phi_off + q, q));
+  }
   for (const Path& P : p.paths) {
     int s = P.l2 * P.l2;
     int n = P.g_off;

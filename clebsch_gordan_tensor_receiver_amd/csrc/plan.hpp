@@ -62,6 +62,12 @@ struct Plan {
   int g_stride = 0;    // padded row stride of G in elements
   int cg_nnz = 0;
   size_t scratch_budget = size_t(256) << 20;
+  // Radial basis computed from |r| inside the kernels (cgtp_plan_set_radial): 0 = none (phi is an
+  // input), 1 = Bessel with the p = 6 polynomial envelope, 2 = Gaussian.  The K values of an edge
+  // sit in its G row at phi_off.
+  int radial = 0;
+  double r_cut = 0.0;
+  int phi_off = 0;
   // Paths into each output block / out of each input block, in path order.
   std::vector<std::vector<int>> by_out, by_in;
   std::string key;     // canonical description used to name and cache kernels

@@ -118,6 +118,21 @@ cgtp_status_t cgtp_plan_compile(cgtp_plan_t plan, int ops);
  * receiver chunks that fit it (Sobek Appendix B.2 bounds its scratch the same way). */
 cgtp_status_t cgtp_plan_set_scratch_budget(cgtp_plan_t plan, size_t bytes);
 
+/* Radial basis computed inside the kernels from the edge length r = |edge vector| instead of
+ * being passed as phi (the pages give phi as an input, Sobek Eq. 12, and name an envelope option
+ * without formulas; this is the plainest reading):
+ *   kind 0  none: phi is an input (default)
+ *   kind 1  Bessel: phi_n = sqrt(2/r_cut) sin(n pi r / r_cut) / r * u(r / r_cut), n = 1..K, with
+ *           the polynomial envelope u(d) = 1 - 28 d^6 + 48 d^7 - 21 d^8 and phi = 0 for r >= r_cut
+ *   kind 2  Gaussian: phi_k = exp(-(r - k D)^2 / (2 D^2)), D = r_cut / (K - 1), k = 0..K-1
+ * With kind 1 or 2 the convolution calls take phi = NULL; no E x K tensor is read, the values
+ * live in the per-chunk workspace rows; cgtp_conv_backward's grad_pos and grad_edge_vec include
+ * the chain rule through phi(r) and grad_phi (optional) is the gradient with respect to the
+ * computed values.  Call before the plan compiles kernels (UNSUPPORTED afterwards).  The double
+ * backward keeps phi as an input (UNSUPPORTED with a radial kind).  INVALID_ARG for an unknown
+ * kind, r_cut <= 0, or kind 2 with K < 2. */
+cgtp_status_t cgtp_plan_set_radial(cgtp_plan_t plan, int kind, double r_cut);
+
 /* ---------------------------------------------------------------- graphs */
 
 /* Sort an edge list into receiver CSR order and build the source CSR (host only, exact).
@@ -146,7 +161,8 @@ cgtp_status_t cgtp_graph_destroy(cgtp_graph_t g);
 cgtp_status_t cgtp_workspace_size(cgtp_plan_t plan, cgtp_graph_t g, cgtp_op_t op, size_t* bytes);
 
 /* Forward.  x: N x C_in; pos: N x 3; shift: E x 3 receiver-sorted image shifts added to
- * pos[send] - pos[recv] (NULL = no shift); phi: E x K receiver-sorted; A: K x N_w;
+ * pos[send] - pos[recv] (NULL = no shift); phi: E x K receiver-sorted (NULL exactly when the
+ * plan computes the radial basis, cgtp_plan_set_radial); A: K x N_w;
  * out: N x C_out (overwritten). */
 cgtp_status_t cgtp_conv_forward(cgtp_plan_t plan, cgtp_graph_t g, cgtp_schedule_t schedule,
                                 const void* x, const void* pos, const void* shift, const void* phi,

@@ -173,6 +173,15 @@ def test_host_validation_before_any_device_work(lib):
     assert so.cgtp_check_edges(plan.handle, g.handle, 1, None, 1, 2, None, ctypes.byref(first)) == WORKSPACE
     assert so.cgtp_check_edges(plan.handle, g.handle, 1, None, 1, 2, None, None) == INVALID_ARG
     assert so.cgtp_plan_set_scratch_budget(plan.handle, 16) == INVALID_ARG
+    # Radial basis: kinds 0..2, positive cutoff; phi NULL exactly when the plan computes it.
+    assert so.cgtp_plan_set_radial(plan.handle, 3, 3.0) == INVALID_ARG
+    assert so.cgtp_plan_set_radial(plan.handle, 1, 0.0) == INVALID_ARG
+    assert so.cgtp_conv_forward(plan.handle, g.handle, 0, 1, 1, None, None, 1, 1, None, 0, None) == INVALID_ARG
+    rad = lib.Plan("8x0e+8x1o", "1x0e+1x1o", "8x0e+8x1o", "uvu", "float64", 4)
+    assert so.cgtp_plan_set_radial(rad.handle, 2, 3.0) == 0
+    assert so.cgtp_conv_forward(rad.handle, g.handle, 0, 1, 1, None, 1, 1, 1, None, 0, None) == INVALID_ARG
+    assert so.cgtp_conv_double_backward(rad.handle, g.handle, 1, 1, None, 1, 1, 1, *[None] * 12, 0,
+                                        None) == UNSUPPORTED
     assert so.cgtp_plan_path(plan.handle, 99, (ctypes.c_int32 * 9)()) == INVALID_ARG
     assert so.cgtp_error_string(WORKSPACE) == b"workspace too small"
 

@@ -447,3 +447,86 @@ def test_double_backward_second_order_symmetry():
 
     a, b = pair(g1, v2), pair(g2, v1)
     assert abs(a - b) <= 1e-10 * max(1.0, abs(a))
+
+
+# ---------------------------------------------------------------- fused radial basis (oracle)
+
+def test_envelope_is_smooth_at_the_cutoff():
+    from oracle import radial
+    d = torch.tensor([0.0, 1.0 - 1e-300], dtype=torch.float64, requires_grad=True)
+    u = (1.0 - 28.0 * d ** 6 + 48.0 * d ** 7 - 21.0 * d ** 8)
+    assert abs(float(radial.envelope(torch.tensor([0.0], dtype=torch.float64))[0]) - 1.0) == 0.0
+    assert float(radial.envelope(torch.tensor([1.0, 1.5], dtype=torch.float64)).abs().max()) == 0.0
+    g1, = torch.autograd.grad(u.sum(), d, create_graph=True)
+    g2, = torch.autograd.grad(g1.sum(), d)
+    # u(1) = u'(1) = u''(1) = 0: the basis and its first two derivatives vanish at r_c.
+    assert abs(float(u[1].detach())) < 1e-12 and abs(float(g1[1].detach())) < 1e-9 and abs(float(g2[1])) < 1e-8
+    assert abs(float(g1[0].detach())) == 0.0
+
+
+def test_bessel_basis_is_orthonormal_without_envelope():
+    # sqrt(2/r_c) sin(n pi r / r_c) / r are orthonormal under r^2 dr on [0, r_c].
+    from oracle import radial
+    rc, K = 5.0, 8
+    xg, wg = np.polynomial.legendre.leggauss(400)
+    r = torch.tensor(0.5 * rc * (xg + 1.0))
+    w = torch.tensor(0.5 * rc * wg)
+    B = radial.basis(radial.BESSEL, r, rc, K, envelope_on=False)
+    gram = (B * (w * r ** 2)[:, None]).T @ B
+    assert float((gram - torch.eye(K, dtype=torch.float64)).abs().max()) < 1e-12
+
+
+def test_gaussian_basis_peak_and_width():
+    from oracle import radial
+    rc, K = 6.0, 16
+    D = rc / (K - 1)
+    mu = torch.arange(K, dtype=torch.float64) * D
+    at_mu = radial.basis(radial.GAUSSIAN, mu, rc, K)
+    assert float((torch.diagonal(at_mu) - 1.0).abs().max()) == 0.0
+    off = radial.basis(radial.GAUSSIAN, mu[3:4] + D, rc, K)
+    assert abs(float(off[0, 3]) - math.exp(-0.5)) < 1e-15
+
+
+@pytest.mark.parametrize("kind", [1, 2])
+def test_radial_derivative_complex_step(kind):
+    from oracle import radial
+    rc, K = 5.0, 8
+    r = torch.tensor([0.7, 1.9, 3.3, 4.6, 4.99], dtype=torch.float64)
+    h = 1e-30
+    cs = radial.basis(kind, r.to(torch.complex128) + 1j * h, rc, K).imag / h
+    d = radial.basis_derivative(kind, r, rc, K)
+    assert float((cs - d).abs().max()) <= 1e-12 * max(1.0, float(d.abs().max()))
+
+
+@pytest.mark.parametrize("kind", [1, 2])
+def test_position_gradient_through_the_radial_basis(kind):
+    # Finite differences of <grad_out, m(pos)> with phi computed from |r|: the oracle backward
+    # (through Y) plus the radial term (sum_q phi-bar_q dphi_q/dr) r-hat, mapped to positions.
+    from oracle import radial
+    ov = dict(irreps_in="2x0e+2x1o+2x2e", irreps_out="2x0e+2x1o+2x2e", irreps_sh=_sh_str(2), mode="uvu")
+    c = make_case(1, irreps_override=ov, n_nodes=12)
+    rc, K = 3.0, c.phi.shape[1]
+
+    def L(pos):
+        ev = conv.edge_vectors(pos, c.shift, c.recv, c.send)
+        phi = radial.basis(kind, radial.edge_lengths(ev), rc, K)
+        return float((conv.forward_conventional(c.problem, c.x, ev, c.recv, c.send, phi, c.A)
+                      * torch.as_tensor(c.grad_out)).sum())
+
+    ev = c.edge_vec
+    phi = radial.basis(kind, radial.edge_lengths(ev), rc, K)
+    b = conv.backward(c.problem, c.x, ev, c.recv, c.send, phi, c.A, c.grad_out, n_nodes=c.n_nodes)
+    ge = b["edge_vec"] + radial.edge_vec_grad(kind, ev, rc, b["phi"])
+    gpos = torch.zeros(c.n_nodes, 3, dtype=torch.float64)
+    gpos.index_add_(0, torch.as_tensor(c.send, dtype=torch.long), ge)
+    gpos.index_add_(0, torch.as_tensor(c.recv, dtype=torch.long), -ge)
+    rng = np.random.default_rng(21)
+    h = 1e-6
+    for _ in range(6):
+        idx = (int(rng.integers(c.n_nodes)), int(rng.integers(3)))
+        pp, pm = c.pos.copy(), c.pos.copy()
+        pp[idx] += h
+        pm[idx] -= h
+        fd = (L(pp) - L(pm)) / (2 * h)
+        got = float(gpos[idx])
+        assert abs(fd - got) <= 1e-6 * max(1.0, abs(got)), (kind, idx, fd, got)
