@@ -195,6 +195,9 @@ def main() -> int:
                     help="scaling axis of the fully connected profiles (one JSON line per point)")
     ap.add_argument("--profile", type=int, default=0, choices=(0, 1, 2, 3),
                     help="irrep profile (L_max) of the sweep; 0: all three")
+    ap.add_argument("--radial", action="store_true",
+                    help="compute the radial basis in the kernels from |r| (Bessel + envelope; Gaussians for "
+                         "workload 5) instead of reading phi")
     ap.add_argument("--points", default="",
                     help="comma-separated sweep points (degrees or copy counts); default: the whole axis")
     args = ap.parse_args()
@@ -224,6 +227,11 @@ def main() -> int:
     plan = cg.Plan(spec["irreps_in"], spec["irreps_sh"], spec["irreps_out"], spec["mode"], dtype, spec["K"])
     if args.scratch_mib > 0:
         plan.set_scratch_budget(args.scratch_mib << 20)
+    if args.radial:
+        if "dbl" in passes:
+            print("--radial: the double backward takes phi as an input", file=sys.stderr)
+            return 2
+        plan.set_radial(2 if spec["radial"] == "gaussian" else 1, spec["rc"])
     graph = cg.Graph(w.n_nodes, w.recv, w.send, w.image)
     perm = graph.perm
     info = plan.info
@@ -258,13 +266,15 @@ def main() -> int:
         gg = dict(gg_x=torch.empty_like(x), gg_pos=torch.empty_like(pos), gg_edge_vec=torch.empty((E, 3), **dev),
                   gg_phi=torch.empty_like(phi), gg_A=torch.empty_like(A), gg_grad_out=torch.empty_like(out))
 
+    phi_in = None if args.radial else phi
+
     def step():
         for ps in passes:
             if ps in ("fwd", "fwds"):
                 sched = cg.CONVENTIONAL if ps == "fwd" else cg.STREAMED
-                cg.conv_forward(plan, graph, sched, x, pos, shift, phi, A, out, ws[ps])
+                cg.conv_forward(plan, graph, sched, x, pos, shift, phi_in, A, out, ws[ps])
             elif ps == "bwd":
-                cg.conv_backward(plan, graph, x, pos, shift, phi, A, gout, grad_x=grads["x"], grad_pos=grads["pos"],
+                cg.conv_backward(plan, graph, x, pos, shift, phi_in, A, gout, grad_x=grads["x"], grad_pos=grads["pos"],
                                  grad_edge_vec=grads["edge_vec"], grad_phi=grads["phi"], grad_A=grads["A"],
                                  workspace=ws[ps])
             else:
@@ -338,13 +348,13 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": f"{desc}; {label}" + ("; gradients of x, phi, A and positions" if "bwd" in passes
                                                      else ""),
-                   "n_nodes": N, "n_edges": E, "passes": list(passes),
+                   "n_nodes": N, "n_edges": E, "passes": list(passes), "radial_in_kernel": bool(args.radial),
                    "scratch_budget_mib": args.scratch_mib or 256},
         "gflops_algorithmic": round(2.0 * step_fma / (ms_per_step * 1e-3) / 1e9, 1) if step_fma else None,
         "kernels": result_kernels,
         "roofline": roofline,
     }
-    if cfg == DEFAULT_WORKLOAD and not args.no_cpu_baseline:
+    if cfg == DEFAULT_WORKLOAD and not args.no_cpu_baseline and not args.radial:
         result["cpu_baseline"], result["parity"] = cpu_baseline(w, plan, perm, x_h, A_h, g_h, out, grads)
     print(json.dumps(result), flush=True)
     return 0
