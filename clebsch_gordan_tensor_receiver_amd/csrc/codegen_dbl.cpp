@@ -360,9 +360,15 @@ void emit_dsrc_task(Out& o, const Plan& p, int ti, const Task& T) {
   for (const auto& S : a_subsets(p, T.paths, kDsrcRegs)) {
     o.open("");
     emit_da_loads(o, p, S);
-    o.open("for (int k = s0; k < s1; ++k)");
-    o.line("const int e = src_edge[k];");
-    o.line("const int i = recv[e];");
+    // Edge ids and receivers of up to 64 out-edges, one per lane, taken with readlane.
+    o.open("for (int kb_ = s0; kb_ < s1; kb_ += 64)");
+    o.line("const int kl_ = kb_ + (int)threadIdx.x;");
+    o.line("const int el_ = src_edge[kl_ < s1 ? kl_ : kb_];");
+    o.line("const int il_ = recv[el_];");
+    o.line("const int ne_ = min(64, s1 - kb_);");
+    o.open("for (int k_ = 0; k_ < ne_; ++k_)");
+    o.line("const int e = __builtin_amdgcn_readlane(el_, k_);");
+    o.line("const int i = __builtin_amdgcn_readlane(il_, k_);");
     o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", 2 * p.g_stride));
     o.line(F("const real* __restrict__ gd = g + %d;", p.g_stride));
     o.line(F("const real* __restrict__ ph = phi + (i64)e * %d;", K));
@@ -392,6 +398,7 @@ void emit_dsrc_task(Out& o, const Plan& p, int ti, const Task& T) {
       for (int m = 0; m < d1; ++m)
         if (started[m]) o.line(F("acc%d = fma(wd%d, b%d_%d, fma(w%d, bd%d_%d, acc%d));", m, pi, pi, m, pi, pi, m, m));
     }
+    o.close();
     o.close();
     o.close();
   }
