@@ -141,7 +141,10 @@ struct GemmSpec {
 };
 
 // LDS-tiled MFMA GEMM: 64 x 64 output tile per 4-wave workgroup, K staged 32 at a time, each wave
-// a 32 x 32 quarter as 2 x 2 MFMA 16x16x4 tiles.  C[r][c] = sum_k A(r, k) B(k, c) over
+// a 32 x 32 quarter as 2 x 2 MFMA 16x16x4 tiles.  A K-fast B operand (stored 32 k values of one
+// column by 32 lanes) has its tile columns XOR-swizzled inside aligned groups of 16 by
+// (k / 2) mod 16: the stores then hit 32 distinct banks instead of 2, the MFMA reads stay
+// conflict-free.  C[r][c] = sum_k A(r, k) B(k, c) over
 // k in [kb, ke); `store` writes value v at (r, c).  Two LDS buffers: the next K slice is loaded
 // into registers while the current one feeds the MFMAs, then stored to the other buffer, so one
 // barrier per slice suffices and the global loads overlap the matrix work.
@@ -187,7 +190,8 @@ void emit_gemm(Out& o, const GemmSpec& g) {
     o.open("for (int t = 0; t < 8; ++t)");
     o.line("const int id = t * 256 + tid;");
     o.line(g.b_kfast ? "const int cc = id >> 5, kk = id & 31;" : "const int cc = id & 63, kk = id >> 6;");
-    o.line("Bs[" + buf + "][kk * 80 + cc] = rb[t];");
+    o.line(g.b_kfast ? "Bs[" + buf + "][kk * 80 + (cc ^ ((kk >> 1) & 15))] = rb[t];"
+                     : "Bs[" + buf + "][kk * 80 + cc] = rb[t];");
     o.close();
   };
   o.open("if (kb < ke)");
@@ -204,8 +208,9 @@ void emit_gemm(Out& o, const GemmSpec& g) {
   o.line("const int ka = s * 4 + (lane >> 4);");
   o.line("const real x0 = As[cur][(32 * (wv >> 1) + (lane & 15)) * 34 + ka];");
   o.line("const real x1 = As[cur][(32 * (wv >> 1) + 16 + (lane & 15)) * 34 + ka];");
-  o.line("const real y0 = Bs[cur][ka * 80 + 32 * (wv & 1) + (lane & 15)];");
-  o.line("const real y1 = Bs[cur][ka * 80 + 32 * (wv & 1) + 16 + (lane & 15)];");
+  o.line(g.b_kfast ? "const int sw = (ka >> 1) & 15;" : "const int sw = 0;");
+  o.line("const real y0 = Bs[cur][ka * 80 + ((32 * (wv & 1) + (lane & 15)) ^ sw)];");
+  o.line("const real y1 = Bs[cur][ka * 80 + ((32 * (wv & 1) + 16 + (lane & 15)) ^ sw)];");
   o.line("a00 = MFMA(x0, y0, a00); a01 = MFMA(x0, y1, a01); a10 = MFMA(x1, y0, a10); a11 = MFMA(x1, y1, a11);");
   o.close();
   o.open("if (more)");
