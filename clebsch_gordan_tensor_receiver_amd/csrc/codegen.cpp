@@ -344,7 +344,6 @@ const char* kFwdArgs =
     " const real* __restrict__ G, const int* __restrict__ row_ptr, const int* __restrict__ col,"
     " real* __restrict__ out";
 
-constexpr bool kLanePrefetch = false;  // gather the next edge's row one edge ahead
 constexpr int kFwdRegs = kRegBudget;   // A registers per lane of one path subset in the forward
 constexpr int kSrcSplit = 2;   // waves sharing one sender's edge list in the source backward
 constexpr int kRecvGroup = 4;  // receivers (one wave each) per workgroup in the receiver backward
@@ -395,21 +394,10 @@ void emit_recv_edge_loop(Out& o, const Plan& p, const std::vector<int>& blocks, 
   o.line("const int el_ = eb_ + li_ * " + stride + ";");
   o.line("const int cl_ = col[el_ < e1 ? el_ : eb_];");
   o.line("const int ne_ = min(64, (e1 - eb_ + " + stride + " - 1) / " + stride + ");");
-  if (kLanePrefetch) {
-    o.line("int jn = __builtin_amdgcn_readlane(cl_, 0);");
-    xrow("xn", "jn", "real ");
-  }
   o.open("for (int k_ = 0; k_ < ne_; ++k_)");
   o.line("const int e = eb_ + k_ * " + stride + ";");
-  if (kLanePrefetch) {
-    for (int b : blocks)
-      for (int m = 0; m < p.in[b].dim(); ++m) o.line(F("const real x%d_%d = xn%d_%d;", b, m, b, m));
-    o.line("jn = __builtin_amdgcn_readlane(cl_, k_ + 1 < ne_ ? k_ + 1 : k_);");
-    xrow("xn", "jn", "");
-  } else {
-    o.line("const int j = __builtin_amdgcn_readlane(cl_, k_);");
-    xrow("x", "j", "const real ");
-  }
+  o.line("const int j = __builtin_amdgcn_readlane(cl_, k_);");
+  xrow("x", "j", "const real ");
   o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", row_stride));
   o.line("const real* __restrict__ ph = " + phi_ptr(p, "e", "g") + ";");
   for (int q = 0; q < p.K; ++q) o.line(F("const real f%d = ph[%d];", q, q));
@@ -901,21 +889,10 @@ void emit_bwd_src_task(Out& o, const Plan& p, int ti, const Task& T) {
   o.line("const int el_ = src_edge[kl_ < s1 ? kl_ : kb_];");
   o.line("const int il_ = recv[el_];");
   o.line(F("const int ne_ = min(64, (s1 - kb_ + %d) / %d);", kSrcSplit - 1, kSrcSplit));
-  if (kLanePrefetch) {
-    o.line("int in_ = __builtin_amdgcn_readlane(il_, 0);");
-    mrow("mn", "in_", "real ");
-  }
   o.open("for (int k_ = 0; k_ < ne_; ++k_)");
   o.line("const int e = __builtin_amdgcn_readlane(el_, k_);");
-  if (kLanePrefetch) {
-    for (int ob : obs)
-      for (int m = 0; m < p.out[ob].dim(); ++m) o.line(F("const real mb%d_%d = mn%d_%d;", ob, m, ob, m));
-    o.line("in_ = __builtin_amdgcn_readlane(il_, k_ + 1 < ne_ ? k_ + 1 : k_);");
-    mrow("mn", "in_", "");
-  } else {
-    o.line("const int i_ = __builtin_amdgcn_readlane(il_, k_);");
-    mrow("mb", "i_", "const real ");
-  }
+  o.line("const int i_ = __builtin_amdgcn_readlane(il_, k_);");
+  mrow("mb", "i_", "const real ");
   o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", bwd_row_stride(p)));
   o.line("const real* __restrict__ ph = " + phi_ptr(p, "e", "g") + ";");
   for (int q = 0; q < K; ++q) o.line(F("const real f%d = ph[%d];", q, q));
