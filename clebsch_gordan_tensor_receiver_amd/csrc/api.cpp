@@ -467,7 +467,9 @@ cgtp_status_t cgtp_conv_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x
   void* gev = grad_edge_vec ? grad_edge_vec : static_cast<void*>(ws + L.gev_off);
   const bool need_edge = grad_edge_vec || grad_pos || grad_phi;
   void* gev_arg = (grad_edge_vec || grad_pos) ? gev : nullptr;
-  if (grad_A) {
+  // With one receiver chunk every A-bar slot is written (not accumulated) by its workgroup.
+  int acc_slots = L.chunks.size() > 1 ? 1 : 0;
+  if (grad_A && acc_slots) {
     long long n = (long long)L.nslot * p.K * p.n_w;
     void* a[] = {&ap, &n};
     if ((st = cgtp::launch(kzero, unsigned((n + 255) / 256), 256, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
@@ -487,7 +489,7 @@ cgtp_status_t cgtp_conv_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x
       int per, nch;
       chunk_geometry(nrec, &per, &nch);
       void* a[] = {(void*)&x, (void*)&phi, (void*)&A, &Gb, (void*)&d.row_ptr, (void*)&d.col, (void*)&grad_out,
-                   &ep, &ap, &i0, &nrec, &per, &nch, &e0, &eps};
+                   &ep, &ap, &i0, &nrec, &per, &nch, &e0, &eps, &acc_slots};
       if ((st = cgtp::launch(krecv, unsigned(8 * nt_r * nch), 64 * kRecvGroup, 0, s, a, &err)) != CGTP_OK)
         return fail(st, err);
     }

@@ -695,7 +695,7 @@ void emit_bwd_recv_task(Out& o, const Plan& p, int ti, const Task& T, int col_of
   const std::vector<int> ycols = recv_task_ycols(p, T);
   const int V = recv_task_width(p, T);
   auto ycol = [&](int y) { return K + int(std::find(ycols.begin(), ycols.end(), y) - ycols.begin()); };
-  o.open(F("DEV void bwr_t%d(%s, real* sm, int node, int e_base, int eps, int slot)", ti, kRecvArgs));
+  o.open(F("DEV void bwr_t%d(%s, real* sm, int node, int e_base, int eps, int slot, int acc)", ti, kRecvArgs));
   o.line("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
   emit_vz(o, p);
   o.line(F("const int u = %d + lane;", T.cb * 64));
@@ -814,9 +814,13 @@ void emit_bwd_recv_task(Out& o, const Plan& p, int ti, const Task& T, int col_of
   emit_wave_combine(o, "aa", int(aa.size()), kRecvGroup);
   o.open(F("if (w == 0 && u < %d)", MUL));
   o.line(F("real* __restrict__ dst = ap + (i64)slot * %d + u;", K * p.n_w));
+  // acc = 0 (a single receiver chunk): the slot is written, not accumulated, so it needs no
+  // zero fill; every slot's workgroup runs, with node = -1 for missing receivers.
   int ai = 0;
   for (int pi : T.paths)
-    for (int q = 0; q < K; ++q, ++ai) o.line(F("dst[%d] += aa%d;", q * p.n_w + p.paths[pi].w_off, ai));
+    for (int q = 0; q < K; ++q, ++ai)
+      o.line(F("dst[%d] = acc ? dst[%d] + aa%d : aa%d;", q * p.n_w + p.paths[pi].w_off,
+               q * p.n_w + p.paths[pi].w_off, ai, ai));
   o.close();
   o.close();
 }
@@ -827,20 +831,22 @@ void emit_recv_dispatch(Out& o, const Plan& p, int ntask) {
   int amax = 0;
   for (const Task& t : recv_backward_tasks(p)) amax = std::max(amax, int(t.paths.size()) * p.K);
   o.line(F("extern \"C\" __global__ void __launch_bounds__(%d)", 64 * kRecvGroup));
-  o.open(std::string("cgtp_bwd_recv(") + kRecvArgs + ", int i0, int nrec, int per, int nch, int e_base, int eps)");
+  o.open(std::string("cgtp_bwd_recv(") + kRecvArgs +
+         ", int i0, int nrec, int per, int nch, int e_base, int eps, int acc)");
   o.line(F("__shared__ real sm[%d];", (kRecvGroup - 1) * amax * 64));
   o.line("const int b = (int)blockIdx.x;");
   o.line("const int xcd = b & 7, s = b >> 3;");
   o.line("const int t = s / nch, c = s - t * nch;");
   o.line(F("const int lo = xcd * per + c * %d;", kRecvGroup));
   o.line(F("int hi = lo + %d; if (hi > (xcd + 1) * per) hi = (xcd + 1) * per; if (hi > nrec) hi = nrec;", kRecvGroup));
-  o.line("if (lo >= hi) return;");
+  o.line("if (lo >= hi && acc) return;");
   o.line("const int r = lo + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
   o.line("const int node = r < hi ? i0 + r : -1;");
   o.line("const int slot = xcd * nch + c;");
   o.open("switch (t)");
   for (int k = 0; k < ntask; ++k)
-    o.line(F("case %d: bwr_t%d(x, phi, A, G, row_ptr, col, gout, ep, ap, sm, node, e_base, eps, slot); break;", k, k));
+    o.line(F("case %d: bwr_t%d(x, phi, A, G, row_ptr, col, gout, ep, ap, sm, node, e_base, eps, slot, acc); break;", k,
+             k));
   o.line("default: break;");
   o.close();
   o.close();
