@@ -518,7 +518,7 @@ cgtp_status_t cgtp_conv_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x
   if (grad_A) {
     int n = p.K * p.n_w, ns = L.nslot;
     void* a[] = {&ap, &ns, &n, &grad_A};
-    if ((st = cgtp::launch(kred, unsigned((n + 63) / 64), 256, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
+    if ((st = cgtp::launch(kred, unsigned((n + 63) / 64), 512, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
   }
   return ok();
 }
@@ -635,7 +635,7 @@ cgtp_status_t cgtp_conv_double_backward(cgtp_plan_t plan, cgtp_graph_t g, const 
   if (gg_A) {
     int n = p.K * p.n_w, ns = L.nslot;
     void* a[] = {&ap, &ns, &n, &gg_A};
-    if ((st = cgtp::launch(kred, unsigned((n + 63) / 64), 256, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
+    if ((st = cgtp::launch(kred, unsigned((n + 63) / 64), 512, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
   }
   return ok();
 }

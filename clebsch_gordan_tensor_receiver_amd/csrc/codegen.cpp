@@ -1115,14 +1115,14 @@ void emit_small_kernels(Out& o) {
   o.line("sx = wave_total(sx); sy = wave_total(sy); sz = wave_total(sz);");
   o.line("if (lane == 0) { gpos[3 * (i64)i] = sx; gpos[3 * (i64)i + 1] = sy; gpos[3 * (i64)i + 2] = sz; }");
   o.close();
-  // A-bar = sum over wave slots of the partials: block = 64 outputs x 4 slot quarters, combined in
-  // LDS in a fixed order.
-  o.line("extern \"C\" __global__ void __launch_bounds__(256)");
+  // A-bar = sum over wave slots of the partials: block = 64 outputs x 8 slot ranges (one wave
+  // each, four interleaved accumulators), combined in LDS in a fixed order.
+  o.line("extern \"C\" __global__ void __launch_bounds__(512)");
   o.open("cgtp_a_reduce(const real* __restrict__ ap, int nslot, int n, real* __restrict__ gA)");
-  o.line("__shared__ real part[4][64];");
+  o.line("__shared__ real part[8][64];");
   o.line("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
   o.line("const int k = (int)blockIdx.x * 64 + lane;");
-  o.line("const int q = (nslot + 3) / 4, s0 = w * q, s1 = min(nslot, s0 + q);");
+  o.line("const int q = (nslot + 7) / 8, s0 = w * q, s1 = min(nslot, s0 + q);");
   o.line("real a0 = R(0), a1 = R(0), a2 = R(0), a3 = R(0);");
   o.open("if (k < n)");
   o.line("int s = s0;");
@@ -1132,7 +1132,8 @@ void emit_small_kernels(Out& o) {
   o.close();
   o.line("part[w][lane] = (a0 + a1) + (a2 + a3);");
   o.line("__syncthreads();");
-  o.line("if (w == 0 && k < n) gA[k] = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);");
+  o.line("if (w == 0 && k < n) gA[k] = ((part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane])) +"
+         " ((part[4][lane] + part[5][lane]) + (part[6][lane] + part[7][lane]));");
   o.close();
 }
 
