@@ -344,7 +344,11 @@ const char* kFwdArgs =
     " const real* __restrict__ G, const int* __restrict__ row_ptr, const int* __restrict__ col,"
     " real* __restrict__ out";
 
-constexpr int kFwdRegs = kRegBudget;   // A registers per lane of one path subset in the forward
+// A coefficients per lane held by one path subset of the conventional forward (K per path; 64-bit
+// values take two registers each).  Four paths at K = 8 walk the edge list fastest in both
+// precisions: larger subsets lower the occupancy of this latency-bound loop more than they save
+// in repeated gathers.
+constexpr int kFwdAValues = 32;
 constexpr int kSrcSplit = 2;   // waves sharing one sender's edge list in the source backward
 constexpr int kRecvGroup = 4;  // receivers (one wave each) per workgroup in the receiver backward
 
@@ -496,7 +500,7 @@ void emit_fwd_task(Out& o, const Plan& p, int ti, const Task& T) {
       o.line("real " + accs.back() + " = R(0);");
     }
   o.line("const int e0 = row_ptr[node], e1 = row_ptr[node + 1];");
-  for (const auto& S : a_subsets(p, T.paths, kFwdRegs)) {
+  for (const auto& S : a_subsets(p, T.paths, kFwdAValues * (p.dtype == CGTP_F64 ? 2 : 1))) {
     o.open("");
     emit_a_loads(o, p, S);
     emit_recv_edge_loop(o, p, in_blocks_of(p, S), "w", std::to_string(fwd_split(p)), [&] {
