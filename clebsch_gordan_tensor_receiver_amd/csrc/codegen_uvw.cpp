@@ -16,6 +16,7 @@
 //   (uvw_zstate, lane = output channel w, over the source CSR), then gemm_xbar_b:
 //   x-bar_j[m1][u] = sum_{(pi, q, w)} Z_j[m1][(pi, q, w)] A[q, w_off_pi + u C_out + w].
 #include <algorithm>
+#include <functional>
 #include <set>
 
 #include "codegen.hpp"
@@ -138,7 +139,22 @@ struct GemmSpec {
   std::string name, args, a_at, b_at, store;
   int N;
   bool a_kfast, b_kfast, split;
+  // 16-byte tile loads: a_at / b_at are element lvalues contiguous along their fast index whose
+  // 4-aligned groups are 16-byte aligned when the base pointers a_ptr and b_ptr are (every
+  // multiplicity a multiple of 4); checked at run time, else one element per load.
+  bool vec = false;
+  std::string a_ptr, b_ptr;
 };
+
+// Every feature block's multiplicity is a multiple of 4: all row strides, block offsets and
+// weight offsets are then multiples of 4 elements.
+bool gemm_vec_ok(const Plan& p) {
+  for (auto& b : p.in)
+    if (b.mul % 4) return false;
+  for (auto& b : p.out)
+    if (b.mul % 4) return false;
+  return true;
+}
 
 // LDS-tiled MFMA GEMM: 64 x 64 output tile per 4-wave workgroup, K staged 32 at a time, each wave
 // a 32 x 32 quarter as 2 x 2 MFMA 16x16x4 tiles.  A K-fast B operand (stored 32 k values of one
@@ -162,10 +178,64 @@ void emit_gemm(Out& o, const GemmSpec& g) {
   }
   o.line("acc4 a00 = {0, 0, 0, 0}, a01 = {0, 0, 0, 0}, a10 = {0, 0, 0, 0}, a11 = {0, 0, 0, 0};");
   o.line("real ra[8], rb[8];");
-  // Global -> registers for the K slice starting at k0.
-  auto load = [&](const std::string& k0) {
-    o.open("");
-    o.line("const int k0_ = " + k0 + ";");
+  // 16-byte loads only where the B operand's columns are the fast index: K-fast B groups would
+  // store four k rows of one column to LDS at once and collide in its banks (measured slower,
+  // also with only the A operand vectorized).
+  const bool vec = g.vec && !g.b_kfast;
+  if (vec)
+    o.line("const bool vec_ = ((unsigned long long)" + g.a_ptr + " & 15) == 0 && ((unsigned long long)" + g.b_ptr +
+           " & 15) == 0;");
+  // Both operands' vector forms under one vec_ branch, else their element forms.
+  auto twoway = [&](const std::function<void()>& vf, const std::function<void()>& sf) {
+    if (vec) {
+      o.open("if (vec_)");
+      vf();
+      o.close();
+      o.open("else");
+      sf();
+      o.close();
+    } else {
+      o.open("");
+      sf();
+      o.close();
+    }
+  };
+  // Vector form: per operand 512 groups of 4 elements along the fast index, 2 per thread; a
+  // group that leaves the matrix is read element by element.
+  auto vgroup = [&](const std::string& dst, const std::string& at, const std::string& full,
+                    const std::string& elem_var, const std::string& elem_val, const std::string& cond) {
+    o.open("if (" + full + ")");
+    o.line("const Q4 q_ = *(const Q4*)&(" + at + ");");
+    o.line(dst + "[4 * t] = q_.a; " + dst + "[4 * t + 1] = q_.b; " + dst + "[4 * t + 2] = q_.c; " + dst +
+           "[4 * t + 3] = q_.d;");
+    o.close();
+    o.open("else");
+    o.open("for (int i = 0; i < 4; ++i)");
+    o.line("const int " + elem_var + " = " + elem_val + ";");
+    o.line(dst + "[4 * t + i] = (" + cond + ") ? (" + at + ") : R(0);");
+    o.close();
+    o.close();
+  };
+  auto vloadA = [&]() {
+    o.open("for (int t = 0; t < 2; ++t)");
+    o.line("const int v = t * 256 + tid;");
+    if (g.a_kfast) {
+      o.line("const int r = r0 + (v >> 3), kq = (v & 7) << 2, k = k0_ + kq;");
+      vgroup("ra", g.a_at, "r < M && k + 3 < ke", "k", "k0_ + kq + i", "r < M && k < ke");
+    } else {
+      o.line("const int rq = (v & 15) << 2, r = r0 + rq, k = k0_ + (v >> 4);");
+      vgroup("ra", g.a_at, "r + 3 < M && k < ke", "r", "r0 + rq + i", "r < M && k < ke");
+    }
+    o.close();
+  };
+  auto vloadB = [&]() {
+    o.open("for (int t = 0; t < 2; ++t)");
+    o.line("const int v = t * 256 + tid;");
+    o.line("const int cq = (v & 15) << 2, c = c0 + cq, k = k0_ + (v >> 4);");
+    vgroup("rb", g.b_at, F("k < ke && c + 3 < %d", g.N), "c", "c0 + cq + i", F("k < ke && c < %d", g.N));
+    o.close();
+  };
+  auto sload = [&]() {
     o.open("for (int t = 0; t < 8; ++t)");
     o.line("const int id = t * 256 + tid;");
     o.line(g.a_kfast ? "const int rr = id >> 5, kk = id & 31;" : "const int rr = id & 63, kk = id >> 6;");
@@ -178,21 +248,44 @@ void emit_gemm(Out& o, const GemmSpec& g) {
     o.line("const int c = c0 + cc, k = k0_ + kk;");
     o.line(F("rb[t] = (k < ke && c < %d) ? (", g.N) + g.b_at + ") : R(0);");
     o.close();
+  };
+  // Global -> registers for the K slice starting at k0.
+  auto load = [&](const std::string& k0) {
+    o.open("");
+    o.line("const int k0_ = " + k0 + ";");
+    twoway([&] { vloadA(); vloadB(); }, sload);
     o.close();
   };
   // Registers -> LDS buffer `buf`.
   auto store = [&](const std::string& buf) {
-    o.open("for (int t = 0; t < 8; ++t)");
-    o.line("const int id = t * 256 + tid;");
-    o.line(g.a_kfast ? "const int rr = id >> 5, kk = id & 31;" : "const int rr = id & 63, kk = id >> 6;");
-    o.line("As[" + buf + "][rr * 34 + kk] = ra[t];");
-    o.close();
-    o.open("for (int t = 0; t < 8; ++t)");
-    o.line("const int id = t * 256 + tid;");
-    o.line(g.b_kfast ? "const int cc = id >> 5, kk = id & 31;" : "const int cc = id & 63, kk = id >> 6;");
-    o.line(g.b_kfast ? "Bs[" + buf + "][kk * 80 + (cc ^ ((kk >> 1) & 15))] = rb[t];"
-                     : "Bs[" + buf + "][kk * 80 + cc] = rb[t];");
-    o.close();
+    twoway([&] {
+      o.open("for (int t = 0; t < 2; ++t)");
+      o.line("const int v = t * 256 + tid;");
+      o.open("");
+      if (g.a_kfast) {
+        o.line("const int rr = v >> 3, kq = (v & 7) << 2;");
+        o.line("for (int i = 0; i < 4; ++i) As[" + buf + "][rr * 34 + kq + i] = ra[4 * t + i];");
+      } else {
+        o.line("const int rq = (v & 15) << 2, kk = v >> 4;");
+        o.line("for (int i = 0; i < 4; ++i) As[" + buf + "][(rq + i) * 34 + kk] = ra[4 * t + i];");
+      }
+      o.close();
+      o.line("const int cq = (v & 15) << 2, kk = v >> 4;");
+      o.line("for (int i = 0; i < 4; ++i) Bs[" + buf + "][kk * 80 + cq + i] = rb[4 * t + i];");
+      o.close();
+    }, [&] {
+      o.open("for (int t = 0; t < 8; ++t)");
+      o.line("const int id = t * 256 + tid;");
+      o.line(g.a_kfast ? "const int rr = id >> 5, kk = id & 31;" : "const int rr = id & 63, kk = id >> 6;");
+      o.line("As[" + buf + "][rr * 34 + kk] = ra[t];");
+      o.close();
+      o.open("for (int t = 0; t < 8; ++t)");
+      o.line("const int id = t * 256 + tid;");
+      o.line(g.b_kfast ? "const int cc = id >> 5, kk = id & 31;" : "const int cc = id & 63, kk = id >> 6;");
+      o.line(g.b_kfast ? "Bs[" + buf + "][kk * 80 + (cc ^ ((kk >> 1) & 15))] = rb[t];"
+                       : "Bs[" + buf + "][kk * 80 + cc] = rb[t];");
+      o.close();
+    });
   };
   o.open("if (kb < ke)");
   load("kb");
@@ -247,6 +340,7 @@ void emit_gemm_reduce(Out& o, const GemmSpec& g, const std::string& args) {
 }
 
 void uvw_prelude_extra(Out& o, const Plan& p) {
+  o.line("struct __attribute__((aligned(16))) Q4 { real a, b, c, d; };  // four consecutive elements");
   if (p.dtype == CGTP_F64) {
     o.line("typedef double acc4 __attribute__((ext_vector_type(4)));");
     o.line("#define MFMA(a, b, c) __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0)");
@@ -634,6 +728,9 @@ std::string generate_uvw_source(const Plan& p, const std::string& family, std::s
       g.a_kfast = true;
       g.b_kfast = false;
       g.split = true;
+      g.vec = gemm_vec_ok(p);
+      g.a_ptr = "S";
+      g.b_ptr = "A";
       emit_gemm(o, g);
       g.store = F("out[(i64)(i0 + r / %d) * %d + %d + (r %% %d) * %d + c] = v;", s.d, p.c_out, OB.offset, s.d, OB.mul);
       emit_gemm_reduce(o, g, "real* __restrict__ out, int i0");
@@ -654,6 +751,9 @@ std::string generate_uvw_source(const Plan& p, const std::string& family, std::s
     g.a_kfast = true;
     g.b_kfast = true;
     g.split = false;
+    g.vec = gemm_vec_ok(p);
+    g.a_ptr = "gout";
+    g.b_ptr = "A";
     emit_gemm(o, g);
     GemmSpec h;  // A-bar partials = S^T mbar over a slice of rows
     h.name = F("cgtp_gemm_abar%d", s.blk);
@@ -665,6 +765,9 @@ std::string generate_uvw_source(const Plan& p, const std::string& family, std::s
     h.a_kfast = false;
     h.b_kfast = false;
     h.split = true;
+    h.vec = gemm_vec_ok(p);
+    h.a_ptr = "S";
+    h.b_ptr = "gout";
     emit_gemm(o, h);
     // A-bar += sum over row slices (fixed order), scattered into the layout of A.
     o.line("extern \"C\" __global__ void __launch_bounds__(256)");
@@ -698,14 +801,17 @@ std::string generate_uvw_source(const Plan& p, const std::string& family, std::s
     g.name = F("cgtp_gemm_xbar%d", s.blk);
     g.args = "const real* __restrict__ Z, const real* __restrict__ A, real* __restrict__ part, int j0";
     g.a_at = state_at("Z", s, zoff[bi], ZS, "r", "k");
-    g.b_at = F("bx%d(A, k, c)", s.blk);
+    g.b_at = F("A[bxi%d(k, c)]", s.blk);
     g.store = F("part[(i64)blockIdx.z * M * %d + (i64)r * %d + c] = v;", IB.mul, IB.mul);
     g.N = IB.mul;
     g.a_kfast = true;
     g.b_kfast = true;
     g.split = true;
-    o.line(F("DEV real bx%d(const real* __restrict__ A, int k, int c) { int st; const i64 b = bz%d(k, st);"
-             " return A[b + (i64)c * st]; }", s.blk, s.blk));
+    g.vec = gemm_vec_ok(p);
+    g.a_ptr = "Z";
+    g.b_ptr = "A";
+    o.line(F("DEV i64 bxi%d(int k, int c) { int st; const i64 b = bz%d(k, st); return b + (i64)c * st; }", s.blk,
+             s.blk));
     emit_gemm(o, g);
     g.store = F("gx[(i64)(j0 + r / %d) * %d + %d + (r %% %d) * %d + c] = v;", s.d, p.c_in, IB.offset, s.d, IB.mul);
     emit_gemm_reduce(o, g, "real* __restrict__ gx, int j0");
