@@ -324,6 +324,89 @@ void emit_gemm(Out& o, const GemmSpec& g) {
   o.close();
 }
 
+// GEMM of depth at most 64 (no K split): the 64 x Kd panel of A is loaded into LDS once and the
+// workgroup sweeps kSbarPanelTiles column tiles of 64, loading the next B tile into registers
+// while the current one feeds the MFMAs (same tile layout, swizzle and wave quarters as
+// emit_gemm; element loads).
+void emit_gemm_panel(Out& o, const GemmSpec& g) {
+  o.line("extern \"C\" __global__ void __launch_bounds__(256)");
+  o.open(g.name + "(" + g.args + ", int M, int Kd, int kper)");
+  o.line("__shared__ real As[2][64 * 34];");
+  o.line("__shared__ real Bs[2][32 * 80];");
+  o.line("const int tid = (int)threadIdx.x, lane = tid & 63, wv = tid >> 6;");
+  o.line("const int r0 = (int)blockIdx.x * 64, ke = Kd;");
+  o.line("(void)kper;");
+  o.line("real rb0[8], rb1[8];");
+  for (int sl = 0; sl < 2; ++sl) {
+    o.open("for (int t = 0; t < 8; ++t)");
+    o.line("const int id = t * 256 + tid;");
+    o.line(g.a_kfast ? "const int rr = id >> 5, kk = id & 31;" : "const int rr = id & 63, kk = id >> 6;");
+    o.line(F("const int r = r0 + rr, k = %d + kk;", 32 * sl));
+    o.line(F("As[%d][rr * 34 + kk] = (r < M && k < ke) ? (", sl) + g.a_at + ") : R(0);");
+    o.close();
+  }
+  auto loadB = [&](const std::string& c0) {
+    o.open("");
+    o.line("const int cb_ = " + c0 + ";");
+    for (int sl = 0; sl < 2; ++sl) {
+      o.open("for (int t = 0; t < 8; ++t)");
+      o.line("const int id = t * 256 + tid;");
+      o.line(g.b_kfast ? "const int cc = id >> 5, kk = id & 31;" : "const int cc = id & 63, kk = id >> 6;");
+      o.line(F("const int c = cb_ + cc, k = %d + kk;", 32 * sl));
+      o.line(F("rb%d[t] = (k < ke && c < %d) ? (", sl, g.N) + g.b_at + ") : R(0);");
+      o.close();
+    }
+    o.close();
+  };
+  auto storeB = [&] {
+    for (int sl = 0; sl < 2; ++sl) {
+      o.open("for (int t = 0; t < 8; ++t)");
+      o.line("const int id = t * 256 + tid;");
+      o.line(g.b_kfast ? "const int cc = id >> 5, kk = id & 31;" : "const int cc = id & 63, kk = id >> 6;");
+      o.line(g.b_kfast ? F("Bs[%d][kk * 80 + (cc ^ ((kk >> 1) & 15))] = rb%d[t];", sl, sl)
+                       : F("Bs[%d][kk * 80 + cc] = rb%d[t];", sl, sl));
+      o.close();
+    }
+  };
+  o.line(F("const int ct0 = (int)blockIdx.y * %d;", kSbarPanelTiles));
+  loadB("ct0 * 64");
+  storeB();
+  o.line("__syncthreads();");
+  o.open(F("for (int ct = 0; ct < %d; ++ct)", kSbarPanelTiles));
+  o.line("const int c0 = (ct0 + ct) * 64;");
+  o.line(F("if (c0 >= %d) break;", g.N));
+  o.line(F("const bool more = ct + 1 < %d && c0 + 64 < %d;", kSbarPanelTiles, g.N));
+  o.open("if (more)");
+  loadB("c0 + 64");
+  o.close();
+  o.line("acc4 a00 = {0, 0, 0, 0}, a01 = {0, 0, 0, 0}, a10 = {0, 0, 0, 0}, a11 = {0, 0, 0, 0};");
+  o.open("for (int s = 0; s < 16; ++s)");
+  o.line("const int cur = s >> 3, ka = (s & 7) * 4 + (lane >> 4);");
+  o.line("const real x0 = As[cur][(32 * (wv >> 1) + (lane & 15)) * 34 + ka];");
+  o.line("const real x1 = As[cur][(32 * (wv >> 1) + 16 + (lane & 15)) * 34 + ka];");
+  o.line(g.b_kfast ? "const int sw = (ka >> 1) & 15;" : "const int sw = 0;");
+  o.line("const real y0 = Bs[cur][ka * 80 + ((32 * (wv & 1) + (lane & 15)) ^ sw)];");
+  o.line("const real y1 = Bs[cur][ka * 80 + ((32 * (wv & 1) + 16 + (lane & 15)) ^ sw)];");
+  o.line("a00 = MFMA(x0, y0, a00); a01 = MFMA(x0, y1, a01); a10 = MFMA(x1, y0, a10); a11 = MFMA(x1, y1, a11);");
+  o.close();
+  o.open("for (int q = 0; q < 4; ++q)");
+  o.line("const int wr = q >> 1, wc = q & 1;");
+  o.line("const acc4 acc = q == 0 ? a00 : (q == 1 ? a01 : (q == 2 ? a10 : a11));");
+  o.open("for (int rr = 0; rr < 4; ++rr)");
+  o.line("const int r = r0 + 32 * (wv >> 1) + 16 * wr + ROWOF(lane, rr);");
+  o.line("const int c = c0 + 32 * (wv & 1) + 16 * wc + (lane & 15);");
+  o.line(F("if (r < M && c < %d) { const real v = acc[rr]; ", g.N) + g.store + " }");
+  o.close();
+  o.close();
+  o.line("__syncthreads();");
+  o.open("if (more)");
+  storeB();
+  o.line("__syncthreads();");
+  o.close();
+  o.close();
+  o.close();
+}
+
 // Fixed-order sum of the split-K partials of a GEMM (part[z][r][c], z < nsplit) and the GEMM's
 // scatter store of the result.
 void emit_gemm_reduce(Out& o, const GemmSpec& g, const std::string& args) {
@@ -754,7 +837,10 @@ std::string generate_uvw_source(const Plan& p, const std::string& family, std::s
     g.vec = gemm_vec_ok(p);
     g.a_ptr = "gout";
     g.b_ptr = "A";
-    emit_gemm(o, g);
+    if (sbar_panel(OB.mul))
+      emit_gemm_panel(o, g);
+    else
+      emit_gemm(o, g);
     GemmSpec h;  // A-bar partials = S^T mbar over a slice of rows
     h.name = F("cgtp_gemm_abar%d", s.blk);
     h.args = "const real* __restrict__ S, const real* __restrict__ gout, real* __restrict__ part, int i0";

@@ -95,6 +95,10 @@ struct UvwLayout {
 UvwLayout uvw_layout(const Plan& p);
 // Waves splitting one receiver's edge list in the fully connected state and edge kernels.
 constexpr int kMaxStripes = 4;
+// The S-bar GEMM of an output block of at most 64 channels (its whole depth) keeps the 64-row
+// panel of m-bar in LDS and sweeps kSbarPanelTiles column tiles of 64 per workgroup.
+constexpr int kSbarPanelTiles = 8;
+inline bool sbar_panel(int mul) { return mul <= 64; }
 
 // Compile (once) and fetch a kernel of a family on the current device.
 cgtp_status_t get_kernel(Plan& p, const std::string& family, const std::string& name, hipFunction_t* f,

@@ -288,7 +288,8 @@ cgtp_status_t uvw_backward(Plan& p, Graph& G, const DeviceGraph& d, const Source
         const auto& side = B.L.recv[gi];
         int M = nrec * side.d, Kd = side.mul, kper = 0;
         void* a[] = {(void*)&gout, (void*)&A, &Sb, &i0, &M, &Kd, &kper};
-        if ((st = launch3(ksb[gi], cdiv(M, 64), cdiv(side.D, 64), 1, 256, s, a, err)) != CGTP_OK) return st;
+        const int cols = sbar_panel(side.mul) ? 64 * kSbarPanelTiles : 64;
+        if ((st = launch3(ksb[gi], cdiv(M, 64), cdiv(side.D, cols), 1, 256, s, a, err)) != CGTP_OK) return st;
         if (grad_A) {
           int Ma = side.D, Ka = nrec * side.d;
           int kp = std::max(32, (Ka + kAbarSplit - 1) / kAbarSplit);

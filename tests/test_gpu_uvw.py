@@ -127,3 +127,37 @@ def test_uvw_config4_full_size_sampled():
     err = rel_err(got["A"][:, cols], gA.numpy())
     print(f"config 4 grad A (paths {pick}, all edges, Eq. 36): rel err {err:.3e}", flush=True)
     assert err <= TOL["float32"]
+
+
+@pytest.mark.parametrize("dtype", ["float32", "float64"])
+def test_uvw_gemm_tile_loads_alignment_independent(dtype):
+    """Multiplicities that are multiples of 4 let the GEMMs read their tiles in 16-byte groups
+    when the tensors are 16-byte aligned; A and grad_out passed as views one element off that
+    alignment take the element-by-element loads, which must give bit-identical results."""
+    from clebsch_gordan_tensor_receiver_amd import _lib
+    from tests.gpu_helpers import TOL, rel_err
+    spec = dict(irreps_in="8x0e+4x1o+4x2e", irreps_out="4x0e+8x1o+4x2e", mode="uvw")
+    case = make_case(1, irreps_override=spec, dtype=dtype)
+    g = _gpu(case)
+    out = g.forward(_lib.STREAMED)
+    grads = g.backward()
+
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        return v
+
+    A_off, gout_off = shifted(g.A), shifted(g.grad_out)
+    assert A_off.data_ptr() % 16 != 0 and gout_off.data_ptr() % 16 != 0
+    out_off = g.conv.forward(g.x, g.pos, g.shift, g.phi, A_off, schedule=_lib.STREAMED)
+    grads_off = g.conv.backward(g.x, g.pos, g.shift, g.phi, A_off, gout_off)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_off)
+    for k in KEYS:
+        assert torch.equal(grads[k], grads_off[k]), k
+    ref = conv.forward_conventional(case.problem, case.x, case.edge_vec, case.recv, case.send, case.phi,
+                                    case.A).numpy()
+    err = rel_err(out.cpu().numpy(), ref)
+    print(f"uvw mul%4 {dtype} forward rel err {err:.3e}", flush=True)
+    assert err <= TOL[dtype]
