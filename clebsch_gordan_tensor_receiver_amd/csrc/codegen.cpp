@@ -80,13 +80,30 @@ void emit_vz(Out& o, const Plan& p) {
   if (p.vec_g) o.line("int vz; asm(\"v_mov_b32 %0, 0\" : \"=v\"(vz));");
 }
 
-void emit_gvec_loads(Out& o, const Plan& p, int pi, const std::string& row, const std::string& tag, bool vec) {
+GStream::GStream(Out& o, const Plan& p, int pi, const std::string& row, const std::string& tag, bool stream)
+    : o_(o), p_(p), pi_(pi), row_(row), tag_(tag) {
   const Path& P = p.paths[pi];
-  if (!vec || !path_vec(P)) return;
-  const int per = p.dtype == CGTP_F64 ? 2 : 4;
-  const int n = (int(P.gpairs.size()) + per - 1) / per;
+  vec_ = path_vec(P);
+  per_ = p.dtype == CGTP_F64 ? 2 : 4;
+  n_ = (int(P.gpairs.size()) + per_ - 1) / per_;
+  if (!vec_) return;
   o.line(F("const V4* __restrict__ gv%s%d = (const V4*)(%s + %d) + vz;", tag.c_str(), pi, row.c_str(), P.g_off));
-  for (int c = 0; c < n; ++c) o.line(F("const V4 gq%s%d_%d = gv%s%d[%d];", tag.c_str(), pi, c, tag.c_str(), pi, c));
+  if (!stream)
+    while (next_ * kGvecChunk < n_) load(next_, false);
+}
+
+void GStream::load(int chunk, bool barrier) {
+  if (barrier && chunk >= 2) o_.line("__builtin_amdgcn_sched_barrier(0);");
+  for (int c = chunk * kGvecChunk; c < std::min(n_, (chunk + 1) * kGvecChunk); ++c)
+    o_.line(F("const V4 gq%s%d_%d = gv%s%d[%d];", tag_.c_str(), pi_, c, tag_.c_str(), pi_, c));
+  next_ = chunk + 1;
+}
+
+std::string GStream::ref(int t) {
+  if (!vec_) return gref(p_, pi_, t, row_, tag_, false);
+  const int chunk = t / per_ / kGvecChunk;
+  while (next_ <= chunk + 1 && next_ * kGvecChunk < n_) load(next_, true);
+  return gref(p_, pi_, t, row_, tag_, true);
 }
 
 std::string gref(const Plan& p, int pi, int t, const std::string& row, const std::string& tag, bool vec) {
@@ -762,11 +779,11 @@ void emit_bwd_recv_task(Out& o, const Plan& p, int ti, const Task& T, int col_of
         continue;
       }
       const int d3 = 2 * P.l3 + 1, ob = P.i_out;
-      emit_gvec_loads(o, p, pi, "g", "");
+      GStream gs(o, p, pi, "g", "", false);
       std::vector<bool> started(d3, false);
       for (size_t t = 0; t < P.gpairs.size(); ++t) {
         int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3;
-        const std::string G = gref(p, pi, int(t), "g", "");
+        const std::string G = gs.ref(int(t));
         if (!started[m3])
           o.line(F("real t%d_%d = %s * x%d_%d;", pi, m3, G.c_str(), P.i_in, m1));
         else

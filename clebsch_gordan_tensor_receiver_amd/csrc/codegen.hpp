@@ -56,9 +56,26 @@ constexpr int kRegBudget = 64;  // registers per lane for A coefficients of one 
 inline bool path_vec(const Path& P) { return int(P.gpairs.size()) > kVecGPairs; }
 void emit_vz(Out& o, const Plan& p);
 // `vec` false: scalar loads whatever the path size (kernels where vector loads measured slower).
-void emit_gvec_loads(Out& o, const Plan& p, int pi, const std::string& row, const std::string& tag,
-                     bool vec = true);
 std::string gref(const Plan& p, int pi, int t, const std::string& row, const std::string& tag, bool vec = true);
+// Coefficients of path pi referenced in increasing pair order t; a large path's row is read with
+// 16-byte vector loads, other paths' values are scalar references.  `stream` false: the whole row
+// is loaded up front.  `stream` true: it is read in chunks of kGvecChunk units, each loaded when
+// the one before it is first used (at most two chunks live), with a scheduling barrier before
+// each chunk that keeps the compiler from hoisting all of them to the top.
+constexpr int kGvecChunk = 4;
+class GStream {
+ public:
+  GStream(Out& o, const Plan& p, int pi, const std::string& row, const std::string& tag, bool stream);
+  std::string ref(int t);
+
+ private:
+  void load(int chunk, bool barrier);
+  Out& o_;
+  const Plan& p_;
+  int pi_, per_, n_, next_ = 0;
+  bool vec_;
+  std::string row_, tag_;
+};
 void prelude(Out& o, const Plan& p, bool dual, bool reduce);
 // Radial values of the current edge (the phi input or the edge's G row), and the radial part of
 // the edge-vector gradient (sr; needs rr = |r| and phi-bar registers <pb>0..K-1 in scope).

@@ -28,7 +28,11 @@ namespace {
 
 // A and A-tangent registers per lane of one path subset in the double backward's forward-tangent
 // and source passes (K values each per path).
-constexpr int kDfwdRegs = 32;
+constexpr int kDfwdRegs = 16;
+// Large paths' coefficient rows are streamed in the tangent forward (with one path per subset
+// this halves its registers: 25 % faster at l <= 6) but loaded whole in the receiver pass, where
+// streaming measured 5 % slower.
+constexpr bool kDfwdStream = true;
 constexpr int kDsrcRegs = 16;
 
 long double dfact2(int n) {
@@ -200,14 +204,13 @@ void emit_wwd(Out& o, const Plan& p, int pi) {
 }
 
 // T[m3] = G x and Tdot[m3] = Gdot x + G xdot of path pi, names t<pi>_<m3>, td<pi>_<m3>.
-std::vector<bool> emit_t_td(Out& o, const Plan& p, int pi, int d3) {
+std::vector<bool> emit_t_td(Out& o, const Plan& p, int pi, int d3, bool stream) {
   const Path& P = p.paths[pi];
-  emit_gvec_loads(o, p, pi, "g", "");
-  emit_gvec_loads(o, p, pi, "gd", "d");
+  GStream gs(o, p, pi, "g", "", stream), gds(o, p, pi, "gd", "d", stream);
   std::vector<bool> started(d3, false);
   for (size_t t = 0; t < P.gpairs.size(); ++t) {
     int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3;
-    const std::string G = gref(p, pi, int(t), "g", ""), Gd = gref(p, pi, int(t), "gd", "d");
+    const std::string G = gs.ref(int(t)), Gd = gds.ref(int(t));
     if (!started[m3]) {
       o.line(F("real t%d_%d = %s * x%d_%d;", pi, m3, G.c_str(), P.i_in, m1));
       o.line(F("real td%d_%d = fma(%s, x%d_%d, %s * xd%d_%d);", pi, m3, Gd.c_str(), P.i_in, m1, G.c_str(), P.i_in,
@@ -238,7 +241,7 @@ void emit_dfwd_task(Out& o, const Plan& p, int ti, const Task& T) {
     emit_dedge_loop(o, p, in_blocks_of(p, S), [&] {
       for (int pi : S) {
         emit_wwd(o, p, pi);
-        auto started = emit_t_td(o, p, pi, d3);
+        auto started = emit_t_td(o, p, pi, d3, kDfwdStream);
         for (int m = 0; m < d3; ++m)
           if (started[m]) o.line(F("acc%d = fma(wd%d, t%d_%d, fma(w%d, td%d_%d, acc%d));", m, pi, pi, m, pi, pi, m, m));
       }
@@ -281,7 +284,7 @@ void emit_drecv_task(Out& o, const Plan& p, int ti, const Task& T, int col_off, 
       const Path& P = p.paths[pi];
       const int y0 = P.l2 * P.l2;
       emit_wwd(o, p, pi);
-      auto started = emit_t_td(o, p, pi, d3);
+      auto started = emit_t_td(o, p, pi, d3, false);
       bool first = true;
       for (int m = 0; m < d3; ++m)
         if (started[m]) {
