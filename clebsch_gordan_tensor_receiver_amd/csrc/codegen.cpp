@@ -1222,10 +1222,10 @@ static std::vector<Task> make_recv_backward_tasks(const Plan& p) {
 
 static std::vector<Task> make_dbl_recv_tasks(const Plan& p) {
   // Per path the receiver pass of the double backward holds A, its tangent and the A-bar tangent
-  // accumulators (3K values per lane).
+  // accumulators (3K values per lane): one task per path up to K = 16 (two at K <= 8).
   std::vector<Task> t;
   for (const Task& f : make_forward_tasks(p))
-    for (const auto& S : a_subsets(p, f.paths, 3 * kRegBudget / 2 / 3)) t.push_back({f.group, f.cb, S});
+    for (const auto& S : a_subsets(p, f.paths, kRegBudget / 4)) t.push_back({f.group, f.cb, S});
   return t;
 }
 

@@ -29,9 +29,9 @@ namespace {
 // A and A-tangent registers per lane of one path subset in the double backward's forward-tangent
 // and source passes (K values each per path).
 constexpr int kDfwdRegs = 16;
-// Large paths' coefficient rows are streamed in the tangent forward (with one path per subset
-// this halves its registers: 25 % faster at l <= 6) but loaded whole in the receiver pass, where
-// streaming measured 5 % slower.
+// Large paths' coefficient rows are streamed in the tangent forward and the receiver pass: with
+// one path per subset (forward) or per task (receiver pass) this keeps the large l <= 6 paths off
+// the 256-VGPR ceiling (forward 25 %, receiver pass 33 % faster).
 constexpr bool kDfwdStream = true;
 constexpr int kDsrcRegs = 16;
 
@@ -284,7 +284,7 @@ void emit_drecv_task(Out& o, const Plan& p, int ti, const Task& T, int col_off, 
       const Path& P = p.paths[pi];
       const int y0 = P.l2 * P.l2;
       emit_wwd(o, p, pi);
-      auto started = emit_t_td(o, p, pi, d3, false);
+      auto started = emit_t_td(o, p, pi, d3, kDfwdStream);
       bool first = true;
       for (int m = 0; m < d3; ++m)
         if (started[m]) {
