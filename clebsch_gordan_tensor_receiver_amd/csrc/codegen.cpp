@@ -701,6 +701,10 @@ std::vector<std::pair<std::pair<int, int>, std::vector<std::pair<int, double>>>>
 // partials w Q[m2] (Eq. 22) without forming T = G x.
 constexpr int kFoldMax = 48;     // largest (m1, m2) table kept in registers
 constexpr int kRecvBudget = 176;  // registers per lane for A, the A-bar accumulators and R of one task
+// Plans with large paths (vector coefficient loads): streamed rows and kRecvLargeDiv times smaller
+// tasks in the receiver backward.
+constexpr bool kRecvStreamLarge = true;
+constexpr int kRecvLargeDiv = 4;
 
 bool folded(const Path& P) { return int(m12_pairs(P).size()) <= kFoldMax; }
 
@@ -779,7 +783,7 @@ void emit_bwd_recv_task(Out& o, const Plan& p, int ti, const Task& T, int col_of
         continue;
       }
       const int d3 = 2 * P.l3 + 1, ob = P.i_out;
-      GStream gs(o, p, pi, "g", "", false);
+      GStream gs(o, p, pi, "g", "", p.vec_g && kRecvStreamLarge);
       std::vector<bool> started(d3, false);
       for (size_t t = 0; t < P.gpairs.size(); ++t) {
         int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3;
@@ -1190,7 +1194,8 @@ static std::vector<Task> make_recv_backward_tasks(const Plan& p) {
     const int mul = p.out[p.paths[pi].i_out].mul;
     for (int cb = 0; cb * 64 < mul; ++cb) by_key[{mul, cb}].push_back(pi);
   }
-  const int budget = p.dtype == CGTP_F64 ? kRecvBudget / 2 : kRecvBudget;  // 64-bit values take two registers
+  int budget = p.dtype == CGTP_F64 ? kRecvBudget / 2 : kRecvBudget;  // 64-bit values take two registers
+  if (p.vec_g) budget /= kRecvLargeDiv;
   std::vector<std::pair<int, Task>> tasks;  // (cost, task)
   for (auto& kv : by_key) {
     std::vector<int> order = kv.second;
