@@ -72,7 +72,7 @@ def _path_table(plan):
     return rows
 
 
-def kernel_fma(plan, spec, n_edges: int, n_nodes: int, passes):
+def kernel_fma(plan, spec, n_edges: int, n_nodes: int, passes, keep_state: bool = False):
     """Algorithmic FMA per step of each kernel, from the plan's path table.
 
     Per path with C channels (uvu), K radial functions, gnz (m1, m3) pairs, p12 (m1, m2) pairs, nnz
@@ -89,7 +89,8 @@ def kernel_fma(plan, spec, n_edges: int, n_nodes: int, passes):
                       Y-bar and the first-order Y-bar, as written in the method's equations
       dsrc            C (3K + 2 gnz + 2 d1)
     Fully connected (C_in, C_out per path):
-      uvw_state       C_in (gnz + K d3) per edge, in every pass that forms S
+      uvw_state       C_in (gnz + K d3) per edge, in every pass that forms S (the forward only
+                      when the backward reads the state the forward kept)
       uvw_edge        C_in (gnz + 2 K d3 + nnz) per edge: T, phi-bar = sum Sbar T, Cbar = sum phi Sbar
                       and the Y-bar contraction
       uvw_zstate      C_out (gnz + K d1) per edge
@@ -135,7 +136,7 @@ def kernel_fma(plan, spec, n_edges: int, n_nodes: int, passes):
     bi, bo = _blocks(spec["irreps_in"]), _blocks(spec["irreps_out"])
     state = sum(bi[r["i_in"]][0] * (r["gnz"] + K * r["d3"]) for r in rows) * E
     for ps in passes:
-        if ps in ("fwds", "bwd"):
+        if ps == "fwds" or (ps == "bwd" and not keep_state):
             add("cgtp_uvw_state", state)
         for g in sorted({r["i_out"] for r in rows}):
             depth = sum(K * bi[r["i_in"]][0] for r in rows if r["i_out"] == g)
@@ -189,6 +190,9 @@ def main() -> int:
     ap.add_argument("--scratch-mib", type=int, default=0,
                     help="scratch budget of the plan in MiB (0: the library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--recompute-state", action="store_true",
+                    help="fully connected: let the backward recompute the receiver state instead of reading "
+                         "the one the forward kept (cgtp_conv_forward_keep_state)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of known size (calibrates the HBM byte counters)")
     ap.add_argument("--sweep", choices=("degree", "copies"),
@@ -267,12 +271,22 @@ def main() -> int:
                   gg_phi=torch.empty_like(phi), gg_A=torch.empty_like(A), gg_grad_out=torch.empty_like(out))
 
     phi_in = None if args.radial else phi
+    # Fully connected forward + backward: the forward keeps the receiver state for the backward.
+    keep_state = spec["mode"] == "uvw" and "bwd" in passes and not args.recompute_state
+    state = conv.state_buffer() if keep_state else None
 
     def step():
         for ps in passes:
             if ps in ("fwd", "fwds"):
                 sched = cg.CONVENTIONAL if ps == "fwd" else cg.STREAMED
-                cg.conv_forward(plan, graph, sched, x, pos, shift, phi_in, A, out, ws[ps])
+                if keep_state:
+                    cg.conv_forward_keep_state(plan, graph, x, pos, shift, phi_in, A, out, state, ws[ps])
+                else:
+                    cg.conv_forward(plan, graph, sched, x, pos, shift, phi_in, A, out, ws[ps])
+            elif ps == "bwd" and keep_state:
+                cg.conv_backward_with_state(plan, graph, x, pos, shift, phi_in, A, gout, state, grad_x=grads["x"],
+                                            grad_pos=grads["pos"], grad_edge_vec=grads["edge_vec"],
+                                            grad_phi=grads["phi"], grad_A=grads["A"], workspace=ws[ps])
             elif ps == "bwd":
                 cg.conv_backward(plan, graph, x, pos, shift, phi_in, A, gout, grad_x=grads["x"], grad_pos=grads["pos"],
                                  grad_edge_vec=grads["edge_vec"], grad_phi=grads["phi"], grad_A=grads["A"],
@@ -299,7 +313,7 @@ def main() -> int:
             step()
         torch.cuda.synchronize()
         prof = cg._lib.profile_end()
-        fma = kernel_fma(plan, spec, E, N, passes)
+        fma = kernel_fma(plan, spec, E, N, passes, keep_state)
         step_fma = sum(fma.values())
         for name, (n, ms) in prof.items():
             us_step = 1e3 * ms / args.profile_steps
@@ -349,6 +363,7 @@ def main() -> int:
         "config": {"workload": f"{desc}; {label}" + ("; gradients of x, phi, A and positions" if "bwd" in passes
                                                      else ""),
                    "n_nodes": N, "n_edges": E, "passes": list(passes), "radial_in_kernel": bool(args.radial),
+                   **({"receiver_state_kept": keep_state} if spec["mode"] == "uvw" else {}),
                    "scratch_budget_mib": args.scratch_mib or 256},
         "gflops_algorithmic": round(2.0 * step_fma / (ms_per_step * 1e-3) / 1e9, 1) if step_fma else None,
         "kernels": result_kernels,

@@ -8,5 +8,5 @@ package holds its build step (``build``) and the ctypes binding (``_lib``).
 from . import _lib  # noqa: F401
 from ._lib import (CONVENTIONAL, STREAMED, OP_BACKWARD, OP_DOUBLE_BACKWARD, OP_FORWARD,  # noqa: F401
                    CgtpError, Convolution, Graph, Plan, check_edges, conv_backward, conv_double_backward, conv_forward,
-                   layout_convert,
+                   conv_backward_with_state, conv_forward_keep_state, layout_convert, state_size,
                    workspace_size)

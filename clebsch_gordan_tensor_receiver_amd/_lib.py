@@ -27,6 +27,7 @@ EXPORTED = [
     "cgtp_plan_compile", "cgtp_plan_set_scratch_budget", "cgtp_plan_set_radial", "cgtp_graph_build", "cgtp_graph_export",
     "cgtp_graph_dims", "cgtp_graph_upload", "cgtp_graph_destroy", "cgtp_workspace_size",
     "cgtp_conv_forward", "cgtp_conv_backward", "cgtp_conv_double_backward", "cgtp_check_edges", "cgtp_layout_convert", "cgtp_error_string", "cgtp_last_error",
+    "cgtp_state_size", "cgtp_conv_forward_keep_state", "cgtp_conv_backward_with_state",
     "cgtp_profile_begin", "cgtp_profile_end", "cgtp_profile_count", "cgtp_profile_get",
 ]
 
@@ -73,6 +74,9 @@ def load() -> ctypes.CDLL:
         "cgtp_conv_forward": [P, P, I, V, V, V, V, V, V, V, Z, V],
         "cgtp_conv_backward": [P, P, V, V, V, V, V, V, V, V, V, V, V, V, Z, V],
         "cgtp_conv_double_backward": [P, P] + [V] * 18 + [Z, V],
+        "cgtp_state_size": [P, P, ctypes.POINTER(Z)],
+        "cgtp_conv_forward_keep_state": [P, P, V, V, V, V, V, V, V, Z, V, Z, V],
+        "cgtp_conv_backward_with_state": [P, P, V, V, V, V, V, V, V, Z, V, V, V, V, V, V, Z, V],
         "cgtp_check_edges": [P, P, V, V, V, Z, V, ctypes.POINTER(ctypes.c_int)],
         "cgtp_layout_convert": [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, V, V, V],
         "cgtp_profile_begin": [],
@@ -249,6 +253,31 @@ def conv_backward(plan: Plan, graph: Graph, x, pos, shift, phi, A, grad_out, gra
                                     workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+def state_size(plan: Plan, graph: Graph) -> int:
+    n = ctypes.c_size_t()
+    check(load().cgtp_state_size(plan.handle, graph.handle, ctypes.byref(n)))
+    return n.value
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def conv_forward_keep_state(plan: Plan, graph: Graph, x, pos, shift, phi, A, out, state, workspace, stream=None):
+    check(load().cgtp_conv_forward_keep_state(plan.handle, graph.handle, _ptr(x), _ptr(pos), _ptr(shift), _ptr(phi),
+                                              _ptr(A), _ptr(out), _ptr(state), _nbytes(state), _ptr(workspace),
+                                              _nbytes(workspace), _stream(stream)))
+
+
+def conv_backward_with_state(plan: Plan, graph: Graph, x, pos, shift, phi, A, grad_out, state, grad_x=None,
+                             grad_pos=None, grad_edge_vec=None, grad_phi=None, grad_A=None, workspace=None,
+                             stream=None):
+    check(load().cgtp_conv_backward_with_state(
+        plan.handle, graph.handle, _ptr(x), _ptr(pos), _ptr(shift), _ptr(phi), _ptr(A), _ptr(grad_out), _ptr(state),
+        _nbytes(state), _ptr(grad_x), _ptr(grad_pos), _ptr(grad_edge_vec), _ptr(grad_phi), _ptr(grad_A),
+        _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
 def conv_double_backward(plan: Plan, graph: Graph, x, pos, shift, phi, A, grad_out, v_x=None, v_pos=None,
                          v_edge_vec=None, v_phi=None, v_A=None, gg_x=None, gg_pos=None, gg_edge_vec=None,
                          gg_phi=None, gg_A=None, gg_grad_out=None, workspace=None, stream=None):
@@ -299,14 +328,24 @@ class Convolution:
             self._ws[op] = ws
         return ws
 
-    def forward(self, x, pos, shift, phi, A, schedule: int = CONVENTIONAL, out=None):
+    def state_buffer(self):
+        """Device buffer for the fully connected receiver state kept by forward(..., state=...)."""
+        import torch
+        return torch.empty(state_size(self.plan, self.graph), dtype=torch.uint8, device="cuda")
+
+    def forward(self, x, pos, shift, phi, A, schedule: int = CONVENTIONAL, out=None, state=None):
+        """With `state` (fully connected, streamed): also keep the receiver state for backward()."""
         import torch
         if out is None:
             out = torch.empty((self.graph.n_nodes, self.plan.info["c_out"]), dtype=self.torch_dtype, device="cuda")
-        conv_forward(self.plan, self.graph, schedule, x, pos, shift, phi, A, out, self.workspace(OP_FORWARD))
+        if state is None:
+            conv_forward(self.plan, self.graph, schedule, x, pos, shift, phi, A, out, self.workspace(OP_FORWARD))
+        else:
+            conv_forward_keep_state(self.plan, self.graph, x, pos, shift, phi, A, out, state,
+                                    self.workspace(OP_FORWARD))
         return out
 
-    def backward(self, x, pos, shift, phi, A, grad_out, want=("x", "pos", "edge_vec", "phi", "A")):
+    def backward(self, x, pos, shift, phi, A, grad_out, want=("x", "pos", "edge_vec", "phi", "A"), state=None):
         import torch
         n, e = self.graph.n_nodes, self.graph.n_edges
         info = self.plan.info
@@ -318,9 +357,14 @@ class Convolution:
             phi=torch.empty((max(e, 1), info["num_radial"]), **dt) if "phi" in want else None,
             A=torch.empty((info["num_radial"], info["n_weights"]), **dt) if "A" in want else None,
         )
-        conv_backward(self.plan, self.graph, x, pos, shift, phi, A, grad_out, grad_x=outs["x"], grad_pos=outs["pos"],
-                      grad_edge_vec=outs["edge_vec"], grad_phi=outs["phi"], grad_A=outs["A"],
-                      workspace=self.workspace(OP_BACKWARD))
+        if state is None:
+            conv_backward(self.plan, self.graph, x, pos, shift, phi, A, grad_out, grad_x=outs["x"],
+                          grad_pos=outs["pos"], grad_edge_vec=outs["edge_vec"], grad_phi=outs["phi"],
+                          grad_A=outs["A"], workspace=self.workspace(OP_BACKWARD))
+        else:
+            conv_backward_with_state(self.plan, self.graph, x, pos, shift, phi, A, grad_out, state,
+                                     grad_x=outs["x"], grad_pos=outs["pos"], grad_edge_vec=outs["edge_vec"],
+                                     grad_phi=outs["phi"], grad_A=outs["A"], workspace=self.workspace(OP_BACKWARD))
         return {k: v for k, v in outs.items() if v is not None}
 
     def double_backward(self, x, pos, shift, phi, A, grad_out, v_x=None, v_pos=None, v_edge_vec=None, v_phi=None,

@@ -362,9 +362,9 @@ cgtp_status_t cgtp_workspace_size(cgtp_plan_t plan, cgtp_graph_t g, cgtp_op_t op
   return ok();
 }
 
-cgtp_status_t cgtp_conv_forward(cgtp_plan_t plan, cgtp_graph_t g, cgtp_schedule_t schedule, const void* x,
-                                const void* pos, const void* shift, const void* phi, const void* A, void* out,
-                                void* workspace, size_t ws_bytes, void* stream) {
+static cgtp_status_t conv_forward_impl(cgtp_plan_t plan, cgtp_graph_t g, cgtp_schedule_t schedule, const void* x,
+                                       const void* pos, const void* shift, const void* phi, const void* A, void* out,
+                                       void* workspace, size_t ws_bytes, void* stream, void* state) {
   if (!plan || !g) return fail(CGTP_ERR_INVALID_ARG, "null plan or graph");
   if (!x || !pos || !A || !out) return fail(CGTP_ERR_INVALID_ARG, "null tensor argument");
   if (schedule != CGTP_STREAMED && schedule != CGTP_CONVENTIONAL) return fail(CGTP_ERR_INVALID_ARG, "bad schedule");
@@ -386,7 +386,7 @@ cgtp_status_t cgtp_conv_forward(cgtp_plan_t plan, cgtp_graph_t g, cgtp_schedule_
     if (schedule != CGTP_STREAMED)
       return fail(CGTP_ERR_UNSUPPORTED, "fully connected mode runs the streamed schedule only: the conventional one "
                                         "would materialise E x N_w edge weights");
-    st = cgtp::uvw_forward(p, G, d, x, pos, shift, phi, A, out, workspace, s0, &err);
+    st = cgtp::uvw_forward(p, G, d, x, pos, shift, phi, A, out, workspace, s0, &err, state);
     return st == CGTP_OK ? ok() : fail(st, err);
   }
   const char* fam = schedule == CGTP_STREAMED ? "fwds" : "fwd";
@@ -415,15 +415,40 @@ cgtp_status_t cgtp_conv_forward(cgtp_plan_t plan, cgtp_graph_t g, cgtp_schedule_
   return ok();
 }
 
+cgtp_status_t cgtp_conv_forward(cgtp_plan_t plan, cgtp_graph_t g, cgtp_schedule_t schedule, const void* x,
+                                const void* pos, const void* shift, const void* phi, const void* A, void* out,
+                                void* workspace, size_t ws_bytes, void* stream) {
+  return conv_forward_impl(plan, g, schedule, x, pos, shift, phi, A, out, workspace, ws_bytes, stream, nullptr);
+}
+
+cgtp_status_t cgtp_state_size(cgtp_plan_t plan, cgtp_graph_t g, size_t* bytes) {
+  if (!plan || !g || !bytes) return fail(CGTP_ERR_INVALID_ARG, "null argument");
+  if (plan->p.mode != CGTP_FULLY_CONNECTED)
+    return fail(CGTP_ERR_UNSUPPORTED, "a kept receiver state exists for the fully connected mode only");
+  *bytes = std::max<size_t>(cgtp::uvw_state_bytes(plan->p, g->g), 256);
+  return ok();
+}
+
+cgtp_status_t cgtp_conv_forward_keep_state(cgtp_plan_t plan, cgtp_graph_t g, const void* x, const void* pos,
+                                           const void* shift, const void* phi, const void* A, void* out, void* state,
+                                           size_t state_bytes, void* workspace, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  cgtp_status_t st = cgtp_state_size(plan, g, &need);
+  if (st != CGTP_OK) return st;
+  if (!state || state_bytes < need) return fail(CGTP_ERR_WORKSPACE, "state buffer too small (cgtp_state_size)");
+  return conv_forward_impl(plan, g, CGTP_STREAMED, x, pos, shift, phi, A, out, workspace, ws_bytes, stream, state);
+}
+
 }  // extern "C"
 
 
 extern "C" {
 
-cgtp_status_t cgtp_conv_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x, const void* pos, const void* shift,
-                                 const void* phi, const void* A, const void* grad_out, void* grad_x, void* grad_pos,
-                                 void* grad_edge_vec, void* grad_phi, void* grad_A, void* workspace, size_t ws_bytes,
-                                 void* stream) {
+static cgtp_status_t conv_backward_impl(cgtp_plan_t plan, cgtp_graph_t g, const void* x, const void* pos,
+                                        const void* shift, const void* phi, const void* A, const void* grad_out,
+                                        void* grad_x, void* grad_pos, void* grad_edge_vec, void* grad_phi,
+                                        void* grad_A, void* workspace, size_t ws_bytes, void* stream,
+                                        const void* state) {
   if (!plan || !g) return fail(CGTP_ERR_INVALID_ARG, "null plan or graph");
   if (!x || !pos || !A || !grad_out) return fail(CGTP_ERR_INVALID_ARG, "null input tensor");
   cgtp::Plan& p = plan->p;
@@ -443,7 +468,7 @@ cgtp_status_t cgtp_conv_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x
     return fail(st, err);
   if (p.mode == CGTP_FULLY_CONNECTED) {
     st = cgtp::uvw_backward(p, G, d, nullptr, x, pos, shift, phi, A, grad_out, grad_x, grad_pos, grad_edge_vec,
-                            grad_phi, grad_A, workspace, static_cast<hipStream_t>(stream), &err);
+                            grad_phi, grad_A, workspace, static_cast<hipStream_t>(stream), &err, state);
     return st == CGTP_OK ? ok() : fail(st, err);
   }
   BwdLayout L = bwd_layout(p, G);
@@ -521,6 +546,27 @@ cgtp_status_t cgtp_conv_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x
     if ((st = cgtp::launch(kred, unsigned((n + 63) / 64), 512, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
   }
   return ok();
+}
+
+cgtp_status_t cgtp_conv_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x, const void* pos, const void* shift,
+                                 const void* phi, const void* A, const void* grad_out, void* grad_x, void* grad_pos,
+                                 void* grad_edge_vec, void* grad_phi, void* grad_A, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+  return conv_backward_impl(plan, g, x, pos, shift, phi, A, grad_out, grad_x, grad_pos, grad_edge_vec, grad_phi,
+                            grad_A, workspace, ws_bytes, stream, nullptr);
+}
+
+cgtp_status_t cgtp_conv_backward_with_state(cgtp_plan_t plan, cgtp_graph_t g, const void* x, const void* pos,
+                                            const void* shift, const void* phi, const void* A, const void* grad_out,
+                                            const void* state, size_t state_bytes, void* grad_x, void* grad_pos,
+                                            void* grad_edge_vec, void* grad_phi, void* grad_A, void* workspace,
+                                            size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  cgtp_status_t st = cgtp_state_size(plan, g, &need);
+  if (st != CGTP_OK) return st;
+  if (!state || state_bytes < need) return fail(CGTP_ERR_WORKSPACE, "state buffer too small (cgtp_state_size)");
+  return conv_backward_impl(plan, g, x, pos, shift, phi, A, grad_out, grad_x, grad_pos, grad_edge_vec, grad_phi,
+                            grad_A, workspace, ws_bytes, stream, state);
 }
 
 cgtp_status_t cgtp_conv_double_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x, const void* pos,

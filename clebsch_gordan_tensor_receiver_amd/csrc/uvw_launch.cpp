@@ -161,9 +161,13 @@ size_t uvw_workspace(const Plan& p, const Graph& g, cgtp_op_t op) {
   return op == CGTP_OP_FORWARD ? layout_fwd(p, g).total : layout_bwd(p, g).total;
 }
 
+size_t uvw_state_bytes(const Plan& p, const Graph& g) {
+  return size_t(g.n) * size_t(uvw_layout(p).recv_stride) * p.elem();
+}
+
 cgtp_status_t uvw_forward(Plan& p, Graph& G, const DeviceGraph& d, const void* x, const void* pos, const void* shift,
                           const void* phi, const void* A, void* out, void* workspace, hipStream_t s,
-                          std::string* err) {
+                          std::string* err, void* state) {
   UvwPlanF F = layout_fwd(p, G);
   cgtp_status_t st;
   hipFunction_t kprep, kstate;
@@ -193,7 +197,8 @@ cgtp_status_t uvw_forward(Plan& p, Graph& G, const DeviceGraph& d, const void* x
     int per = (nrec + 7) / 8;
     const size_t lds_w = size_t(F.L.state_acc) * 64 * p.elem();
     const int nst = stripes(nrec, F.L.n_state_tasks, lds_w);
-    void* b[] = {(void*)&x, (void*)&phi, &Gb, (void*)&d.row_ptr, (void*)&d.col, &S, &i0, &nrec, &per, &e0};
+    void* Sc = state ? static_cast<void*>(static_cast<char*>(state) + size_t(i0) * F.L.recv_stride * p.elem()) : S;
+    void* b[] = {(void*)&x, (void*)&phi, &Gb, (void*)&d.row_ptr, (void*)&d.col, &Sc, &i0, &nrec, &per, &e0};
     if ((st = launch(kstate, unsigned(8 * F.L.n_state_tasks * per), 64 * nst, unsigned((nst - 1) * lds_w), s, b,
                      err)) != CGTP_OK)
       return st;
@@ -201,7 +206,7 @@ cgtp_status_t uvw_forward(Plan& p, Graph& G, const DeviceGraph& d, const void* x
       const auto& side = F.L.recv[gi];
       int M = nrec * side.d, Kd = side.D, kper = 0;
       int ns = gemm_split(M, side.mul, Kd, &kper);
-      void* a[] = {&S, (void*)&A, &part, &i0, &M, &Kd, &kper};
+      void* a[] = {&Sc, (void*)&A, &part, &i0, &M, &Kd, &kper};
       if ((st = launch3(kg[gi], cdiv(M, 64), cdiv(side.mul, 64), unsigned(ns), 256, s, a, err)) != CGTP_OK)
         return st;
       void* b[] = {&part, &ns, &M, &out, &i0};
@@ -215,7 +220,7 @@ cgtp_status_t uvw_forward(Plan& p, Graph& G, const DeviceGraph& d, const void* x
 cgtp_status_t uvw_backward(Plan& p, Graph& G, const DeviceGraph& d, const SourceViews* views, const void* x,
                            const void* pos, const void* shift, const void* phi, const void* A, const void* gout,
                            void* grad_x, void* grad_pos, void* grad_edge_vec, void* grad_phi, void* grad_A,
-                           void* workspace, hipStream_t s, std::string* err) {
+                           void* workspace, hipStream_t s, std::string* err, const void* state) {
   (void)views;
   UvwPlanB B = layout_bwd(p, G);
   cgtp_status_t st;
@@ -276,7 +281,10 @@ cgtp_status_t uvw_backward(Plan& p, Graph& G, const DeviceGraph& d, const Source
         void* a[] = {(void*)&pos, (void*)&shift, (void*)&d.recv, (void*)&d.col, &e0, &e1, &Gb};
         if ((st = launch(kprep, cdiv(e1 - e0, 64), 64, 0, s, a, err)) != CGTP_OK) return st;
       }
-      if (grad_A) {
+      // S of the chunk: kept by the forward, or recomputed into the workspace.
+      void* Sc = state ? const_cast<char*>(static_cast<const char*>(state)) + size_t(i0) * B.L.recv_stride * p.elem()
+                       : S;
+      if (grad_A && !state) {
         const size_t lds_w = size_t(B.L.state_acc) * 64 * p.elem();
         const int nst = stripes(nrec, B.L.n_state_tasks, lds_w);
         void* b[] = {(void*)&x, (void*)&phi, &Gb, (void*)&d.row_ptr, (void*)&d.col, &S, &i0, &nrec, &per, &e0};
@@ -295,7 +303,7 @@ cgtp_status_t uvw_backward(Plan& p, Graph& G, const DeviceGraph& d, const Source
           int kp = std::max(32, (Ka + kAbarSplit - 1) / kAbarSplit);
           kp = (kp + 31) / 32 * 32;
           int nsplit = (Ka + kp - 1) / kp;
-          void* b[] = {&S, (void*)&gout, &ap, &i0, &Ma, &Ka, &kp};
+          void* b[] = {&Sc, (void*)&gout, &ap, &i0, &Ma, &Ka, &kp};
           if ((st = launch3(kab[gi], cdiv(Ma, 64), cdiv(side.mul, 64), unsigned(nsplit), 256, s, b, err)) != CGTP_OK)
             return st;
           void* c2[] = {&ap, &nsplit, &grad_A};

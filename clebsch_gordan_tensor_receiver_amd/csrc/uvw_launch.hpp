@@ -12,12 +12,17 @@
 namespace cgtp {
 
 size_t uvw_workspace(const Plan& p, const Graph& g, cgtp_op_t op);
+// Bytes of the receiver state S of every node (node-major, the per-node layout of the state
+// kernel's output).
+size_t uvw_state_bytes(const Plan& p, const Graph& g);
+// `state` (nullable): the forward writes S of every node there instead of into the workspace.
 cgtp_status_t uvw_forward(Plan& p, Graph& G, const DeviceGraph& d, const void* x, const void* pos, const void* shift,
                           const void* phi, const void* A, void* out, void* workspace, hipStream_t s,
-                          std::string* err);
+                          std::string* err, void* state = nullptr);
+// `state` (nullable): S kept by the forward; the backward then reads it instead of recomputing it.
 cgtp_status_t uvw_backward(Plan& p, Graph& G, const DeviceGraph& d, const SourceViews* views, const void* x,
                            const void* pos, const void* shift, const void* phi, const void* A, const void* gout,
                            void* grad_x, void* grad_pos, void* grad_edge_vec, void* grad_phi, void* grad_A,
-                           void* workspace, hipStream_t s, std::string* err);
+                           void* workspace, hipStream_t s, std::string* err, const void* state = nullptr);
 
 }  // namespace cgtp

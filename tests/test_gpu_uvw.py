@@ -161,3 +161,37 @@ def test_uvw_gemm_tile_loads_alignment_independent(dtype):
     err = rel_err(out.cpu().numpy(), ref)
     print(f"uvw mul%4 {dtype} forward rel err {err:.3e}", flush=True)
     assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,budget", [("float64", 0), ("float32", 0), ("float64", 64 << 10)])
+def test_uvw_kept_state_gives_identical_results(dtype, budget):
+    """Forward keeping the receiver state and the backward reading it: bitwise the results of the
+    plain forward and of the backward that recomputes the state (also with a small scratch budget,
+    where the forward and the backward cut the receivers into different chunks)."""
+    from clebsch_gordan_tensor_receiver_amd import _lib
+    case = make_case(1, irreps_override=RAGGED, dtype=dtype)
+    g = _gpu(case)
+    if budget:
+        g.plan.set_scratch_budget(budget)
+    out = g.forward(_lib.STREAMED)
+    grads = g.backward()
+    state = g.conv.state_buffer()
+    assert state.numel() == _lib.state_size(g.plan, g.graph)
+    out_k = g.conv.forward(g.x, g.pos, g.shift, g.phi, g.A, schedule=_lib.STREAMED, state=state)
+    grads_k = g.conv.backward(g.x, g.pos, g.shift, g.phi, g.A, g.grad_out, state=state)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_k)
+    for k in KEYS:
+        assert torch.equal(grads[k], grads_k[k]), k
+    # Without grad_A the state is not read: the other gradients are unchanged.
+    part = g.conv.backward(g.x, g.pos, g.shift, g.phi, g.A, g.grad_out, want=("x", "phi"), state=state)
+    assert torch.equal(part["x"], grads["x"]) and torch.equal(part["phi"], grads["phi"])
+
+
+def test_kept_state_refused_for_channelwise_plans():
+    from clebsch_gordan_tensor_receiver_amd import _lib
+    case = make_case(1)
+    g = _gpu(case)
+    with pytest.raises(_lib.CgtpError) as e:
+        g.conv.state_buffer()
+    assert e.value.status == 2
