@@ -95,3 +95,22 @@ def test_radial_argument_rules():
         h.conv.forward(h.x, h.pos, h.shift, None, h.A)
     assert e.value.status == 1
     _ = np
+
+
+def test_fused_radial_with_kept_state():
+    """Fully connected plan with the in-kernel Gaussian basis: the receiver state kept by the
+    forward gives the same forward output and gradients, bit for bit, as the recomputing path."""
+    from clebsch_gordan_tensor_receiver_amd import _lib
+    from tests.gpu_helpers import GpuCase
+    case = make_case(1, irreps_override=RAGGED_UVW, dtype="float64")
+    g = GpuCase(case)
+    g.plan.set_radial(2, case.raw.spec["rc"])
+    out = g.conv.forward(g.x, g.pos, g.shift, None, g.A, schedule=_lib.STREAMED)
+    grads = g.conv.backward(g.x, g.pos, g.shift, None, g.A, g.grad_out)
+    state = g.conv.state_buffer()
+    out_k = g.conv.forward(g.x, g.pos, g.shift, None, g.A, schedule=_lib.STREAMED, state=state)
+    grads_k = g.conv.backward(g.x, g.pos, g.shift, None, g.A, g.grad_out, state=state)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_k)
+    for k in KEYS:
+        assert torch.equal(grads[k], grads_k[k]), k
