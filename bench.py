@@ -195,7 +195,7 @@ def main() -> int:
                          "the one the forward kept (cgtp_conv_forward_keep_state)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of known size (calibrates the HBM byte counters)")
-    ap.add_argument("--sweep", choices=("degree", "copies"),
+    ap.add_argument("--sweep", choices=("degree", "copies", "channels", "lmax"),
                     help="scaling axis of the fully connected profiles (one JSON line per point)")
     ap.add_argument("--profile", type=int, default=0, choices=(0, 1, 2, 3),
                     help="irrep profile (L_max) of the sweep; 0: all three")
@@ -375,11 +375,88 @@ def main() -> int:
     return 0
 
 
+def channelwise_sweep(torch, cg, args) -> int:
+    """Channelwise (uvu) sweeps on the 1,024-atom diamond graph, conventional forward + backward
+    (fp32, 8 radial functions): `channels` varies the multiplicity C of the l <= 3 profile
+    (C x (0e,1o,2e) -> C x (0e,1o,2e,3o), SH l <= 3); `lmax` varies L with 64 channels
+    (64 x (0..L) -> 64 x (0..L), SH l <= L, parities (-1)^l)."""
+    from workloads import CONFIGS, make_workload, normal_tensor
+    from workloads.sweeps import CHANNEL_POINTS, LMAX_POINTS, channelwise_profile
+    cfg = 2
+    base = CONFIGS[cfg]
+    w = make_workload(cfg)
+    points = CHANNEL_POINTS if args.sweep == "channels" else LMAX_POINTS
+    if args.points:
+        points = [int(v) for v in args.points.split(",")]
+    steps, warmup = max(1, min(args.steps, 20)), max(1, min(args.warmup, 3))
+    K = base["K"]
+    graph = cg.Graph(w.n_nodes, w.recv, w.send, w.image)
+    perm = graph.perm
+    N, E = w.n_nodes, graph.n_edges
+    dev = dict(dtype=torch.float32, device="cuda")
+    r32 = lambda a: a.astype(np.float32).astype(np.float64)  # noqa: E731
+    pos = torch.tensor(r32(w.pos), **dev)
+    shift = torch.tensor(r32(w.shift[perm]), **dev).contiguous()
+    phi = torch.tensor(r32(w.phi[perm]), **dev).contiguous()
+    graph.upload()
+    for pt in points:
+        irr_in, irr_sh, irr_out = channelwise_profile(args.sweep, pt)
+        spec = dict(base, irreps_in=irr_in, irreps_sh=irr_sh, irreps_out=irr_out)
+        plan = cg.Plan(irr_in, irr_sh, irr_out, "uvu", "float32", K)
+        plan.compile((cg.OP_FORWARD, cg.OP_BACKWARD))
+        info = plan.info
+        x = torch.tensor(normal_tensor(cfg, 1, (N, info["c_in"]), dtype="float32"), **dev)
+        A = torch.tensor(normal_tensor(cfg, 2, (K, info["n_weights"]), std=1.0 / np.sqrt(K), dtype="float32"), **dev)
+        gout = torch.tensor(normal_tensor(cfg, 3, (N, info["c_out"]), dtype="float32"), **dev)
+        conv = cg.Convolution(plan, graph)
+        ws_f, ws_b = conv.workspace(cg.OP_FORWARD), conv.workspace(cg.OP_BACKWARD)
+        out = torch.empty((N, info["c_out"]), **dev)
+        grads = dict(x=torch.empty_like(x), pos=torch.empty_like(pos), edge_vec=torch.empty((E, 3), **dev),
+                     phi=torch.empty_like(phi), A=torch.empty_like(A))
+
+        def step():
+            cg.conv_forward(plan, graph, cg.CONVENTIONAL, x, pos, shift, phi, A, out, ws_f)
+            cg.conv_backward(plan, graph, x, pos, shift, phi, A, gout, grad_x=grads["x"], grad_pos=grads["pos"],
+                             grad_edge_vec=grads["edge_vec"], grad_phi=grads["phi"], grad_A=grads["A"],
+                             workspace=ws_b)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / steps
+        kernels = {}
+        if args.profile_steps > 0:
+            cg._lib.profile_begin()
+            step()
+            torch.cuda.synchronize()
+            prof = cg._lib.profile_end()
+            fma = kernel_fma(plan, spec, E, N, ("fwd", "bwd"))
+            for name, (n, ms) in prof.items():
+                entry = {"us": round(1e3 * ms, 2)}
+                if name in fma and ms > 0:
+                    entry["tflops"] = round(2.0 * fma[name] / (ms * 1e-3) / 1e12, 3)
+                    entry["frac"] = round(entry["tflops"] / PEAK_ALU_TFLOPS, 4)
+                kernels[name] = entry
+        line = {"sweep": args.sweep, "point": pt, "irreps_in": irr_in, "irreps_out": irr_out,
+                "n_paths": info["n_paths"], "n_weights": info["n_weights"], "n_nodes": N, "n_edges": E,
+                "ms_fwd_bwd": round(1e3 * dt, 3), "edges_per_s_fwd_bwd": round(E / dt, 1), "steps": steps,
+                "kernels": kernels}
+        print(json.dumps(line), flush=True)
+        del plan, conv, ws_f, ws_b, out, grads, x, A, gout
+    return 0
+
+
 def sweep(torch, cg, args) -> int:
     """Scaling axis `args.sweep` of the fully connected profiles: streamed forward and backward
     (gradients of x, phi, A and positions) per point, timed separately with the library's default
     scratch budget."""
     from workloads import sweeps
+    if args.sweep in ("channels", "lmax"):
+        return channelwise_sweep(torch, cg, args)
 
     points = sweeps.DEGREES if args.sweep == "degree" else sweeps.COPIES
     if args.points:

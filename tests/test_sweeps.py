@@ -58,3 +58,18 @@ def test_workspace_is_bounded_along_the_axes(lib, axis, point):
         # slots (K x N_w per XCD group), never a multiple of E x N_w.
         assert ws <= budget + 64 * E + 8 * 4 * K * nw + (64 << 20), (op, ws)
         assert ws < 4 * E * nw / 8, (op, ws)
+
+
+@pytest.mark.parametrize("axis,points", [("channels", sweeps.CHANNEL_POINTS), ("lmax", sweeps.LMAX_POINTS)])
+def test_channelwise_sweep_profiles_match_the_oracle_paths(lib, axis, points):
+    """Channelwise sweep plans: the library's path and weight counts equal the oracle's path
+    enumeration for every point (17 paths for every multiplicity of the l <= 3 profile)."""
+    from oracle.irreps import make_problem
+    for pt in points:
+        irr_in, irr_sh, irr_out = sweeps.channelwise_profile(axis, pt)
+        prob = make_problem(irr_in, irr_sh, irr_out, "uvu")
+        plan = lib.Plan(irr_in, irr_sh, irr_out, "uvu", "float32", 8)
+        assert plan.info["n_paths"] == len(prob.paths)
+        assert plan.info["n_weights"] == prob.n_weights
+        if axis == "channels":
+            assert len(prob.paths) == 17

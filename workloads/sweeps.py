@@ -116,6 +116,20 @@ def sweep_graph(axis: str, point: int) -> SweepGraph:
     return degree_graph(point) if axis == "degree" else copies_graph(point)
 
 
+# Channelwise sweeps on the 1,024-atom diamond graph (the l <= 3 workload's graph):
+# multiplicity C of C x (0e,1o,2e) -> C x (0e,1o,2e,3o) with SH l <= 3, and L of
+# 64 x (0..L) -> 64 x (0..L) with SH l <= L (parities (-1)^l).
+CHANNEL_POINTS = (16, 32, 64, 128, 256)
+LMAX_POINTS = (1, 2, 3, 4)
+
+
+def channelwise_profile(axis: str, point: int):
+    """(irreps_in, irreps_sh, irreps_out) of a channelwise sweep point (axis "channels" or "lmax")."""
+    if axis == "channels":
+        return _alt(2, point, point), _sh(3), _alt(3, point, point)
+    return _alt(point, 64, 64), _sh(point), _alt(point, 64, 64)
+
+
 def normal(stream: int, shape, std: float = 1.0) -> np.ndarray:
     """N(0, std^2) draws rounded to float32 (kept as float64)."""
     return _rng(stream).normal(0.0, std, size=shape).astype(np.float32).astype(np.float64)
