@@ -68,7 +68,7 @@ typedef enum { CGTP_OP_FORWARD = 0, CGTP_OP_BACKWARD = 1, CGTP_OP_DOUBLE_BACKWAR
 typedef enum {
   CGTP_OK = 0,
   CGTP_ERR_INVALID_ARG = 1,    /* malformed irreps, bad sizes, null required pointer, bad CSR */
-  CGTP_ERR_UNSUPPORTED = 2,    /* valid request this build does not implement (see message)  */
+  CGTP_ERR_UNSUPPORTED = 2,    /* valid request the library does not implement (see message) */
   CGTP_ERR_WORKSPACE = 3,      /* workspace smaller than cgtp_workspace_size()                */
   CGTP_ERR_DEGENERATE_EDGE = 4,/* an edge of zero length was found by cgtp_check_edges        */
   CGTP_ERR_HIP = 5,            /* a HIP runtime call failed (message names it)                */
