@@ -325,17 +325,19 @@ cgtp_status_t cgtp_graph_upload(cgtp_graph_t g) {
 
 cgtp_status_t cgtp_graph_destroy(cgtp_graph_t g) {
   if (!g) return ok();
+  // Best-effort release on every device the graph was uploaded to (errors cannot be reported
+  // from a destructor-like call and do not leak host state).
   int cur = 0;
-  hipGetDevice(&cur);
+  (void)hipGetDevice(&cur);
   for (auto& kv : g->g.dev) {
-    hipSetDevice(kv.first);
-    hipFree(kv.second.base);
+    (void)hipSetDevice(kv.first);
+    (void)hipFree(kv.second.base);
   }
   for (auto& kv : g->g.views) {
-    hipSetDevice(kv.first.first);
-    hipFree(kv.second.base);
+    (void)hipSetDevice(kv.first.first);
+    (void)hipFree(kv.second.base);
   }
-  hipSetDevice(cur);
+  (void)hipSetDevice(cur);
   delete g;
   return ok();
 }

@@ -726,12 +726,11 @@ void emit_bwd_recv_task(Out& o, const Plan& p, int ti, const Task& T, int col_of
   o.line(F("const int u = %d + lane;", T.cb * 64));
   o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
   emit_a_loads(o, p, T.paths);
-  std::vector<std::string> aa;
-  for (int pi : T.paths)
-    for (int q = 0; q < K; ++q) {
-      o.line(F("real aa%d = R(0);", int(aa.size())));
-      aa.push_back(F("aa%d", int(aa.size())));
-    }
+  std::vector<std::string> aa;  // A-bar accumulators: K per path of the task
+  for (size_t n = 0; n < T.paths.size() * size_t(K); ++n) {
+    o.line(F("real aa%d = R(0);", int(aa.size())));
+    aa.push_back(F("aa%d", int(aa.size())));
+  }
   o.open("if (node >= 0)");
   o.line(F("const real* __restrict__ gr = gout + (i64)node * %d + uc;", p.c_out));
   for (int ob : out_blocks_of(p, T.paths)) {

@@ -120,7 +120,7 @@ cgtp_status_t device_graph(Graph& g, DeviceGraph* out, std::string* err) {
     e = hipMemcpy(c.dst, c.src->data(), c.src->size() * sizeof(int32_t), hipMemcpyHostToDevice);
     if (e != hipSuccess) {
       *err = std::string("hipMemcpy(graph): ") + hipGetErrorString(e);
-      hipFree(d.base);
+      (void)hipFree(d.base);  // already failing: release and report the first error
       return CGTP_ERR_HIP;
     }
   }
@@ -169,7 +169,7 @@ cgtp_status_t source_views(Graph& g, long long cap, const SourceViews** out, std
   }
   e = hipMemcpy(v.base, host.data(), host.size() * sizeof(int32_t), hipMemcpyHostToDevice);
   if (e != hipSuccess) {
-    hipFree(v.base);
+    (void)hipFree(v.base);  // already failing: release and report the first error
     *err = std::string("hipMemcpy(source views): ") + hipGetErrorString(e);
     return CGTP_ERR_HIP;
   }

@@ -235,10 +235,10 @@ cgtp_status_t launch_grid(hipFunction_t f, unsigned gx, unsigned gy, unsigned gz
       pname = it == g_names.end() ? "?" : it->second;
     }
   }
-  if (ea) hipEventRecord(ea, s);
+  if (ea) (void)hipEventRecord(ea, s);  // timing only: a failed record leaves that launch untimed
   hipError_t e = hipModuleLaunchKernel(f, gx, gy, gz, block, 1, 1, shmem, s, args, nullptr);
   if (eb) {
-    hipEventRecord(eb, s);
+    (void)hipEventRecord(eb, s);
     std::lock_guard<std::mutex> lock(g_prof_mu);
     g_pending.push_back({pname, ea, eb});
   }
