@@ -160,7 +160,7 @@ def generator_digest() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "clebsch_gordan_tensor_receiver_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.startswith("codegen") or name in ("plan.cpp", "plan.hpp", "kernels.hpp"):
+        if name.startswith("codegen") or name in ("plan.cpp", "plan.hpp", "kernels.hpp", "runtime.cpp"):
             with open(os.path.join(csrc, name), "rb") as fh:
                 h.update(name.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]

@@ -78,6 +78,11 @@ cgtp_status_t compile_family(Plan& p, const std::string& family, std::string* er
   int ver_major = 0, ver_minor = 0;
   hiprtcVersion(&ver_major, &ver_minor);
   std::string tag = src + "|" + std::to_string(ver_major) + "." + std::to_string(ver_minor);
+  // The runtime compiler in use is whichever libhiprtc the process bound first (a Python process
+  // that imported PyTorch-ROCm first uses the one PyTorch ships): different compilers produce
+  // different code for the same source, so the library's path is part of the cache key.
+  Dl_info rtc;
+  if (dladdr(reinterpret_cast<void*>(&hiprtcCompileProgram), &rtc) && rtc.dli_fname) tag += std::string("|") + rtc.dli_fname;
   for (int k = 0; k < kNumOptions; ++k) tag += std::string("|") + kOptions[k];
   char name[64];
   snprintf(name, sizeof name, "%016llx.co", (unsigned long long)fnv1a(tag));
