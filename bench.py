@@ -110,7 +110,7 @@ def kernel_fma(plan, spec, n_edges: int, n_nodes: int, passes, keep_state: bool 
         nnz = sum(r["nnz"] for r in rows)
         fwd = sum(r["n_weights"] * (K + r["gnz"] + min(r["d1"], r["d3"])) for r in rows) * E
         for ps in passes:
-            if ps in ("fwd", "fwds", "bwd"):
+            if ps in ("fwd", "fwds") or (ps == "bwd" and not keep_state):
                 add("cgtp_prep", nnz * E)
             if ps == "fwd":
                 add("cgtp_fwd", fwd)
@@ -191,8 +191,9 @@ def main() -> int:
                     help="scratch budget of the plan in MiB (0: the library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--recompute-state", action="store_true",
-                    help="fully connected: let the backward recompute the receiver state instead of reading "
-                         "the one the forward kept (cgtp_conv_forward_keep_state)")
+                    help="let the backward recompute its state (fully connected: the receiver state; channelwise: "
+                         "the per-edge coefficient rows) instead of reading the one the forward kept "
+                         "(cgtp_conv_forward_keep_state)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of known size (calibrates the HBM byte counters)")
     ap.add_argument("--sweep", choices=("degree", "copies", "channels", "lmax"),
@@ -271,15 +272,17 @@ def main() -> int:
                   gg_phi=torch.empty_like(phi), gg_A=torch.empty_like(A), gg_grad_out=torch.empty_like(out))
 
     phi_in = None if args.radial else phi
-    # Fully connected forward + backward: the forward keeps the receiver state for the backward.
-    keep_state = spec["mode"] == "uvw" and "bwd" in passes and not args.recompute_state
+    # Forward + backward: the forward keeps its state for the backward (fully connected: the
+    # receiver state S; channelwise: the per-edge coefficient rows of the conventional forward).
+    keep_state = "bwd" in passes and not args.recompute_state and (
+        "fwds" in passes if spec["mode"] == "uvw" else "fwd" in passes)
     state = conv.state_buffer() if keep_state else None
 
     def step():
         for ps in passes:
             if ps in ("fwd", "fwds"):
                 sched = cg.CONVENTIONAL if ps == "fwd" else cg.STREAMED
-                if keep_state:
+                if keep_state and sched == (cg.STREAMED if spec["mode"] == "uvw" else cg.CONVENTIONAL):
                     cg.conv_forward_keep_state(plan, graph, x, pos, shift, phi_in, A, out, state, ws[ps])
                 else:
                     cg.conv_forward(plan, graph, sched, x, pos, shift, phi_in, A, out, ws[ps])
@@ -363,7 +366,8 @@ def main() -> int:
         "config": {"workload": f"{desc}; {label}" + ("; gradients of x, phi, A and positions" if "bwd" in passes
                                                      else ""),
                    "n_nodes": N, "n_edges": E, "passes": list(passes), "radial_in_kernel": bool(args.radial),
-                   **({"receiver_state_kept": keep_state} if spec["mode"] == "uvw" else {}),
+                   **({"receiver_state_kept": keep_state} if spec["mode"] == "uvw" else
+                      {"edge_rows_kept": keep_state} if "bwd" in passes else {}),
                    "scratch_budget_mib": args.scratch_mib or 256},
         "gflops_algorithmic": round(2.0 * step_fma / (ms_per_step * 1e-3) / 1e9, 1) if step_fma else None,
         "kernels": result_kernels,

@@ -329,13 +329,20 @@ class Convolution:
         return ws
 
     def state_buffer(self):
-        """Device buffer for the fully connected receiver state kept by forward(..., state=...)."""
+        """Device buffer for the state kept by forward(..., state=...): the receiver state of a
+        fully connected plan, or the per-edge coefficient rows of a channelwise one."""
         import torch
         return torch.empty(state_size(self.plan, self.graph), dtype=torch.uint8, device="cuda")
 
     def forward(self, x, pos, shift, phi, A, schedule: int = CONVENTIONAL, out=None, state=None):
-        """With `state` (fully connected, streamed): also keep the receiver state for backward()."""
+        """With `state`: also keep the state for backward(); fully connected plans keep it in the
+        streamed schedule, channelwise plans in the conventional one (ValueError otherwise)."""
         import torch
+        if state is not None:
+            keeps = STREAMED if self.plan.info["mode"] == FULLY_CONNECTED else CONVENTIONAL
+            if schedule != keeps:
+                raise ValueError("this plan keeps its state in the "
+                                 + ("streamed" if keeps == STREAMED else "conventional") + " forward only")
         if out is None:
             out = torch.empty((self.graph.n_nodes, self.plan.info["c_out"]), dtype=self.torch_dtype, device="cuda")
         if state is None:

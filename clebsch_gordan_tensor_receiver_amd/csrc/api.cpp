@@ -266,6 +266,8 @@ cgtp_status_t cgtp_plan_compile(cgtp_plan_t plan, int ops) {
       fams.push_back("fwds");
     }
     if (ops & (1 << CGTP_OP_BACKWARD)) fams.push_back("bwd");
+    // Forward and backward together: also the forward that keeps its edge rows for the backward.
+    if ((ops & (1 << CGTP_OP_FORWARD)) && (ops & (1 << CGTP_OP_BACKWARD))) fams.push_back("fwdk");
     if (ops & (1 << CGTP_OP_DOUBLE_BACKWARD)) fams.push_back("dbl");
   } else {
     if (ops & (1 << CGTP_OP_DOUBLE_BACKWARD))
@@ -391,7 +393,9 @@ static cgtp_status_t conv_forward_impl(cgtp_plan_t plan, cgtp_graph_t g, cgtp_sc
     st = cgtp::uvw_forward(p, G, d, x, pos, shift, phi, A, out, workspace, s0, &err, state);
     return st == CGTP_OK ? ok() : fail(st, err);
   }
-  const char* fam = schedule == CGTP_STREAMED ? "fwds" : "fwd";
+  if (state && schedule != CGTP_CONVENTIONAL)
+    return fail(CGTP_ERR_UNSUPPORTED, "channelwise plans keep their edge rows in the conventional forward only");
+  const char* fam = state ? "fwdk" : schedule == CGTP_STREAMED ? "fwds" : "fwd";
   hipFunction_t kprep, kfwd;
   if ((st = cgtp::get_kernel(p, fam, "cgtp_prep", &kprep, &err)) != CGTP_OK) return fail(st, err);
   if ((st = cgtp::get_kernel(p, fam, schedule == CGTP_STREAMED ? "cgtp_fwd_streamed" : "cgtp_fwd", &kfwd, &err)) !=
@@ -400,8 +404,12 @@ static cgtp_status_t conv_forward_impl(cgtp_plan_t plan, cgtp_graph_t g, cgtp_sc
   hipStream_t s = static_cast<hipStream_t>(stream);
   const cgtp::TaskGroups tg = cgtp::task_groups(cgtp::forward_tasks(p));
   const int ngroup = int(tg.tasks.size());
-  void* G_ws = workspace;
-  for (auto& c : G.chunks(g_chunk_edges(p, G))) {
+  // With a state buffer every edge's row goes there, in one receiver chunk.
+  void* G_ws = state ? state : workspace;
+  const std::vector<std::pair<int, int>> fchunks =
+      !state ? G.chunks(g_chunk_edges(p, G))
+             : G.n > 0 ? std::vector<std::pair<int, int>>{{0, G.n}} : std::vector<std::pair<int, int>>{};
+  for (auto& c : fchunks) {
     int i0 = c.first, nrec = c.second - c.first;
     int e0 = G.row_ptr[c.first], e1 = G.row_ptr[c.second];
     if (e1 > e0) {
@@ -425,9 +433,11 @@ cgtp_status_t cgtp_conv_forward(cgtp_plan_t plan, cgtp_graph_t g, cgtp_schedule_
 
 cgtp_status_t cgtp_state_size(cgtp_plan_t plan, cgtp_graph_t g, size_t* bytes) {
   if (!plan || !g || !bytes) return fail(CGTP_ERR_INVALID_ARG, "null argument");
-  if (plan->p.mode != CGTP_FULLY_CONNECTED)
-    return fail(CGTP_ERR_UNSUPPORTED, "a kept receiver state exists for the fully connected mode only");
-  *bytes = std::max<size_t>(cgtp::uvw_state_bytes(plan->p, g->g), 256);
+  const cgtp::Plan& p = plan->p;
+  if (p.mode == CGTP_FULLY_CONNECTED)
+    *bytes = std::max<size_t>(cgtp::uvw_state_bytes(p, g->g), 256);
+  else  // channelwise: the backward's per-edge rows (G, then Y) of every edge
+    *bytes = std::max<size_t>(size_t(g->g.e) * size_t(cgtp::bwd_row_stride(p)) * p.elem(), 256);
   return ok();
 }
 
@@ -438,7 +448,8 @@ cgtp_status_t cgtp_conv_forward_keep_state(cgtp_plan_t plan, cgtp_graph_t g, con
   cgtp_status_t st = cgtp_state_size(plan, g, &need);
   if (st != CGTP_OK) return st;
   if (!state || state_bytes < need) return fail(CGTP_ERR_WORKSPACE, "state buffer too small (cgtp_state_size)");
-  return conv_forward_impl(plan, g, CGTP_STREAMED, x, pos, shift, phi, A, out, workspace, ws_bytes, stream, state);
+  const cgtp_schedule_t sched = plan->p.mode == CGTP_FULLY_CONNECTED ? CGTP_STREAMED : CGTP_CONVENTIONAL;
+  return conv_forward_impl(plan, g, sched, x, pos, shift, phi, A, out, workspace, ws_bytes, stream, state);
 }
 
 }  // extern "C"
@@ -507,7 +518,9 @@ static cgtp_status_t conv_backward_impl(cgtp_plan_t plan, cgtp_graph_t g, const 
   for (size_t c = 0; c < L.chunks.size(); ++c) {
     int i0 = L.chunks[c].first, nrec = L.chunks[c].second - L.chunks[c].first;
     int e0 = G.row_ptr[L.chunks[c].first], e1 = G.row_ptr[L.chunks[c].second];
-    if (e1 > e0) {
+    if (state) {  // the rows the forward kept, for every edge: this chunk's start
+      Gb = const_cast<char*>(static_cast<const char*>(state)) + size_t(e0) * size_t(cgtp::bwd_row_stride(p)) * p.elem();
+    } else if (e1 > e0) {
       void* a[] = {(void*)&pos, (void*)&shift, (void*)&d.recv, (void*)&d.col, &e0, &e1, &Gb};
       if ((st = cgtp::launch(kprep, unsigned((e1 - e0 + 63) / 64), 64, 0, s, a, &err)) != CGTP_OK)
         return fail(st, err);

@@ -501,7 +501,7 @@ void emit_wave_combine_names(Out& o, const std::vector<std::string>& names, int 
 // the receiver's edges are dealt round-robin to the fwd_split waves of the workgroup and their
 // partial sums combined in LDS.  Paths are processed in register-budgeted subsets, each
 // re-walking the edges.
-void emit_fwd_task(Out& o, const Plan& p, int ti, const Task& T) {
+void emit_fwd_task(Out& o, const Plan& p, int ti, const Task& T, int row_stride = 0) {
   const int MUL = p.out[p.paths[T.paths[0]].i_out].mul;
   const std::vector<int> obs = out_blocks_of(p, T.paths);
   o.open(F("DEV void fwd_t%d(%s, real* sm, int node, int e_base)", ti, kFwdArgs));
@@ -525,7 +525,7 @@ void emit_fwd_task(Out& o, const Plan& p, int ti, const Task& T) {
         emit_w(o, p, pi);
         emit_path_accumulate(o, p, pi, F("acc%d_", p.paths[pi].i_out));
       }
-    });
+    }, false, row_stride);
     o.close();
   }
   emit_wave_combine_names(o, accs, fwd_split(p));
@@ -1334,17 +1334,20 @@ std::string generate_source(const Plan& p, const std::string& family, std::strin
     return o.s.str();
   }
   if (p.mode != CGTP_CHANNELWISE) return generate_uvw_source(p, family, err);
-  if (family == "fwd" || family == "fwds") {
+  // fwdk: the conventional forward writing (and reading) the backward's row layout (G, then Y),
+  // so that a backward called with the rows the forward kept needs no prep of its own.
+  if (family == "fwd" || family == "fwds" || family == "fwdk") {
+    const bool keep = family == "fwdk";
     prelude(o, p, false, false);
     emit_sh(o, p.lmax);
-    emit_prep(o, p);
-    emit_check_edges(o);
+    emit_prep(o, p, keep);
+    if (!keep) emit_check_edges(o);
     bool streamed = family == "fwds";
     auto tasks = forward_tasks(p);
     int nacc = 1;
     for (int k = 0; k < int(tasks.size()); ++k) {
       if (streamed) emit_fwd_streamed_task(o, p, k, tasks[k]);
-      else emit_fwd_task(o, p, k, tasks[k]);
+      else emit_fwd_task(o, p, k, tasks[k], keep ? bwd_row_stride(p) : 0);
       int n = 0;
       for (int ob : out_blocks_of(p, tasks[k].paths)) n += p.out[ob].dim();
       nacc = std::max(nacc, n);

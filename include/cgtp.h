@@ -179,20 +179,25 @@ cgtp_status_t cgtp_conv_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x
                                  void* grad_x, void* grad_pos, void* grad_edge_vec, void* grad_phi,
                                  void* grad_A, void* workspace, size_t ws_bytes, void* stream);
 
-/* Kept receiver state (fully connected mode).  The streamed forward accumulates per receiver the
- * state S_i = sum over in-edges of phi_ij (x) CG(x_j, Y_ij) (Sobek section 4, Eqs. 32-33) and
- * the backward needs it again for grad_A = S^T grad_out (Sobek section 3.2, Eq. 19 in
- * receiver-state form).  cgtp_conv_backward recomputes S; these calls let the forward keep it
- * instead, trading cgtp_state_size bytes (node-sized: N times the state width, e.g. 71.7 KB per
- * node for 64x(0e,1o,2e) with K = 8; never edge-sized) for the recomputation.
- *   cgtp_state_size               bytes of the state buffer (UNSUPPORTED for channelwise plans)
- *   cgtp_conv_forward_keep_state  the streamed forward (as cgtp_conv_forward with
- *                                 CGTP_STREAMED) that also leaves S of every node in `state`
- *                                 (caller-owned device memory, state_bytes >= cgtp_state_size)
- *   cgtp_conv_backward_with_state as cgtp_conv_backward, reading S from `state`; the state must
- *                                 come from cgtp_conv_forward_keep_state with the same plan,
- *                                 graph, x, pos, shift and phi (A does not enter S); results are
- *                                 bitwise those of cgtp_conv_backward.
+/* Kept forward state, for a backward with the same inputs.
+ * Fully connected plans: the streamed forward accumulates per receiver the state
+ * S_i = sum over in-edges of phi_ij (x) CG(x_j, Y_ij) (Sobek section 4, Eqs. 32-33) and the
+ * backward needs it again for grad_A = S^T grad_out (Sobek section 3.2, Eq. 19 in receiver-state
+ * form); the state is node-sized (N times the state width, e.g. 71.7 KB per node for
+ * 64x(0e,1o,2e) with K = 8).
+ * Channelwise plans: the state is the per-edge row of folded coefficients G = sum c Y and the
+ * real SH Y that the forward and backward both derive from the edge vector (LunaTP section 4.3,
+ * product reuse across passes); E times the row width (about 0.9 KB per edge for the l <= 3
+ * profile in fp32), i.e. O(E), never O(E x N_w).
+ *   cgtp_state_size               bytes of the state buffer
+ *   cgtp_conv_forward_keep_state  the forward (fully connected: CGTP_STREAMED; channelwise:
+ *                                 CGTP_CONVENTIONAL, as cgtp_conv_forward) that also leaves the
+ *                                 state of every node or edge in `state` (caller-owned device
+ *                                 memory, state_bytes >= cgtp_state_size)
+ *   cgtp_conv_backward_with_state as cgtp_conv_backward, reading the state instead of recomputing
+ *                                 it; the state must come from cgtp_conv_forward_keep_state with
+ *                                 the same plan, graph, x, pos, shift and phi (A does not enter
+ *                                 it); results are bitwise those of cgtp_conv_backward.
  * WORKSPACE when `state` is NULL or smaller than cgtp_state_size; other errors as the plain
  * calls.  The workspace requirements are those of the plain calls. */
 cgtp_status_t cgtp_state_size(cgtp_plan_t plan, cgtp_graph_t g, size_t* bytes);

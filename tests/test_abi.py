@@ -184,16 +184,19 @@ def test_host_validation_before_any_device_work(lib):
                                         None) == UNSUPPORTED
     assert so.cgtp_plan_path(plan.handle, 99, (ctypes.c_int32 * 9)()) == INVALID_ARG
     assert so.cgtp_error_string(WORKSPACE) == b"workspace too small"
-    # Kept receiver state: fully connected plans only; sized N x state width; checked before the device.
-    assert so.cgtp_state_size(plan.handle, g.handle, ctypes.byref(n)) == UNSUPPORTED
+    # Kept state: channelwise plans keep E rows of whole 16-byte units; fully connected ones N x state
+    # width; buffer sizes checked before the device.
+    assert so.cgtp_state_size(plan.handle, g.handle, ctypes.byref(n)) == 0
+    rows = n.value
+    assert rows >= 256 and rows % 16 == 0
+    assert so.cgtp_conv_backward_with_state(plan.handle, g.handle, *[1] * 6, 1, rows - 1, *[None] * 5, 1, 16,
+                                            None) == WORKSPACE
     assert so.cgtp_state_size(uvw.handle, g.handle, ctypes.byref(n)) == 0
     assert n.value >= 256 and n.value % (3 * 8) == 0
     assert so.cgtp_conv_forward_keep_state(uvw.handle, g.handle, *[1] * 6, None, 0, 1, 16, None) == WORKSPACE
     assert so.cgtp_conv_forward_keep_state(uvw.handle, g.handle, *[1] * 6, 1, n.value - 1, 1, 16, None) == WORKSPACE
     assert so.cgtp_conv_backward_with_state(uvw.handle, g.handle, *[1] * 6, None, 0, *[None] * 5, 1, 16,
                                             None) == WORKSPACE
-    assert so.cgtp_conv_backward_with_state(plan.handle, g.handle, *[1] * 6, 1, 1 << 20, *[None] * 5, 1, 16,
-                                            None) == UNSUPPORTED
 
 
 def test_workspace_is_bounded_by_the_scratch_budget(lib):

@@ -113,3 +113,36 @@ def test_backward_config5_reduced_full():
     case = make_case(5, n_nodes=200)
     g = _gpu(case)
     _compare(g.backward(), _oracle_full(case), "float32", label="config 5 reduced")
+
+
+@pytest.mark.parametrize("dtype,budget,radial", [("float64", 0, 0), ("float32", 64 << 10, 0),
+                                                 ("float32", 0, 1)])
+def test_backward_with_kept_edge_rows(dtype, budget, radial):
+    """Channelwise forward keeping its per-edge coefficient rows and the backward reading them
+    instead of deriving them again: bitwise the plain forward and backward (also with a small
+    scratch budget, where the backward cuts the receivers into chunks the forward does not, and
+    with the radial basis computed in the kernels), and within tolerance of the oracle."""
+    from clebsch_gordan_tensor_receiver_amd import _lib
+    case = make_case(1, irreps_override=SMALL_L3, dtype=dtype)
+    g = _gpu(case)
+    phi = g.phi
+    if radial:
+        g.plan.set_radial(radial, case.raw.spec["rc"])
+        phi = None
+    if budget:
+        g.plan.set_scratch_budget(budget)
+    out = g.conv.forward(g.x, g.pos, g.shift, phi, g.A, schedule=_lib.CONVENTIONAL)
+    grads = g.conv.backward(g.x, g.pos, g.shift, phi, g.A, g.grad_out)
+    state = g.conv.state_buffer()
+    assert state.numel() == _lib.state_size(g.plan, g.graph)
+    out_k = g.conv.forward(g.x, g.pos, g.shift, phi, g.A, schedule=_lib.CONVENTIONAL, state=state)
+    grads_k = g.conv.backward(g.x, g.pos, g.shift, phi, g.A, g.grad_out, state=state)
+    torch.cuda.synchronize()
+    print(f"kept rows {dtype} budget {budget} radial {radial}: {state.numel()} bytes", flush=True)
+    assert torch.equal(out, out_k)
+    for k in KEYS:
+        assert torch.equal(grads[k], grads_k[k]), k
+    if not radial:
+        _compare(grads_k, _oracle_full(case), dtype, label=f"kept rows {dtype}")
+    with pytest.raises(ValueError):   # the rows are kept by the conventional forward only
+        g.conv.forward(g.x, g.pos, g.shift, phi, g.A, schedule=_lib.STREAMED, state=state)

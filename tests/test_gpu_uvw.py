@@ -188,10 +188,11 @@ def test_uvw_kept_state_gives_identical_results(dtype, budget):
     assert torch.equal(part["x"], grads["x"]) and torch.equal(part["phi"], grads["phi"])
 
 
-def test_kept_state_refused_for_channelwise_plans():
+def test_kept_state_schedule_rule():
+    """A fully connected plan keeps its receiver state in the streamed forward only."""
     from clebsch_gordan_tensor_receiver_amd import _lib
-    case = make_case(1)
+    case = make_case(1, irreps_override=RAGGED, dtype="float64")
     g = _gpu(case)
-    with pytest.raises(_lib.CgtpError) as e:
-        g.conv.state_buffer()
-    assert e.value.status == 2
+    state = g.conv.state_buffer()
+    with pytest.raises(ValueError):
+        g.conv.forward(g.x, g.pos, g.shift, g.phi, g.A, schedule=_lib.CONVENTIONAL, state=state)
