@@ -187,7 +187,7 @@ cgtp_status_t cgtp_conv_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x
  * 64x(0e,1o,2e) with K = 8).
  * Channelwise plans: the state is the per-edge row of folded coefficients G = sum c Y and the
  * real SH Y that the forward and backward both derive from the edge vector (LunaTP section 4.3,
- * product reuse across passes); E times the row width (about 0.9 KB per edge for the l <= 3
+ * product reuse across passes); E times the row width (816 bytes per edge for the l <= 3
  * profile in fp32), i.e. O(E), never O(E x N_w).
  *   cgtp_state_size               bytes of the state buffer
  *   cgtp_conv_forward_keep_state  the forward (fully connected: CGTP_STREAMED; channelwise:
