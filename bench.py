@@ -40,12 +40,18 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 DEFAULT_WORKLOAD = 2
-# Vector-ALU FMA peak without packed FP32: 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz.  The
-# build keeps packed FP32 off, so this (not the 157.3 TFLOP/s packed figure) bounds the VALU
-# kernels; the fp64 vector peak is the same 78.6 TFLOP/s.  Dense MFMA: fp32 157.3, fp64 78.6.
-PEAK_ALU_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
-PEAK_ALU_PACKED_FP32_TFLOPS = 157.3
+# Published MI355X vector peaks: fp32 157.3 TFLOP/s (counted with packed fp32 FMA, two per lane
+# per cycle), fp64 78.6.  The kernels are built without packed fp32 instructions, so the vector
+# FMA rate they can reach is 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz = 78.6 TFLOP/s in
+# either precision; both fractions are reported, and the measured FMA rate of a plain probe kernel
+# beside them.  Dense MFMA: fp32 157.3, fp64 78.6.  HBM 8 TB/s.
+PEAK_ALU_UNPACKED_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+PEAK_ALU_PUBLISHED_TFLOPS = {"float32": 157.3, "float64": 78.6}
 PEAK_MFMA_TFLOPS = {"float32": 157.3, "float64": 78.6}
+PEAK_HBM_GBS = 8000.0
+PREROLL_MS = 100.0          # untimed steps before the warm-up, so that the clocks have ramped
+PROTOCOL_MIN_MS = 250.0     # sample time of the median protocol (Sobek section 5.1)
+PROTOCOL_MIN_SAMPLES = 10
 
 PASSES = {1: ("fwd", "fwds"), 2: ("fwd", "bwd"), 3: ("fwd",), 4: ("fwds", "bwd"), 5: ("fwd", "bwd", "dbl")}
 PASS_NAMES = {"fwd": "forward (conventional)", "fwds": "forward (streamed)", "bwd": "backward",
@@ -190,6 +196,8 @@ def main() -> int:
     ap.add_argument("--scratch-mib", type=int, default=0,
                     help="scratch budget of the plan in MiB (0: the library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peak-probe", action="store_true",
+                    help="skip the measured FMA and copy ceilings (cgtp_measure_peak)")
     ap.add_argument("--recompute-state", action="store_true",
                     help="let the backward recompute its state (fully connected: the receiver state; channelwise: "
                          "the per-edge coefficient rows) instead of reading the one the forward kept "
@@ -276,6 +284,13 @@ def main() -> int:
     # receiver state S; channelwise: the per-edge coefficient rows of the conventional forward).
     keep_state = "bwd" in passes and not args.recompute_state and (
         "fwds" in passes if spec["mode"] == "uvw" else "fwd" in passes)
+    if keep_state:
+        try:
+            cg.state_size(plan, graph)
+        except cg.CgtpError as err:   # rows longer than N_w (high l): the backward recomputes them
+            if err.status != 2:
+                raise
+            keep_state = False
     state = conv.state_buffer() if keep_state else None
 
     def step():
@@ -297,16 +312,52 @@ def main() -> int:
             else:
                 cg.conv_double_backward(plan, graph, x, pos, shift, phi, A, gout, **dirs, **gg, workspace=ws[ps])
 
+    # Pre-roll: untimed steps for at least PREROLL_MS, so that the W warm-up steps and the K timed
+    # steps run at ramped clocks.  Then exactly W warm-up and K timed steps, bracketed by
+    # synchronisations; HIP events on the launch stream between the timed steps give per-step
+    # durations for the median.
+    torch.cuda.synchronize()
+    t_pre, n_pre = time.perf_counter(), 0
+    while (time.perf_counter() - t_pre) * 1e3 < PREROLL_MS or n_pre < 3:
+        step()
+        n_pre += 1
+        if n_pre % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    preroll_ms = (time.perf_counter() - t_pre) * 1e3
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    ev[0].record()
+    for k in range(args.steps):
         step()
+        ev[k + 1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = 1e3 * elapsed / args.steps
     value = E * args.steps / elapsed
+    step_ms = sorted(ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps))
+    median_ms = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * (
+        step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2])
+
+    # Median protocol of the Sobek page (section 5.1): >= 50 ms of warm-up (the pre-roll and the
+    # W steps above), then per-step event samples totalling >= 250 ms (at least 10), median.
+    samples = list(step_ms)
+    while sum(samples) < PROTOCOL_MIN_MS or len(samples) < PROTOCOL_MIN_SAMPLES:
+        batch = [torch.cuda.Event(enable_timing=True) for _ in range(9)]
+        batch[0].record()
+        for k in range(8):
+            step()
+            batch[k + 1].record()
+        torch.cuda.synchronize()
+        samples += [batch[k].elapsed_time(batch[k + 1]) for k in range(8)]
+    samples.sort()
+    proto_median = samples[len(samples) // 2]
+    protocol = {"warmup_ms": round(preroll_ms + args.warmup * ms_per_step, 1), "samples": len(samples),
+                "sample_ms_total": round(sum(samples), 1), "median_ms_per_step": round(proto_median, 4),
+                "edges_per_s_median": round(E / (proto_median * 1e-3), 1)}
 
     # Per-kernel durations from HIP events around each launch (a separate region).
     result_kernels, roofline, step_fma = {}, None, 0.0
@@ -328,14 +379,19 @@ def main() -> int:
         dominant = max(prof, key=lambda k: prof[k][1])
         d = result_kernels[dominant]
         mfma = dominant.startswith("cgtp_gemm")
-        peak = PEAK_MFMA_TFLOPS[dtype] if mfma else PEAK_ALU_TFLOPS
+        peak = PEAK_MFMA_TFLOPS[dtype] if mfma else PEAK_ALU_PUBLISHED_TFLOPS[dtype]
         achieved = d.get("tflops")
         roofline = {"kernel": dominant, "bound": "mfma" if mfma else "alu", "achieved": achieved,
                     "peak": round(peak, 1), "unit": "TFLOP/s",
                     "frac": round(achieved / peak, 4) if achieved else None,
                     "traffic": recorded_traffic(dominant) if cfg == DEFAULT_WORKLOAD else None}
-        if not mfma and dtype == "float32" and achieved:
-            roofline["frac_of_packed_fp32_peak"] = round(achieved / PEAK_ALU_PACKED_FP32_TFLOPS, 4)
+        if not mfma and achieved:
+            roofline["peak_unpacked_fma"] = round(PEAK_ALU_UNPACKED_TFLOPS, 1)
+            roofline["frac_of_unpacked_fma_peak"] = round(achieved / PEAK_ALU_UNPACKED_TFLOPS, 4)
+            if not args.no_peak_probe:
+                meas = measured_peaks(torch, cg, dtype)
+                roofline["measured_peak"] = meas
+                roofline["frac_of_measured_fma_peak"] = round(achieved / meas["fma_tflops"], 4)
 
     desc = {2: "1,024-atom perturbed diamond (4x4x8 cells, a=3.57 A, sigma 0.05 A), cutoff 5 A; "
                "128x0e+128x1o+128x2e -> 128x0e+128x1o+128x2e+128x3o, SH lmax 3, channelwise, "
@@ -358,6 +414,9 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "median_ms_per_step": round(median_ms, 4),
+        "preroll": {"steps": n_pre, "ms": round(preroll_ms, 1)},
+        "protocol": protocol,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -443,7 +502,7 @@ def channelwise_sweep(torch, cg, args) -> int:
                 entry = {"us": round(1e3 * ms, 2)}
                 if name in fma and ms > 0:
                     entry["tflops"] = round(2.0 * fma[name] / (ms * 1e-3) / 1e12, 3)
-                    entry["frac"] = round(entry["tflops"] / PEAK_ALU_TFLOPS, 4)
+                    entry["frac"] = round(entry["tflops"] / PEAK_ALU_UNPACKED_TFLOPS, 4)
                 kernels[name] = entry
         line = {"sweep": args.sweep, "point": pt, "irreps_in": irr_in, "irreps_out": irr_out,
                 "n_paths": info["n_paths"], "n_weights": info["n_weights"], "n_nodes": N, "n_edges": E,
@@ -539,6 +598,22 @@ def sweep(torch, cg, args) -> int:
 COPY_BYTES = 256 << 20
 
 
+def measured_peaks(torch, cg, dtype):
+    """Achievable ceilings on this device from the library's probe kernels: the FMA rate of the
+    kernels' precision (no packed fp32) and the copy bandwidth over 2 x 512 MiB (read + write)."""
+    lib = cg._lib
+    small = torch.zeros(8, dtype=torch.float64, device="cuda")
+    kind = lib.PEAK_FMA_F64 if dtype == "float64" else lib.PEAK_FMA_F32
+    fma_best, fma_med = lib.measure_peak(kind, small, reps=5)
+    src = torch.ones(512 << 18, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    bw_best, bw_med = lib.measure_peak(lib.PEAK_COPY, dst, src, reps=5)
+    del src, dst
+    return {"fma_tflops": round(fma_best, 2), "fma_tflops_median": round(fma_med, 2),
+            "copy_gbs": round(bw_best, 1), "copy_gbs_median": round(bw_med, 1),
+            "copy_frac_of_8tbs": round(bw_best / PEAK_HBM_GBS, 4)}
+
+
 def copy_probe(torch) -> int:
     """Five copies of a 256 MiB buffer: each reads and writes COPY_BYTES of HBM.  The FETCH_SIZE and
     WRITE_SIZE counters of these dispatches, divided by COPY_BYTES, give the factors that turn the
@@ -580,16 +655,47 @@ def cpu_baseline(w, plan, perm, x_h, A_h, g_h, out, grads):
     m = oconv.forward_conventional(problem, x_h, ev, recv, send, phi, A_h)
     b = oconv.backward(problem, x_h, ev, recv, send, phi, A_h, g_h, n_nodes=w.n_nodes)
     dt = time.perf_counter() - t0
+    times = [dt]
+    for _ in range(2):      # median of three runs
+        t1 = time.perf_counter()
+        ev = oconv.edge_vectors(pos, shift, recv, send)
+        oconv.forward_conventional(problem, x_h, ev, recv, send, phi, A_h)
+        oconv.backward(problem, x_h, ev, recv, send, phi, A_h, g_h, n_nodes=w.n_nodes)
+        times.append(time.perf_counter() - t1)
+    times.sort()
+    dt_med = times[1]
     rel = lambda a, r: float(np.abs(a - r).max() / np.abs(r).max())  # noqa: E731
+    # x-bar and pos-bar of 8 seeded nodes: the oracle backward over every edge that touches them
+    # (their in- and out-edges), outside the timed baseline.
+    inside = np.unique(np.random.default_rng(2).choice(w.n_nodes, 8, replace=False))
+    touch = np.nonzero(np.isin(w.recv[operm], inside) | np.isin(w.send[operm], inside))[0]
+    te = operm[touch]
+    bn = oconv.backward(problem, x_h, oconv.edge_vectors(pos, r32(w.shift[te]), w.recv[te], w.send[te]),
+                        w.recv[te], w.send[te], r32(w.phi[te]), A_h, g_h, n_nodes=w.n_nodes)
     parity = {
         "forward_rows": rel(out.cpu().numpy()[:n_slice], m.numpy()[:n_slice]),
         "grad_phi_edges": rel(grads["phi"].cpu().numpy()[:e_hi], b["phi"].numpy()),
         "grad_edge_vec_edges": rel(grads["edge_vec"].cpu().numpy()[:e_hi], b["edge_vec"].numpy()),
+        "grad_x_nodes": rel(grads["x"].cpu().numpy()[inside], bn["x"].numpy()[inside]),
+        "grad_pos_nodes": rel(grads["pos"].cpu().numpy()[inside], bn["pos"].numpy()[inside]),
+        "nodes_checked": [int(v) for v in inside],
         "tolerance": 1e-5,
     }
-    baseline = {"value": round(e_hi / dt, 1), "unit": "edges/s", "cores": torch.get_num_threads(), "kind": "oracle",
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    baseline = {"value": round(e_hi / dt_med, 1), "unit": "edges/s", "cores": torch.get_num_threads(),
+                "kind": "oracle",
                 "sample": f"receivers 0..{n_slice - 1} of the workload with their {e_hi} incoming edges, "
-                          f"float64 forward + backward, {dt:.1f} s", "host_cpus": os.cpu_count()}
+                          f"float64 forward + backward, median of 3 runs ({', '.join(f'{t:.1f}' for t in times)} s)",
+                "host_cpus": os.cpu_count(), "cpu_model": cpu_model,
+                "threads_env": {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "MKL_NUM_THREADS")}}
     assert np.array_equal(perm[:e_hi], sel), "library and oracle CSR orders differ"
     return baseline, parity
 

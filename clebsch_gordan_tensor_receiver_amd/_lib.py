@@ -28,7 +28,7 @@ EXPORTED = [
     "cgtp_graph_dims", "cgtp_graph_upload", "cgtp_graph_destroy", "cgtp_workspace_size",
     "cgtp_conv_forward", "cgtp_conv_backward", "cgtp_conv_double_backward", "cgtp_check_edges", "cgtp_layout_convert", "cgtp_error_string", "cgtp_last_error",
     "cgtp_state_size", "cgtp_conv_forward_keep_state", "cgtp_conv_backward_with_state",
-    "cgtp_profile_begin", "cgtp_profile_end", "cgtp_profile_count", "cgtp_profile_get",
+    "cgtp_profile_begin", "cgtp_profile_end", "cgtp_profile_count", "cgtp_profile_get", "cgtp_measure_peak",
 ]
 
 
@@ -84,6 +84,7 @@ def load() -> ctypes.CDLL:
         "cgtp_profile_count": [],
         "cgtp_profile_get": [I, ctypes.c_char_p, I, ctypes.POINTER(ctypes.c_longlong),
                              ctypes.POINTER(ctypes.c_double)],
+        "cgtp_measure_peak": [I, V, V, Z, I, V, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -224,6 +225,19 @@ def profile_end():
         check(lib.cgtp_profile_get(k, buf, 128, ctypes.byref(n), ctypes.byref(ms)))
         out[buf.value.decode()] = (int(n.value), float(ms.value))
     return out
+
+
+PEAK_FMA_F32, PEAK_FMA_F64, PEAK_COPY = 0, 1, 2
+
+
+def measure_peak(kind: int, dst, src=None, reps: int = 5, stream=None):
+    """Measured device ceiling (cgtp_measure_peak): (best, median) in TFLOP/s (kinds 0, 1) or GB/s
+    (kind 2, a copy of src into dst, both device tensors of the same byte size)."""
+    best, med = ctypes.c_double(), ctypes.c_double()
+    nbytes = dst.numel() * dst.element_size()
+    check(load().cgtp_measure_peak(int(kind), _ptr(dst), _ptr(src), nbytes if kind == PEAK_COPY else 0, int(reps),
+                                   _stream(stream), ctypes.byref(best), ctypes.byref(med)))
+    return float(best.value), float(med.value)
 
 
 def workspace_size(plan: Plan, graph: Graph, op: int) -> int:

@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "cgtp.h"
+#include "errors.hpp"
 #include "graph.hpp"
 #include "kernels.hpp"
 #include "plan.hpp"
@@ -54,14 +55,15 @@ long long max_chunk_edges(const cgtp::Graph& g, const std::vector<std::pair<int,
 constexpr int kSrcSplit = 2;    // waves per sender in the source backward
 constexpr int kRecvGroup = 4;   // receivers (one wave each) per workgroup in the receiver backward
 
-// Workspace plan of a backward call.
+// Workspace plan of a backward or double-backward call.
 struct BwdLayout {
   long long cap = 0;            // edges per receiver chunk
+  long long rcap = 0;           // receivers per chunk (bounds the A-bar partial slots)
   std::vector<std::pair<int, int>> chunks;
   int ntask_r = 0, ntask_s = 0, V = 0, row = 0;
   int nslot = 0;                // A-bar partial slots (max over chunks)
   long long emax = 0;           // edges of the largest chunk (stride of the edge partials)
-  size_t g_off = 0, ep_off = 0, ap_off = 0, gev_off = 0, total = 0;
+  size_t g_off = 0, ep_off = 0, ap_off = 0, gev_off = 0, sb_off = 0, total = 0;
 };
 
 // Receivers per XCD and receiver groups per XCD of a chunk; the groups are the A-bar slots.
@@ -70,17 +72,32 @@ void chunk_geometry(int nrec, int* per, int* nch) {
   *nch = (*per + kRecvGroup - 1) / kRecvGroup;
 }
 
-BwdLayout bwd_layout(const cgtp::Plan& p, const cgtp::Graph& g) {
+// Shared by the backward (grow = G + Y values per edge) and the double backward (grow = G and its
+// tangent).  The scratch budget covers the per-edge rows, the edge partials and the A-bar slots
+// (K x N_w values each, one per workgroup of 4 receivers).  It is split between the two in the
+// ratio of their cost per receiver at the graph's mean in-degree: the slot share caps the
+// receivers per chunk, the row share the edges per chunk, so that neither grows with the other
+// (a low-degree graph has many receivers per edge).  Beyond the budget the workspace holds E x 3
+// edge-vector values and, with several chunks, the begin/end bounds of each sender's source-CSR
+// run (2 N int32).
+BwdLayout chunked_layout(const cgtp::Plan& p, const cgtp::Graph& g, int grow, int row, int ntask_r) {
   BwdLayout L;
-  L.ntask_r = int(cgtp::recv_backward_tasks(p).size());
+  L.ntask_r = ntask_r;
   L.ntask_s = int(cgtp::source_tasks(p).size());
   L.V = 0;
-  L.row = cgtp::recv_partial_row(p);
-  const int grow = cgtp::bwd_row_stride(p);
+  L.row = row;
+  const size_t slot_bytes = size_t(p.K) * size_t(p.n_w) * p.elem();
   long long row_bytes = (long long)(grow + L.row) * (long long)p.elem();
-  L.cap = std::max<long long>(std::max<long long>(1, (long long)(p.scratch_budget / size_t(row_bytes))),
-                              g.max_in_degree);
-  L.chunks = g.chunks(L.cap);
+  const double deg = g.n > 0 ? double(g.e) / double(g.n) : 1.0;
+  const double per_recv_slots = double(slot_bytes) / kRecvGroup, per_recv_rows = deg * double(row_bytes);
+  const double frac = std::min(7.0 / 8.0, std::max(1.0 / 16.0, per_recv_slots / (per_recv_slots + per_recv_rows)));
+  const size_t slot_share = size_t(frac * double(p.scratch_budget));
+  const long long nch_max = std::max<long long>(1, (long long)(slot_share / slot_bytes) / 8);
+  L.rcap = 8LL * kRecvGroup * nch_max;
+  const size_t slot_area = size_t(8 * nch_max) * slot_bytes;
+  const size_t rest = p.scratch_budget > slot_area ? p.scratch_budget - slot_area : 0;
+  L.cap = std::max<long long>(std::max<long long>(1, (long long)(rest / size_t(row_bytes))), g.max_in_degree);
+  L.chunks = g.chunks(L.cap, L.rcap);
   long long emax = std::max<long long>(1, max_chunk_edges(g, L.chunks));
   L.emax = emax;
   for (auto& c : L.chunks) {
@@ -94,43 +111,46 @@ BwdLayout bwd_layout(const cgtp::Plan& p, const cgtp::Graph& g) {
   L.ep_off = off;
   off += align256(size_t((emax + 63) / 64 * 64) * size_t(L.row) * p.elem());  // tiles of 64 edges
   L.ap_off = off;
-  off += align256(size_t(L.nslot) * size_t(p.K) * size_t(p.n_w) * p.elem());
+  off += align256(size_t(L.nslot) * slot_bytes);
   L.gev_off = off;
   off += align256(size_t(std::max(g.e, 1)) * 3 * p.elem());
+  L.sb_off = off;
+  if (L.chunks.size() > 1) off += align256(2 * size_t(g.n) * sizeof(int32_t));
   L.total = off;
   return L;
 }
 
-// Workspace plan of a double-backward call: G and Gdot rows (2 g_stride per edge), the edge
-// partials of the receiver pass, A-bar-dot slots and an edge-vector buffer.
+BwdLayout bwd_layout(const cgtp::Plan& p, const cgtp::Graph& g) {
+  return chunked_layout(p, g, cgtp::bwd_row_stride(p), cgtp::recv_partial_row(p),
+                        int(cgtp::recv_backward_tasks(p).size()));
+}
+
+// Double backward: G and Gdot rows (2 g_stride per edge), the edge partials of the receiver pass,
+// A-bar-dot slots, an edge-vector buffer.
 BwdLayout dbl_layout(const cgtp::Plan& p, const cgtp::Graph& g) {
-  BwdLayout L;
-  L.ntask_r = int(cgtp::dbl_recv_tasks(p).size());
-  L.ntask_s = int(cgtp::source_tasks(p).size());
-  L.V = 0;
-  L.row = cgtp::dbl_partial_row(p);
-  long long row_bytes = (long long)(2 * p.g_stride + L.row) * (long long)p.elem();
-  L.cap = std::max<long long>(std::max<long long>(1, (long long)(p.scratch_budget / size_t(row_bytes))),
-                              g.max_in_degree);
-  L.chunks = g.chunks(L.cap);
-  long long emax = std::max<long long>(1, max_chunk_edges(g, L.chunks));
-  L.emax = emax;
-  for (auto& c : L.chunks) {
-    int per, nch;
-    chunk_geometry(c.second - c.first, &per, &nch);
-    L.nslot = std::max(L.nslot, 8 * nch);
+  return chunked_layout(p, g, 2 * p.g_stride, cgtp::dbl_partial_row(p), int(cgtp::dbl_recv_tasks(p).size()));
+}
+
+// Begin/end bounds of every sender's out-edges inside receiver chunk c, for the source passes.
+// One chunk: the whole source CSR (src_ptr and src_ptr + 1).  Several: computed on the device
+// into the workspace (cgtp_src_bounds), in stream order before the chunk's source pass.
+cgtp_status_t source_bounds(cgtp::Plan& p, const char* fam, const cgtp::Graph& G, const cgtp::DeviceGraph& d,
+                            const BwdLayout& L, size_t c, char* ws, hipStream_t s, void** beg, void** end,
+                            std::string* err) {
+  if (L.chunks.size() == 1) {
+    *beg = d.src_ptr;
+    *end = d.src_ptr + 1;
+    return CGTP_OK;
   }
-  size_t off = 0;
-  L.g_off = off;
-  off += align256(size_t(emax) * size_t(2 * p.g_stride) * p.elem());
-  L.ep_off = off;
-  off += align256(size_t((emax + 63) / 64 * 64) * size_t(L.row) * p.elem());  // tiles of 64 edges
-  L.ap_off = off;
-  off += align256(size_t(L.nslot) * size_t(p.K) * size_t(p.n_w) * p.elem());
-  L.gev_off = off;
-  off += align256(size_t(std::max(g.e, 1)) * 3 * p.elem());
-  L.total = off;
-  return L;
+  hipFunction_t kb;
+  cgtp_status_t st = cgtp::get_kernel(p, fam, "cgtp_src_bounds", &kb, err);
+  if (st != CGTP_OK) return st;
+  int32_t* b = reinterpret_cast<int32_t*>(ws + L.sb_off);
+  *beg = b;
+  *end = b + G.n;
+  int n = G.n, e0 = G.row_ptr[L.chunks[c].first], e1 = G.row_ptr[L.chunks[c].second];
+  void* a[] = {(void*)&d.src_ptr, (void*)&d.src_edge, &n, &e0, &e1, beg, end};
+  return cgtp::launch(kb, unsigned((n + 255) / 256), 256, 0, s, a, err);
 }
 
 // Feature blocks that no path reaches (output side) or leaves (input side) are not written by
@@ -151,6 +171,13 @@ cgtp_status_t zero_unreached(cgtp::Plan& p, void* buf, int n, bool out_side, hip
 }
 
 }  // namespace
+
+namespace cgtp {
+cgtp_status_t set_error(cgtp_status_t status, const std::string& message) {
+  g_last_error = message;
+  return status;
+}
+}  // namespace cgtp
 
 extern "C" {
 
@@ -335,10 +362,6 @@ cgtp_status_t cgtp_graph_destroy(cgtp_graph_t g) {
     (void)hipSetDevice(kv.first);
     (void)hipFree(kv.second.base);
   }
-  for (auto& kv : g->g.views) {
-    (void)hipSetDevice(kv.first.first);
-    (void)hipFree(kv.second.base);
-  }
   (void)hipSetDevice(cur);
   delete g;
   return ok();
@@ -436,8 +459,16 @@ cgtp_status_t cgtp_state_size(cgtp_plan_t plan, cgtp_graph_t g, size_t* bytes) {
   const cgtp::Plan& p = plan->p;
   if (p.mode == CGTP_FULLY_CONNECTED)
     *bytes = std::max<size_t>(cgtp::uvw_state_bytes(p, g->g), 256);
-  else  // channelwise: the backward's per-edge rows (G, then Y) of every edge
+  else {  // channelwise: the backward's per-edge rows (G, then Y) of every edge
+    // A row longer than the N_w edge weights would make the kept state larger than the E x N_w
+    // weight tensor the streamed design exists to avoid (high-l plans: 5,196 values per edge
+    // against N_w = 3,392 at l <= 6 with 32 channels); such plans recompute the rows instead.
+    if (cgtp::bwd_row_stride(p) > p.n_w)
+      return fail(CGTP_ERR_UNSUPPORTED, "the per-edge rows (" + std::to_string(cgtp::bwd_row_stride(p)) +
+                                            " values) are longer than the N_w = " + std::to_string(p.n_w) +
+                                            " edge weights: keeping them is refused, the backward recomputes them");
     *bytes = std::max<size_t>(size_t(g->g.e) * size_t(cgtp::bwd_row_stride(p)) * p.elem(), 256);
+  }
   return ok();
 }
 
@@ -480,13 +511,11 @@ static cgtp_status_t conv_backward_impl(cgtp_plan_t plan, cgtp_graph_t g, const 
   if (grad_x && (st = zero_unreached(p, grad_x, G.n, false, static_cast<hipStream_t>(stream), &err)) != CGTP_OK)
     return fail(st, err);
   if (p.mode == CGTP_FULLY_CONNECTED) {
-    st = cgtp::uvw_backward(p, G, d, nullptr, x, pos, shift, phi, A, grad_out, grad_x, grad_pos, grad_edge_vec,
+    st = cgtp::uvw_backward(p, G, d, x, pos, shift, phi, A, grad_out, grad_x, grad_pos, grad_edge_vec,
                             grad_phi, grad_A, workspace, static_cast<hipStream_t>(stream), &err, state);
     return st == CGTP_OK ? ok() : fail(st, err);
   }
   BwdLayout L = bwd_layout(p, G);
-  const cgtp::SourceViews* views = nullptr;
-  if (grad_x && (st = cgtp::source_views(G, L.cap, &views, &err)) != CGTP_OK) return fail(st, err);
   hipFunction_t kzero, kprep, krecv, ksrc, kfinal, kpos, kred;
   const char* fam = "bwd";
   if ((st = cgtp::get_kernel(p, fam, "cgtp_fill_zero", &kzero, &err)) != CGTP_OK ||
@@ -535,10 +564,10 @@ static cgtp_status_t conv_backward_impl(cgtp_plan_t plan, cgtp_graph_t g, const 
     }
     if (grad_x) {
       int n = G.n, per = (G.n + 7) / 8, acc = c > 0 ? 1 : 0;
-      void* sp = static_cast<int32_t*>(views->base) + views->ptr_off[c];
-      void* se = static_cast<int32_t*>(views->base) + views->edge_off[c];
-      void* a[] = {(void*)&phi, (void*)&A, &Gb, (void*)&grad_out, (void*)&d.recv, &sp, &se, &grad_x, &n, &per, &e0,
-                   &acc};
+      void *sb = nullptr, *se = nullptr;
+      if ((st = source_bounds(p, fam, G, d, L, c, ws, s, &sb, &se, &err)) != CGTP_OK) return fail(st, err);
+      void* a[] = {(void*)&phi, (void*)&A, &Gb, (void*)&grad_out, (void*)&d.recv, &sb, &se, (void*)&d.src_edge,
+                   &grad_x, &n, &per, &e0, &acc};
       if ((st = cgtp::launch(ksrc, unsigned(8 * tsrc.tasks.size() * per), 64 * kSrcSplit * tsrc.ncb, 0, s, a, &err)) !=
           CGTP_OK)
         return fail(st, err);
@@ -608,8 +637,6 @@ cgtp_status_t cgtp_conv_double_backward(cgtp_plan_t plan, cgtp_graph_t g, const 
   if (gg_x && (st = zero_unreached(p, gg_x, G.n, false, s, &err)) != CGTP_OK) return fail(st, err);
   if (gg_grad_out && (st = zero_unreached(p, gg_grad_out, G.n, true, s, &err)) != CGTP_OK) return fail(st, err);
   BwdLayout L = dbl_layout(p, G);
-  const cgtp::SourceViews* views = nullptr;
-  if (gg_x && (st = cgtp::source_views(G, L.cap, &views, &err)) != CGTP_OK) return fail(st, err);
   hipFunction_t kzero, kprep, kfwd, krecv, ksrc, kfinal, kpos, kred;
   const char* fam = "dbl";
   if ((st = cgtp::get_kernel(p, fam, "cgtp_fill_zero", &kzero, &err)) != CGTP_OK ||
@@ -675,10 +702,10 @@ cgtp_status_t cgtp_conv_double_backward(cgtp_plan_t plan, cgtp_graph_t g, const 
     }
     if (gg_x) {
       int n = G.n, per = (G.n + 7) / 8, acc = c > 0 ? 1 : 0;
-      void* sp = static_cast<int32_t*>(views->base) + views->ptr_off[c];
-      void* se = static_cast<int32_t*>(views->base) + views->edge_off[c];
-      void* a[] = {(void*)&phi, (void*)&vphi, (void*)&A, (void*)&vA, &Gb, (void*)&grad_out, (void*)&d.recv, &sp, &se,
-                   &gg_x, psphi, psA, &n, &per, &e0, &acc};
+      void *sb = nullptr, *se = nullptr;
+      if ((st = source_bounds(p, fam, G, d, L, c, ws, s, &sb, &se, &err)) != CGTP_OK) return fail(st, err);
+      void* a[] = {(void*)&phi, (void*)&vphi, (void*)&A, (void*)&vA, &Gb, (void*)&grad_out, (void*)&d.recv, &sb, &se,
+                   (void*)&d.src_edge, &gg_x, psphi, psA, &n, &per, &e0, &acc};
       if ((st = cgtp::launch(ksrc, unsigned(8 * nt_s * per), 64, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
     }
     if (need_edge && e1 > e0) {

@@ -878,8 +878,8 @@ void emit_recv_dispatch(Out& o, const Plan& p, int ntask) {
 
 const char* kSrcArgs =
     "const real* __restrict__ phi, const real* __restrict__ A, const real* __restrict__ G,"
-    " const real* __restrict__ gout, const int* __restrict__ recv, const int* __restrict__ src_ptr,"
-    " const int* __restrict__ src_edge, real* __restrict__ gx";
+    " const real* __restrict__ gout, const int* __restrict__ recv, const int* __restrict__ src_beg,"
+    " const int* __restrict__ src_end, const int* __restrict__ src_edge, real* __restrict__ gx";
 
 // Source-major x-bar of task (input block b, channel block cb) for one sender (Eq. 21):
 // x-bar_j[m1] = sum over out-edges, paths of w_pi sum_m3 G[m1,m3] mbar_i[m3].  The out-edges are
@@ -900,7 +900,7 @@ void emit_bwd_src_task(Out& o, const Plan& p, int ti, const Task& T) {
       accs.push_back(F("acc%d_%d", ib, m));
       o.line("real " + accs.back() + " = R(0);");
     }
-  o.line("const int s0 = src_ptr[node], s1 = src_ptr[node + 1];");
+  o.line("const int s0 = src_beg[node], s1 = src_end[node];");
   for (const auto& S : a_subsets(p, T.paths, kRegBudget)) {
   o.open("");
   emit_a_loads(o, p, S);
@@ -989,7 +989,7 @@ void emit_src_dispatch(Out& o, const Plan& p, int ntask) {
   o.line("if (node >= nrec) return;");
   o.line(F("const int cb = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) / %d;", kSrcSplit));
   o.line(F("real* const smc = sm + cb * %d;", slice));
-  emit_group_switch(o, tg, "bws_t%T(phi, A, G, gout, recv, src_ptr, src_edge, gx, smc, node, e_base, accumulate);",
+  emit_group_switch(o, tg, "bws_t%T(phi, A, G, gout, recv, src_beg, src_end, src_edge, gx, smc, node, e_base, accumulate);",
                     kSrcSplit > 1);
   o.close();
 }
@@ -1138,6 +1138,22 @@ void emit_small_kernels(Out& o) {
   o.close();
   o.line("sx = wave_total(sx); sy = wave_total(sy); sz = wave_total(sz);");
   o.line("if (lane == 0) { gpos[3 * (i64)i] = sx; gpos[3 * (i64)i + 1] = sy; gpos[3 * (i64)i + 2] = sz; }");
+  o.close();
+  // Source view of one receiver chunk: the out-edges of sender j whose sorted positions lie in
+  // the chunk's range [e0, e1) form one run of j's ascending source-CSR list; beg[j], end[j]
+  // bound that run (two binary searches, one thread per sender).
+  o.line("extern \"C\" __global__ void __launch_bounds__(256)");
+  o.open("cgtp_src_bounds(const int* __restrict__ src_ptr, const int* __restrict__ src_edge, int n, int e0, int e1,"
+         " int* __restrict__ beg, int* __restrict__ end)");
+  o.line("const int j = (int)blockIdx.x * 256 + (int)threadIdx.x;");
+  o.line("if (j >= n) return;");
+  o.line("int a = src_ptr[j], b = src_ptr[j + 1];");
+  o.line("const int top = b;");
+  o.line("while (a < b) { const int m = (a + b) >> 1; if (src_edge[m] < e0) a = m + 1; else b = m; }");
+  o.line("beg[j] = a;");
+  o.line("b = top;");
+  o.line("while (a < b) { const int m = (a + b) >> 1; if (src_edge[m] < e1) a = m + 1; else b = m; }");
+  o.line("end[j] = a;");
   o.close();
   // A-bar = sum over wave slots of the partials: block = 64 outputs x 8 slot ranges (one wave
   // each, four interleaved accumulators), combined in LDS in a fixed order.

@@ -347,7 +347,8 @@ void emit_drecv_task(Out& o, const Plan& p, int ti, const Task& T, int col_off, 
 const char* kDSrcArgs =
     "const real* __restrict__ phi, const real* __restrict__ vphi, const real* __restrict__ A,"
     " const real* __restrict__ vA, const real* __restrict__ G, const real* __restrict__ gout,"
-    " const int* __restrict__ recv, const int* __restrict__ src_ptr, const int* __restrict__ src_edge,"
+    " const int* __restrict__ recv, const int* __restrict__ src_beg, const int* __restrict__ src_end,"
+    " const int* __restrict__ src_edge,"
     " real* __restrict__ gx, real sphi, real sA";
 
 // x-bar-dot of task (input block b, channel block) for one sender (Eq. 30).
@@ -359,7 +360,7 @@ void emit_dsrc_task(Out& o, const Plan& p, int ti, const Task& T) {
   o.line(F("const int u = %d + (int)threadIdx.x;", T.cb * 64));
   o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
   for (int m = 0; m < d1; ++m) o.line(F("real acc%d = R(0);", m));
-  o.line("const int s0 = src_ptr[node], s1 = src_ptr[node + 1];");
+  o.line("const int s0 = src_beg[node], s1 = src_end[node];");
   for (const auto& S : a_subsets(p, T.paths, kDsrcRegs)) {
     o.open("");
     emit_da_loads(o, p, S);
@@ -557,7 +558,7 @@ std::string generate_dbl_source(const Plan& p, std::string* err) {
   o.line("if (node >= nrec) return;");
   o.open("switch (t)");
   for (int k = 0; k < int(st.size()); ++k)
-    o.line(F("case %d: dsr_t%d(phi, vphi, A, vA, G, gout, recv, src_ptr, src_edge, gx, sphi, sA, node, e_base,"
+    o.line(F("case %d: dsr_t%d(phi, vphi, A, vA, G, gout, recv, src_beg, src_end, src_edge, gx, sphi, sA, node, e_base,"
              " accumulate); break;", k, k));
   o.line("default: break;");
   o.close();

@@ -183,8 +183,10 @@ cgtp_status_t build_plan(const char* irreps_in, const char* irreps_sh, const cha
     return CGTP_ERR_INVALID_ARG;
   for (size_t k = 0; k < p->sh.size(); ++k) {
     const Block& b = p->sh[k];
-    if (b.mul != 1 || b.l != int(k) || b.parity != ((b.l & 1) ? -1 : 1)) {
-      *err = "spherical-harmonic irreps must be 1x0e+1x1o+...+1xLp in order";
+    // The parity label of an edge block (normally (-1)^l) only enters path selection: the values
+    // are always the real spherical harmonics (LunaTP's C1 profile labels degree 1 "1e").
+    if (b.mul != 1 || b.l != int(k)) {
+      *err = "spherical-harmonic irreps must be 1x0e+1x1?+...+1xL? (one block per degree, in order)";
       return CGTP_ERR_INVALID_ARG;
     }
   }

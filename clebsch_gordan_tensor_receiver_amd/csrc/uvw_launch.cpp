@@ -217,11 +217,10 @@ cgtp_status_t uvw_forward(Plan& p, Graph& G, const DeviceGraph& d, const void* x
   return CGTP_OK;
 }
 
-cgtp_status_t uvw_backward(Plan& p, Graph& G, const DeviceGraph& d, const SourceViews* views, const void* x,
+cgtp_status_t uvw_backward(Plan& p, Graph& G, const DeviceGraph& d, const void* x,
                            const void* pos, const void* shift, const void* phi, const void* A, const void* gout,
                            void* grad_x, void* grad_pos, void* grad_edge_vec, void* grad_phi, void* grad_A,
                            void* workspace, hipStream_t s, std::string* err, const void* state) {
-  (void)views;
   UvwPlanB B = layout_bwd(p, G);
   cgtp_status_t st;
   const char* fam = "uvw_bwd";

@@ -20,7 +20,7 @@ cgtp_status_t uvw_forward(Plan& p, Graph& G, const DeviceGraph& d, const void* x
                           const void* phi, const void* A, void* out, void* workspace, hipStream_t s,
                           std::string* err, void* state = nullptr);
 // `state` (nullable): S kept by the forward; the backward then reads it instead of recomputing it.
-cgtp_status_t uvw_backward(Plan& p, Graph& G, const DeviceGraph& d, const SourceViews* views, const void* x,
+cgtp_status_t uvw_backward(Plan& p, Graph& G, const DeviceGraph& d, const void* x,
                            const void* pos, const void* shift, const void* phi, const void* A, const void* gout,
                            void* grad_x, void* grad_pos, void* grad_edge_vec, void* grad_phi, void* grad_A,
                            void* workspace, hipStream_t s, std::string* err, const void* state = nullptr);

@@ -18,7 +18,11 @@
  *
  * Conventions fixed by this library (the pages leave them open):
  *  - Irreps strings are "MULxLp" tokens joined by '+', p in {e, o}, e.g. "128x0e+128x1o".
- *    The spherical-harmonic irreps must be "1x0e+1x1o+...+1xLp" with parity (-1)^l.
+ *    The spherical-harmonic irreps are one block of multiplicity 1 per degree 0..L in order,
+ *    normally "1x0e+1x1o+...+1xLp" with parity (-1)^l.  The block values are always the real
+ *    spherical harmonics of the edge direction; a block's parity label only enters path
+ *    selection, so another label (LunaTP Appendix A.1 profile C1: "1x0e+1x1e+1x2e") is accepted
+ *    as given.
  *  - Features use the ir_mul layout (Sobek section 4.5): block b of multiplicity C and
  *    degree l occupies C*(2l+1) consecutive values, component m (0..2l) major, channel minor.
  *    A node row holds its blocks back to back: x is N x C_in, out is N x C_out, row-major.
@@ -43,9 +47,17 @@
  * run asynchronously on the caller's HIP stream (`stream` is a hipStream_t, NULL = default
  * stream).  Outputs are overwritten, not accumulated.  The caller supplies a device
  * workspace of at least cgtp_workspace_size() bytes; the convolution calls never allocate
- * device memory except for the one-off upload of a graph to a device (see
- * cgtp_graph_upload).  Errors are returned as status codes; nothing is thrown across the
- * ABI.  cgtp_last_error() gives a readable message for the calling thread.
+ * device memory and never synchronise, except for the one-off upload of a graph to a device
+ * (cgtp_graph_upload; call it before the first convolution call) and the one-off compilation
+ * and loading of a plan's kernels (cgtp_plan_compile).  Errors are returned as status codes;
+ * nothing is thrown across the ABI.  cgtp_last_error() gives a readable message for the
+ * calling thread.
+ *
+ * Zero-length edges: an edge whose vector pos[send] - pos[recv] + shift is exactly zero has no
+ * direction, so its spherical harmonics are undefined.  The convolution calls do not test for
+ * it (the test would need a synchronisation); such an edge turns the outputs it reaches into
+ * NaN (its receiver's row, its sender's gradient row, its own per-edge gradients, grad_A).
+ * cgtp_check_edges finds such edges on the device and returns CGTP_ERR_DEGENERATE_EDGE.
  */
 #ifndef CGTP_H
 #define CGTP_H
@@ -156,8 +168,11 @@ cgtp_status_t cgtp_graph_destroy(cgtp_graph_t g);
 
 /* ---------------------------------------------------------------- convolution (device) */
 
-/* Workspace bytes needed by `op` for this plan and graph (bounded by the scratch budget plus
- * O(N + parameter) terms; never O(E x N_w)). */
+/* Workspace bytes needed by `op` for this plan and graph: at most the scratch budget (per-edge
+ * rows, edge partials and grad_A partial slots of one receiver chunk) plus E x 3 edge-vector
+ * values and 2 N int32 source-CSR bounds; never O(E x N_w).  A graph whose rows do not fit is
+ * processed in receiver chunks; the receivers per chunk are also capped so that the grad_A
+ * partial slots stay inside the budget at low in-degree. */
 cgtp_status_t cgtp_workspace_size(cgtp_plan_t plan, cgtp_graph_t g, cgtp_op_t op, size_t* bytes);
 
 /* Forward.  x: N x C_in; pos: N x 3; shift: E x 3 receiver-sorted image shifts added to
@@ -188,7 +203,9 @@ cgtp_status_t cgtp_conv_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x
  * Channelwise plans: the state is the per-edge row of folded coefficients G = sum c Y and the
  * real SH Y that the forward and backward both derive from the edge vector (LunaTP section 4.3,
  * product reuse across passes); E times the row width (816 bytes per edge for the l <= 3
- * profile in fp32), i.e. O(E), never O(E x N_w).
+ * profile in fp32).  The state is never larger than E x N_w: cgtp_state_size returns
+ * UNSUPPORTED when a row is longer than the N_w edge weights (e.g. 5,196 values against
+ * N_w = 3,392 for 32x(0e..6e) with SH l <= 6); such plans let the backward recompute its rows.
  *   cgtp_state_size               bytes of the state buffer
  *   cgtp_conv_forward_keep_state  the forward (fully connected: CGTP_STREAMED; channelwise:
  *                                 CGTP_CONVENTIONAL, as cgtp_conv_forward) that also leaves the
@@ -198,8 +215,9 @@ cgtp_status_t cgtp_conv_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x
  *                                 it; the state must come from cgtp_conv_forward_keep_state with
  *                                 the same plan, graph, x, pos, shift and phi (A does not enter
  *                                 it); results are bitwise those of cgtp_conv_backward.
- * WORKSPACE when `state` is NULL or smaller than cgtp_state_size; other errors as the plain
- * calls.  The workspace requirements are those of the plain calls. */
+ * WORKSPACE when `state` is NULL or smaller than cgtp_state_size; UNSUPPORTED when the plan keeps
+ * no state (above); other errors as the plain calls.  The workspace requirements are those of the
+ * plain calls. */
 cgtp_status_t cgtp_state_size(cgtp_plan_t plan, cgtp_graph_t g, size_t* bytes);
 cgtp_status_t cgtp_conv_forward_keep_state(cgtp_plan_t plan, cgtp_graph_t g, const void* x, const void* pos,
                                            const void* shift, const void* phi, const void* A, void* out,
@@ -267,6 +285,24 @@ cgtp_status_t cgtp_profile_end(void);
  * the kernel name (NUL-terminated, truncated to `capacity`), launch count and summed ms. */
 int cgtp_profile_count(void);
 cgtp_status_t cgtp_profile_get(int index, char* name, int capacity, long long* launches, double* total_ms);
+
+/* ---------------------------------------------------------------- achievable peaks */
+
+/* Measured ceilings of the current device, for roofline fractions beside the published peaks.
+ * Plain kernels of this library, timed with HIP events on `stream` (the call synchronises it):
+ *   kind 0  fp32 fused multiply-add throughput (16 independent chains per lane, eight waves per
+ *           SIMD, no packed instructions), TFLOP/s (2 flop per FMA)
+ *   kind 1  the same in fp64, TFLOP/s
+ *   kind 2  device copy of `bytes` from src to dst in 16-byte units, counted as bytes read plus
+ *           bytes written, GB/s
+ * Two untimed launches raise the clocks; `reps` timed launches follow.  *best receives the highest
+ * rate, *median (nullable) the median.  dst: caller-owned device memory, at least 8 bytes for
+ * kinds 0 and 1 (never written for the values used, kept to make the chains live), `bytes` for
+ * kind 2; src: `bytes` of device memory for kind 2 (unused otherwise).  INVALID_ARG for an
+ * unknown kind, reps < 1, null best or dst, or (kind 2) null src or bytes not a positive
+ * multiple of 16. */
+cgtp_status_t cgtp_measure_peak(int kind, void* dst, const void* src, size_t bytes, int reps, void* stream,
+                                double* best, double* median);
 
 const char* cgtp_error_string(cgtp_status_t status);
 const char* cgtp_last_error(void);

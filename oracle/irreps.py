@@ -106,9 +106,10 @@ def make_problem(irreps_in: str, irreps_sh: str, irreps_out: str, mode: str) -> 
             raise ValueError("spherical-harmonic irreps must have multiplicity 1")
     if [b.l for b in bs] != list(range(len(bs))):
         raise ValueError("spherical-harmonic irreps must be 0..lmax in order")
-    for b in bs:
-        if b.parity != (-1) ** b.l:
-            raise ValueError("spherical harmonic of degree l has parity (-1)^l")
+    # The edge blocks always hold the real spherical harmonics of the edge direction; their parity
+    # label, normally (-1)^l, only enters path selection.  LunaTP's profile C1 (Appendix A.1, table
+    # of node, edge and output irreps) labels its degree-1 edge block "1e"; that label is accepted
+    # as given (the resulting operator is then rotation- but not inversion-equivariant).
     if mode not in ("uvu", "uvw"):
         raise ValueError(mode)
     paths: List[Path] = []

@@ -134,7 +134,9 @@ def test_invalid_plans_are_rejected(lib):
     mk = lib.Plan
     assert _status(lambda: mk("8x0e+bad", "1x0e+1x1o", "8x0e", "uvu")) == INVALID_ARG
     assert _status(lambda: mk("8x0e", "1x0e+1x2e", "8x0e", "uvu")) == INVALID_ARG      # SH degrees not 0..L
-    assert _status(lambda: mk("8x0e", "1x0e+1x1e", "8x0e", "uvu")) == INVALID_ARG      # SH parity
+    assert _status(lambda: mk("8x0e", "1x0e+2x1o", "8x0e", "uvu")) == INVALID_ARG      # SH multiplicity
+    assert _status(lambda: mk("8x0e", "1x1o+1x0e", "8x0e", "uvu")) == INVALID_ARG      # SH degree order
+    assert mk("8x0e+8x1e", "1x0e+1x1e", "8x0e+8x1e", "uvu").info["n_paths"] == 5      # parity label as given
     assert _status(lambda: mk("8x0e", "1x0e", "8x0e", "uvu", num_radial=0)) == INVALID_ARG
     assert _status(lambda: mk("8x0e", "1x0e", "8x1o", "uvu")) == UNSUPPORTED           # no admissible path
     assert _status(lambda: mk("8x0e", "1x0e", "4x0e", "uvu")) == UNSUPPORTED           # uvu needs mul_in = mul_out
@@ -209,14 +211,33 @@ def test_workspace_is_bounded_by_the_scratch_budget(lib):
     small = [lib.workspace_size(plan, g, op) for op in (0, 1, 2)]
     for b, sm in zip(big, small):
         assert sm < b
-    # Budget plus the O(N + E + parameter) terms: A-bar partial slots (8 per XCD group of 4
-    # receivers at most), one edge-vector buffer and alignment.  Never E x N_w.
+    # The budget covers the per-edge rows, the edge partials and the A-bar partial slots; beyond it
+    # only an E x 3 edge-vector buffer, 2 N int32 source bounds and alignment.  Never E x N_w.
     E, N = g.n_edges, g.n_nodes
-    K, nw = plan.info["num_radial"], plan.info["n_weights"]
-    nslot = 8 * (((N + 7) // 8 + 3) // 4)
+    nw = plan.info["n_weights"]
+    slots_min = 8 * plan.info["num_radial"] * nw * 4      # the eight slots of a chunk, at least
     for sm in small:
-        assert sm <= (1 << 20) + 4 * (nslot * K * nw + 3 * E) + 1024
+        assert sm <= (1 << 20) + slots_min + 4 * 3 * E + 8 * N + 4096
         assert sm < E * nw * 4
+
+
+def test_workspace_bound_low_degree_large_graph(lib):
+    """l <= 3, 128 channels on a 2M-edge graph of in-degree 4 (500k receivers): many receivers per
+    edge, so the A-bar partial slots (one K x N_w block per group of 4 receivers) would outgrow
+    the budget if the receivers per chunk were not capped.  Host only: workspace sizes."""
+    s = CONFIGS[2]
+    plan = lib.Plan(s["irreps_in"], s["irreps_sh"], s["irreps_out"], s["mode"], s["dtype"], s["K"])
+    rng = np.random.default_rng(7)
+    N, deg = 500_000, 4
+    recv = np.repeat(np.arange(N, dtype=np.int32), deg)
+    send = rng.integers(0, N, size=N * deg).astype(np.int32)
+    g = lib.Graph(N, recv, send)
+    E = g.n_edges
+    budget = 256 << 20
+    for op in (0, 1, 2):
+        ws = lib.workspace_size(plan, g, op)
+        print(f"op {op}: workspace {ws / 2**20:.1f} MiB for {E} edges", flush=True)
+        assert ws <= budget + 64 * E + (32 << 20), (op, ws)
 
 
 def test_sweep_profile_weight_counts(lib):

@@ -75,12 +75,10 @@ def test_backward_repeatable_bitwise():
         assert torch.equal(a[k], b[k]), k
 
 
-def test_backward_config2_full_size():
-    """1,024-atom diamond graph, fp32: every output of sampled nodes/edges, and A-bar in full."""
+def _check_config2_sampled(case, got, label):
+    """Every output of 24 sampled nodes and their edges against the oracle on those edges, and
+    A-bar in full (it sums over every edge)."""
     from tests.gpu_helpers import TOL, rel_err
-    case = make_case(2)
-    g = _gpu(case)
-    got = {k: v.cpu().numpy() for k, v in g.backward().items()}
     for v in got.values():
         assert np.isfinite(v).all()
     rng = np.random.default_rng(22)
@@ -99,13 +97,78 @@ def test_backward_config2_full_size():
     }
     for k, (a, b) in checks.items():
         err = rel_err(a, b)
-        print(f"config 2 sampled grad {k}: rel err {err:.3e}", flush=True)
+        print(f"{label} sampled grad {k}: rel err {err:.3e}", flush=True)
         assert err <= TOL["float32"], (k, err)
     assert len(out_edges) > 0
     full = _oracle_full(case)
     err = rel_err(got["A"], full["A"].numpy())
-    print(f"config 2 grad A (full): rel err {err:.3e}", flush=True)
+    print(f"{label} grad A (full): rel err {err:.3e}", flush=True)
     assert err <= TOL["float32"]
+
+
+def test_backward_config2_full_size():
+    """1,024-atom diamond graph, fp32: every output of sampled nodes/edges, and A-bar in full."""
+    case = make_case(2)
+    g = _gpu(case)
+    got = {k: v.cpu().numpy() for k, v in g.backward().items()}
+    _check_config2_sampled(case, got, "config 2")
+
+
+def test_backward_config2_full_size_with_kept_edge_rows():
+    """The measured step at full size: the conventional forward keeping its per-edge rows, then
+    the backward reading them.  The forward rows and all five gradients against the oracle
+    (sampled as above), and bitwise equal to the forward and backward that derive the rows."""
+    from clebsch_gordan_tensor_receiver_amd import _lib
+    from tests.gpu_helpers import TOL, rel_err
+    case = make_case(2)
+    g = _gpu(case)
+    state = g.conv.state_buffer()
+    out_k = g.conv.forward(g.x, g.pos, g.shift, g.phi, g.A, schedule=_lib.CONVENTIONAL, state=state)
+    grads_k = g.conv.backward(g.x, g.pos, g.shift, g.phi, g.A, g.grad_out, state=state)
+    out = g.forward()
+    grads = g.backward()
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_k)
+    for k in KEYS:
+        assert torch.equal(grads[k], grads_k[k]), k
+    rng = np.random.default_rng(23)
+    rows = np.unique(np.concatenate([rng.choice(case.n_nodes, 32, replace=False), [0, case.n_nodes - 1]]))
+    keep = np.isin(case.recv, rows)
+    ev = case.edge_vec[torch.as_tensor(np.nonzero(keep)[0])]
+    ref = conv.forward_conventional(case.problem, case.x, ev, case.recv[keep], case.send[keep], case.phi[keep],
+                                    case.A).numpy()[rows]
+    err = rel_err(out_k.cpu().numpy()[rows], ref)
+    print(f"config 2 kept rows forward sampled rel err {err:.3e}", flush=True)
+    assert err <= TOL["float32"]
+    _check_config2_sampled(case, {k: v.cpu().numpy() for k, v in grads_k.items()}, "config 2 kept rows")
+
+
+def test_backward_allocates_no_device_memory():
+    """After the graph upload and the kernels' first load, a backward allocates nothing on the
+    device: not with one receiver chunk, and not after a smaller scratch budget splits the
+    receivers into many chunks (each chunk's source-CSR bounds are computed on the device into the
+    caller's workspace).  Free device memory is compared around the calls."""
+    from clebsch_gordan_tensor_receiver_amd import _lib
+    case = make_case(1, irreps_override=SMALL_L3, dtype="float32")
+    g = _gpu(case)
+    g.graph.upload()
+    g.plan.set_scratch_budget(64 << 10)       # many chunks
+    ref = g.backward()                       # first calls: load the plan's kernels
+    g.plan.set_scratch_budget(48 << 10)       # a different chunking from here on
+    ws = g.conv.workspace(_lib.OP_BACKWARD)   # allocated by the caller beforehand
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    outs = {k: torch.empty_like(v) for k, v in ref.items()}
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    _lib.conv_backward(g.plan, g.graph, g.x, g.pos, g.shift, g.phi, g.A, g.grad_out, grad_x=outs["x"],
+                       grad_pos=outs["pos"], grad_edge_vec=outs["edge_vec"], grad_phi=outs["phi"], grad_A=outs["A"],
+                       workspace=ws)
+    torch.cuda.synchronize()
+    free2, _ = torch.cuda.mem_get_info()
+    print(f"free device memory: {free0} -> {free1} (outputs) -> {free2} (chunked backward)", flush=True)
+    assert free2 == free1
+    _compare(outs, _oracle_full(case), "float32", label="chunked, no allocation")
 
 
 def test_backward_config5_reduced_full():

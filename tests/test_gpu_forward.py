@@ -68,17 +68,23 @@ def test_forward_l3_ragged_channels(dtype, schedule):
     assert err <= TOL[dtype]
 
 
+@pytest.mark.parametrize("schedule", ["conventional", "streamed"])
 @pytest.mark.parametrize("config", [2, 3])
-def test_forward_full_size_sampled(config):
+def test_forward_full_size_sampled(config, schedule):
+    """Full-size diamond graph (1,024 atoms, 91k edges), fp32 (config 2) and fp64 (config 3), both
+    schedules (Sobek section 3.1, Eqs. 15-16: the streamed S_i = sum phi (x) CG, then m = S A, and
+    the conventional per-edge weights): sampled receiver rows against the oracle."""
+    from clebsch_gordan_tensor_receiver_amd import _lib
     from tests.gpu_helpers import TOL, rel_err
     case = make_case(config)
     g = _gpu(case)
     assert np.array_equal(g.perm, case.perm)
-    out = g.forward().cpu().numpy()
+    sch = _lib.CONVENTIONAL if schedule == "conventional" else _lib.STREAMED
+    out = g.forward(sch).cpu().numpy()
     rows = _sample_receivers(case, 48, seed=config)
     ref = _oracle_rows(case, rows)
     err = rel_err(out[rows], ref)
-    print(f"config {config} sampled rel err {err:.3e}", flush=True)
+    print(f"config {config} {schedule} sampled rel err {err:.3e}", flush=True)
     assert err <= TOL[case.dtype]
     assert np.isfinite(out).all()
 

@@ -53,6 +53,27 @@ def test_hetero_forward_backward(profile, dtype):
     _cmp(g.backward(), b, dtype, KEYS, f"{profile} {dtype} grad")
 
 
+@pytest.mark.parametrize("profile", ["C1", "C5", "C7", "C9"])
+def test_lunatp_profiles_forward_backward(profile):
+    """LunaTP's mixed-multiplicity cases (Appendix A.1): C5 (l <= 4, a 320-channel scalar block:
+    five channel blocks, the last ragged), C7 (l <= 5), C9 (l <= 6, 32-channel blocks on half
+    waves) and C1 (edge block 1 labelled 1e, so all paths are even), fp32 on the 64-atom graph:
+    both forward schedules and every gradient against the oracle."""
+    from clebsch_gordan_tensor_receiver_amd import _lib
+    from tests.gpu_helpers import TOL, rel_err
+    from workloads.sweeps import lunatp_profile
+    case = make_case(1, irreps_override=lunatp_profile(profile), dtype="float32")
+    g = _gpu(case)
+    ref = conv.forward_conventional(case.problem, case.x, case.edge_vec, case.recv, case.send, case.phi,
+                                    case.A).numpy()
+    for sched, name in ((_lib.CONVENTIONAL, "conventional"), (_lib.STREAMED, "streamed")):
+        err = rel_err(g.forward(sched).cpu().numpy(), ref)
+        print(f"{profile} forward {name}: rel err {err:.3e} ({len(case.problem.paths)} paths)", flush=True)
+        assert err <= TOL["float32"], name
+    b = conv.backward(case.problem, case.x, case.edge_vec, case.recv, case.send, case.phi, case.A, case.grad_out)
+    _cmp(g.backward(), b, "float32", KEYS, f"{profile} grad")
+
+
 @pytest.mark.parametrize("dtype", ["float32", "float64"])
 def test_hetero_double_backward(dtype):
     case = make_case(1, irreps_override=C3, dtype=dtype)

@@ -311,6 +311,37 @@ def test_brute_force_scalar_graph():
     np.testing.assert_allclose(m, want, atol=1e-15)
 
 
+def test_brute_force_vector_graph_fixes_argument_order():
+    """Degree-1 couplings written out by hand on a 3-node graph: the scalar-vector products,
+    the dot product (1,1 -> 0) = (x . Y_1) / sqrt(3) and the cross product
+    (1,1 -> 1) = (x cross Y_1) / sqrt(2), with x the sender's vector and Y_1 = sqrt(3) (y, z, x) / r
+    both in (y, z, x) component order (a cyclic reordering, so np.cross on them is the cross
+    product in the same order).  x cross Y and Y cross x differ in sign: this pins which operand
+    of the coupling is the feature and which the harmonic."""
+    P = make_problem("1x0e+1x1o", "1x0e+1x1o", "1x0e+1x1o+1x1e", "uvu")
+    # Paths in enumeration order: (0e,0e->0e), (0e,1o->1o), (1o,0e->1o), (1o,1o->0e), (1o,1o->1e).
+    got = [(p.l1, p.l2, p.l3) for p in P.paths]
+    assert got == [(0, 0, 0), (0, 1, 1), (1, 0, 1), (1, 1, 0), (1, 1, 1)]
+    pos = np.array([[0.0, 0.0, 0.0], [1.0, 0.2, -0.3], [0.1, 1.3, 0.4]])
+    recv = np.array([0, 0, 1, 2, 2]); send = np.array([1, 2, 0, 0, 1])
+    shift = np.zeros((5, 3)); shift[4] = [0.0, 0.5, -2.0]
+    rng = np.random.default_rng(3)
+    K = 3
+    phi = rng.normal(size=(5, K)); A = rng.normal(size=(K, P.n_weights)); x = rng.normal(size=(3, 4))
+    ev = conv.edge_vectors(pos, shift, recv, send).numpy()
+    m = conv.forward_conventional(P, x, ev, recv, send, phi, A).numpy()
+    want = np.zeros((3, 7))           # out row: [0e | 1o (y,z,x) | 1e (y,z,x)]
+    for e in range(5):
+        w = phi[e] @ A                # one weight per path (one channel)
+        r = ev[e]
+        y1 = np.sqrt(3.0) * np.array([r[1], r[2], r[0]]) / np.linalg.norm(r)
+        s, v = x[send[e], 0], x[send[e], 1:4]
+        want[recv[e], 0] += w[0] * s + w[3] * (v @ y1) / np.sqrt(3.0)
+        want[recv[e], 1:4] += w[1] * s * y1 + w[2] * v
+        want[recv[e], 4:7] += w[4] * np.cross(v, y1) / np.sqrt(2.0)
+    np.testing.assert_allclose(m, want, atol=1e-13)
+
+
 def test_backward_matches_finite_differences():
     ov = dict(irreps_in="2x0e+2x1o+2x2e", irreps_out="2x0e+2x1o+2x2e", irreps_sh=_sh_str(2))
     for mode in ("uvu", "uvw"):

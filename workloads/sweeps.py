@@ -40,6 +40,26 @@ def _sh(lmax: int) -> str:
     return "+".join(f"1x{l}{'e' if l % 2 == 0 else 'o'}" for l in range(lmax + 1))
 
 
+# Profiles with blocks of different multiplicities: the node and edge irreps of LunaTP's kernel
+# microbenchmark cases (Appendix A.1, table of cases C1-C10) that mix multiplicities, with outputs
+# equal to the inputs (channelwise paths join blocks of equal multiplicity).  C1 labels its
+# degree-1 edge block "1e" as the page does.
+LUNATP_HETERO = {
+    "C1": dict(irreps_in="128x0e+64x1e+32x2e", irreps_sh="1x0e+1x1e+1x2e"),
+    "C3": dict(irreps_in="128x0e+64x1o+32x2e+32x3o", irreps_sh=None),
+    "C5": dict(irreps_in="320x0e+96x1o+64x2e+32x3o+32x4e", irreps_sh=None),
+    "C7": dict(irreps_in="128x0e+64x1o+32x2e+32x3o+32x4e+32x5o", irreps_sh=None),
+    "C9": dict(irreps_in="128x0e+64x1o+32x2e+32x3o+32x4e+32x5o+32x6e", irreps_sh=None),
+}
+
+
+def lunatp_profile(case: str) -> dict:
+    """irreps_in / irreps_sh / irreps_out of a LunaTP heterogeneous case (SH up to its largest degree)."""
+    d = LUNATP_HETERO[case]
+    lmax = max(int(tok.split("x")[1][:-1]) for tok in d["irreps_in"].split("+"))
+    return dict(irreps_in=d["irreps_in"], irreps_sh=d["irreps_sh"] or _sh(lmax), irreps_out=d["irreps_in"])
+
+
 # L_max -> irreps of the "128/64", "128/64/64" and "128/64/64/64" profiles.
 PROFILES = {L: dict(irreps_in=_alt(L), irreps_sh=_sh(L), irreps_out=_alt(L), mode="uvw", dtype="float32", K=K)
             for L in (1, 2, 3)}
