@@ -29,6 +29,7 @@ EXPORTED = [
     "cgtp_conv_forward", "cgtp_conv_backward", "cgtp_conv_double_backward", "cgtp_check_edges", "cgtp_layout_convert", "cgtp_error_string", "cgtp_last_error",
     "cgtp_state_size", "cgtp_conv_forward_keep_state", "cgtp_conv_backward_with_state",
     "cgtp_profile_begin", "cgtp_profile_end", "cgtp_profile_count", "cgtp_profile_get", "cgtp_measure_peak",
+    "cgtp_conv_forward_static",
 ]
 
 
@@ -85,6 +86,7 @@ def load() -> ctypes.CDLL:
         "cgtp_profile_get": [I, ctypes.c_char_p, I, ctypes.POINTER(ctypes.c_longlong),
                              ctypes.POINTER(ctypes.c_double)],
         "cgtp_measure_peak": [I, V, V, Z, I, V, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)],
+        "cgtp_conv_forward_static": [P, P, I, V, V, V, V, V, V, V],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -257,6 +259,12 @@ def conv_forward(plan: Plan, graph: Graph, schedule: int, x, pos, shift, phi, A,
     check(load().cgtp_conv_forward(plan.handle, graph.handle, schedule, _ptr(x), _ptr(pos), _ptr(shift), _ptr(phi),
                                    _ptr(A), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                    _stream(stream)))
+
+
+def conv_forward_static(plan: Plan, graph: Graph, schedule: int, x, pos, shift, phi, A, out, stream=None):
+    """cgtp_conv_forward_static: the forward with the library's static device scratch (no workspace)."""
+    check(load().cgtp_conv_forward_static(plan.handle, graph.handle, schedule, _ptr(x), _ptr(pos), _ptr(shift),
+                                          _ptr(phi), _ptr(A), _ptr(out), _stream(stream)))
 
 
 def conv_backward(plan: Plan, graph: Graph, x, pos, shift, phi, A, grad_out, grad_x=None, grad_pos=None,

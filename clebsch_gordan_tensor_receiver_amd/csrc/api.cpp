@@ -10,6 +10,7 @@
 
 #include "cgtp.h"
 #include "errors.hpp"
+#include "forward.hpp"
 #include "graph.hpp"
 #include "kernels.hpp"
 #include "plan.hpp"
@@ -38,10 +39,10 @@ cgtp_status_t ok() {
 
 size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
-// Edges of G rows that fit in the scratch budget (at least the largest in-degree).
-long long g_chunk_edges(const cgtp::Plan& p, const cgtp::Graph& g) {
+// Edges of G rows that fit in `budget` bytes (at least the largest in-degree).
+long long g_chunk_edges(const cgtp::Plan& p, const cgtp::Graph& g, size_t budget) {
   long long row = (long long)p.g_stride * (long long)p.elem();
-  long long cap = std::max<long long>(1, (long long)(p.scratch_budget / size_t(row)));
+  long long cap = std::max<long long>(1, (long long)(budget / size_t(row)));
   return std::max<long long>(cap, g.max_in_degree);
 }
 
@@ -49,6 +50,12 @@ long long max_chunk_edges(const cgtp::Graph& g, const std::vector<std::pair<int,
   long long m = 0;
   for (auto& c : ch) m = std::max<long long>(m, g.row_ptr[c.second] - g.row_ptr[c.first]);
   return m;
+}
+
+// Channelwise forward workspace: the G rows of the largest receiver chunk under `budget`.
+size_t forward_rows_bytes(const cgtp::Plan& p, const cgtp::Graph& g, size_t budget) {
+  auto ch = g.chunks(g_chunk_edges(p, g, budget));
+  return align256(size_t(max_chunk_edges(g, ch)) * size_t(p.g_stride) * p.elem());
 }
 
 // Launch geometry shared with the generated kernels (codegen.cpp).
@@ -155,7 +162,8 @@ cgtp_status_t source_bounds(cgtp::Plan& p, const char* fam, const cgtp::Graph& G
 
 // Feature blocks that no path reaches (output side) or leaves (input side) are not written by
 // the kernels; zero the whole tensor first when such a block exists.
-cgtp_status_t zero_unreached(cgtp::Plan& p, void* buf, int n, bool out_side, hipStream_t s, std::string* err) {
+cgtp_status_t zero_unreached(cgtp::Plan& p, void* buf, int n, bool out_side, hipStream_t s, std::string* err,
+                             bool loaded_only = false) {
   const auto& blocks = out_side ? p.out : p.in;
   const auto& by = out_side ? p.by_out : p.by_in;
   bool any = false;
@@ -163,7 +171,7 @@ cgtp_status_t zero_unreached(cgtp::Plan& p, void* buf, int n, bool out_side, hip
   if (!any) return CGTP_OK;
   const char* fam = p.mode == CGTP_CHANNELWISE ? "fwd" : "uvw_fwd";
   hipFunction_t kz;
-  cgtp_status_t st = cgtp::get_kernel(p, fam, "cgtp_fill_zero", &kz, err);
+  cgtp_status_t st = cgtp::get_kernel(p, fam, "cgtp_fill_zero", &kz, err, loaded_only);
   if (st != CGTP_OK) return st;
   long long cnt = (long long)n * (out_side ? p.c_out : p.c_in);
   void* a[] = {&buf, &cnt};
@@ -378,8 +386,7 @@ cgtp_status_t cgtp_workspace_size(cgtp_plan_t plan, cgtp_graph_t g, cgtp_op_t op
     return ok();
   }
   if (op == CGTP_OP_FORWARD) {
-    auto ch = G.chunks(g_chunk_edges(p, G));
-    need = align256(size_t(max_chunk_edges(G, ch)) * size_t(p.g_stride) * p.elem());
+    need = forward_rows_bytes(p, G, p.scratch_budget);
   } else if (op == CGTP_OP_BACKWARD) {
     need = bwd_layout(p, G).total;
   } else {
@@ -389,9 +396,13 @@ cgtp_status_t cgtp_workspace_size(cgtp_plan_t plan, cgtp_graph_t g, cgtp_op_t op
   return ok();
 }
 
+// `budget`: bytes of G rows per receiver chunk (the plan's scratch budget, or the static scratch of
+// the allocation-free entry point).  `no_alloc`: the graph must already be on the device and the
+// kernels loaded there; nothing is uploaded, compiled or loaded (no device allocation).
 static cgtp_status_t conv_forward_impl(cgtp_plan_t plan, cgtp_graph_t g, cgtp_schedule_t schedule, const void* x,
                                        const void* pos, const void* shift, const void* phi, const void* A, void* out,
-                                       void* workspace, size_t ws_bytes, void* stream, void* state) {
+                                       void* workspace, size_t ws_bytes, void* stream, void* state, size_t budget,
+                                       bool no_alloc) {
   if (!plan || !g) return fail(CGTP_ERR_INVALID_ARG, "null plan or graph");
   if (!x || !pos || !A || !out) return fail(CGTP_ERR_INVALID_ARG, "null tensor argument");
   if (schedule != CGTP_STREAMED && schedule != CGTP_CONVENTIONAL) return fail(CGTP_ERR_INVALID_ARG, "bad schedule");
@@ -401,14 +412,21 @@ static cgtp_status_t conv_forward_impl(cgtp_plan_t plan, cgtp_graph_t g, cgtp_sc
                                                : "null phi (the plan has no radial basis of its own)");
   cgtp::Graph& G = g->g;
   size_t need = 0;
-  cgtp_workspace_size(plan, g, CGTP_OP_FORWARD, &need);
-  if (ws_bytes < need || (!workspace && need > 0)) return fail(CGTP_ERR_WORKSPACE, "workspace too small");
+  if (no_alloc)
+    need = p.mode == CGTP_CHANNELWISE ? forward_rows_bytes(p, G, budget) : 0;
+  else
+    cgtp_workspace_size(plan, g, CGTP_OP_FORWARD, &need);
+  if (ws_bytes < need || (!workspace && need > 0))
+    return fail(CGTP_ERR_WORKSPACE, "workspace too small: " + std::to_string(need) + " bytes needed, " +
+                                        std::to_string(ws_bytes) + " given");
   std::string err;
   cgtp::DeviceGraph d;
-  cgtp_status_t st = cgtp::device_graph(G, &d, &err);
+  cgtp_status_t st = no_alloc ? cgtp::resident_graph(G, &d, &err) : cgtp::device_graph(G, &d, &err);
   if (st != CGTP_OK) return fail(st, err);
   hipStream_t s0 = static_cast<hipStream_t>(stream);
-  if ((st = zero_unreached(p, out, G.n, true, s0, &err)) != CGTP_OK) return fail(st, err);
+  if (no_alloc && p.mode != CGTP_CHANNELWISE)
+    return fail(CGTP_ERR_UNSUPPORTED, "the allocation-free forward runs channelwise plans only");
+  if ((st = zero_unreached(p, out, G.n, true, s0, &err, no_alloc)) != CGTP_OK) return fail(st, err);
   if (p.mode == CGTP_FULLY_CONNECTED) {
     if (schedule != CGTP_STREAMED)
       return fail(CGTP_ERR_UNSUPPORTED, "fully connected mode runs the streamed schedule only: the conventional one "
@@ -420,9 +438,9 @@ static cgtp_status_t conv_forward_impl(cgtp_plan_t plan, cgtp_graph_t g, cgtp_sc
     return fail(CGTP_ERR_UNSUPPORTED, "channelwise plans keep their edge rows in the conventional forward only");
   const char* fam = state ? "fwdk" : schedule == CGTP_STREAMED ? "fwds" : "fwd";
   hipFunction_t kprep, kfwd;
-  if ((st = cgtp::get_kernel(p, fam, "cgtp_prep", &kprep, &err)) != CGTP_OK) return fail(st, err);
-  if ((st = cgtp::get_kernel(p, fam, schedule == CGTP_STREAMED ? "cgtp_fwd_streamed" : "cgtp_fwd", &kfwd, &err)) !=
-      CGTP_OK)
+  if ((st = cgtp::get_kernel(p, fam, "cgtp_prep", &kprep, &err, no_alloc)) != CGTP_OK) return fail(st, err);
+  if ((st = cgtp::get_kernel(p, fam, schedule == CGTP_STREAMED ? "cgtp_fwd_streamed" : "cgtp_fwd", &kfwd, &err,
+                             no_alloc)) != CGTP_OK)
     return fail(st, err);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const cgtp::TaskGroups tg = cgtp::task_groups(cgtp::forward_tasks(p));
@@ -430,7 +448,7 @@ static cgtp_status_t conv_forward_impl(cgtp_plan_t plan, cgtp_graph_t g, cgtp_sc
   // With a state buffer every edge's row goes there, in one receiver chunk.
   void* G_ws = state ? state : workspace;
   const std::vector<std::pair<int, int>> fchunks =
-      !state ? G.chunks(g_chunk_edges(p, G))
+      !state ? G.chunks(g_chunk_edges(p, G, budget))
              : G.n > 0 ? std::vector<std::pair<int, int>>{{0, G.n}} : std::vector<std::pair<int, int>>{};
   for (auto& c : fchunks) {
     int i0 = c.first, nrec = c.second - c.first;
@@ -451,8 +469,22 @@ static cgtp_status_t conv_forward_impl(cgtp_plan_t plan, cgtp_graph_t g, cgtp_sc
 cgtp_status_t cgtp_conv_forward(cgtp_plan_t plan, cgtp_graph_t g, cgtp_schedule_t schedule, const void* x,
                                 const void* pos, const void* shift, const void* phi, const void* A, void* out,
                                 void* workspace, size_t ws_bytes, void* stream) {
-  return conv_forward_impl(plan, g, schedule, x, pos, shift, phi, A, out, workspace, ws_bytes, stream, nullptr);
+  return conv_forward_impl(plan, g, schedule, x, pos, shift, phi, A, out, workspace, ws_bytes, stream, nullptr,
+                           plan ? plan->p.scratch_budget : 0, false);
 }
+
+}  // extern "C"
+
+namespace cgtp {
+cgtp_status_t forward_in_scratch(cgtp_plan_t plan, cgtp_graph_t g, cgtp_schedule_t schedule, const void* x,
+                                 const void* pos, const void* shift, const void* phi, const void* A, void* out,
+                                 void* scratch, size_t scratch_bytes, void* stream) {
+  return conv_forward_impl(plan, g, schedule, x, pos, shift, phi, A, out, scratch, scratch_bytes, stream, nullptr,
+                           scratch_bytes, true);
+}
+}  // namespace cgtp
+
+extern "C" {
 
 cgtp_status_t cgtp_state_size(cgtp_plan_t plan, cgtp_graph_t g, size_t* bytes) {
   if (!plan || !g || !bytes) return fail(CGTP_ERR_INVALID_ARG, "null argument");
@@ -480,7 +512,8 @@ cgtp_status_t cgtp_conv_forward_keep_state(cgtp_plan_t plan, cgtp_graph_t g, con
   if (st != CGTP_OK) return st;
   if (!state || state_bytes < need) return fail(CGTP_ERR_WORKSPACE, "state buffer too small (cgtp_state_size)");
   const cgtp_schedule_t sched = plan->p.mode == CGTP_FULLY_CONNECTED ? CGTP_STREAMED : CGTP_CONVENTIONAL;
-  return conv_forward_impl(plan, g, sched, x, pos, shift, phi, A, out, workspace, ws_bytes, stream, state);
+  return conv_forward_impl(plan, g, sched, x, pos, shift, phi, A, out, workspace, ws_bytes, stream, state,
+                           plan->p.scratch_budget, false);
 }
 
 }  // extern "C"

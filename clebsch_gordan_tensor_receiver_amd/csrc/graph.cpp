@@ -131,4 +131,20 @@ cgtp_status_t device_graph(Graph& g, DeviceGraph* out, std::string* err) {
   return CGTP_OK;
 }
 
+cgtp_status_t resident_graph(Graph& g, DeviceGraph* out, std::string* err) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    *err = "hipGetDevice failed";
+    return CGTP_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g.mu);
+  auto it = g.dev.find(dev);
+  if (it == g.dev.end()) {
+    *err = "the graph is not on device " + std::to_string(dev) + ": call cgtp_graph_upload first";
+    return CGTP_ERR_INVALID_ARG;
+  }
+  *out = it->second;
+  return CGTP_OK;
+}
+
 }  // namespace cgtp

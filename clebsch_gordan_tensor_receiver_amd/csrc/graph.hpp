@@ -30,5 +30,7 @@ struct Graph {
 cgtp_status_t build_graph(int n_nodes, int n_edges, const int32_t* recv, const int32_t* send, const int32_t* image,
                           Graph* g, std::string* err);
 cgtp_status_t device_graph(Graph& g, DeviceGraph* out, std::string* err);
+// The device copy on the current device if it exists (INVALID_ARG otherwise); never allocates.
+cgtp_status_t resident_graph(Graph& g, DeviceGraph* out, std::string* err);
 
 }  // namespace cgtp

@@ -101,8 +101,10 @@ constexpr int kSbarPanelTiles = 8;
 inline bool sbar_panel(int mul) { return mul <= 64; }
 
 // Compile (once) and fetch a kernel of a family on the current device.
+// loaded_only: fetch only from a module already loaded on the current device (no compilation, no
+// module load, hence no device allocation); UNSUPPORTED otherwise.
 cgtp_status_t get_kernel(Plan& p, const std::string& family, const std::string& name, hipFunction_t* f,
-                         std::string* err);
+                         std::string* err, bool loaded_only = false);
 cgtp_status_t compile_family(Plan& p, const std::string& family, std::string* err);
 
 // Launch timing (see cgtp_profile_begin in cgtp.h).

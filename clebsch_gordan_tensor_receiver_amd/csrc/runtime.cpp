@@ -180,9 +180,11 @@ std::vector<ProfileEntry> profile_entries() {
 }
 
 cgtp_status_t get_kernel(Plan& p, const std::string& family, const std::string& name, hipFunction_t* f,
-                         std::string* err) {
-  cgtp_status_t st = compile_family(p, family, err);
-  if (st != CGTP_OK) return st;
+                         std::string* err, bool loaded_only) {
+  if (!loaded_only) {
+    cgtp_status_t st = compile_family(p, family, err);
+    if (st != CGTP_OK) return st;
+  }
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
     *err = "hipGetDevice failed";
@@ -197,6 +199,11 @@ cgtp_status_t get_kernel(Plan& p, const std::string& family, const std::string& 
     return CGTP_OK;
   }
   auto mit = m.loaded.find(dev);
+  if (mit == m.loaded.end() && loaded_only) {
+    *err = "the plan's '" + family + "' kernels are not loaded on device " + std::to_string(dev) +
+           ": an allocating call of the same operation must run once on this device first";
+    return CGTP_ERR_UNSUPPORTED;
+  }
   if (mit == m.loaded.end()) {
     hipModule_t mod;
     hipError_t e = hipModuleLoadData(&mod, m.code.data());

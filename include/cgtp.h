@@ -194,6 +194,24 @@ cgtp_status_t cgtp_conv_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x
                                  void* grad_x, void* grad_pos, void* grad_edge_vec, void* grad_phi,
                                  void* grad_A, void* workspace, size_t ws_bytes, void* stream);
 
+/* Allocation-free forward, for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  Same arguments and results as
+ * cgtp_conv_forward, without the workspace: the per-chunk rows of folded coefficients live in a
+ * static device array of CGTP_STATIC_SCRATCH_BYTES held by the library on every GPU it runs on
+ * until the process ends; receiver chunks are cut to fit it.  Channelwise plans only
+ * (UNSUPPORTED for fully connected ones); both schedules.  Preconditions, checked on the host:
+ * the graph is on the current device (cgtp_graph_upload; INVALID_ARG otherwise) and the plan's
+ * forward kernels of `schedule` are loaded there (one cgtp_conv_forward call with that schedule on
+ * this device; UNSUPPORTED otherwise).  The call then uploads, compiles, loads and allocates
+ * nothing; the first call on a device looks up that device's copy of the array.  WORKSPACE when one
+ * receiver's rows (in-degree x row width) exceed the array.  Calls on one GPU share its array: calls
+ * that overlap in time on one GPU (different streams) race; calls on one stream do not.  Nothing in
+ * the array needs clearing between calls (every row read is written first by the same call). */
+#define CGTP_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+cgtp_status_t cgtp_conv_forward_static(cgtp_plan_t plan, cgtp_graph_t g, cgtp_schedule_t schedule, const void* x,
+                                       const void* pos, const void* shift, const void* phi, const void* A, void* out,
+                                       void* stream);
+
 /* Kept forward state, for a backward with the same inputs.
  * Fully connected plans: the streamed forward accumulates per receiver the state
  * S_i = sum over in-edges of phi_ij (x) CG(x_j, Y_ij) (Sobek section 4, Eqs. 32-33) and the
