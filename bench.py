@@ -204,7 +204,7 @@ def main() -> int:
                          "(cgtp_conv_forward_keep_state)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of known size (calibrates the HBM byte counters)")
-    ap.add_argument("--sweep", choices=("degree", "copies", "channels", "lmax"),
+    ap.add_argument("--sweep", choices=("degree", "copies", "channels", "lmax", "skew"),
                     help="scaling axis of the fully connected profiles (one JSON line per point)")
     ap.add_argument("--profile", type=int, default=0, choices=(0, 1, 2, 3),
                     help="irrep profile (L_max) of the sweep; 0: all three")
@@ -513,6 +513,71 @@ def channelwise_sweep(torch, cg, args) -> int:
     return 0
 
 
+def skew_sweep(torch, cg, args) -> int:
+    """Skewed in-degrees (LunaTP section 4.2, "task ordering"): the l <= 3, 128-channel channelwise
+    profile (K = 16) on 4,096-node graphs whose receivers draw their expected degree from
+    32 exp(sigma z); conventional forward + backward per point, once with the nodes in index order
+    and once heaviest first (cgtp_graph_set_order), 1 GiB scratch budget (one receiver chunk)."""
+    from workloads import sweeps
+    s = sweeps.SKEW_PROFILE
+    points = sweeps.SKEW_POINTS if not args.points else [int(v) for v in args.points.split(",")]
+    steps, warmup = max(1, min(args.steps, 20)), max(1, min(args.warmup, 5))
+    plan = cg.Plan(s["irreps_in"], s["irreps_sh"], s["irreps_out"], s["mode"], s["dtype"], s["K"])
+    plan.set_scratch_budget(1 << 30)
+    plan.compile((cg.OP_FORWARD, cg.OP_BACKWARD))
+    info = plan.info
+    dev = dict(dtype=torch.float32, device="cuda")
+    for pt in points:
+        g = sweeps.skew_graph(pt)
+        deg = np.bincount(g.recv, minlength=g.n_nodes)
+        line = {"sweep": "skew", "point": pt, "sigma": pt / 10.0, "n_nodes": g.n_nodes, "n_edges": g.n_edges,
+                "mean_degree": round(float(deg.mean()), 2), "max_degree": int(deg.max()),
+                "irreps_in": s["irreps_in"], "steps": steps}
+        for order, name in ((0, "index"), (1, "degree")):
+            graph = cg.Graph(g.n_nodes, g.recv, g.send, g.image)
+            graph.set_order(order)
+            perm = graph.perm
+            x = torch.tensor(sweeps.normal(1, (g.n_nodes, info["c_in"])), **dev)
+            A = torch.tensor(sweeps.normal(2, (s["K"], info["n_weights"]), std=1.0 / np.sqrt(s["K"])), **dev)
+            gout = torch.tensor(sweeps.normal(3, (g.n_nodes, info["c_out"])), **dev)
+            pos = torch.tensor(g.pos.astype(np.float32), **dev)
+            shift = torch.tensor(g.shift[perm].astype(np.float32), **dev).contiguous()
+            phi = torch.tensor(g.phi[perm].astype(np.float32), **dev).contiguous()
+            graph.upload()
+            conv = cg.Convolution(plan, graph)
+            ws_f, ws_b = conv.workspace(cg.OP_FORWARD), conv.workspace(cg.OP_BACKWARD)
+            out = torch.empty((g.n_nodes, info["c_out"]), **dev)
+            grads = dict(x=torch.empty_like(x), pos=torch.empty_like(pos),
+                         edge_vec=torch.empty((g.n_edges, 3), **dev), phi=torch.empty_like(phi), A=torch.empty_like(A))
+
+            def step():
+                cg.conv_forward(plan, graph, cg.CONVENTIONAL, x, pos, shift, phi, A, out, ws_f)
+                cg.conv_backward(plan, graph, x, pos, shift, phi, A, gout, grad_x=grads["x"], grad_pos=grads["pos"],
+                                 grad_edge_vec=grads["edge_vec"], grad_phi=grads["phi"], grad_A=grads["A"],
+                                 workspace=ws_b)
+
+            for _ in range(warmup):
+                step()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                step()
+            torch.cuda.synchronize()
+            dt = (time.perf_counter() - t0) / steps
+            kernels = {}
+            if args.profile_steps > 0:
+                cg._lib.profile_begin()
+                step()
+                torch.cuda.synchronize()
+                kernels = {k: round(1e3 * ms, 1) for k, (n, ms) in cg._lib.profile_end().items()}
+            line[name] = {"ms_fwd_bwd": round(1e3 * dt, 3), "edges_per_s_fwd_bwd": round(g.n_edges / dt, 1),
+                          "kernel_us": kernels}
+            del graph, conv, ws_f, ws_b, out, grads, x, A, gout, pos, shift, phi
+        line["speedup_degree_order"] = round(line["index"]["ms_fwd_bwd"] / line["degree"]["ms_fwd_bwd"], 3)
+        print(json.dumps(line), flush=True)
+    return 0
+
+
 def sweep(torch, cg, args) -> int:
     """Scaling axis `args.sweep` of the fully connected profiles: streamed forward and backward
     (gradients of x, phi, A and positions) per point, timed separately with the library's default
@@ -520,6 +585,8 @@ def sweep(torch, cg, args) -> int:
     from workloads import sweeps
     if args.sweep in ("channels", "lmax"):
         return channelwise_sweep(torch, cg, args)
+    if args.sweep == "skew":
+        return skew_sweep(torch, cg, args)
 
     points = sweeps.DEGREES if args.sweep == "degree" else sweeps.COPIES
     if args.points:

@@ -29,7 +29,7 @@ EXPORTED = [
     "cgtp_conv_forward", "cgtp_conv_backward", "cgtp_conv_double_backward", "cgtp_check_edges", "cgtp_layout_convert", "cgtp_error_string", "cgtp_last_error",
     "cgtp_state_size", "cgtp_conv_forward_keep_state", "cgtp_conv_backward_with_state",
     "cgtp_profile_begin", "cgtp_profile_end", "cgtp_profile_count", "cgtp_profile_get", "cgtp_measure_peak",
-    "cgtp_conv_forward_static",
+    "cgtp_conv_forward_static", "cgtp_graph_set_order",
 ]
 
 
@@ -70,6 +70,7 @@ def load() -> ctypes.CDLL:
         "cgtp_graph_export": [P, ip, ip, ip, ip],
         "cgtp_graph_dims": [P, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)],
         "cgtp_graph_upload": [P],
+        "cgtp_graph_set_order": [P, I],
         "cgtp_graph_destroy": [P],
         "cgtp_workspace_size": [P, P, I, ctypes.POINTER(Z)],
         "cgtp_conv_forward": [P, P, I, V, V, V, V, V, V, V, Z, V],
@@ -209,6 +210,10 @@ class Graph:
 
     def upload(self) -> None:
         check(load().cgtp_graph_upload(self.handle))
+
+    def set_order(self, mode: int) -> None:
+        """Node dispatch order (before upload): 0 index, 1 by degree, 2 automatic (default)."""
+        check(load().cgtp_graph_set_order(self.handle, int(mode)))
 
 
 def profile_begin() -> None:

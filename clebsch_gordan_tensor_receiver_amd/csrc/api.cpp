@@ -352,6 +352,15 @@ cgtp_status_t cgtp_graph_dims(cgtp_graph_t g, int* n_nodes, int* n_edges) {
   return ok();
 }
 
+cgtp_status_t cgtp_graph_set_order(cgtp_graph_t g, int mode) {
+  if (!g) return fail(CGTP_ERR_INVALID_ARG, "null graph");
+  if (mode < 0 || mode > 2) return fail(CGTP_ERR_INVALID_ARG, "order mode must be 0, 1 or 2");
+  std::lock_guard<std::mutex> lock(g->g.mu);
+  if (!g->g.dev.empty()) return fail(CGTP_ERR_UNSUPPORTED, "set the order before the graph is uploaded");
+  g->g.order_mode = mode;
+  return ok();
+}
+
 cgtp_status_t cgtp_graph_upload(cgtp_graph_t g) {
   if (!g) return fail(CGTP_ERR_INVALID_ARG, "null graph");
   cgtp::DeviceGraph d;
@@ -459,7 +468,10 @@ static cgtp_status_t conv_forward_impl(cgtp_plan_t plan, cgtp_graph_t g, cgtp_sc
         return fail(st, err);
     }
     int per = (nrec + 7) / 8;
-    void* b[] = {(void*)&x, (void*)&phi, (void*)&A, &G_ws, (void*)&d.row_ptr, (void*)&d.col, &out, &i0, &nrec, &per, &e0};
+    // Heaviest-first slot order: valid for a launch over every receiver (per = ceil(N / 8)).
+    const int32_t* ord = (i0 == 0 && nrec == G.n) ? d.rorder : nullptr;
+    void* b[] = {(void*)&x, (void*)&phi, (void*)&A, &G_ws, (void*)&d.row_ptr, (void*)&d.col, &out, &i0, &nrec, &per, &e0,
+                 (void*)&ord};
     if ((st = cgtp::launch(kfwd, unsigned(8 * ngroup * per), 64 * cgtp::fwd_split(p) * tg.ncb, 0, s, b, &err)) != CGTP_OK)
       return fail(st, err);
   }
@@ -590,8 +602,9 @@ static cgtp_status_t conv_backward_impl(cgtp_plan_t plan, cgtp_graph_t g, const 
     if (need_edge || grad_A) {
       int per, nch;
       chunk_geometry(nrec, &per, &nch);
+      const int32_t* ord = (i0 == 0 && nrec == G.n) ? d.rorder : nullptr;
       void* a[] = {(void*)&x, (void*)&phi, (void*)&A, &Gb, (void*)&d.row_ptr, (void*)&d.col, (void*)&grad_out,
-                   &ep, &ap, &i0, &nrec, &per, &nch, &e0, &eps, &acc_slots};
+                   &ep, &ap, &i0, &nrec, &per, &nch, &e0, &eps, &acc_slots, (void*)&ord};
       if ((st = cgtp::launch(krecv, unsigned(8 * nt_r * nch), 64 * kRecvGroup, 0, s, a, &err)) != CGTP_OK)
         return fail(st, err);
     }
@@ -600,7 +613,7 @@ static cgtp_status_t conv_backward_impl(cgtp_plan_t plan, cgtp_graph_t g, const 
       void *sb = nullptr, *se = nullptr;
       if ((st = source_bounds(p, fam, G, d, L, c, ws, s, &sb, &se, &err)) != CGTP_OK) return fail(st, err);
       void* a[] = {(void*)&phi, (void*)&A, &Gb, (void*)&grad_out, (void*)&d.recv, &sb, &se, (void*)&d.src_edge,
-                   &grad_x, &n, &per, &e0, &acc};
+                   &grad_x, &n, &per, &e0, &acc, (void*)&d.sorder};
       if ((st = cgtp::launch(ksrc, unsigned(8 * tsrc.tasks.size() * per), 64 * kSrcSplit * tsrc.ncb, 0, s, a, &err)) !=
           CGTP_OK)
         return fail(st, err);
@@ -717,19 +730,20 @@ cgtp_status_t cgtp_conv_double_backward(cgtp_plan_t plan, cgtp_graph_t g, const 
     void* out_arg = gg_grad_out;
     void* common[] = {(void*)&x, (void*)&vx, (void*)&phi, (void*)&vphi, (void*)&A, (void*)&vA, &Gb,
                       (void*)&d.row_ptr, (void*)&d.col, (void*)&grad_out, &out_arg, &ep, &ap, psx, psphi, psA};
+    const int32_t* ord = (i0 == 0 && nrec == G.n) ? d.rorder : nullptr;
     if (gg_grad_out) {
       int per = (nrec + 7) / 8;
-      void* a[20];
+      void* a[21];
       std::copy(common, common + 16, a);
-      a[16] = &i0; a[17] = &nrec; a[18] = &per; a[19] = &e0;
+      a[16] = &i0; a[17] = &nrec; a[18] = &per; a[19] = &e0; a[20] = (void*)&ord;
       if ((st = cgtp::launch(kfwd, unsigned(8 * nt_f * per), 64, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
     }
     if (need_edge || gg_A) {
       int per, nch;
       chunk_geometry(nrec, &per, &nch);
-      void* a[22];
+      void* a[23];
       std::copy(common, common + 16, a);
-      a[16] = &i0; a[17] = &nrec; a[18] = &per; a[19] = &nch; a[20] = &e0; a[21] = &eps;
+      a[16] = &i0; a[17] = &nrec; a[18] = &per; a[19] = &nch; a[20] = &e0; a[21] = &eps; a[22] = (void*)&ord;
       if ((st = cgtp::launch(krecv, unsigned(8 * nt_r * nch), 64 * kRecvGroup, 0, s, a, &err)) != CGTP_OK)
         return fail(st, err);
     }
@@ -738,7 +752,7 @@ cgtp_status_t cgtp_conv_double_backward(cgtp_plan_t plan, cgtp_graph_t g, const 
       void *sb = nullptr, *se = nullptr;
       if ((st = source_bounds(p, fam, G, d, L, c, ws, s, &sb, &se, &err)) != CGTP_OK) return fail(st, err);
       void* a[] = {(void*)&phi, (void*)&vphi, (void*)&A, (void*)&vA, &Gb, (void*)&grad_out, (void*)&d.recv, &sb, &se,
-                   (void*)&d.src_edge, &gg_x, psphi, psA, &n, &per, &e0, &acc};
+                   (void*)&d.src_edge, &gg_x, psphi, psA, &n, &per, &e0, &acc, (void*)&d.sorder};
       if ((st = cgtp::launch(ksrc, unsigned(8 * nt_s * per), 64, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
     }
     if (need_edge && e1 > e0) {

@@ -619,14 +619,15 @@ void emit_node_dispatch(Out& o, const Plan& p, const std::string& kname, const s
                         const std::string& call, const TaskGroups& tg, int nacc) {
   const int slice = (fwd_split(p) - 1) * nacc * 64;
   o.line(F("extern \"C\" __global__ void __launch_bounds__(%d)", 64 * fwd_split(p) * tg.ncb));
-  o.open(kname + "(" + args + ", int i0, int nrec, int per, int e_base)");
+  // order (nullable): slot -> receiver of a launch over every node, heaviest first per XCD range.
+  o.open(kname + "(" + args + ", int i0, int nrec, int per, int e_base, const int* __restrict__ order)");
   o.line(F("__shared__ real sm[%d];", std::max(1, tg.ncb * slice)));
   o.line("const int b = (int)blockIdx.x;");
   o.line("const int xcd = b & 7, s = b >> 3;");
   o.line("const int t = s / per, il = s - t * per;");
   o.line("const int i = xcd * per + il;");
   o.line("if (i >= nrec) return;");
-  o.line("const int node = i0 + i;");
+  o.line("const int node = order ? order[i] : i0 + i;");
   o.line(F("const int cb = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) / %d;", fwd_split(p)));
   o.line(F("real* const smc = sm + cb * %d;", slice));
   emit_group_switch(o, tg, call + "%T(x, phi, A, G, row_ptr, col, out, smc, node, e_base);", fwd_split(p) > 1);
@@ -856,7 +857,7 @@ void emit_recv_dispatch(Out& o, const Plan& p, int ntask) {
   for (const Task& t : recv_backward_tasks(p)) amax = std::max(amax, int(t.paths.size()) * p.K);
   o.line(F("extern \"C\" __global__ void __launch_bounds__(%d)", 64 * kRecvGroup));
   o.open(std::string("cgtp_bwd_recv(") + kRecvArgs +
-         ", int i0, int nrec, int per, int nch, int e_base, int eps, int acc)");
+         ", int i0, int nrec, int per, int nch, int e_base, int eps, int acc, const int* __restrict__ order)");
   o.line(F("__shared__ real sm[%d];", (kRecvGroup - 1) * amax * 64));
   o.line("const int b = (int)blockIdx.x;");
   o.line("const int xcd = b & 7, s = b >> 3;");
@@ -865,7 +866,7 @@ void emit_recv_dispatch(Out& o, const Plan& p, int ntask) {
   o.line(F("int hi = lo + %d; if (hi > (xcd + 1) * per) hi = (xcd + 1) * per; if (hi > nrec) hi = nrec;", kRecvGroup));
   o.line("if (lo >= hi && acc) return;");
   o.line("const int r = lo + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
-  o.line("const int node = r < hi ? i0 + r : -1;");
+  o.line("const int node = r < hi ? (order ? order[r] : i0 + r) : -1;");
   o.line("const int slot = xcd * nch + c;");
   o.open("switch (t)");
   for (int k = 0; k < ntask; ++k)
@@ -980,13 +981,15 @@ void emit_src_dispatch(Out& o, const Plan& p, int ntask) {
   (void)ntask;
   const int slice = (kSrcSplit - 1) * nacc * 64;
   o.line(F("extern \"C\" __global__ void __launch_bounds__(%d)", 64 * kSrcSplit * tg.ncb));
-  o.open(std::string("cgtp_bwd_src(") + kSrcArgs + ", int nrec, int per, int e_base, int accumulate)");
+  o.open(std::string("cgtp_bwd_src(") + kSrcArgs +
+         ", int nrec, int per, int e_base, int accumulate, const int* __restrict__ order)");
   o.line(F("__shared__ real sm[%d];", std::max(1, tg.ncb * slice)));
   o.line("const int b = (int)blockIdx.x;");
   o.line("const int xcd = b & 7, s = b >> 3;");
   o.line("const int t = s / per, il = s - t * per;");
-  o.line("const int node = xcd * per + il;");
-  o.line("if (node >= nrec) return;");
+  o.line("const int slot = xcd * per + il;");
+  o.line("if (slot >= nrec) return;");
+  o.line("const int node = order ? order[slot] : slot;");
   o.line(F("const int cb = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) / %d;", kSrcSplit));
   o.line(F("real* const smc = sm + cb * %d;", slice));
   emit_group_switch(o, tg, "bws_t%T(phi, A, G, gout, recv, src_beg, src_end, src_edge, gx, smc, node, e_base, accumulate);",
@@ -1276,13 +1279,42 @@ static std::vector<Task> make_source_tasks(const Plan& p) {
   return t;
 }
 
+// Task order of a launch, heaviest first (LunaTP section 4.2, "task ordering": path groups by
+// their count of non-zero CG terms, descending, so that the last workgroups a launch dispatches
+// are light ones).  A task's cost is the CG terms of its paths times its channels; tasks of one
+// feature block (the channel blocks that share a workgroup) move together, ordered by the block's
+// heaviest task; ties keep the plan order.
+std::vector<Task> heaviest_first(const Plan& p, std::vector<Task> tasks) {
+  auto cost = [&](const Task& t) {
+    long long c = 0;
+    for (int pi : t.paths) c += (long long)p.paths[pi].terms.size();
+    return c * std::max(1, std::min(64, p.paths[t.paths[0]].n_w - 64 * t.cb));
+  };
+  std::map<int, long long> group_cost;
+  for (const Task& t : tasks) group_cost[t.group] = std::max(group_cost[t.group], cost(t));
+  std::stable_sort(tasks.begin(), tasks.end(), [&](const Task& a, const Task& b) {
+    const long long ca = group_cost[a.group], cb = group_cost[b.group];
+    if (ca != cb) return ca > cb;
+    return a.group < b.group;
+  });
+  return tasks;
+}
+
 const TaskTables& task_tables(const Plan& p) {
   std::call_once(p.tables_once, [&p] {
     auto t = std::make_unique<TaskTables>();
-    t->fwd = make_forward_tasks(p);
+    t->fwd = heaviest_first(p, make_forward_tasks(p));
     t->recv = make_recv_backward_tasks(p);
+    std::stable_sort(t->recv.begin(), t->recv.end(), [&p](const Task& a, const Task& b) {
+      auto c = [&p](const Task& t) {
+        long long n = 0;
+        for (int pi : t.paths) n += (long long)p.paths[pi].terms.size();
+        return n;
+      };
+      return c(a) > c(b);
+    });
     t->dbl_recv = make_dbl_recv_tasks(p);
-    t->src = make_source_tasks(p);
+    t->src = heaviest_first(p, make_source_tasks(p));
     for (const Task& k : t->recv) t->recv_row += recv_task_width(p, k);
     for (const Task& k : t->dbl_recv) t->dbl_row += dbl_task_width(p, k);
     p.tables = std::move(t);

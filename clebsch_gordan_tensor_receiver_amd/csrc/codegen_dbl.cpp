@@ -510,14 +510,16 @@ std::string generate_dbl_source(const Plan& p, std::string* err) {
   auto ft = forward_tasks(p);
   for (int k = 0; k < int(ft.size()); ++k) emit_dfwd_task(o, p, k, ft[k]);
   o.line("extern \"C\" __global__ void __launch_bounds__(64)");
-  o.open(std::string("cgtp_dfwd(") + kDArgs + ", int i0, int nrec, int per, int e_base)");
+  // order (nullable): slot -> node of a launch over every node, heaviest first per XCD range.
+  o.open(std::string("cgtp_dfwd(") + kDArgs + ", int i0, int nrec, int per, int e_base, const int* __restrict__ order)");
   o.line("const int b = (int)blockIdx.x;");
   o.line("const int xcd = b & 7, s = b >> 3;");
   o.line("const int t = s / per, i = xcd * per + (s - t * per);");
   o.line("if (i >= nrec) return;");
+  o.line("const int node = order ? order[i] : i0 + i;");
   o.open("switch (t)");
   for (int k = 0; k < int(ft.size()); ++k)
-    o.line(F("case %d: dfw_t%d(x, vx, phi, vphi, A, vA, G, row_ptr, col, gout, out, ep, ap, sx, sphi, sA, i0 + i, e_base);"
+    o.line(F("case %d: dfw_t%d(x, vx, phi, vphi, A, vA, G, row_ptr, col, gout, out, ep, ap, sx, sphi, sA, node, e_base);"
              " break;", k, k));
   o.line("default: break;");
   o.close();
@@ -530,7 +532,8 @@ std::string generate_dbl_source(const Plan& p, std::string* err) {
     amax = std::max(amax, int(rt[k].paths.size()) * p.K);
   }
   o.line("extern \"C\" __global__ void __launch_bounds__(256)");
-  o.open(std::string("cgtp_drecv(") + kDArgs + ", int i0, int nrec, int per, int nch, int e_base, int eps)");
+  o.open(std::string("cgtp_drecv(") + kDArgs +
+         ", int i0, int nrec, int per, int nch, int e_base, int eps, const int* __restrict__ order)");
   o.line(F("__shared__ real sm[%d];", 3 * amax * 64));
   o.line("const int b = (int)blockIdx.x;");
   o.line("const int xcd = b & 7, s = b >> 3;");
@@ -539,7 +542,7 @@ std::string generate_dbl_source(const Plan& p, std::string* err) {
   o.line("int hi = lo + 4; if (hi > (xcd + 1) * per) hi = (xcd + 1) * per; if (hi > nrec) hi = nrec;");
   o.line("if (lo >= hi) return;");
   o.line("const int r = lo + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
-  o.line("const int node = r < hi ? i0 + r : -1;");
+  o.line("const int node = r < hi ? (order ? order[r] : i0 + r) : -1;");
   o.line("const int slot = xcd * nch + c;");
   o.open("switch (t)");
   for (int k = 0; k < int(rt.size()); ++k)
@@ -551,11 +554,13 @@ std::string generate_dbl_source(const Plan& p, std::string* err) {
   auto st = source_tasks(p);
   for (int k = 0; k < int(st.size()); ++k) emit_dsrc_task(o, p, k, st[k]);
   o.line("extern \"C\" __global__ void __launch_bounds__(64)");
-  o.open(std::string("cgtp_dsrc(") + kDSrcArgs + ", int nrec, int per, int e_base, int accumulate)");
+  o.open(std::string("cgtp_dsrc(") + kDSrcArgs +
+         ", int nrec, int per, int e_base, int accumulate, const int* __restrict__ order)");
   o.line("const int b = (int)blockIdx.x;");
   o.line("const int xcd = b & 7, s = b >> 3;");
-  o.line("const int t = s / per, node = xcd * per + (s - t * per);");
-  o.line("if (node >= nrec) return;");
+  o.line("const int t = s / per, slot = xcd * per + (s - t * per);");
+  o.line("if (slot >= nrec) return;");
+  o.line("const int node = order ? order[slot] : slot;");
   o.open("switch (t)");
   for (int k = 0; k < int(st.size()); ++k)
     o.line(F("case %d: dsr_t%d(phi, vphi, A, vA, G, gout, recv, src_beg, src_end, src_edge, gx, sphi, sA, node, e_base,"

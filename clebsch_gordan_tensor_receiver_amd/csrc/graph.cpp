@@ -81,6 +81,33 @@ std::vector<std::pair<int, int>> Graph::chunks(long long cap, long long rcap) co
   return out;
 }
 
+// Automatic mode orders by degree when the in-degrees are skewed: the largest exceeds twice the mean.
+bool Graph::degree_order() const {
+  if (order_mode == kOrderIndex) return false;
+  if (order_mode == kOrderDegree) return true;
+  return n > 0 && e > 0 && double(max_in_degree) > 2.0 * double(e) / double(n);
+}
+
+namespace {
+
+// Slot order of a launch over all n nodes (LunaTP section 4.2, "task ordering": nodes by degree,
+// descending, heaviest tasks first).  Slots are dealt to the 8 XCDs in contiguous ranges of
+// ceil(n / 8) (the kernels' block -> XCD mapping), so each XCD keeps its own range of nodes and its
+// L2 locality; inside a range the nodes are sorted by descending degree, ties by index.
+std::vector<int32_t> degree_slots(const std::vector<int32_t>& ptr, int n) {
+  std::vector<int32_t> ord(static_cast<size_t>(n));
+  std::iota(ord.begin(), ord.end(), 0);
+  const int per = (n + 7) / 8;
+  for (int x = 0; x < 8; ++x) {
+    const int a = std::min(n, x * per), b = std::min(n, (x + 1) * per);
+    std::stable_sort(ord.begin() + a, ord.begin() + b,
+                     [&](int32_t i, int32_t j) { return ptr[i + 1] - ptr[i] > ptr[j + 1] - ptr[j]; });
+  }
+  return ord;
+}
+
+}  // namespace
+
 cgtp_status_t device_graph(Graph& g, DeviceGraph* out, std::string* err) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
@@ -95,7 +122,13 @@ cgtp_status_t device_graph(Graph& g, DeviceGraph* out, std::string* err) {
   }
   size_t n1 = size_t(g.n) + 1, ne = size_t(g.e);
   auto al = [](size_t n) { return (n * sizeof(int32_t) + 255) / 256 * 256; };
-  size_t bytes = 2 * al(n1) + 3 * al(std::max<size_t>(ne, 1));
+  const bool ordered = g.degree_order();
+  std::vector<int32_t> rorder, sorder;
+  if (ordered) {
+    rorder = degree_slots(g.row_ptr, g.n);
+    sorder = degree_slots(g.src_ptr, g.n);
+  }
+  size_t bytes = 2 * al(n1) + 3 * al(std::max<size_t>(ne, 1)) + (ordered ? 2 * al(size_t(g.n)) : 0);
   DeviceGraph d;
   hipError_t e = hipMalloc(&d.base, bytes);
   if (e != hipSuccess) {
@@ -112,11 +145,17 @@ cgtp_status_t device_graph(Graph& g, DeviceGraph* out, std::string* err) {
   d.recv = reinterpret_cast<int32_t*>(p);
   p += al(std::max<size_t>(ne, 1));
   d.src_edge = reinterpret_cast<int32_t*>(p);
+  p += al(std::max<size_t>(ne, 1));
+  if (ordered) {
+    d.rorder = reinterpret_cast<int32_t*>(p);
+    p += al(size_t(g.n));
+    d.sorder = reinterpret_cast<int32_t*>(p);
+  }
   struct {
     int32_t* dst;
     const std::vector<int32_t>* src;
   } copies[] = {{d.row_ptr, &g.row_ptr}, {d.src_ptr, &g.src_ptr}, {d.col, &g.col}, {d.recv, &g.recv},
-                {d.src_edge, &g.src_edge}};
+                {d.src_edge, &g.src_edge}, {d.rorder, &rorder}, {d.sorder, &sorder}};
   for (auto& c : copies) {
     if (c.src->empty()) continue;
     e = hipMemcpy(c.dst, c.src->data(), c.src->size() * sizeof(int32_t), hipMemcpyHostToDevice);

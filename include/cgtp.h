@@ -161,6 +161,21 @@ cgtp_status_t cgtp_graph_export(cgtp_graph_t g, int32_t* row_ptr, int32_t* col, 
                                 int32_t* src_edge);
 cgtp_status_t cgtp_graph_dims(cgtp_graph_t g, int* n_nodes, int* n_edges);
 
+/* Node dispatch order of the channelwise kernels (LunaTP section 4.2, "task ordering": heavier
+ * tasks first, so that a launch does not end on a tail of heavy workgroups):
+ *   0  index order;
+ *   1  by degree: a launch over every node deals the nodes to the 8 XCDs in contiguous index
+ *      ranges of ceil(N / 8) (each XCD keeps its neighbourhood in its L2) and runs each range in
+ *      descending in-degree (receiver passes) or out-degree (source passes), ties by index;
+ *   2  automatic (default): 1 when the in-degrees are skewed (the largest above twice the mean),
+ *      else 0.
+ * Launches over part of the receivers (a graph split into receiver chunks by the scratch budget)
+ * run in index order.  Tasks (feature blocks and path subsets) are always dispatched heaviest
+ * first by their count of CG terms.  The order changes no result beyond the order of the
+ * fixed-order grad_A partial sums.  Call before cgtp_graph_upload (UNSUPPORTED afterwards);
+ * INVALID_ARG for another mode. */
+cgtp_status_t cgtp_graph_set_order(cgtp_graph_t g, int mode);
+
 /* Upload the CSR to the current device (once per device; later calls return at once).
  * The convolution calls do it themselves on first use; call it before a timed region. */
 cgtp_status_t cgtp_graph_upload(cgtp_graph_t g);

@@ -132,7 +132,31 @@ def copies_graph(copies: int) -> SweepGraph:
     return _finish("copies", copies, pos, box, rc, recv, send, image)
 
 
+# Skewed in-degrees (the "task ordering" setting of LunaTP section 4.2): 4,096 uniform positions at
+# DENSITY; receiver i keeps the senders within its own cutoff, chosen for an expected degree
+# d_i = 32 exp(sigma z_i), z_i ~ N(0, 1) (stream 12), clipped to [4, 1024].  Point = 10 sigma.
+SKEW_POINTS = (0, 5, 10, 15)
+# The channelwise profile measured on it: the l <= 3, 128-channel irreps of the diamond workload
+# with this module's K = 16 Gaussian radial functions.
+SKEW_PROFILE = dict(irreps_in=_alt(2, 128, 128), irreps_sh=_sh(3), irreps_out=_alt(3, 128, 128), mode="uvu",
+                    dtype="float32", K=K)
+
+
+def skew_graph(point: int, n: int = 4096) -> SweepGraph:
+    sigma = point / 10.0
+    pos, box = _uniform(n, 11)
+    z = _rng(12).normal(size=n)
+    deg = np.clip(np.round(32.0 * np.exp(sigma * z)), 4, 1024)
+    rcut = np.array([_cutoff(d) for d in deg])
+    recv, send, image = neighbour_list(pos, box, float(rcut.max()))
+    r = np.linalg.norm(pos[send] - pos[recv] + image * box[None, :], axis=1)
+    keep = r < rcut[recv]
+    return _finish("skew", point, pos, box, float(rcut.max()), recv[keep], send[keep], image[keep])
+
+
 def sweep_graph(axis: str, point: int) -> SweepGraph:
+    if axis == "skew":
+        return skew_graph(point)
     return degree_graph(point) if axis == "degree" else copies_graph(point)
 
 
