@@ -75,10 +75,19 @@ def _angular(problem: Problem, p, x: torch.Tensor, Y: torch.Tensor, send: torch.
 def forward_conventional(problem: Problem, x, edge_vec, recv, send, phi, A,
                          edge_chunk: int = 1 << 14) -> torch.Tensor:
     """Sobek Eqs. 11-12: materialise W = phi A per path, form each edge message, sum into receivers."""
-    x, phi, A = _t(x), _t(phi), _t(A)
-    recv, send = _idx(recv), _idx(send)
-    N, E = x.shape[0], recv.shape[0]
     Y = spherical_harmonics(problem, edge_vec)
+    return forward_from_sh(problem, x, Y, recv, send, phi, A, edge_chunk=edge_chunk)
+
+
+def forward_from_sh(problem: Problem, x, Y, recv, send, phi, A, n_nodes: Optional[int] = None,
+                    edge_chunk: int = 1 << 14) -> torch.Tensor:
+    """The conventional forward with the edge operand given: Y (E x sh_dim) holds the angular edge
+    values (the real harmonics of the edge directions in forward_conventional; LunaTP Eq. 1 and
+    Algorithm 1 take them as the input y)."""
+    x, phi, A, Y = _t(x), _t(phi), _t(A), _t(Y)
+    recv, send = _idx(recv), _idx(send)
+    N = x.shape[0] if n_nodes is None else n_nodes
+    E = recv.shape[0]
     out = torch.zeros(N, problem.c_out, dtype=_F64)
     for p in problem.paths:
         bo = problem.irreps_out[p.i_out]
@@ -320,3 +329,90 @@ def double_backward(problem: Problem, x, edge_vec, recv, send, phi, A, grad_out,
     gg["edge_vec"] = ge
     gg["pos"] = gpos
     return gg
+
+
+# --------------------------------------------------------------------------------------------
+# Third-order derivative (LunaTP Appendix F, Algorithm 4), channelwise.
+#
+# The operands are those of the page's algorithm: node features x, the angular edge operand Y
+# (E x sh_dim, the harmonics of the edge directions), the edge weights w = phi A (kept factored:
+# phi per edge, A shared) and the output cotangent g.  With these the convolution is the 4-linear
+# form Phi(a, b, c, d) = sum_e sum_paths sum_u c_e,u sum C a_send(e),m1,u b_e,m2 d_recv(e),m3,u.
+# The first-order outputs are the gradients of Phi(x, Y, w, g); the second-order ones (directions
+# v = (v_x, v_Y, v_phi, v_A)) the gradients of
+#   S2 = Phi(v_x, Y, w, g) + Phi(x, v_Y, w, g) + Phi(x, Y, wv, g),   wv = v_phi A + phi v_A;
+# the third-order ones (cotangents q = (q_x, q_Y, q_phi, q_A, q_g) of the second-order outputs)
+# the gradients of S3 = <q, grad S2>, the derivative of S2 along q, with respect to
+# x, Y, phi, A, g and the directions v.  With wq = q_phi A + phi q_A and wvq = v_phi q_A + q_phi v_A:
+_TRIPLE_TERMS = (
+    # (a, b, weight factors (phi-type, A-type), d)
+    ("v_x", "q_Y", (("phi", "A"),), "g"),
+    ("v_x", "Y", (("q_phi", "A"), ("phi", "q_A")), "g"),
+    ("v_x", "Y", (("phi", "A"),), "q_g"),
+    ("q_x", "v_Y", (("phi", "A"),), "g"),
+    ("x", "v_Y", (("q_phi", "A"), ("phi", "q_A")), "g"),
+    ("x", "v_Y", (("phi", "A"),), "q_g"),
+    ("q_x", "Y", (("v_phi", "A"), ("phi", "v_A")), "g"),
+    ("x", "q_Y", (("v_phi", "A"), ("phi", "v_A")), "g"),
+    ("x", "Y", (("v_phi", "q_A"), ("q_phi", "v_A")), "g"),
+    ("x", "Y", (("v_phi", "A"), ("phi", "v_A")), "q_g"),
+)
+# Outputs: the variables of S3 that are not cotangents.
+TRIPLE_OUTPUTS = ("x", "Y", "phi", "A", "g", "v_x", "v_Y", "v_phi", "v_A")
+
+
+def triple_backward(problem: Problem, x, Y, recv, send, phi, A, grad_out, v_x=None, v_Y=None, v_phi=None,
+                    v_A=None, q_x=None, q_Y=None, q_phi=None, q_A=None, q_grad_out=None,
+                    n_nodes: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """Gradients of S3 (above) with respect to x, Y, phi, A, g (key "g") and v_x, v_Y, v_phi, v_A.
+
+    S3 is the sum of the ten terms of _TRIPLE_TERMS.  Each term is linear in each of its four
+    slots, so its gradient with respect to the variable in a slot is the form with that slot left
+    open; a weight slot c = sum_k phi_k A_k passes H = dPhi/dc on as dc/dphi_k = H A_k^T and
+    dc/dA_k = phi_k^T H.  Missing directions and cotangents are zero (their terms vanish).
+    """
+    if problem.mode != "uvu":
+        raise ValueError("the third-order oracle covers the channelwise mode")
+    x, Y, phi, A, g = _t(x), _t(Y), _t(phi), _t(A), _t(grad_out)
+    recv, send = _idx(recv), _idx(send)
+    N = x.shape[0] if n_nodes is None else n_nodes
+    E = recv.shape[0]
+    z = dict(x=x, Y=Y, phi=phi, A=A, g=g,
+             v_x=None if v_x is None else _t(v_x), v_Y=None if v_Y is None else _t(v_Y),
+             v_phi=None if v_phi is None else _t(v_phi), v_A=None if v_A is None else _t(v_A),
+             q_x=None if q_x is None else _t(q_x), q_Y=None if q_Y is None else _t(q_Y),
+             q_phi=None if q_phi is None else _t(q_phi), q_A=None if q_A is None else _t(q_A),
+             q_g=None if q_grad_out is None else _t(q_grad_out))
+    shapes = dict(x=x.shape, Y=Y.shape, phi=phi.shape, A=A.shape, g=(N, problem.c_out))
+    out = {k: torch.zeros(shapes[k.replace("v_", "")], dtype=_F64) for k in TRIPLE_OUTPUTS}
+    for a_name, b_name, factors, d_name in _TRIPLE_TERMS:
+        factors = tuple(f for f in factors if z[f[0]] is not None and z[f[1]] is not None)
+        if z[a_name] is None or z[b_name] is None or z[d_name] is None or not factors:
+            continue
+        a, b, d = z[a_name], z[b_name], z[d_name]
+        for p in problem.paths:
+            bi, bs, bo = problem.irreps_in[p.i_in], problem.irreps_sh[p.i_sh], problem.irreps_out[p.i_out]
+            c = _coupling(p)
+            cols = slice(p.weight_offset, p.weight_offset + p.n_weights)
+            ae = _block(a, bi)[send]                      # (E, d1, C)
+            be = b[:, bs.offset:bs.offset + bs.dim]       # (E, d2)
+            de = _block(d, bo)[recv]                      # (E, d3, C)
+            w = sum(z[fp] @ z[fA][:, cols] for fp, fA in factors)   # (E, C)
+            if a_name in out:        # slot a open: sum over the sender's out-edges
+                ga = torch.zeros(N, bi.dim, bi.mul, dtype=_F64)
+                ga.index_add_(0, send, torch.einsum("abc,eb,ecu,eu->eau", c, be, de, w))
+                out[a_name][:, bi.offset:bi.offset + bi.size] += ga.reshape(N, -1)[:x.shape[0]]
+            if b_name in out:        # slot b open: per edge, summed over channels
+                out[b_name][:, bs.offset:bs.offset + bs.dim] += torch.einsum("abc,eau,ecu,eu->eb", c, ae, de, w)
+            if d_name in out:        # slot d open: sum over the receiver's in-edges
+                gd = torch.zeros(N, bo.dim, bo.mul, dtype=_F64)
+                gd.index_add_(0, recv, torch.einsum("abc,eau,eb,eu->ecu", c, ae, be, w))
+                out[d_name][:, bo.offset:bo.offset + bo.size] += gd.reshape(N, -1)
+            H = torch.einsum("abc,eau,eb,ecu->eu", c, ae, be, de)   # slot c open: (E, C)
+            for fp, fA in factors:
+                if fp in out:
+                    out[fp] += H @ z[fA][:, cols].T
+                if fA in out:
+                    out[fA][:, cols] += z[fp].T @ H
+    out["grad_out"] = out.pop("g")
+    return out

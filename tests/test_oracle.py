@@ -561,3 +561,83 @@ def test_position_gradient_through_the_radial_basis(kind):
         fd = (L(pp) - L(pm)) / (2 * h)
         got = float(gpos[idx])
         assert abs(fd - got) <= 1e-6 * max(1.0, abs(got)), (kind, idx, fd, got)
+
+
+# ------------------------------------------------------------------ third-order derivative
+
+def _triple_case(n_nodes=10, seed=41, with_y_dirs=True):
+    """A small channelwise problem with every operand of the third-order derivative: the edge
+    operand Y is the harmonics of the edge vectors; directions and cotangents are N(0, 1)."""
+    ov = dict(irreps_in="2x0e+2x1o+2x2e", irreps_out="2x0e+2x1o+2x2e", irreps_sh=_sh_str(2))
+    c = make_case(1, irreps_override=ov, n_nodes=n_nodes)
+    Y = conv.spherical_harmonics(c.problem, c.edge_vec).numpy()
+    rng = np.random.default_rng(seed)
+    nrm = lambda shape: rng.normal(size=shape)  # noqa: E731
+    d = dict(v_x=nrm(c.x.shape), v_Y=nrm(Y.shape) if with_y_dirs else None, v_phi=nrm(c.phi.shape),
+             v_A=nrm(c.A.shape), q_x=nrm(c.x.shape), q_Y=nrm(Y.shape) if with_y_dirs else None,
+             q_phi=nrm(c.phi.shape), q_A=nrm(c.A.shape), q_grad_out=nrm(c.grad_out.shape))
+    return c, Y, d
+
+
+def test_triple_backward_matches_third_order_autograd():
+    """The explicit third-order formulas against autograd taken three times over the oracle
+    forward with the edge operand given: f = <g, m(x, Y, phi, A)>, S2 = <v, grad f>,
+    S3 = <q, grad S2>, T = grad S3 (LunaTP Appendix F, Algorithms 2-4 in that nesting)."""
+    c, Y, d = _triple_case()
+    leaf = lambda a: torch.tensor(np.asarray(a), dtype=torch.float64, requires_grad=True)  # noqa: E731
+    x, Yt, phi, A, g = leaf(c.x), leaf(Y), leaf(c.phi), leaf(c.A), leaf(c.grad_out)
+    vx, vY, vphi, vA = leaf(d["v_x"]), leaf(d["v_Y"]), leaf(d["v_phi"]), leaf(d["v_A"])
+    f = (conv.forward_from_sh(c.problem, x, Yt, c.recv, c.send, phi, A) * g).sum()
+    gx, gY, gphi, gA = torch.autograd.grad(f, (x, Yt, phi, A), create_graph=True)
+    S2 = (vx * gx).sum() + (vY * gY).sum() + (vphi * gphi).sum() + (vA * gA).sum()
+    D = torch.autograd.grad(S2, (x, Yt, phi, A, g), create_graph=True)
+    qs = [torch.as_tensor(d[k]) for k in ("q_x", "q_Y", "q_phi", "q_A", "q_grad_out")]
+    S3 = sum((q * Dk).sum() for q, Dk in zip(qs, D))
+    want = torch.autograd.grad(S3, (x, Yt, phi, A, g, vx, vY, vphi, vA))
+    got = conv.triple_backward(c.problem, c.x, Y, c.recv, c.send, c.phi, c.A, c.grad_out, **d)
+    for k, w in zip(("x", "Y", "phi", "A", "grad_out", "v_x", "v_Y", "v_phi", "v_A"), want):
+        ref = w.detach().numpy()
+        err = np.abs(got[k].numpy() - ref).max() / np.abs(ref).max()
+        assert np.abs(ref).max() > 0, k
+        assert err < 1e-12, (k, err)
+
+
+def test_triple_backward_finite_differences_of_double_backward():
+    """With the edge operand held fixed (no Y directions), S3 = <q, second-order outputs> is
+    computed by the position-level double backward (its edge-vector direction zero); central
+    differences of S3 in x, phi, A, g and the directions pin the third-order outputs."""
+    c, Y, d = _triple_case(with_y_dirs=False)
+
+    def S3(x=c.x, phi=c.phi, A=c.A, g=c.grad_out, v_x=d["v_x"], v_phi=d["v_phi"], v_A=d["v_A"]):
+        dd = conv.double_backward(c.problem, x, c.edge_vec, c.recv, c.send, phi, A, g, v_x=v_x, v_phi=v_phi, v_A=v_A)
+        return float((torch.as_tensor(d["q_x"]) * dd["x"]).sum() + (torch.as_tensor(d["q_phi"]) * dd["phi"]).sum()
+                     + (torch.as_tensor(d["q_A"]) * dd["A"]).sum()
+                     + (torch.as_tensor(d["q_grad_out"]) * dd["grad_out"]).sum())
+
+    got = conv.triple_backward(c.problem, c.x, Y, c.recv, c.send, c.phi, c.A, c.grad_out, **d)
+    rng = np.random.default_rng(43)
+    base = dict(x=c.x, phi=c.phi, A=c.A, g=c.grad_out, v_x=d["v_x"], v_phi=d["v_phi"], v_A=d["v_A"])
+    keys = dict(x="x", phi="phi", A="A", g="grad_out", v_x="v_x", v_phi="v_phi", v_A="v_A")
+    h = 1e-3
+    for k, out_key in keys.items():
+        delta = rng.normal(size=np.shape(base[k]))
+        plus = dict(base, **{k: base[k] + h * delta})
+        minus = dict(base, **{k: base[k] - h * delta})
+        fd = (S3(**plus) - S3(**minus)) / (2 * h)
+        an = float((got[out_key].numpy() * delta).sum())
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (k, fd, an)
+
+
+def test_triple_backward_direction_gradients_are_second_order_outputs():
+    """Symmetry of mixed partials: the gradients with respect to the directions v equal the
+    second-order outputs along the cotangents q plus the first-order outputs for the output
+    cotangent q_g (edge operand fixed: no Y directions)."""
+    c, Y, d = _triple_case(with_y_dirs=False)
+    got = conv.triple_backward(c.problem, c.x, Y, c.recv, c.send, c.phi, c.A, c.grad_out, **d)
+    dd = conv.double_backward(c.problem, c.x, c.edge_vec, c.recv, c.send, c.phi, c.A, c.grad_out,
+                              v_x=d["q_x"], v_phi=d["q_phi"], v_A=d["q_A"])
+    b = conv.backward(c.problem, c.x, c.edge_vec, c.recv, c.send, c.phi, c.A, d["q_grad_out"])
+    for k in ("x", "phi", "A"):
+        ref = (dd[k] + b[k]).numpy()
+        err = np.abs(got["v_" + k].numpy() - ref).max() / np.abs(ref).max()
+        assert err < 1e-12, (k, err)
