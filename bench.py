@@ -211,6 +211,12 @@ def main() -> int:
     ap.add_argument("--radial", action="store_true",
                     help="compute the radial basis in the kernels from |r| (Bessel + envelope; Gaussians for "
                          "workload 5) instead of reading phi")
+    ap.add_argument("--order", type=int, default=2, choices=(0, 1, 2),
+                    help="node dispatch order of the graph: 0 index, 1 by degree, 2 automatic (default)")
+    ap.add_argument("--triple", action="store_true",
+                    help="measure the third-order derivative (LunaTP Algorithm 4) on the workload's graph and "
+                         "irreps, edge operand = the harmonics of the edge vectors, all directions and cotangents "
+                         "present, fp32/fp64 as the workload")
     ap.add_argument("--points", default="",
                     help="comma-separated sweep points (degrees or copy counts); default: the whole axis")
     args = ap.parse_args()
@@ -246,9 +252,12 @@ def main() -> int:
             return 2
         plan.set_radial(2 if spec["radial"] == "gaussian" else 1, spec["rc"])
     graph = cg.Graph(w.n_nodes, w.recv, w.send, w.image)
+    graph.set_order(args.order)
     perm = graph.perm
     info = plan.info
     K, E, N = spec["K"], graph.n_edges, w.n_nodes
+    if args.triple:
+        return triple_bench(torch, cg, args, cfg, spec, w, plan, graph)
     tdt = torch.float64 if dtype == "float64" else torch.float32
     dev = dict(dtype=tdt, device="cuda")
     rnd = (lambda a: a.astype(np.float32).astype(np.float64)) if dtype == "float32" else (lambda a: a)
@@ -663,6 +672,60 @@ def sweep(torch, cg, args) -> int:
 
 
 COPY_BYTES = 256 << 20
+
+
+def triple_bench(torch, cg, args, cfg, spec, w, plan, graph):
+    """Third-order derivative (cgtp_conv_triple_backward) on a standard workload: one JSON line with
+    the time per call (HIP events around each call, median) and edges/s, and per-kernel times."""
+    from workloads import normal_tensor
+    dtype = spec["dtype"]
+    tdt = torch.float64 if dtype == "float64" else torch.float32
+    dev = dict(dtype=tdt, device="cuda")
+    info = plan.info
+    N, E, K = w.n_nodes, graph.n_edges, spec["K"]
+    perm = graph.perm
+    rnd = (lambda a: a.astype(np.float32).astype(np.float64)) if dtype == "float32" else (lambda a: a)
+    # The edge operand: any E x sh_dim values drive the same kernels; seeded N(0, 1) draws stand in
+    # for the harmonics (the bench does not evaluate the method's arithmetic on the host).
+    shapes = dict(x=(N, info["c_in"]), Y=(E, info["sh_dim"]), phi=(E, K), A=(K, info["n_weights"]),
+                  grad_out=(N, info["c_out"]))
+    h = dict(x=normal_tensor(cfg, 1, shapes["x"], dtype=dtype), Y=normal_tensor(cfg, 30, shapes["Y"], dtype=dtype),
+             phi=rnd(w.phi[perm]), A=normal_tensor(cfg, 2, shapes["A"], std=1.0 / np.sqrt(K), dtype=dtype),
+             grad_out=normal_tensor(cfg, 3, shapes["grad_out"], dtype=dtype))
+    for s_, name in enumerate(("v_x", "v_Y", "v_phi", "v_A", "q_x", "q_Y", "q_phi", "q_A", "q_grad_out")):
+        h[name] = normal_tensor(cfg, 20 + s_, shapes[name[2:]], dtype=dtype)
+    t = {k: torch.tensor(np.ascontiguousarray(v), **dev) for k, v in h.items()}
+    plan.compile((cg.OP_TRIPLE_BACKWARD,))
+    graph.upload()
+    conv = cg.Convolution(plan, graph)
+    ws = conv.workspace(cg.OP_TRIPLE_BACKWARD)
+    outs = {k: torch.empty_like(t[k.replace("v_", "")]) for k in cg._lib.TRIPLE_OUTPUTS}
+
+    def call():
+        cg._lib.conv_triple_backward(plan, graph, t, outs, ws)
+
+    for _ in range(max(3, args.warmup)):
+        call()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record()
+    for k in range(args.steps):
+        call()
+        evs[k + 1].record()
+    torch.cuda.synchronize()
+    ms = sorted(evs[k].elapsed_time(evs[k + 1]) for k in range(args.steps))
+    med = ms[len(ms) // 2]
+    kernels = {}
+    cg._lib.profile_begin()
+    call()
+    torch.cuda.synchronize()
+    for name, (n, tot) in cg._lib.profile_end().items():
+        kernels[name] = {"launches": n, "us": round(1e3 * tot, 1)}
+    line = {"pass": "triple backward", "workload": cfg, "n_nodes": N, "n_edges": E, "dtype": dtype,
+            "irreps_in": spec["irreps_in"], "steps": args.steps, "median_ms": round(med, 3),
+            "edges_per_s": round(E / (med * 1e-3), 1), "workspace_bytes": int(ws.numel()), "kernel_us": kernels}
+    print(json.dumps(line), flush=True)
+    return 0
 
 
 def measured_peaks(torch, cg, dtype):

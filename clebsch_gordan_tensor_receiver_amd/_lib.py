@@ -20,7 +20,7 @@ CHANNELWISE, FULLY_CONNECTED = 0, 1
 F32, F64 = 0, 1
 STREAMED, CONVENTIONAL = 0, 1
 DEGENERATE_EDGE = 4
-OP_FORWARD, OP_BACKWARD, OP_DOUBLE_BACKWARD = 0, 1, 2
+OP_FORWARD, OP_BACKWARD, OP_DOUBLE_BACKWARD, OP_TRIPLE_BACKWARD = 0, 1, 2, 3
 
 EXPORTED = [
     "cgtp_plan_create", "cgtp_plan_destroy", "cgtp_plan_info", "cgtp_plan_path", "cgtp_plan_cg_table",
@@ -29,7 +29,7 @@ EXPORTED = [
     "cgtp_conv_forward", "cgtp_conv_backward", "cgtp_conv_double_backward", "cgtp_check_edges", "cgtp_layout_convert", "cgtp_error_string", "cgtp_last_error",
     "cgtp_state_size", "cgtp_conv_forward_keep_state", "cgtp_conv_backward_with_state",
     "cgtp_profile_begin", "cgtp_profile_end", "cgtp_profile_count", "cgtp_profile_get", "cgtp_measure_peak",
-    "cgtp_conv_forward_static", "cgtp_graph_set_order",
+    "cgtp_conv_forward_static", "cgtp_graph_set_order", "cgtp_conv_triple_backward",
 ]
 
 
@@ -76,6 +76,7 @@ def load() -> ctypes.CDLL:
         "cgtp_conv_forward": [P, P, I, V, V, V, V, V, V, V, Z, V],
         "cgtp_conv_backward": [P, P, V, V, V, V, V, V, V, V, V, V, V, V, Z, V],
         "cgtp_conv_double_backward": [P, P] + [V] * 18 + [Z, V],
+        "cgtp_conv_triple_backward": [P, P] + [V] * 24 + [Z, V],
         "cgtp_state_size": [P, P, ctypes.POINTER(Z)],
         "cgtp_conv_forward_keep_state": [P, P, V, V, V, V, V, V, V, Z, V, Z, V],
         "cgtp_conv_backward_with_state": [P, P, V, V, V, V, V, V, V, Z, V, V, V, V, V, V, Z, V],
@@ -315,6 +316,19 @@ def conv_double_backward(plan: Plan, graph: Graph, x, pos, shift, phi, A, grad_o
         workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+TRIPLE_INPUTS = ("x", "Y", "phi", "A", "grad_out", "v_x", "v_Y", "v_phi", "v_A", "q_x", "q_Y", "q_phi", "q_A",
+                 "q_grad_out")
+TRIPLE_OUTPUTS = ("x", "Y", "phi", "A", "grad_out", "v_x", "v_Y", "v_phi", "v_A")
+
+
+def conv_triple_backward(plan: Plan, graph: Graph, inputs: dict, outputs: dict, workspace, stream=None):
+    """cgtp_conv_triple_backward: `inputs` maps TRIPLE_INPUTS names to device tensors (missing
+    directions / cotangents = zero), `outputs` maps TRIPLE_OUTPUTS names to device tensors to fill."""
+    args = [_ptr(inputs.get(k)) for k in TRIPLE_INPUTS] + [_ptr(outputs.get(k)) for k in TRIPLE_OUTPUTS]
+    check(load().cgtp_conv_triple_backward(plan.handle, graph.handle, *args, _ptr(workspace), _nbytes(workspace),
+                                           _stream(stream)))
+
+
 def layout_convert(plan: Plan, side: int, direction: int, src, dst, stream=None) -> None:
     """Feature layout conversion: side 0 input / 1 output features, direction 0 mul_ir -> ir_mul,
     1 ir_mul -> mul_ir; src and dst are device tensors of shape (N, width)."""
@@ -400,6 +414,19 @@ class Convolution:
                                      grad_x=outs["x"], grad_pos=outs["pos"], grad_edge_vec=outs["edge_vec"],
                                      grad_phi=outs["phi"], grad_A=outs["A"], workspace=self.workspace(OP_BACKWARD))
         return {k: v for k, v in outs.items() if v is not None}
+
+    def triple_backward(self, inputs: dict, want=TRIPLE_OUTPUTS):
+        """Third-order derivative on the edge operand Y (see conv_triple_backward); returns the
+        requested outputs as new device tensors."""
+        import torch
+        n, e = self.graph.n_nodes, self.graph.n_edges
+        info = self.plan.info
+        dt = dict(dtype=self.torch_dtype, device="cuda")
+        shapes = dict(x=(n, info["c_in"]), Y=(max(e, 1), info["sh_dim"]), phi=(max(e, 1), info["num_radial"]),
+                      A=(info["num_radial"], info["n_weights"]), grad_out=(n, info["c_out"]))
+        outs = {k: torch.empty(shapes[k.replace("v_", "")], **dt) for k in want}
+        conv_triple_backward(self.plan, self.graph, inputs, outs, self.workspace(OP_TRIPLE_BACKWARD))
+        return outs
 
     def double_backward(self, x, pos, shift, phi, A, grad_out, v_x=None, v_pos=None, v_edge_vec=None, v_phi=None,
                         v_A=None, want=("x", "pos", "edge_vec", "phi", "A", "grad_out")):

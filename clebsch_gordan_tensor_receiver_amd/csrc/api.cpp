@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
+#include <memory>
 #include <new>
 #include <string>
 #include <vector>
@@ -160,6 +161,60 @@ cgtp_status_t source_bounds(cgtp::Plan& p, const char* fam, const cgtp::Graph& G
   return cgtp::launch(kb, unsigned((n + 255) / 256), 256, 0, s, a, err);
 }
 
+// The plan with 2K radial values of the third-order passes (created on first use).
+cgtp_status_t tri_plan(cgtp::Plan& p, cgtp::Plan** out, std::string* err) {
+  std::lock_guard<std::mutex> lock(p.mu);
+  if (!p.tri) {
+    if (2 * p.K > 64) {
+      *err = "the third-order passes need 2K <= 64 radial values";
+      return CGTP_ERR_UNSUPPORTED;
+    }
+    std::unique_ptr<cgtp::Plan> t(new cgtp::Plan());
+    cgtp_status_t st = cgtp::build_plan(p.irreps_in_s.c_str(), p.irreps_sh_s.c_str(), p.irreps_out_s.c_str(), p.mode,
+                                        p.dtype, 2 * p.K, t.get(), err);
+    if (st != CGTP_OK) return st;
+    t->scratch_budget = p.scratch_budget;
+    p.tri = std::move(t);
+  }
+  p.tri->scratch_budget = p.scratch_budget;
+  *out = p.tri.get();
+  return CGTP_OK;
+}
+
+// Workspace of the third-order passes (on the 2K plan tp): per edge of a receiver chunk the rows of
+// the three edge operands (Y, v_Y, q_Y), the packed radial factors (2K), and the phi-bar (2K) and
+// Y-bar (sh_dim) results of a receiver pass; the receiver pass's partials and A-bar slots; beyond
+// the budget the packed A factors, an A-bar result (2K x N_w each), a forward result (N x C_out)
+// and the chunked source bounds.
+struct TriLayout {
+  BwdLayout L;
+  size_t gy_off[3] = {0, 0, 0}, pk_off = 0, pb_off = 0, yb_off = 0, ak_off = 0, ab_off = 0, m_off = 0, total = 0;
+};
+
+TriLayout tri_layout(const cgtp::Plan& tp, const cgtp::Graph& g) {
+  TriLayout T;
+  const int rs = cgtp::bwd_row_stride(tp), K2 = tp.K;
+  const int grow = 3 * rs + 2 * K2 + tp.sh_dim;
+  T.L = chunked_layout(tp, g, grow, cgtp::recv_partial_row(tp), int(cgtp::recv_backward_tasks(tp).size()));
+  const size_t em = size_t(T.L.emax), el = tp.elem();
+  size_t off = T.L.g_off;
+  for (int k = 0; k < 3; ++k, off += em * size_t(rs) * el) T.gy_off[k] = off;
+  T.pk_off = off;
+  off += em * size_t(K2) * el;
+  T.pb_off = off;
+  off += em * size_t(K2) * el;
+  T.yb_off = off;
+  off = T.L.total;
+  T.ak_off = off;
+  off += align256(size_t(K2) * size_t(tp.n_w) * el);
+  T.ab_off = off;
+  off += align256(size_t(K2) * size_t(tp.n_w) * el);
+  T.m_off = off;
+  off += align256(size_t(std::max(g.n, 1)) * size_t(tp.c_out) * el);
+  T.total = off;
+  return T;
+}
+
 // Feature blocks that no path reaches (output side) or leaves (input side) are not written by
 // the kernels; zero the whole tensor first when such a block exists.
 cgtp_status_t zero_unreached(cgtp::Plan& p, void* buf, int n, bool out_side, hipStream_t s, std::string* err,
@@ -304,9 +359,15 @@ cgtp_status_t cgtp_plan_compile(cgtp_plan_t plan, int ops) {
     // Forward and backward together: also the forward that keeps its edge rows for the backward.
     if ((ops & (1 << CGTP_OP_FORWARD)) && (ops & (1 << CGTP_OP_BACKWARD))) fams.push_back("fwdk");
     if (ops & (1 << CGTP_OP_DOUBLE_BACKWARD)) fams.push_back("dbl");
+    if (ops & (1 << CGTP_OP_TRIPLE_BACKWARD)) {
+      cgtp::Plan* tp = nullptr;
+      cgtp_status_t st = tri_plan(plan->p, &tp, &err);
+      if (st == CGTP_OK) st = cgtp::compile_family(*tp, "tri", &err);
+      if (st != CGTP_OK) return fail(st, err);
+    }
   } else {
-    if (ops & (1 << CGTP_OP_DOUBLE_BACKWARD))
-      return fail(CGTP_ERR_UNSUPPORTED, "double backward is channelwise only");
+    if (ops & ((1 << CGTP_OP_DOUBLE_BACKWARD) | (1 << CGTP_OP_TRIPLE_BACKWARD)))
+      return fail(CGTP_ERR_UNSUPPORTED, "the double and triple backward are channelwise only");
     if (ops & (1 << CGTP_OP_FORWARD)) fams.push_back("uvw_fwd");
     if (ops & (1 << CGTP_OP_BACKWARD)) fams.push_back("uvw_bwd");
   }
@@ -390,11 +451,18 @@ cgtp_status_t cgtp_workspace_size(cgtp_plan_t plan, cgtp_graph_t g, cgtp_op_t op
   const cgtp::Graph& G = g->g;
   size_t need = 0;
   if (p.mode == CGTP_FULLY_CONNECTED) {
-    if (op == CGTP_OP_DOUBLE_BACKWARD) return fail(CGTP_ERR_UNSUPPORTED, "double backward is channelwise only");
+    if (op == CGTP_OP_DOUBLE_BACKWARD || op == CGTP_OP_TRIPLE_BACKWARD)
+      return fail(CGTP_ERR_UNSUPPORTED, "the double and triple backward are channelwise only");
     *bytes = std::max<size_t>(cgtp::uvw_workspace(p, G, op), 256);
     return ok();
   }
-  if (op == CGTP_OP_FORWARD) {
+  if (op == CGTP_OP_TRIPLE_BACKWARD) {
+    cgtp::Plan* tp = nullptr;
+    std::string err;
+    cgtp_status_t st = tri_plan(plan->p, &tp, &err);
+    if (st != CGTP_OK) return fail(st, err);
+    need = tri_layout(*tp, G).total;
+  } else if (op == CGTP_OP_FORWARD) {
     need = forward_rows_bytes(p, G, p.scratch_budget);
   } else if (op == CGTP_OP_BACKWARD) {
     need = bwd_layout(p, G).total;
@@ -771,6 +839,224 @@ cgtp_status_t cgtp_conv_double_backward(cgtp_plan_t plan, cgtp_graph_t g, const 
     int n = p.K * p.n_w, ns = L.nslot;
     void* a[] = {&ap, &ns, &n, &gg_A};
     if ((st = cgtp::launch(kred, unsigned((n + 63) / 64), 512, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
+  }
+  return ok();
+}
+
+// Third-order derivative (LunaTP Appendix F, Algorithm 4): the gradients of
+// S3 = <q, second-order outputs> as the sum over the ten 4-linear terms below, each evaluated by
+// the backward's passes on the 2K plan with one slot open: the source pass for the node slot a,
+// the forward for the cotangent slot d, the receiver pass for the edge-operand slot b and, through
+// phi-bar = A_k H and A-bar = phi_k^T H, for the weight factors.
+namespace {
+enum TriVar { TV_X, TV_Y, TV_PHI, TV_A, TV_G, TV_VX, TV_VY, TV_VPHI, TV_VA, TV_QX, TV_QY, TV_QPHI, TV_QA, TV_QG, TV_N };
+struct TriTerm {
+  int a, b, f[2][2], d;
+};
+// (a, b, weight factors (phi-type, A-type) x2, d); -1 = no second factor.
+const TriTerm kTriTerms[10] = {
+    {TV_VX, TV_QY, {{TV_PHI, TV_A}, {-1, -1}}, TV_G},
+    {TV_VX, TV_Y, {{TV_QPHI, TV_A}, {TV_PHI, TV_QA}}, TV_G},
+    {TV_VX, TV_Y, {{TV_PHI, TV_A}, {-1, -1}}, TV_QG},
+    {TV_QX, TV_VY, {{TV_PHI, TV_A}, {-1, -1}}, TV_G},
+    {TV_X, TV_VY, {{TV_QPHI, TV_A}, {TV_PHI, TV_QA}}, TV_G},
+    {TV_X, TV_VY, {{TV_PHI, TV_A}, {-1, -1}}, TV_QG},
+    {TV_QX, TV_Y, {{TV_VPHI, TV_A}, {TV_PHI, TV_VA}}, TV_G},
+    {TV_X, TV_QY, {{TV_VPHI, TV_A}, {TV_PHI, TV_VA}}, TV_G},
+    {TV_X, TV_Y, {{TV_VPHI, TV_QA}, {TV_QPHI, TV_VA}}, TV_G},
+    {TV_X, TV_Y, {{TV_VPHI, TV_A}, {TV_PHI, TV_VA}}, TV_QG},
+};
+}  // namespace
+
+cgtp_status_t cgtp_conv_triple_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x, const void* Y,
+                                        const void* phi, const void* A, const void* grad_out, const void* v_x,
+                                        const void* v_Y, const void* v_phi, const void* v_A, const void* q_x,
+                                        const void* q_Y, const void* q_phi, const void* q_A, const void* q_grad_out,
+                                        void* t_x, void* t_Y, void* t_phi, void* t_A, void* t_grad_out, void* t_vx,
+                                        void* t_vY, void* t_vphi, void* t_vA, void* workspace, size_t ws_bytes,
+                                        void* stream) {
+  if (!plan || !g) return fail(CGTP_ERR_INVALID_ARG, "null plan or graph");
+  if (!x || !Y || !phi || !A || !grad_out) return fail(CGTP_ERR_INVALID_ARG, "null input tensor");
+  cgtp::Plan& p = plan->p;
+  cgtp::Graph& G = g->g;
+  if (p.mode != CGTP_CHANNELWISE) return fail(CGTP_ERR_UNSUPPORTED, "the triple backward is channelwise only");
+  if (p.radial) return fail(CGTP_ERR_UNSUPPORTED, "the triple backward takes phi as an input (no fused radial basis)");
+  const void* in[TV_N] = {x, Y, phi, A, grad_out, v_x, v_Y, v_phi, v_A, q_x, q_Y, q_phi, q_A, q_grad_out};
+  void* out[TV_N] = {t_x, t_Y, t_phi, t_A, t_grad_out, t_vx, t_vY, t_vphi, t_vA,
+                     nullptr, nullptr, nullptr, nullptr, nullptr};
+  bool any = false;
+  for (int k = 0; k < TV_QX; ++k) any = any || out[k];
+  if (!any) return ok();
+  std::string err;
+  cgtp::Plan* tpp = nullptr;
+  cgtp_status_t st = tri_plan(p, &tpp, &err);
+  if (st != CGTP_OK) return fail(st, err);
+  cgtp::Plan& tp = *tpp;
+  const TriLayout T = tri_layout(tp, G);
+  if (!workspace || ws_bytes < T.total) return fail(CGTP_ERR_WORKSPACE, "workspace too small");
+  cgtp::DeviceGraph d;
+  if ((st = cgtp::device_graph(G, &d, &err)) != CGTP_OK) return fail(st, err);
+  const char* fam = "tri";
+  hipFunction_t kzero, kprep, kfwd, krecv, ksrc, kfinal, kred, kpphi, kpa, kacc;
+  if ((st = cgtp::get_kernel(tp, fam, "cgtp_fill_zero", &kzero, &err)) != CGTP_OK ||
+      (st = cgtp::get_kernel(tp, fam, "cgtp_prep_y", &kprep, &err)) != CGTP_OK ||
+      (st = cgtp::get_kernel(tp, fam, "cgtp_fwd", &kfwd, &err)) != CGTP_OK ||
+      (st = cgtp::get_kernel(tp, fam, "cgtp_bwd_recv", &krecv, &err)) != CGTP_OK ||
+      (st = cgtp::get_kernel(tp, fam, "cgtp_bwd_src", &ksrc, &err)) != CGTP_OK ||
+      (st = cgtp::get_kernel(tp, fam, "cgtp_edge_final_y", &kfinal, &err)) != CGTP_OK ||
+      (st = cgtp::get_kernel(tp, fam, "cgtp_a_reduce", &kred, &err)) != CGTP_OK ||
+      (st = cgtp::get_kernel(tp, fam, "cgtp_tri_pack_phi", &kpphi, &err)) != CGTP_OK ||
+      (st = cgtp::get_kernel(tp, fam, "cgtp_tri_pack_a", &kpa, &err)) != CGTP_OK ||
+      (st = cgtp::get_kernel(tp, fam, "cgtp_tri_accum", &kacc, &err)) != CGTP_OK)
+    return fail(st, err);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int K = p.K, K2 = tp.K, SH = p.sh_dim, NW = p.n_w, el = int(p.elem());
+  char* ws = static_cast<char*>(workspace);
+  auto zero = [&](void* buf, long long n) -> cgtp_status_t {
+    if (!buf || n <= 0) return CGTP_OK;
+    void* a[] = {&buf, &n};
+    return cgtp::launch(kzero, unsigned((n + 255) / 256), 256, 0, s, a, &err);
+  };
+  auto accum = [&](void* dst, int dst_ld, const void* src, int src_ld, int src_off, int rows, int cols) {
+    void* a[] = {&dst, &dst_ld, (void*)&src, &src_ld, &src_off, &rows, &cols};
+    long long n = (long long)rows * cols;
+    return cgtp::launch(kacc, unsigned((n + 255) / 256), 256, 0, s, a, &err);
+  };
+  // Outputs are sums over terms: zeroed first, then accumulated.
+  const long long sizes[TV_QX] = {(long long)G.n * p.c_in, (long long)G.e * SH, (long long)G.e * K,
+                                  (long long)K * NW, (long long)G.n * p.c_out, (long long)G.n * p.c_in,
+                                  (long long)G.e * SH, (long long)G.e * K, (long long)K * NW};
+  for (int k = 0; k < TV_QX; ++k)
+    if ((st = zero(out[k], sizes[k])) != CGTP_OK) return fail(st, err);
+  void* mtmp = ws + T.m_off;
+  if (out[TV_G] && (st = zero(mtmp, (long long)G.n * p.c_out)) != CGTP_OK) return fail(st, err);
+  void* apk = ws + T.ak_off;
+  void* abar = ws + T.ab_off;
+  void* ep = ws + T.L.ep_off;
+  void* ap = ws + T.L.ap_off;
+  void* pk = ws + T.pk_off;
+  void* pbar = ws + T.pb_off;
+  void* ybar = ws + T.yb_off;
+  const BwdLayout& L = T.L;
+  int eps = int(L.emax);
+  for (size_t c = 0; c < L.chunks.size(); ++c) {
+    int i0 = L.chunks[c].first, nrec = L.chunks[c].second - L.chunks[c].first;
+    int e0 = G.row_ptr[L.chunks[c].first], e1 = G.row_ptr[L.chunks[c].second];
+    // Rows of the edge operands present (slot 0: Y, 1: v_Y, 2: q_Y).
+    void* rows[3] = {nullptr, nullptr, nullptr};
+    const void* yops[3] = {Y, v_Y, q_Y};
+    for (int k = 0; k < 3; ++k) {
+      if (!yops[k]) continue;
+      rows[k] = ws + T.gy_off[k];
+      if (e1 > e0) {
+        void* a[] = {(void*)&yops[k], &e0, &e1, &rows[k]};
+        if ((st = cgtp::launch(kprep, unsigned((e1 - e0 + 63) / 64), 64, 0, s, a, &err)) != CGTP_OK)
+          return fail(st, err);
+      }
+    }
+    auto rows_of = [&](int var) -> void* { return var == TV_Y ? rows[0] : var == TV_VY ? rows[1] : rows[2]; };
+    void *sb = nullptr, *se = nullptr;
+    bool bounds_done = false;
+    const int32_t* ord = (i0 == 0 && nrec == G.n) ? d.rorder : nullptr;
+    for (const TriTerm& tt : kTriTerms) {
+      const void* fp[2] = {nullptr, nullptr};
+      const void* fa[2] = {nullptr, nullptr};
+      bool live = false;
+      for (int k = 0; k < 2; ++k)
+        if (tt.f[k][0] >= 0 && in[tt.f[k][0]] && in[tt.f[k][1]]) {
+          fp[k] = in[tt.f[k][0]];
+          fa[k] = in[tt.f[k][1]];
+          live = true;
+        }
+      if (!live || !in[tt.a] || !in[tt.b] || !in[tt.d]) continue;
+      const bool want_a = out[tt.a] != nullptr, want_d = out[tt.d] != nullptr, want_b = out[tt.b] != nullptr;
+      bool want_f = false;
+      for (int k = 0; k < 2; ++k)
+        if (fp[k]) want_f = want_f || out[tt.f[k][0]] || out[tt.f[k][1]];
+      if (!want_a && !want_d && !want_b && !want_f) continue;
+      // Stacked factors [phi_1 | phi_2] for the chunk's edges and [A_1; A_2].
+      if (e1 > e0) {
+        void* a[] = {(void*)&fp[0], (void*)&fp[1], &e0, &e1, &pk};
+        long long n = (long long)(e1 - e0) * K2;
+        if ((st = cgtp::launch(kpphi, unsigned((n + 255) / 256), 256, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
+      }
+      {
+        void* a[] = {(void*)&fa[0], (void*)&fa[1], &apk};
+        long long n = (long long)K2 * NW;
+        if ((st = cgtp::launch(kpa, unsigned((n + 255) / 256), 256, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
+      }
+      // The kernels index the radial values by sorted edge: shift the chunk's packed rows to e0.
+      const void* phi_arg = static_cast<const char*>(pk) - (ptrdiff_t)e0 * K2 * el;
+      void* Gb = rows_of(tt.b);
+      const void* av = in[tt.a];
+      const void* dv = in[tt.d];
+      if (want_a) {   // node slot open: the source pass, accumulated into the output
+        if (!bounds_done) {
+          if ((st = source_bounds(tp, fam, G, d, L, c, ws, s, &sb, &se, &err)) != CGTP_OK) return fail(st, err);
+          bounds_done = true;
+        }
+        const cgtp::TaskGroups tsrc = cgtp::task_groups(cgtp::source_tasks(tp));
+        int n = G.n, per = (G.n + 7) / 8, acc = 1;
+        void* dst = out[tt.a];
+        void* a[] = {(void*)&phi_arg, &apk, &Gb, (void*)&dv, (void*)&d.recv, &sb, &se, (void*)&d.src_edge,
+                     &dst, &n, &per, &e0, &acc, (void*)&d.sorder};
+        if ((st = cgtp::launch(ksrc, unsigned(8 * tsrc.tasks.size() * per), 64 * kSrcSplit * tsrc.ncb, 0, s, a,
+                               &err)) != CGTP_OK)
+          return fail(st, err);
+      }
+      if (want_d && nrec > 0) {   // cotangent slot open: the forward over the chunk's receivers
+        const cgtp::TaskGroups tg = cgtp::task_groups(cgtp::forward_tasks(tp));
+        int per = (nrec + 7) / 8;
+        void* a[] = {(void*)&av, (void*)&phi_arg, &apk, &Gb, (void*)&d.row_ptr, (void*)&d.col, &mtmp, &i0, &nrec,
+                     &per, &e0, (void*)&ord};
+        if ((st = cgtp::launch(kfwd, unsigned(8 * tg.tasks.size() * per), 64 * cgtp::fwd_split(tp) * tg.ncb, 0, s, a,
+                               &err)) != CGTP_OK)
+          return fail(st, err);
+        void* dst = static_cast<char*>(out[tt.d]) + (size_t)i0 * p.c_out * el;
+        const void* src = static_cast<char*>(mtmp) + (size_t)i0 * p.c_out * el;
+        if ((st = accum(dst, p.c_out, src, p.c_out, 0, nrec, p.c_out)) != CGTP_OK) return fail(st, err);
+      }
+      if ((want_b || want_f) && nrec > 0) {   // edge-operand and weight slots: the receiver pass
+        int per, nch, acc_slots = 0;
+        chunk_geometry(nrec, &per, &nch);
+        void* a[] = {(void*)&av, (void*)&phi_arg, &apk, &Gb, (void*)&d.row_ptr, (void*)&d.col, (void*)&dv,
+                     &ep, &ap, &i0, &nrec, &per, &nch, &e0, &eps, &acc_slots, (void*)&ord};
+        if ((st = cgtp::launch(krecv, unsigned(8 * L.ntask_r * nch), 64 * kRecvGroup, 0, s, a, &err)) != CGTP_OK)
+          return fail(st, err);
+        bool want_pb = false, want_ab = false;
+        for (int k = 0; k < 2; ++k)
+          if (fp[k]) {
+            want_pb = want_pb || out[tt.f[k][0]];
+            want_ab = want_ab || out[tt.f[k][1]];
+          }
+        if (e1 > e0) {
+          void* gph = want_pb ? pbar : nullptr;
+          void* gy = want_b ? ybar : nullptr;
+          void* b[] = {&ep, &e0, &e1, &gph, &gy};
+          if ((st = cgtp::launch(kfinal, unsigned((e1 - e0 + 63) / 64), 64, 0, s, b, &err)) != CGTP_OK)
+            return fail(st, err);
+          if (want_b) {
+            void* dst = static_cast<char*>(out[tt.b]) + (size_t)e0 * SH * el;
+            if ((st = accum(dst, SH, ybar, SH, 0, e1 - e0, SH)) != CGTP_OK) return fail(st, err);
+          }
+          for (int k = 0; k < 2; ++k)
+            if (fp[k] && out[tt.f[k][0]]) {   // d/dphi_k = A_k H: half k of phi-bar
+              void* dst = static_cast<char*>(out[tt.f[k][0]]) + (size_t)e0 * K * el;
+              if ((st = accum(dst, K, pbar, K2, k * K, e1 - e0, K)) != CGTP_OK) return fail(st, err);
+            }
+        }
+        if (want_ab) {   // d/dA_k = phi_k^T H: rows k K .. k K + K - 1 of A-bar
+          int n = K2 * NW, ns = 8 * nch;   // the slots this chunk's receiver pass wrote
+          void* b[] = {&ap, &ns, &n, &abar};
+          if ((st = cgtp::launch(kred, unsigned((n + 63) / 64), 512, 0, s, b, &err)) != CGTP_OK) return fail(st, err);
+          for (int k = 0; k < 2; ++k)
+            if (fp[k] && out[tt.f[k][1]]) {
+              const void* src = static_cast<char*>(abar) + (size_t)k * K * NW * el;
+              if ((st = accum(out[tt.f[k][1]], NW, src, NW, 0, K, NW)) != CGTP_OK) return fail(st, err);
+            }
+        }
+      }
+    }
   }
   return ok();
 }

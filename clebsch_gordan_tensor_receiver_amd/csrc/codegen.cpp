@@ -295,6 +295,57 @@ void emit_prep(Out& o, const Plan& p, bool with_y) {
   o.close();
 }
 
+// Rows of the third-order passes: the folded coefficients G = sum c b and the edge operand b itself
+// (the backward's row layout), from an edge operand b given per sorted edge (E x sh_dim) instead of
+// the harmonics of the edge vector.  Lane = edge; the same LDS-staged 16-byte row stores as
+// cgtp_prep.
+void emit_prep_y(Out& o, const Plan& p) {
+  const int per = p.dtype == CGTP_F64 ? 2 : 4;
+  const int stride = bwd_row_stride(p);
+  const int block_vals = 16 * per;
+  o.line("extern \"C\" __global__ void __launch_bounds__(64)");
+  o.open("cgtp_prep_y(const real* __restrict__ yop, int e0, int e1, real* __restrict__ G)");
+  o.line("__shared__ V4 tile[64 * 17];");
+  o.line("const int lane = (int)threadIdx.x;");
+  o.line("const int eb = e0 + (int)blockIdx.x * 64;");
+  o.line("const int e = min(eb + lane, e1 - 1);");
+  o.line(F("real Y[%d];", p.sh_dim));
+  o.line(F("for (int m = 0; m < %d; ++m) Y[m] = yop[(i64)e * %d + m];", p.sh_dim, p.sh_dim));
+  std::vector<std::string> vals(size_t(p.g_stride), "R(0)");
+  for (const Path& P : p.paths) {
+    int s0 = P.l2 * P.l2;
+    for (size_t t = 0; t < P.gpairs.size(); ++t) {
+      std::string ex;
+      for (auto& tm : P.gpairs[t].terms) {
+        if (!ex.empty()) ex += " + ";
+        ex += lit(tm.second) + " * Y[" + std::to_string(s0 + tm.first) + "]";
+      }
+      vals[size_t(P.g_off) + t] = ex;
+    }
+  }
+  for (int m = 0; m < p.sh_dim; ++m) vals.push_back(F("Y[%d]", m));
+  while (int(vals.size()) < stride) vals.push_back("R(0)");
+  const int nblocks = (stride + block_vals - 1) / block_vals;
+  for (int b = 0; b < nblocks; ++b) {
+    const int v0 = b * block_vals, nv = std::min(block_vals, stride - v0) / per;
+    o.open("");
+    for (int k = 0; k < nv; ++k) {
+      std::string v;
+      for (int t = 0; t < per; ++t) v += (t ? ", " : "") + vals[v0 + k * per + t];
+      o.line(F("tile[lane * 17 + %d] = V4{", k) + v + "};");
+    }
+    o.line("__syncthreads();");
+    o.open("for (int it = 0; it < 16; ++it)");
+    o.line("const int row = it * 4 + (lane >> 4), c = lane & 15;");
+    o.line(F("if (eb + row < e1 && c < %d) ((V4*)(G + (i64)(eb + row - e0) * %d + %d))[c] = tile[row * 17 + c];", nv,
+             stride, v0));
+    o.close();
+    o.line("__syncthreads();");
+    o.close();
+  }
+  o.close();
+}
+
 int path_cost(const Plan& p, const Path& P) {
   return p.K + int(P.gpairs.size()) + std::min(2 * P.l1 + 1, 2 * P.l3 + 1);
 }
@@ -1095,6 +1146,77 @@ void emit_recv_edge_final(Out& o, const Plan& p, const std::vector<Task>& tasks)
   o.close();
 }
 
+// Per-edge finalisation of the third-order passes: phi-bar (K values) and the edge-operand
+// gradient Y-bar (sh_dim values) as fixed-order sums of the receiver pass's task partials, written
+// for the chunk's edges (rows e - e0).
+void emit_recv_edge_final_y(Out& o, const Plan& p, const std::vector<Task>& tasks) {
+  const int K = p.K, row = recv_partial_row(p);
+  std::vector<int> off;
+  for (int k = 0, c = 0; k < int(tasks.size()); c += recv_task_width(p, tasks[k]), ++k) off.push_back(c);
+  o.line("extern \"C\" __global__ void __launch_bounds__(64)");
+  o.open("cgtp_edge_final_y(const real* __restrict__ ep, int e0, int e1, real* __restrict__ gphi,"
+         " real* __restrict__ gy)");
+  o.line("const int e = e0 + (int)(blockIdx.x * 64 + threadIdx.x);");
+  o.line("if (e >= e1) return;");
+  o.line(F("const real* __restrict__ rw = ep + (i64)((e - e0) >> 6) * %d + ((e - e0) & 63);", 64 * row));
+  o.line("#define RW(c) rw[64 * (c)]");
+  o.open("if (gphi)");
+  for (int q = 0; q < K; ++q) {
+    std::string ex;
+    for (size_t t = 0; t < tasks.size(); ++t) ex += (t ? " + " : "") + F("RW(%d)", off[t] + q);
+    o.line(F("gphi[(i64)(e - e0) * %d + %d] = ", K, q) + ex + ";");
+  }
+  o.close();
+  o.open("if (gy)");
+  std::vector<std::vector<int>> yc;
+  for (const Task& t : tasks) yc.push_back(recv_task_ycols(p, t));
+  for (int m = 0; m < p.sh_dim; ++m) {
+    std::string ex;
+    for (size_t t = 0; t < tasks.size(); ++t) {
+      auto it = std::find(yc[t].begin(), yc[t].end(), m);
+      if (it == yc[t].end()) continue;
+      ex += (ex.empty() ? "" : " + ") + F("RW(%d)", off[t] + K + int(it - yc[t].begin()));
+    }
+    o.line(F("gy[(i64)(e - e0) * %d + %d] = ", p.sh_dim, m) + (ex.empty() ? std::string("R(0)") : ex) + ";");
+  }
+  o.close();
+  o.line("#undef RW");
+  o.close();
+}
+
+// Operand packing and accumulation of the third-order passes.  Their kernels are generated for
+// 2K radial values, so that a weight phi_1 A_1 + phi_2 A_2 is one product of the stacked
+// [phi_1 | phi_2] (E x 2K) and [A_1; A_2] (2K x N_w); a missing factor is zero.
+void emit_tri_helpers(Out& o, const Plan& p) {
+  const int K2 = p.K, K = p.K / 2;
+  o.line("extern \"C\" __global__ void __launch_bounds__(256)");
+  o.open("cgtp_tri_pack_phi(const real* __restrict__ p1, const real* __restrict__ p2, int e0, int e1,"
+         " real* __restrict__ dst)");
+  o.line(F("const i64 k = (i64)blockIdx.x * 256 + threadIdx.x, n = (i64)(e1 - e0) * %d;", K2));
+  o.line("if (k >= n) return;");
+  o.line(F("const i64 e = e0 + k / %d; const int q = (int)(k %% %d);", K2, K2));
+  o.line(F("const real* src = q < %d ? p1 : p2;", K));
+  o.line(F("dst[k] = src ? src[e * %d + (q %% %d)] : R(0);", K, K));
+  o.close();
+  o.line("extern \"C\" __global__ void __launch_bounds__(256)");
+  o.open("cgtp_tri_pack_a(const real* __restrict__ a1, const real* __restrict__ a2, real* __restrict__ dst)");
+  o.line(F("const i64 k = (i64)blockIdx.x * 256 + threadIdx.x, n = (i64)%d * %d;", K2, p.n_w));
+  o.line("if (k >= n) return;");
+  o.line(F("const i64 half = (i64)%d * %d;", K, p.n_w));
+  o.line("const real* src = k < half ? a1 : a2;");
+  o.line("dst[k] = src ? src[k < half ? k : k - half] : R(0);");
+  o.close();
+  // dst[r * dst_ld + c] += src[r * src_ld + src_off + c] for r < rows, c < cols.
+  o.line("extern \"C\" __global__ void __launch_bounds__(256)");
+  o.open("cgtp_tri_accum(real* __restrict__ dst, int dst_ld, const real* __restrict__ src, int src_ld, int src_off,"
+         " int rows, int cols)");
+  o.line("const i64 k = (i64)blockIdx.x * 256 + threadIdx.x;");
+  o.line("if (k >= (i64)rows * cols) return;");
+  o.line("const i64 r = k / cols; const int c = (int)(k - r * cols);");
+  o.line("dst[r * dst_ld + c] += src[r * src_ld + src_off + c];");
+  o.close();
+}
+
 // Zero-length edge check: per 256-edge block, the smallest sorted edge index whose vector
 // pos[send] - pos[recv] + shift is exactly zero (INT_MAX if none), reduced in LDS in a fixed order.
 void emit_check_edges(Out& o) {
@@ -1408,6 +1530,35 @@ std::string generate_source(const Plan& p, const std::string& family, std::strin
   if (family == "uvw_fwd" || family == "uvw_bwd") {
     *err = "fully connected families are generated by generate_uvw_source";
     return "";
+  }
+  // tri: the passes of the third-order derivative, generated for a plan with 2K radial values
+  // (the parent plan's K twice): rows from an edge operand, the forward over the backward's row
+  // layout, the receiver and source passes of the backward, edge finalisation without the
+  // position chain, and the packing / accumulation helpers.
+  if (family == "tri") {
+    prelude(o, p, false, true);
+    emit_prep_y(o, p);
+    const std::vector<Task>& ft = forward_tasks(p);
+    int nacc = 1;
+    for (int k = 0; k < int(ft.size()); ++k) {
+      emit_fwd_task(o, p, k, ft[k], bwd_row_stride(p));
+      int n = 0;
+      for (int ob : out_blocks_of(p, ft[k].paths)) n += p.out[ob].dim();
+      nacc = std::max(nacc, n);
+    }
+    emit_node_dispatch(o, p, "cgtp_fwd", kFwdArgs, "fwd_t", task_groups(ft), nacc);
+    auto rt = recv_backward_tasks(p);
+    const int row = recv_partial_row(p);
+    for (int k = 0, off = 0; k < int(rt.size()); off += recv_task_width(p, rt[k]), ++k)
+      emit_bwd_recv_task(o, p, k, rt[k], off, row);
+    emit_recv_dispatch(o, p, int(rt.size()));
+    auto st = source_tasks(p);
+    for (int k = 0; k < int(st.size()); ++k) emit_bwd_src_task(o, p, k, st[k]);
+    emit_src_dispatch(o, p, int(st.size()));
+    emit_recv_edge_final_y(o, p, rt);
+    emit_small_kernels(o);
+    emit_tri_helpers(o, p);
+    return o.s.str();
   }
   if (family == "bwd") {
     prelude(o, p, true, true);

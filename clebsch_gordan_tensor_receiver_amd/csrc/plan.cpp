@@ -269,6 +269,9 @@ cgtp_status_t build_plan(const char* irreps_in, const char* irreps_sh, const cha
   key << "v1|" << irreps_in << "|" << irreps_sh << "|" << irreps_out << "|" << int(mode) << "|"
       << int(dtype) << "|" << K;
   p->key = key.str();
+  p->irreps_in_s = irreps_in;
+  p->irreps_sh_s = irreps_sh;
+  p->irreps_out_s = irreps_out;
   p->kernels = make_kernel_set();
   return CGTP_OK;
 }

@@ -71,6 +71,10 @@ struct Plan {
   // Paths into each output block / out of each input block, in path order.
   std::vector<std::vector<int>> by_out, by_in;
   std::string key;     // canonical description used to name and cache kernels
+  std::string irreps_in_s, irreps_sh_s, irreps_out_s;  // as given to build_plan
+  // The same irreps with 2K radial values, whose kernels run the third-order passes (a weight
+  // phi_1 A_1 + phi_2 A_2 as one product of stacked factors); built on first use, under `mu`.
+  std::unique_ptr<Plan> tri;
   std::unique_ptr<KernelSet> kernels;
   std::mutex mu;
   mutable std::once_flag tables_once;              // task lists (kernels.hpp), built on first use

@@ -75,7 +75,12 @@ typedef struct cgtp_graph_s* cgtp_graph_t;
 typedef enum { CGTP_CHANNELWISE = 0, CGTP_FULLY_CONNECTED = 1 } cgtp_mode_t;
 typedef enum { CGTP_F32 = 0, CGTP_F64 = 1 } cgtp_dtype_t;
 typedef enum { CGTP_STREAMED = 0, CGTP_CONVENTIONAL = 1 } cgtp_schedule_t;
-typedef enum { CGTP_OP_FORWARD = 0, CGTP_OP_BACKWARD = 1, CGTP_OP_DOUBLE_BACKWARD = 2 } cgtp_op_t;
+typedef enum {
+  CGTP_OP_FORWARD = 0,
+  CGTP_OP_BACKWARD = 1,
+  CGTP_OP_DOUBLE_BACKWARD = 2,
+  CGTP_OP_TRIPLE_BACKWARD = 3
+} cgtp_op_t;
 
 typedef enum {
   CGTP_OK = 0,
@@ -281,6 +286,34 @@ cgtp_status_t cgtp_conv_double_backward(cgtp_plan_t plan, cgtp_graph_t g, const 
                                         const void* v_edge_vec, const void* v_phi, const void* v_A,
                                         void* gg_x, void* gg_pos, void* gg_edge_vec, void* gg_phi,
                                         void* gg_A, void* gg_grad_out, void* workspace, size_t ws_bytes,
+                                        void* stream);
+
+/* Triple backward (channelwise mode only): the third-order derivative of the convolution on the
+ * operands of LunaTP Appendix F, Algorithm 4 ("Third-Order Derivative of Clebsch-Gordan Tensor
+ * Product Convolution"): node features x, the angular edge operand Y, the edge weights
+ * w = phi A (kept factored) and the output cotangent g = grad_out.  With the second-order map
+ *   S2(x, Y, phi, A, g; v) = <v_x, grad_x> + <v_Y, grad_Y> + <v_phi, grad_phi> + <v_A, grad_A>
+ * (the first-order outputs of <g, out> along the directions v) and the cotangents q of its
+ * gradients, the outputs are the gradients of S3 = <q_x, dS2/dx> + <q_Y, dS2/dY> +
+ * <q_phi, dS2/dphi> + <q_A, dS2/dA> + <q_grad_out, dS2/dg> with respect to x, Y, phi, A, g and the
+ * directions v_x, v_Y, v_phi, v_A.  As in the page's algorithm the edge operand is an input: the
+ * chain rule through the harmonics of the edge vectors is not applied (Y is normally the real
+ * spherical harmonics of the edge directions, E x sh_dim, receiver-sorted, (L+1)^2 values per
+ * edge in the plan's order; any values of that shape are accepted).
+ * Inputs: x (N x C_in), Y (E x sh_dim), phi (E x K), A (K x N_w), grad_out (N x C_out); directions
+ * v_x, v_Y, v_phi, v_A and cotangents q_x, q_Y, q_phi, q_A, q_grad_out of the same shapes, each
+ * optional (NULL = zero).  Outputs, each optional (NULL = not requested) and overwritten: t_x, t_Y,
+ * t_phi, t_A, t_grad_out (N x C_out), t_vx, t_vY, t_vphi, t_vA.  Workspace: cgtp_workspace_size
+ * with CGTP_OP_TRIPLE_BACKWARD.  The passes run with 2K radial values (a weight phi_1 A_1 +
+ * phi_2 A_2 as one product of stacked factors), so K must be at most 32.  Fixed-order reductions:
+ * bitwise repeatable.  UNSUPPORTED for the fully connected mode, a plan with an in-kernel radial
+ * basis, or K > 32. */
+cgtp_status_t cgtp_conv_triple_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x, const void* Y,
+                                        const void* phi, const void* A, const void* grad_out, const void* v_x,
+                                        const void* v_Y, const void* v_phi, const void* v_A, const void* q_x,
+                                        const void* q_Y, const void* q_phi, const void* q_A, const void* q_grad_out,
+                                        void* t_x, void* t_Y, void* t_phi, void* t_A, void* t_grad_out, void* t_vx,
+                                        void* t_vY, void* t_vphi, void* t_vA, void* workspace, size_t ws_bytes,
                                         void* stream);
 
 /* Check on the device that no edge vector pos[send] - pos[recv] + shift is exactly zero (such an

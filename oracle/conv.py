@@ -363,13 +363,15 @@ TRIPLE_OUTPUTS = ("x", "Y", "phi", "A", "g", "v_x", "v_Y", "v_phi", "v_A")
 
 def triple_backward(problem: Problem, x, Y, recv, send, phi, A, grad_out, v_x=None, v_Y=None, v_phi=None,
                     v_A=None, q_x=None, q_Y=None, q_phi=None, q_A=None, q_grad_out=None,
-                    n_nodes: Optional[int] = None) -> Dict[str, torch.Tensor]:
-    """Gradients of S3 (above) with respect to x, Y, phi, A, g (key "g") and v_x, v_Y, v_phi, v_A.
+                    n_nodes: Optional[int] = None, outputs=None, paths=None) -> Dict[str, torch.Tensor]:
+    """Gradients of S3 (above) with respect to x, Y, phi, A, g (key "grad_out") and v_x, v_Y, v_phi, v_A.
 
     S3 is the sum of the ten terms of _TRIPLE_TERMS.  Each term is linear in each of its four
     slots, so its gradient with respect to the variable in a slot is the form with that slot left
     open; a weight slot c = sum_k phi_k A_k passes H = dPhi/dc on as dc/dphi_k = H A_k^T and
     dc/dA_k = phi_k^T H.  Missing directions and cotangents are zero (their terms vanish).
+    ``outputs`` (names) limits what is computed; ``paths`` (indices) limits the sum over paths,
+    which leaves the weight-gradient columns of those paths exact (used at large sizes).
     """
     if problem.mode != "uvu":
         raise ValueError("the third-order oracle covers the channelwise mode")
@@ -384,13 +386,16 @@ def triple_backward(problem: Problem, x, Y, recv, send, phi, A, grad_out, v_x=No
              q_phi=None if q_phi is None else _t(q_phi), q_A=None if q_A is None else _t(q_A),
              q_g=None if q_grad_out is None else _t(q_grad_out))
     shapes = dict(x=x.shape, Y=Y.shape, phi=phi.shape, A=A.shape, g=(N, problem.c_out))
-    out = {k: torch.zeros(shapes[k.replace("v_", "")], dtype=_F64) for k in TRIPLE_OUTPUTS}
+    wanted = set(TRIPLE_OUTPUTS) if outputs is None else {("g" if k == "grad_out" else k) for k in outputs}
+    out = {k: torch.zeros(shapes[k.replace("v_", "")], dtype=_F64) for k in TRIPLE_OUTPUTS if k in wanted}
     for a_name, b_name, factors, d_name in _TRIPLE_TERMS:
         factors = tuple(f for f in factors if z[f[0]] is not None and z[f[1]] is not None)
         if z[a_name] is None or z[b_name] is None or z[d_name] is None or not factors:
             continue
         a, b, d = z[a_name], z[b_name], z[d_name]
         for p in problem.paths:
+            if paths is not None and p.index not in paths:
+                continue
             bi, bs, bo = problem.irreps_in[p.i_in], problem.irreps_sh[p.i_sh], problem.irreps_out[p.i_out]
             c = _coupling(p)
             cols = slice(p.weight_offset, p.weight_offset + p.n_weights)
@@ -408,11 +413,14 @@ def triple_backward(problem: Problem, x, Y, recv, send, phi, A, grad_out, v_x=No
                 gd = torch.zeros(N, bo.dim, bo.mul, dtype=_F64)
                 gd.index_add_(0, recv, torch.einsum("abc,eau,eb,eu->ecu", c, ae, be, w))
                 out[d_name][:, bo.offset:bo.offset + bo.size] += gd.reshape(N, -1)
+            if not any(f in out for fac in factors for f in fac):
+                continue
             H = torch.einsum("abc,eau,eb,ecu->eu", c, ae, be, de)   # slot c open: (E, C)
             for fp, fA in factors:
                 if fp in out:
                     out[fp] += H @ z[fA][:, cols].T
                 if fA in out:
                     out[fA][:, cols] += z[fp].T @ H
-    out["grad_out"] = out.pop("g")
+    if "g" in out:
+        out["grad_out"] = out.pop("g")
     return out
