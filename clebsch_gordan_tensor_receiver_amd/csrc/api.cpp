@@ -182,35 +182,27 @@ cgtp_status_t tri_plan(cgtp::Plan& p, cgtp::Plan** out, std::string* err) {
 }
 
 // Workspace of the third-order passes (on the 2K plan tp): per edge of a receiver chunk the rows of
-// the three edge operands (Y, v_Y, q_Y), the packed radial factors (2K), and the phi-bar (2K) and
-// Y-bar (sh_dim) results of a receiver pass; the receiver pass's partials and A-bar slots; beyond
-// the budget the packed A factors, an A-bar result (2K x N_w each), a forward result (N x C_out)
-// and the chunked source bounds.
+// one edge operand (Y, v_Y or q_Y: the terms run grouped by it) and the packed radial factors
+// (2K); the receiver pass's partials and A-bar slots; beyond the budget the packed A factors
+// (2K x N_w) and the chunked source bounds.  Every pass adds its results into the outputs.
 struct TriLayout {
   BwdLayout L;
-  size_t gy_off[3] = {0, 0, 0}, pk_off = 0, pb_off = 0, yb_off = 0, ak_off = 0, ab_off = 0, m_off = 0, total = 0;
+  size_t gy_off[3] = {0, 0, 0}, pk_off = 0, ak_off = 0, total = 0;
 };
 
 TriLayout tri_layout(const cgtp::Plan& tp, const cgtp::Graph& g) {
   TriLayout T;
   const int rs = cgtp::bwd_row_stride(tp), K2 = tp.K;
-  const int grow = 3 * rs + 2 * K2 + tp.sh_dim;
+  const int grow = rs + K2;   // the rows of one edge operand at a time, and the packed radial factors
   T.L = chunked_layout(tp, g, grow, cgtp::recv_partial_row(tp), int(cgtp::recv_backward_tasks(tp).size()));
   const size_t em = size_t(T.L.emax), el = tp.elem();
   size_t off = T.L.g_off;
-  for (int k = 0; k < 3; ++k, off += em * size_t(rs) * el) T.gy_off[k] = off;
+  T.gy_off[0] = T.gy_off[1] = T.gy_off[2] = off;
+  off += em * size_t(rs) * el;
   T.pk_off = off;
-  off += em * size_t(K2) * el;
-  T.pb_off = off;
-  off += em * size_t(K2) * el;
-  T.yb_off = off;
   off = T.L.total;
   T.ak_off = off;
   off += align256(size_t(K2) * size_t(tp.n_w) * el);
-  T.ab_off = off;
-  off += align256(size_t(K2) * size_t(tp.n_w) * el);
-  T.m_off = off;
-  off += align256(size_t(std::max(g.n, 1)) * size_t(tp.c_out) * el);
   T.total = off;
   return T;
 }
@@ -897,17 +889,16 @@ cgtp_status_t cgtp_conv_triple_backward(cgtp_plan_t plan, cgtp_graph_t g, const 
   cgtp::DeviceGraph d;
   if ((st = cgtp::device_graph(G, &d, &err)) != CGTP_OK) return fail(st, err);
   const char* fam = "tri";
-  hipFunction_t kzero, kprep, kfwd, krecv, ksrc, kfinal, kred, kpphi, kpa, kacc;
+  hipFunction_t kzero, kprep, kfwd, krecv, ksrc, kfinal, kred, kpphi, kpa;
   if ((st = cgtp::get_kernel(tp, fam, "cgtp_fill_zero", &kzero, &err)) != CGTP_OK ||
       (st = cgtp::get_kernel(tp, fam, "cgtp_prep_y", &kprep, &err)) != CGTP_OK ||
       (st = cgtp::get_kernel(tp, fam, "cgtp_fwd", &kfwd, &err)) != CGTP_OK ||
       (st = cgtp::get_kernel(tp, fam, "cgtp_bwd_recv", &krecv, &err)) != CGTP_OK ||
       (st = cgtp::get_kernel(tp, fam, "cgtp_bwd_src", &ksrc, &err)) != CGTP_OK ||
       (st = cgtp::get_kernel(tp, fam, "cgtp_edge_final_y", &kfinal, &err)) != CGTP_OK ||
-      (st = cgtp::get_kernel(tp, fam, "cgtp_a_reduce", &kred, &err)) != CGTP_OK ||
+      (st = cgtp::get_kernel(tp, fam, "cgtp_tri_a_reduce", &kred, &err)) != CGTP_OK ||
       (st = cgtp::get_kernel(tp, fam, "cgtp_tri_pack_phi", &kpphi, &err)) != CGTP_OK ||
-      (st = cgtp::get_kernel(tp, fam, "cgtp_tri_pack_a", &kpa, &err)) != CGTP_OK ||
-      (st = cgtp::get_kernel(tp, fam, "cgtp_tri_accum", &kacc, &err)) != CGTP_OK)
+      (st = cgtp::get_kernel(tp, fam, "cgtp_tri_pack_a", &kpa, &err)) != CGTP_OK)
     return fail(st, err);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int K = p.K, K2 = tp.K, SH = p.sh_dim, NW = p.n_w, el = int(p.elem());
@@ -917,143 +908,123 @@ cgtp_status_t cgtp_conv_triple_backward(cgtp_plan_t plan, cgtp_graph_t g, const 
     void* a[] = {&buf, &n};
     return cgtp::launch(kzero, unsigned((n + 255) / 256), 256, 0, s, a, &err);
   };
-  auto accum = [&](void* dst, int dst_ld, const void* src, int src_ld, int src_off, int rows, int cols) {
-    void* a[] = {&dst, &dst_ld, (void*)&src, &src_ld, &src_off, &rows, &cols};
-    long long n = (long long)rows * cols;
-    return cgtp::launch(kacc, unsigned((n + 255) / 256), 256, 0, s, a, &err);
-  };
-  // Outputs are sums over terms: zeroed first, then accumulated.
+  // Outputs are sums over terms: zeroed first, then every pass adds into them.
   const long long sizes[TV_QX] = {(long long)G.n * p.c_in, (long long)G.e * SH, (long long)G.e * K,
                                   (long long)K * NW, (long long)G.n * p.c_out, (long long)G.n * p.c_in,
                                   (long long)G.e * SH, (long long)G.e * K, (long long)K * NW};
   for (int k = 0; k < TV_QX; ++k)
     if ((st = zero(out[k], sizes[k])) != CGTP_OK) return fail(st, err);
-  void* mtmp = ws + T.m_off;
-  if (out[TV_G] && (st = zero(mtmp, (long long)G.n * p.c_out)) != CGTP_OK) return fail(st, err);
   void* apk = ws + T.ak_off;
-  void* abar = ws + T.ab_off;
   void* ep = ws + T.L.ep_off;
   void* ap = ws + T.L.ap_off;
   void* pk = ws + T.pk_off;
-  void* pbar = ws + T.pb_off;
-  void* ybar = ws + T.yb_off;
+  void* Gb = ws + T.gy_off[0];
   const BwdLayout& L = T.L;
   int eps = int(L.emax);
+  auto rows_at = [&](void* base, int e0, int width) -> void* {
+    return base ? static_cast<char*>(base) + (size_t)e0 * width * el : nullptr;
+  };
   for (size_t c = 0; c < L.chunks.size(); ++c) {
     int i0 = L.chunks[c].first, nrec = L.chunks[c].second - L.chunks[c].first;
     int e0 = G.row_ptr[L.chunks[c].first], e1 = G.row_ptr[L.chunks[c].second];
-    // Rows of the edge operands present (slot 0: Y, 1: v_Y, 2: q_Y).
-    void* rows[3] = {nullptr, nullptr, nullptr};
-    const void* yops[3] = {Y, v_Y, q_Y};
-    for (int k = 0; k < 3; ++k) {
-      if (!yops[k]) continue;
-      rows[k] = ws + T.gy_off[k];
-      if (e1 > e0) {
-        void* a[] = {(void*)&yops[k], &e0, &e1, &rows[k]};
-        if ((st = cgtp::launch(kprep, unsigned((e1 - e0 + 63) / 64), 64, 0, s, a, &err)) != CGTP_OK)
-          return fail(st, err);
-      }
-    }
-    auto rows_of = [&](int var) -> void* { return var == TV_Y ? rows[0] : var == TV_VY ? rows[1] : rows[2]; };
     void *sb = nullptr, *se = nullptr;
     bool bounds_done = false;
     const int32_t* ord = (i0 == 0 && nrec == G.n) ? d.rorder : nullptr;
-    for (const TriTerm& tt : kTriTerms) {
-      const void* fp[2] = {nullptr, nullptr};
-      const void* fa[2] = {nullptr, nullptr};
-      bool live = false;
-      for (int k = 0; k < 2; ++k)
-        if (tt.f[k][0] >= 0 && in[tt.f[k][0]] && in[tt.f[k][1]]) {
-          fp[k] = in[tt.f[k][0]];
-          fa[k] = in[tt.f[k][1]];
-          live = true;
-        }
-      if (!live || !in[tt.a] || !in[tt.b] || !in[tt.d]) continue;
-      const bool want_a = out[tt.a] != nullptr, want_d = out[tt.d] != nullptr, want_b = out[tt.b] != nullptr;
-      bool want_f = false;
-      for (int k = 0; k < 2; ++k)
-        if (fp[k]) want_f = want_f || out[tt.f[k][0]] || out[tt.f[k][1]];
-      if (!want_a && !want_d && !want_b && !want_f) continue;
-      // Stacked factors [phi_1 | phi_2] for the chunk's edges and [A_1; A_2].
-      if (e1 > e0) {
-        void* a[] = {(void*)&fp[0], (void*)&fp[1], &e0, &e1, &pk};
-        long long n = (long long)(e1 - e0) * K2;
-        if ((st = cgtp::launch(kpphi, unsigned((n + 255) / 256), 256, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
-      }
-      {
-        void* a[] = {(void*)&fa[0], (void*)&fa[1], &apk};
-        long long n = (long long)K2 * NW;
-        if ((st = cgtp::launch(kpa, unsigned((n + 255) / 256), 256, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
-      }
-      // The kernels index the radial values by sorted edge: shift the chunk's packed rows to e0.
-      const void* phi_arg = static_cast<const char*>(pk) - (ptrdiff_t)e0 * K2 * el;
-      void* Gb = rows_of(tt.b);
-      const void* av = in[tt.a];
-      const void* dv = in[tt.d];
-      if (want_a) {   // node slot open: the source pass, accumulated into the output
-        if (!bounds_done) {
-          if ((st = source_bounds(tp, fam, G, d, L, c, ws, s, &sb, &se, &err)) != CGTP_OK) return fail(st, err);
-          bounds_done = true;
-        }
-        const cgtp::TaskGroups tsrc = cgtp::task_groups(cgtp::source_tasks(tp));
-        int n = G.n, per = (G.n + 7) / 8, acc = 1;
-        void* dst = out[tt.a];
-        void* a[] = {(void*)&phi_arg, &apk, &Gb, (void*)&dv, (void*)&d.recv, &sb, &se, (void*)&d.src_edge,
-                     &dst, &n, &per, &e0, &acc, (void*)&d.sorder};
-        if ((st = cgtp::launch(ksrc, unsigned(8 * tsrc.tasks.size() * per), 64 * kSrcSplit * tsrc.ncb, 0, s, a,
-                               &err)) != CGTP_OK)
-          return fail(st, err);
-      }
-      if (want_d && nrec > 0) {   // cotangent slot open: the forward over the chunk's receivers
-        const cgtp::TaskGroups tg = cgtp::task_groups(cgtp::forward_tasks(tp));
-        int per = (nrec + 7) / 8;
-        void* a[] = {(void*)&av, (void*)&phi_arg, &apk, &Gb, (void*)&d.row_ptr, (void*)&d.col, &mtmp, &i0, &nrec,
-                     &per, &e0, (void*)&ord};
-        if ((st = cgtp::launch(kfwd, unsigned(8 * tg.tasks.size() * per), 64 * cgtp::fwd_split(tp) * tg.ncb, 0, s, a,
-                               &err)) != CGTP_OK)
-          return fail(st, err);
-        void* dst = static_cast<char*>(out[tt.d]) + (size_t)i0 * p.c_out * el;
-        const void* src = static_cast<char*>(mtmp) + (size_t)i0 * p.c_out * el;
-        if ((st = accum(dst, p.c_out, src, p.c_out, 0, nrec, p.c_out)) != CGTP_OK) return fail(st, err);
-      }
-      if ((want_b || want_f) && nrec > 0) {   // edge-operand and weight slots: the receiver pass
-        int per, nch, acc_slots = 0;
-        chunk_geometry(nrec, &per, &nch);
-        void* a[] = {(void*)&av, (void*)&phi_arg, &apk, &Gb, (void*)&d.row_ptr, (void*)&d.col, (void*)&dv,
-                     &ep, &ap, &i0, &nrec, &per, &nch, &e0, &eps, &acc_slots, (void*)&ord};
-        if ((st = cgtp::launch(krecv, unsigned(8 * L.ntask_r * nch), 64 * kRecvGroup, 0, s, a, &err)) != CGTP_OK)
-          return fail(st, err);
-        bool want_pb = false, want_ab = false;
+    // Terms grouped by their edge operand: one operand's rows are in the workspace at a time.
+    for (int bvar : {TV_Y, TV_VY, TV_QY}) {
+      if (!in[bvar]) continue;
+      bool rows_ready = false;
+      for (const TriTerm& tt : kTriTerms) {
+        if (tt.b != bvar) continue;
+        const void* fp[2] = {nullptr, nullptr};
+        const void* fa[2] = {nullptr, nullptr};
+        bool live = false;
+        for (int k = 0; k < 2; ++k)
+          if (tt.f[k][0] >= 0 && in[tt.f[k][0]] && in[tt.f[k][1]]) {
+            fp[k] = in[tt.f[k][0]];
+            fa[k] = in[tt.f[k][1]];
+            live = true;
+          }
+        if (!live || !in[tt.a] || !in[tt.d]) continue;
+        void* dphi[2] = {nullptr, nullptr};
+        void* dA[2] = {nullptr, nullptr};
         for (int k = 0; k < 2; ++k)
           if (fp[k]) {
-            want_pb = want_pb || out[tt.f[k][0]];
-            want_ab = want_ab || out[tt.f[k][1]];
+            dphi[k] = out[tt.f[k][0]];
+            dA[k] = out[tt.f[k][1]];
           }
-        if (e1 > e0) {
-          void* gph = want_pb ? pbar : nullptr;
-          void* gy = want_b ? ybar : nullptr;
-          void* b[] = {&ep, &e0, &e1, &gph, &gy};
-          if ((st = cgtp::launch(kfinal, unsigned((e1 - e0 + 63) / 64), 64, 0, s, b, &err)) != CGTP_OK)
+        const bool want_a = out[tt.a] != nullptr, want_d = out[tt.d] != nullptr, want_b = out[tt.b] != nullptr;
+        const bool want_pb = dphi[0] || dphi[1], want_ab = dA[0] || dA[1];
+        if (!want_a && !want_d && !want_b && !want_pb && !want_ab) continue;
+        if (!rows_ready && e1 > e0) {
+          const void* yop = in[bvar];
+          void* a[] = {(void*)&yop, &e0, &e1, &Gb};
+          if ((st = cgtp::launch(kprep, unsigned((e1 - e0 + 63) / 64), 64, 0, s, a, &err)) != CGTP_OK)
             return fail(st, err);
-          if (want_b) {
-            void* dst = static_cast<char*>(out[tt.b]) + (size_t)e0 * SH * el;
-            if ((st = accum(dst, SH, ybar, SH, 0, e1 - e0, SH)) != CGTP_OK) return fail(st, err);
-          }
-          for (int k = 0; k < 2; ++k)
-            if (fp[k] && out[tt.f[k][0]]) {   // d/dphi_k = A_k H: half k of phi-bar
-              void* dst = static_cast<char*>(out[tt.f[k][0]]) + (size_t)e0 * K * el;
-              if ((st = accum(dst, K, pbar, K2, k * K, e1 - e0, K)) != CGTP_OK) return fail(st, err);
-            }
         }
-        if (want_ab) {   // d/dA_k = phi_k^T H: rows k K .. k K + K - 1 of A-bar
-          int n = K2 * NW, ns = 8 * nch;   // the slots this chunk's receiver pass wrote
-          void* b[] = {&ap, &ns, &n, &abar};
-          if ((st = cgtp::launch(kred, unsigned((n + 63) / 64), 512, 0, s, b, &err)) != CGTP_OK) return fail(st, err);
-          for (int k = 0; k < 2; ++k)
-            if (fp[k] && out[tt.f[k][1]]) {
-              const void* src = static_cast<char*>(abar) + (size_t)k * K * NW * el;
-              if ((st = accum(out[tt.f[k][1]], NW, src, NW, 0, K, NW)) != CGTP_OK) return fail(st, err);
-            }
+        rows_ready = true;
+        // Stacked factors [phi_1 | phi_2] for the chunk's edges and [A_1; A_2].
+        if (e1 > e0) {
+          void* a[] = {(void*)&fp[0], (void*)&fp[1], &e0, &e1, &pk};
+          long long n = (long long)(e1 - e0) * K2;
+          if ((st = cgtp::launch(kpphi, unsigned((n + 255) / 256), 256, 0, s, a, &err)) != CGTP_OK)
+            return fail(st, err);
+        }
+        {
+          void* a[] = {(void*)&fa[0], (void*)&fa[1], &apk};
+          long long n = (long long)K2 * NW;
+          if ((st = cgtp::launch(kpa, unsigned((n + 255) / 256), 256, 0, s, a, &err)) != CGTP_OK)
+            return fail(st, err);
+        }
+        // The kernels index the radial values by sorted edge: shift the chunk's packed rows to e0.
+        const void* phi_arg = static_cast<const char*>(pk) - (ptrdiff_t)e0 * K2 * el;
+        const void* av = in[tt.a];
+        const void* dv = in[tt.d];
+        if (want_a) {   // node slot open: the source pass, added into the output
+          if (!bounds_done) {
+            if ((st = source_bounds(tp, fam, G, d, L, c, ws, s, &sb, &se, &err)) != CGTP_OK) return fail(st, err);
+            bounds_done = true;
+          }
+          const cgtp::TaskGroups tsrc = cgtp::task_groups(cgtp::source_tasks(tp));
+          int n = G.n, per = (G.n + 7) / 8, acc = 1;
+          void* dst = out[tt.a];
+          void* a[] = {(void*)&phi_arg, &apk, &Gb, (void*)&dv, (void*)&d.recv, &sb, &se, (void*)&d.src_edge,
+                       &dst, &n, &per, &e0, &acc, (void*)&d.sorder};
+          if ((st = cgtp::launch(ksrc, unsigned(8 * tsrc.tasks.size() * per), 64 * kSrcSplit * tsrc.ncb, 0, s, a,
+                                 &err)) != CGTP_OK)
+            return fail(st, err);
+        }
+        if (want_d && nrec > 0) {   // cotangent slot open: the forward, added into the output rows
+          const cgtp::TaskGroups tg = cgtp::task_groups(cgtp::forward_tasks(tp));
+          int per = (nrec + 7) / 8;
+          void* dst = out[tt.d];
+          void* a[] = {(void*)&av, (void*)&phi_arg, &apk, &Gb, (void*)&d.row_ptr, (void*)&d.col, &dst, &i0, &nrec,
+                       &per, &e0, (void*)&ord};
+          if ((st = cgtp::launch(kfwd, unsigned(8 * tg.tasks.size() * per), 64 * cgtp::fwd_split(tp) * tg.ncb, 0, s,
+                                 a, &err)) != CGTP_OK)
+            return fail(st, err);
+        }
+        if ((want_b || want_pb || want_ab) && nrec > 0) {   // edge-operand and weight slots: the receiver pass
+          int per, nch, acc_slots = 0;
+          chunk_geometry(nrec, &per, &nch);
+          void* a[] = {(void*)&av, (void*)&phi_arg, &apk, &Gb, (void*)&d.row_ptr, (void*)&d.col, (void*)&dv,
+                       &ep, &ap, &i0, &nrec, &per, &nch, &e0, &eps, &acc_slots, (void*)&ord};
+          if ((st = cgtp::launch(krecv, unsigned(8 * L.ntask_r * nch), 64 * kRecvGroup, 0, s, a, &err)) != CGTP_OK)
+            return fail(st, err);
+          if (e1 > e0 && (want_b || want_pb)) {   // d/dphi_k = A_k H: half k of phi-bar; Y-bar of slot b
+            void* g1 = rows_at(dphi[0], e0, K);
+            void* g2 = rows_at(dphi[1], e0, K);
+            void* gy = want_b ? rows_at(out[tt.b], e0, SH) : nullptr;
+            void* b[] = {&ep, &e0, &e1, &g1, &g2, &gy};
+            if ((st = cgtp::launch(kfinal, unsigned((e1 - e0 + 63) / 64), 64, 0, s, b, &err)) != CGTP_OK)
+              return fail(st, err);
+          }
+          if (want_ab) {   // d/dA_k = phi_k^T H: rows k K .. k K + K - 1 of this pass's A-bar
+            int ns = 8 * nch;   // the slots this chunk's receiver pass wrote
+            void* b[] = {&ap, &ns, &dA[0], &dA[1]};
+            if ((st = cgtp::launch(kred, unsigned((K2 * NW + 63) / 64), 512, 0, s, b, &err)) != CGTP_OK)
+              return fail(st, err);
+          }
         }
       }
     }

@@ -552,7 +552,8 @@ void emit_wave_combine_names(Out& o, const std::vector<std::string>& names, int 
 // the receiver's edges are dealt round-robin to the fwd_split waves of the workgroup and their
 // partial sums combined in LDS.  Paths are processed in register-budgeted subsets, each
 // re-walking the edges.
-void emit_fwd_task(Out& o, const Plan& p, int ti, const Task& T, int row_stride = 0) {
+// accumulate: add into `out` instead of overwriting it (the third-order passes sum terms there).
+void emit_fwd_task(Out& o, const Plan& p, int ti, const Task& T, int row_stride = 0, bool accumulate = false) {
   const int MUL = p.out[p.paths[T.paths[0]].i_out].mul;
   const std::vector<int> obs = out_blocks_of(p, T.paths);
   o.open(F("DEV void fwd_t%d(%s, real* sm, int node, int e_base)", ti, kFwdArgs));
@@ -584,7 +585,7 @@ void emit_fwd_task(Out& o, const Plan& p, int ti, const Task& T, int row_stride 
   o.line(F("real* __restrict__ dst = out + (i64)node * %d + u;", p.c_out));
   for (int ob : obs)
     for (int m = 0; m < p.out[ob].dim(); ++m)
-      o.line(F("dst[%d] = acc%d_%d;", p.out[ob].offset + m * MUL, ob, m));
+      o.line(F(accumulate ? "dst[%d] += acc%d_%d;" : "dst[%d] = acc%d_%d;", p.out[ob].offset + m * MUL, ob, m));
   o.close();
   o.close();
 }
@@ -1153,20 +1154,26 @@ void emit_recv_edge_final_y(Out& o, const Plan& p, const std::vector<Task>& task
   const int K = p.K, row = recv_partial_row(p);
   std::vector<int> off;
   for (int k = 0, c = 0; k < int(tasks.size()); c += recv_task_width(p, tasks[k]), ++k) off.push_back(c);
+  // Added into the destinations (rows e - e0): phi-bar columns 0 .. K/2 - 1 into gphi1 and
+  // K/2 .. K - 1 into gphi2 (the derivatives for the two stacked radial factors), Y-bar into gy;
+  // each nullable.
+  const int Kh = K / 2;
   o.line("extern \"C\" __global__ void __launch_bounds__(64)");
-  o.open("cgtp_edge_final_y(const real* __restrict__ ep, int e0, int e1, real* __restrict__ gphi,"
-         " real* __restrict__ gy)");
+  o.open("cgtp_edge_final_y(const real* __restrict__ ep, int e0, int e1, real* __restrict__ gphi1,"
+         " real* __restrict__ gphi2, real* __restrict__ gy)");
   o.line("const int e = e0 + (int)(blockIdx.x * 64 + threadIdx.x);");
   o.line("if (e >= e1) return;");
   o.line(F("const real* __restrict__ rw = ep + (i64)((e - e0) >> 6) * %d + ((e - e0) & 63);", 64 * row));
   o.line("#define RW(c) rw[64 * (c)]");
-  o.open("if (gphi)");
-  for (int q = 0; q < K; ++q) {
-    std::string ex;
-    for (size_t t = 0; t < tasks.size(); ++t) ex += (t ? " + " : "") + F("RW(%d)", off[t] + q);
-    o.line(F("gphi[(i64)(e - e0) * %d + %d] = ", K, q) + ex + ";");
+  for (int h = 0; h < 2; ++h) {
+    o.open(F("if (gphi%d)", h + 1));
+    for (int q = h * Kh; q < (h + 1) * Kh; ++q) {
+      std::string ex;
+      for (size_t t = 0; t < tasks.size(); ++t) ex += (t ? " + " : "") + F("RW(%d)", off[t] + q);
+      o.line(F("gphi%d[(i64)(e - e0) * %d + %d] += ", h + 1, Kh, q - h * Kh) + ex + ";");
+    }
+    o.close();
   }
-  o.close();
   o.open("if (gy)");
   std::vector<std::vector<int>> yc;
   for (const Task& t : tasks) yc.push_back(recv_task_ycols(p, t));
@@ -1177,14 +1184,14 @@ void emit_recv_edge_final_y(Out& o, const Plan& p, const std::vector<Task>& task
       if (it == yc[t].end()) continue;
       ex += (ex.empty() ? "" : " + ") + F("RW(%d)", off[t] + K + int(it - yc[t].begin()));
     }
-    o.line(F("gy[(i64)(e - e0) * %d + %d] = ", p.sh_dim, m) + (ex.empty() ? std::string("R(0)") : ex) + ";");
+    if (!ex.empty()) o.line(F("gy[(i64)(e - e0) * %d + %d] += ", p.sh_dim, m) + ex + ";");
   }
   o.close();
   o.line("#undef RW");
   o.close();
 }
 
-// Operand packing and accumulation of the third-order passes.  Their kernels are generated for
+// Operand packing and A-bar reduction of the third-order passes.  Their kernels are generated for
 // 2K radial values, so that a weight phi_1 A_1 + phi_2 A_2 is one product of the stacked
 // [phi_1 | phi_2] (E x 2K) and [A_1; A_2] (2K x N_w); a missing factor is zero.
 void emit_tri_helpers(Out& o, const Plan& p) {
@@ -1206,14 +1213,30 @@ void emit_tri_helpers(Out& o, const Plan& p) {
   o.line("const real* src = k < half ? a1 : a2;");
   o.line("dst[k] = src ? src[k < half ? k : k - half] : R(0);");
   o.close();
-  // dst[r * dst_ld + c] += src[r * src_ld + src_off + c] for r < rows, c < cols.
-  o.line("extern \"C\" __global__ void __launch_bounds__(256)");
-  o.open("cgtp_tri_accum(real* __restrict__ dst, int dst_ld, const real* __restrict__ src, int src_ld, int src_off,"
-         " int rows, int cols)");
-  o.line("const i64 k = (i64)blockIdx.x * 256 + threadIdx.x;");
-  o.line("if (k >= (i64)rows * cols) return;");
-  o.line("const i64 r = k / cols; const int c = (int)(k - r * cols);");
-  o.line("dst[r * dst_ld + c] += src[r * src_ld + src_off + c];");
+  // A-bar of a receiver pass: the fixed-order sum of its nslot partial slots (as cgtp_a_reduce),
+  // rows 0 .. K/2 - 1 added into dst1 and rows K/2 .. K - 1 into dst2 (each nullable).
+  o.line("extern \"C\" __global__ void __launch_bounds__(512)");
+  o.open("cgtp_tri_a_reduce(const real* __restrict__ ap, int nslot, real* __restrict__ dst1, real* __restrict__ dst2)");
+  o.line(F("const int n = %d;", K2 * p.n_w));
+  o.line("__shared__ real part[8][64];");
+  o.line("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
+  o.line("const int k = (int)blockIdx.x * 64 + lane;");
+  o.line("const int q = (nslot + 7) / 8, s0 = w * q, s1 = min(nslot, s0 + q);");
+  o.line("real a0 = R(0), a1 = R(0), a2 = R(0), a3 = R(0);");
+  o.open("if (k < n)");
+  o.line("int s = s0;");
+  o.line("for (; s + 3 < s1; s += 4) { a0 += ap[(i64)s * n + k]; a1 += ap[(i64)(s + 1) * n + k];"
+         " a2 += ap[(i64)(s + 2) * n + k]; a3 += ap[(i64)(s + 3) * n + k]; }");
+  o.line("for (; s < s1; ++s) a0 += ap[(i64)s * n + k];");
+  o.close();
+  o.line("part[w][lane] = (a0 + a1) + (a2 + a3);");
+  o.line("__syncthreads();");
+  o.open("if (w == 0 && k < n)");
+  o.line("const real v = ((part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane])) +"
+         " ((part[4][lane] + part[5][lane]) + (part[6][lane] + part[7][lane]));");
+  o.line(F("const int half = %d;", K * p.n_w));
+  o.line("if (k < half) { if (dst1) dst1[k] += v; } else { if (dst2) dst2[k - half] += v; }");
+  o.close();
   o.close();
 }
 
@@ -1541,7 +1564,7 @@ std::string generate_source(const Plan& p, const std::string& family, std::strin
     const std::vector<Task>& ft = forward_tasks(p);
     int nacc = 1;
     for (int k = 0; k < int(ft.size()); ++k) {
-      emit_fwd_task(o, p, k, ft[k], bwd_row_stride(p));
+      emit_fwd_task(o, p, k, ft[k], bwd_row_stride(p), true);
       int n = 0;
       for (int ob : out_blocks_of(p, ft[k].paths)) n += p.out[ob].dim();
       nacc = std::max(nacc, n);
