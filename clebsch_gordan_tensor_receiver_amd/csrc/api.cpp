@@ -190,11 +190,14 @@ struct TriLayout {
   size_t gy_off[3] = {0, 0, 0}, pk_off = 0, ak_off = 0, total = 0;
 };
 
-TriLayout tri_layout(const cgtp::Plan& tp, const cgtp::Graph& g) {
+TriLayout tri_layout(const cgtp::Plan& p, const cgtp::Plan& tp, const cgtp::Graph& g) {
   TriLayout T;
   const int rs = cgtp::bwd_row_stride(tp), K2 = tp.K;
   const int grow = rs + K2;   // the rows of one edge operand at a time, and the packed radial factors
-  T.L = chunked_layout(tp, g, grow, cgtp::recv_partial_row(tp), int(cgtp::recv_backward_tasks(tp).size()));
+  // The receiver passes run on the 2K plan (stacked factors) or on the plan itself (one factor):
+  // partial rows for the wider of the two; the A-bar slots are sized by the 2K plan.
+  const int row = std::max(cgtp::recv_partial_row(tp), cgtp::recv_partial_row(p));
+  T.L = chunked_layout(tp, g, grow, row, int(cgtp::recv_backward_tasks(tp).size()));
   const size_t em = size_t(T.L.emax), el = tp.elem();
   size_t off = T.L.g_off;
   T.gy_off[0] = T.gy_off[1] = T.gy_off[2] = off;
@@ -355,6 +358,7 @@ cgtp_status_t cgtp_plan_compile(cgtp_plan_t plan, int ops) {
       cgtp::Plan* tp = nullptr;
       cgtp_status_t st = tri_plan(plan->p, &tp, &err);
       if (st == CGTP_OK) st = cgtp::compile_family(*tp, "tri", &err);
+      if (st == CGTP_OK) st = cgtp::compile_family(plan->p, "tri1", &err);
       if (st != CGTP_OK) return fail(st, err);
     }
   } else {
@@ -453,7 +457,7 @@ cgtp_status_t cgtp_workspace_size(cgtp_plan_t plan, cgtp_graph_t g, cgtp_op_t op
     std::string err;
     cgtp_status_t st = tri_plan(plan->p, &tp, &err);
     if (st != CGTP_OK) return fail(st, err);
-    need = tri_layout(*tp, G).total;
+    need = tri_layout(plan->p, *tp, G).total;
   } else if (op == CGTP_OP_FORWARD) {
     need = forward_rows_bytes(p, G, p.scratch_budget);
   } else if (op == CGTP_OP_BACKWARD) {
@@ -884,7 +888,7 @@ cgtp_status_t cgtp_conv_triple_backward(cgtp_plan_t plan, cgtp_graph_t g, const 
   cgtp_status_t st = tri_plan(p, &tpp, &err);
   if (st != CGTP_OK) return fail(st, err);
   cgtp::Plan& tp = *tpp;
-  const TriLayout T = tri_layout(tp, G);
+  const TriLayout T = tri_layout(p, tp, G);
   if (!workspace || ws_bytes < T.total) return fail(CGTP_ERR_WORKSPACE, "workspace too small");
   cgtp::DeviceGraph d;
   if ((st = cgtp::device_graph(G, &d, &err)) != CGTP_OK) return fail(st, err);
@@ -899,6 +903,15 @@ cgtp_status_t cgtp_conv_triple_backward(cgtp_plan_t plan, cgtp_graph_t g, const 
       (st = cgtp::get_kernel(tp, fam, "cgtp_tri_a_reduce", &kred, &err)) != CGTP_OK ||
       (st = cgtp::get_kernel(tp, fam, "cgtp_tri_pack_phi", &kpphi, &err)) != CGTP_OK ||
       (st = cgtp::get_kernel(tp, fam, "cgtp_tri_pack_a", &kpa, &err)) != CGTP_OK)
+    return fail(st, err);
+  // The same passes with the plan's own K, for terms with one weight factor (no stacking).
+  hipFunction_t k1fwd, k1recv, k1src, k1final, k1red;
+  const char* fam1 = "tri1";
+  if ((st = cgtp::get_kernel(p, fam1, "cgtp_fwd", &k1fwd, &err)) != CGTP_OK ||
+      (st = cgtp::get_kernel(p, fam1, "cgtp_bwd_recv", &k1recv, &err)) != CGTP_OK ||
+      (st = cgtp::get_kernel(p, fam1, "cgtp_bwd_src", &k1src, &err)) != CGTP_OK ||
+      (st = cgtp::get_kernel(p, fam1, "cgtp_edge_final_y", &k1final, &err)) != CGTP_OK ||
+      (st = cgtp::get_kernel(p, fam1, "cgtp_tri_a_reduce", &k1red, &err)) != CGTP_OK)
     return fail(st, err);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int K = p.K, K2 = tp.K, SH = p.sh_dim, NW = p.n_w, el = int(p.elem());
@@ -963,21 +976,38 @@ cgtp_status_t cgtp_conv_triple_backward(cgtp_plan_t plan, cgtp_graph_t g, const 
             return fail(st, err);
         }
         rows_ready = true;
-        // Stacked factors [phi_1 | phi_2] for the chunk's edges and [A_1; A_2].
-        if (e1 > e0) {
-          void* a[] = {(void*)&fp[0], (void*)&fp[1], &e0, &e1, &pk};
-          long long n = (long long)(e1 - e0) * K2;
-          if ((st = cgtp::launch(kpphi, unsigned((n + 255) / 256), 256, 0, s, a, &err)) != CGTP_OK)
-            return fail(st, err);
-        }
-        {
+        // One live weight factor: the plan's own kernels take it as (phi, A).  Two: the 2K plan's
+        // kernels take the stacked factors [phi_1 | phi_2] (chunk rows) and [A_1; A_2].
+        const int one = fp[0] && fp[1] ? -1 : fp[0] ? 0 : 1;
+        const cgtp::Plan& kp = one >= 0 ? p : tp;
+        hipFunction_t kf = one >= 0 ? k1fwd : kfwd, kr = one >= 0 ? k1recv : krecv;
+        hipFunction_t ks = one >= 0 ? k1src : ksrc, kfi = one >= 0 ? k1final : kfinal;
+        hipFunction_t krd = one >= 0 ? k1red : kred;
+        const void* phi_arg = nullptr;
+        const void* a_arg = nullptr;
+        if (one >= 0) {
+          phi_arg = fp[one];
+          a_arg = fa[one];
+          if (one == 1) {   // the stacked kernels' first half carries it in the single-factor ones
+            dphi[0] = dphi[1];
+            dA[0] = dA[1];
+          }
+          dphi[1] = dA[1] = nullptr;
+        } else {
+          if (e1 > e0) {
+            void* a[] = {(void*)&fp[0], (void*)&fp[1], &e0, &e1, &pk};
+            long long n = (long long)(e1 - e0) * K2;
+            if ((st = cgtp::launch(kpphi, unsigned((n + 255) / 256), 256, 0, s, a, &err)) != CGTP_OK)
+              return fail(st, err);
+          }
           void* a[] = {(void*)&fa[0], (void*)&fa[1], &apk};
           long long n = (long long)K2 * NW;
           if ((st = cgtp::launch(kpa, unsigned((n + 255) / 256), 256, 0, s, a, &err)) != CGTP_OK)
             return fail(st, err);
+          // The kernels index the radial values by sorted edge: shift the chunk's packed rows to e0.
+          phi_arg = static_cast<const char*>(pk) - (ptrdiff_t)e0 * K2 * el;
+          a_arg = apk;
         }
-        // The kernels index the radial values by sorted edge: shift the chunk's packed rows to e0.
-        const void* phi_arg = static_cast<const char*>(pk) - (ptrdiff_t)e0 * K2 * el;
         const void* av = in[tt.a];
         const void* dv = in[tt.d];
         if (want_a) {   // node slot open: the source pass, added into the output
@@ -985,44 +1015,45 @@ cgtp_status_t cgtp_conv_triple_backward(cgtp_plan_t plan, cgtp_graph_t g, const 
             if ((st = source_bounds(tp, fam, G, d, L, c, ws, s, &sb, &se, &err)) != CGTP_OK) return fail(st, err);
             bounds_done = true;
           }
-          const cgtp::TaskGroups tsrc = cgtp::task_groups(cgtp::source_tasks(tp));
+          const cgtp::TaskGroups tsrc = cgtp::task_groups(cgtp::source_tasks(kp));
           int n = G.n, per = (G.n + 7) / 8, acc = 1;
           void* dst = out[tt.a];
-          void* a[] = {(void*)&phi_arg, &apk, &Gb, (void*)&dv, (void*)&d.recv, &sb, &se, (void*)&d.src_edge,
+          void* a[] = {(void*)&phi_arg, (void*)&a_arg, &Gb, (void*)&dv, (void*)&d.recv, &sb, &se, (void*)&d.src_edge,
                        &dst, &n, &per, &e0, &acc, (void*)&d.sorder};
-          if ((st = cgtp::launch(ksrc, unsigned(8 * tsrc.tasks.size() * per), 64 * kSrcSplit * tsrc.ncb, 0, s, a,
+          if ((st = cgtp::launch(ks, unsigned(8 * tsrc.tasks.size() * per), 64 * kSrcSplit * tsrc.ncb, 0, s, a,
                                  &err)) != CGTP_OK)
             return fail(st, err);
         }
         if (want_d && nrec > 0) {   // cotangent slot open: the forward, added into the output rows
-          const cgtp::TaskGroups tg = cgtp::task_groups(cgtp::forward_tasks(tp));
+          const cgtp::TaskGroups tg = cgtp::task_groups(cgtp::forward_tasks(kp));
           int per = (nrec + 7) / 8;
           void* dst = out[tt.d];
-          void* a[] = {(void*)&av, (void*)&phi_arg, &apk, &Gb, (void*)&d.row_ptr, (void*)&d.col, &dst, &i0, &nrec,
-                       &per, &e0, (void*)&ord};
-          if ((st = cgtp::launch(kfwd, unsigned(8 * tg.tasks.size() * per), 64 * cgtp::fwd_split(tp) * tg.ncb, 0, s,
+          void* a[] = {(void*)&av, (void*)&phi_arg, (void*)&a_arg, &Gb, (void*)&d.row_ptr, (void*)&d.col, &dst, &i0,
+                       &nrec, &per, &e0, (void*)&ord};
+          if ((st = cgtp::launch(kf, unsigned(8 * tg.tasks.size() * per), 64 * cgtp::fwd_split(kp) * tg.ncb, 0, s,
                                  a, &err)) != CGTP_OK)
             return fail(st, err);
         }
         if ((want_b || want_pb || want_ab) && nrec > 0) {   // edge-operand and weight slots: the receiver pass
           int per, nch, acc_slots = 0;
           chunk_geometry(nrec, &per, &nch);
-          void* a[] = {(void*)&av, (void*)&phi_arg, &apk, &Gb, (void*)&d.row_ptr, (void*)&d.col, (void*)&dv,
+          const int ntask_r = int(cgtp::recv_backward_tasks(kp).size());
+          void* a[] = {(void*)&av, (void*)&phi_arg, (void*)&a_arg, &Gb, (void*)&d.row_ptr, (void*)&d.col, (void*)&dv,
                        &ep, &ap, &i0, &nrec, &per, &nch, &e0, &eps, &acc_slots, (void*)&ord};
-          if ((st = cgtp::launch(krecv, unsigned(8 * L.ntask_r * nch), 64 * kRecvGroup, 0, s, a, &err)) != CGTP_OK)
+          if ((st = cgtp::launch(kr, unsigned(8 * ntask_r * nch), 64 * kRecvGroup, 0, s, a, &err)) != CGTP_OK)
             return fail(st, err);
           if (e1 > e0 && (want_b || want_pb)) {   // d/dphi_k = A_k H: half k of phi-bar; Y-bar of slot b
             void* g1 = rows_at(dphi[0], e0, K);
             void* g2 = rows_at(dphi[1], e0, K);
             void* gy = want_b ? rows_at(out[tt.b], e0, SH) : nullptr;
             void* b[] = {&ep, &e0, &e1, &g1, &g2, &gy};
-            if ((st = cgtp::launch(kfinal, unsigned((e1 - e0 + 63) / 64), 64, 0, s, b, &err)) != CGTP_OK)
+            if ((st = cgtp::launch(kfi, unsigned((e1 - e0 + 63) / 64), 64, 0, s, b, &err)) != CGTP_OK)
               return fail(st, err);
           }
           if (want_ab) {   // d/dA_k = phi_k^T H: rows k K .. k K + K - 1 of this pass's A-bar
             int ns = 8 * nch;   // the slots this chunk's receiver pass wrote
             void* b[] = {&ap, &ns, &dA[0], &dA[1]};
-            if ((st = cgtp::launch(kred, unsigned((K2 * NW + 63) / 64), 512, 0, s, b, &err)) != CGTP_OK)
+            if ((st = cgtp::launch(krd, unsigned((kp.K * NW + 63) / 64), 512, 0, s, b, &err)) != CGTP_OK)
               return fail(st, err);
           }
         }

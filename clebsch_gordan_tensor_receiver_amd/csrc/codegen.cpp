@@ -1150,14 +1150,14 @@ void emit_recv_edge_final(Out& o, const Plan& p, const std::vector<Task>& tasks)
 // Per-edge finalisation of the third-order passes: phi-bar (K values) and the edge-operand
 // gradient Y-bar (sh_dim values) as fixed-order sums of the receiver pass's task partials, written
 // for the chunk's edges (rows e - e0).
-void emit_recv_edge_final_y(Out& o, const Plan& p, const std::vector<Task>& tasks) {
+void emit_recv_edge_final_y(Out& o, const Plan& p, const std::vector<Task>& tasks, bool stacked) {
   const int K = p.K, row = recv_partial_row(p);
   std::vector<int> off;
   for (int k = 0, c = 0; k < int(tasks.size()); c += recv_task_width(p, tasks[k]), ++k) off.push_back(c);
-  // Added into the destinations (rows e - e0): phi-bar columns 0 .. K/2 - 1 into gphi1 and
-  // K/2 .. K - 1 into gphi2 (the derivatives for the two stacked radial factors), Y-bar into gy;
-  // each nullable.
-  const int Kh = K / 2;
+  // Added into the destinations (rows e - e0): with stacked factors phi-bar columns 0 .. K/2 - 1
+  // into gphi1 and K/2 .. K - 1 into gphi2 (the derivatives for the two radial factors), else all
+  // K columns into gphi1; Y-bar into gy; each nullable.
+  const int Kh = stacked ? K / 2 : K;
   o.line("extern \"C\" __global__ void __launch_bounds__(64)");
   o.open("cgtp_edge_final_y(const real* __restrict__ ep, int e0, int e1, real* __restrict__ gphi1,"
          " real* __restrict__ gphi2, real* __restrict__ gy)");
@@ -1165,7 +1165,8 @@ void emit_recv_edge_final_y(Out& o, const Plan& p, const std::vector<Task>& task
   o.line("if (e >= e1) return;");
   o.line(F("const real* __restrict__ rw = ep + (i64)((e - e0) >> 6) * %d + ((e - e0) & 63);", 64 * row));
   o.line("#define RW(c) rw[64 * (c)]");
-  for (int h = 0; h < 2; ++h) {
+  if (!stacked) o.line("(void)gphi2;");
+  for (int h = 0; h < (stacked ? 2 : 1); ++h) {
     o.open(F("if (gphi%d)", h + 1));
     for (int q = h * Kh; q < (h + 1) * Kh; ++q) {
       std::string ex;
@@ -1194,8 +1195,10 @@ void emit_recv_edge_final_y(Out& o, const Plan& p, const std::vector<Task>& task
 // Operand packing and A-bar reduction of the third-order passes.  Their kernels are generated for
 // 2K radial values, so that a weight phi_1 A_1 + phi_2 A_2 is one product of the stacked
 // [phi_1 | phi_2] (E x 2K) and [A_1; A_2] (2K x N_w); a missing factor is zero.
-void emit_tri_helpers(Out& o, const Plan& p) {
-  const int K2 = p.K, K = p.K / 2;
+// stacked false (the plan's own K, one radial factor): only the A-bar reduction, all rows into dst1.
+void emit_tri_helpers(Out& o, const Plan& p, bool stacked) {
+  const int K2 = p.K, K = stacked ? p.K / 2 : p.K;
+  if (stacked) {
   o.line("extern \"C\" __global__ void __launch_bounds__(256)");
   o.open("cgtp_tri_pack_phi(const real* __restrict__ p1, const real* __restrict__ p2, int e0, int e1,"
          " real* __restrict__ dst)");
@@ -1213,6 +1216,7 @@ void emit_tri_helpers(Out& o, const Plan& p) {
   o.line("const real* src = k < half ? a1 : a2;");
   o.line("dst[k] = src ? src[k < half ? k : k - half] : R(0);");
   o.close();
+  }
   // A-bar of a receiver pass: the fixed-order sum of its nslot partial slots (as cgtp_a_reduce),
   // rows 0 .. K/2 - 1 added into dst1 and rows K/2 .. K - 1 into dst2 (each nullable).
   o.line("extern \"C\" __global__ void __launch_bounds__(512)");
@@ -1235,7 +1239,10 @@ void emit_tri_helpers(Out& o, const Plan& p) {
   o.line("const real v = ((part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane])) +"
          " ((part[4][lane] + part[5][lane]) + (part[6][lane] + part[7][lane]));");
   o.line(F("const int half = %d;", K * p.n_w));
-  o.line("if (k < half) { if (dst1) dst1[k] += v; } else { if (dst2) dst2[k - half] += v; }");
+  if (stacked)
+    o.line("if (k < half) { if (dst1) dst1[k] += v; } else { if (dst2) dst2[k - half] += v; }");
+  else
+    o.line("(void)half; (void)dst2; if (dst1) dst1[k] += v;");
   o.close();
   o.close();
 }
@@ -1558,7 +1565,9 @@ std::string generate_source(const Plan& p, const std::string& family, std::strin
   // (the parent plan's K twice): rows from an edge operand, the forward over the backward's row
   // layout, the receiver and source passes of the backward, edge finalisation without the
   // position chain, and the packing / accumulation helpers.
-  if (family == "tri") {
+  // tri1: the same passes on the plan itself (K radial values), for terms with one weight factor.
+  if (family == "tri" || family == "tri1") {
+    const bool stacked = family == "tri";
     prelude(o, p, false, true);
     emit_prep_y(o, p);
     const std::vector<Task>& ft = forward_tasks(p);
@@ -1578,9 +1587,9 @@ std::string generate_source(const Plan& p, const std::string& family, std::strin
     auto st = source_tasks(p);
     for (int k = 0; k < int(st.size()); ++k) emit_bwd_src_task(o, p, k, st[k]);
     emit_src_dispatch(o, p, int(st.size()));
-    emit_recv_edge_final_y(o, p, rt);
+    emit_recv_edge_final_y(o, p, rt, stacked);
     emit_small_kernels(o);
-    emit_tri_helpers(o, p);
+    emit_tri_helpers(o, p, stacked);
     return o.s.str();
   }
   if (family == "bwd") {
