@@ -447,7 +447,7 @@ std::string phi_ptr(const Plan& p, const std::string& e, const std::string& grow
 
 void emit_recv_edge_loop(Out& o, const Plan& p, const std::vector<int>& blocks, const std::string& start,
                          const std::string& stride, const std::function<void()>& body, bool block_uc,
-                         int row_stride) {
+                         int row_stride, int nE) {
   auto ucn = [&](int b) { return block_uc ? F("uc%d", b) : std::string("uc"); };
   if (row_stride <= 0) row_stride = p.g_stride;
   auto xrow = [&](const char* pre, const char* j, const char* type) {
@@ -466,6 +466,24 @@ void emit_recv_edge_loop(Out& o, const Plan& p, const std::vector<int>& blocks, 
   o.line("const int el_ = eb_ + li_ * " + stride + ";");
   o.line("const int cl_ = col[el_ < e1 ? el_ : eb_];");
   o.line("const int ne_ = min(64, (e1 - eb_ + " + stride + " - 1) / " + stride + ");");
+  if (nE > 1) {
+    // Group h_ of the wave takes edge k_ + h_ of the batch: its sender from lane k_ + h_ of cl_
+    // (cl_ holds a valid sender in every lane), its rows and phi by per-lane pointers.
+    o.line(F("const int h_ = li_ / %d;", 64 / nE));
+    o.open(F("for (int k_ = 0; k_ < ne_; k_ += %d)", nE));
+    o.line("const bool ok_ = k_ + h_ < ne_;");
+    o.line("const int e = eb_ + (ok_ ? k_ + h_ : k_) * " + stride + ";");
+    o.line("const int j = __shfl(cl_, k_ + h_);");
+    xrow("x", "j", "const real ");
+    o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", row_stride));
+    o.line("const real* __restrict__ ph = " + phi_ptr(p, "e", "g") + ";");
+    for (int q = 0; q < p.K; ++q) o.line(F("const real f%d = ok_ ? ph[%d] : R(0);", q, q));
+    body();
+    o.close();
+    o.close();
+    o.close();
+    return;
+  }
   o.open("for (int k_ = 0; k_ < ne_; ++k_)");
   o.line("const int e = eb_ + k_ * " + stride + ";");
   o.line("const int j = __builtin_amdgcn_readlane(cl_, k_);");
@@ -553,14 +571,26 @@ void emit_wave_combine_names(Out& o, const std::vector<std::string>& names, int 
 // partial sums combined in LDS.  Paths are processed in register-budgeted subsets, each
 // re-walking the edges.
 // accumulate: add into `out` instead of overwriting it (the third-order passes sum terms there).
+// Edges per wave step of the channelwise forward: a block of at most 16 channels fills only a
+// quarter of the 64 lanes with one edge, so 4 edges of the receiver share the wave (their
+// coefficient rows then come through per-lane loads instead of scalar ones).  Measured: 16
+// channels, l <= 3 diamond graph, 99 -> 61 us; two edges of 32-channel blocks measured slower
+// (102 -> 109 us at l <= 3, 7.2 -> 9.9 ms at l <= 6: the per-lane row loads cost more than the
+// idle half of the lanes), so blocks above 16 channels keep one edge per wave.
+int edges_per_wave(int mul) { return mul <= 16 ? 4 : 1; }
+
 void emit_fwd_task(Out& o, const Plan& p, int ti, const Task& T, int row_stride = 0, bool accumulate = false) {
   const int MUL = p.out[p.paths[T.paths[0]].i_out].mul;
+  const int nE = edges_per_wave(MUL), gsz = 64 / nE;
   const std::vector<int> obs = out_blocks_of(p, T.paths);
   o.open(F("DEV void fwd_t%d(%s, real* sm, int node, int e_base)", ti, kFwdArgs));
   o.line(F("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) %% %d;",
            fwd_split(p)));
   emit_vz(o, p);
-  o.line(F("const int u = %d + lane;", T.cb * 64));
+  if (nE > 1)   // channel of the lane inside its edge group
+    o.line(F("const int u = lane %% %d;", gsz));
+  else
+    o.line(F("const int u = %d + lane;", T.cb * 64));
   o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
   std::vector<std::string> accs;
   for (int ob : obs)
@@ -577,11 +607,14 @@ void emit_fwd_task(Out& o, const Plan& p, int ti, const Task& T, int row_stride 
         emit_w(o, p, pi);
         emit_path_accumulate(o, p, pi, F("acc%d_", p.paths[pi].i_out));
       }
-    }, false, row_stride);
+    }, false, row_stride, nE);
     o.close();
   }
+  // Edge groups of the wave hold partial sums of the same channels: add them (fixed order).
+  for (int span = gsz; span < 64; span *= 2)
+    for (const std::string& a : accs) o.line(F("%s += __shfl_xor(%s, %d);", a.c_str(), a.c_str(), span));
   emit_wave_combine_names(o, accs, fwd_split(p));
-  o.open(F("if (w == 0 && u < %d)", MUL));
+  o.open(nE > 1 ? F("if (w == 0 && lane < %d && u < %d)", gsz, MUL) : F("if (w == 0 && u < %d)", MUL));
   o.line(F("real* __restrict__ dst = out + (i64)node * %d + u;", p.c_out));
   for (int ob : obs)
     for (int m = 0; m < p.out[ob].dim(); ++m)
@@ -940,12 +973,17 @@ const char* kSrcArgs =
 // receivers' mbar rows of the next edge are loaded one edge ahead.
 void emit_bwd_src_task(Out& o, const Plan& p, int ti, const Task& T) {
   const int MUL = p.in[p.paths[T.paths[0]].i_in].mul, K = p.K;
+  // Blocks of at most 16 channels: 4 out-edges per wave step, one per 16-lane group (as the forward).
+  const int nE = edges_per_wave(MUL), gsz = 64 / nE;
   const std::vector<int> ibs = in_blocks_of(p, T.paths);
   o.open(F("DEV void bws_t%d(%s, real* sm, int node, int e_base, int accumulate)", ti, kSrcArgs));
   o.line(F("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) %% %d;",
            kSrcSplit));
   emit_vz(o, p);
-  o.line(F("const int u = %d + lane;", T.cb * 64));
+  if (nE > 1)
+    o.line(F("const int u = lane %% %d, h_ = lane / %d;", gsz, gsz));
+  else
+    o.line(F("const int u = %d + lane;", T.cb * 64));
   o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
   std::vector<std::string> accs;
   for (int ib : ibs)
@@ -972,13 +1010,21 @@ void emit_bwd_src_task(Out& o, const Plan& p, int ti, const Task& T) {
   o.line("const int el_ = src_edge[kl_ < s1 ? kl_ : kb_];");
   o.line("const int il_ = recv[el_];");
   o.line(F("const int ne_ = min(64, (s1 - kb_ + %d) / %d);", kSrcSplit - 1, kSrcSplit));
-  o.open("for (int k_ = 0; k_ < ne_; ++k_)");
-  o.line("const int e = __builtin_amdgcn_readlane(el_, k_);");
-  o.line("const int i_ = __builtin_amdgcn_readlane(il_, k_);");
+  if (nE > 1) {   // group h_ takes out-edge k_ + h_ (el_, il_ hold valid ids in every lane)
+    o.open(F("for (int k_ = 0; k_ < ne_; k_ += %d)", nE));
+    o.line("const bool ok_ = k_ + h_ < ne_;");
+    o.line("const int e = __shfl(el_, k_ + h_);");
+    o.line("const int i_ = __shfl(il_, k_ + h_);");
+  } else {
+    o.open("for (int k_ = 0; k_ < ne_; ++k_)");
+    o.line("const int e = __builtin_amdgcn_readlane(el_, k_);");
+    o.line("const int i_ = __builtin_amdgcn_readlane(il_, k_);");
+  }
   mrow("mb", "i_", "const real ");
   o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", bwd_row_stride(p)));
   o.line("const real* __restrict__ ph = " + phi_ptr(p, "e", "g") + ";");
-  for (int q = 0; q < K; ++q) o.line(F("const real f%d = ph[%d];", q, q));
+  for (int q = 0; q < K; ++q)
+    o.line(nE > 1 ? F("const real f%d = ok_ ? ph[%d] : R(0);", q, q) : F("const real f%d = ph[%d];", q, q));
   for (int pi : S) {
     const Path& P = p.paths[pi];
     const int d1 = 2 * P.l1 + 1, d3 = 2 * P.l3 + 1, ib = P.i_in;
@@ -1007,8 +1053,10 @@ void emit_bwd_src_task(Out& o, const Plan& p, int ti, const Task& T) {
   o.close();
   o.close();
   }
+  for (int span = gsz; span < 64; span *= 2)
+    for (const std::string& a : accs) o.line(F("%s += __shfl_xor(%s, %d);", a.c_str(), a.c_str(), span));
   emit_wave_combine_names(o, accs, kSrcSplit);
-  o.open(F("if (w == 0 && u < %d)", MUL));
+  o.open(nE > 1 ? F("if (w == 0 && lane < %d && u < %d)", gsz, MUL) : F("if (w == 0 && u < %d)", MUL));
   o.line(F("real* __restrict__ dst = gx + (i64)node * %d + u;", p.c_in));
   o.open("if (accumulate)");
   for (int ib : ibs)

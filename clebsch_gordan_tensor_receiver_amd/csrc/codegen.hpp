@@ -86,9 +86,13 @@ void emit_edge_vector(Out& o);
 void emit_prep(Out& o, const Plan& p, bool with_y = false);
 std::vector<int> in_blocks_of(const Plan& p, const std::vector<int>& paths);
 std::vector<int> out_blocks_of(const Plan& p, const std::vector<int>& paths);
+// nE > 1 (2 or 4): the wave's lanes form nE groups of 64 / nE channels and take nE consecutive
+// edges of its share at a time, group h the h-th (blocks of at most 64 / nE channels); the edge
+// index e, sender j, row pointer g and phi values f<q> are then per lane (zero phi for a group
+// past the last edge).
 void emit_recv_edge_loop(Out& o, const Plan& p, const std::vector<int>& blocks, const std::string& start,
                          const std::string& stride, const std::function<void()>& body, bool block_uc = false,
-                         int row_stride = 0);
+                         int row_stride = 0, int nE = 1);
 void emit_wave_combine(Out& o, const std::string& prefix, int n, int nw);
 void emit_swaps(Out& o, const std::vector<std::pair<std::string, std::string>>& pairs, int width, bool f64);
 void emit_edge_final(Out& o, const Plan& p, int ntask, int V);
