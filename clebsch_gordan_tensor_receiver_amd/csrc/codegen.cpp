@@ -806,10 +806,19 @@ void emit_bwd_recv_task(Out& o, const Plan& p, int ti, const Task& T, int col_of
   const std::vector<int> ycols = recv_task_ycols(p, T);
   const int V = recv_task_width(p, T);
   auto ycol = [&](int y) { return K + int(std::find(ycols.begin(), ycols.end(), y) - ycols.begin()); };
+  // Blocks of at most 16 (32) channels: 4 (2) edges per wave step, one per 16-lane row (32-lane
+  // half); the per-edge channel reductions are then row sums (and one add across the two rows of a
+  // half) instead of the 64-lane transposition, and each group stores its own edge's columns.  The
+  // rows this pass reads per edge are short (Y, or large paths' coefficients already read per lane),
+  // so unlike the forward the 32-channel case gains too.
+  const int nE = MUL <= 16 ? 4 : MUL <= 32 ? 2 : 1, gsz = 64 / nE;
   o.open(F("DEV void bwr_t%d(%s, real* sm, int node, int e_base, int eps, int slot, int acc)", ti, kRecvArgs));
   o.line("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
   emit_vz(o, p);
-  o.line(F("const int u = %d + lane;", T.cb * 64));
+  if (nE > 1)
+    o.line(F("const int u = lane %% %d;", gsz));
+  else
+    o.line(F("const int u = %d + lane;", T.cb * 64));
   o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
   emit_a_loads(o, p, T.paths);
   std::vector<std::string> aa;  // A-bar accumulators: K per path of the task
@@ -836,7 +845,7 @@ void emit_bwd_recv_task(Out& o, const Plan& p, int ti, const Task& T, int col_of
   }
   o.line("const int e0 = row_ptr[node], e1 = row_ptr[node + 1];");
   const int yoff = p.g_stride;  // Y values follow the G values in a workspace row
-  emit_recv_edge_loop2(o, p, in_blocks_of(p, T.paths), bwd_row_stride(p), [&] {
+  auto body = [&] {
     for (int v = 0; v < V; ++v) o.line(F("real v%d = R(0);", v));
     int ai = 0;
     for (int pi : T.paths) {
@@ -900,6 +909,19 @@ void emit_bwd_recv_task(Out& o, const Plan& p, int ti, const Task& T, int col_of
         o.line("}");
       }
     }
+    if (nE > 1) {   // one edge per group: row sums (and the two rows of a half), stored by its first lane
+      for (int k = 0; k < V; ++k) {
+        o.line(F("v%d = rowsum(v%d);", k, k));
+        if (gsz == 32) o.line(F("v%d += __shfl_xor(v%d, 16);", k, k));
+        o.line(F("asm volatile(\"\" : \"+v\"(v%d));", k));
+      }
+      o.open(F("if ((lane & %d) == 0 && ok_)", gsz - 1));
+      o.line(F("real* __restrict__ dst = ep + ((i64)((e - e_base) >> 6) * %d + %d) * 64 + ((e - e_base) & 63);", row,
+               col_off));
+      for (int k = 0; k < V; ++k) o.line(F("dst[%d] = v%d;", 64 * k, k));
+      o.close();
+      return;
+    }
     // Transpose-reduce the V partial sums over the 64 lanes: afterwards lane group r = lane / 16
     // holds columns r Q .. r Q + Q - 1 in v0 .. v(Q-1).  The empty asm keeps the row sums in all
     // lanes, so that their last DPP step is not moved under the store's lane mask.
@@ -919,10 +941,16 @@ void emit_bwd_recv_task(Out& o, const Plan& p, int ti, const Task& T, int col_of
              " + ((e - e_base) & 63);", row, col_off, Q));
     for (int k = 0; k < Q; ++k) o.line(F("dst[%d] = v%d;", 64 * k, k));
     o.close();
-  });
+  };
+  if (nE > 1)
+    emit_recv_edge_loop(o, p, in_blocks_of(p, T.paths), "0", "1", body, false, bwd_row_stride(p), nE);
+  else
+    emit_recv_edge_loop2(o, p, in_blocks_of(p, T.paths), bwd_row_stride(p), body);
+  for (int span = gsz; span < 64; span *= 2)
+    for (const std::string& a : aa) o.line(F("%s += __shfl_xor(%s, %d);", a.c_str(), a.c_str(), span));
   o.close();  // node >= 0
   emit_wave_combine(o, "aa", int(aa.size()), kRecvGroup);
-  o.open(F("if (w == 0 && u < %d)", MUL));
+  o.open(nE > 1 ? F("if (w == 0 && lane < %d && u < %d)", gsz, MUL) : F("if (w == 0 && u < %d)", MUL));
   o.line(F("real* __restrict__ dst = ap + (i64)slot * %d + u;", K * p.n_w));
   // acc = 0 (a single receiver chunk): the slot is written, not accumulated, so it needs no
   // zero fill; every slot's workgroup runs, with node = -1 for missing receivers.
