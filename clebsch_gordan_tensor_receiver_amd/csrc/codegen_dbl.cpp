@@ -164,14 +164,26 @@ const char* kDArgs =
 
 // Edge loop over the receiver's in-edges (one wave); loads x and xdot rows, phi and phidot, the G
 // and Gdot rows.  Body sees e, g (G row), gd (Gdot row), f<q>, fd<q>, x<b>_<m>, xd<b>_<m>.
-void emit_dedge_loop(Out& o, const Plan& p, const std::vector<int>& blocks, const std::function<void()>& body) {
-  o.open("for (int e = e0; e < e1; ++e)");
+// nE > 1 (2 or 4): lane group h_ (64 / nE lanes, `h_` in scope) takes edge eb + h_ of each step
+// of nE edges; e, j and the row pointers are then per lane, and a group past the last edge reads
+// the step's first edge with zero phi and phi-dot (`ok_` false).
+void emit_dedge_loop(Out& o, const Plan& p, const std::vector<int>& blocks, const std::function<void()>& body,
+                     int nE = 1) {
+  if (nE > 1) {
+    o.open(F("for (int eb_ = e0; eb_ < e1; eb_ += %d)", nE));
+    o.line("const bool ok_ = eb_ + h_ < e1;");
+    o.line("const int e = ok_ ? eb_ + h_ : eb_;");
+  } else {
+    o.open("for (int e = e0; e < e1; ++e)");
+    o.line("const bool ok_ = true;");
+  }
   o.line("const int j = col[e];");
   o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", 2 * p.g_stride));
   o.line(F("const real* __restrict__ gd = g + %d;", p.g_stride));
   o.line(F("const real* __restrict__ ph = phi + (i64)e * %d;", p.K));
   o.line(F("const real* __restrict__ phd = vphi + (i64)e * %d;", p.K));
-  for (int q = 0; q < p.K; ++q) o.line(F("const real f%d = ph[%d], fd%d = sphi * phd[%d];", q, q, q, q));
+  for (int q = 0; q < p.K; ++q)
+    o.line(F("const real f%d = ok_ ? ph[%d] : R(0), fd%d = ok_ ? sphi * phd[%d] : R(0);", q, q, q, q));
   for (int b : blocks) {
     const Block& B = p.in[b];
     for (int m = 0; m < B.dim(); ++m) {
@@ -265,10 +277,17 @@ void emit_drecv_task(Out& o, const Plan& p, int ti, const Task& T, int col_off, 
   // Columns: K phi-bar-dot partials, then Y-bar-dot and first-order Y-bar over the task's Y entries.
   auto cd = [&](int y) { return K + int(std::find(yc.begin(), yc.end(), y) - yc.begin()); };
   auto cw = [&](int y) { return cd(y) + ny; };
+  // Blocks of at most 16 channels: 4 edges per wave step.  (Two edges per step for 32-channel
+  // blocks measured slower: per-lane coefficient rows of G and G-dot cost the registers that the
+  // wave-uniform rows keep in scalar ones.)
+  const int nE = MUL <= 16 ? 4 : 1, gsz = 64 / nE;
   o.open(F("DEV void drc_t%d(%s, real* sm, int node, int e_base, int eps, int slot)", ti, kDArgs));
   emit_vz(o, p);
   o.line("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
-  o.line(F("const int u = %d + lane;", T.cb * 64));
+  if (nE > 1)
+    o.line(F("const int u = lane %% %d, h_ = lane / %d;", gsz, gsz));
+  else
+    o.line(F("const int u = %d + lane;", T.cb * 64));
   o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
   emit_da_loads(o, p, T.paths);
   int na = 0;
@@ -316,6 +335,19 @@ void emit_drecv_task(Out& o, const Plan& p, int ti, const Task& T, int col_off, 
         o.line("}");
       }
     }
+    if (nE > 1) {   // one edge per group: row sums (and the two rows of a half), stored by its first lane
+      for (int k = 0; k < V; ++k) {
+        o.line(F("v%d = rowsum(v%d);", k, k));
+        if (gsz == 32) o.line(F("v%d += __shfl_xor(v%d, 16);", k, k));
+        o.line(F("asm volatile(\"\" : \"+v\"(v%d));", k));
+      }
+      o.open(F("if ((lane & %d) == 0 && ok_)", gsz - 1));
+      o.line(F("real* __restrict__ dst = ep + ((i64)((e - e_base) >> 6) * %d + %d) * 64 + ((e - e_base) & 63);", row,
+               col_off));
+      for (int k = 0; k < V; ++k) o.line(F("dst[%d] = v%d;", 64 * k, k));
+      o.close();
+      return;
+    }
     const int H = V / 2, Q = V / 4;
     const bool f64 = p.dtype == CGTP_F64;
     std::vector<std::pair<std::string, std::string>> pr;
@@ -332,10 +364,12 @@ void emit_drecv_task(Out& o, const Plan& p, int ti, const Task& T, int col_off, 
              " + ((e - e_base) & 63);", row, col_off, Q));
     for (int k = 0; k < Q; ++k) o.line(F("dst[%d] = v%d;", 64 * k, k));
     o.close();
-  });
+  }, nE);
+  for (int span = gsz; span < 64; span *= 2)
+    for (int k = 0; k < na; ++k) o.line(F("aa%d += __shfl_xor(aa%d, %d);", k, k, span));
   o.close();
   emit_wave_combine(o, "aa", na, 4);
-  o.open(F("if (w == 0 && u < %d)", MUL));
+  o.open(nE > 1 ? F("if (w == 0 && lane < %d && u < %d)", gsz, MUL) : F("if (w == 0 && u < %d)", MUL));
   o.line(F("real* __restrict__ dst = ap + (i64)slot * %d + u;", K * p.n_w));
   int ai = 0;
   for (int pi : T.paths)

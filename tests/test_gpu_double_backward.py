@@ -55,6 +55,17 @@ def test_double_backward_l3_ragged_channels(dtype):
     _compare(_gpu(case).double_backward(dirs), _oracle(case, dirs), dtype, label=f"l3 ragged {dtype}")
 
 
+@pytest.mark.parametrize("mul,dtype", [(16, "float32"), (12, "float64"), (24, "float32")])
+def test_double_backward_l3_narrow_blocks(mul, dtype):
+    # Blocks of at most 16 (32) channels take four (two) edges per wave step, a ragged tail of
+    # lanes past the block's width in each lane group.
+    irreps = dict(irreps_in=f"{mul}x0e+{mul}x1o+{mul}x2e", irreps_sh="1x0e+1x1o+1x2e+1x3o",
+                  irreps_out=f"{mul}x0e+{mul}x1o+{mul}x2e+{mul}x3o")
+    case = make_case(1, irreps_override=irreps, dtype=dtype)
+    dirs = make_directions(case)
+    _compare(_gpu(case).double_backward(dirs), _oracle(case, dirs), dtype, label=f"l3 {mul}ch {dtype}")
+
+
 @pytest.mark.parametrize("which", [("v_x",), ("v_pos",), ("v_edge_vec",), ("v_phi", "v_A"), ("v_A",)])
 def test_double_backward_partial_directions(which):
     # Missing directions are zero.
