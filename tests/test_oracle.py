@@ -563,6 +563,98 @@ def test_position_gradient_through_the_radial_basis(kind):
         assert abs(fd - got) <= 1e-6 * max(1.0, abs(got)), (kind, idx, fd, got)
 
 
+@pytest.mark.parametrize("kind", [1, 2])
+def test_radial_second_derivative_complex_step(kind):
+    from oracle import radial
+    rc, K = 5.0, 8
+    r = torch.tensor([0.7, 1.9, 3.3, 4.6, 4.99], dtype=torch.float64)
+    h = 1e-30
+    # Complex step of the first derivative written with complex-safe operations (the oracle's
+    # basis_derivative clips at the cutoff with torch.where on real inputs only).
+    def dphi(z):
+        if kind == radial.BESSEL:
+            n = torch.arange(1, K + 1, dtype=torch.float64)
+            a = n[None, :] * (math.pi / rc)
+            zz = z[:, None]
+            s, c = torch.sin(a * zz), torch.cos(a * zz)
+            b = math.sqrt(2.0 / rc) * s / zz
+            db = math.sqrt(2.0 / rc) * (a * c * zz - s) / zz ** 2
+            d = z / rc
+            u = 1.0 - 28.0 * d ** 6 + 48.0 * d ** 7 - 21.0 * d ** 8
+            du = (-168.0 * d ** 5 + 336.0 * d ** 6 - 168.0 * d ** 7) / rc
+            return db * u[:, None] + b * du[:, None]
+        D = rc / (K - 1)
+        diff = z[:, None] - torch.arange(K, dtype=torch.float64) * D
+        return -diff / (D * D) * torch.exp(-(diff ** 2) / (2.0 * D * D))
+    assert float((dphi(r.to(torch.complex128)).real - radial.basis_derivative(kind, r, rc, K)).abs().max()) < 1e-13
+    cs = dphi(r.to(torch.complex128) + 1j * h).imag / h
+    d2 = radial.basis_second_derivative(kind, r, rc, K)
+    assert float((cs - d2).abs().max()) <= 1e-12 * max(1.0, float(d2.abs().max()))
+    # Beyond the cutoff the Bessel basis and its derivatives are zero.
+    if kind == radial.BESSEL:
+        assert float(radial.basis_second_derivative(kind, torch.tensor([5.0, 6.0]), rc, K).abs().max()) == 0.0
+
+
+def _radial_dbl_case(kind):
+    ov = dict(irreps_in="2x0e+2x1o+2x2e", irreps_out="2x0e+2x1o+2x2e", irreps_sh=_sh_str(2), mode="uvu")
+    c = make_case(1, irreps_override=ov, n_nodes=10)
+    g = np.random.default_rng(61 + kind)
+    v = dict(v_x=g.normal(size=c.x.shape), v_e=g.normal(size=(len(c.recv), 3)), v_A=g.normal(size=c.A.shape))
+    return c, v, 3.0
+
+
+@pytest.mark.parametrize("kind", [1, 2])
+def test_radial_double_backward_matches_autograd(kind):
+    # Independent route: torch autograd of the forward with phi = basis(|r|), taken twice.
+    from oracle import radial
+    c, v, rc = _radial_dbl_case(kind)
+    K = c.phi.shape[1]
+    x = torch.tensor(c.x, requires_grad=True)
+    pos = torch.tensor(c.pos, requires_grad=True)
+    A = torch.tensor(c.A, requires_grad=True)
+    mbar = torch.tensor(c.grad_out, requires_grad=True)
+    ev = conv.edge_vectors(pos, c.shift, c.recv, c.send)
+    phi = radial.basis(kind, torch.sqrt((ev ** 2).sum(1)), rc, K)
+    m = conv.forward_conventional(c.problem, x, ev, c.recv, c.send, phi, A)
+    gx, gev, gA = torch.autograd.grad((m * mbar).sum(), (x, ev, A), create_graph=True)
+    s = ((gx * torch.as_tensor(v["v_x"])).sum() + (gev * torch.as_tensor(v["v_e"])).sum()
+         + (gA * torch.as_tensor(v["v_A"])).sum())
+    rx, rpos, rA, rm = torch.autograd.grad(s, (x, pos, A, mbar))
+    got = radial.double_backward(kind, rc, c.problem, c.x, c.edge_vec, c.recv, c.send, c.A, c.grad_out, **v,
+                                 n_nodes=c.n_nodes)
+    for k, ref in (("x", rx), ("pos", rpos), ("A", rA), ("grad_out", rm)):
+        np.testing.assert_allclose(got[k].numpy(), ref.numpy(), atol=1e-11 * max(1.0, ref.abs().max().item()))
+
+
+@pytest.mark.parametrize("kind", [1, 2])
+def test_radial_double_backward_matches_finite_differences(kind):
+    # <gg_theta, d> = d/dt <v, B(theta + t d)> with the first-order radial backward B (e-bar
+    # through Y plus the radial term), by central differences.
+    from oracle import radial
+    c, v, rc = _radial_dbl_case(kind)
+    K = c.phi.shape[1]
+    gg = radial.double_backward(kind, rc, c.problem, c.x, c.edge_vec, c.recv, c.send, c.A, c.grad_out, **v,
+                                n_nodes=c.n_nodes)
+    rng = np.random.default_rng(62)
+    d = dict(x=rng.normal(size=c.x.shape), pos=rng.normal(size=c.pos.shape), A=rng.normal(size=c.A.shape),
+             mbar=rng.normal(size=c.grad_out.shape))
+
+    def pairing(t):
+        x, pos, A, mb = (c.x + t * d["x"], c.pos + t * d["pos"], c.A + t * d["A"], c.grad_out + t * d["mbar"])
+        ev = conv.edge_vectors(pos, c.shift, c.recv, c.send)
+        phi = radial.basis(kind, radial.edge_lengths(ev), rc, K)
+        b = conv.backward(c.problem, x, ev, c.recv, c.send, phi, A, mb, n_nodes=c.n_nodes)
+        ge = b["edge_vec"] + radial.edge_vec_grad(kind, ev, rc, b["phi"])
+        return float((b["x"].numpy() * v["v_x"]).sum() + (ge.numpy() * v["v_e"]).sum()
+                     + (b["A"].numpy() * v["v_A"]).sum())
+
+    h = 1e-5
+    fd = (pairing(h) - pairing(-h)) / (2 * h)
+    an = float((gg["x"].numpy() * d["x"]).sum() + (gg["pos"].numpy() * d["pos"]).sum()
+               + (gg["A"].numpy() * d["A"]).sum() + (gg["grad_out"].numpy() * d["mbar"]).sum())
+    assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (fd, an)
+
+
 # ------------------------------------------------------------------ third-order derivative
 
 def _triple_case(n_nodes=10, seed=41, with_y_dirs=True):
