@@ -247,9 +247,6 @@ def main() -> int:
     if args.scratch_mib > 0:
         plan.set_scratch_budget(args.scratch_mib << 20)
     if args.radial:
-        if "dbl" in passes:
-            print("--radial: the double backward takes phi as an input", file=sys.stderr)
-            return 2
         plan.set_radial(2 if spec["radial"] == "gaussian" else 1, spec["rc"])
     graph = cg.Graph(w.n_nodes, w.recv, w.send, w.image)
     graph.set_order(args.order)
@@ -285,6 +282,8 @@ def main() -> int:
                     v_edge_vec=torch.tensor(normal_tensor(cfg, 6, (E, 3), dtype=dtype)[perm], **dev).contiguous(),
                     v_phi=torch.tensor(normal_tensor(cfg, 7, (E, K), dtype=dtype)[perm], **dev).contiguous(),
                     v_A=torch.tensor(normal_tensor(cfg, 9, (K, info["n_weights"]), dtype=dtype), **dev))
+        if args.radial:   # the radial values' direction follows from the position directions
+            del dirs["v_phi"]
         gg = dict(gg_x=torch.empty_like(x), gg_pos=torch.empty_like(pos), gg_edge_vec=torch.empty((E, 3), **dev),
                   gg_phi=torch.empty_like(phi), gg_A=torch.empty_like(A), gg_grad_out=torch.empty_like(out))
 
@@ -319,7 +318,7 @@ def main() -> int:
                                  grad_edge_vec=grads["edge_vec"], grad_phi=grads["phi"], grad_A=grads["A"],
                                  workspace=ws[ps])
             else:
-                cg.conv_double_backward(plan, graph, x, pos, shift, phi, A, gout, **dirs, **gg, workspace=ws[ps])
+                cg.conv_double_backward(plan, graph, x, pos, shift, phi_in, A, gout, **dirs, **gg, workspace=ws[ps])
 
     # Pre-roll: untimed steps for at least PREROLL_MS, so that the W warm-up steps and the K timed
     # steps run at ramped clocks.  Then exactly W warm-up and K timed steps, bracketed by

@@ -730,11 +730,16 @@ cgtp_status_t cgtp_conv_double_backward(cgtp_plan_t plan, cgtp_graph_t g, const 
                                         void* gg_edge_vec, void* gg_phi, void* gg_A, void* gg_grad_out,
                                         void* workspace, size_t ws_bytes, void* stream) {
   if (!plan || !g) return fail(CGTP_ERR_INVALID_ARG, "null plan or graph");
-  if (!x || !pos || !phi || !A || !grad_out) return fail(CGTP_ERR_INVALID_ARG, "null input tensor");
+  if (!x || !pos || !A || !grad_out) return fail(CGTP_ERR_INVALID_ARG, "null input tensor");
   cgtp::Plan& p = plan->p;
   cgtp::Graph& G = g->g;
   if (p.mode != CGTP_CHANNELWISE) return fail(CGTP_ERR_UNSUPPORTED, "double backward is channelwise only");
-  if (p.radial) return fail(CGTP_ERR_UNSUPPORTED, "double backward takes phi as an input (no fused radial basis)");
+  if ((phi == nullptr) != (p.radial != 0))
+    return fail(CGTP_ERR_INVALID_ARG, p.radial ? "phi must be NULL: the plan computes the radial basis"
+                                               : "null phi (the plan has no radial basis of its own)");
+  if (p.radial && v_phi)
+    return fail(CGTP_ERR_INVALID_ARG, "v_phi must be NULL with an in-kernel radial basis: the radial values' "
+                                      "direction follows from v_edge_vec and v_pos");
   if (!gg_x && !gg_pos && !gg_edge_vec && !gg_phi && !gg_A && !gg_grad_out) return ok();
   size_t need = 0;
   cgtp_status_t st = cgtp_workspace_size(plan, g, CGTP_OP_DOUBLE_BACKWARD, &need);
@@ -760,7 +765,8 @@ cgtp_status_t cgtp_conv_double_backward(cgtp_plan_t plan, cgtp_graph_t g, const 
     return fail(st, err);
   // A missing direction is read from a primal array of the same shape with a zero scale.
   const bool f64 = p.dtype == CGTP_F64;
-  double sxd = v_x ? 1.0 : 0.0, sphid = v_phi ? 1.0 : 0.0, sAd = v_A ? 1.0 : 0.0;
+  // With an in-kernel radial basis the radial tangent is computed (Gdot rows), never absent.
+  double sxd = v_x ? 1.0 : 0.0, sphid = (v_phi || p.radial) ? 1.0 : 0.0, sAd = v_A ? 1.0 : 0.0;
   float sxf = float(sxd), sphif = float(sphid), sAf = float(sAd);
   void* psx = f64 ? (void*)&sxd : (void*)&sxf;
   void* psphi = f64 ? (void*)&sphid : (void*)&sphif;

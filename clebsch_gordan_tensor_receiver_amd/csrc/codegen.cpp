@@ -115,23 +115,26 @@ std::string gref(const Plan& p, int pi, int t, const std::string& row, const std
 
 // Radial basis of |r| (plan.radial 1: Bessel with the p = 6 polynomial envelope, zero beyond the
 // cutoff; 2: Gaussians centred at k r_c / (K - 1) with width r_c / (K - 1)), with d/dr when df is
-// non-null.
+// non-null and d^2/dr^2 (the double backward's curvature term) when d2f is non-null.
 void emit_radial(Out& o, const Plan& p) {
   const int K = p.K;
-  o.open("DEV void radial_eval(real r, real* f, real* df)");
+  o.open("DEV void radial_eval(real r, real* f, real* df, real* d2f)");
   if (p.radial == 1) {
     o.line(F("const real rc = R(%.17g), d = r / rc;", p.r_cut));
-    o.line("const real d2 = d * d, d5 = d2 * d2 * d, d6 = d5 * d, d7 = d6 * d, d8 = d7 * d;");
+    o.line("const real d2 = d * d, d4 = d2 * d2, d5 = d4 * d, d6 = d5 * d, d7 = d6 * d, d8 = d7 * d;");
     o.line("const bool in = d < R(1);");
     o.line("const real u = in ? R(1) - R(28) * d6 + R(48) * d7 - R(21) * d8 : R(0);");
     o.line("const real du = in ? (R(-168) * d5 + R(336) * d6 - R(168) * d7) / rc : R(0);");
+    o.line("const real d2u = in ? (R(-840) * d4 + R(2016) * d5 - R(1176) * d6) / (rc * rc) : R(0);");
     o.line(F("const real nrm = R(%.17g), ir = R(1) / r;", std::sqrt(2.0 / p.r_cut)));
     o.open(F("for (int n = 0; n < %d; ++n)", K));
     o.line(F("const real a = R(n + 1) * R(%.17g);", M_PI / p.r_cut));
     o.line("const real sn = sin(a * r), cs = cos(a * r);");
-    o.line("const real b = nrm * sn * ir;");
+    o.line("const real b = nrm * sn * ir, db = nrm * (a * cs * r - sn) * ir * ir;");
     o.line("f[n] = b * u;");
-    o.line("if (df) df[n] = nrm * (a * cs * r - sn) * ir * ir * u + b * du;");
+    o.line("if (df) df[n] = db * u + b * du;");
+    o.line("if (d2f) d2f[n] = nrm * (R(2) * sn - R(2) * a * r * cs - a * a * r * r * sn) * ir * ir * ir * u"
+           " + R(2) * db * du + b * d2u;");
     o.close();
   } else {
     o.line(F("const real D = R(%.17g), inv2 = R(1) / (R(2) * D * D);", p.r_cut / (K - 1)));
@@ -139,6 +142,7 @@ void emit_radial(Out& o, const Plan& p) {
     o.line("const real t = r - R(k) * D, g = exp(-t * t * inv2);");
     o.line("f[k] = g;");
     o.line("if (df) df[k] = -t * R(2) * inv2 * g;");
+    o.line("if (d2f) d2f[k] = (R(4) * t * t * inv2 * inv2 - R(2) * inv2) * g;");
     o.close();
   }
   o.close();
@@ -257,7 +261,7 @@ void emit_prep(Out& o, const Plan& p, bool with_y) {
   std::vector<std::string> vals(size_t(p.g_stride), "R(0)");
   if (p.radial) {
     o.line(F("real fr[%d];", p.K));
-    o.line("radial_eval(rr, fr, nullptr);");
+    o.line("radial_eval(rr, fr, nullptr, nullptr);");
     for (int q = 0; q < p.K; ++q) vals[size_t(p.phi_off + q)] = F("fr[%d]", q);
   }
   for (const Path& P : p.paths) {
@@ -432,7 +436,7 @@ void emit_radial_term(Out& o, const Plan& p, const std::string& pb) {
     return;
   }
   o.line(F("real fr[%d], dfr[%d];", p.K, p.K));
-  o.line("radial_eval(rr, fr, dfr);");
+  o.line("radial_eval(rr, fr, dfr, nullptr);");
   std::string ex = F("%s0 * dfr[0]", pb.c_str());
   for (int q = 1; q < p.K; ++q) ex += F(" + %s%d * dfr[%d]", pb.c_str(), q, q);
   o.line("const real sr = " + ex + ";");

@@ -12,6 +12,9 @@
 //   dsrc       (lane = channel): x-bar-dot_j = sum_out-edges sum_pi wdot G^T mbar + w Gdot^T mbar;
 //   dedge_final(lane = edge):    e-bar-dot = J_Y^T Y-bar-dot + grad_r <J_Y(r) rdot, Y-bar> with the
 //                                curvature term from nested dual numbers.
+// With an in-kernel radial basis phi(|r|), phidot = phi'(|r|) (r-hat . rdot) sits in the Gdot row
+// beside phi in the G row, the receiver pass adds the first-order phi-bar columns, and the edge
+// finalisation adds the chain through phi and the curvature of phi to e-bar-dot.
 // A missing direction is read from its primal array with a zero scale, so every load stays in
 // bounds; rdot = v_edge_vec + v_pos[send] - v_pos[recv] (either part optional).
 #include <algorithm>
@@ -109,6 +112,18 @@ void emit_sh_contract(Out& o, int L, const std::string& S, const std::string& xs
   o.close();
 }
 
+// Pointers ph, phd to the current edge's K radial values and their tangent: the phi and v_phi
+// inputs, or (plans with an in-kernel radial basis) the edge's G and Gdot rows (g, gd in scope).
+void emit_phi_rows(Out& o, const Plan& p) {
+  if (p.radial) {
+    o.line(F("const real* __restrict__ ph = g + %d;", p.phi_off));
+    o.line(F("const real* __restrict__ phd = gd + %d;", p.phi_off));
+    return;
+  }
+  o.line(F("const real* __restrict__ ph = phi + (i64)e * %d;", p.K));
+  o.line(F("const real* __restrict__ phd = vphi + (i64)e * %d;", p.K));
+}
+
 // Effective edge-vector direction rdot of sorted edge e (ri, sj in scope) into vex, vey, vez.
 void emit_edge_direction(Out& o) {
   o.line("real vex = R(0), vey = R(0), vez = R(0);");
@@ -134,6 +149,14 @@ void emit_prep2(Out& o, const Plan& p) {
   o.line(F("D1 Y[%d];", p.sh_dim));
   o.line("sh_eval<D1>(D1(nx, dx), D1(ny, dy), D1(nz, dz), Y);");
   o.line(F("real* __restrict__ dst = G + (i64)(e - e0) * %d;", 2 * p.g_stride));
+  if (p.radial) {   // phi(|r|) in the G row, its tangent phi'(|r|) (r-hat . rdot) in the Gdot row
+    o.line(F("real fr[%d], dfr[%d];", p.K, p.K));
+    o.line("radial_eval(R(1) / inv, fr, dfr, nullptr);");
+    for (int q = 0; q < p.K; ++q) {
+      o.line(F("dst[%d] = fr[%d];", p.phi_off + q, q));
+      o.line(F("dst[%d] = dfr[%d] * nv;", p.g_stride + p.phi_off + q, q));
+    }
+  }
   for (const Path& P : p.paths) {
     int s = P.l2 * P.l2;
     int n = P.g_off;
@@ -180,8 +203,7 @@ void emit_dedge_loop(Out& o, const Plan& p, const std::vector<int>& blocks, cons
   o.line("const int j = col[e];");
   o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", 2 * p.g_stride));
   o.line(F("const real* __restrict__ gd = g + %d;", p.g_stride));
-  o.line(F("const real* __restrict__ ph = phi + (i64)e * %d;", p.K));
-  o.line(F("const real* __restrict__ phd = vphi + (i64)e * %d;", p.K));
+  emit_phi_rows(o, p);
   for (int q = 0; q < p.K; ++q)
     o.line(F("const real f%d = ok_ ? ph[%d] : R(0), fd%d = ok_ ? sphi * phd[%d] : R(0);", q, q, q, q));
   for (int b : blocks) {
@@ -277,6 +299,9 @@ void emit_drecv_task(Out& o, const Plan& p, int ti, const Task& T, int col_off, 
   // Columns: K phi-bar-dot partials, then Y-bar-dot and first-order Y-bar over the task's Y entries.
   auto cd = [&](int y) { return K + int(std::find(yc.begin(), yc.end(), y) - yc.begin()); };
   auto cw = [&](int y) { return cd(y) + ny; };
+  // With an in-kernel radial basis, K more columns: the first-order phi-bar (A h) of the task,
+  // for the curvature of phi(|r|) in the edge-vector gradient.
+  auto cb = [&](int q) { return K + 2 * ny + q; };
   // Blocks of at most 16 channels: 4 edges per wave step.  (Two edges per step for 32-channel
   // blocks measured slower: per-lane coefficient rows of G and G-dot cost the registers that the
   // wave-uniform rows keep in scalar ones.)
@@ -319,6 +344,7 @@ void emit_drecv_task(Out& o, const Plan& p, int ti, const Task& T, int col_off, 
       for (int q = 0; q < K; ++q, ++ai) {
         o.line(F("aa%d = fma(fd%d, h%d, fma(f%d, hd%d, aa%d));", ai, q, pi, q, pi, ai));
         o.line(F("v%d = fma(ad%d_%d, h%d, fma(a%d_%d, hd%d, v%d));", q, pi, q, pi, pi, q, pi, q));
+        if (p.radial) o.line(F("v%d = fma(a%d_%d, h%d, v%d);", cb(q), pi, q, pi, cb(q)));
       }
       const int d1 = 2 * P.l1 + 1;
       for (int m = 0; m < d1; ++m)
@@ -409,8 +435,7 @@ void emit_dsrc_task(Out& o, const Plan& p, int ti, const Task& T) {
     o.line("const int i = __builtin_amdgcn_readlane(il_, k_);");
     o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", 2 * p.g_stride));
     o.line(F("const real* __restrict__ gd = g + %d;", p.g_stride));
-    o.line(F("const real* __restrict__ ph = phi + (i64)e * %d;", K));
-    o.line(F("const real* __restrict__ phd = vphi + (i64)e * %d;", K));
+    emit_phi_rows(o, p);
     for (int q = 0; q < K; ++q) o.line(F("const real f%d = ph[%d], fd%d = sphi * phd[%d];", q, q, q, q));
     o.line(F("const real* __restrict__ gi = gout + (i64)i * %d + uc;", p.c_out));
     for (int ob : out_blocks_of(p, S)) {
@@ -481,12 +506,13 @@ void emit_dedge_final(Out& o, const Plan& p, const std::vector<Task>& tasks) {
     }
     return ex.empty() ? std::string("R(0)") : ex;
   };
-  o.open("if (gphi)");
   for (int q = 0; q < K; ++q) {
     std::string ex;
     for (size_t t = 0; t < tasks.size(); ++t) ex += (t ? " + " : "") + F("ROWV(%d)", off[t] + q);
-    o.line(F("gphi[(i64)e * %d + %d] = ", K, q) + ex + ";");
+    o.line(F("const real gp%d = ", q) + ex + ";");
   }
+  o.open("if (gphi)");
+  for (int q = 0; q < K; ++q) o.line(F("gphi[(i64)e * %d + %d] = gp%d;", K, q, q));
   o.close();
   o.line("if (!gev) return;");
   emit_edge_vector(o);
@@ -518,6 +544,27 @@ void emit_dedge_final(Out& o, const Plan& p, const std::vector<Task>& tasks) {
   o.line("gx += (-dx * np_ - nx * dp + (hx - nx * nh)) * inv - (wx - nx * np_) * nv * inv * inv;");
   o.line("gy += (-dy * np_ - ny * dp + (hy - ny * nh)) * inv - (wy - ny * np_) * nv * inv * inv;");
   o.line("gz += (-dz * np_ - nz * dp + (hz - nz * nh)) * inv - (wz - nz * np_) * nv * inv * inv;");
+  if (p.radial) {
+    // Through phi(|r|): the chain J_phi^T phi-bar-dot = (sum gp phi') r-hat, and the curvature
+    // grad_r [s (r-hat . rdot)] = s' t r-hat + s (rdot - t r-hat) / |r| with s = sum phi-bar phi',
+    // s' = sum phi-bar phi'', t = r-hat . rdot.
+    for (int q = 0; q < K; ++q) {
+      std::string ex;
+      for (size_t t = 0; t < tasks.size(); ++t)
+        ex += (t ? " + " : "") + F("ROWV(%d)", off[t] + K + 2 * int(yc[t].size()) + q);
+      o.line(F("const real pb%d = ", q) + ex + ";");
+    }
+    o.line(F("real fr[%d], dfr[%d], d2fr[%d];", K, K, K));
+    o.line("radial_eval(R(1) / inv, fr, dfr, d2fr);");
+    o.line("real sc = R(0), s1 = R(0), s2 = R(0);");
+    for (int q = 0; q < K; ++q) {
+      o.line(F("sc = fma(gp%d, dfr[%d], sc);", q, q));
+      o.line(F("s1 = fma(pb%d, dfr[%d], s1);", q, q));
+      o.line(F("s2 = fma(pb%d, d2fr[%d], s2);", q, q));
+    }
+    o.line("const real cn = sc + (s2 - s1 * inv) * nv, cv = s1 * inv;");
+    o.line("gx += cn * nx + cv * vex; gy += cn * ny + cv * vey; gz += cn * nz + cv * vez;");
+  }
   o.line("gev[3 * (i64)e] = gx; gev[3 * (i64)e + 1] = gy; gev[3 * (i64)e + 2] = gz;");
   o.line("#undef ROWV");
   o.close();
@@ -526,7 +573,7 @@ void emit_dedge_final(Out& o, const Plan& p, const std::vector<Task>& tasks) {
 }  // namespace
 
 int dbl_task_width(const Plan& p, const Task& T) {
-  return (p.K + 2 * int(recv_task_ycols(p, T).size()) + 3) / 4 * 4;
+  return ((p.radial ? 2 : 1) * p.K + 2 * int(recv_task_ycols(p, T).size()) + 3) / 4 * 4;
 }
 
 int dbl_partial_row(const Plan& p) { return task_tables(p).dbl_row; }

@@ -722,7 +722,7 @@ void emit_prep_src(Out& o, const Plan& p) {
   o.line(F("real* __restrict__ dst = G + (i64)(k - k0) * %d;", p.g_stride));
   if (p.radial) {
     o.line(F("real fr[%d];", p.K));
-    o.line("radial_eval(rr, fr, nullptr);");
+    o.line("radial_eval(rr, fr, nullptr, nullptr);");
     for (int q = 0; q < p.K; ++q) o.line(F("dst[%d] = fr[%d];", p.phi_off + q, q));
   }
   for (const Path& P : p.paths) {

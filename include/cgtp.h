@@ -145,9 +145,11 @@ cgtp_status_t cgtp_plan_set_scratch_budget(cgtp_plan_t plan, size_t bytes);
  * With kind 1 or 2 the convolution calls take phi = NULL; no E x K tensor is read, the values
  * live in the per-chunk workspace rows; cgtp_conv_backward's grad_pos and grad_edge_vec include
  * the chain rule through phi(r) and grad_phi (optional) is the gradient with respect to the
- * computed values.  Call before the plan compiles kernels (UNSUPPORTED afterwards).  The double
- * backward keeps phi as an input (UNSUPPORTED with a radial kind).  INVALID_ARG for an unknown
- * kind, r_cut <= 0, or kind 2 with K < 2. */
+ * computed values.  cgtp_conv_double_backward takes phi = NULL and v_phi = NULL: the radial
+ * direction is phi'(|r|) (r-hat . v_r) and its gg_edge_vec / gg_pos include the chain through
+ * phi(r) and the basis' second derivative; the triple backward keeps phi as an input
+ * (UNSUPPORTED with a radial kind).  Call before the plan compiles kernels (UNSUPPORTED
+ * afterwards).  INVALID_ARG for an unknown kind, r_cut <= 0, or kind 2 with K < 2. */
 cgtp_status_t cgtp_plan_set_radial(cgtp_plan_t plan, int kind, double r_cut);
 
 /* ---------------------------------------------------------------- graphs */
@@ -279,7 +281,11 @@ cgtp_status_t cgtp_conv_backward_with_state(cgtp_plan_t plan, cgtp_graph_t g, co
  * gg_pos (N x 3, out-edge minus in-edge sums of gg_edge_vec), gg_edge_vec (E x 3), gg_phi
  * (E x K), gg_A (K x N_w) and gg_grad_out (N x C_out, the derivative with respect to grad_out,
  * which is the tangent of the forward output).  Fixed-order reductions: bitwise repeatable.
- * UNSUPPORTED for the fully connected mode. */
+ * With an in-kernel radial basis (cgtp_plan_set_radial) phi and v_phi are NULL (INVALID_ARG
+ * otherwise), the map differentiated is (x, r, A, grad_out) -> (grad_x, grad_edge_vec, grad_A)
+ * with grad_edge_vec through phi(|r|) as in cgtp_conv_backward, and gg_phi (optional) is the
+ * gradient with respect to the computed radial values.  UNSUPPORTED for the fully connected
+ * mode. */
 cgtp_status_t cgtp_conv_double_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x, const void* pos,
                                         const void* shift, const void* phi, const void* A,
                                         const void* grad_out, const void* v_x, const void* v_pos,

@@ -182,8 +182,11 @@ def test_host_validation_before_any_device_work(lib):
     rad = lib.Plan("8x0e+8x1o", "1x0e+1x1o", "8x0e+8x1o", "uvu", "float64", 4)
     assert so.cgtp_plan_set_radial(rad.handle, 2, 3.0) == 0
     assert so.cgtp_conv_forward(rad.handle, g.handle, 0, 1, 1, None, 1, 1, 1, None, 0, None) == INVALID_ARG
+    # The double backward of a radial plan takes neither phi nor a phi direction.
     assert so.cgtp_conv_double_backward(rad.handle, g.handle, 1, 1, None, 1, 1, 1, *[None] * 12, 0,
-                                        None) == UNSUPPORTED
+                                        None) == INVALID_ARG
+    assert so.cgtp_conv_double_backward(rad.handle, g.handle, 1, 1, None, None, 1, 1, None, None, None, 1,
+                                        *[None] * 8, 0, None) == INVALID_ARG
     assert so.cgtp_plan_path(plan.handle, 99, (ctypes.c_int32 * 9)()) == INVALID_ARG
     assert so.cgtp_error_string(WORKSPACE) == b"workspace too small"
     # Kept state: channelwise plans keep E rows of whole 16-byte units; fully connected ones N x state

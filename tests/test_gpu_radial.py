@@ -114,3 +114,51 @@ def test_fused_radial_with_kept_state():
     assert torch.equal(out, out_k)
     for k in KEYS:
         assert torch.equal(grads[k], grads_k[k]), k
+
+
+NARROW16 = dict(irreps_in="16x0e+16x1o+16x2e", irreps_sh="1x0e+1x1o+1x2e+1x3o",
+                irreps_out="16x0e+16x1o+16x2e+16x3o")
+
+
+@pytest.mark.parametrize("kind,ov,dtype", [
+    (1, None, "float64"),
+    (2, SMALL_L3, "float32"),
+    (1, NARROW16, "float32"),
+    (2, None, "float64"),
+])
+def test_fused_radial_double_backward(kind, ov, dtype):
+    """Double backward with phi computed from |r| in the kernels: every output against the oracle
+    (phi-input double backward with phidot = phi'(|r|) r-hat.v, plus the chain through phi and
+    the curvature of the basis on the edge vector)."""
+    from tests.gpu_helpers import GpuCase, TOL, rel_err
+    from tests.oracle_helpers import effective_edge_direction, make_directions
+    case = make_case(1, irreps_override=ov, dtype=dtype)
+    rc = case.raw.spec["rc"]
+    dirs = make_directions(case)
+    dirs.pop("v_phi")
+    g = GpuCase(case)
+    g.plan.set_radial(kind, rc)
+    dt = torch.float64 if dtype == "float64" else torch.float32
+    dev = {k: torch.tensor(v, dtype=dt, device="cuda").contiguous() for k, v in dirs.items()}
+    got = g.conv.double_backward(g.x, g.pos, g.shift, None, g.A, g.grad_out, **dev)
+    v_e = effective_edge_direction(case, dirs["v_edge_vec"], dirs["v_pos"])
+    ref = radial.double_backward(kind, rc, case.problem, case.x, case.edge_vec, case.recv, case.send, case.A,
+                                 case.grad_out, v_x=dirs["v_x"], v_e=v_e, v_A=dirs["v_A"], n_nodes=case.n_nodes)
+    for k in ("x", "pos", "edge_vec", "phi", "A", "grad_out"):
+        err = rel_err(got[k].cpu().numpy()[:len(ref[k])], ref[k].numpy())
+        print(f"radial kind {kind} {dtype} double backward {k}: rel err {err:.3e}", flush=True)
+        assert err <= TOL[dtype], k
+
+
+def test_fused_radial_double_backward_argument_rules():
+    from clebsch_gordan_tensor_receiver_amd import _lib
+    from tests.gpu_helpers import GpuCase
+    case = make_case(1)
+    g = GpuCase(case)
+    g.plan.set_radial(1, case.raw.spec["rc"])
+    with pytest.raises(_lib.CgtpError) as e:   # phi must be NULL
+        g.conv.double_backward(g.x, g.pos, g.shift, g.phi, g.A, g.grad_out)
+    assert e.value.status == 1
+    with pytest.raises(_lib.CgtpError) as e:   # and so must v_phi
+        g.conv.double_backward(g.x, g.pos, g.shift, None, g.A, g.grad_out, v_phi=g.phi)
+    assert e.value.status == 1
