@@ -362,10 +362,13 @@ cgtp_status_t cgtp_plan_compile(cgtp_plan_t plan, int ops) {
       if (st != CGTP_OK) return fail(st, err);
     }
   } else {
-    if (ops & ((1 << CGTP_OP_DOUBLE_BACKWARD) | (1 << CGTP_OP_TRIPLE_BACKWARD)))
-      return fail(CGTP_ERR_UNSUPPORTED, "the double and triple backward are channelwise only");
+    if (ops & (1 << CGTP_OP_TRIPLE_BACKWARD))
+      return fail(CGTP_ERR_UNSUPPORTED, "the triple backward is channelwise only");
+    if ((ops & (1 << CGTP_OP_DOUBLE_BACKWARD)) && plan->p.radial)
+      return fail(CGTP_ERR_UNSUPPORTED, "the fully connected double backward takes phi as an input");
     if (ops & (1 << CGTP_OP_FORWARD)) fams.push_back("uvw_fwd");
     if (ops & (1 << CGTP_OP_BACKWARD)) fams.push_back("uvw_bwd");
+    if (ops & (1 << CGTP_OP_DOUBLE_BACKWARD)) fams.push_back("uvw_dbl");
   }
   if (ops & (1 << CGTP_OP_FORWARD)) fams.push_back("layout");  // boundary layout conversion
   for (auto& f : fams) {
@@ -447,8 +450,9 @@ cgtp_status_t cgtp_workspace_size(cgtp_plan_t plan, cgtp_graph_t g, cgtp_op_t op
   const cgtp::Graph& G = g->g;
   size_t need = 0;
   if (p.mode == CGTP_FULLY_CONNECTED) {
-    if (op == CGTP_OP_DOUBLE_BACKWARD || op == CGTP_OP_TRIPLE_BACKWARD)
-      return fail(CGTP_ERR_UNSUPPORTED, "the double and triple backward are channelwise only");
+    if (op == CGTP_OP_TRIPLE_BACKWARD) return fail(CGTP_ERR_UNSUPPORTED, "the triple backward is channelwise only");
+    if (op == CGTP_OP_DOUBLE_BACKWARD && p.radial)
+      return fail(CGTP_ERR_UNSUPPORTED, "the fully connected double backward takes phi as an input");
     *bytes = std::max<size_t>(cgtp::uvw_workspace(p, G, op), 256);
     return ok();
   }
@@ -733,7 +737,8 @@ cgtp_status_t cgtp_conv_double_backward(cgtp_plan_t plan, cgtp_graph_t g, const 
   if (!x || !pos || !A || !grad_out) return fail(CGTP_ERR_INVALID_ARG, "null input tensor");
   cgtp::Plan& p = plan->p;
   cgtp::Graph& G = g->g;
-  if (p.mode != CGTP_CHANNELWISE) return fail(CGTP_ERR_UNSUPPORTED, "double backward is channelwise only");
+  if (p.mode != CGTP_CHANNELWISE && p.radial)
+    return fail(CGTP_ERR_UNSUPPORTED, "the fully connected double backward takes phi as an input");
   if ((phi == nullptr) != (p.radial != 0))
     return fail(CGTP_ERR_INVALID_ARG, p.radial ? "phi must be NULL: the plan computes the radial basis"
                                                : "null phi (the plan has no radial basis of its own)");
@@ -749,6 +754,11 @@ cgtp_status_t cgtp_conv_double_backward(cgtp_plan_t plan, cgtp_graph_t g, const 
   cgtp::DeviceGraph d;
   if ((st = cgtp::device_graph(G, &d, &err)) != CGTP_OK) return fail(st, err);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.mode == CGTP_FULLY_CONNECTED) {
+    st = cgtp::uvw_double_backward(p, G, d, x, pos, shift, phi, A, grad_out, v_x, v_pos, v_edge_vec, v_phi, v_A, gg_x,
+                                   gg_pos, gg_edge_vec, gg_phi, gg_A, gg_grad_out, workspace, s, &err);
+    return st == CGTP_OK ? ok() : fail(st, err);
+  }
   if (gg_x && (st = zero_unreached(p, gg_x, G.n, false, s, &err)) != CGTP_OK) return fail(st, err);
   if (gg_grad_out && (st = zero_unreached(p, gg_grad_out, G.n, true, s, &err)) != CGTP_OK) return fail(st, err);
   BwdLayout L = dbl_layout(p, G);

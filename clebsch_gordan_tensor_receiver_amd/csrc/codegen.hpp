@@ -98,6 +98,9 @@ void emit_swaps(Out& o, const std::vector<std::pair<std::string, std::string>>& 
 void emit_edge_final(Out& o, const Plan& p, int ntask, int V);
 void emit_recv_edge_final(Out& o, const Plan& p, const std::vector<Task>& tasks);
 void emit_small_kernels(Out& o);
+// Gdot-row preps and the edge finalisation of the fully connected double backward (ntask edge
+// tasks of V partial columns each).
+void emit_uvw_dbl_kernels(Out& o, const Plan& p, int ntask, int V);
 void emit_check_edges(Out& o);
 
 }  // namespace gen

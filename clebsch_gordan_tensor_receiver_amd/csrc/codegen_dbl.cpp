@@ -477,6 +477,64 @@ void emit_dsrc_task(Out& o, const Plan& p, int ti, const Task& T) {
   o.close();
 }
 
+// e-bar-dot of edge e (lane = edge) from Y-bar-dot ybd[] and the first-order Y-bar ybw[], which
+// `fill` assigns: J_Y^T ybd + grad_r <J_Y(r) rdot, ybw>, into gx, gy, gz.  Also leaves in scope
+// the unit vector nx, ny, nz, inv = 1 / |r|, the direction rdot (vex, vey, vez) and nv = n . rdot.
+void emit_ebar_dot(Out& o, const Plan& p, const std::function<void()>& fill) {
+  const int Yd = p.sh_dim;
+  emit_edge_vector(o);
+  emit_edge_direction(o);
+  o.line("const real inv = R(1) / sqrt(rx * rx + ry * ry + rz * rz);");
+  o.line("const real nx = rx * inv, ny = ry * inv, nz = rz * inv;");
+  o.line("const real nv = nx * vex + ny * vey + nz * vez;");
+  o.line("const real dx = (vex - nx * nv) * inv, dy = (vey - ny * nv) * inv, dz = (vez - nz * nv) * inv;");
+  o.line(F("real ybd[%d], ybw[%d];", Yd, Yd));
+  fill();
+  o.line("DD accw(R(0));");
+  o.line("DD accd(R(0));");
+  emit_sh_contract(o, p.lmax, "DD", "DD(D3(nx, R(1), R(0), R(0)), D3(dx, R(0), R(0), R(0)))",
+                   "DD(D3(ny, R(0), R(1), R(0)), D3(dy, R(0), R(0), R(0)))",
+                   "DD(D3(nz, R(0), R(0), R(1)), D3(dz, R(0), R(0), R(0)))",
+                   {{"accw", [](int i) { return F("ybw[%d]", i); }}, {"accd", [](int i) { return F("ybd[%d]", i); }}});
+  // J^T Ybar_d = Pi p_d / rho with p_d the gradient of sum Ybar_d P at n.
+  o.line("real px = accd.a.x, py = accd.a.y, pz = accd.a.z;");
+  o.line("real pn = nx * px + ny * py + nz * pz;");
+  o.line("real gx = (px - nx * pn) * inv, gy = (py - ny * pn) * inv, gz = (pz - nz * pn) * inv;");
+  // Curvature: H v = [-dn (n.p) - n (dn.p) + Pi (H_P dn)] / rho - Pi p (n.v) / rho^2, p, H_P dn of sum Ybar_w P.
+  o.line("const real wx = accw.a.x, wy = accw.a.y, wz = accw.a.z;");
+  o.line("const real hx = accw.b.x, hy = accw.b.y, hz = accw.b.z;");
+  o.line("const real np_ = nx * wx + ny * wy + nz * wz, dp = dx * wx + dy * wy + dz * wz;");
+  o.line("const real nh = nx * hx + ny * hy + nz * hz;");
+  o.line("gx += (-dx * np_ - nx * dp + (hx - nx * nh)) * inv - (wx - nx * np_) * nv * inv * inv;");
+  o.line("gy += (-dy * np_ - ny * dp + (hy - ny * nh)) * inv - (wy - ny * np_) * nv * inv * inv;");
+  o.line("gz += (-dz * np_ - nz * dp + (hz - nz * nh)) * inv - (wz - nz * np_) * nv * inv * inv;");
+}
+
+// Gdot row (G's layout) of the current edge e into dst: the directional derivative of G along
+// rdot, from a dual-number pass of the harmonics.
+void emit_gdot_row(Out& o, const Plan& p) {
+  emit_edge_vector(o);
+  emit_edge_direction(o);
+  o.line("const real inv = R(1) / sqrt(rx * rx + ry * ry + rz * rz);");
+  o.line("const real nx = rx * inv, ny = ry * inv, nz = rz * inv;");
+  o.line("const real nv = nx * vex + ny * vey + nz * vez;");
+  o.line("const real dx = (vex - nx * nv) * inv, dy = (vey - ny * nv) * inv, dz = (vez - nz * nv) * inv;");
+  o.line(F("D1 Y[%d];", p.sh_dim));
+  o.line("sh_eval<D1>(D1(nx, dx), D1(ny, dy), D1(nz, dz), Y);");
+  for (const Path& P : p.paths) {
+    int s = P.l2 * P.l2;
+    int n = P.g_off;
+    for (const GPair& gp : P.gpairs) {
+      std::string ed;
+      for (auto& t : gp.terms) {
+        if (!ed.empty()) ed += " + ";
+        ed += lit(t.second) + " * Y[" + std::to_string(s + t.first) + "].d";
+      }
+      o.line(F("dst[%d] = ", n++) + ed + ";");
+    }
+  }
+}
+
 // Edge finalisation: phi-bar-dot sums, e-bar-dot = J^T Ybar_d + the curvature term.
 void emit_dedge_final(Out& o, const Plan& p, const std::vector<Task>& tasks) {
   const int K = p.K, Yd = p.sh_dim, row = dbl_partial_row(p);
@@ -515,35 +573,12 @@ void emit_dedge_final(Out& o, const Plan& p, const std::vector<Task>& tasks) {
   for (int q = 0; q < K; ++q) o.line(F("gphi[(i64)e * %d + %d] = gp%d;", K, q, q));
   o.close();
   o.line("if (!gev) return;");
-  emit_edge_vector(o);
-  emit_edge_direction(o);
-  o.line("const real inv = R(1) / sqrt(rx * rx + ry * ry + rz * rz);");
-  o.line("const real nx = rx * inv, ny = ry * inv, nz = rz * inv;");
-  o.line("const real nv = nx * vex + ny * vey + nz * vez;");
-  o.line("const real dx = (vex - nx * nv) * inv, dy = (vey - ny * nv) * inv, dz = (vez - nz * nv) * inv;");
-  o.line(F("real ybd[%d], ybw[%d];", Yd, Yd));
-  for (int m = 0; m < Yd; ++m) {
-    o.line(F("ybd[%d] = ", m) + sum_y(m, 0) + ";");
-    o.line(F("ybw[%d] = ", m) + sum_y(m, 1) + ";");
-  }
-  o.line("DD accw(R(0));");
-  o.line("DD accd(R(0));");
-  emit_sh_contract(o, p.lmax, "DD", "DD(D3(nx, R(1), R(0), R(0)), D3(dx, R(0), R(0), R(0)))",
-                   "DD(D3(ny, R(0), R(1), R(0)), D3(dy, R(0), R(0), R(0)))",
-                   "DD(D3(nz, R(0), R(0), R(1)), D3(dz, R(0), R(0), R(0)))",
-                   {{"accw", [](int i) { return F("ybw[%d]", i); }}, {"accd", [](int i) { return F("ybd[%d]", i); }}});
-  // J^T Ybar_d = Pi p_d / rho with p_d the gradient of sum Ybar_d P at n.
-  o.line("real px = accd.a.x, py = accd.a.y, pz = accd.a.z;");
-  o.line("real pn = nx * px + ny * py + nz * pz;");
-  o.line("real gx = (px - nx * pn) * inv, gy = (py - ny * pn) * inv, gz = (pz - nz * pn) * inv;");
-  // Curvature: H v = [-dn (n.p) - n (dn.p) + Pi (H_P dn)] / rho - Pi p (n.v) / rho^2, p, H_P dn of sum Ybar_w P.
-  o.line("const real wx = accw.a.x, wy = accw.a.y, wz = accw.a.z;");
-  o.line("const real hx = accw.b.x, hy = accw.b.y, hz = accw.b.z;");
-  o.line("const real np_ = nx * wx + ny * wy + nz * wz, dp = dx * wx + dy * wy + dz * wz;");
-  o.line("const real nh = nx * hx + ny * hy + nz * hz;");
-  o.line("gx += (-dx * np_ - nx * dp + (hx - nx * nh)) * inv - (wx - nx * np_) * nv * inv * inv;");
-  o.line("gy += (-dy * np_ - ny * dp + (hy - ny * nh)) * inv - (wy - ny * np_) * nv * inv * inv;");
-  o.line("gz += (-dz * np_ - nz * dp + (hz - nz * nh)) * inv - (wz - nz * np_) * nv * inv * inv;");
+  emit_ebar_dot(o, p, [&] {
+    for (int m = 0; m < Yd; ++m) {
+      o.line(F("ybd[%d] = ", m) + sum_y(m, 0) + ";");
+      o.line(F("ybw[%d] = ", m) + sum_y(m, 1) + ";");
+    }
+  });
   if (p.radial) {
     // Through phi(|r|): the chain J_phi^T phi-bar-dot = (sum gp phi') r-hat, and the curvature
     // grad_r [s (r-hat . rdot)] = s' t r-hat + s (rdot - t r-hat) / |r| with s = sum phi-bar phi',
@@ -653,5 +688,78 @@ std::string generate_dbl_source(const Plan& p, std::string* err) {
   emit_small_kernels(o);
   return o.s.str();
 }
+
+namespace gen {
+
+// Kernels of the fully connected double backward beyond the first-order passes it reuses:
+//   cgtp_prep_dot / cgtp_prep_src_dot: Gdot rows of the edges of a receiver chunk (receiver
+//     order) or of a sender chunk (source-CSR order), the tangent of G along rdot;
+//   cgtp_uvw_dedge_final: phi-bar-dot and e-bar-dot of each edge from the partial columns of up
+//     to three edge passes (their sums are phi-bar-dot and Y-bar-dot) and of the first-order pass
+//     (Y-bar, for the curvature term); each buffer holds ntask tasks of V columns, K phi-bar
+//     columns then sh_dim Y-bar columns, column c of edge e at c eps + (e - e0).
+void emit_uvw_dbl_kernels(Out& o, const Plan& p, int ntask, int V) {
+  const int K = p.K, Yd = p.sh_dim;
+  dual_types(o);
+  o.line("extern \"C\" __global__ void __launch_bounds__(64)");
+  o.open("cgtp_prep_dot(const real* __restrict__ pos, const real* __restrict__ shift, const int* __restrict__ recv,"
+         " const int* __restrict__ send, const real* __restrict__ vev, const real* __restrict__ vpos, int e0,"
+         " int e1, real* __restrict__ Gd)");
+  o.line("const int e = e0 + (int)(blockIdx.x * 64 + threadIdx.x);");
+  o.line("if (e >= e1) return;");
+  o.line(F("real* __restrict__ dst = Gd + (i64)(e - e0) * %d;", p.g_stride));
+  emit_gdot_row(o, p);
+  o.close();
+  o.line("extern \"C\" __global__ void __launch_bounds__(64)");
+  o.open("cgtp_prep_src_dot(const real* __restrict__ pos, const real* __restrict__ shift,"
+         " const int* __restrict__ recv, const int* __restrict__ send, const int* __restrict__ src_edge,"
+         " const real* __restrict__ vev, const real* __restrict__ vpos, int k0, int k1, real* __restrict__ Gd)");
+  o.line("const int k = k0 + (int)(blockIdx.x * 64 + threadIdx.x);");
+  o.line("if (k >= k1) return;");
+  o.line("const int e = src_edge[k];");
+  o.line(F("real* __restrict__ dst = Gd + (i64)(k - k0) * %d;", p.g_stride));
+  emit_gdot_row(o, p);
+  o.close();
+  o.line("extern \"C\" __global__ void __launch_bounds__(64)");
+  o.open("cgtp_uvw_dedge_final(const real* __restrict__ pos, const real* __restrict__ shift,"
+         " const int* __restrict__ recv, const int* __restrict__ send, const real* __restrict__ vev,"
+         " const real* __restrict__ vpos, const real* __restrict__ epa, const real* __restrict__ epb,"
+         " const real* __restrict__ epc, const real* __restrict__ epw, int e0, int e1, int eps,"
+         " real* __restrict__ gphi, real* __restrict__ gev)");
+  o.line("const int e = e0 + (int)(blockIdx.x * 64 + threadIdx.x);");
+  o.line("if (e >= e1) return;");
+  o.line("const i64 el_ = e - e0;");
+  // Column c summed over the tasks of buffer P.
+  auto col_sum = [&](const char* P, int c) {
+    std::string ex;
+    for (int t = 0; t < ntask; ++t) ex += (t ? " + " : "") + F("%s[(i64)%d * eps + el_]", P, t * V + c);
+    return ex;
+  };
+  for (int q = 0; q < K; ++q) o.line(F("real gp%d = R(0);", q));
+  for (const char* P : {"epa", "epb", "epc"}) {
+    o.open(F("if (%s)", P));
+    for (int q = 0; q < K; ++q) o.line(F("gp%d += ", q) + col_sum(P, q) + ";");
+    o.close();
+  }
+  o.open("if (gphi)");
+  for (int q = 0; q < K; ++q) o.line(F("gphi[(i64)e * %d + %d] = gp%d;", K, q, q));
+  o.close();
+  o.line("if (!gev) return;");
+  emit_ebar_dot(o, p, [&] {
+    for (int m = 0; m < Yd; ++m) o.line(F("ybd[%d] = R(0); ybw[%d] = R(0);", m, m));
+    for (const char* P : {"epa", "epb", "epc"}) {
+      o.open(F("if (%s)", P));
+      for (int m = 0; m < Yd; ++m) o.line(F("ybd[%d] += ", m) + col_sum(P, K + m) + ";");
+      o.close();
+    }
+    o.open("if (epw)");
+    for (int m = 0; m < Yd; ++m) o.line(F("ybw[%d] = ", m) + col_sum("epw", K + m) + ";");
+    o.close();
+  });
+  o.line("gev[3 * (i64)e] = gx; gev[3 * (i64)e + 1] = gy; gev[3 * (i64)e + 2] = gz;");
+  o.close();
+}
+
+}  // namespace gen
 
 }  // namespace cgtp

@@ -777,11 +777,13 @@ UvwLayout uvw_layout(const Plan& p) {
 }
 
 std::string generate_uvw_source(const Plan& p, const std::string& family, std::string* err) {
-  if (family != "uvw_fwd" && family != "uvw_bwd") {
+  if (family != "uvw_fwd" && family != "uvw_bwd" && family != "uvw_dbl") {
     *err = "the fully connected mode supports the streamed schedule only (family " + family + ")";
     return "";
   }
-  const bool bwd = family == "uvw_bwd";
+  // uvw_dbl: the backward's kernels, the forward GEMMs and the double backward's own kernels.
+  const bool dbl = family == "uvw_dbl";
+  const bool bwd = family != "uvw_fwd";
   Out o;
   prelude(o, p, bwd, bwd);
   uvw_prelude_extra(o, p);
@@ -797,7 +799,7 @@ std::string generate_uvw_source(const Plan& p, const std::string& family, std::s
   for (auto& s : rs) {
     emit_brow(o, p, s, F("brow%d", s.blk));
   }
-  if (!bwd) {
+  if (!bwd || dbl) {
     for (size_t gi = 0; gi < rs.size(); ++gi) {
       const Side& s = rs[gi];
       const Block& OB = p.out[s.blk];
@@ -818,7 +820,7 @@ std::string generate_uvw_source(const Plan& p, const std::string& family, std::s
       g.store = F("out[(i64)(i0 + r / %d) * %d + %d + (r %% %d) * %d + c] = v;", s.d, p.c_out, OB.offset, s.d, OB.mul);
       emit_gemm_reduce(o, g, "real* __restrict__ out, int i0");
     }
-    return o.s.str();
+    if (!bwd) return o.s.str();
   }
   // ---- backward
   for (size_t gi = 0; gi < rs.size(); ++gi) {
@@ -902,6 +904,7 @@ std::string generate_uvw_source(const Plan& p, const std::string& family, std::s
     g.store = F("gx[(i64)(j0 + r / %d) * %d + %d + (r %% %d) * %d + c] = v;", s.d, p.c_in, IB.offset, s.d, IB.mul);
     emit_gemm_reduce(o, g, "real* __restrict__ gx, int j0");
   }
+  if (dbl) emit_uvw_dbl_kernels(o, p, int(st.size()), V);
   return o.s.str();
 }
 

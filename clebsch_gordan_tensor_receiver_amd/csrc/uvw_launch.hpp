@@ -25,4 +25,12 @@ cgtp_status_t uvw_backward(Plan& p, Graph& G, const DeviceGraph& d, const void* 
                            void* grad_x, void* grad_pos, void* grad_edge_vec, void* grad_phi, void* grad_A,
                            void* workspace, hipStream_t s, std::string* err, const void* state = nullptr);
 
+// Double backward (Sobek section 3.3 and Eqs. 37-39) by linearity: every second-order output is a
+// sum of first-order passes with one operand replaced by its direction.  Directions nullable.
+cgtp_status_t uvw_double_backward(Plan& p, Graph& G, const DeviceGraph& d, const void* x, const void* pos,
+                                  const void* shift, const void* phi, const void* A, const void* gout,
+                                  const void* v_x, const void* v_pos, const void* v_edge_vec, const void* v_phi,
+                                  const void* v_A, void* gg_x, void* gg_pos, void* gg_edge_vec, void* gg_phi,
+                                  void* gg_A, void* gg_grad_out, void* workspace, hipStream_t s, std::string* err);
+
 }  // namespace cgtp

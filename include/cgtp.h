@@ -194,7 +194,9 @@ cgtp_status_t cgtp_graph_destroy(cgtp_graph_t g);
  * rows, edge partials and grad_A partial slots of one receiver chunk) plus E x 3 edge-vector
  * values and 2 N int32 source-CSR bounds; never O(E x N_w).  A graph whose rows do not fit is
  * processed in receiver chunks; the receivers per chunk are also capped so that the grad_A
- * partial slots stay inside the budget at low in-degree. */
+ * partial slots stay inside the budget at low in-degree.  The fully connected double backward
+ * adds E x K values (a zero phi direction when v_phi is NULL).  UNSUPPORTED for the triple
+ * backward of a fully connected plan. */
 cgtp_status_t cgtp_workspace_size(cgtp_plan_t plan, cgtp_graph_t g, cgtp_op_t op, size_t* bytes);
 
 /* Forward.  x: N x C_in; pos: N x 3; shift: E x 3 receiver-sorted image shifts added to
@@ -269,7 +271,7 @@ cgtp_status_t cgtp_conv_backward_with_state(cgtp_plan_t plan, cgtp_graph_t g, co
                                             void* grad_x, void* grad_pos, void* grad_edge_vec, void* grad_phi,
                                             void* grad_A, void* workspace, size_t ws_bytes, void* stream);
 
-/* Double backward (channelwise mode only): the vector-Jacobian product of the backward map
+/* Double backward: the vector-Jacobian product of the backward map
  * (x, r, phi, A, grad_out) -> (grad_x, grad_edge_vec, grad_phi, grad_A) along the cotangent
  * directions (v_x, v_edge, v_phi, v_A), i.e. the gradient of
  *   <v_x, grad_x> + <v_edge, grad_edge_vec> + <v_phi, grad_phi> + <v_A, grad_A>
@@ -284,8 +286,10 @@ cgtp_status_t cgtp_conv_backward_with_state(cgtp_plan_t plan, cgtp_graph_t g, co
  * With an in-kernel radial basis (cgtp_plan_set_radial) phi and v_phi are NULL (INVALID_ARG
  * otherwise), the map differentiated is (x, r, A, grad_out) -> (grad_x, grad_edge_vec, grad_A)
  * with grad_edge_vec through phi(|r|) as in cgtp_conv_backward, and gg_phi (optional) is the
- * gradient with respect to the computed radial values.  UNSUPPORTED for the fully connected
- * mode. */
+ * gradient with respect to the computed radial values.  Fully connected mode: evaluated by
+ * linearity from the streamed first-order passes (Sobek Eqs. 37-39: m-dot = S-dot A + S A-dot,
+ * Sbar-dot = mbar A-dot^T, A-bar-dot = S-dot^T mbar, and the edge and source passes with one
+ * operand replaced by its direction), with phi as an input (UNSUPPORTED with a radial kind). */
 cgtp_status_t cgtp_conv_double_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x, const void* pos,
                                         const void* shift, const void* phi, const void* A,
                                         const void* grad_out, const void* v_x, const void* v_pos,

@@ -76,14 +76,14 @@ int main() {
       for (int op = 0; op < 4; ++op) {
         size_t bytes = 0;
         cgtp_status_t st = cgtp_workspace_size(plan, g, cgtp_op_t(op), &bytes);
-        const bool refused = pr.mode == CGTP_FULLY_CONNECTED && op >= 2;
+        const bool refused = pr.mode == CGTP_FULLY_CONNECTED && op == 3;
         expect(refused ? st == CGTP_ERR_UNSUPPORTED : (st == CGTP_OK && bytes >= 256), "workspace_size");
       }
       size_t sb = 0;
       cgtp_status_t st = cgtp_state_size(plan, g, &sb);
       expect(st == CGTP_OK || st == CGTP_ERR_UNSUPPORTED, "state_size");
       expect(cgtp_plan_set_scratch_budget(plan, 64 << 10) == CGTP_OK, "set_scratch_budget");
-      for (int op = 0; op < 2; ++op) {
+      for (int op = 0; op < 3; ++op) {
         size_t bytes = 0;
         expect(cgtp_workspace_size(plan, g, cgtp_op_t(op), &bytes) == CGTP_OK, "chunked workspace_size");
       }

@@ -158,14 +158,17 @@ def test_host_validation_before_any_device_work(lib):
     g = lib.Graph(3, np.array([0, 1], np.int32), np.array([1, 2], np.int32))
     n = ctypes.c_size_t()
     assert so.cgtp_workspace_size(plan.handle, g.handle, 2, ctypes.byref(n)) == 0 and n.value >= 256
-    assert so.cgtp_workspace_size(uvw.handle, g.handle, 2, ctypes.byref(n)) == UNSUPPORTED
-    assert so.cgtp_plan_compile(uvw.handle, 1 << 2) == UNSUPPORTED
+    # Fully connected: double backward yes (phi an input), triple backward no.
+    assert so.cgtp_workspace_size(uvw.handle, g.handle, 2, ctypes.byref(n)) == 0 and n.value >= 256
+    assert so.cgtp_workspace_size(uvw.handle, g.handle, 3, ctypes.byref(n)) == UNSUPPORTED
+    assert so.cgtp_plan_compile(uvw.handle, 1 << 3) == UNSUPPORTED
     nul = [None] * 10
     assert so.cgtp_conv_forward(plan.handle, g.handle, 0, *[None] * 6, None, 0, None) == INVALID_ARG
     assert so.cgtp_conv_forward(plan.handle, g.handle, 7, *[1] * 6, None, 0, None) == INVALID_ARG  # bad schedule
     assert so.cgtp_conv_backward(plan.handle, g.handle, *nul, None, None, 0, None) == INVALID_ARG
     assert so.cgtp_conv_double_backward(plan.handle, g.handle, *[None] * 18, 0, None) == INVALID_ARG
-    assert so.cgtp_conv_double_backward(uvw.handle, g.handle, *[1] * 6, *[None] * 12, 0, None) == UNSUPPORTED
+    assert so.cgtp_conv_double_backward(uvw.handle, g.handle, *[1] * 6, *[None] * 5, 1, *[None] * 5, 1, 16,
+                                        None) == WORKSPACE
     # Workspace smaller than cgtp_workspace_size: refused before touching the device.
     assert so.cgtp_conv_backward(plan.handle, g.handle, *[1] * 6, 1, None, None, None, None, 1, 16, None) == WORKSPACE
     assert so.cgtp_conv_double_backward(plan.handle, g.handle, *[1] * 6, *[None] * 5, 1, *[None] * 5, 1, 16,
