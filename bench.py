@@ -102,6 +102,10 @@ def kernel_fma(plan, spec, n_edges: int, n_nodes: int, passes, keep_state: bool 
       uvw_zstate      C_out (gnz + K d1) per edge
       gemm_fwd<g>, gemm_sbar<g>, gemm_abar<g>: (N d3_g) x C_out x sum_{paths into g} K C_in
       gemm_xbar<b>    (N d1_b) x C_in x sum_{paths from b} K C_out
+    The fully connected double backward (every direction given) runs the state kernel and the
+    forward GEMMs four times (three terms of S-dot, and S for S A-dot), the A-bar GEMMs three
+    times, the Sbar GEMMs twice, the edge kernel four times (three tangent passes and the
+    first-order Y-bar), and the source state and x-bar GEMMs three times.
     Kernels without an entry (edge finalisation, reductions) are reported by time only.
     """
     K, E, N = plan.info["num_radial"], n_edges, n_nodes
@@ -152,12 +156,23 @@ def kernel_fma(plan, spec, n_edges: int, n_nodes: int, passes, keep_state: bool 
             if ps == "bwd":
                 add(f"cgtp_gemm_sbar{g}", mac)
                 add(f"cgtp_gemm_abar{g}", mac)
-        if ps == "bwd":
-            add("cgtp_uvw_edge", sum(bi[r["i_in"]][0] * (r["gnz"] + 2 * K * r["d3"] + r["nnz"]) for r in rows) * E)
-            add("cgtp_uvw_zstate", sum(bo[r["i_out"]][0] * (r["gnz"] + K * r["d1"]) for r in rows) * E)
+        # Launch multiplicities: (state, gemm_fwd, gemm_sbar, gemm_abar, edge, zstate, gemm_xbar).
+        mult = {"fwds": (0, 1, 0, 0, 0, 0, 0), "bwd": (0, 0, 1, 1, 1, 1, 1), "dbl": (4, 4, 2, 3, 4, 3, 3)}.get(ps)
+        if ps == "dbl":
+            add("cgtp_uvw_state", 4 * state)
+            for g in sorted({r["i_out"] for r in rows}):
+                depth = sum(K * bi[r["i_in"]][0] for r in rows if r["i_out"] == g)
+                mac = N * (2 * bo[g][1] + 1) * bo[g][0] * depth
+                add(f"cgtp_gemm_fwd{g}", mult[1] * mac)
+                add(f"cgtp_gemm_sbar{g}", mult[2] * mac)
+                add(f"cgtp_gemm_abar{g}", mult[3] * mac)
+        if ps in ("bwd", "dbl"):
+            add("cgtp_uvw_edge", mult[4] * sum(bi[r["i_in"]][0] * (r["gnz"] + 2 * K * r["d3"] + r["nnz"])
+                                               for r in rows) * E)
+            add("cgtp_uvw_zstate", mult[5] * sum(bo[r["i_out"]][0] * (r["gnz"] + K * r["d1"]) for r in rows) * E)
             for b in sorted({r["i_in"] for r in rows}):
                 depth = sum(K * bo[r["i_out"]][0] for r in rows if r["i_in"] == b)
-                add(f"cgtp_gemm_xbar{b}", N * (2 * bi[b][1] + 1) * bi[b][0] * depth)
+                add(f"cgtp_gemm_xbar{b}", mult[6] * N * (2 * bi[b][1] + 1) * bi[b][0] * depth)
     return f
 
 
@@ -213,6 +228,9 @@ def main() -> int:
                          "workload 5) instead of reading phi")
     ap.add_argument("--order", type=int, default=2, choices=(0, 1, 2),
                     help="node dispatch order of the graph: 0 index, 1 by degree, 2 automatic (default)")
+    ap.add_argument("--double", action="store_true",
+                    help="add the double backward to the workload's passes (the l <= 6 workload has it already; "
+                         "with workload 4 the fully connected double backward)")
     ap.add_argument("--triple", action="store_true",
                     help="measure the third-order derivative (LunaTP Algorithm 4) on the workload's graph and "
                          "irreps, edge operand = the harmonics of the edge vectors, all directions and cotangents "
@@ -240,6 +258,8 @@ def main() -> int:
         return sweep(torch, cg, args)
     cfg = args.workload
     passes = PASSES[cfg]
+    if args.double and "dbl" not in passes:
+        passes = passes + ("dbl",)
     spec = CONFIGS[cfg]
     w = make_workload(cfg)
     dtype = spec["dtype"]
