@@ -53,6 +53,10 @@ PREROLL_MS = 100.0          # untimed steps before the warm-up, so that the cloc
 PROTOCOL_MIN_MS = 250.0     # sample time of the median protocol (Sobek section 5.1)
 PROTOCOL_MIN_SAMPLES = 10
 
+# Scratch budget per workload when --scratch-mib is not given: the library's default (256 MiB) for
+# the small ones; the 16k-atom fully connected and the l <= 6 workloads are quoted with budgets that
+# hold their receiver state (4 GiB) and coefficient rows (16 GiB) in one chunk (of 288 GB of HBM).
+WORKLOAD_SCRATCH_MIB = {4: 4096, 5: 16384}
 PASSES = {1: ("fwd", "fwds"), 2: ("fwd", "bwd"), 3: ("fwd",), 4: ("fwds", "bwd"), 5: ("fwd", "bwd", "dbl")}
 PASS_NAMES = {"fwd": "forward (conventional)", "fwds": "forward (streamed)", "bwd": "backward",
               "dbl": "double backward"}
@@ -209,7 +213,8 @@ def main() -> int:
     ap.add_argument("--profile-steps", type=int, default=10)
     ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD, choices=sorted(PASSES))
     ap.add_argument("--scratch-mib", type=int, default=0,
-                    help="scratch budget of the plan in MiB (0: the library default)")
+                    help="scratch budget of the plan in MiB (0: 4096 for workload 4, 16384 for workload 5, "
+                         "else the library default of 256)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peak-probe", action="store_true",
                     help="skip the measured FMA and copy ceilings (cgtp_measure_peak)")
@@ -264,8 +269,9 @@ def main() -> int:
     w = make_workload(cfg)
     dtype = spec["dtype"]
     plan = cg.Plan(spec["irreps_in"], spec["irreps_sh"], spec["irreps_out"], spec["mode"], dtype, spec["K"])
-    if args.scratch_mib > 0:
-        plan.set_scratch_budget(args.scratch_mib << 20)
+    if args.scratch_mib <= 0:
+        args.scratch_mib = WORKLOAD_SCRATCH_MIB.get(cfg, 256)
+    plan.set_scratch_budget(args.scratch_mib << 20)
     if args.radial:
         plan.set_radial(2 if spec["radial"] == "gaussian" else 1, spec["rc"])
     graph = cg.Graph(w.n_nodes, w.recv, w.send, w.image)
@@ -455,7 +461,7 @@ def main() -> int:
                    "n_nodes": N, "n_edges": E, "passes": list(passes), "radial_in_kernel": bool(args.radial),
                    **({"receiver_state_kept": keep_state} if spec["mode"] == "uvw" else
                       {"edge_rows_kept": keep_state} if "bwd" in passes else {}),
-                   "scratch_budget_mib": args.scratch_mib or 256},
+                   "scratch_budget_mib": args.scratch_mib},
         "gflops_algorithmic": round(2.0 * step_fma / (ms_per_step * 1e-3) / 1e9, 1) if step_fma else None,
         "kernels": result_kernels,
         "roofline": roofline,
