@@ -240,13 +240,40 @@ void emit_edge_vector(Out& o) {
   o.close();
 }
 
+// Row stores of a lane-per-edge kernel (`lane`, `eb` = first edge of the wave's 64, `e0`, `e1`, the
+// destination G and a `__shared__ V4 tile[64 * 17]` in scope): the row of `stride` values whose
+// expressions are `vals` (padded with zeros) goes to G + (eb + lane - e0) * stride, 64 values at a
+// time through the LDS tile, so that the global stores are 16-byte units in which 16 lanes cover
+// 256 contiguous bytes of one row.
+void emit_staged_rows(Out& o, const Plan& p, std::vector<std::string> vals, int stride) {
+  const int per = p.dtype == CGTP_F64 ? 2 : 4;  // values per 16-byte unit
+  const int block_vals = 16 * per;             // values per tile column block
+  while (int(vals.size()) < stride) vals.push_back("R(0)");
+  const int nblocks = (stride + block_vals - 1) / block_vals;
+  for (int b = 0; b < nblocks; ++b) {
+    const int v0 = b * block_vals, nv = std::min(block_vals, stride - v0) / per;
+    o.open("");
+    for (int k = 0; k < nv; ++k) {
+      std::string v;
+      for (int t = 0; t < per; ++t) v += (t ? ", " : "") + vals[size_t(v0 + k * per + t)];
+      o.line(F("tile[lane * 17 + %d] = V4{", k) + v + "};");
+    }
+    o.line("__syncthreads();");
+    o.open("for (int it = 0; it < 16; ++it)");
+    o.line("const int row = it * 4 + (lane >> 4), c = lane & 15;");
+    o.line(F("if (eb + row < e1 && c < %d) ((V4*)(G + (i64)(eb + row - e0) * %d + %d))[c] = tile[row * 17 + c];", nv,
+             stride, v0));
+    o.close();
+    o.line("__syncthreads();");
+    o.close();
+  }
+}
+
 // prep: lane = edge, one wave per 64 edges; writes the G row of every edge of [e0, e1) at
 // G + (e - e0) * stride.  Rows are produced 64 values at a time into an LDS tile and copied out
 // with 16-byte stores in which 16 lanes cover 256 contiguous bytes of one row.
 void emit_prep(Out& o, const Plan& p, bool with_y) {
-  const int per = p.dtype == CGTP_F64 ? 2 : 4;  // values per 16-byte unit
   const int stride = with_y ? bwd_row_stride(p) : p.g_stride;
-  const int block_vals = 16 * per;             // values per tile column block
   o.line("extern \"C\" __global__ void __launch_bounds__(64)");
   o.open("cgtp_prep(const real* __restrict__ pos, const real* __restrict__ shift, const int* __restrict__ recv,"
          " const int* __restrict__ send, int e0, int e1, real* __restrict__ G)");
@@ -277,25 +304,7 @@ void emit_prep(Out& o, const Plan& p, bool with_y) {
   }
   if (with_y)
     for (int m = 0; m < p.sh_dim; ++m) vals.push_back(F("Y[%d]", m));
-  while (int(vals.size()) < stride) vals.push_back("R(0)");
-  const int nblocks = (stride + block_vals - 1) / block_vals;
-  for (int b = 0; b < nblocks; ++b) {
-    const int v0 = b * block_vals, nv = std::min(block_vals, stride - v0) / per;
-    o.open("");
-    for (int k = 0; k < nv; ++k) {
-      std::string v;
-      for (int t = 0; t < per; ++t) v += (t ? ", " : "") + vals[v0 + k * per + t];
-      o.line(F("tile[lane * 17 + %d] = V4{", k) + v + "};");
-    }
-    o.line("__syncthreads();");
-    o.open("for (int it = 0; it < 16; ++it)");
-    o.line("const int row = it * 4 + (lane >> 4), c = lane & 15;");
-    o.line(F("if (eb + row < e1 && c < %d) ((V4*)(G + (i64)(eb + row - e0) * %d + %d))[c] = tile[row * 17 + c];", nv,
-             stride, v0));
-    o.close();
-    o.line("__syncthreads();");
-    o.close();
-  }
+  emit_staged_rows(o, p, vals, stride);
   o.close();
 }
 
@@ -304,9 +313,7 @@ void emit_prep(Out& o, const Plan& p, bool with_y) {
 // the harmonics of the edge vector.  Lane = edge; the same LDS-staged 16-byte row stores as
 // cgtp_prep.
 void emit_prep_y(Out& o, const Plan& p) {
-  const int per = p.dtype == CGTP_F64 ? 2 : 4;
   const int stride = bwd_row_stride(p);
-  const int block_vals = 16 * per;
   o.line("extern \"C\" __global__ void __launch_bounds__(64)");
   o.open("cgtp_prep_y(const real* __restrict__ yop, int e0, int e1, real* __restrict__ G)");
   o.line("__shared__ V4 tile[64 * 17];");
@@ -328,25 +335,7 @@ void emit_prep_y(Out& o, const Plan& p) {
     }
   }
   for (int m = 0; m < p.sh_dim; ++m) vals.push_back(F("Y[%d]", m));
-  while (int(vals.size()) < stride) vals.push_back("R(0)");
-  const int nblocks = (stride + block_vals - 1) / block_vals;
-  for (int b = 0; b < nblocks; ++b) {
-    const int v0 = b * block_vals, nv = std::min(block_vals, stride - v0) / per;
-    o.open("");
-    for (int k = 0; k < nv; ++k) {
-      std::string v;
-      for (int t = 0; t < per; ++t) v += (t ? ", " : "") + vals[v0 + k * per + t];
-      o.line(F("tile[lane * 17 + %d] = V4{", k) + v + "};");
-    }
-    o.line("__syncthreads();");
-    o.open("for (int it = 0; it < 16; ++it)");
-    o.line("const int row = it * 4 + (lane >> 4), c = lane & 15;");
-    o.line(F("if (eb + row < e1 && c < %d) ((V4*)(G + (i64)(eb + row - e0) * %d + %d))[c] = tile[row * 17 + c];", nv,
-             stride, v0));
-    o.close();
-    o.line("__syncthreads();");
-    o.close();
-  }
+  emit_staged_rows(o, p, vals, stride);
   o.close();
 }
 

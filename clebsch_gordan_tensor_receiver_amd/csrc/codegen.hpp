@@ -84,6 +84,8 @@ void emit_radial_term(Out& o, const Plan& p, const std::string& pb);
 void emit_sh(Out& o, int L);
 void emit_edge_vector(Out& o);
 void emit_prep(Out& o, const Plan& p, bool with_y = false);
+// LDS-staged 16-byte stores of per-edge rows (lane = edge); see codegen.cpp.
+void emit_staged_rows(Out& o, const Plan& p, std::vector<std::string> vals, int stride);
 std::vector<int> in_blocks_of(const Plan& p, const std::vector<int>& paths);
 std::vector<int> out_blocks_of(const Plan& p, const std::vector<int>& paths);
 // nE > 1 (2 or 4): the wave's lanes form nE groups of 64 / nE channels and take nE consecutive

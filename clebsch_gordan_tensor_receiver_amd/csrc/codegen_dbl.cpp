@@ -132,14 +132,17 @@ void emit_edge_direction(Out& o) {
          " vez += vpos[3 * (i64)sj + 2] - vpos[3 * (i64)ri + 2]; }");
 }
 
-// prep2: G (columns 0..g_stride) and Gdot (columns g_stride..2 g_stride) of every edge of [e0, e1).
+// prep2: G (columns 0..g_stride) and Gdot (columns g_stride..2 g_stride) of every edge of [e0, e1),
+// lane = edge, rows stored through the LDS tile as cgtp_prep's.
 void emit_prep2(Out& o, const Plan& p) {
   o.line("extern \"C\" __global__ void __launch_bounds__(64)");
   o.open("cgtp_prep2(const real* __restrict__ pos, const real* __restrict__ shift, const int* __restrict__ recv,"
          " const int* __restrict__ send, const real* __restrict__ vev, const real* __restrict__ vpos, int e0,"
          " int e1, real* __restrict__ G)");
-  o.line("const int e = e0 + (int)(blockIdx.x * 64 + threadIdx.x);");
-  o.line("if (e >= e1) return;");
+  o.line("__shared__ V4 tile[64 * 17];");
+  o.line("const int lane = (int)threadIdx.x;");
+  o.line("const int eb = e0 + (int)blockIdx.x * 64;");
+  o.line("const int e = min(eb + lane, e1 - 1);");
   emit_edge_vector(o);
   emit_edge_direction(o);
   o.line("const real inv = R(1) / sqrt(rx * rx + ry * ry + rz * rz);");
@@ -148,13 +151,13 @@ void emit_prep2(Out& o, const Plan& p) {
   o.line("const real dx = (vex - nx * nv) * inv, dy = (vey - ny * nv) * inv, dz = (vez - nz * nv) * inv;");
   o.line(F("D1 Y[%d];", p.sh_dim));
   o.line("sh_eval<D1>(D1(nx, dx), D1(ny, dy), D1(nz, dz), Y);");
-  o.line(F("real* __restrict__ dst = G + (i64)(e - e0) * %d;", 2 * p.g_stride));
+  std::vector<std::string> vals(size_t(2 * p.g_stride), "R(0)");
   if (p.radial) {   // phi(|r|) in the G row, its tangent phi'(|r|) (r-hat . rdot) in the Gdot row
     o.line(F("real fr[%d], dfr[%d];", p.K, p.K));
     o.line("radial_eval(R(1) / inv, fr, dfr, nullptr);");
     for (int q = 0; q < p.K; ++q) {
-      o.line(F("dst[%d] = fr[%d];", p.phi_off + q, q));
-      o.line(F("dst[%d] = dfr[%d] * nv;", p.g_stride + p.phi_off + q, q));
+      vals[size_t(p.phi_off + q)] = F("fr[%d]", q);
+      vals[size_t(p.g_stride + p.phi_off + q)] = F("dfr[%d] * nv", q);
     }
   }
   for (const Path& P : p.paths) {
@@ -170,11 +173,12 @@ void emit_prep2(Out& o, const Plan& p) {
         ev += lit(t.second) + " * Y[" + std::to_string(s + t.first) + "].v";
         ed += lit(t.second) + " * Y[" + std::to_string(s + t.first) + "].d";
       }
-      o.line(F("dst[%d] = ", n) + ev + ";");
-      o.line(F("dst[%d] = ", n + p.g_stride) + ed + ";");
+      vals[size_t(n)] = ev;
+      vals[size_t(n + p.g_stride)] = ed;
       ++n;
     }
   }
+  emit_staged_rows(o, p, vals, 2 * p.g_stride);
   o.close();
 }
 
@@ -510,8 +514,9 @@ void emit_ebar_dot(Out& o, const Plan& p, const std::function<void()>& fill) {
   o.line("gz += (-dz * np_ - nz * dp + (hz - nz * nh)) * inv - (wz - nz * np_) * nv * inv * inv;");
 }
 
-// Gdot row (G's layout) of the current edge e into dst: the directional derivative of G along
-// rdot, from a dual-number pass of the harmonics.
+// Gdot row (G's layout) of the current edge e, stored through the LDS tile (lane = edge; `tile`,
+// `lane`, `eb`, `e0`, `e1` and the destination `G` in scope): the directional derivative of G
+// along rdot, from a dual-number pass of the harmonics.
 void emit_gdot_row(Out& o, const Plan& p) {
   emit_edge_vector(o);
   emit_edge_direction(o);
@@ -521,6 +526,7 @@ void emit_gdot_row(Out& o, const Plan& p) {
   o.line("const real dx = (vex - nx * nv) * inv, dy = (vey - ny * nv) * inv, dz = (vez - nz * nv) * inv;");
   o.line(F("D1 Y[%d];", p.sh_dim));
   o.line("sh_eval<D1>(D1(nx, dx), D1(ny, dy), D1(nz, dz), Y);");
+  std::vector<std::string> vals(size_t(p.g_stride), "R(0)");
   for (const Path& P : p.paths) {
     int s = P.l2 * P.l2;
     int n = P.g_off;
@@ -530,9 +536,10 @@ void emit_gdot_row(Out& o, const Plan& p) {
         if (!ed.empty()) ed += " + ";
         ed += lit(t.second) + " * Y[" + std::to_string(s + t.first) + "].d";
       }
-      o.line(F("dst[%d] = ", n++) + ed + ";");
+      vals[size_t(n++)] = ed;
     }
   }
+  emit_staged_rows(o, p, vals, p.g_stride);
 }
 
 // Edge finalisation: phi-bar-dot sums, e-bar-dot = J^T Ybar_d + the curvature term.
@@ -705,19 +712,23 @@ void emit_uvw_dbl_kernels(Out& o, const Plan& p, int ntask, int V) {
   o.open("cgtp_prep_dot(const real* __restrict__ pos, const real* __restrict__ shift, const int* __restrict__ recv,"
          " const int* __restrict__ send, const real* __restrict__ vev, const real* __restrict__ vpos, int e0,"
          " int e1, real* __restrict__ Gd)");
-  o.line("const int e = e0 + (int)(blockIdx.x * 64 + threadIdx.x);");
-  o.line("if (e >= e1) return;");
-  o.line(F("real* __restrict__ dst = Gd + (i64)(e - e0) * %d;", p.g_stride));
+  o.line("__shared__ V4 tile[64 * 17];");
+  o.line("real* __restrict__ G = Gd;");
+  o.line("const int lane = (int)threadIdx.x;");
+  o.line("const int eb = e0 + (int)blockIdx.x * 64;");
+  o.line("const int e = min(eb + lane, e1 - 1);");
   emit_gdot_row(o, p);
   o.close();
   o.line("extern \"C\" __global__ void __launch_bounds__(64)");
   o.open("cgtp_prep_src_dot(const real* __restrict__ pos, const real* __restrict__ shift,"
          " const int* __restrict__ recv, const int* __restrict__ send, const int* __restrict__ src_edge,"
          " const real* __restrict__ vev, const real* __restrict__ vpos, int k0, int k1, real* __restrict__ Gd)");
-  o.line("const int k = k0 + (int)(blockIdx.x * 64 + threadIdx.x);");
-  o.line("if (k >= k1) return;");
-  o.line("const int e = src_edge[k];");
-  o.line(F("real* __restrict__ dst = Gd + (i64)(k - k0) * %d;", p.g_stride));
+  // Rows at source-CSR positions: the staged stores index them by k (eb, e0, e1 name positions).
+  o.line("__shared__ V4 tile[64 * 17];");
+  o.line("real* __restrict__ G = Gd;");
+  o.line("const int lane = (int)threadIdx.x;");
+  o.line("const int e0 = k0, e1 = k1, eb = k0 + (int)blockIdx.x * 64;");
+  o.line("const int e = src_edge[min(eb + lane, k1 - 1)];");
   emit_gdot_row(o, p);
   o.close();
   o.line("extern \"C\" __global__ void __launch_bounds__(64)");
