@@ -595,19 +595,19 @@ def test_radial_second_derivative_complex_step(kind):
         assert float(radial.basis_second_derivative(kind, torch.tensor([5.0, 6.0]), rc, K).abs().max()) == 0.0
 
 
-def _radial_dbl_case(kind):
-    ov = dict(irreps_in="2x0e+2x1o+2x2e", irreps_out="2x0e+2x1o+2x2e", irreps_sh=_sh_str(2), mode="uvu")
+def _radial_dbl_case(kind, mode="uvu"):
+    ov = dict(irreps_in="2x0e+2x1o+2x2e", irreps_out="2x0e+2x1o+2x2e", irreps_sh=_sh_str(2), mode=mode)
     c = make_case(1, irreps_override=ov, n_nodes=10)
     g = np.random.default_rng(61 + kind)
     v = dict(v_x=g.normal(size=c.x.shape), v_e=g.normal(size=(len(c.recv), 3)), v_A=g.normal(size=c.A.shape))
     return c, v, 3.0
 
 
-@pytest.mark.parametrize("kind", [1, 2])
-def test_radial_double_backward_matches_autograd(kind):
+@pytest.mark.parametrize("kind,mode", [(1, "uvu"), (2, "uvu"), (1, "uvw"), (2, "uvw")])
+def test_radial_double_backward_matches_autograd(kind, mode):
     # Independent route: torch autograd of the forward with phi = basis(|r|), taken twice.
     from oracle import radial
-    c, v, rc = _radial_dbl_case(kind)
+    c, v, rc = _radial_dbl_case(kind, mode)
     K = c.phi.shape[1]
     x = torch.tensor(c.x, requires_grad=True)
     pos = torch.tensor(c.pos, requires_grad=True)
