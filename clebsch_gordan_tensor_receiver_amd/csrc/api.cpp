@@ -181,6 +181,42 @@ cgtp_status_t tri_plan(cgtp::Plan& p, cgtp::Plan** out, std::string* err) {
   return CGTP_OK;
 }
 
+// The plan's twin without a radial basis (created on first use): the fully connected double
+// backward of a plan with one runs on it, phi and phi-dot materialised per edge.
+cgtp_status_t plain_plan(cgtp::Plan& p, cgtp::Plan** out, std::string* err) {
+  std::lock_guard<std::mutex> lock(p.mu);
+  if (!p.plain) {
+    std::unique_ptr<cgtp::Plan> t(new cgtp::Plan());
+    cgtp_status_t st = cgtp::build_plan(p.irreps_in_s.c_str(), p.irreps_sh_s.c_str(), p.irreps_out_s.c_str(), p.mode,
+                                        p.dtype, p.K, t.get(), err);
+    if (st != CGTP_OK) return st;
+    p.plain = std::move(t);
+  }
+  p.plain->scratch_budget = p.scratch_budget;
+  *out = p.plain.get();
+  return CGTP_OK;
+}
+
+// Workspace of the fully connected double backward with a radial basis: phi, phi-dot, the
+// gradient in phi and the first-order phi-bar (E x K each), e-bar-dot (E x 3), then the workspace
+// of the double backward on the plain twin.
+struct RadialDblLayout {
+  size_t phi_off = 0, vphi_off = 0, gphi_off = 0, pb_off = 0, gev_off = 0, inner_off = 0, total = 0;
+};
+RadialDblLayout radial_dbl_layout(const cgtp::Plan& p, const cgtp::Plan& pp, const cgtp::Graph& G) {
+  auto al = [](size_t n) { return (n + 255) / 256 * 256; };
+  RadialDblLayout L;
+  const size_t ek = al(size_t(std::max(G.e, 1)) * p.K * p.elem());
+  L.phi_off = 0;
+  L.vphi_off = ek;
+  L.gphi_off = 2 * ek;
+  L.pb_off = 3 * ek;
+  L.gev_off = 4 * ek;
+  L.inner_off = L.gev_off + al(size_t(std::max(G.e, 1)) * 3 * p.elem());
+  L.total = L.inner_off + cgtp::uvw_workspace(pp, G, CGTP_OP_DOUBLE_BACKWARD);
+  return L;
+}
+
 // Workspace of the third-order passes (on the 2K plan tp): per edge of a receiver chunk the rows of
 // one edge operand (Y, v_Y or q_Y: the terms run grouped by it) and the packed radial factors
 // (2K); the receiver pass's partials and A-bar slots; beyond the budget the packed A factors
@@ -364,11 +400,19 @@ cgtp_status_t cgtp_plan_compile(cgtp_plan_t plan, int ops) {
   } else {
     if (ops & (1 << CGTP_OP_TRIPLE_BACKWARD))
       return fail(CGTP_ERR_UNSUPPORTED, "the triple backward is channelwise only");
-    if ((ops & (1 << CGTP_OP_DOUBLE_BACKWARD)) && plan->p.radial)
-      return fail(CGTP_ERR_UNSUPPORTED, "the fully connected double backward takes phi as an input");
     if (ops & (1 << CGTP_OP_FORWARD)) fams.push_back("uvw_fwd");
     if (ops & (1 << CGTP_OP_BACKWARD)) fams.push_back("uvw_bwd");
-    if (ops & (1 << CGTP_OP_DOUBLE_BACKWARD)) fams.push_back("uvw_dbl");
+    if (ops & (1 << CGTP_OP_DOUBLE_BACKWARD)) {
+      if (plan->p.radial) {
+        cgtp::Plan* pp = nullptr;
+        cgtp_status_t st = plain_plan(plan->p, &pp, &err);
+        if (st == CGTP_OK) st = cgtp::compile_family(*pp, "uvw_dbl", &err);
+        if (st != CGTP_OK) return fail(st, err);
+        fams.push_back("uvw_rdbl");
+      } else {
+        fams.push_back("uvw_dbl");
+      }
+    }
   }
   if (ops & (1 << CGTP_OP_FORWARD)) fams.push_back("layout");  // boundary layout conversion
   for (auto& f : fams) {
@@ -451,8 +495,14 @@ cgtp_status_t cgtp_workspace_size(cgtp_plan_t plan, cgtp_graph_t g, cgtp_op_t op
   size_t need = 0;
   if (p.mode == CGTP_FULLY_CONNECTED) {
     if (op == CGTP_OP_TRIPLE_BACKWARD) return fail(CGTP_ERR_UNSUPPORTED, "the triple backward is channelwise only");
-    if (op == CGTP_OP_DOUBLE_BACKWARD && p.radial)
-      return fail(CGTP_ERR_UNSUPPORTED, "the fully connected double backward takes phi as an input");
+    if (op == CGTP_OP_DOUBLE_BACKWARD && p.radial) {
+      cgtp::Plan* pp = nullptr;
+      std::string err;
+      cgtp_status_t st = plain_plan(plan->p, &pp, &err);
+      if (st != CGTP_OK) return fail(st, err);
+      *bytes = std::max<size_t>(radial_dbl_layout(p, *pp, G).total, 256);
+      return ok();
+    }
     *bytes = std::max<size_t>(cgtp::uvw_workspace(p, G, op), 256);
     return ok();
   }
@@ -737,8 +787,6 @@ cgtp_status_t cgtp_conv_double_backward(cgtp_plan_t plan, cgtp_graph_t g, const 
   if (!x || !pos || !A || !grad_out) return fail(CGTP_ERR_INVALID_ARG, "null input tensor");
   cgtp::Plan& p = plan->p;
   cgtp::Graph& G = g->g;
-  if (p.mode != CGTP_CHANNELWISE && p.radial)
-    return fail(CGTP_ERR_UNSUPPORTED, "the fully connected double backward takes phi as an input");
   if ((phi == nullptr) != (p.radial != 0))
     return fail(CGTP_ERR_INVALID_ARG, p.radial ? "phi must be NULL: the plan computes the radial basis"
                                                : "null phi (the plan has no radial basis of its own)");
@@ -754,6 +802,47 @@ cgtp_status_t cgtp_conv_double_backward(cgtp_plan_t plan, cgtp_graph_t g, const 
   cgtp::DeviceGraph d;
   if ((st = cgtp::device_graph(G, &d, &err)) != CGTP_OK) return fail(st, err);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.mode == CGTP_FULLY_CONNECTED && p.radial) {
+    // phi and phidot = phi'(|r|) (r-hat . rdot) per edge, the double backward on the plain twin
+    // with them as inputs (its gg_phi and the first-order phi-bar kept), then the radial terms
+    // of e-bar-dot and the position sums.
+    cgtp::Plan* pp = nullptr;
+    if ((st = plain_plan(p, &pp, &err)) != CGTP_OK) return fail(st, err);
+    const RadialDblLayout R = radial_dbl_layout(p, *pp, G);
+    char* ws = static_cast<char*>(workspace);
+    void* phi_a = ws + R.phi_off;
+    void* vphi_a = ws + R.vphi_off;
+    void* gphi = gg_phi ? gg_phi : static_cast<void*>(ws + R.gphi_off);
+    void* pb = ws + R.pb_off;
+    const bool want_ev = gg_edge_vec || gg_pos;
+    void* gev = gg_edge_vec ? gg_edge_vec : static_cast<void*>(ws + R.gev_off);
+    hipFunction_t kvals, kdedge, kpos;
+    if ((st = cgtp::get_kernel(p, "uvw_rdbl", "cgtp_radial_vals", &kvals, &err)) != CGTP_OK ||
+        (st = cgtp::get_kernel(p, "uvw_rdbl", "cgtp_radial_dedge", &kdedge, &err)) != CGTP_OK ||
+        (st = cgtp::get_kernel(p, "uvw_rdbl", "cgtp_pos_grad", &kpos, &err)) != CGTP_OK)
+      return fail(st, err);
+    int e0 = 0, e1 = G.e;
+    if (e1 > 0) {
+      void* a[] = {(void*)&pos, (void*)&shift, (void*)&d.recv, (void*)&d.col, (void*)&v_edge_vec, (void*)&v_pos,
+                   &e0, &e1, &phi_a, &vphi_a};
+      if ((st = cgtp::launch(kvals, unsigned((e1 + 63) / 64), 64, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
+    }
+    st = cgtp::uvw_double_backward(*pp, G, d, x, pos, shift, phi_a, A, grad_out, v_x, v_pos, v_edge_vec, vphi_a, v_A,
+                                   gg_x, nullptr, want_ev ? gev : nullptr, gphi, gg_A, gg_grad_out,
+                                   ws + R.inner_off, s, &err, want_ev ? pb : nullptr);
+    if (st != CGTP_OK) return fail(st, err);
+    if (want_ev && e1 > 0) {
+      void* a[] = {(void*)&pos, (void*)&shift, (void*)&d.recv, (void*)&d.col, (void*)&v_edge_vec, (void*)&v_pos,
+                   &gphi, &pb, &e0, &e1, &gev};
+      if ((st = cgtp::launch(kdedge, unsigned((e1 + 63) / 64), 64, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
+    }
+    if (gg_pos) {
+      int n = G.n;
+      void* a[] = {&gev, (void*)&d.row_ptr, (void*)&d.src_ptr, (void*)&d.src_edge, &n, &gg_pos};
+      if ((st = cgtp::launch(kpos, unsigned(n), 64, 0, s, a, &err)) != CGTP_OK) return fail(st, err);
+    }
+    return ok();
+  }
   if (p.mode == CGTP_FULLY_CONNECTED) {
     st = cgtp::uvw_double_backward(p, G, d, x, pos, shift, phi, A, grad_out, v_x, v_pos, v_edge_vec, v_phi, v_A, gg_x,
                                    gg_pos, gg_edge_vec, gg_phi, gg_A, gg_grad_out, workspace, s, &err);

@@ -1602,7 +1602,8 @@ std::string generate_source(const Plan& p, const std::string& family, std::strin
     emit_layout_kernel(o, p.out, p.c_out, "cgtp_layout_out");
     return o.s.str();
   }
-  if (p.mode != CGTP_CHANNELWISE) return generate_uvw_source(p, family, err);
+  if (p.mode != CGTP_CHANNELWISE)
+    return family == "uvw_rdbl" ? generate_uvw_radial_dbl_source(p, err) : generate_uvw_source(p, family, err);
   // fwdk: the conventional forward writing (and reading) the backward's row layout (G, then Y),
   // so that a backward called with the rows the forward kept needs no prep of its own.
   if (family == "fwd" || family == "fwds" || family == "fwdk") {

@@ -109,6 +109,9 @@ void emit_check_edges(Out& o);
 
 // Channelwise double backward (family "dbl").
 std::string generate_dbl_source(const Plan& p, std::string* err);
+// Fully connected double backward with an in-kernel radial basis (family "uvw_rdbl"): phi and its
+// tangent per edge, and the radial terms of the edge-vector gradient.
+std::string generate_uvw_radial_dbl_source(const Plan& p, std::string* err);
 
 // Fully connected (uvw) kernel families "uvw_fwd" and "uvw_bwd".
 std::string generate_uvw_source(const Plan& p, const std::string& family, std::string* err);

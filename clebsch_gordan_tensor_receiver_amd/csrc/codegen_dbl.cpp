@@ -736,7 +736,7 @@ void emit_uvw_dbl_kernels(Out& o, const Plan& p, int ntask, int V) {
          " const int* __restrict__ recv, const int* __restrict__ send, const real* __restrict__ vev,"
          " const real* __restrict__ vpos, const real* __restrict__ epa, const real* __restrict__ epb,"
          " const real* __restrict__ epc, const real* __restrict__ epw, int e0, int e1, int eps,"
-         " real* __restrict__ gphi, real* __restrict__ gev)");
+         " real* __restrict__ gphi, real* __restrict__ gev, real* __restrict__ pb1)");
   o.line("const int e = e0 + (int)(blockIdx.x * 64 + threadIdx.x);");
   o.line("if (e >= e1) return;");
   o.line("const i64 el_ = e - e0;");
@@ -755,6 +755,10 @@ void emit_uvw_dbl_kernels(Out& o, const Plan& p, int ntask, int V) {
   o.open("if (gphi)");
   for (int q = 0; q < K; ++q) o.line(F("gphi[(i64)e * %d + %d] = gp%d;", K, q, q));
   o.close();
+  // pb1 (nullable): the first-order phi-bar, the phi-bar columns of the first-order pass.
+  o.open("if (pb1 && epw)");
+  for (int q = 0; q < K; ++q) o.line(F("pb1[(i64)e * %d + %d] = ", K, q) + col_sum("epw", q) + ";");
+  o.close();
   o.line("if (!gev) return;");
   emit_ebar_dot(o, p, [&] {
     for (int m = 0; m < Yd; ++m) o.line(F("ybd[%d] = R(0); ybw[%d] = R(0);", m, m));
@@ -772,5 +776,65 @@ void emit_uvw_dbl_kernels(Out& o, const Plan& p, int ntask, int V) {
 }
 
 }  // namespace gen
+
+// Family "uvw_rdbl" of a fully connected plan with an in-kernel radial basis:
+//   cgtp_radial_vals (lane = edge): phi(|r|) and phidot = phi'(|r|) (r-hat . rdot) of every edge of
+//     [e0, e1) into E x K arrays (the inputs of the double backward run on the plan without a basis);
+//   cgtp_radial_dedge (lane = edge): adds to e-bar-dot the chain through phi, J_phi^T phi-bar-dot =
+//     (sum gphi_q phi'_q) r-hat, and the curvature grad_r [s (r-hat . rdot)] = s' t r-hat +
+//     s (rdot - t r-hat) / |r| with s = sum pb_q phi'_q, s' = sum pb_q phi''_q, t = r-hat . rdot,
+//     pb the first-order phi-bar.
+std::string generate_uvw_radial_dbl_source(const Plan& p, std::string* err) {
+  if (p.mode != CGTP_FULLY_CONNECTED || !p.radial) {
+    *err = "family uvw_rdbl is generated for fully connected plans with a radial basis";
+    return "";
+  }
+  const int K = p.K;
+  Out o;
+  prelude(o, p, false, true);
+  o.line("extern \"C\" __global__ void __launch_bounds__(64)");
+  o.open("cgtp_radial_vals(const real* __restrict__ pos, const real* __restrict__ shift, const int* __restrict__ recv,"
+         " const int* __restrict__ send, const real* __restrict__ vev, const real* __restrict__ vpos, int e0,"
+         " int e1, real* __restrict__ phi, real* __restrict__ vphi)");
+  o.line("const int e = e0 + (int)(blockIdx.x * 64 + threadIdx.x);");
+  o.line("if (e >= e1) return;");
+  emit_edge_vector(o);
+  emit_edge_direction(o);
+  o.line("const real rr = sqrt(rx * rx + ry * ry + rz * rz), inv = R(1) / rr;");
+  o.line("const real nv = (rx * vex + ry * vey + rz * vez) * inv;");
+  o.line(F("real fr[%d], dfr[%d];", K, K));
+  o.line("radial_eval(rr, fr, dfr, nullptr);");
+  for (int q = 0; q < K; ++q) {
+    o.line(F("phi[(i64)e * %d + %d] = fr[%d];", K, q, q));
+    o.line(F("vphi[(i64)e * %d + %d] = dfr[%d] * nv;", K, q, q));
+  }
+  o.close();
+  o.line("extern \"C\" __global__ void __launch_bounds__(64)");
+  o.open("cgtp_radial_dedge(const real* __restrict__ pos, const real* __restrict__ shift, const int* __restrict__ recv,"
+         " const int* __restrict__ send, const real* __restrict__ vev, const real* __restrict__ vpos,"
+         " const real* __restrict__ gphi, const real* __restrict__ pb, int e0, int e1, real* __restrict__ gev)");
+  o.line("const int e = e0 + (int)(blockIdx.x * 64 + threadIdx.x);");
+  o.line("if (e >= e1) return;");
+  emit_edge_vector(o);
+  emit_edge_direction(o);
+  o.line("const real rr = sqrt(rx * rx + ry * ry + rz * rz), inv = R(1) / rr;");
+  o.line("const real nx = rx * inv, ny = ry * inv, nz = rz * inv;");
+  o.line("const real nv = nx * vex + ny * vey + nz * vez;");
+  o.line(F("real fr[%d], dfr[%d], d2fr[%d];", K, K, K));
+  o.line("radial_eval(rr, fr, dfr, d2fr);");
+  o.line("real sc = R(0), s1 = R(0), s2 = R(0);");
+  for (int q = 0; q < K; ++q) {
+    o.line(F("sc = fma(gphi[(i64)e * %d + %d], dfr[%d], sc);", K, q, q));
+    o.line(F("s1 = fma(pb[(i64)e * %d + %d], dfr[%d], s1);", K, q, q));
+    o.line(F("s2 = fma(pb[(i64)e * %d + %d], d2fr[%d], s2);", K, q, q));
+  }
+  o.line("const real cn = sc + (s2 - s1 * inv) * nv, cv = s1 * inv;");
+  o.line("gev[3 * (i64)e] += cn * nx + cv * vex;");
+  o.line("gev[3 * (i64)e + 1] += cn * ny + cv * vey;");
+  o.line("gev[3 * (i64)e + 2] += cn * nz + cv * vez;");
+  o.close();
+  emit_small_kernels(o);
+  return o.s.str();
+}
 
 }  // namespace cgtp

@@ -75,6 +75,9 @@ struct Plan {
   // The same irreps with 2K radial values, whose kernels run the third-order passes (a weight
   // phi_1 A_1 + phi_2 A_2 as one product of stacked factors); built on first use, under `mu`.
   std::unique_ptr<Plan> tri;
+  // The same irreps and K without a radial basis: the fully connected double backward of a plan
+  // with one runs on it with phi and phi-dot materialised per edge; built on first use, under `mu`.
+  std::unique_ptr<Plan> plain;
   std::unique_ptr<KernelSet> kernels;
   std::mutex mu;
   mutable std::once_flag tables_once;              // task lists (kernels.hpp), built on first use

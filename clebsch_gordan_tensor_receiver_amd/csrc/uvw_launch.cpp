@@ -436,7 +436,8 @@ cgtp_status_t uvw_double_backward(Plan& p, Graph& G, const DeviceGraph& d, const
                                   const void* shift, const void* phi, const void* A, const void* gout,
                                   const void* v_x, const void* v_pos, const void* v_edge_vec, const void* v_phi,
                                   const void* v_A, void* gg_x, void* gg_pos, void* gg_edge_vec, void* gg_phi,
-                                  void* gg_A, void* gg_grad_out, void* workspace, hipStream_t s, std::string* err) {
+                                  void* gg_A, void* gg_grad_out, void* workspace, hipStream_t s, std::string* err,
+                                  void* phibar_out) {
   UvwPlanD B = layout_dbl(p, G);
   cgtp_status_t st;
   const char* fam = "uvw_dbl";
@@ -488,7 +489,8 @@ cgtp_status_t uvw_double_backward(Plan& p, Graph& G, const DeviceGraph& d, const
   void* ap = ws + B.ap_off;
   void* gev = gg_edge_vec ? gg_edge_vec : static_cast<void*>(ws + B.gev_off);
   void* gev_arg = (gg_edge_vec || gg_pos) ? gev : nullptr;
-  const bool need_edge = gg_edge_vec || gg_pos || gg_phi;
+  // phibar_out (nullable): the first-order phi-bar per edge (E x K), from the first-order pass.
+  const bool need_edge = gg_edge_vec || gg_pos || gg_phi || phibar_out;
   const bool rdir = v_pos || v_edge_vec;
   auto zero = [&](void* ptr, long long n) {
     void* a[] = {&ptr, &n};
@@ -605,7 +607,7 @@ cgtp_status_t uvw_double_backward(Plan& p, Graph& G, const DeviceGraph& d, const
         void* epa = v_A ? ep0 : nullptr;
         void* epb = v_x ? ep0 + B.ep_bytes : nullptr;
         void* epc = ep0 + 2 * B.ep_bytes;
-        void* epw = gev_arg ? ep0 + 3 * B.ep_bytes : nullptr;
+        void* epw = (gev_arg || phibar_out) ? ep0 + 3 * B.ep_bytes : nullptr;
         int nst = stripes(nrec, B.L.n_state_tasks, 0);
         auto edge = [&](const void* xx, const void* ff, void* gg, void* sb, void* ep) {
           void* a[] = {(void*)&xx, (void*)&ff, &gg, (void*)&d.row_ptr, (void*)&d.col, &sb, &ep, &i0, &nrec, &per,
@@ -617,7 +619,7 @@ cgtp_status_t uvw_double_backward(Plan& p, Graph& G, const DeviceGraph& d, const
         if ((st = edge(x, vphi, Gdb, Sb, epc)) != CGTP_OK) return st;
         if (epw && (st = edge(x, phi, Gb, Sb, epw)) != CGTP_OK) return st;
         void* b[] = {(void*)&pos, (void*)&shift, (void*)&d.recv, (void*)&d.col, (void*)&v_edge_vec, (void*)&v_pos,
-                     &epa, &epb, &epc, &epw, &e0, &e1, &eps, &gg_phi, &gev_arg};
+                     &epa, &epb, &epc, &epw, &e0, &e1, &eps, &gg_phi, &gev_arg, &phibar_out};
         if ((st = launch(kfinal, cdiv(e1 - e0, 64), 64, 0, s, b, err)) != CGTP_OK) return st;
       }
     }

@@ -31,6 +31,7 @@ cgtp_status_t uvw_double_backward(Plan& p, Graph& G, const DeviceGraph& d, const
                                   const void* shift, const void* phi, const void* A, const void* gout,
                                   const void* v_x, const void* v_pos, const void* v_edge_vec, const void* v_phi,
                                   const void* v_A, void* gg_x, void* gg_pos, void* gg_edge_vec, void* gg_phi,
-                                  void* gg_A, void* gg_grad_out, void* workspace, hipStream_t s, std::string* err);
+                                  void* gg_A, void* gg_grad_out, void* workspace, hipStream_t s, std::string* err,
+                                  void* phibar_out = nullptr);
 
 }  // namespace cgtp

@@ -145,9 +145,9 @@ cgtp_status_t cgtp_plan_set_scratch_budget(cgtp_plan_t plan, size_t bytes);
  * With kind 1 or 2 the convolution calls take phi = NULL; no E x K tensor is read, the values
  * live in the per-chunk workspace rows; cgtp_conv_backward's grad_pos and grad_edge_vec include
  * the chain rule through phi(r) and grad_phi (optional) is the gradient with respect to the
- * computed values.  cgtp_conv_double_backward takes phi = NULL and v_phi = NULL: the radial
- * direction is phi'(|r|) (r-hat . v_r) and its gg_edge_vec / gg_pos include the chain through
- * phi(r) and the basis' second derivative; the triple backward keeps phi as an input
+ * computed values.  cgtp_conv_double_backward (both modes) takes phi = NULL and v_phi = NULL: the
+ * radial direction is phi'(|r|) (r-hat . v_r) and its gg_edge_vec / gg_pos include the chain
+ * through phi(r) and the basis' second derivative; the triple backward keeps phi as an input
  * (UNSUPPORTED with a radial kind).  Call before the plan compiles kernels (UNSUPPORTED
  * afterwards).  INVALID_ARG for an unknown kind, r_cut <= 0, or kind 2 with K < 2. */
 cgtp_status_t cgtp_plan_set_radial(cgtp_plan_t plan, int kind, double r_cut);
@@ -195,7 +195,7 @@ cgtp_status_t cgtp_graph_destroy(cgtp_graph_t g);
  * values and 2 N int32 source-CSR bounds; never O(E x N_w).  A graph whose rows do not fit is
  * processed in receiver chunks; the receivers per chunk are also capped so that the grad_A
  * partial slots stay inside the budget at low in-degree.  The fully connected double backward
- * adds E x K values (a zero phi direction when v_phi is NULL).  UNSUPPORTED for the triple
+ * adds E x K values (a zero phi direction when v_phi is NULL; 4 E x K + E x 3 with a radial kind).  UNSUPPORTED for the triple
  * backward of a fully connected plan. */
 cgtp_status_t cgtp_workspace_size(cgtp_plan_t plan, cgtp_graph_t g, cgtp_op_t op, size_t* bytes);
 
@@ -289,7 +289,9 @@ cgtp_status_t cgtp_conv_backward_with_state(cgtp_plan_t plan, cgtp_graph_t g, co
  * gradient with respect to the computed radial values.  Fully connected mode: evaluated by
  * linearity from the streamed first-order passes (Sobek Eqs. 37-39: m-dot = S-dot A + S A-dot,
  * Sbar-dot = mbar A-dot^T, A-bar-dot = S-dot^T mbar, and the edge and source passes with one
- * operand replaced by its direction), with phi as an input (UNSUPPORTED with a radial kind). */
+ * operand replaced by its direction); with a radial kind it runs on the plan's twin without a
+ * basis, phi and phi-dot materialised per edge in the workspace (E x K each, plus E x K for the
+ * gradient in phi and the first-order phi-bar), and adds the radial terms of gg_edge_vec. */
 cgtp_status_t cgtp_conv_double_backward(cgtp_plan_t plan, cgtp_graph_t g, const void* x, const void* pos,
                                         const void* shift, const void* phi, const void* A,
                                         const void* grad_out, const void* v_x, const void* v_pos,

@@ -125,11 +125,14 @@ NARROW16 = dict(irreps_in="16x0e+16x1o+16x2e", irreps_sh="1x0e+1x1o+1x2e+1x3o",
     (2, SMALL_L3, "float32"),
     (1, NARROW16, "float32"),
     (2, None, "float64"),
+    (2, RAGGED_UVW, "float64"),
+    (1, RAGGED_UVW, "float64"),
+    (1, RAGGED_UVW, "float32"),
 ])
 def test_fused_radial_double_backward(kind, ov, dtype):
     """Double backward with phi computed from |r| in the kernels: every output against the oracle
     (phi-input double backward with phidot = phi'(|r|) r-hat.v, plus the chain through phi and
-    the curvature of the basis on the edge vector)."""
+    the curvature of the basis on the edge vector); channelwise and fully connected plans."""
     from tests.gpu_helpers import GpuCase, TOL, rel_err
     from tests.oracle_helpers import effective_edge_direction, make_directions
     case = make_case(1, irreps_override=ov, dtype=dtype)
@@ -162,3 +165,25 @@ def test_fused_radial_double_backward_argument_rules():
     with pytest.raises(_lib.CgtpError) as e:   # and so must v_phi
         g.conv.double_backward(g.x, g.pos, g.shift, None, g.A, g.grad_out, v_phi=g.phi)
     assert e.value.status == 1
+
+
+def test_fused_radial_double_backward_uvw_config4_irreps():
+    """Fully connected 64 x (0e, 1o, 2e), SH l <= 2, 8 Bessel functions, fp32, 300 atoms: every
+    output against the oracle."""
+    from tests.gpu_helpers import GpuCase, TOL, rel_err
+    from tests.oracle_helpers import effective_edge_direction, make_directions
+    case = make_case(4, n_nodes=300)
+    rc = case.raw.spec["rc"]
+    dirs = make_directions(case)
+    dirs.pop("v_phi")
+    g = GpuCase(case)
+    g.plan.set_radial(1, rc)
+    dev = {k: torch.tensor(v, dtype=torch.float32, device="cuda").contiguous() for k, v in dirs.items()}
+    got = g.conv.double_backward(g.x, g.pos, g.shift, None, g.A, g.grad_out, **dev)
+    v_e = effective_edge_direction(case, dirs["v_edge_vec"], dirs["v_pos"])
+    ref = radial.double_backward(1, rc, case.problem, case.x, case.edge_vec, case.recv, case.send, case.A,
+                                 case.grad_out, v_x=dirs["v_x"], v_e=v_e, v_A=dirs["v_A"], n_nodes=case.n_nodes)
+    for k in ("x", "pos", "edge_vec", "phi", "A", "grad_out"):
+        err = rel_err(got[k].cpu().numpy()[:len(ref[k])], ref[k].numpy())
+        print(f"uvw config-4 irreps radial double backward {k}: rel err {err:.3e}", flush=True)
+        assert err <= TOL["float32"], k

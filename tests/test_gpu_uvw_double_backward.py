@@ -94,13 +94,3 @@ def test_uvw_double_backward_config4_full_size_sampled():
         err = rel_err(a, b)
         print(f"uvw config 4 sampled gg {k}: rel err {err:.3e}", flush=True)
         assert err <= TOL["float32"], (k, err)
-
-
-def test_uvw_double_backward_refuses_radial_plans():
-    from clebsch_gordan_tensor_receiver_amd import _lib
-    case = make_case(1, irreps_override=RAGGED, dtype="float64")
-    g = _gpu(case)
-    g.plan.set_radial(2, case.raw.spec["rc"])
-    with pytest.raises(_lib.CgtpError) as e:
-        g.conv.double_backward(g.x, g.pos, g.shift, None, g.A, g.grad_out)
-    assert e.value.status == 2
