@@ -127,3 +127,95 @@ def test_single_atom_periodic_images():
             assert float(np.abs(got[k].cpu().numpy()).max()) <= 1e-12
         else:
             assert err <= TOL["float64"], k
+
+
+UVW_IRREPS = dict(irreps_in="4x0e+3x1o+2x2e", irreps_sh="1x0e+1x1o+1x2e", irreps_out="3x0e+2x1o+5x2e")
+
+
+def _dbl_inputs(mode, n, recv, send, K, seed):
+    irr = IRREPS if mode == "uvu" else UVW_IRREPS
+    g = np.random.default_rng(seed)
+    prob = make_problem(irr["irreps_in"], irr["irreps_sh"], irr["irreps_out"], mode)
+    E = len(recv)
+    d = dict(x=g.normal(size=(n, prob.c_in)), pos=g.uniform(0, 4, size=(n, 3)), phi=g.normal(size=(E, K)),
+             A=g.normal(size=(K, prob.n_weights)) / np.sqrt(K), grad_out=g.normal(size=(n, prob.c_out)),
+             v_x=g.normal(size=(n, prob.c_in)), v_pos=g.normal(size=(n, 3)), v_edge_vec=g.normal(size=(E, 3)),
+             v_phi=g.normal(size=(E, K)), v_A=g.normal(size=(K, prob.n_weights)))
+    return irr, prob, d
+
+
+def _dbl_run(mode, irr, n, recv, send, d, K, radial=0, rc=3.0):
+    from clebsch_gordan_tensor_receiver_amd import _lib
+    plan = _lib.Plan(irr["irreps_in"], irr["irreps_sh"], irr["irreps_out"], mode, "float64", K)
+    if radial:
+        plan.set_radial(radial, rc)
+    graph = _lib.Graph(n, np.asarray(recv, np.int32), np.asarray(send, np.int32))
+    perm = graph.perm
+    conv_ = _lib.Convolution(plan, graph)
+    dev = dict(dtype=torch.float64, device="cuda")
+    E = len(recv)
+    edge = lambda a, w: torch.tensor(a[perm] if E else np.zeros((1, w)), **dev).contiguous()  # noqa: E731
+    t = {k: torch.tensor(d[k], **dev) for k in ("x", "pos", "A", "grad_out", "v_x", "v_pos", "v_A")}
+    phi = None if radial else edge(d["phi"], K)
+    v_phi = None if radial else edge(d["v_phi"], K)
+    gg = conv_.double_backward(t["x"], t["pos"], torch.zeros((max(E, 1), 3), **dev), phi, t["A"], t["grad_out"],
+                               v_x=t["v_x"], v_pos=t["v_pos"], v_edge_vec=edge(d["v_edge_vec"], 3), v_phi=v_phi,
+                               v_A=t["v_A"])
+    return perm, gg
+
+
+@pytest.mark.parametrize("mode,radial", [("uvu", 0), ("uvw", 0), ("uvu", 1), ("uvw", 2)])
+def test_double_backward_empty_edge_list(mode, radial):
+    K, n = 4, 5
+    irr, prob, d = _dbl_inputs(mode, n, [], [], K, seed=14)
+    _, gg = _dbl_run(mode, irr, n, [], [], d, K, radial)
+    for k in ("x", "pos", "A", "grad_out"):
+        assert float(gg[k].abs().max()) == 0.0, k
+
+
+@pytest.mark.parametrize("mode,radial", [("uvu", 0), ("uvw", 0), ("uvw", 1)])
+def test_double_backward_receivers_without_edges(mode, radial):
+    # Receivers 0, 5 and 9 have no incoming edges and 9 sends none: every output against the oracle.
+    from oracle import radial as oradial
+    from tests.gpu_helpers import TOL, rel_err
+    K, n, rc = 4, 10, 6.0
+    rng = np.random.default_rng(15)
+    pairs = [(i, j) for i in range(n) for j in range(n - 1) if i != j and i not in (0, 5, 9) and rng.random() < 0.5]
+    recv = np.array([p[0] for p in pairs], np.int32)
+    send = np.array([p[1] for p in pairs], np.int32)
+    irr, prob, d = _dbl_inputs(mode, n, recv, send, K, seed=16)
+    perm, gg = _dbl_run(mode, irr, n, recv, send, d, K, radial, rc)
+    r, s = recv[perm], send[perm]
+    ev = conv.edge_vectors(d["pos"], np.zeros((len(r), 3)), r, s)
+    v_e = d["v_edge_vec"][perm] + d["v_pos"][s] - d["v_pos"][r]
+    if radial:
+        ref = oradial.double_backward(radial, rc, prob, d["x"], ev, r, s, d["A"], d["grad_out"], v_x=d["v_x"],
+                                      v_e=v_e, v_A=d["v_A"], n_nodes=n)
+    else:
+        ref = conv.double_backward(prob, d["x"], ev, r, s, d["phi"][perm], d["A"], d["grad_out"], v_x=d["v_x"],
+                                   v_e=v_e, v_phi=d["v_phi"][perm], v_A=d["v_A"], n_nodes=n)
+    for k in ("x", "pos", "edge_vec", "phi", "A", "grad_out"):
+        err = rel_err(gg[k].cpu().numpy()[:len(ref[k])], ref[k].numpy())
+        print(f"{mode} radial {radial} isolated receivers gg {k}: {err:.3e}", flush=True)
+        assert err <= TOL["float64"], k
+    assert float(gg["grad_out"][[0, 5, 9]].abs().max()) == 0.0
+
+
+def test_triple_backward_empty_edge_list():
+    from clebsch_gordan_tensor_receiver_amd import _lib
+    K, n = 4, 5
+    plan = _plan(K=K)
+    graph = _lib.Graph(n, np.zeros(0, np.int32), np.zeros(0, np.int32))
+    conv_ = _lib.Convolution(plan, graph)
+    info = plan.info
+    g = torch.Generator().manual_seed(17)
+    dev = dict(dtype=torch.float64, device="cuda")
+    r = lambda *sh: torch.randn(*sh, generator=g, dtype=torch.float64).to("cuda")  # noqa: E731
+    inputs = dict(x=r(n, info["c_in"]), Y=torch.zeros((1, info["sh_dim"]), **dev), phi=torch.zeros((1, K), **dev),
+                  A=r(K, info["n_weights"]), grad_out=r(n, info["c_out"]), v_x=r(n, info["c_in"]),
+                  v_A=r(K, info["n_weights"]), q_x=r(n, info["c_in"]), q_grad_out=r(n, info["c_out"]))
+    outs = conv_.triple_backward(inputs)
+    for k, v in outs.items():
+        if k in ("Y", "phi", "v_Y", "v_phi"):
+            continue   # edge-sized outputs of an empty edge list hold nothing
+        assert float(v.abs().max()) == 0.0, k
