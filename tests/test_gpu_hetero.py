@@ -113,3 +113,27 @@ def test_layout_convert_matches_block_transpose(dtype):
         torch.cuda.synchronize()
         assert np.array_equal(mid.cpu().numpy(), want.astype(src.cpu().numpy().dtype))
         assert np.array_equal(back.cpu().numpy(), src.cpu().numpy())
+
+
+@pytest.mark.parametrize("profile", ["C1", "C5", "C7", "C9"])
+def test_lunatp_profiles_double_backward(profile):
+    """Double backward on LunaTP's mixed-multiplicity cases (Appendix A.1; the page quotes its
+    largest double-backward gain on C9), fp32 on the 64-atom graph: every output against the
+    oracle."""
+    from tests.test_gpu_double_backward import _compare as dcompare, _oracle as doracle
+    from workloads.sweeps import lunatp_profile
+    case = make_case(1, irreps_override=lunatp_profile(profile), dtype="float32")
+    dirs = make_directions(case)
+    dcompare(_gpu(case).double_backward(dirs), doracle(case, dirs), "float32", label=f"{profile}")
+
+
+@pytest.mark.parametrize("profile", ["C1", "C5", "C7", "C9"])
+def test_lunatp_profiles_triple_backward(profile):
+    """Third-order derivative (LunaTP Appendix F, Algorithm 4) on the mixed-multiplicity cases,
+    fp32 on the 64-atom graph: every output against the oracle."""
+    from tests.test_gpu_triple_backward import _compare as tcompare, _gpu_run, _inputs, _oracle as toracle
+    from workloads.sweeps import lunatp_profile
+    case = make_case(1, irreps_override=lunatp_profile(profile), dtype="float32")
+    h = _inputs(case)
+    _, got = _gpu_run(case, h)
+    tcompare(got, toracle(case, h), "float32", f"{profile} triple")
