@@ -31,6 +31,7 @@
 #include <cstdio>
 #include <functional>
 #include <map>
+#include <memory>
 #include <numeric>
 #include <set>
 #include <sstream>
@@ -158,6 +159,22 @@ void prelude(Out& o, const Plan& p, bool dual, bool reduce) {
     o.line("struct __attribute__((aligned(16))) V4 { real a, b; };  // 16-byte store unit");
   else
     o.line("struct __attribute__((aligned(16))) V4 { real a, b, c, d; };  // 16-byte store unit");
+  if (!f64) {
+    // acc += c[lane r of the row] * x and d = c[lane r of the row] * x: the coefficient operand
+    // read from lane r of each 16-lane row (DPP row_newbcast), so that each row of a wave can take
+    // the coefficients of its own edge from one register.  The register read this way always
+    // comes from a memory load, never from a VALU result just before it.
+    o.line("#define BFMA(acc, c, x, r) asm(\"v_fmac_f32_dpp %0, %1, %2 row_newbcast:\" #r \" row_mask:0xf bank_mask:0xf\""
+           " : \"+v\"(acc) : \"v\"(c), \"v\"(x))");
+    o.line("#define BMUL(d, c, x, r) asm(\"v_mul_f32_dpp %0, %1, %2 row_newbcast:\" #r \" row_mask:0xf bank_mask:0xf\""
+           " : \"=v\"(d) : \"v\"(c), \"v\"(x))");
+    // 64 consecutive coefficients of a row from `base` on, four per lane of each 16-lane row
+    // (lane r holds base + 4r .. 4r + 3); lanes past the row's end `lim` (a multiple of 4) read
+    // its last four values instead, which no coefficient reference uses.
+    o.line("DEV V4 gchunk(const real* __restrict__ g, int base, int lim, int r16) {");
+    o.line("  return *(const V4*)(g + min(base + 4 * r16, lim - 4));");
+    o.line("}");
+  }
   o.line("extern \"C\" __global__ void __launch_bounds__(256) cgtp_fill_zero(real* __restrict__ p, i64 n) {");
   o.line("  i64 k = (i64)blockIdx.x * 256 + threadIdx.x;");
   o.line("  if (k < n) p[k] = R(0);");
@@ -373,23 +390,70 @@ void emit_w(Out& o, const Plan& p, int pi) {
   for (int q = 1; q < p.K; ++q) o.line(F("w%d = fma(f%d, a%d_%d, w%d);", pi, q, pi, q, pi));
 }
 
+// Statement `dst (=|+=) G[idx] * xop` with G[idx] taken from its chunk by row broadcast; the
+// chunk is loaded on first use.
+std::vector<int> chunks_of(const std::vector<std::pair<int, int>>& ranges) {
+  std::vector<int> out;
+  for (auto& r : ranges)
+    for (int c = r.first / 64; r.second > r.first && c <= (r.second - 1) / 64; ++c)
+      if (std::find(out.begin(), out.end(), c) == out.end()) out.push_back(c);
+  return out;
+}
+
+std::vector<std::pair<int, int>> g_ranges(const Plan& p, const std::vector<int>& paths) {
+  std::vector<std::pair<int, int>> v;
+  for (int pi : paths) v.push_back({p.paths[pi].g_off, p.paths[pi].g_off + int(p.paths[pi].gpairs.size())});
+  return v;
+}
+
+std::string bcast_term(Out& o, RowChunks& rc, int idx, const std::string& dst, const std::string& xop, bool first) {
+  const int c = idx / 64, r = (idx % 64) / 4;
+  auto load = [&](int k) {
+    if (rc.loaded.insert(k).second)
+      o.line(F("const V4 gc%s%d = gchunk(%s, %d, %d, r16_);", rc.tag.c_str(), k, rc.row.c_str(), 64 * k, rc.lim));
+  };
+  if (!rc.loaded.count(c)) {
+    load(c);
+    auto it = std::find(rc.order.begin(), rc.order.end(), c);
+    if (it != rc.order.end()) {
+      bool ahead = false;
+      for (int n = 1; n <= kChunkAhead && it + n < rc.order.end(); ++n)
+        if (!rc.loaded.count(*(it + n))) {
+          load(*(it + n));
+          ahead = true;
+        }
+      if (ahead) o.line("__builtin_amdgcn_sched_barrier(0);");
+    }
+  }
+  const std::string reg = F("gc%s%d.%c", rc.tag.c_str(), c, "abcd"[idx % 4]);
+  if (first) return F("real %s; BMUL(%s, %s, %s, %d);", dst.c_str(), dst.c_str(), reg.c_str(), xop.c_str(), r);
+  return F("BFMA(%s, %s, %s, %d);", dst.c_str(), reg.c_str(), xop.c_str(), r);
+}
+
 // acc<m3> += w * sum_m1 G[m1,m3] x[m1] for path pi, choosing where to apply w by cost.  The
-// accumulators are named <acc><m3>.
-void emit_path_accumulate(Out& o, const Plan& p, int pi, const std::string& acc = "acc") {
+// accumulators are named <acc><m3>.  With `rc` the coefficients come by row broadcast from
+// per-row chunks (each 16-lane row of the wave on its own edge).
+void emit_path_accumulate(Out& o, const Plan& p, int pi, const std::string& acc = "acc", RowChunks* rc = nullptr) {
   const Path& P = p.paths[pi];
   const int d1 = 2 * P.l1 + 1, d3 = 2 * P.l3 + 1;
   const char* A = acc.c_str();
   auto G = [&](size_t t) { return gref(p, pi, int(t), "g", "", false); };
   if (d1 <= d3) {
     for (int m = 0; m < d1; ++m) o.line(F("const real s%d_%d = w%d * x%d_%d;", pi, m, pi, P.i_in, m));
-    for (size_t t = 0; t < P.gpairs.size(); ++t)
-      o.line(F("%s%d = fma(%s, s%d_%d, %s%d);", A, P.gpairs[t].m3, G(t).c_str(), pi, P.gpairs[t].m1, A,
-               P.gpairs[t].m3));
+    for (size_t t = 0; t < P.gpairs.size(); ++t) {
+      const int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3;
+      if (rc)
+        o.line(bcast_term(o, *rc, P.g_off + int(t), F("%s%d", A, m3), F("s%d_%d", pi, m1), false));
+      else
+        o.line(F("%s%d = fma(%s, s%d_%d, %s%d);", A, m3, G(t).c_str(), pi, m1, A, m3));
+    }
   } else {
     std::vector<bool> started(d3, false);
     for (size_t t = 0; t < P.gpairs.size(); ++t) {
       int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3;
-      if (!started[m3])
+      if (rc)
+        o.line(bcast_term(o, *rc, P.g_off + int(t), F("t%d_%d", pi, m3), F("x%d_%d", P.i_in, m1), !started[m3]));
+      else if (!started[m3])
         o.line(F("real t%d_%d = %s * x%d_%d;", pi, m3, G(t).c_str(), P.i_in, m1));
       else
         o.line(F("t%d_%d = fma(%s, x%d_%d, t%d_%d);", pi, m3, G(t).c_str(), P.i_in, m1, pi, m3));
@@ -470,7 +534,9 @@ void emit_recv_edge_loop(Out& o, const Plan& p, const std::vector<int>& blocks, 
     xrow("x", "j", "const real ");
     o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", row_stride));
     o.line("const real* __restrict__ ph = " + phi_ptr(p, "e", "g") + ";");
-    for (int q = 0; q < p.K; ++q) o.line(F("const real f%d = ok_ ? ph[%d] : R(0);", q, q));
+    // Loaded unconditionally (e is a valid edge in every lane) and then masked: a load under the
+    // condition would become one branch per value.
+    for (int q = 0; q < p.K; ++q) o.line(F("const real fl%d_ = ph[%d], f%d = ok_ ? fl%d_ : R(0);", q, q, q, q));
     body();
     o.close();
     o.close();
@@ -572,9 +638,19 @@ void emit_wave_combine_names(Out& o, const std::vector<std::string>& names, int 
 // idle half of the lanes), so blocks above 16 channels keep one edge per wave.
 int edges_per_wave(int mul) { return mul <= 16 ? 4 : 1; }
 
+// Edges per wave step of the channelwise passes that read coefficient rows per edge: in fp32 each
+// 16-lane row takes its coefficients from its own row chunk by row broadcast (one 16-byte load
+// per lane serves 64 coefficients), so blocks of at most 32 channels share the wave between 2 or
+// 4 edges.  Measured at l <= 6 with 32 channels: forward 7.2 -> 4.1 ms.
+int bcast_edges_per_wave(const Plan& p, int mul) {
+  if (p.dtype == CGTP_F64) return edges_per_wave(mul);
+  return mul <= 16 ? 4 : mul <= 32 ? 2 : 1;
+}
+
 void emit_fwd_task(Out& o, const Plan& p, int ti, const Task& T, int row_stride = 0, bool accumulate = false) {
   const int MUL = p.out[p.paths[T.paths[0]].i_out].mul;
-  const int nE = edges_per_wave(MUL), gsz = 64 / nE;
+  const int nE = bcast_edges_per_wave(p, MUL), gsz = 64 / nE;
+  const bool bcast = nE > 1 && p.dtype != CGTP_F64;
   const std::vector<int> obs = out_blocks_of(p, T.paths);
   o.open(F("DEV void fwd_t%d(%s, real* sm, int node, int e_base)", ti, kFwdArgs));
   o.line(F("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) %% %d;",
@@ -585,6 +661,7 @@ void emit_fwd_task(Out& o, const Plan& p, int ti, const Task& T, int row_stride 
   else
     o.line(F("const int u = %d + lane;", T.cb * 64));
   o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
+  if (bcast) o.line("const int r16_ = lane & 15;");
   std::vector<std::string> accs;
   for (int ob : obs)
     for (int m = 0; m < p.out[ob].dim(); ++m) {
@@ -596,9 +673,10 @@ void emit_fwd_task(Out& o, const Plan& p, int ti, const Task& T, int row_stride 
     o.open("");
     emit_a_loads(o, p, S);
     emit_recv_edge_loop(o, p, in_blocks_of(p, S), "w", std::to_string(fwd_split(p)), [&] {
+      RowChunks rc{row_stride > 0 ? row_stride : p.g_stride, "g", "", chunks_of(g_ranges(p, S))};
       for (int pi : S) {
         emit_w(o, p, pi);
-        emit_path_accumulate(o, p, pi, F("acc%d_", p.paths[pi].i_out));
+        emit_path_accumulate(o, p, pi, F("acc%d_", p.paths[pi].i_out), bcast ? &rc : nullptr);
       }
     }, false, row_stride, nE);
     o.close();
@@ -804,9 +882,12 @@ void emit_bwd_recv_task(Out& o, const Plan& p, int ti, const Task& T, int col_of
   // half) instead of the 64-lane transposition, and each group stores its own edge's columns.  The
   // rows this pass reads per edge are short (Y, or large paths' coefficients already read per lane),
   // so unlike the forward the 32-channel case gains too.
+  // In fp32 each row takes its edge's coefficients and Y values by row broadcast.
   const int nE = MUL <= 16 ? 4 : MUL <= 32 ? 2 : 1, gsz = 64 / nE;
+  const bool bcast = nE > 1 && p.dtype != CGTP_F64;
   o.open(F("DEV void bwr_t%d(%s, real* sm, int node, int e_base, int eps, int slot, int acc)", ti, kRecvArgs));
   o.line("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
+  if (bcast) o.line("const int r16_ = lane & 15;");
   emit_vz(o, p);
   if (nE > 1)
     o.line(F("const int u = lane %% %d;", gsz));
@@ -841,6 +922,13 @@ void emit_bwd_recv_task(Out& o, const Plan& p, int ti, const Task& T, int col_of
   auto body = [&] {
     for (int v = 0; v < V; ++v) o.line(F("real v%d = R(0);", v));
     int ai = 0;
+    std::vector<std::pair<int, int>> ranges;   // Y values of folded paths, G rows of the others
+    for (int pi : T.paths) {
+      const Path& P = p.paths[pi];
+      if (folded(P)) ranges.push_back({yoff + P.l2 * P.l2, yoff + (P.l2 + 1) * (P.l2 + 1)});
+      else ranges.push_back({P.g_off, P.g_off + int(P.gpairs.size())});
+    }
+    RowChunks rc{bwd_row_stride(p), "g", "", chunks_of(ranges)};
     for (int pi : T.paths) {
       const Path& P = p.paths[pi];
       const int s = K + P.l2 * P.l2;  // Y-bar slot of this path's SH block
@@ -857,7 +945,8 @@ void emit_bwd_recv_task(Out& o, const Plan& p, int ti, const Task& T, int col_of
         bool first = true;
         for (int m = 0; m < d2; ++m)
           if (qs[m]) {
-            if (first) o.line(F("real h%d = g[%d] * q%d_%d;", pi, yoff + P.l2 * P.l2 + m, pi, m));
+            if (bcast) o.line(bcast_term(o, rc, yoff + P.l2 * P.l2 + m, F("h%d", pi), F("q%d_%d", pi, m), first));
+            else if (first) o.line(F("real h%d = g[%d] * q%d_%d;", pi, yoff + P.l2 * P.l2 + m, pi, m));
             else o.line(F("h%d = fma(g[%d], q%d_%d, h%d);", pi, yoff + P.l2 * P.l2 + m, pi, m, pi));
             first = false;
           }
@@ -870,11 +959,17 @@ void emit_bwd_recv_task(Out& o, const Plan& p, int ti, const Task& T, int col_of
         continue;
       }
       const int d3 = 2 * P.l3 + 1, ob = P.i_out;
-      GStream gs(o, p, pi, "g", "", p.vec_g && kRecvStreamLarge);
+      std::unique_ptr<GStream> gs;
+      if (!bcast) gs.reset(new GStream(o, p, pi, "g", "", p.vec_g && kRecvStreamLarge));
       std::vector<bool> started(d3, false);
       for (size_t t = 0; t < P.gpairs.size(); ++t) {
         int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3;
-        const std::string G = gs.ref(int(t));
+        if (bcast) {
+          o.line(bcast_term(o, rc, P.g_off + int(t), F("t%d_%d", pi, m3), F("x%d_%d", P.i_in, m1), !started[m3]));
+          started[m3] = true;
+          continue;
+        }
+        const std::string G = gs->ref(int(t));
         if (!started[m3])
           o.line(F("real t%d_%d = %s * x%d_%d;", pi, m3, G.c_str(), P.i_in, m1));
         else
@@ -994,8 +1089,9 @@ const char* kSrcArgs =
 // receivers' mbar rows of the next edge are loaded one edge ahead.
 void emit_bwd_src_task(Out& o, const Plan& p, int ti, const Task& T) {
   const int MUL = p.in[p.paths[T.paths[0]].i_in].mul, K = p.K;
-  // Blocks of at most 16 channels: 4 out-edges per wave step, one per 16-lane group (as the forward).
-  const int nE = edges_per_wave(MUL), gsz = 64 / nE;
+  // Blocks of at most 32 channels: 2 or 4 out-edges per wave step, one per lane group (as the forward).
+  const int nE = bcast_edges_per_wave(p, MUL), gsz = 64 / nE;
+  const bool bcast = nE > 1 && p.dtype != CGTP_F64;
   const std::vector<int> ibs = in_blocks_of(p, T.paths);
   o.open(F("DEV void bws_t%d(%s, real* sm, int node, int e_base, int accumulate)", ti, kSrcArgs));
   o.line(F("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) %% %d;",
@@ -1006,6 +1102,7 @@ void emit_bwd_src_task(Out& o, const Plan& p, int ti, const Task& T) {
   else
     o.line(F("const int u = %d + lane;", T.cb * 64));
   o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
+  if (bcast) o.line("const int r16_ = lane & 15;");
   std::vector<std::string> accs;
   for (int ib : ibs)
     for (int m = 0; m < p.in[ib].dim(); ++m) {
@@ -1045,7 +1142,9 @@ void emit_bwd_src_task(Out& o, const Plan& p, int ti, const Task& T) {
   o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", bwd_row_stride(p)));
   o.line("const real* __restrict__ ph = " + phi_ptr(p, "e", "g") + ";");
   for (int q = 0; q < K; ++q)
-    o.line(nE > 1 ? F("const real f%d = ok_ ? ph[%d] : R(0);", q, q) : F("const real f%d = ph[%d];", q, q));
+    o.line(nE > 1 ? F("const real fl%d_ = ph[%d], f%d = ok_ ? fl%d_ : R(0);", q, q, q, q)
+                  : F("const real f%d = ph[%d];", q, q));
+  RowChunks rc{bwd_row_stride(p), "g", "", chunks_of(g_ranges(p, S))};
   for (int pi : S) {
     const Path& P = p.paths[pi];
     const int d1 = 2 * P.l1 + 1, d3 = 2 * P.l3 + 1, ib = P.i_in;
@@ -1053,14 +1152,20 @@ void emit_bwd_src_task(Out& o, const Plan& p, int ti, const Task& T) {
     auto G = [&](size_t t) { return gref(p, pi, int(t), "g", "", false); };
     if (d3 <= d1) {
       for (int m = 0; m < d3; ++m) o.line(F("const real s%d_%d = w%d * mb%d_%d;", pi, m, pi, P.i_out, m));
-      for (size_t t = 0; t < P.gpairs.size(); ++t)
-        o.line(F("acc%d_%d = fma(%s, s%d_%d, acc%d_%d);", ib, P.gpairs[t].m1, G(t).c_str(), pi,
-                 P.gpairs[t].m3, ib, P.gpairs[t].m1));
+      for (size_t t = 0; t < P.gpairs.size(); ++t) {
+        const int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3;
+        if (bcast)
+          o.line(bcast_term(o, rc, P.g_off + int(t), F("acc%d_%d", ib, m1), F("s%d_%d", pi, m3), false));
+        else
+          o.line(F("acc%d_%d = fma(%s, s%d_%d, acc%d_%d);", ib, m1, G(t).c_str(), pi, m3, ib, m1));
+      }
     } else {
       std::vector<bool> started(d1, false);
       for (size_t t = 0; t < P.gpairs.size(); ++t) {
         int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3;
-        if (!started[m1])
+        if (bcast)
+          o.line(bcast_term(o, rc, P.g_off + int(t), F("b%d_%d", pi, m1), F("mb%d_%d", P.i_out, m3), !started[m1]));
+        else if (!started[m1])
           o.line(F("real b%d_%d = %s * mb%d_%d;", pi, m1, G(t).c_str(), P.i_out, m3));
         else
           o.line(F("b%d_%d = fma(%s, mb%d_%d, b%d_%d);", pi, m1, G(t).c_str(), P.i_out, m3, pi, m1));

@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <functional>
 #include <sstream>
+#include <set>
 #include <string>
 #include <utility>
 #include <vector>
@@ -76,6 +77,28 @@ class GStream {
   bool vec_;
   std::string row_, tag_;
 };
+// Coefficient rows read by row broadcast (fp32, one edge per 16-lane row, `r16_` = lane & 15 in
+// scope): the 64-value chunks of row pointer `row` loaded so far (gchunk, one 16-byte load per
+// lane), named gc<tag><chunk>; `lim` is the row length in values.  `order` lists the chunks in
+// the order the body first uses them (chunks_of): when a chunk is first used, the next
+// kChunkAhead chunks of the list are loaded too, ahead of a scheduling barrier, so that their
+// latency overlaps the arithmetic on the chunks before them.
+constexpr int kChunkAhead = 2;
+struct RowChunks {
+  int lim;
+  std::string row = "g", tag = "";
+  std::vector<int> order = {};
+  std::set<int> loaded = {};
+};
+// Chunks (64 values) touched by the value ranges [first, second) of a row, in order of first use.
+std::vector<int> chunks_of(const std::vector<std::pair<int, int>>& ranges);
+// Value ranges of the coefficient rows of the given paths, in path order.
+std::vector<std::pair<int, int>> g_ranges(const Plan& p, const std::vector<int>& paths);
+// Statement `dst = G[idx] * xop` (first) or `dst += G[idx] * xop`, G[idx] read from its chunk by
+// row broadcast; the chunk (and the kChunkAhead after it) is loaded on its first use.
+std::string bcast_term(Out& o, RowChunks& rc, int idx, const std::string& dst, const std::string& xop, bool first);
+// Edges per wave step of the channelwise passes that read coefficient rows per edge.
+int bcast_edges_per_wave(const Plan& p, int mul);
 void prelude(Out& o, const Plan& p, bool dual, bool reduce);
 // Radial values of the current edge (the phi input or the edge's G row), and the radial part of
 // the edge-vector gradient (sr; needs rr = |r| and phi-bar registers <pb>0..K-1 in scope).

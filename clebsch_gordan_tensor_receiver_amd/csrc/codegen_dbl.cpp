@@ -193,7 +193,8 @@ const char* kDArgs =
 // and Gdot rows.  Body sees e, g (G row), gd (Gdot row), f<q>, fd<q>, x<b>_<m>, xd<b>_<m>.
 // nE > 1 (2 or 4): lane group h_ (64 / nE lanes, `h_` in scope) takes edge eb + h_ of each step
 // of nE edges; e, j and the row pointers are then per lane, and a group past the last edge reads
-// the step's first edge with zero phi and phi-dot (`ok_` false).
+// the step's first edge with zero phi and phi-dot (`ok_` false; the values are loaded
+// unconditionally and masked, since a load under the condition becomes a branch per value).
 void emit_dedge_loop(Out& o, const Plan& p, const std::vector<int>& blocks, const std::function<void()>& body,
                      int nE = 1) {
   if (nE > 1) {
@@ -209,7 +210,8 @@ void emit_dedge_loop(Out& o, const Plan& p, const std::vector<int>& blocks, cons
   o.line(F("const real* __restrict__ gd = g + %d;", p.g_stride));
   emit_phi_rows(o, p);
   for (int q = 0; q < p.K; ++q)
-    o.line(F("const real f%d = ok_ ? ph[%d] : R(0), fd%d = ok_ ? sphi * phd[%d] : R(0);", q, q, q, q));
+    o.line(F("const real fl%d_ = ph[%d], fdl%d_ = phd[%d];", q, q, q, q) +
+           F(" const real f%d = ok_ ? fl%d_ : R(0), fd%d = ok_ ? sphi * fdl%d_ : R(0);", q, q, q, q));
   for (int b : blocks) {
     const Block& B = p.in[b];
     for (int m = 0; m < B.dim(); ++m) {
@@ -241,11 +243,23 @@ void emit_wwd(Out& o, const Plan& p, int pi) {
   }
 }
 
-// T[m3] = G x and Tdot[m3] = Gdot x + G xdot of path pi, names t<pi>_<m3>, td<pi>_<m3>.
-std::vector<bool> emit_t_td(Out& o, const Plan& p, int pi, int d3, bool stream) {
+// T[m3] = G x and Tdot[m3] = Gdot x + G xdot of path pi, names t<pi>_<m3>, td<pi>_<m3>.  With
+// `rc` the G and Gdot coefficients come by row broadcast from the chunks rc[0] (G) and rc[1] (Gdot).
+std::vector<bool> emit_t_td(Out& o, const Plan& p, int pi, int d3, bool stream, RowChunks* rc = nullptr) {
   const Path& P = p.paths[pi];
-  GStream gs(o, p, pi, "g", "", stream), gds(o, p, pi, "gd", "d", stream);
   std::vector<bool> started(d3, false);
+  if (rc) {
+    for (size_t t = 0; t < P.gpairs.size(); ++t) {
+      const int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3, idx = P.g_off + int(t);
+      const bool first = !started[m3];
+      o.line(bcast_term(o, rc[0], idx, F("t%d_%d", pi, m3), F("x%d_%d", P.i_in, m1), first));
+      o.line(bcast_term(o, rc[0], idx, F("td%d_%d", pi, m3), F("xd%d_%d", P.i_in, m1), first));
+      o.line(bcast_term(o, rc[1], idx, F("td%d_%d", pi, m3), F("x%d_%d", P.i_in, m1), false));
+      started[m3] = true;
+    }
+    return started;
+  }
+  GStream gs(o, p, pi, "g", "", stream), gds(o, p, pi, "gd", "d", stream);
   for (size_t t = 0; t < P.gpairs.size(); ++t) {
     int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3;
     const std::string G = gs.ref(int(t)), Gd = gds.ref(int(t));
@@ -267,9 +281,19 @@ std::vector<bool> emit_t_td(Out& o, const Plan& p, int pi, int d3, bool stream) 
 void emit_dfwd_task(Out& o, const Plan& p, int ti, const Task& T) {
   const Block& OB = p.out[T.group];
   const int d3 = OB.dim(), MUL = OB.mul;
+  // Blocks of at most 32 channels in fp32: 2 or 4 edges per wave step, one per lane group, with
+  // the G and Gdot coefficients by row broadcast; the groups' partial sums are added at the end.
+  const int nE = bcast_edges_per_wave(p, MUL), gsz = 64 / nE;
+  const bool bcast = nE > 1 && p.dtype != CGTP_F64;
   o.open(F("DEV void dfw_t%d(%s, int node, int e_base)", ti, kDArgs));
   emit_vz(o, p);
-  o.line(F("const int u = %d + (int)threadIdx.x;", T.cb * 64));
+  o.line("const int lane = (int)threadIdx.x & 63;");
+  if (nE > 1) {
+    o.line(F("const int u = lane %% %d, h_ = lane / %d;", gsz, gsz));
+    if (bcast) o.line("const int r16_ = lane & 15;");
+  } else {
+    o.line(F("const int u = %d + lane;", T.cb * 64));
+  }
   o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
   for (int m = 0; m < d3; ++m) o.line(F("real acc%d = R(0);", m));
   o.line("const int e0 = row_ptr[node], e1 = row_ptr[node + 1];");
@@ -277,16 +301,20 @@ void emit_dfwd_task(Out& o, const Plan& p, int ti, const Task& T) {
     o.open("");
     emit_da_loads(o, p, S);
     emit_dedge_loop(o, p, in_blocks_of(p, S), [&] {
+      const auto order = chunks_of(g_ranges(p, S));
+      RowChunks rc[2] = {{p.g_stride, "g", "", order}, {p.g_stride, "gd", "d", order}};
       for (int pi : S) {
         emit_wwd(o, p, pi);
-        auto started = emit_t_td(o, p, pi, d3, kDfwdStream);
+        auto started = emit_t_td(o, p, pi, d3, kDfwdStream, bcast ? rc : nullptr);
         for (int m = 0; m < d3; ++m)
           if (started[m]) o.line(F("acc%d = fma(wd%d, t%d_%d, fma(w%d, td%d_%d, acc%d));", m, pi, pi, m, pi, pi, m, m));
       }
-    });
+    }, nE);
     o.close();
   }
-  o.open(F("if (u < %d)", MUL));
+  for (int span = gsz; span < 64; span *= 2)
+    for (int m = 0; m < d3; ++m) o.line(F("acc%d += __shfl_xor(acc%d, %d);", m, m, span));
+  o.open(nE > 1 ? F("if (lane < %d && u < %d)", gsz, MUL) : F("if (u < %d)", MUL));
   o.line(F("real* __restrict__ dst = out + (i64)node * %d + %d + u;", p.c_out, OB.offset));
   for (int m = 0; m < d3; ++m) o.line(F("dst[%d] = acc%d;", m * MUL, m));
   o.close();
@@ -306,13 +334,17 @@ void emit_drecv_task(Out& o, const Plan& p, int ti, const Task& T, int col_off, 
   // With an in-kernel radial basis, K more columns: the first-order phi-bar (A h) of the task,
   // for the curvature of phi(|r|) in the edge-vector gradient.
   auto cb = [&](int q) { return K + 2 * ny + q; };
-  // Blocks of at most 16 channels: 4 edges per wave step.  (Two edges per step for 32-channel
-  // blocks measured slower: per-lane coefficient rows of G and G-dot cost the registers that the
-  // wave-uniform rows keep in scalar ones.)
-  const int nE = MUL <= 16 ? 4 : 1, gsz = 64 / nE;
+  // Blocks of at most 16 channels: 4 edges per wave step.  In fp64, 32-channel blocks keep one
+  // edge per step (two measured slower: per-lane coefficient rows of G and G-dot cost the
+  // registers that the wave-uniform rows keep in scalar ones); in fp32 the coefficients come by
+  // row broadcast and 32-channel blocks take 2 edges per step.
+  const bool f64 = p.dtype == CGTP_F64;
+  const int nE = f64 ? (MUL <= 16 ? 4 : 1) : bcast_edges_per_wave(p, MUL), gsz = 64 / nE;
+  const bool bcast = nE > 1 && !f64;
   o.open(F("DEV void drc_t%d(%s, real* sm, int node, int e_base, int eps, int slot)", ti, kDArgs));
   emit_vz(o, p);
   o.line("const int lane = (int)threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);");
+  if (bcast) o.line("const int r16_ = lane & 15;");
   if (nE > 1)
     o.line(F("const int u = lane %% %d, h_ = lane / %d;", gsz, gsz));
   else
@@ -328,11 +360,13 @@ void emit_drecv_task(Out& o, const Plan& p, int ti, const Task& T, int col_off, 
   emit_dedge_loop(o, p, in_blocks_of(p, T.paths), [&] {
     for (int v = 0; v < V; ++v) o.line(F("real v%d = R(0);", v));
     int ai = 0;
+    const auto order = chunks_of(g_ranges(p, T.paths));
+    RowChunks rc[2] = {{p.g_stride, "g", "", order}, {p.g_stride, "gd", "d", order}};
     for (int pi : T.paths) {
       const Path& P = p.paths[pi];
       const int y0 = P.l2 * P.l2;
       emit_wwd(o, p, pi);
-      auto started = emit_t_td(o, p, pi, d3, kDfwdStream);
+      auto started = emit_t_td(o, p, pi, d3, kDfwdStream, bcast ? rc : nullptr);
       bool first = true;
       for (int m = 0; m < d3; ++m)
         if (started[m]) {
@@ -379,7 +413,6 @@ void emit_drecv_task(Out& o, const Plan& p, int ti, const Task& T, int col_off, 
       return;
     }
     const int H = V / 2, Q = V / 4;
-    const bool f64 = p.dtype == CGTP_F64;
     std::vector<std::pair<std::string, std::string>> pr;
     for (int k = 0; k < H; ++k) pr.push_back({F("v%d", k), F("v%d", k + H)});
     emit_swaps(o, pr, 32, f64);
@@ -419,39 +452,70 @@ const char* kDSrcArgs =
 void emit_dsrc_task(Out& o, const Plan& p, int ti, const Task& T) {
   const Block& IB = p.in[T.group];
   const int d1 = IB.dim(), MUL = IB.mul, K = p.K;
+  // Blocks of at most 32 channels in fp32: 2 or 4 out-edges per wave step, one per lane group,
+  // with the G and Gdot coefficients by row broadcast; the groups' partial sums are added at the end.
+  const int nE = bcast_edges_per_wave(p, MUL), gsz = 64 / nE;
+  const bool bcast = nE > 1 && p.dtype != CGTP_F64;
   o.open(F("DEV void dsr_t%d(%s, int node, int e_base, int accumulate)", ti, kDSrcArgs));
   emit_vz(o, p);
-  o.line(F("const int u = %d + (int)threadIdx.x;", T.cb * 64));
+  o.line("const int lane = (int)threadIdx.x & 63;");
+  if (nE > 1) {
+    o.line(F("const int u = lane %% %d, h_ = lane / %d;", gsz, gsz));
+    if (bcast) o.line("const int r16_ = lane & 15;");
+  } else {
+    o.line(F("const int u = %d + lane;", T.cb * 64));
+  }
   o.line(F("const int uc = u < %d ? u : %d;", MUL, MUL - 1));
   for (int m = 0; m < d1; ++m) o.line(F("real acc%d = R(0);", m));
   o.line("const int s0 = src_beg[node], s1 = src_end[node];");
   for (const auto& S : a_subsets(p, T.paths, kDsrcRegs)) {
     o.open("");
     emit_da_loads(o, p, S);
-    // Edge ids and receivers of up to 64 out-edges, one per lane, taken with readlane.
+    // Edge ids and receivers of up to 64 out-edges, one per lane, taken with readlane (one
+    // edge per step) or, per lane group, with a lane shuffle (nE edges per step; el_ and il_ hold
+    // valid ids in every lane, and a group past the last edge gets zero phi and phi-dot).
     o.open("for (int kb_ = s0; kb_ < s1; kb_ += 64)");
-    o.line("const int kl_ = kb_ + (int)threadIdx.x;");
+    o.line("const int kl_ = kb_ + lane;");
     o.line("const int el_ = src_edge[kl_ < s1 ? kl_ : kb_];");
     o.line("const int il_ = recv[el_];");
     o.line("const int ne_ = min(64, s1 - kb_);");
-    o.open("for (int k_ = 0; k_ < ne_; ++k_)");
-    o.line("const int e = __builtin_amdgcn_readlane(el_, k_);");
-    o.line("const int i = __builtin_amdgcn_readlane(il_, k_);");
+    if (nE > 1) {
+      o.open(F("for (int k_ = 0; k_ < ne_; k_ += %d)", nE));
+      o.line("const bool ok_ = k_ + h_ < ne_;");
+      o.line("const int e = __shfl(el_, k_ + h_);");
+      o.line("const int i = __shfl(il_, k_ + h_);");
+    } else {
+      o.open("for (int k_ = 0; k_ < ne_; ++k_)");
+      o.line("const bool ok_ = true;");
+      o.line("const int e = __builtin_amdgcn_readlane(el_, k_);");
+      o.line("const int i = __builtin_amdgcn_readlane(il_, k_);");
+    }
     o.line(F("const real* __restrict__ g = G + (i64)(e - e_base) * %d;", 2 * p.g_stride));
     o.line(F("const real* __restrict__ gd = g + %d;", p.g_stride));
     emit_phi_rows(o, p);
-    for (int q = 0; q < K; ++q) o.line(F("const real f%d = ph[%d], fd%d = sphi * phd[%d];", q, q, q, q));
+    for (int q = 0; q < K; ++q)
+      o.line(F("const real fl%d_ = ph[%d], fdl%d_ = phd[%d];", q, q, q, q) +
+             F(" const real f%d = ok_ ? fl%d_ : R(0), fd%d = ok_ ? sphi * fdl%d_ : R(0);", q, q, q, q));
     o.line(F("const real* __restrict__ gi = gout + (i64)i * %d + uc;", p.c_out));
     for (int ob : out_blocks_of(p, S)) {
       const Block& B = p.out[ob];
       for (int m = 0; m < B.dim(); ++m) o.line(F("const real mb%d_%d = gi[%d];", ob, m, B.offset + m * B.mul));
     }
+    const auto order = chunks_of(g_ranges(p, S));
+    RowChunks rc[2] = {{p.g_stride, "g", "", order}, {p.g_stride, "gd", "d", order}};
     for (int pi : S) {
       const Path& P = p.paths[pi];
       emit_wwd(o, p, pi);
       std::vector<bool> started(d1, false);
       for (size_t t = 0; t < P.gpairs.size(); ++t) {
         int m1 = P.gpairs[t].m1, m3 = P.gpairs[t].m3;
+        if (bcast) {
+          const int idx = P.g_off + int(t);
+          o.line(bcast_term(o, rc[0], idx, F("b%d_%d", pi, m1), F("mb%d_%d", P.i_out, m3), !started[m1]));
+          o.line(bcast_term(o, rc[1], idx, F("bd%d_%d", pi, m1), F("mb%d_%d", P.i_out, m3), !started[m1]));
+          started[m1] = true;
+          continue;
+        }
         const std::string G = gref(p, pi, int(t), "g", "", false), Gd = gref(p, pi, int(t), "gd", "d", false);
         if (!started[m1]) {
           o.line(F("real b%d_%d = %s * mb%d_%d;", pi, m1, G.c_str(), P.i_out, m3));
@@ -469,7 +533,9 @@ void emit_dsrc_task(Out& o, const Plan& p, int ti, const Task& T) {
     o.close();
     o.close();
   }
-  o.open(F("if (u < %d)", MUL));
+  for (int span = gsz; span < 64; span *= 2)
+    for (int m = 0; m < d1; ++m) o.line(F("acc%d += __shfl_xor(acc%d, %d);", m, m, span));
+  o.open(nE > 1 ? F("if (lane < %d && u < %d)", gsz, MUL) : F("if (u < %d)", MUL));
   o.line(F("real* __restrict__ dst = gx + (i64)node * %d + %d + u;", p.c_in, IB.offset));
   o.open("if (accumulate)");
   for (int m = 0; m < d1; ++m) o.line(F("dst[%d] += acc%d;", m * MUL, m));
