@@ -832,6 +832,30 @@ void emit_swaps(Out& o, const std::vector<std::pair<std::string, std::string>>& 
   }
 }
 
+void emit_group_reduce_store(Out& o, int V, int gsz, bool f64, const std::string& dst_expr) {
+  if (gsz == 32) {
+    // Columns k and k + V/2 of the two 32-lane halves: one permlane16 swap puts column k of edge A,
+    // column k + V/2 of A, k of B and k + V/2 of B in rows 0..3, each row holding 16 lanes' worth
+    // of both rows of its half; one row sum then completes all four.
+    const int H = V / 2;
+    std::vector<std::pair<std::string, std::string>> pr;
+    for (int k = 0; k < H; ++k) pr.push_back({F("v%d", k), F("v%d", k + H)});
+    emit_swaps(o, pr, 16, f64);
+    for (int k = 0; k < H; ++k) o.line(F("v%d += v%d;", k, k + H));
+    for (int k = 0; k < H; ++k) o.line(F("v%d = rowsum(v%d); asm volatile(\"\" : \"+v\"(v%d));", k, k, k));
+    o.open("if ((lane & 15) == 0 && ok_)");
+    o.line("real* __restrict__ dst = " + dst_expr + " + ((lane >> 4) & 1) * " + std::to_string(64 * H) + ";");
+    for (int k = 0; k < H; ++k) o.line(F("dst[%d] = v%d;", 64 * k, k));
+    o.close();
+    return;
+  }
+  for (int k = 0; k < V; ++k) o.line(F("v%d = rowsum(v%d); asm volatile(\"\" : \"+v\"(v%d));", k, k, k));
+  o.open(F("if ((lane & %d) == 0 && ok_)", gsz - 1));
+  o.line("real* __restrict__ dst = " + dst_expr + ";");
+  for (int k = 0; k < V; ++k) o.line(F("dst[%d] = v%d;", 64 * k, k));
+  o.close();
+}
+
 const char* kRecvArgs =
     "const real* __restrict__ x, const real* __restrict__ phi, const real* __restrict__ A,"
     " const real* __restrict__ G, const int* __restrict__ row_ptr, const int* __restrict__ col,"
@@ -997,17 +1021,9 @@ void emit_bwd_recv_task(Out& o, const Plan& p, int ti, const Task& T, int col_of
         o.line("}");
       }
     }
-    if (nE > 1) {   // one edge per group: row sums (and the two rows of a half), stored by its first lane
-      for (int k = 0; k < V; ++k) {
-        o.line(F("v%d = rowsum(v%d);", k, k));
-        if (gsz == 32) o.line(F("v%d += __shfl_xor(v%d, 16);", k, k));
-        o.line(F("asm volatile(\"\" : \"+v\"(v%d));", k));
-      }
-      o.open(F("if ((lane & %d) == 0 && ok_)", gsz - 1));
-      o.line(F("real* __restrict__ dst = ep + ((i64)((e - e_base) >> 6) * %d + %d) * 64 + ((e - e_base) & 63);", row,
-               col_off));
-      for (int k = 0; k < V; ++k) o.line(F("dst[%d] = v%d;", 64 * k, k));
-      o.close();
+    if (nE > 1) {   // one edge per group: its columns reduced over the group's lanes and stored
+      emit_group_reduce_store(o, V, gsz, p.dtype == CGTP_F64,
+                              F("ep + ((i64)((e - e_base) >> 6) * %d + %d) * 64 + ((e - e_base) & 63)", row, col_off));
       return;
     }
     // Transpose-reduce the V partial sums over the 64 lanes: afterwards lane group r = lane / 16
@@ -1538,10 +1554,14 @@ static std::vector<Task> make_recv_backward_tasks(const Plan& p) {
     const int mul = p.out[p.paths[pi].i_out].mul;
     for (int cb = 0; cb * 64 < mul; ++cb) by_key[{mul, cb}].push_back(pi);
   }
-  int budget = p.dtype == CGTP_F64 ? kRecvBudget / 2 : kRecvBudget;  // 64-bit values take two registers
-  if (p.vec_g) budget /= kRecvLargeDiv;
   std::vector<std::pair<int, Task>> tasks;  // (cost, task)
   for (auto& kv : by_key) {
+    int budget = p.dtype == CGTP_F64 ? kRecvBudget / 2 : kRecvBudget;  // 64-bit values take two registers
+    // Large paths read per lane take registers for their coefficient vectors; blocks whose rows
+    // come by row broadcast (at most 32 channels in fp32) hold only a few chunks instead and take
+    // twice the budget of those (l <= 6, 32 channels: 106 -> 68 tasks, 12.1 -> 11.7 ms; the full
+    // budget drops to one wave per SIMD and measured 14.3 ms).
+    if (p.vec_g) budget /= bcast_edges_per_wave(p, kv.first.first) > 1 ? kRecvLargeDiv / 2 : kRecvLargeDiv;
     std::vector<int> order = kv.second;
     std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return regs(a) > regs(b); });
     std::vector<Task> bins;
@@ -1571,7 +1591,9 @@ static std::vector<Task> make_recv_backward_tasks(const Plan& p) {
 
 static std::vector<Task> make_dbl_recv_tasks(const Plan& p) {
   // Per path the receiver pass of the double backward holds A, its tangent and the A-bar tangent
-  // accumulators (3K values per lane): one task per path up to K = 16 (two at K <= 8).
+  // accumulators (3K values per lane): one task per path up to K = 16 (two at K <= 8).  (Two per
+  // task at K = 16 halve the per-edge channel reductions per path but drop to one wave per SIMD:
+  // l <= 6, 32 channels, 27.2 -> 36.8 ms.)
   std::vector<Task> t;
   for (const Task& f : make_forward_tasks(p))
     for (const auto& S : a_subsets(p, f.paths, kRegBudget / 4)) t.push_back({f.group, f.cb, S});

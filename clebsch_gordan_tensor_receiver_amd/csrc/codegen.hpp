@@ -120,6 +120,10 @@ void emit_recv_edge_loop(Out& o, const Plan& p, const std::vector<int>& blocks, 
                          int row_stride = 0, int nE = 1);
 void emit_wave_combine(Out& o, const std::string& prefix, int n, int nw);
 void emit_swaps(Out& o, const std::vector<std::pair<std::string, std::string>>& pairs, int width, bool f64);
+// Per-edge partial columns v0..v(V-1) of a wave whose lane groups of gsz lanes (16 or 32) each hold
+// one edge (`lane`, `ok_` in scope; V even): summed over each group's lanes and stored, column k
+// at dst[64 k], by one lane of each group with a valid edge, dst = `dst_expr` evaluated per lane.
+void emit_group_reduce_store(Out& o, int V, int gsz, bool f64, const std::string& dst_expr);
 void emit_edge_final(Out& o, const Plan& p, int ntask, int V);
 void emit_recv_edge_final(Out& o, const Plan& p, const std::vector<Task>& tasks);
 void emit_small_kernels(Out& o);

@@ -399,17 +399,9 @@ void emit_drecv_task(Out& o, const Plan& p, int ti, const Task& T, int col_off, 
         o.line("}");
       }
     }
-    if (nE > 1) {   // one edge per group: row sums (and the two rows of a half), stored by its first lane
-      for (int k = 0; k < V; ++k) {
-        o.line(F("v%d = rowsum(v%d);", k, k));
-        if (gsz == 32) o.line(F("v%d += __shfl_xor(v%d, 16);", k, k));
-        o.line(F("asm volatile(\"\" : \"+v\"(v%d));", k));
-      }
-      o.open(F("if ((lane & %d) == 0 && ok_)", gsz - 1));
-      o.line(F("real* __restrict__ dst = ep + ((i64)((e - e_base) >> 6) * %d + %d) * 64 + ((e - e_base) & 63);", row,
-               col_off));
-      for (int k = 0; k < V; ++k) o.line(F("dst[%d] = v%d;", 64 * k, k));
-      o.close();
+    if (nE > 1) {   // one edge per group: its columns reduced over the group's lanes and stored
+      emit_group_reduce_store(o, V, gsz, p.dtype == CGTP_F64,
+                              F("ep + ((i64)((e - e_base) >> 6) * %d + %d) * 64 + ((e - e_base) & 63)", row, col_off));
       return;
     }
     const int H = V / 2, Q = V / 4;
