@@ -832,7 +832,96 @@ void emit_swaps(Out& o, const std::vector<std::pair<std::string, std::string>>& 
   }
 }
 
-void emit_group_reduce_store(Out& o, int V, int gsz, bool f64, const std::string& dst_expr) {
+// Sums over the 16 lanes of every row of the fp32 registers v0 .. v(n-1), whose row r holds the 16
+// partials of one output each, and the stores of the sums.  Instead of a row sum per register
+// (four DPP adds each) the registers are transposed pairwise inside the rows: a bank-masked
+// row_mirror add puts register 2i's 8-lane partial sums in lanes 0-7 and register 2i+1's in
+// lanes 8-15 of register 2i; a row_half_mirror add then merges registers 4j and 4j+2 so that each
+// 4-lane bank holds one output (banks 0-3: registers 4j, 4j+2, 4j+1, 4j+3), and two quad
+// permutations complete the sums in every lane of the bank: 2 instructions per register where the
+// row sums take 4, and one store per four registers.
+// The DPP adds are inline assembly: each group starts with two wait states, so no source was
+// written by a VALU instruction right before, and the last one ends with two.  `store(kk, val)` is the statement that stores the
+// sum `val` of register `kk` (an int expression) for row r_ = lane >> 4; it runs in the lanes with
+// lane & 3 == 0 for which `ok` holds.
+void emit_row_reduce_store(Out& o, int n, const std::string& ok,
+                           const std::function<std::string(const std::string&, const std::string&)>& store) {
+  const int n4 = (n + 3) / 4 * 4;
+  // Registers past n exist only as positions: the adds that would fold them are left out (their
+  // lanes hold partials of other registers then, and their outputs are never stored).
+  auto reg = [&](int k) { return k < n ? F("v%d", k) : std::string(); };
+  // One asm group of pair steps: dst = dst + ctrl(dst) on banks m1, dst = src + ctrl(src) on banks
+  // m2 (left out without a src).
+  auto group = [&](const std::vector<std::array<std::string, 2>>& pairs, const char* ctrl, const char* m1,
+                   const char* m2) {
+    const size_t kMax = 14;
+    for (size_t at = 0; at < pairs.size(); at += kMax) {
+      const size_t cnt = std::min(pairs.size() - at, kMax);
+      int nsrc = 0;
+      for (size_t k = 0; k < cnt; ++k) nsrc += !pairs[at + k][1].empty();
+      // outputs %0 .. %(cnt-1): the pairs' first registers; inputs %cnt ..: the second ones
+      std::string t2, ops, ins;
+      for (size_t k = 0, si = 0; k < cnt; ++k) {
+        t2 += F("v_add_f32_dpp %%%d, %%%d, %%%d %s row_mask:0xf bank_mask:%s\\n\\t", int(k), int(k), int(k), ctrl, m1);
+        ops += F("%s\"+v\"(%s)", k ? ", " : "", pairs[at + k][0].c_str());
+        if (pairs[at + k][1].empty()) continue;
+        const int src = int(cnt + si);
+        t2 += F("v_add_f32_dpp %%%d, %%%d, %%%d %s row_mask:0xf bank_mask:%s\\n\\t", int(k), src, src, ctrl, m2);
+        ins += F("%s\"v\"(%s)", si ? ", " : "", pairs[at + k][1].c_str());
+        ++si;
+      }
+      o.line("asm volatile(\"s_nop 1\\n\\t" + t2 + "\" : " + ops + (nsrc ? " : " + ins : "") + ");");
+    }
+  };
+  std::vector<std::array<std::string, 2>> pr;
+  for (int i = 0; 2 * i < n; ++i) pr.push_back({reg(2 * i), reg(2 * i + 1)});
+  group(pr, "row_mirror", "0x3", "0xc");
+  pr.clear();
+  for (int j = 0; j < n4 / 4; ++j) pr.push_back({reg(4 * j), reg(4 * j + 2)});
+  group(pr, "row_half_mirror", "0x5", "0xa");
+  for (const char* qp : {"quad_perm:[1,0,3,2]", "quad_perm:[2,3,0,1]"})
+    for (int j0 = 0; j0 < n4 / 4; j0 += 14) {
+      std::string t, ops;
+      for (int j = j0; j < std::min(n4 / 4, j0 + 14); ++j) {
+        t += F("v_add_f32_dpp %%%d, %%%d, %%%d %s row_mask:0xf bank_mask:0xf\\n\\t", j - j0, j - j0, j - j0, qp);
+        ops += F("%s\"+v\"(%s)", j > j0 ? ", " : "", reg(4 * j).c_str());
+      }
+      // the last group ends with two wait states too, before code that does not know its writes
+      const bool last = std::string(qp) == "quad_perm:[2,3,0,1]" && j0 + 14 >= n4 / 4;
+      o.line("asm volatile(\"s_nop 1\\n\\t" + t + (last ? "s_nop 1" : "") + "\" : " + ops + ");");
+    }
+  o.open("if ((lane & 3) == 0 && (" + ok + "))");
+  o.line("const int r_ = lane >> 4, pb_ = (((lane >> 2) & 1) << 1) | ((lane >> 3) & 1);");
+  o.line("(void)r_;");
+  for (int j = 0; j < n4 / 4; ++j) {
+    o.open("");
+    o.line(F("const int kk_ = %d + pb_;", 4 * j));
+    o.line(F("if (kk_ < %d) ", n) + store("kk_", reg(4 * j)));
+    o.close();
+  }
+  o.close();
+}
+
+void emit_group_reduce_store(Out& o, int V, int nreal, int gsz, bool f64, const std::string& dst_expr) {
+  if (!f64) {
+    if (gsz == 32) {
+      // Columns k and k + V/2 of the two 32-lane halves: one permlane16 swap puts column k of edge
+      // A, column k + V/2 of A, k of B and k + V/2 of B in rows 0..3 of register k.
+      const int H = V / 2;
+      std::vector<std::pair<std::string, std::string>> pr;
+      for (int k = 0; k < H; ++k) pr.push_back({F("v%d", k), F("v%d", k + H)});
+      emit_swaps(o, pr, 16, false);
+      for (int k = 0; k < H; ++k) o.line(F("v%d += v%d;", k, k + H));
+      emit_row_reduce_store(o, H, "ok_", [&](const std::string& kk, const std::string& val) {
+        return "(" + dst_expr + F(")[64 * (%s + (r_ & 1) * %d)] = %s;", kk.c_str(), H, val.c_str());
+      });
+    } else {   // one edge per row, its columns in v0 .. v(nreal - 1) (the rest are padding, zero)
+      emit_row_reduce_store(o, nreal, "ok_", [&](const std::string& kk, const std::string& val) {
+        return "(" + dst_expr + ")[64 * " + kk + "] = " + val + ";";
+      });
+    }
+    return;
+  }
   if (gsz == 32) {
     // Columns k and k + V/2 of the two 32-lane halves: one permlane16 swap puts column k of edge A,
     // column k + V/2 of A, k of B and k + V/2 of B in rows 0..3, each row holding 16 lanes' worth
@@ -1022,7 +1111,7 @@ void emit_bwd_recv_task(Out& o, const Plan& p, int ti, const Task& T, int col_of
       }
     }
     if (nE > 1) {   // one edge per group: its columns reduced over the group's lanes and stored
-      emit_group_reduce_store(o, V, gsz, p.dtype == CGTP_F64,
+      emit_group_reduce_store(o, V, K + int(ycols.size()), gsz, p.dtype == CGTP_F64,
                               F("ep + ((i64)((e - e_base) >> 6) * %d + %d) * 64 + ((e - e_base) & 63)", row, col_off));
       return;
     }
@@ -1039,6 +1128,13 @@ void emit_bwd_recv_task(Out& o, const Plan& p, int ti, const Task& T, int col_of
     for (int k = 0; k < Q; ++k) pr.push_back({F("v%d", k), F("v%d", k + Q)});
     emit_swaps(o, pr, 16, f64);
     for (int k = 0; k < Q; ++k) o.line(F("v%d += v%d;", k, k + Q));
+    if (!f64) {   // column r Q + k of row r in v_k
+      emit_row_reduce_store(o, Q, "true", [&](const std::string& kk, const std::string& val) {
+        return F("ep[((i64)((e - e_base) >> 6) * %d + %d + r_ * %d + ", row, col_off, Q) + kk +
+               ") * 64 + ((e - e_base) & 63)] = " + val + ";";
+      });
+      return;
+    }
     for (int k = 0; k < Q; ++k) o.line(F("v%d = rowsum(v%d); asm volatile(\"\" : \"+v\"(v%d));", k, k, k));
     o.open("if ((lane & 15) == 0)");
     o.line(F("real* __restrict__ dst = ep + ((i64)((e - e_base) >> 6) * %d + %d + (lane >> 4) * %d) * 64"

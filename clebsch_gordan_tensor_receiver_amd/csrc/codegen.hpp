@@ -2,6 +2,7 @@
 // the shared edge/SH kernels; codegen_uvw.cpp: fully connected kernels).
 #pragma once
 
+#include <array>
 #include <cstdarg>
 #include <cstdio>
 #include <functional>
@@ -123,7 +124,11 @@ void emit_swaps(Out& o, const std::vector<std::pair<std::string, std::string>>& 
 // Per-edge partial columns v0..v(V-1) of a wave whose lane groups of gsz lanes (16 or 32) each hold
 // one edge (`lane`, `ok_` in scope; V even): summed over each group's lanes and stored, column k
 // at dst[64 k], by one lane of each group with a valid edge, dst = `dst_expr` evaluated per lane.
-void emit_group_reduce_store(Out& o, int V, int gsz, bool f64, const std::string& dst_expr);
+// Column sums of one edge per lane group of gsz lanes (V columns, the first nreal of them read by
+// the edge finalisation) and their stores.
+void emit_group_reduce_store(Out& o, int V, int nreal, int gsz, bool f64, const std::string& dst_expr);
+void emit_row_reduce_store(Out& o, int n, const std::string& ok,
+                           const std::function<std::string(const std::string&, const std::string&)>& store);
 void emit_edge_final(Out& o, const Plan& p, int ntask, int V);
 void emit_recv_edge_final(Out& o, const Plan& p, const std::vector<Task>& tasks);
 void emit_small_kernels(Out& o);

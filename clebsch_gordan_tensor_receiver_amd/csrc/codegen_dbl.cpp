@@ -400,7 +400,7 @@ void emit_drecv_task(Out& o, const Plan& p, int ti, const Task& T, int col_off, 
       }
     }
     if (nE > 1) {   // one edge per group: its columns reduced over the group's lanes and stored
-      emit_group_reduce_store(o, V, gsz, p.dtype == CGTP_F64,
+      emit_group_reduce_store(o, V, (p.radial ? 2 : 1) * K + 2 * ny, gsz, p.dtype == CGTP_F64,
                               F("ep + ((i64)((e - e_base) >> 6) * %d + %d) * 64 + ((e - e_base) & 63)", row, col_off));
       return;
     }
@@ -413,6 +413,13 @@ void emit_drecv_task(Out& o, const Plan& p, int ti, const Task& T, int col_off, 
     for (int k = 0; k < Q; ++k) pr.push_back({F("v%d", k), F("v%d", k + Q)});
     emit_swaps(o, pr, 16, f64);
     for (int k = 0; k < Q; ++k) o.line(F("v%d += v%d;", k, k + Q));
+    if (!f64) {   // column r Q + k of row r in v_k
+      emit_row_reduce_store(o, Q, "true", [&](const std::string& kk, const std::string& val) {
+        return F("ep[((i64)((e - e_base) >> 6) * %d + %d + r_ * %d + ", row, col_off, Q) + kk +
+               ") * 64 + ((e - e_base) & 63)] = " + val + ";";
+      });
+      return;
+    }
     for (int k = 0; k < Q; ++k) o.line(F("v%d = rowsum(v%d); asm volatile(\"\" : \"+v\"(v%d));", k, k, k));
     o.open("if ((lane & 15) == 0)");
     o.line(F("real* __restrict__ dst = ep + ((i64)((e - e_base) >> 6) * %d + %d + (lane >> 4) * %d) * 64"

@@ -591,6 +591,12 @@ void emit_edge_task(Out& o, const Plan& p, const std::vector<Side>& sides, int t
     for (int k = 0; k < Q; ++k) pr.push_back({F("v%d", k), F("v%d", k + Q)});
     emit_swaps(o, pr, 16, f64);
     for (int k = 0; k < Q; ++k) o.line(F("v%d += v%d;", k, k + Q));
+    if (!f64) {   // column r Q + k of row r in v_k
+      emit_row_reduce_store(o, Q, "true", [&](const std::string& kk, const std::string& val) {
+        return F("ep[(i64)(%d + r_ * %d + ", ti * V, Q) + kk + ") * eps + (e - e_base)] = " + val + ";";
+      });
+      return;
+    }
     for (int k = 0; k < Q; ++k) o.line(F("v%d = rowsum(v%d);", k, k));
     o.open("if ((lane & 15) == 0)");
     o.line(F("real* __restrict__ dst = ep + (i64)(%d + (lane >> 4) * %d) * eps + (e - e_base);", ti * V, Q));

@@ -1,11 +1,13 @@
-"""The row-broadcast FMAs of the channelwise kernels are inline assembly (v_fmac_f32_dpp and
-v_mul_f32_dpp with row_newbcast), whose operand hazards the compiler does not check: on gfx9 a
-DPP instruction must not read a VGPR that a VALU instruction wrote fewer than two wait states
-before.  The generated kernels only feed these instructions registers filled by memory loads;
-this test compiles 16- and 32-channel plans (forward, backward, double backward, which all take
-several edges per wave) and checks every broadcast in the disassembled code objects, following
-branches into each instruction's predecessors.  Runs on the CPU (the compiler targets gfx950
-without a GPU)."""
+"""The row-broadcast FMAs of the channelwise kernels (v_fmac_f32_dpp and v_mul_f32_dpp with
+row_newbcast) and the in-row transposing adds of their per-edge channel reductions (v_add_f32_dpp
+with row_mirror, row_half_mirror and quad permutations under bank masks) are inline assembly,
+whose operand hazards the compiler does not check: on gfx9 a DPP instruction must not read a VGPR
+that a VALU instruction wrote fewer than two wait states before.  The generated kernels feed the
+broadcasts only registers filled by memory loads and start every group of reduction adds with
+two wait states; this test compiles 16-, 32- and 64-channel plans (forward, backward, double
+backward: four, two and one edge per wave) and a fully connected plan, and checks every DPP
+instruction in the disassembled code objects, following branches into each instruction's
+predecessors.  Runs on the CPU (the compiler targets gfx950 without a GPU)."""
 import os
 import re
 import shutil
@@ -71,9 +73,9 @@ def _hazards(text):
 
     bad, count = [], 0
     for k, (a, op, args) in enumerate(insts):
-        if "row_newbcast" not in args:
+        if not op.endswith("_dpp"):
             continue
-        count += 1
+        count += "row_newbcast" in args
         src0 = _vregs(args.split(",")[1])
         # depth-first over predecessors until two wait states separate them from the DPP read
         stack = [(j, 0) for j in preds[k]]
@@ -99,10 +101,11 @@ def test_row_broadcast_operands_come_from_loads(tmp_path, monkeypatch):
     cache = tmp_path / "kernels"
     cache.mkdir()
     monkeypatch.setenv("CGTP_KERNEL_CACHE", str(cache))
-    for c in (16, 32):
+    for c in (16, 32, 64):
         irreps = f"{c}x0e+{c}x1o+{c}x2e"
         plan = cg.Plan(irreps, "1x0e+1x1o+1x2e", irreps, "uvu", "float32", 8)
         plan.compile((0, 1, 2))
+    cg.Plan("32x0e+32x1o", "1x0e+1x1o", "32x0e+32x1o", "uvw", "float32", 8).compile((0, 1))
     total = 0
     for co in sorted(cache.glob("*.co")):
         text = subprocess.run([OBJDUMP, "-d", "--mcpu=gfx950", str(co)], check=True, capture_output=True,
@@ -136,3 +139,8 @@ def test_hazard_scanner_flags_a_planted_hazard():
         "\tv_fmac_f32_dpp v1, v5, v2 row_newbcast:3 row_mask:0xf bank_mask:0xf // 000000001010: 00000000\n"
     )
     assert len(_hazards(branched)[1]) == 1
+    # any DPP source, not only row broadcasts: the transposing adds of the reductions
+    mirror = body.replace("v_fmac_f32_dpp v1, v5, v2 row_newbcast:3 row_mask:0xf bank_mask:0xf",
+                          "v_add_f32_dpp v1, v5, v5 row_mirror row_mask:0xf bank_mask:0xc")
+    assert _hazards(mirror) == (0, [mirror.splitlines()[1].split("//")[0].strip().split(None, 1)[0] + " " +
+                                   "v5, 0 -> v_add_f32_dpp v1, v5, v5 row_mirror row_mask:0xf bank_mask:0xc at 0x1004"])
