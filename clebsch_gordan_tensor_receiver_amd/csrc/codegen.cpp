@@ -477,10 +477,6 @@ constexpr int kFwdAValues = 32;
 constexpr int kSrcSplit = 2;   // waves sharing one sender's edge list in the source backward
 constexpr int kRecvGroup = 4;  // receivers (one wave each) per workgroup in the receiver backward
 
-// Loop over the in-edges e0 + start, e0 + start + stride, ... of a receiver (`e0`, `e1` in
-// scope).  Rows x_j of the input blocks `blocks` are loaded one edge ahead (software
-// pipelining), so their latency overlaps the arithmetic of the current edge.  The body sees
-// e, j, g (G row), f<q> (phi) and x<b>_<m>.
 // sr = sum_q phi-bar_q dphi_q/dr at rr (the radial part of the edge-vector gradient is sr r-hat);
 // 0 when phi is an input.  `pb` names the phi-bar registers pb0..pb{K-1}.
 void emit_radial_term(Out& o, const Plan& p, const std::string& pb) {
@@ -502,6 +498,11 @@ std::string phi_ptr(const Plan& p, const std::string& e, const std::string& grow
   return F("phi + (i64)%s * %d", e.c_str(), p.K);
 }
 
+// Loop over the in-edges e0 + start, e0 + start + stride, ... of a receiver (`e0`, `e1` in
+// scope).  The rows x_j of the input blocks `blocks` are gathered at the top of each edge's body
+// (other waves of the SIMD cover the latency; gathering the next edge's row ahead of the current
+// edge's arithmetic measured slower in the forward).  The body sees e, j, g (G row), f<q> (phi)
+// and x<b>_<m>.
 void emit_recv_edge_loop(Out& o, const Plan& p, const std::vector<int>& blocks, const std::string& start,
                          const std::string& stride, const std::function<void()>& body, bool block_uc,
                          int row_stride, int nE) {
