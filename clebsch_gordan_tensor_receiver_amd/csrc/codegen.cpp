@@ -840,10 +840,10 @@ void emit_swaps(Out& o, const std::vector<std::pair<std::string, std::string>>& 
 // lanes 8-15 of register 2i; a row_half_mirror add then merges registers 4j and 4j+2 so that each
 // 4-lane bank holds one output (banks 0-3: registers 4j, 4j+2, 4j+1, 4j+3), and two quad
 // permutations complete the sums in every lane of the bank: 2 instructions per register where the
-// row sums take 4, and one store per four registers.
-// The DPP adds are inline assembly: each group starts with two wait states, so no source was
-// written by a VALU instruction right before, and the last one ends with two.  `store(kk, val)` is the statement that stores the
-// sum `val` of register `kk` (an int expression) for row r_ = lane >> 4; it runs in the lanes with
+// row sums take 4, and one store per four registers.  The DPP adds are inline assembly: each
+// group starts with two wait states, so no source was written by a VALU instruction right before,
+// and the last one ends with two.  `store(kk, val)` is the statement that stores the sum `val` of
+// register `kk` (an int expression) for row r_ = lane >> 4; it runs in the lanes with
 // lane & 3 == 0 for which `ok` holds.
 void emit_row_reduce_store(Out& o, int n, const std::string& ok,
                            const std::function<std::string(const std::string&, const std::string&)>& store) {
@@ -861,17 +861,17 @@ void emit_row_reduce_store(Out& o, int n, const std::string& ok,
       int nsrc = 0;
       for (size_t k = 0; k < cnt; ++k) nsrc += !pairs[at + k][1].empty();
       // outputs %0 .. %(cnt-1): the pairs' first registers; inputs %cnt ..: the second ones
-      std::string t2, ops, ins;
+      std::string text, ops, ins;
       for (size_t k = 0, si = 0; k < cnt; ++k) {
-        t2 += F("v_add_f32_dpp %%%d, %%%d, %%%d %s row_mask:0xf bank_mask:%s\\n\\t", int(k), int(k), int(k), ctrl, m1);
+        text += F("v_add_f32_dpp %%%d, %%%d, %%%d %s row_mask:0xf bank_mask:%s\\n\\t", int(k), int(k), int(k), ctrl, m1);
         ops += F("%s\"+v\"(%s)", k ? ", " : "", pairs[at + k][0].c_str());
         if (pairs[at + k][1].empty()) continue;
         const int src = int(cnt + si);
-        t2 += F("v_add_f32_dpp %%%d, %%%d, %%%d %s row_mask:0xf bank_mask:%s\\n\\t", int(k), src, src, ctrl, m2);
+        text += F("v_add_f32_dpp %%%d, %%%d, %%%d %s row_mask:0xf bank_mask:%s\\n\\t", int(k), src, src, ctrl, m2);
         ins += F("%s\"v\"(%s)", si ? ", " : "", pairs[at + k][1].c_str());
         ++si;
       }
-      o.line("asm volatile(\"s_nop 1\\n\\t" + t2 + "\" : " + ops + (nsrc ? " : " + ins : "") + ");");
+      o.line("asm volatile(\"s_nop 1\\n\\t" + text + "\" : " + ops + (nsrc ? " : " + ins : "") + ");");
     }
   };
   std::vector<std::array<std::string, 2>> pr;
