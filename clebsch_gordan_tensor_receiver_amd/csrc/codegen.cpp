@@ -412,8 +412,10 @@ std::string bcast_term(Out& o, RowChunks& rc, int idx, const std::string& dst, c
     if (rc.loaded.insert(k).second)
       o.line(F("const V4 gc%s%d = gchunk(%s, %d, %d, r16_);", rc.tag.c_str(), k, rc.row.c_str(), 64 * k, rc.lim));
   };
-  if (!rc.loaded.count(c)) {
-    load(c);
+  // The first use of each chunk keeps the next kChunkAhead chunks of the list in flight (a sliding
+  // window rather than a burst of loads at every chunk not yet loaded).
+  if (rc.used.insert(c).second) {
+    if (!rc.loaded.count(c)) load(c);
     auto it = std::find(rc.order.begin(), rc.order.end(), c);
     if (it != rc.order.end()) {
       bool ahead = false;

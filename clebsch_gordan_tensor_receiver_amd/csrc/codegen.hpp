@@ -90,6 +90,7 @@ struct RowChunks {
   std::string row = "g", tag = "";
   std::vector<int> order = {};
   std::set<int> loaded = {};
+  std::set<int> used = {};
 };
 // Chunks (64 values) touched by the value ranges [first, second) of a row, in order of first use.
 std::vector<int> chunks_of(const std::vector<std::pair<int, int>>& ranges);
