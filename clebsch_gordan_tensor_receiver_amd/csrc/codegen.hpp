@@ -124,10 +124,12 @@ void emit_wave_combine(Out& o, const std::string& prefix, int n, int nw);
 void emit_swaps(Out& o, const std::vector<std::pair<std::string, std::string>>& pairs, int width, bool f64);
 // Per-edge partial columns v0..v(V-1) of a wave whose lane groups of gsz lanes (16 or 32) each hold
 // one edge (`lane`, `ok_` in scope; V even): summed over each group's lanes and stored, column k
-// at dst[64 k], by one lane of each group with a valid edge, dst = `dst_expr` evaluated per lane.
-// Column sums of one edge per lane group of gsz lanes (V columns, the first nreal of them read by
-// the edge finalisation) and their stores.
+// at dst[64 k] for an edge that is valid, dst = `dst_expr` evaluated per lane.  Only the first
+// nreal columns are read later; with 16-lane groups the rest (padding) are not summed in fp32.
 void emit_group_reduce_store(Out& o, int V, int nreal, int gsz, bool f64, const std::string& dst_expr);
+// Sums over the 16 lanes of each row of the fp32 registers v0..v(n-1) (row r of register k holds
+// the partials of one output) by an in-row transposition, and the statements `store(kk, val)`
+// that store them (see codegen.cpp).
 void emit_row_reduce_store(Out& o, int n, const std::string& ok,
                            const std::function<std::string(const std::string&, const std::string&)>& store);
 void emit_edge_final(Out& o, const Plan& p, int ntask, int V);
